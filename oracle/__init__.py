@@ -1,0 +1,17 @@
+"""CPU oracle for the HISA and flat DSA indexers -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The product path never calls it.
+"""
+from .oracle import (  # noqa: F401
+    load,
+    num_threads,
+    score,
+    mean_rows,
+    pool,
+    flat_query,
+    refine_query,
+    hisa_query,
+    hisa_batch,
+    flat_batch,
+)

@@ -1,0 +1,310 @@
+/*
+ * HISA hierarchical indexer and flat DSA indexer -- CPU ORACLE.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Plain, slow, obviously correct reference of what
+ * the indexing path computes.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library; the product path never
+ * does.  It shares no code, header, table or helper with the HIP library.
+ *
+ * Sources (the pages about "HISA: Efficient Hierarchical Indexing for
+ * Fine-Grained Sparse Attention", arXiv 2603.28458):
+ *   [P2-Method]  gptget.net English summary, "Methodology": two stages, block
+ *                representatives by mean pooling, top-m blocks, then the
+ *                original indexer on the tokens of the kept blocks.
+ *   [P5-Detail]  gptget.net Chinese summary, method details (方法详解): split
+ *                the length-L prefix into contiguous blocks of size B, mean-pool
+ *                each block, score every block representative with the
+ *                original indexer, keep the top m blocks, take all their
+ *                tokens, re-score them with the original indexer, keep k.
+ *   [Abstract]   arXiv abstract (mlsanity.com page): the indexer scores every
+ *                historical key of the prefix for each query (flat DSA); HISA
+ *                keeps the token-level top-k set the sparse attention consumes.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - indexer score s(q,w,x) = sum_h w_h * max(0, q_h . x), no extra scale;
+ *   - a query at position t sees keys j <= t (inclusive causal prefix);
+ *   - blocks are aligned at token 0; the query's own block b_t = floor(t/B) is
+ *     represented by the mean of its keys j in [b_t*B, t] only;
+ *   - representative = bf16_RNE(fp32_RNE(sum_j K_j / cnt)), the sum taken in
+ *     fp64 in increasing j (bf16 representatives feed a bf16 scorer);
+ *   - ranking is by (score descending, index ascending); -0 equals +0;
+ *   - fewer than k candidates: the rest of the row is -1 (score -inf).
+ *
+ * Arithmetic: every dot product and the head sum are accumulated in fp64
+ * from the exact bf16/fp32 inputs; ranks are taken on the fp64 values; the
+ * reported scores are those values rounded to fp32.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------- bf16 <-> binary64/binary32 (data decoding, not method) ---------- */
+
+static double bf16_val(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* float32 -> bf16, round to nearest, ties to even (finite inputs). */
+static uint16_t bf16_round(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+/* ---------- the indexer score (DSA form) ---------- */
+
+/* s(q, w, x) = sum over heads h of w_h * ReLU(q_h . x)
+ * q: H x d bf16 (row h = head h), w: H fp32, x: d bf16. */
+double oracle_score(const uint16_t *q, const float *w, const uint16_t *x, int H, int d)
+{
+    double s = 0.0;
+    for (int h = 0; h < H; ++h) {
+        double dot = 0.0;
+        for (int i = 0; i < d; ++i)
+            dot += bf16_val(q[(size_t)h * d + i]) * bf16_val(x[i]);
+        double relu = dot > 0.0 ? dot : 0.0;
+        s += (double)w[h] * relu;
+    }
+    return s;
+}
+
+/* ---------- mean pooling of a run of key rows ---------- */
+
+/* out = bf16(fp32(mean of rows [row0, row1) of K)), K rows of d bf16. */
+void oracle_mean_rows(const uint16_t *K, int64_t row0, int64_t row1, int d, uint16_t *out)
+{
+    double cnt = (double)(row1 - row0);
+    for (int i = 0; i < d; ++i) {
+        double sum = 0.0;
+        for (int64_t j = row0; j < row1; ++j)
+            sum += bf16_val(K[(size_t)j * d + i]);
+        out[i] = bf16_round((float)(sum / cnt));
+    }
+}
+
+/* Block pool of a key cache holding L rows: block b covers rows
+ * [b*B, min(b*B + B, L)).  means: [S, ceil(L/B), d]. */
+void oracle_pool(const uint16_t *K, int64_t k_seq_stride, int S, int64_t L, int d, int B,
+                 uint16_t *means)
+{
+    int64_t nblk = (L + B - 1) / B;
+    for (int s = 0; s < S; ++s) {
+        const uint16_t *Ks = K + (size_t)s * k_seq_stride;
+#pragma omp parallel for schedule(static)
+        for (int64_t b = 0; b < nblk; ++b) {
+            int64_t r1 = (b + 1) * B < L ? (b + 1) * B : L;
+            oracle_mean_rows(Ks, b * B, r1, d, means + ((size_t)s * nblk + b) * d);
+        }
+    }
+}
+
+/* ---------- ranking: (score desc, index asc) ---------- */
+
+typedef struct {
+    double s;
+    int64_t i;
+} cand_t;
+
+static int by_score_then_index(const void *pa, const void *pb)
+{
+    const cand_t *a = (const cand_t *)pa, *b = (const cand_t *)pb;
+    if (a->s > b->s) return -1;
+    if (a->s < b->s) return 1;
+    return (a->i < b->i) ? -1 : (a->i > b->i);
+}
+
+static int by_index(const void *pa, const void *pb)
+{
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return (a > b) - (a < b);
+}
+
+/* Keep the first min(k, n) entries of the ranked list; pad with -1 / -inf. */
+static int emit_top(cand_t *c, int64_t n, int k, int32_t *out_idx, float *out_score)
+{
+    qsort(c, (size_t)n, sizeof *c, by_score_then_index);
+    int keff = n < k ? (int)n : k;
+    for (int i = 0; i < keff; ++i) {
+        out_idx[i] = (int32_t)c[i].i;
+        if (out_score) out_score[i] = (float)c[i].s;
+    }
+    for (int i = keff; i < k; ++i) {
+        out_idx[i] = -1;
+        if (out_score) out_score[i] = -INFINITY;
+    }
+    return keff;
+}
+
+/* ---------- flat DSA indexer: every key of the prefix ---------- */
+
+/* Top-k over j in [0, t] of s(q, w, K_j).  Returns k_eff = min(k, t+1).
+ * Output is ranked (score desc, index asc).  all_scores (nullable, t+1). */
+int oracle_flat_query(const uint16_t *q, const float *w, const uint16_t *K, int H, int d,
+                      int64_t t, int k, int32_t *out_idx, float *out_score, double *all_scores)
+{
+    int64_t n = t + 1;
+    cand_t *c = (cand_t *)malloc((size_t)n * sizeof *c);
+    if (!c) return -1;
+    for (int64_t j = 0; j < n; ++j) {
+        c[j].s = oracle_score(q, w, K + (size_t)j * d, H, d);
+        c[j].i = j;
+        if (all_scores) all_scores[j] = c[j].s;
+    }
+    int keff = emit_top(c, n, k, out_idx, out_score);
+    free(c);
+    return keff;
+}
+
+/* ---------- HISA: token refinement inside a given block set ---------- */
+
+/* Candidates C = { j : floor(j/B) in blocks, j <= t }; top-k of s(q,w,K_j) over C.
+ * blocks: nsel distinct block ids (any order).  Returns k_eff = min(k, |C|).
+ * cand_count (nullable) receives |C|. */
+int oracle_refine_query(const uint16_t *q, const float *w, const uint16_t *K, int H, int d,
+                        int64_t t, int B, const int32_t *blocks, int nsel, int k,
+                        int32_t *out_idx, float *out_score, int64_t *cand_count)
+{
+    int64_t n = 0;
+    cand_t *c = (cand_t *)malloc(((size_t)nsel * B + 1) * sizeof *c);
+    if (!c) return -1;
+    for (int b = 0; b < nsel; ++b) {
+        int64_t j0 = (int64_t)blocks[b] * B;
+        for (int64_t j = j0; j < j0 + B && j <= t; ++j) {
+            c[n].s = oracle_score(q, w, K + (size_t)j * d, H, d);
+            c[n].i = j;
+            ++n;
+        }
+    }
+    if (cand_count) *cand_count = n;
+    int keff = emit_top(c, n, k, out_idx, out_score);
+    free(c);
+    return keff;
+}
+
+/* ---------- HISA: full two-stage query ---------- */
+
+/* One query at position t against the key cache K (rows 0..t are read).
+ *  full_means (nullable): precomputed bf16 means of complete blocks
+ *      ([b][d] for b < floor(t/B)); when null they are computed here.
+ *  out_blk [m]: kept block ids, ascending, -1 padded.
+ *  blk_score (nullable) [floor(t/B)+1]: fp64 block scores.
+ *  Returns k_eff. */
+int oracle_hisa_query(const uint16_t *q, const float *w, const uint16_t *K,
+                      const uint16_t *full_means, int H, int d, int64_t t, int B, int m, int k,
+                      int32_t *out_idx, float *out_score, int32_t *out_blk, double *blk_score)
+{
+    int64_t bt = t / B;          /* the query's own block */
+    int64_t nb = bt + 1;         /* blocks visible to the query */
+    uint16_t *rep = (uint16_t *)malloc((size_t)d * sizeof *rep);
+    cand_t *bc = (cand_t *)malloc((size_t)nb * sizeof *bc);
+    int32_t *sel = (int32_t *)malloc((size_t)(m > 0 ? m : 1) * sizeof *sel);
+    if (!rep || !bc || !sel) {
+        free(rep); free(bc); free(sel);
+        return -1;
+    }
+    /* stage 1: score every block representative with the original indexer */
+    for (int64_t b = 0; b < nb; ++b) {
+        const uint16_t *r;
+        if (b < bt && full_means) {
+            r = full_means + (size_t)b * d;
+        } else {
+            int64_t r1 = (b < bt) ? (b + 1) * B : t + 1;
+            oracle_mean_rows(K, b * B, r1, d, rep);
+            r = rep;
+        }
+        bc[b].s = oracle_score(q, w, r, H, d);
+        bc[b].i = b;
+        if (blk_score) blk_score[b] = bc[b].s;
+    }
+    /* keep the top m blocks */
+    qsort(bc, (size_t)nb, sizeof *bc, by_score_then_index);
+    int meff = nb < m ? (int)nb : m;
+    for (int i = 0; i < meff; ++i) sel[i] = (int32_t)bc[i].i;
+    qsort(sel, (size_t)meff, sizeof *sel, by_index);
+    for (int i = 0; i < m; ++i) out_blk[i] = i < meff ? sel[i] : -1;
+    /* stage 2: original indexer on every token of the kept blocks */
+    int keff = oracle_refine_query(q, w, K, H, d, t, B, sel, meff, k, out_idx, out_score, NULL);
+    free(rep); free(bc); free(sel);
+    return keff;
+}
+
+/* ---------- batched drivers (OpenMP over queries) ---------- */
+
+/* Queries are q[S][T][H][d], w[S][T][H], qpos[S][T]; K row j of sequence s at
+ * K + s*k_seq_stride + j*d.  sel (nullable): list of nsel flat query ids
+ * (s*T + i) to evaluate; null = all S*T.  Outputs are indexed by flat id.
+ * Returns 0, or -1 on a bad position or allocation failure. */
+int oracle_hisa_batch(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
+                      int64_t k_seq_stride, int64_t L, int S, int T, int H, int d, int B, int m,
+                      int k, const int32_t *sel, int nsel, int32_t *out_idx, float *out_score,
+                      int32_t *out_blk)
+{
+    int n = sel ? nsel : S * T;
+    int64_t nfull = L / B;       /* blocks complete within the cache */
+    uint16_t *means = (uint16_t *)malloc((size_t)S * (nfull > 0 ? nfull : 1) * d * sizeof *means);
+    if (!means) return -1;
+    for (int s = 0; s < S; ++s) {
+        const uint16_t *Ks = K + (size_t)s * k_seq_stride;
+#pragma omp parallel for schedule(static)
+        for (int64_t b = 0; b < nfull; ++b)
+            oracle_mean_rows(Ks, b * B, (b + 1) * B, d, means + ((size_t)s * nfull + b) * d);
+    }
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|| : bad)
+    for (int e = 0; e < n; ++e) {
+        int id = sel ? sel[e] : e;
+        int s = id / T;
+        int64_t t = qpos[id];
+        if (t < 0 || t >= L) { bad = 1; continue; }
+        int r = oracle_hisa_query(q + (size_t)id * H * d, w + (size_t)id * H,
+                                  K + (size_t)s * k_seq_stride, means + (size_t)s * nfull * d,
+                                  H, d, t, B, m, k, out_idx + (size_t)id * k,
+                                  out_score ? out_score + (size_t)id * k : NULL,
+                                  out_blk + (size_t)id * m, NULL);
+        if (r < 0) bad = 1;
+    }
+    free(means);
+    return bad ? -1 : 0;
+}
+
+int oracle_flat_batch(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
+                      int64_t k_seq_stride, int64_t L, int S, int T, int H, int d, int k,
+                      const int32_t *sel, int nsel, int32_t *out_idx, float *out_score)
+{
+    int n = sel ? nsel : S * T;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|| : bad)
+    for (int e = 0; e < n; ++e) {
+        int id = sel ? sel[e] : e;
+        int s = id / T;
+        int64_t t = qpos[id];
+        if (t < 0 || t >= L) { bad = 1; continue; }
+        int r = oracle_flat_query(q + (size_t)id * H * d, w + (size_t)id * H,
+                                  K + (size_t)s * k_seq_stride, H, d, t, k,
+                                  out_idx + (size_t)id * k,
+                                  out_score ? out_score + (size_t)id * k : NULL, NULL);
+        if (r < 0) bad = 1;
+    }
+    return bad ? -1 : 0;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

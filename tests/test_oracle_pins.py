@@ -1,0 +1,336 @@
+"""Pins for the CPU oracle: each test checks the oracle against something other
+than itself -- hand-derived values, closed forms, textbook routines (a stable
+lexicographic sort, an exactly rounded sum), brute force on tiny inputs, and
+invariants the method fixes (keeping every block reduces HISA to the flat
+indexer; block size 1 makes blocks tokens; the result never depends on keys
+after the query position).
+
+Integer-valued inputs are used wherever a ranking is compared exactly, so that
+every score is exact in binary64 on both sides and ties are real ties.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from sparse_attention_token_amd.synth import bf16_bits, bf16_to_f32, gaussian_case, clustered_case
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_example.json")
+
+
+# ---------------------------------------------------------------- helpers (numpy brute force)
+
+def np_scores(q_bits, w, K_bits):
+    """s_j = sum_h w_h * max(0, q_h . K_j), float64, for all rows of K."""
+    qf = bf16_to_f32(q_bits).astype(np.float64)          # [H, d]
+    Kf = bf16_to_f32(K_bits).astype(np.float64)          # [n, d]
+    dots = Kf @ qf.T                                     # [n, H]
+    return (np.maximum(dots, 0.0) * w.astype(np.float64)[None, :]).sum(axis=1)
+
+
+def np_topk(scores, ids, k):
+    """Textbook ranking: stable sort by (score desc, id asc), keep k, pad -1."""
+    order = np.lexsort((ids, -scores))[:k]
+    out = np.full(k, -1, dtype=np.int64)
+    out[: len(order)] = ids[order]
+    return out
+
+
+def np_mean_bits(rows_bits):
+    """bf16(fp32(exact mean)) of bf16 rows [n, d] -- exact sum via math.fsum."""
+    f = bf16_to_f32(rows_bits).astype(np.float64)
+    n = f.shape[0]
+    means = np.array([math.fsum(f[:, i]) / n for i in range(f.shape[1])], dtype=np.float64)
+    return bf16_bits(means.astype(np.float32))
+
+
+def int_case(rng, L, H, d, lo=-3, hi=4):
+    """Small-integer keys/queries/weights: every score is exact in binary64."""
+    K = bf16_bits(rng.integers(lo, hi, size=(L, d)).astype(np.float32))
+    q = bf16_bits(rng.integers(lo, hi, size=(H, d)).astype(np.float32))
+    w = rng.integers(-2, 3, size=H).astype(np.float32)
+    w[w == 0] = 1.0
+    return q, w, K
+
+
+def np_hisa(q, w, K, t, B, m, k):
+    """Brute-force HISA for one query (tiny sizes): returns (blocks, idx)."""
+    bt = t // B
+    reps = []
+    for b in range(bt + 1):
+        r1 = (b + 1) * B if b < bt else t + 1
+        reps.append(np_mean_bits(K[b * B:r1]))
+    sig = np_scores(q, w, np.stack(reps))
+    blocks = np.sort(np_topk(sig, np.arange(bt + 1), min(m, bt + 1)))
+    cand = np.array([j for b in blocks for j in range(b * B, min(b * B + B, t + 1))], dtype=np.int64)
+    sc = np_scores(q, w, K[cand])
+    return blocks, np_topk(sc, cand, k), sig
+
+
+# ---------------------------------------------------------------- golden, hand-derived
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _golden_inputs(g):
+    q = bf16_bits(np.array(g["q"], dtype=np.float32))
+    w = np.array(g["w"], dtype=np.float32)
+    K = bf16_bits(np.array(g["K"], dtype=np.float32))
+    return q, w, K
+
+
+def _fl(v):
+    return np.array([-np.inf if x == "-inf" else x for x in v], dtype=np.float32)
+
+
+def test_golden_token_scores(orc):
+    g = _golden()
+    q, w, K = _golden_inputs(g)
+    got = [orc.score(q, w, K[j]) for j in range(g["L"])]
+    assert got == g["token_scores"]
+
+
+@pytest.mark.parametrize("ci", range(5))
+def test_golden_hisa_cases(orc, ci):
+    g = _golden()
+    c = g["cases"][ci]
+    q, w, K = _golden_inputs(g)
+    idx, sc, blk, bsc, keff = orc.hisa_query(q, w, K, c["t"], g["B"], c["m"], c["k"])
+    assert list(bsc) == c["block_scores"]
+    assert [b for b in blk if b >= 0] == c["blocks"]
+    assert list(idx) == c["idx"]
+    np.testing.assert_array_equal(sc, _fl(c["score"]))
+    fidx, fsc, _ = orc.flat_query(q, w, K, c["t"], c["k"])
+    assert list(fidx) == c["flat_idx"]
+    np.testing.assert_array_equal(fsc, _fl(c["flat_score"]))
+
+
+def test_golden_mean_rounding(orc):
+    g = _golden()
+    for c in g["means"]["cases"]:
+        rows = np.array([[int(h, 16)] for h in c["rows"]], dtype=np.uint16)
+        got = orc.mean_rows(rows, 0, len(rows))
+        assert int(got[0]) == int(c["mean"], 16), c["why"]
+
+
+# ---------------------------------------------------------------- the score
+
+@pytest.mark.parametrize("H,d", [(1, 2), (3, 8), (4, 64), (64, 128)])
+def test_score_bruteforce(orc, H, d):
+    rng = np.random.default_rng(1000 + H * d)
+    q = bf16_bits(rng.standard_normal((H, d)).astype(np.float32))
+    w = rng.standard_normal(H).astype(np.float32)
+    K = bf16_bits(rng.standard_normal((20, d)).astype(np.float32))
+    ref = np_scores(q, w, K)
+    got = np.array([orc.score(q, w, K[j]) for j in range(20)])
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_score_closed_forms(orc):
+    rng = np.random.default_rng(7)
+    d = 16
+    x = bf16_bits(rng.standard_normal(d).astype(np.float32))
+    xf = bf16_to_f32(x)
+    for i in range(d):
+        e = np.zeros((1, d), np.float32)
+        e[0, i] = 1.0
+        # one head, unit weight, unit query along axis i: s = max(0, x_i)
+        assert orc.score(bf16_bits(e), np.ones(1, np.float32), x) == max(0.0, float(xf[i]))
+    # a negative weight flips the sign of the (non-negative) ReLU term
+    q = bf16_bits(rng.standard_normal((1, d)).astype(np.float32))
+    pos = orc.score(q, np.array([1.0], np.float32), x)
+    neg = orc.score(q, np.array([-1.0], np.float32), x)
+    assert neg == -pos and pos >= 0.0
+    # heads add up: s over 3 heads == sum of the one-head scores
+    q3 = bf16_bits(rng.standard_normal((3, d)).astype(np.float32))
+    w3 = np.array([0.5, -0.25, 2.0], np.float32)
+    parts = sum(orc.score(q3[h:h + 1], w3[h:h + 1], x) for h in range(3))
+    assert abs(orc.score(q3, w3, x) - parts) <= 1e-12 * (1 + abs(parts))
+
+
+# ---------------------------------------------------------------- flat DSA top-k
+
+@pytest.mark.parametrize("seed", range(6))
+def test_flat_matches_textbook_sort(orc, seed):
+    rng = np.random.default_rng(seed)
+    L, H, d = 40, 3, 8
+    q, w, K = int_case(rng, L, H, d)
+    for t in (0, 5, 17, 39):
+        for k in (1, 4, 16, 64):
+            idx, sc, keff = orc.flat_query(q, w, K, t, k)
+            s = np_scores(q, w, K[: t + 1])
+            ref = np_topk(s, np.arange(t + 1), k)
+            np.testing.assert_array_equal(idx, ref)
+            assert keff == min(k, t + 1)
+            np.testing.assert_array_equal(sc[:keff], s[ref[:keff]].astype(np.float32))
+            assert np.all(np.isneginf(sc[keff:]))
+
+
+def test_flat_ties_and_signed_zero(orc):
+    # duplicate keys tie exactly: the lower index ranks first.  Keys orthogonal to
+    # every head score exactly 0 whatever the sign of w (w*0 may be -0): -0 == +0.
+    d = 4
+    q = bf16_bits(np.array([[1, 0, 0, 0], [0, 1, 0, 0]], np.float32))
+    w = np.array([-1.0, 1.0], np.float32)
+    K = bf16_bits(np.array([[0, 0, 1, 0],      # 0 (both dots 0)
+                            [0, 2, 0, 0],      # 2
+                            [-1, 0, 5, 5],     # 0 (head0 dot <0, head1 dot 0)
+                            [0, 2, 0, 0],      # 2 (duplicate of row 1)
+                            [1, 0, 0, 0],      # -1
+                            [0, 0, 0, 1]], np.float32))   # 0
+    idx, sc, _ = orc.flat_query(q, w, K, 5, 4)
+    assert list(idx) == [1, 3, 0, 2]
+    idx, sc, _ = orc.flat_query(q, w, K, 5, 3)
+    assert list(idx) == [1, 3, 0]
+
+
+# ---------------------------------------------------------------- representatives
+
+@pytest.mark.parametrize("B,L", [(1, 7), (4, 30), (64, 1000), (128, 128 * 3 + 77)])
+def test_pool_is_exact_mean(orc, B, L):
+    rng = np.random.default_rng(B + L)
+    d = 32
+    K = bf16_bits(rng.standard_normal((2, L, d)).astype(np.float32) * 3)
+    got = orc.pool(K, L, B)
+    nblk = -(-L // B)
+    assert got.shape == (2, nblk, d)
+    for s in range(2):
+        for b in range(nblk):
+            ref = np_mean_bits(K[s, b * B:min(b * B + B, L)])
+            np.testing.assert_array_equal(got[s, b], ref)
+
+
+def test_pool_within_one_ulp_of_float64_mean(orc):
+    rng = np.random.default_rng(3)
+    K = bf16_bits(rng.standard_normal((1, 256, 64)).astype(np.float32))
+    got = bf16_to_f32(orc.pool(K, 256, 128)).astype(np.float64)
+    ref = bf16_to_f32(K).astype(np.float64).reshape(2, 128, 64).mean(axis=1)
+    ulp = np.abs(ref) * 2.0 ** -7 + 1e-30
+    assert np.all(np.abs(got[0] - ref) <= ulp)
+
+
+# ---------------------------------------------------------------- HISA invariants
+
+@pytest.mark.parametrize("seed", range(4))
+def test_hisa_keep_all_blocks_is_flat(orc, seed):
+    c = gaussian_case(1, 300, 4, 4, 64, 16, 0, 50, seed=seed, qpos=[16, 120, 255, 299])
+    for i in range(4):
+        t = int(c.qpos[0, i])
+        nb = t // c.B + 1
+        for m in (nb, nb + 3):
+            idx, sc, blk, _, keff = orc.hisa_query(c.q[0, i], c.w[0, i], c.K[0], t, c.B, m, c.k)
+            fidx, fsc, fkeff = orc.flat_query(c.q[0, i], c.w[0, i], c.K[0], t, c.k)
+            np.testing.assert_array_equal(idx, fidx)
+            np.testing.assert_array_equal(sc, fsc)
+            assert keff == fkeff
+            assert list(blk[:nb]) == list(range(nb)) and np.all(blk[nb:] == -1)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_hisa_block_size_one_is_flat(orc, seed):
+    # B = 1: each representative is its own key, so the top-m blocks are the top-m
+    # tokens and for k <= m the refined top-k is the flat top-k.
+    rng = np.random.default_rng(100 + seed)
+    q, w, K = int_case(rng, 50, 3, 8)
+    for t in (3, 20, 49):
+        for m, k in ((4, 4), (10, 3), (60, 60)):
+            idx, sc, blk, bsc, _ = orc.hisa_query(q, w, K, t, 1, m, k)
+            fidx, fsc, _ = orc.flat_query(q, w, K, t, k)
+            np.testing.assert_array_equal(idx, fidx)
+            np.testing.assert_array_equal(bsc, np_scores(q, w, K[: t + 1]))
+
+
+def test_hisa_constructed_block_choice(orc):
+    # keys of the chosen blocks point along u, all others along -u; every head
+    # is u with a positive weight -> chosen blocks score > 0, the rest exactly 0.
+    d, B, H = 8, 4, 2
+    u = np.zeros(d, np.float32)
+    u[:3] = [1, 2, -1]
+    chosen = [1, 4, 6]
+    L = 8 * B
+    K = np.array([(1.0 + (j % 3)) * (u if (j // B) in chosen else -u) for j in range(L)], np.float32)
+    q = bf16_bits(np.stack([u, 2 * u]))
+    w = np.array([1.0, 0.5], np.float32)
+    idx, sc, blk, bsc, keff = orc.hisa_query(q, w, bf16_bits(K), L - 1, B, 3, 5)
+    assert list(blk) == chosen
+    assert all(bsc[b] > 0 for b in chosen) and all(bsc[b] == 0 for b in range(8) if b not in chosen)
+    # token j of a chosen block is (1 + j%3) u: score (1 + j%3) * (|u|^2 + 0.5*2|u|^2) = 12 (1 + j%3).
+    # Kept tokens 4..7, 16..19, 24..27: j%3==2 -> {5, 17, 26} at 36, then j%3==1 -> {4, 7, ...} at 24.
+    assert list(idx) == [5, 17, 26, 4, 7]
+    np.testing.assert_array_equal(sc, np.array([36, 36, 36, 24, 24], np.float32))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_hisa_bruteforce_tiny(orc, seed):
+    rng = np.random.default_rng(200 + seed)
+    L, H, d = 48, 2, 6
+    q, w, K = int_case(rng, L, H, d)
+    for B in (1, 2, 4, 8):
+        for t in (0, B - 1, B, 23, 47):
+            for m, k in ((1, 1), (2, 5), (3, 16), (5, 48)):
+                idx, sc, blk, bsc, keff = orc.hisa_query(q, w, K, t, B, m, k)
+                rblk, ridx, rsig = np_hisa(q, w, K, t, B, m, k)
+                np.testing.assert_array_equal(bsc, rsig)
+                np.testing.assert_array_equal(blk[: len(rblk)], rblk)
+                assert np.all(blk[len(rblk):] == -1)
+                np.testing.assert_array_equal(idx, ridx)
+
+
+def test_hisa_monotone_in_m(orc):
+    # nested block sets: the i-th best kept score can only grow with m
+    c = gaussian_case(1, 512, 1, 4, 64, 32, 0, 40, seed=5)
+    t = 511
+    prev = None
+    for m in range(1, 17):
+        idx, sc, blk, _, keff = orc.hisa_query(c.q[0, 0], c.w[0, 0], c.K[0], t, 32, m, 40)
+        if prev is not None:
+            blk_prev, sc_prev, keff_prev = prev
+            assert set(blk_prev[blk_prev >= 0]) <= set(blk[blk >= 0])
+            assert np.all(sc[:keff_prev] >= sc_prev[:keff_prev])
+        prev = (blk, sc, keff)
+
+
+def test_results_ignore_future_keys(orc):
+    c = clustered_case(1, 1000, 1, 8, 64, 64, 3, 30, seed=9, qpos=[700], latent_block=64)
+    K2 = c.K.copy()
+    K2[0, 701:] = bf16_bits(np.full((299, 64), 7.0, np.float32))
+    a = orc.hisa_query(c.q[0, 0], c.w[0, 0], c.K[0], 700, 64, 3, 30)
+    b = orc.hisa_query(c.q[0, 0], c.w[0, 0], K2[0], 700, 64, 3, 30)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    fa = orc.flat_query(c.q[0, 0], c.w[0, 0], c.K[0], 700, 30)
+    fb = orc.flat_query(c.q[0, 0], c.w[0, 0], K2[0], 700, 30)
+    np.testing.assert_array_equal(fa[0], fb[0])
+    assert np.all(fa[0] <= 700)
+
+
+def test_padding_when_few_candidates(orc):
+    c = gaussian_case(1, 64, 1, 4, 64, 16, 2, 40, seed=11, qpos=[20])
+    idx, sc, blk, _, keff = orc.hisa_query(c.q[0, 0], c.w[0, 0], c.K[0], 20, 16, 2, 40)
+    assert keff == 21 and np.all(idx[21:] == -1) and np.all(np.isneginf(sc[21:]))
+    assert sorted(idx[:21]) == list(range(21))
+    fidx, fsc, fkeff = orc.flat_query(c.q[0, 0], c.w[0, 0], c.K[0], 20, 40)
+    assert fkeff == 21 and np.all(fidx[21:] == -1)
+
+
+def test_batch_drivers_match_single_queries(orc):
+    c = clustered_case(2, 700, 3, 4, 64, 64, 4, 32, seed=12, latent_block=64,
+                       qpos=[[100, 400, 699], [63, 64, 650]])
+    idx, sc, blk = orc.hisa_batch(c.q, c.w, c.qpos, c.K, c.L, c.B, c.m, c.k)
+    fidx, fsc = orc.flat_batch(c.q, c.w, c.qpos, c.K, c.L, c.k)
+    for s in range(2):
+        for i in range(3):
+            t = int(c.qpos[s, i])
+            a = orc.hisa_query(c.q[s, i], c.w[s, i], c.K[s], t, c.B, c.m, c.k)
+            np.testing.assert_array_equal(idx[s, i], a[0])
+            np.testing.assert_array_equal(sc[s, i], a[1])
+            np.testing.assert_array_equal(blk[s, i], a[2])
+            f = orc.flat_query(c.q[s, i], c.w[s, i], c.K[s], t, c.k)
+            np.testing.assert_array_equal(fidx[s, i], f[0])
+    sub_idx, _, _ = orc.hisa_batch(c.q, c.w, c.qpos, c.K, c.L, c.B, c.m, c.k, sel=[4])
+    np.testing.assert_array_equal(sub_idx[1, 1], idx[1, 1])
+    assert np.all(sub_idx[0] == -2)
