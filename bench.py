@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""HISA indexer benchmark on one MI355X.
+
+A step is one pass of the indexing hot path over one batch: fold the batch's
+newest key rows into the block pool (hisa_pool_append), then index every query
+(hisa_index: block scores -> top-m blocks -> token refinement -> top-k).  The
+flat DSA indexer (dsa_flat_index) runs on the same inputs as the in-run
+baseline.  Inputs are seeded synthetic workloads resident in HBM before the
+timed region.  Each step reads a different replica of the key cache (and its
+pool), so successive calls miss the 256 MB last-level cache as a real
+per-layer call would; whole steps are captured in HIP graphs and replayed, so
+the timing is of GPU work, not of Python launch overhead.
+
+Prints one JSON line.  Default workload: decode, 8 sequences x 32K keys.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer queries/s & µs/query at L=32K/64K/128K; speedup vs flat DSA; % roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
+DEFAULT_WORKLOAD = 1
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=None)
+    p.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD,
+                   help="0 tiny, 1 decode 32K, 2 decode 64K, 3 decode 128K, 4 prefill chunk")
+    p.add_argument("--rotate-mib", type=int, default=1024,
+                   help="cycle key-cache replicas until at least this much is touched per cycle")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-flat", action="store_true", help="skip the flat DSA baseline")
+    p.add_argument("--profile-steps", type=int, default=None,
+                   help="eager steps bracketed by per-kernel HIP events")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- algorithmic work models
+
+def kernel_models(case, blocks):
+    """Algorithmic bytes and flops per launch of each kernel for this workload.
+
+    Bytes count what the method must move: bf16 rows it scores (block means or
+    keys), the queries and weights, and the int32 indices it returns;
+    intermediates (candidate scores) are not counted.  Flops count the q.x
+    contractions: 2*H*d per scored row.
+    """
+    S, T, H, d, B, m, k = case.S, case.T, case.H, case.d, case.B, case.m, case.k
+    t = case.qpos.astype(np.int64).reshape(-1)
+    nb = t // B + 1
+    meff = np.minimum(m, nb)
+    # exact candidate counts from the kept blocks the GPU returned
+    cand = np.zeros_like(t)
+    flat_blocks = blocks.reshape(S * T, m)
+    for qi in range(S * T):
+        bl = flat_blocks[qi][flat_blocks[qi] >= 0].astype(np.int64)
+        cand[qi] = np.minimum(B, t[qi] + 1 - bl * B).sum()
+    qw = S * T * (H * d * 2 + H * 4)
+    row = d * 2
+    models = {
+        "score_blocks": dict(bytes=int(nb.sum() * row + qw), flops=int(2 * H * d * nb.sum())),
+        "score_refine": dict(bytes=int(cand.sum() * row + qw), flops=int(2 * H * d * cand.sum())),
+        "select_blocks": dict(bytes=int(nb.sum() * 4 + S * T * m * 4), flops=0),
+        "select_refine": dict(bytes=int(cand.sum() * 4 + S * T * k * 8), flops=0),
+        "score_flat": dict(bytes=int((t + 1).sum() * row + qw), flops=int(2 * H * d * (t + 1).sum())),
+        "select_flat": dict(bytes=int((t + 1).sum() * 4 + S * T * k * 8), flops=0),
+    }
+    per_query_hisa = (nb.sum() + cand.sum()) * row + qw + S * T * k * 4
+    return models, int(per_query_hisa), int(cand.sum())
+
+
+def traffic_from_profiles(kernel, workload_name):
+    """Measured HBM bytes per launch from a committed counter summary, if its
+    kernel source hash still matches (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload_name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    src = os.path.join(ROOT, "sparse_attention_token_amd", "csrc", kv.get("source", ""))
+    if not os.path.exists(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("source_sha256"):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the indexer has no "
+                                   "multi-GPU path here (sequences would shard across GPUs "
+                                   "without communication). Use --gpus 1."}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_token_amd import hisa, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hisa.lib()
+    case = synth.workload(args.workload)
+    S, T, H, d, L, B, m, k = case.S, case.T, case.H, case.d, case.L, case.B, case.m, case.k
+    prefill = T > 1
+    steps = args.steps if args.steps is not None else (20 if prefill else 400)
+    warmup = args.warmup if args.warmup is not None else (3 if prefill else 40)
+    log(f"workload {case.name}: S={S} T={T} L={L} H={H} d={d} B={B} m={m} k={k}")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    K0 = bf(case.K)
+    q = bf(case.q)
+    w = torch.from_numpy(case.w).to(dev)
+    nblk = -(-L // B)
+
+    # replicas of the key cache and its pool
+    touched_hisa = S * T * (min(m, nblk) * B + nblk) * d * 2 if not prefill else K0.numel() * 2
+    R = max(1, math.ceil(args.rotate_mib * 2**20 / touched_hisa))
+    R = min(R, 4 if prefill else 128, max(1, (16 * 2**30) // (K0.numel() * 2)))
+    Ks, pools = [], []
+    for r in range(R):
+        Kr = K0 if r == 0 else K0.clone()
+        pr = torch.zeros((S, nblk, d), dtype=torch.bfloat16, device=dev)
+        hisa.hisa_pool_append(Kr, pr, 0, L, B)
+        Ks.append(Kr)
+        pools.append(pr)
+    torch.cuda.synchronize()
+    log(f"{R} replicas of the key cache ({R * K0.numel() * 2 / 2**30:.2f} GiB)")
+
+    out_idx = torch.empty((S, T, k), dtype=torch.int32, device=dev)
+    out_score = torch.empty((S, T, k), dtype=torch.float32, device=dev)
+    ws = torch.empty(hisa.hisa_index_workspace(S, T, H, d, L, B, m, k), dtype=torch.uint8, device=dev)
+    f_idx = torch.empty((S, T, k), dtype=torch.int32, device=dev)
+    f_score = torch.empty((S, T, k), dtype=torch.float32, device=dev)
+    fws = torch.empty(hisa.dsa_flat_workspace(S, T, H, d, L, k), dtype=torch.uint8, device=dev)
+    L_new_rows = T                       # the step appends the batch's own newest key rows
+
+    def hisa_step(r):
+        hisa.hisa_pool_append(Ks[r], pools[r], L - L_new_rows, L, B)
+        hisa.hisa_index(q, w, Ks[r], L, pools[r], B, m, k, None, out_idx=out_idx,
+                        out_score=out_score, workspace=ws)
+
+    def flat_step(r):
+        hisa.dsa_flat_index(q, w, Ks[r], L, k, None, out_idx=f_idx, out_score=f_score, workspace=fws)
+
+    def time_graphs(step_fn, nsteps, nwarm, label):
+        for i in range(nwarm):
+            step_fn(i % R)
+        torch.cuda.synchronize()
+        full = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(full):
+            for r in range(R):
+                step_fn(r)
+        rem = nsteps % R
+        part = None
+        if rem:
+            part = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(part):
+                for r in range(rem):
+                    step_fn(r)
+        full.replay()                     # one untimed replay of the captured graph
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record()
+        for _ in range(nsteps // R):
+            full.replay()
+        if part is not None:
+            part.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        ms = e0.elapsed_time(e1) / nsteps
+        log(f"{label}: {nsteps} steps, {ms * 1e3:.2f} us/step (wall {wall * 1e3 / nsteps * 1e3:.2f} us/step)")
+        return ms
+
+    # ---- correctness snapshot for the reports (kept blocks, IoU vs flat, needles)
+    idx_h, _, blk_h = hisa.hisa_index(q, w, K0, L, pools[0], B, m, k, None, want_blocks=True)
+    torch.cuda.synchronize()
+    blocks = blk_h.cpu().numpy()
+    models, hisa_bytes, n_cand = kernel_models(case, blocks)
+
+    # ---- timed HISA steps
+    hisa_ms = time_graphs(hisa_step, steps, warmup, "hisa step (pool append + index)")
+
+    # ---- index-only timing, for the speedup of the indexer itself
+    def hisa_index_only(r):
+        hisa.hisa_index(q, w, Ks[r], L, pools[r], B, m, k, None, out_idx=out_idx,
+                        out_score=out_score, workspace=ws)
+    index_ms = time_graphs(hisa_index_only, steps, 2, "hisa_index only")
+
+    flat_ms = None
+    iou = None
+    needle = None
+    if not args.no_flat:
+        flat_steps = max(R, min(steps, 40)) if prefill else steps
+        flat_ms = time_graphs(flat_step, flat_steps, 2, "flat DSA")
+        fi, _ = hisa.dsa_flat_index(q, w, K0, L, k, None)
+        torch.cuda.synchronize()
+        a, b = idx_h.cpu().numpy().reshape(S * T, k), fi.cpu().numpy().reshape(S * T, k)
+        ious = []
+        for x, y in zip(a, b):
+            sx, sy = set(x[x >= 0].tolist()), set(y[y >= 0].tolist())
+            ious.append(len(sx & sy) / max(1, len(sx | sy)))
+        iou = float(np.mean(ious))
+        if case.needles is not None:
+            hit = sum(int(j in set(a[s].tolist())) for s in range(S) for j in case.needles[s])
+            fhit = sum(int(j in set(b[s].tolist())) for s in range(S) for j in case.needles[s])
+            needle = {"hisa": hit / case.needles.size, "flat": fhit / case.needles.size,
+                      "needles": int(case.needles.size)}
+
+    # ---- per-kernel durations: HIP events around each kernel, eager launches
+    # queued behind a long matrix product so the GPU never waits on the host
+    pro_steps = args.profile_steps if args.profile_steps is not None else (4 if prefill else min(2 * R, 64))
+    kernels = {}
+    big = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    for label, fn, n in (("hisa", hisa_step, pro_steps), ("flat", flat_step, 0 if args.no_flat else pro_steps)):
+        if n == 0:
+            continue
+        torch.cuda.synchronize()
+        hisa.profile_enable(8 * n)
+        for _ in range(6 if prefill else 12):
+            torch.mm(big, big)
+        for i in range(n):
+            fn(i % R)
+        res = hisa.profile_read()
+        hisa.profile_enable(0)
+        for name, (tot, cnt) in res.items():
+            kernels[name] = {"avg_us": tot * 1e3 / cnt, "launches_per_step": cnt / n}
+    del big
+
+    # ---- roofline of the dominant kernel
+    roofline = None
+    timed = {n: v for n, v in kernels.items() if n in models}
+    hisa_kern = {n: v for n, v in timed.items() if not n.endswith("_flat")}
+    if hisa_kern:
+        dom = max(hisa_kern, key=lambda n: hisa_kern[n]["avg_us"] * hisa_kern[n]["launches_per_step"])
+        mdl = models[dom]
+        sec = hisa_kern[dom]["avg_us"] * 1e-6
+        if prefill and mdl["flops"] > 0:
+            ach = mdl["flops"] / sec / 1e12
+            roofline = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                        "algorithmic_flops_per_launch": mdl["flops"]}
+        else:
+            ach = mdl["bytes"] / sec / 1e9
+            roofline = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                        "algorithmic_bytes_per_launch": mdl["bytes"]}
+        roofline["avg_launch_us"] = hisa_kern[dom]["avg_us"]
+        roofline["traffic"] = traffic_from_profiles(dom, case.name)
+
+    # ---- CPU oracle baseline (bounded sample of the same workload)
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+
+        n = S * T
+        sel = np.arange(n, dtype=np.int32) if n <= 16 else np.linspace(0, n - 1, 64).astype(np.int32)
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.hisa_batch(case.q, case.w, case.qpos, case.K, L, B, m, k, sel=sel)
+            times.append(time.perf_counter() - t0)
+        tc = float(np.median(times))
+        cpu = {"value": len(sel) / tc, "unit": "queries/s", "cores": oracle.num_threads(),
+               "kind": "oracle",
+               "sample": f"{len(sel)} of {n} queries of {case.name} through the fp64 C oracle "
+                         f"(HISA, median of 3 runs, {tc:.2f} s each)",
+               "us_per_query": tc / len(sel) * 1e6}
+
+    nq = S * T
+    value = nq / (hisa_ms * 1e-3)
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": hisa_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": case.name, "S": S, "T": T, "L": L, "H": H, "d": d, "B": B, "m": m,
+                   "k": k, "key_cache_replicas": R, "parallelism": "single GPU"},
+        "us_per_query": hisa_ms * 1e3 / nq,
+        "index_only": {"ms_per_call": index_ms, "queries_per_s": nq / (index_ms * 1e-3)},
+        "flat": None if flat_ms is None else {"ms_per_call": flat_ms, "queries_per_s": nq / (flat_ms * 1e-3),
+                                              "us_per_query": flat_ms * 1e3 / nq},
+        "speedup_vs_flat": None if flat_ms is None else flat_ms / hisa_ms,
+        "speedup_vs_flat_index_only": None if flat_ms is None else flat_ms / index_ms,
+        "iou_vs_flat": iou,
+        "needle_recall": needle,
+        "hisa_algorithmic_bytes_per_call": hisa_bytes,
+        "candidates_per_call": n_cand,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * libhisa -- HISA hierarchical indexer and flat DSA indexer for token-level
+ * sparse attention, hand-written HIP for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (pages about "HISA: Efficient Hierarchical Indexing for
+ * Fine-Grained Sparse Attention", arXiv 2603.28458):
+ *
+ *   DSA indexer score of key x for a query with H indexer heads
+ *       s(q, w, x) = sum_h w_h * ReLU(q_h . x)
+ *   (the pages describe the original indexer as a lightweight dot-product
+ *   scorer over the key cache; the per-head weighted ReLU form is the DSA one.)
+ *
+ *   dsa_flat_index   -- the flat indexer: score every key j <= t of the
+ *                       prefix, keep the k best ("the indexer must still scan
+ *                       the entire prefix for every query", arXiv abstract).
+ *   hisa_pool_append -- block representatives: mean pooling of contiguous
+ *                       blocks of B keys (gptget.net English summary,
+ *                       "Methodology"; Chinese summary, method details),
+ *                       maintained as keys are appended to the cache.
+ *   hisa_index       -- the two-stage replacement of the flat indexer:
+ *                       (1) score the block representatives with the original
+ *                       indexer and keep the top m blocks; (2) re-score every
+ *                       token of the kept blocks with the original indexer and
+ *                       keep the top k tokens (same pages and sections).
+ *
+ * Conventions shared by every entry point
+ *   - bf16 tensors are passed as uint16_t bit patterns; fp32 as float.
+ *   - All tensor pointers are DEVICE pointers (hipMalloc / torch CUDA tensors)
+ *     unless stated otherwise.  The caller owns every buffer.  The library
+ *     makes no device allocation and keeps no state between calls (the
+ *     optional profiler below is the one exception).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t, NULL = the
+ *     legacy default stream).  Outputs are valid once the stream has reached
+ *     the end of the call.  Calls on distinct buffers are thread-safe.
+ *   - Query positions are 0-based.  A query at position t sees keys j <= t.
+ *   - Ranking everywhere is (score descending, index ascending); -0 == +0.
+ *   - Every argument is checked on the host before anything is enqueued; on
+ *     error nothing is enqueued and a negative HISA_ERR_* code is returned.
+ *     Device-side values (query positions) outside [0, L) are not errors: such
+ *     a query selects nothing (its output row is all -1).
+ *   - Supported shapes: d in {64, 128}; 1 <= H <= 64; B in {16,32,64,128,256};
+ *     1 <= m <= 4096, m*B <= 2^20; 1 <= k <= 65536; 1 <= L < 2^31;
+ *     S*T <= 65535.  Other values return HISA_ERR_UNSUPPORTED.
+ *   - Strides are in elements and must be multiples of 8 (16-byte rows).
+ */
+#ifndef HISA_H
+#define HISA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HISA_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define HISA_API __attribute__((visibility("default")))
+#else
+#define HISA_API
+#endif
+
+enum hisa_status {
+    HISA_OK = 0,
+    HISA_ERR_ARG = -1,          /* null pointer, negative size, inconsistent stride or length */
+    HISA_ERR_UNSUPPORTED = -2,  /* shape outside the supported set above */
+    HISA_ERR_WORKSPACE = -3,    /* ws_bytes smaller than the *_workspace() size */
+    HISA_ERR_HIP = -4           /* a HIP runtime error while enqueuing the kernels */
+};
+
+/* HISA_ABI_VERSION of the loaded library. */
+HISA_API int hisa_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+HISA_API const char *hisa_status_string(int status);
+
+/*
+ * hisa_pool_append -- fold key rows [L_old, L_new) into their blocks' means.
+ * (Mean-pooled block representatives: gptget.net English summary,
+ * "Methodology"; maintenance as the cache grows: its "Limitations" and
+ * "Future Work" sections name the storage and upkeep of the representatives.)
+ *
+ *   K         bf16 [S][*][d]: row j of sequence s at K + s*k_seq_stride + j*d.
+ *             Rows [0, L_new) must already hold the keys.
+ *   pool_mean bf16 [S][*][d]: entry b of sequence s at
+ *             pool_mean + s*pool_seq_stride + b*d.  Block b covers rows
+ *             [b*B, min(b*B + B, L_new)).
+ *   Every block that holds at least one row of [L_old, L_new) is recomputed
+ *   from K:   mean_b = bf16_RNE( fp32_RNE( (sum_j K_j in fp64, increasing j) / cnt_b ) ).
+ *   The result is a pure function of K and L_new: re-running a call, or
+ *   splitting [L_old, L_new) into several calls, gives the same bits as one
+ *   bulk call with L_old = 0.  Cost: at most B rows read per touched block.
+ *   Blocks entirely before L_old are not touched.  L_old == L_new is a no-op.
+ *   Requires 0 <= L_old <= L_new; for S > 1, k_seq_stride >= L_new*d and
+ *   pool_seq_stride >= ceil(L_new/B)*d.
+ */
+HISA_API int hisa_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
+                              int64_t L_old, int64_t L_new,
+                              uint16_t *pool_mean, int64_t pool_seq_stride, void *stream);
+
+/* Bytes of device workspace hisa_index needs for these sizes (0 on bad sizes). */
+HISA_API size_t hisa_index_workspace(int S, int T, int H, int d, int64_t L, int B, int m, int k);
+
+/*
+ * hisa_index -- the two-stage HISA indexer (drop-in for the flat indexer).
+ *
+ *   q        bf16 [S][T][H][d]  indexer queries (row-major, contiguous)
+ *   w        fp32 [S][T][H]     per-head weights
+ *   qpos     int32 [S][T] or NULL; NULL means t = L - T + i for query i.
+ *   K        key cache, layout as in hisa_pool_append; rows [0, L) are read.
+ *   pool_mean block means as left by hisa_pool_append(..., L_new = L); every
+ *            block b < floor(t/B) must be current.  The query's own block
+ *            floor(t/B) is read from the pool only when the pool entry covers
+ *            exactly rows [floor(t/B)*B, t]; otherwise its mean over those rows
+ *            is recomputed from K with the same arithmetic.
+ *   Steps per query (t = its position, b_t = floor(t/B)):
+ *     1. sigma_b = s(q, w, mean_b) for b = 0..b_t                      (fp32)
+ *     2. M = top min(m, b_t+1) blocks by (sigma desc, b asc)
+ *     3. C = { j : floor(j/B) in M, j <= t }
+ *     4. s_j = s(q, w, K_j) for j in C                                 (fp32)
+ *     5. top min(k, |C|) of C by (s desc, j asc)
+ *   Arithmetic: bf16 x bf16 products accumulated in fp32 on the matrix cores,
+ *   fp32 ReLU, weighting and head sum.
+ *   out_idx   int32 [S][T][k]  selected token ids, ascending, then -1 padding.
+ *   out_score fp32 [S][T][k] or NULL: s_j of out_idx (-inf for padding).
+ *   out_blk   int32 [S][T][m] or NULL: M ascending, then -1 padding.
+ *   ws        device workspace of at least hisa_index_workspace(...) bytes
+ *             (any alignment: the size includes slack for internal
+ *             alignment); contents on entry are ignored and are clobbered.
+ */
+HISA_API int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos,
+                        const uint16_t *K, int64_t k_seq_stride, int64_t L,
+                        const uint16_t *pool_mean, int64_t pool_seq_stride,
+                        int S, int T, int H, int d, int B, int m, int k,
+                        int32_t *out_idx, float *out_score, int32_t *out_blk,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of device workspace dsa_flat_index needs for these sizes (0 on bad sizes). */
+HISA_API size_t dsa_flat_workspace(int S, int T, int H, int d, int64_t L, int k);
+
+/*
+ * dsa_flat_index -- the flat DSA indexer (the baseline HISA replaces): for each
+ * query, s_j = s(q, w, K_j) for every j <= t, keep the top min(k, t+1) by
+ * (s desc, j asc).  Same argument conventions and output layout as hisa_index.
+ * Uses the same scoring arithmetic as hisa_index, so for a given (query, key)
+ * both return the same fp32 bits.
+ */
+HISA_API int dsa_flat_index(const uint16_t *q, const float *w, const int32_t *qpos,
+                            const uint16_t *K, int64_t k_seq_stride, int64_t L,
+                            int S, int T, int H, int d, int k,
+                            int32_t *out_idx, float *out_score,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Optional kernel profiler (for benchmarks; not thread-safe).
+ * hisa_profile_enable(n > 0) starts recording a HIP event pair around every
+ * kernel the library enqueues, for up to n kernel launches; n == 0 stops and
+ * releases the events.  hisa_profile_read() synchronises the recorded events
+ * and returns, for kernel kind `kind`, the summed duration in milliseconds and
+ * the number of launches recorded since enable; it returns HISA_ERR_ARG for an
+ * unknown kind.  hisa_kernel_name(kind) names kind 0..hisa_kernel_kinds()-1.
+ */
+HISA_API int hisa_profile_enable(int max_launches);
+HISA_API int hisa_profile_read(int kind, double *total_ms, int *launches);
+HISA_API int hisa_kernel_kinds(void);
+HISA_API const char *hisa_kernel_name(int kind);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HISA_H */

@@ -1,0 +1,318 @@
+// C-ABI entry points of libhisa: argument checks, workspace layout, launches.
+// Every check runs on the host before anything is enqueued.
+
+#include <cstring>
+#include <vector>
+
+#include "../../include/hisa.h"
+#include "hisa_internal.h"
+
+namespace hisa {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool block_size_ok(int B) {
+    return B == 16 || B == 32 || B == 64 || B == 128 || B == 256;
+}
+
+int check_query_shape(int S, int T, int H, int d, int64_t L, int k) {
+    if (S < 1 || T < 1 || H < 1 || d < 1 || L < 1 || k < 1) return HISA_ERR_ARG;
+    if (d != 64 && d != 128) return HISA_ERR_UNSUPPORTED;
+    if (H > 64) return HISA_ERR_UNSUPPORTED;
+    if (L >= (int64_t{1} << 31)) return HISA_ERR_UNSUPPORTED;
+    if (k > 65536) return HISA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(S) * T > 65535) return HISA_ERR_UNSUPPORTED;
+    return HISA_OK;
+}
+
+int check_hisa_params(int B, int m) {
+    if (B < 1 || m < 1) return HISA_ERR_ARG;
+    if (!block_size_ok(B)) return HISA_ERR_UNSUPPORTED;
+    if (m > 4096 || static_cast<int64_t>(m) * B > (int64_t{1} << 20)) return HISA_ERR_UNSUPPORTED;
+    return HISA_OK;
+}
+
+int check_cache(const uint16_t *K, int64_t k_seq_stride, int S, int d, int64_t L) {
+    if (!K || !aligned16(K)) return HISA_ERR_ARG;
+    if (k_seq_stride < 0 || (k_seq_stride & 7) != 0) return HISA_ERR_ARG;
+    if (S > 1 && k_seq_stride < L * d) return HISA_ERR_ARG;
+    return HISA_OK;
+}
+
+int check_pool(const uint16_t *pool, int64_t pool_seq_stride, int S, int d, int64_t L, int B) {
+    if (!pool || !aligned16(pool)) return HISA_ERR_ARG;
+    if (pool_seq_stride < 0 || (pool_seq_stride & 7) != 0) return HISA_ERR_ARG;
+    if (S > 1 && pool_seq_stride < ceil_div(L, B) * d) return HISA_ERR_ARG;
+    return HISA_OK;
+}
+
+// ---------------------------------------------------------------- workspace layouts
+struct HisaLayout {
+    size_t own_rep, blk_keys, sel_blk, cand_keys, total;
+    int64_t blk_stride, cand_stride;
+};
+
+HisaLayout hisa_layout(int S, int T, int d, int64_t L, int B, int m) {
+    HisaLayout l{};
+    const int64_t nq = static_cast<int64_t>(S) * T;
+    l.blk_stride = static_cast<int64_t>(align_up(static_cast<size_t>(ceil_div(L, B)), 64));
+    l.cand_stride = static_cast<int64_t>(align_up(static_cast<size_t>(m) * B, 64));
+    size_t off = 0;
+    l.own_rep = off;   off = align_up(off + static_cast<size_t>(nq) * d * sizeof(uint16_t), kAlign);
+    l.blk_keys = off;  off = align_up(off + static_cast<size_t>(nq) * l.blk_stride * sizeof(uint32_t), kAlign);
+    l.sel_blk = off;   off = align_up(off + static_cast<size_t>(nq) * m * sizeof(int32_t), kAlign);
+    l.cand_keys = off; off = align_up(off + static_cast<size_t>(nq) * l.cand_stride * sizeof(uint32_t), kAlign);
+    l.total = off + kAlign;   // slack to align the caller's base pointer
+    return l;
+}
+
+struct FlatLayout {
+    size_t keys, total;
+    int64_t stride;
+};
+
+FlatLayout flat_layout(int S, int T, int64_t L) {
+    FlatLayout l{};
+    l.stride = static_cast<int64_t>(align_up(static_cast<size_t>(L), 64));
+    l.keys = 0;
+    l.total = align_up(static_cast<size_t>(S) * T * l.stride * sizeof(uint32_t), kAlign) + kAlign;
+    return l;
+}
+
+inline char *align_ptr(void *p) {
+    return reinterpret_cast<char *>(align_up(reinterpret_cast<uintptr_t>(p), kAlign));
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? HISA_OK : HISA_ERR_HIP; }
+
+// ---------------------------------------------------------------- profiler state
+struct Profiler {
+    bool on = false;
+    int cap = 0;
+    int used = 0;
+    bool open = false;
+    std::vector<hipEvent_t> ev;
+    std::vector<int> kind;
+};
+Profiler g_prof;
+
+void prof_release() {
+    for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+    g_prof.ev.clear();
+    g_prof.kind.clear();
+    g_prof.on = false;
+    g_prof.cap = g_prof.used = 0;
+    g_prof.open = false;
+}
+
+const char *const kKindNames[kKindCount] = {
+    "pool_append", "own_mean", "score_blocks", "select_blocks",
+    "score_refine", "select_refine", "score_flat", "select_flat",
+};
+
+}  // namespace
+
+void prof_begin(KernelKind kind, hipStream_t st) {
+    if (!g_prof.on || g_prof.used >= g_prof.cap) return;
+    (void)hipEventRecord(g_prof.ev[2 * g_prof.used], st);
+    g_prof.kind[g_prof.used] = kind;
+    g_prof.open = true;
+}
+
+void prof_end(KernelKind kind, hipStream_t st) {
+    if (!g_prof.on || !g_prof.open || g_prof.used >= g_prof.cap) return;
+    (void)kind;
+    (void)hipEventRecord(g_prof.ev[2 * g_prof.used + 1], st);
+    ++g_prof.used;
+    g_prof.open = false;
+}
+
+}  // namespace hisa
+
+using namespace hisa;
+
+extern "C" {
+
+int hisa_abi_version(void) { return HISA_ABI_VERSION; }
+
+const char *hisa_status_string(int status) {
+    switch (status) {
+        case HISA_OK: return "ok";
+        case HISA_ERR_ARG: return "invalid argument (null pointer, negative size, bad stride or length)";
+        case HISA_ERR_UNSUPPORTED: return "unsupported shape";
+        case HISA_ERR_WORKSPACE: return "workspace too small";
+        case HISA_ERR_HIP: return "HIP runtime error while enqueuing";
+        default: return "unknown status";
+    }
+}
+
+int hisa_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
+                     int64_t L_old, int64_t L_new, uint16_t *pool_mean, int64_t pool_seq_stride,
+                     void *stream) {
+    if (S < 1 || d < 1 || B < 1 || L_old < 0 || L_new < L_old) return HISA_ERR_ARG;
+    if (d != 64 && d != 128) return HISA_ERR_UNSUPPORTED;
+    if (!block_size_ok(B)) return HISA_ERR_UNSUPPORTED;
+    if (L_new >= (int64_t{1} << 31) || S > 65535) return HISA_ERR_UNSUPPORTED;
+    int st = check_cache(K, k_seq_stride, S, d, L_new);
+    if (st != HISA_OK) return st;
+    st = check_pool(pool_mean, pool_seq_stride, S, d, L_new, B);
+    if (st != HISA_OK) return st;
+    if (L_old == L_new) return HISA_OK;
+    const int64_t blk0 = L_old / B;
+    const int64_t blk1 = (L_new - 1) / B;
+    return hip_status(launch_pool_append(K, k_seq_stride, S, d, B, blk0, blk1 - blk0 + 1, L_new,
+                                         pool_mean, pool_seq_stride,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+size_t hisa_index_workspace(int S, int T, int H, int d, int64_t L, int B, int m, int k) {
+    if (check_query_shape(S, T, H, d, L, k) != HISA_OK) return 0;
+    if (check_hisa_params(B, m) != HISA_OK) return 0;
+    return hisa_layout(S, T, d, L, B, m).total;
+}
+
+int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
+               int64_t k_seq_stride, int64_t L, const uint16_t *pool_mean,
+               int64_t pool_seq_stride, int S, int T, int H, int d, int B, int m, int k,
+               int32_t *out_idx, float *out_score, int32_t *out_blk, void *ws, size_t ws_bytes,
+               void *stream) {
+    int st = check_query_shape(S, T, H, d, L, k);
+    if (st != HISA_OK) return st;
+    st = check_hisa_params(B, m);
+    if (st != HISA_OK) return st;
+    if (!q || !w || !out_idx || !aligned16(q)) return HISA_ERR_ARG;
+    if (!qpos && T > L) return HISA_ERR_ARG;
+    st = check_cache(K, k_seq_stride, S, d, L);
+    if (st != HISA_OK) return st;
+    st = check_pool(pool_mean, pool_seq_stride, S, d, L, B);
+    if (st != HISA_OK) return st;
+    const HisaLayout lay = hisa_layout(S, T, d, L, B, m);
+    if (!ws) return HISA_ERR_ARG;
+    if (ws_bytes < lay.total) return HISA_ERR_WORKSPACE;
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    char *base = align_ptr(ws);
+    uint16_t *own_rep = reinterpret_cast<uint16_t *>(base + lay.own_rep);
+    uint32_t *blk_keys = reinterpret_cast<uint32_t *>(base + lay.blk_keys);
+    int32_t *sel_blk = reinterpret_cast<int32_t *>(base + lay.sel_blk);
+    uint32_t *cand_keys = reinterpret_cast<uint32_t *>(base + lay.cand_keys);
+    const int nq = S * T;
+
+    // own-block means that the pool does not hold exactly (never the case for a
+    // single query at the newest position L-1)
+    if (qpos || T > 1) {
+        st = hip_status(launch_own_mean(K, k_seq_stride, qpos, L, S, T, d, B, own_rep, hs));
+        if (st != HISA_OK) return st;
+    }
+
+    ScoreArgs sa{};
+    sa.q = q; sa.w = w; sa.qpos = qpos;
+    sa.K = K; sa.k_seq_stride = k_seq_stride; sa.L = L;
+    sa.pool = pool_mean; sa.pool_seq_stride = pool_seq_stride;
+    sa.own_rep = own_rep; sa.sel_blk = sel_blk;
+    sa.S = S; sa.T = T; sa.H = H; sa.d = d; sa.B = B; sa.m = m;
+
+    // stage 1: block scores and the top-m blocks
+    sa.keys = blk_keys; sa.keys_stride = lay.blk_stride;
+    st = hip_status(launch_score(kScoreBlocks, sa, ceil_div(L, B), hs));
+    if (st != HISA_OK) return st;
+    SelectArgs se{};
+    se.keys = blk_keys; se.keys_stride = lay.blk_stride;
+    se.qpos = qpos; se.L = L; se.T = T; se.B = B; se.m = m;
+    se.kout = m; se.sel_blk = nullptr;
+    se.out_id = sel_blk; se.out_score = nullptr; se.out_id_copy = out_blk;
+    st = hip_status(launch_select(kScoreBlocks, se, nq, hs));
+    if (st != HISA_OK) return st;
+
+    // stage 2: token refinement inside the kept blocks and the final top-k
+    sa.keys = cand_keys; sa.keys_stride = lay.cand_stride;
+    st = hip_status(launch_score(kScoreRefine, sa, static_cast<int64_t>(m) * B, hs));
+    if (st != HISA_OK) return st;
+    se.keys = cand_keys; se.keys_stride = lay.cand_stride;
+    se.kout = k; se.sel_blk = sel_blk;
+    se.out_id = out_idx; se.out_score = out_score; se.out_id_copy = nullptr;
+    return hip_status(launch_select(kScoreRefine, se, nq, hs));
+}
+
+size_t dsa_flat_workspace(int S, int T, int H, int d, int64_t L, int k) {
+    if (check_query_shape(S, T, H, d, L, k) != HISA_OK) return 0;
+    return flat_layout(S, T, L).total;
+}
+
+int dsa_flat_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
+                   int64_t k_seq_stride, int64_t L, int S, int T, int H, int d, int k,
+                   int32_t *out_idx, float *out_score, void *ws, size_t ws_bytes, void *stream) {
+    int st = check_query_shape(S, T, H, d, L, k);
+    if (st != HISA_OK) return st;
+    if (!q || !w || !out_idx || !aligned16(q)) return HISA_ERR_ARG;
+    if (!qpos && T > L) return HISA_ERR_ARG;
+    st = check_cache(K, k_seq_stride, S, d, L);
+    if (st != HISA_OK) return st;
+    const FlatLayout lay = flat_layout(S, T, L);
+    if (!ws) return HISA_ERR_ARG;
+    if (ws_bytes < lay.total) return HISA_ERR_WORKSPACE;
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    uint32_t *keys = reinterpret_cast<uint32_t *>(align_ptr(ws) + lay.keys);
+    ScoreArgs sa{};
+    sa.q = q; sa.w = w; sa.qpos = qpos;
+    sa.K = K; sa.k_seq_stride = k_seq_stride; sa.L = L;
+    sa.keys = keys; sa.keys_stride = lay.stride;
+    sa.S = S; sa.T = T; sa.H = H; sa.d = d; sa.B = 1; sa.m = 1;
+    st = hip_status(launch_score(kScoreFlat, sa, L, hs));
+    if (st != HISA_OK) return st;
+    SelectArgs se{};
+    se.keys = keys; se.keys_stride = lay.stride;
+    se.qpos = qpos; se.L = L; se.T = T; se.B = 1; se.m = 1;
+    se.kout = k; se.out_id = out_idx; se.out_score = out_score;
+    return hip_status(launch_select(kScoreFlat, se, S * T, hs));
+}
+
+int hisa_profile_enable(int max_launches) {
+    if (max_launches < 0) return HISA_ERR_ARG;
+    prof_release();
+    if (max_launches == 0) return HISA_OK;
+    g_prof.ev.resize(2 * static_cast<size_t>(max_launches));
+    for (auto &e : g_prof.ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            e = nullptr;
+            prof_release();
+            return HISA_ERR_HIP;
+        }
+    }
+    g_prof.kind.assign(static_cast<size_t>(max_launches), -1);
+    g_prof.cap = max_launches;
+    g_prof.on = true;
+    return HISA_OK;
+}
+
+int hisa_profile_read(int kind, double *total_ms, int *launches) {
+    if (kind < 0 || kind >= kKindCount || !total_ms || !launches) return HISA_ERR_ARG;
+    *total_ms = 0.0;
+    *launches = 0;
+    if (!g_prof.on || g_prof.used == 0) return HISA_OK;
+    if (hipEventSynchronize(g_prof.ev[2 * g_prof.used - 1]) != hipSuccess) return HISA_ERR_HIP;
+    for (int i = 0; i < g_prof.used; ++i) {
+        if (g_prof.kind[i] != kind) continue;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess)
+            return HISA_ERR_HIP;
+        *total_ms += ms;
+        ++*launches;
+    }
+    return HISA_OK;
+}
+
+int hisa_kernel_kinds(void) { return kKindCount; }
+
+const char *hisa_kernel_name(int kind) {
+    return (kind >= 0 && kind < kKindCount) ? kKindNames[kind] : "unknown";
+}
+
+}  // extern "C"

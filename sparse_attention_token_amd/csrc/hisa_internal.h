@@ -1,0 +1,108 @@
+// Internal declarations of libhisa (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hisa {
+
+// ---------------------------------------------------------------- types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 <-> fp32
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// ---------------------------------------------------------------- sortable keys
+// Scores are ranked through an order-preserving map float -> uint32 (larger
+// score -> larger key; -0 is first folded onto +0 so the two tie).  Key 0 is
+// reserved for "no candidate": no finite score maps to it.
+__device__ __forceinline__ uint32_t score_to_key(float f) {
+    uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_score(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+constexpr uint32_t kNoCandidate = 0u;
+
+// Query position of flat query id qi = s*T + i (qpos == nullptr: t = L - T + i).
+// Returns -1 for positions outside [0, L).
+__device__ __forceinline__ int64_t query_pos(const int32_t *qpos, int qi, int i, int64_t L, int T) {
+    int64_t t = qpos ? static_cast<int64_t>(qpos[qi]) : (L - T + i);
+    return (t >= 0 && t < L) ? t : -1;
+}
+
+// ---------------------------------------------------------------- launchers
+enum ScoreMode { kScoreBlocks = 0, kScoreRefine = 1, kScoreFlat = 2 };
+
+struct ScoreArgs {
+    const uint16_t *q;        // [S*T][H][d]
+    const float *w;           // [S*T][H]
+    const int32_t *qpos;      // [S*T] or null
+    const uint16_t *K;        // key cache
+    int64_t k_seq_stride;
+    int64_t L;
+    const uint16_t *pool;     // block means
+    int64_t pool_seq_stride;
+    const uint16_t *own_rep;  // [S*T][d] own-block partial means (blocks mode)
+    const int32_t *sel_blk;   // [S*T][m] kept blocks, ascending (refine mode)
+    uint32_t *keys;           // out: [S*T][keys_stride]
+    int64_t keys_stride;
+    int S, T, H, d, B, m;
+};
+
+struct SelectArgs {
+    const uint32_t *keys;     // [S*T][keys_stride]
+    int64_t keys_stride;
+    const int32_t *qpos;
+    int64_t L;
+    int T, B, m;
+    int kout;                 // entries per output row
+    const int32_t *sel_blk;   // refine mode: [S*T][m]
+    int32_t *out_id;          // [S*T][kout]
+    float *out_score;         // [S*T][kout] or null
+    int32_t *out_id_copy;     // [S*T][kout] or null (second copy of out_id)
+};
+
+hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
+                              int64_t blk0, int64_t nblk, int64_t L_new, uint16_t *pool,
+                              int64_t pool_seq_stride, hipStream_t st);
+
+hipError_t launch_own_mean(const uint16_t *K, int64_t k_seq_stride, const int32_t *qpos,
+                           int64_t L, int S, int T, int d, int B, uint16_t *own_rep,
+                           hipStream_t st);
+
+hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int64_t max_pos, hipStream_t st);
+
+hipError_t launch_select(ScoreMode mode, const SelectArgs &a, int nq, hipStream_t st);
+
+// profiler hooks (hisa_abi.hip)
+enum KernelKind {
+    kKindPoolAppend = 0,
+    kKindOwnMean,
+    kKindScoreBlocks,
+    kKindSelectBlocks,
+    kKindScoreRefine,
+    kKindSelectRefine,
+    kKindScoreFlat,
+    kKindSelectFlat,
+    kKindCount
+};
+void prof_begin(KernelKind kind, hipStream_t st);
+void prof_end(KernelKind kind, hipStream_t st);
+
+}  // namespace hisa

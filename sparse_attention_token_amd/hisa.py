@@ -1,0 +1,229 @@
+"""Thin Python binding over libhisa (include/hisa.h).
+
+Argument marshalling only: tensors are checked for dtype, device, shape and
+layout, outputs and workspace are allocated with torch, and the raw device
+pointers plus torch's current HIP stream are handed to the C ABI.  Every step
+of the indexing path runs in the library's HIP kernels; there is no fallback.
+If the built library is missing this module raises on first use.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhisa.so")
+_lib = None
+
+HISA_OK = 0
+HISA_ERR_ARG = -1
+HISA_ERR_UNSUPPORTED = -2
+HISA_ERR_WORKSPACE = -3
+HISA_ERR_HIP = -4
+
+
+class HisaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().hisa_status_string(status).decode()
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libhisa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"libhisa.so not built ({_LIB_PATH}); run __graft_entry__.build()")
+    L = C.CDLL(_LIB_PATH)
+    vp, i32, i64, sz = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
+    L.hisa_abi_version.restype = i32
+    L.hisa_abi_version.argtypes = []
+    L.hisa_status_string.restype = C.c_char_p
+    L.hisa_status_string.argtypes = [i32]
+    L.hisa_pool_append.restype = i32
+    L.hisa_pool_append.argtypes = [vp, i64, i32, i32, i32, i64, i64, vp, i64, vp]
+    L.hisa_index_workspace.restype = sz
+    L.hisa_index_workspace.argtypes = [i32, i32, i32, i32, i64, i32, i32, i32]
+    L.hisa_index.restype = i32
+    L.hisa_index.argtypes = [vp, vp, vp, vp, i64, i64, vp, i64, i32, i32, i32, i32, i32, i32, i32,
+                             vp, vp, vp, vp, sz, vp]
+    L.dsa_flat_workspace.restype = sz
+    L.dsa_flat_workspace.argtypes = [i32, i32, i32, i32, i64, i32]
+    L.dsa_flat_index.restype = i32
+    L.dsa_flat_index.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp,
+                                 sz, vp]
+    L.hisa_profile_enable.restype = i32
+    L.hisa_profile_enable.argtypes = [i32]
+    L.hisa_profile_read.restype = i32
+    L.hisa_profile_read.argtypes = [i32, C.POINTER(C.c_double), C.POINTER(C.c_int)]
+    L.hisa_kernel_kinds.restype = i32
+    L.hisa_kernel_kinds.argtypes = []
+    L.hisa_kernel_name.restype = C.c_char_p
+    L.hisa_kernel_name.argtypes = [i32]
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------- helpers
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _bf16(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must be bfloat16 (or its 16-bit pattern), got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t
+
+
+def _rows(t: torch.Tensor, name: str, d: int):
+    """A [S, N, d] tensor with unit stride rows; returns the sequence stride in elements."""
+    if t.dim() != 3 or t.shape[2] != d or t.stride(2) != 1 or t.stride(1) != d:
+        raise ValueError(f"{name} must be [S, N, {d}] with contiguous rows")
+    return t.stride(0)
+
+
+def _check(fn: str, st: int):
+    if st != HISA_OK:
+        raise HisaError(fn, st)
+
+
+# ---------------------------------------------------------------- the ABI calls
+
+def hisa_abi_version() -> int:
+    return int(lib().hisa_abi_version())
+
+
+def hisa_pool_append(K: torch.Tensor, pool_mean: torch.Tensor, L_old: int, L_new: int, B: int):
+    """Fold key rows [L_old, L_new) of K [S, L_cap, d] into pool_mean [S, nblk_cap, d] (in place)."""
+    _bf16(K, "K")
+    _bf16(pool_mean, "pool_mean")
+    S, _, d = K.shape
+    kss = _rows(K, "K", d)
+    pss = _rows(pool_mean, "pool_mean", d)
+    if pool_mean.shape[0] != S:
+        raise ValueError("pool_mean and K disagree on S")
+    if pool_mean.shape[1] * B < L_new or K.shape[1] < L_new:
+        raise ValueError("K or pool_mean too short for L_new")
+    st = lib().hisa_pool_append(_ptr(K), kss, S, d, B, int(L_old), int(L_new), _ptr(pool_mean),
+                                pss, _stream(K.device))
+    _check("hisa_pool_append", st)
+    return pool_mean
+
+
+def hisa_index_workspace(S, T, H, d, L, B, m, k) -> int:
+    return int(lib().hisa_index_workspace(S, T, H, d, L, B, m, k))
+
+
+def dsa_flat_workspace(S, T, H, d, L, k) -> int:
+    return int(lib().dsa_flat_workspace(S, T, H, d, L, k))
+
+
+def _query_args(q, w, qpos, K, L):
+    _bf16(q, "q")
+    _bf16(K, "K")
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [S, T, H, d] tensor")
+    S, T, H, d = q.shape
+    if w.dtype != torch.float32 or tuple(w.shape) != (S, T, H) or not w.is_contiguous():
+        raise ValueError("w must be a contiguous float32 [S, T, H] tensor")
+    if K.shape[0] != S or K.shape[1] < L:
+        raise ValueError("K must be [S, >= L, d]")
+    kss = _rows(K, "K", d)
+    if qpos is not None:
+        if qpos.dtype != torch.int32 or tuple(qpos.shape) != (S, T) or not qpos.is_contiguous():
+            raise ValueError("qpos must be a contiguous int32 [S, T] tensor")
+    for t in (w, K) + (() if qpos is None else (qpos,)):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on the same device")
+    return S, T, H, d, kss
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if workspace.device != device or workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must be a device buffer of >= {nbytes} bytes")
+    return workspace
+
+
+def hisa_index(q, w, K, L: int, pool_mean, B: int, m: int, k: int, qpos=None, *,
+               want_scores: bool = True, want_blocks: bool = False, out_idx=None, out_score=None,
+               out_blk=None, workspace=None):
+    """HISA two-stage indexer.  Returns (idx [S,T,k] int32, score [S,T,k] fp32 | None,
+    blocks [S,T,m] int32 | None)."""
+    S, T, H, d, kss = _query_args(q, w, qpos, K, L)
+    _bf16(pool_mean, "pool_mean")
+    pss = _rows(pool_mean, "pool_mean", d)
+    if pool_mean.shape[0] != S or pool_mean.shape[1] * B < L:
+        raise ValueError("pool_mean must be [S, >= ceil(L/B), d]")
+    dev = q.device
+    if out_idx is None:
+        out_idx = torch.empty((S, T, k), dtype=torch.int32, device=dev)
+    if want_scores and out_score is None:
+        out_score = torch.empty((S, T, k), dtype=torch.float32, device=dev)
+    if want_blocks and out_blk is None:
+        out_blk = torch.empty((S, T, m), dtype=torch.int32, device=dev)
+    nbytes = hisa_index_workspace(S, T, H, d, L, B, m, k)
+    if nbytes == 0:
+        _check("hisa_index", lib().hisa_index(None, None, None, None, 0, L, None, 0, S, T, H, d, B,
+                                              m, k, None, None, None, None, 0, None))
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().hisa_index(_ptr(q), _ptr(w), _ptr(qpos), _ptr(K), kss, int(L), _ptr(pool_mean),
+                          pss, S, T, H, d, B, m, k, _ptr(out_idx), _ptr(out_score), _ptr(out_blk),
+                          _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    _check("hisa_index", st)
+    return out_idx, out_score, out_blk
+
+
+def dsa_flat_index(q, w, K, L: int, k: int, qpos=None, *, want_scores: bool = True,
+                   out_idx=None, out_score=None, workspace=None):
+    """Flat DSA indexer.  Returns (idx [S,T,k] int32, score [S,T,k] fp32 | None)."""
+    S, T, H, d, kss = _query_args(q, w, qpos, K, L)
+    dev = q.device
+    if out_idx is None:
+        out_idx = torch.empty((S, T, k), dtype=torch.int32, device=dev)
+    if want_scores and out_score is None:
+        out_score = torch.empty((S, T, k), dtype=torch.float32, device=dev)
+    nbytes = dsa_flat_workspace(S, T, H, d, L, k)
+    if nbytes == 0:
+        _check("dsa_flat_index", lib().dsa_flat_index(None, None, None, None, 0, L, S, T, H, d, k,
+                                                      None, None, None, 0, None))
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().dsa_flat_index(_ptr(q), _ptr(w), _ptr(qpos), _ptr(K), kss, int(L), S, T, H, d, k,
+                              _ptr(out_idx), _ptr(out_score), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(dev))
+    _check("dsa_flat_index", st)
+    return out_idx, out_score
+
+
+# ---------------------------------------------------------------- profiler
+
+def profile_enable(max_launches: int):
+    _check("hisa_profile_enable", lib().hisa_profile_enable(int(max_launches)))
+
+
+def profile_read() -> dict:
+    """{kernel name: (total_ms, launches)} for every kernel kind recorded since enable."""
+    L = lib()
+    out = {}
+    for kind in range(L.hisa_kernel_kinds()):
+        ms, n = C.c_double(0.0), C.c_int(0)
+        _check("hisa_profile_read", L.hisa_profile_read(kind, C.byref(ms), C.byref(n)))
+        if n.value:
+            out[L.hisa_kernel_name(kind).decode()] = (ms.value, n.value)
+    return out

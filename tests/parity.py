@@ -1,0 +1,149 @@
+"""Parity helpers: move seeded inputs to the GPU and compare GPU rows with the oracle.
+
+Comparison rule (floating point decides which indices are kept, and the GPU
+ranks fp32 scores while the oracle ranks fp64 ones):
+  tol(x) = ABS_TOL + REL_TOL * |x|
+  1. every returned GPU score is within tol of the oracle's score of that index;
+  2. kept blocks: the GPU set may differ from the oracle's only by blocks whose
+     oracle score is within tol of the oracle's m-th best block score;
+  3. kept tokens: the oracle re-runs the refinement on the GPU's kept blocks
+     (conditional oracle); the GPU set may differ from that result only by
+     tokens whose oracle score is within tol of its k-th best score.
+Everything else -- counts, padding, ordering (ascending ids) -- is exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+REL_TOL = 1e-3
+ABS_TOL = 1e-4
+
+
+def tol(x):
+    return ABS_TOL + REL_TOL * abs(x)
+
+
+def to_dev(case, device="cuda"):
+    import torch
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    return dict(
+        K=bf(case.K),
+        q=bf(case.q),
+        w=torch.from_numpy(np.ascontiguousarray(case.w)).to(device),
+        qpos=torch.from_numpy(np.ascontiguousarray(case.qpos)).to(device),
+    )
+
+
+def bits(t):
+    """bf16 torch tensor -> numpy uint16 bit patterns."""
+    import torch
+
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def build_pool(hisa, K, L, B, L_bulk=None, step=1):
+    """Pool means for rows [0, L): one bulk append of [0, L_bulk), then appends of `step` rows."""
+    import torch
+
+    S, _, d = K.shape
+    nblk = -(-L // B)
+    pool = torch.zeros((S, nblk, d), dtype=torch.bfloat16, device=K.device)
+    L_bulk = L if L_bulk is None else L_bulk
+    hisa.hisa_pool_append(K, pool, 0, L_bulk, B)
+    x = L_bulk
+    while x < L:
+        y = min(L, x + step)
+        hisa.hisa_pool_append(K, pool, x, y, B)
+        x = y
+    return pool
+
+
+def _kth(scores_desc, n):
+    return scores_desc[n - 1]
+
+
+def check_hisa_row(orc, case, s, i, g_idx, g_score, g_blk, report=None):
+    """Apply the comparison rule to one GPU output row of hisa_index."""
+    q, w, K = case.q[s, i], case.w[s, i], case.K[s]
+    t = int(case.qpos[s, i])
+    B, m, k = case.B, case.m, case.k
+    nb = t // B + 1
+    meff = min(m, nb)
+    o_idx, o_sc, o_blk, o_bsc, o_keff = orc.hisa_query(q, w, K, t, B, m, k)
+
+    # -- blocks
+    g_blk = np.asarray(g_blk)
+    assert np.all(g_blk[meff:] == -1), "block padding"
+    gb = g_blk[:meff]
+    assert np.all(gb >= 0) and np.all(np.diff(gb) > 0), "kept blocks must be ascending and distinct"
+    assert gb[-1] < nb
+    c_m = _kth(np.sort(o_bsc)[::-1], meff)
+    diff = set(gb.tolist()) ^ set(o_blk[:meff].tolist())
+    for b in diff:
+        assert abs(o_bsc[b] - c_m) <= tol(c_m), f"block {b} differs (score {o_bsc[b]} vs cutoff {c_m})"
+
+    # -- tokens, against the conditional oracle on the GPU's blocks
+    c_idx, c_sc, c_keff, nC = orc.refine_query(q, w, K, t, B, gb, k)
+    g_idx = np.asarray(g_idx)
+    assert np.all(g_idx[c_keff:] == -1), "token padding"
+    gt = g_idx[:c_keff]
+    assert np.all(gt >= 0) and np.all(np.diff(gt) > 0), "kept tokens must be ascending and distinct"
+    assert np.all(gt <= t), "causality"
+    assert np.all(np.isin(gt // B, gb)), "tokens must come from kept blocks"
+    c_k = float(orc.score(q, w, K[c_idx[c_keff - 1]])) if c_keff > 0 else 0.0
+    tdiff = set(gt.tolist()) ^ set(c_idx[:c_keff].tolist())
+    for j in tdiff:
+        sj = orc.score(q, w, K[j])
+        assert abs(sj - c_k) <= tol(c_k), f"token {j} differs (score {sj} vs cutoff {c_k})"
+
+    # -- scores of the returned tokens
+    if g_score is not None:
+        g_score = np.asarray(g_score)
+        assert np.all(np.isneginf(g_score[c_keff:]))
+        ref = dict(zip(c_idx[:c_keff].tolist(), c_sc[:c_keff].astype(np.float64).tolist()))
+        for pos, j in enumerate(gt.tolist()):
+            sj = ref[j] if j in ref else orc.score(q, w, K[j])
+            assert abs(g_score[pos] - sj) <= tol(sj), f"score of token {j}: {g_score[pos]} vs {sj}"
+    if report is not None:
+        report.setdefault("block_diffs", 0)
+        report.setdefault("token_diffs", 0)
+        report["block_diffs"] += len(diff)
+        report["token_diffs"] += len(tdiff)
+    return o_idx, o_keff
+
+
+def check_flat_row(orc, case, s, i, g_idx, g_score, report=None, pre=None):
+    """Comparison rule for one row of dsa_flat_index; pre = (idx, score, k_eff) from the oracle."""
+    q, w, K = case.q[s, i], case.w[s, i], case.K[s]
+    t = int(case.qpos[s, i])
+    k = case.k
+    o_idx, o_sc, o_keff = pre if pre is not None else orc.flat_query(q, w, K, t, k)
+    g_idx = np.asarray(g_idx)
+    assert np.all(g_idx[o_keff:] == -1)
+    gt = g_idx[:o_keff]
+    assert np.all(gt >= 0) and np.all(np.diff(gt) > 0) and np.all(gt <= t)
+    c_k = float(orc.score(q, w, K[o_idx[o_keff - 1]])) if o_keff > 0 else 0.0
+    tdiff = set(gt.tolist()) ^ set(o_idx[:o_keff].tolist())
+    for j in tdiff:
+        sj = orc.score(q, w, K[j])
+        assert abs(sj - c_k) <= tol(c_k), f"token {j} differs (score {sj} vs cutoff {c_k})"
+    if g_score is not None:
+        g_score = np.asarray(g_score)
+        ref = dict(zip(o_idx[:o_keff].tolist(), o_sc[:o_keff].astype(np.float64).tolist()))
+        for pos, j in enumerate(gt.tolist()):
+            sj = ref[j] if j in ref else orc.score(q, w, K[j])
+            assert abs(g_score[pos] - sj) <= tol(sj), f"score of token {j}: {g_score[pos]} vs {sj}"
+    if report is not None:
+        report.setdefault("flat_token_diffs", 0)
+        report["flat_token_diffs"] += len(tdiff)
+    return o_idx, o_keff
+
+
+def iou(a, b):
+    a = set(int(x) for x in a if x >= 0)
+    b = set(int(x) for x in b if x >= 0)
+    u = a | b
+    return len(a & b) / len(u) if u else 1.0

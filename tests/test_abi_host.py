@@ -1,0 +1,135 @@
+"""Host-only checks of the C ABI: the library loads without a GPU, exports every
+function include/hisa.h declares, sizes workspaces, and rejects bad arguments
+with the documented status codes before enqueuing anything.
+
+Calls that pass non-null placeholder pointers are only made where no GPU is
+visible: they must be rejected by the host-side checks, and on a machine
+without a device a check that wrongly passed would still fail in the runtime
+rather than touch memory.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hisa.h")
+
+OK, ARG, UNSUP, WS, HIP = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"HISA_API\s+[\w\s\*]*?\b((?:hisa|dsa)_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_attention_token_amd import hisa
+
+    return hisa.lib()
+
+
+def _gpu_visible():
+    try:
+        import torch
+
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("hisa_pool_append", "hisa_index", "dsa_flat_index", "hisa_index_workspace",
+              "dsa_flat_workspace", "hisa_status_string", "hisa_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in hisa.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.hisa_abi_version() == 1
+    for code in (OK, ARG, UNSUP, WS, HIP, 12345):
+        assert isinstance(lib.hisa_status_string(code), bytes)
+    assert lib.hisa_status_string(WS) != lib.hisa_status_string(ARG)
+    assert lib.hisa_kernel_kinds() >= 8
+    assert lib.hisa_kernel_name(0) == b"pool_append"
+
+
+def test_workspace_sizes(lib):
+    a = lib.hisa_index_workspace(8, 1, 64, 128, 32768, 128, 64, 2048)
+    # own-block means + block keys + kept blocks + candidate keys, plus slack
+    assert a >= 8 * 128 * 2 + 8 * 256 * 4 + 8 * 64 * 4 + 8 * 64 * 128 * 4
+    assert a < 2 * (8 * 128 * 2 + 8 * 256 * 4 + 8 * 64 * 4 + 8 * 64 * 128 * 4) + 4096
+    f = lib.dsa_flat_workspace(8, 1, 64, 128, 32768, 2048)
+    assert f >= 8 * 32768 * 4
+    big = lib.dsa_flat_workspace(1, 4096, 64, 128, 131072, 2048)
+    assert big >= 4096 * 131072 * 4          # 2 GiB of fp32 keys: size_t arithmetic
+    for bad in [(0, 1, 64, 128, 100, 64, 4, 8), (1, 1, 65, 128, 100, 64, 4, 8),
+                (1, 1, 64, 96, 100, 64, 4, 8), (1, 1, 64, 128, 100, 48, 4, 8),
+                (1, 1, 64, 128, 100, 64, 0, 8), (1, 1, 64, 128, 100, 64, 4, 0),
+                (1, 1, 64, 128, 1 << 31, 64, 4, 8), (1, 1, 64, 128, 100, 256, 8192, 8)]:
+        assert lib.hisa_index_workspace(*bad) == 0, bad
+
+
+def test_argument_checks_with_null_pointers(lib):
+    # null tensors: rejected before anything is enqueued
+    assert lib.hisa_index(None, None, None, None, 0, 100, None, 0, 1, 1, 4, 64, 64, 2, 8,
+                          None, None, None, None, 0, None) == ARG
+    assert lib.dsa_flat_index(None, None, None, None, 0, 100, 1, 1, 4, 64, 8, None, None, None,
+                              0, None) == ARG
+    assert lib.hisa_pool_append(None, 0, 1, 64, 64, 0, 10, None, 0, None) == ARG
+    # unsupported shapes are reported as such even before pointer checks
+    assert lib.hisa_index(None, None, None, None, 0, 100, None, 0, 1, 1, 4, 96, 64, 2, 8,
+                          None, None, None, None, 0, None) == UNSUP
+    assert lib.hisa_index(None, None, None, None, 0, 100, None, 0, 1, 1, 4, 64, 48, 2, 8,
+                          None, None, None, None, 0, None) == UNSUP
+    assert lib.hisa_pool_append(None, 0, 1, 64, 64, 10, 5, None, 0, None) == ARG   # L_new < L_old
+    assert lib.hisa_pool_append(None, 0, 1, 64, 64, -1, 5, None, 0, None) == ARG
+    # profiler argument checks
+    ms, n = C.c_double(), C.c_int()
+    assert lib.hisa_profile_read(-1, C.byref(ms), C.byref(n)) == ARG
+    assert lib.hisa_profile_read(99, C.byref(ms), C.byref(n)) == ARG
+    assert lib.hisa_profile_enable(-5) == ARG
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="placeholder-pointer checks run only where no GPU is visible")
+def test_argument_checks_with_placeholder_pointers(lib):
+    buf = (C.c_uint8 * 4096)()
+    base = (C.addressof(buf) + 255) // 256 * 256
+    p = C.c_void_p(base)
+    odd = C.c_void_p(base + 2)          # not 16-byte aligned
+    S, T, H, d, L, B, m, k = 2, 1, 4, 64, 1000, 64, 4, 16
+    need = lib.hisa_index_workspace(S, T, H, d, L, B, m, k)
+    kss, pss = L * d, 16 * d
+
+    def idx(**kw):
+        a = dict(q=p, w=p, qpos=None, K=p, kss=kss, L=L, pool=p, pss=pss, S=S, T=T, H=H, d=d, B=B,
+                 m=m, k=k, out=p, sc=None, blk=None, ws=p, wsb=need)
+        a.update(kw)
+        return lib.hisa_index(a["q"], a["w"], a["qpos"], a["K"], a["kss"], a["L"], a["pool"],
+                              a["pss"], a["S"], a["T"], a["H"], a["d"], a["B"], a["m"], a["k"],
+                              a["out"], a["sc"], a["blk"], a["ws"], a["wsb"], None)
+
+    assert idx(wsb=need - 1) == WS
+    assert idx(ws=None) == ARG
+    assert idx(kss=L * d - 8) == ARG        # sequences would overlap
+    assert idx(kss=L * d + 4) == ARG        # not a multiple of 8 elements
+    assert idx(pss=15 * d) == ARG           # pool rows of the sequences overlap
+    assert idx(q=odd) == ARG
+    assert idx(K=odd) == ARG
+    assert idx(T=L + 1) == ARG              # default positions would be negative
+    assert idx(H=0) == ARG
+    assert idx(S=300, T=300) == UNSUP       # S*T > 65535
+    assert idx(k=70000) == UNSUP
+    assert idx(m=4097) == UNSUP
+    fneed = lib.dsa_flat_workspace(S, T, H, d, L, k)
+    assert lib.dsa_flat_index(p, p, None, p, kss, L, S, T, H, d, k, p, None, p, fneed - 1, None) == WS
+    assert lib.hisa_pool_append(p, kss, S, d, B, 0, L, p, 15 * d, None) == ARG
+    assert lib.hisa_pool_append(p, kss, S, d, 24, 0, L, p, pss, None) == UNSUP
+    assert lib.hisa_pool_append(p, kss, S, d, B, 5, 5, p, pss, None) == OK   # empty range: no work

@@ -1,0 +1,229 @@
+"""GPU parity: libhisa (through its C ABI, via the ctypes binding) against the CPU oracle.
+
+Small cases span several 128-row tiles, ragged tails, every supported block
+size and both head dimensions; the five workloads run at full size in the same
+launch configuration as the benchmark, checked on sampled queries.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+from sparse_attention_token_amd import synth
+from parity import bits, build_pool, check_flat_row, check_hisa_row, iou, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def hisa():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from sparse_attention_token_amd import hisa as h
+
+    h.lib()
+    return h
+
+
+def _run(hisa, case, qpos_on_device=True, want_flat=True):
+    import torch
+
+    dev = to_dev(case)
+    pool = build_pool(hisa, dev["K"], case.L, case.B, case.L_bulk)
+    qpos = dev["qpos"] if qpos_on_device else None
+    idx, sc, blk = hisa.hisa_index(dev["q"], dev["w"], dev["K"], case.L, pool, case.B, case.m,
+                                   case.k, qpos, want_blocks=True)
+    out = dict(idx=idx.cpu().numpy(), sc=sc.cpu().numpy(), blk=blk.cpu().numpy(), pool=pool)
+    if want_flat:
+        fidx, fsc = hisa.dsa_flat_index(dev["q"], dev["w"], dev["K"], case.L, case.k, qpos)
+        out.update(fidx=fidx.cpu().numpy(), fsc=fsc.cpu().numpy())
+    torch.cuda.synchronize()
+    return out
+
+
+def test_abi_version(hisa):
+    assert hisa.hisa_abi_version() == 1
+
+
+# ---------------------------------------------------------------- block pool
+
+@pytest.mark.parametrize("B,d,L,S", [(16, 64, 100, 2), (64, 64, 1000, 1), (128, 128, 128 * 5 + 77, 2),
+                                     (256, 128, 3000, 1), (32, 128, 31, 1)])
+def test_pool_bit_exact(hisa, orc, B, d, L, S):
+    _say(f"pool B={B} d={d} L={L} S={S}")
+    c = synth.gaussian_case(S, L, 1, 1, d, B, 1, 1, seed=B + L)
+    c.K = synth.bf16_bits(synth.bf16_to_f32(c.K) * 3.0 + 0.25)
+    dev = to_dev(c)
+    ref = orc.pool(c.K, L, B)
+    bulk = build_pool(hisa, dev["K"], L, B)
+    np.testing.assert_array_equal(bits(bulk), ref)
+    # incremental maintenance: one row at a time after a partial bulk build, and
+    # uneven chunks, must give the same bits as the bulk build
+    inc = build_pool(hisa, dev["K"], L, B, L_bulk=L // 3, step=1)
+    np.testing.assert_array_equal(bits(inc), ref)
+    inc7 = build_pool(hisa, dev["K"], L, B, L_bulk=0, step=7)
+    np.testing.assert_array_equal(bits(inc7), ref)
+
+
+def test_pool_append_is_idempotent(hisa, orc):
+    c = synth.gaussian_case(1, 500, 1, 1, 128, 64, 1, 1, seed=3)
+    dev = to_dev(c)
+    pool = build_pool(hisa, dev["K"], 500, 64)
+    hisa.hisa_pool_append(dev["K"], pool, 450, 500, 64)
+    hisa.hisa_pool_append(dev["K"], pool, 499, 500, 64)
+    np.testing.assert_array_equal(bits(pool), orc.pool(c.K, 500, 64))
+
+
+# ---------------------------------------------------------------- small cases
+
+def _edge_qpos(L, B, T, rng):
+    cands = [0, B - 1, B, 2 * B - 1, L // 2, L - 2, L - 1, B + 1]
+    cands = [x for x in cands if 0 <= x < L]
+    extra = rng.integers(0, L, size=max(0, T - len(cands))).tolist()
+    return np.array((cands + extra)[:T], dtype=np.int32)
+
+
+SMALL = [
+    # name, S, L, T, H, d, B, m, k, kind
+    ("g_h8_d64_B64", 2, 1000, 8, 8, 64, 64, 3, 50, "gaussian"),
+    ("c_h64_d128_B128", 1, 3000, 8, 64, 128, 128, 4, 300, "clustered"),
+    ("c_h20_d128_B32", 2, 2000, 6, 20, 128, 32, 7, 100, "clustered"),
+    ("g_h4_d64_B16", 1, 700, 8, 4, 64, 16, 20, 64, "gaussian"),
+    ("c_h64_d64_B256", 1, 2600, 8, 64, 64, 256, 2, 300, "clustered"),
+    ("c_pad_k_gt_C", 1, 1500, 8, 32, 128, 128, 1, 600, "clustered"),
+    ("c_h1_d128_B64", 1, 900, 5, 1, 128, 64, 5, 40, "clustered"),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[s[0] for s in SMALL])
+def test_hisa_and_flat_small(hisa, orc, spec):
+    name, S, L, T, H, d, B, m, k, kind = spec
+    _say(f"small case {name}")
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    qpos = np.stack([_edge_qpos(L, B, T, rng) for _ in range(S)])
+    if kind == "gaussian":
+        c = synth.gaussian_case(S, L, T, H, d, B, m, k, seed=7, qpos=qpos)
+    else:
+        c = synth.clustered_case(S, L, T, H, d, B, m, k, seed=7, qpos=qpos, latent_block=B)
+    out = _run(hisa, c)
+    rep = {}
+    for s in range(S):
+        for i in range(T):
+            check_hisa_row(orc, c, s, i, out["idx"][s, i], out["sc"][s, i], out["blk"][s, i], rep)
+            check_flat_row(orc, c, s, i, out["fidx"][s, i], out["fsc"][s, i], rep)
+    _say(f"  {rep}")
+
+
+def test_tiny_workload(hisa, orc):
+    c = synth.workload(0)
+    out = _run(hisa, c, qpos_on_device=False)
+    rep = {}
+    for i in range(c.T):
+        check_hisa_row(orc, c, 0, i, out["idx"][0, i], out["sc"][0, i], out["blk"][0, i], rep)
+        check_flat_row(orc, c, 0, i, out["fidx"][0, i], out["fsc"][0, i], rep)
+    _say(f"tiny: {rep}")
+
+
+def test_prefill_chunk_small(hisa, orc):
+    # a chunk of consecutive queries ending at L (positions from the default rule)
+    c = synth.clustered_case(1, 4096, 300, 64, 128, 128, 6, 256, seed=21)
+    out = _run(hisa, c, qpos_on_device=False)
+    rep = {}
+    for i in range(0, 300, 7):
+        check_hisa_row(orc, c, 0, i, out["idx"][0, i], out["sc"][0, i], out["blk"][0, i], rep)
+        check_flat_row(orc, c, 0, i, out["fidx"][0, i], out["fsc"][0, i], rep)
+    _say(f"prefill small: {rep}")
+
+
+def test_keep_all_blocks_equals_flat_bitwise(hisa):
+    # with m >= number of blocks, HISA keeps every token <= t, and the shared
+    # scorer gives identical fp32 scores: the outputs must match bit for bit
+    c = synth.clustered_case(2, 1500, 5, 64, 128, 64, 64, 200, seed=4,
+                             qpos=[[0, 63, 64, 700, 1499], [5, 127, 128, 1000, 1400]], latent_block=64)
+    c.m = -(-c.L // c.B)
+    out = _run(hisa, c)
+    np.testing.assert_array_equal(out["idx"], out["fidx"])
+    np.testing.assert_array_equal(out["sc"].view(np.uint32), out["fsc"].view(np.uint32))
+
+
+def test_out_of_range_positions_select_nothing(hisa):
+    import torch
+
+    c = synth.gaussian_case(1, 300, 3, 4, 64, 64, 2, 10, seed=5, qpos=[[-1, 300, 299]])
+    out = _run(hisa, c)
+    assert np.all(out["idx"][0, :2] == -1) and np.all(out["blk"][0, :2] == -1)
+    assert np.all(np.isneginf(out["sc"][0, :2]))
+    assert np.all(out["fidx"][0, :2] == -1)
+    assert np.all(out["idx"][0, 2] >= 0)
+
+
+def test_deterministic(hisa):
+    c = synth.clustered_case(2, 5000, 3, 64, 128, 128, 8, 512, seed=8)
+    a = _run(hisa, c)
+    b = _run(hisa, c)
+    for key in ("idx", "sc", "blk", "fidx", "fsc"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_errors_raise(hisa):
+    import torch
+
+    c = synth.gaussian_case(1, 256, 1, 4, 64, 64, 2, 10, seed=1)
+    dev = to_dev(c)
+    pool = build_pool(hisa, dev["K"], 256, 64)
+    with pytest.raises(hisa.HisaError) as e:
+        hisa.hisa_index(dev["q"], dev["w"], dev["K"], 256, pool, 64, 5000, 10)   # m > 4096
+    assert e.value.status == hisa.HISA_ERR_UNSUPPORTED
+    small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(hisa.HisaError) as e:
+        hisa.hisa_index(dev["q"], dev["w"], dev["K"], 256, pool, 64, 2, 10, workspace=small_ws)
+    assert e.value.status == hisa.HISA_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+_FULL_SAMPLES = {1: None, 2: None, 3: None, 4: 12}
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4])
+def test_full_workload(hisa, orc, wid):
+    import torch
+
+    c = synth.workload(wid)
+    _say(f"workload {wid} {c.name}: S={c.S} T={c.T} L={c.L} B={c.B} m={c.m} k={c.k}")
+    out = _run(hisa, c, qpos_on_device=False)
+    if wid == 3:
+        # the pool grown by a bulk append and 77 single-row appends equals the
+        # oracle's means of every block (the last one holding 77 keys)
+        ref_tail = orc.pool(c.K[:, 131072 - 128 * 3:], c.L - (131072 - 128 * 3), c.B)
+        np.testing.assert_array_equal(bits(out["pool"])[:, -4:], ref_tail)
+    n = c.S * c.T
+    if _FULL_SAMPLES[wid] is None:
+        ids = list(range(n))
+    else:
+        ids = sorted(set(np.linspace(0, n - 1, _FULL_SAMPLES[wid]).astype(int).tolist()))
+    rep = {}
+    fsel = np.array(ids, dtype=np.int32)
+    f_idx, f_sc = orc.flat_batch(c.q, c.w, c.qpos, c.K, c.L, c.k, sel=fsel)
+    ious = []
+    for qid in ids:
+        s, i = divmod(qid, c.T)
+        check_hisa_row(orc, c, s, i, out["idx"][s, i], out["sc"][s, i], out["blk"][s, i], rep)
+        keff = int((f_idx[s, i] >= 0).sum())
+        check_flat_row(orc, c, s, i, out["fidx"][s, i], out["fsc"][s, i], rep,
+                       pre=(f_idx[s, i], f_sc[s, i], keff))
+        ious.append(iou(out["idx"][s, i], out["fidx"][s, i]))
+    msg = f"  checked {len(ids)} queries: {rep}; mean IoU(HISA, flat) = {np.mean(ious):.4f}"
+    if c.needles is not None:
+        hit = sum(int(j in set(out["idx"][s, 0].tolist())) for s in range(c.S) for j in c.needles[s])
+        fhit = sum(int(j in set(out["fidx"][s, 0].tolist())) for s in range(c.S) for j in c.needles[s])
+        msg += f"; needle recall HISA {hit}/{c.needles.size}, flat {fhit}/{c.needles.size}"
+    _say(msg)
