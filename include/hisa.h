@@ -39,7 +39,7 @@
  *     Device-side values (query positions) outside [0, L) are not errors: such
  *     a query selects nothing (its output row is all -1).
  *   - Supported shapes: d in {64, 128}; 1 <= H <= 64; B in {16,32,64,128,256};
- *     1 <= m <= 4096, m*B <= 2^20; 1 <= k <= 65536; 1 <= L < 2^31;
+ *     1 <= m <= 4096, m*B <= 2^20; 1 <= k <= 16384; 1 <= L < 2^31;
  *     S*T <= 65535.  Other values return HISA_ERR_UNSUPPORTED.
  *   - Strides are in elements and must be multiples of 8 (16-byte rows).
  */
@@ -109,11 +109,13 @@ HISA_API size_t hisa_index_workspace(int S, int T, int H, int d, int64_t L, int 
  *   w        fp32 [S][T][H]     per-head weights
  *   qpos     int32 [S][T] or NULL; NULL means t = L - T + i for query i.
  *   K        key cache, layout as in hisa_pool_append; rows [0, L) are read.
- *   pool_mean block means as left by hisa_pool_append(..., L_new = L); every
- *            block b < floor(t/B) must be current.  The query's own block
- *            floor(t/B) is read from the pool only when the pool entry covers
- *            exactly rows [floor(t/B)*B, t]; otherwise its mean over those rows
- *            is recomputed from K with the same arithmetic.
+ *   pool_mean block means as left by hisa_pool_append(); every block
+ *            b < floor(t/B) must be current.  The pool entry of the query's own
+ *            block floor(t/B) is never read: its representative, the mean of
+ *            rows [floor(t/B)*B, t], is recomputed from K with the same
+ *            arithmetic.  So the hisa_pool_append() of the newest rows may run
+ *            concurrently with (on another stream than) the hisa_index() that
+ *            queries them.
  *   Steps per query (t = its position, b_t = floor(t/B)):
  *     1. sigma_b = s(q, w, mean_b) for b = 0..b_t                      (fp32)
  *     2. M = top min(m, b_t+1) blocks by (sigma desc, b asc)

@@ -1,6 +1,7 @@
 // C-ABI entry points of libhisa: argument checks, workspace layout, launches.
 // Every check runs on the host before anything is enqueued.
 
+#include <algorithm>
 #include <cstring>
 #include <vector>
 
@@ -26,7 +27,7 @@ int check_query_shape(int S, int T, int H, int d, int64_t L, int k) {
     if (d != 64 && d != 128) return HISA_ERR_UNSUPPORTED;
     if (H > 64) return HISA_ERR_UNSUPPORTED;
     if (L >= (int64_t{1} << 31)) return HISA_ERR_UNSUPPORTED;
-    if (k > 65536) return HISA_ERR_UNSUPPORTED;
+    if (k > 16384) return HISA_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(S) * T > 65535) return HISA_ERR_UNSUPPORTED;
     return HISA_OK;
 }
@@ -53,21 +54,42 @@ int check_pool(const uint16_t *pool, int64_t pool_seq_stride, int S, int d, int6
 }
 
 // ---------------------------------------------------------------- workspace layouts
+struct StageBufs {
+    size_t keys[2], ids[2];
+    int64_t stride;
+};
+
+// carve the two ping-pong (key, id) buffers of the chunked selection
+size_t carve_stage(size_t off, int64_t nq, int64_t len, StageBufs &sb) {
+    sb.stride = static_cast<int64_t>(align_up(static_cast<size_t>(len), 64));
+    const size_t bytes = static_cast<size_t>(nq) * sb.stride * 4;
+    for (int i = 0; i < 2; ++i) {
+        sb.keys[i] = off; off = align_up(off + bytes, kAlign);
+        sb.ids[i] = off;  off = align_up(off + bytes, kAlign);
+    }
+    return off;
+}
+
 struct HisaLayout {
     size_t own_rep, blk_keys, sel_blk, cand_keys, total;
     int64_t blk_stride, cand_stride;
+    StageBufs stage;
 };
 
-HisaLayout hisa_layout(int S, int T, int d, int64_t L, int B, int m) {
+HisaLayout hisa_layout(int S, int T, int d, int64_t L, int B, int m, int k) {
     HisaLayout l{};
     const int64_t nq = static_cast<int64_t>(S) * T;
-    l.blk_stride = static_cast<int64_t>(align_up(static_cast<size_t>(ceil_div(L, B)), 64));
+    const int64_t nblk = ceil_div(L, B);
+    l.blk_stride = static_cast<int64_t>(align_up(static_cast<size_t>(nblk), 64));
     l.cand_stride = static_cast<int64_t>(align_up(static_cast<size_t>(m) * B, 64));
     size_t off = 0;
     l.own_rep = off;   off = align_up(off + static_cast<size_t>(nq) * d * sizeof(uint16_t), kAlign);
     l.blk_keys = off;  off = align_up(off + static_cast<size_t>(nq) * l.blk_stride * sizeof(uint32_t), kAlign);
     l.sel_blk = off;   off = align_up(off + static_cast<size_t>(nq) * m * sizeof(int32_t), kAlign);
     l.cand_keys = off; off = align_up(off + static_cast<size_t>(nq) * l.cand_stride * sizeof(uint32_t), kAlign);
+    const int64_t len = std::max(select_stage_len(nblk, m, B, false),
+                                 select_stage_len(static_cast<int64_t>(m) * B, k, B, true));
+    off = carve_stage(off, nq, len, l.stage);
     l.total = off + kAlign;   // slack to align the caller's base pointer
     return l;
 }
@@ -75,14 +97,26 @@ HisaLayout hisa_layout(int S, int T, int d, int64_t L, int B, int m) {
 struct FlatLayout {
     size_t keys, total;
     int64_t stride;
+    StageBufs stage;
 };
 
-FlatLayout flat_layout(int S, int T, int64_t L) {
+FlatLayout flat_layout(int S, int T, int64_t L, int k) {
     FlatLayout l{};
+    const int64_t nq = static_cast<int64_t>(S) * T;
     l.stride = static_cast<int64_t>(align_up(static_cast<size_t>(L), 64));
     l.keys = 0;
-    l.total = align_up(static_cast<size_t>(S) * T * l.stride * sizeof(uint32_t), kAlign) + kAlign;
+    size_t off = align_up(static_cast<size_t>(nq) * l.stride * sizeof(uint32_t), kAlign);
+    off = carve_stage(off, nq, select_stage_len(L, k, 1, false), l.stage);
+    l.total = off + kAlign;
     return l;
+}
+
+void set_stage(SelectArgs &se, char *base, const StageBufs &sb) {
+    for (int i = 0; i < 2; ++i) {
+        se.stage_keys[i] = reinterpret_cast<uint32_t *>(base + sb.keys[i]);
+        se.stage_ids[i] = reinterpret_cast<int32_t *>(base + sb.ids[i]);
+    }
+    se.stage_stride = sb.stride;
 }
 
 inline char *align_ptr(void *p) {
@@ -96,7 +130,6 @@ struct Profiler {
     bool on = false;
     int cap = 0;
     int used = 0;
-    bool open = false;
     std::vector<hipEvent_t> ev;
     std::vector<int> kind;
 };
@@ -108,7 +141,6 @@ void prof_release() {
     g_prof.kind.clear();
     g_prof.on = false;
     g_prof.cap = g_prof.used = 0;
-    g_prof.open = false;
 }
 
 const char *const kKindNames[kKindCount] = {
@@ -118,19 +150,13 @@ const char *const kKindNames[kKindCount] = {
 
 }  // namespace
 
-void prof_begin(KernelKind kind, hipStream_t st) {
-    if (!g_prof.on || g_prof.used >= g_prof.cap) return;
-    (void)hipEventRecord(g_prof.ev[2 * g_prof.used], st);
+bool prof_events(KernelKind kind, hipEvent_t *start, hipEvent_t *stop) {
+    if (!g_prof.on || g_prof.used >= g_prof.cap) return false;
+    *start = g_prof.ev[2 * g_prof.used];
+    *stop = g_prof.ev[2 * g_prof.used + 1];
     g_prof.kind[g_prof.used] = kind;
-    g_prof.open = true;
-}
-
-void prof_end(KernelKind kind, hipStream_t st) {
-    if (!g_prof.on || !g_prof.open || g_prof.used >= g_prof.cap) return;
-    (void)kind;
-    (void)hipEventRecord(g_prof.ev[2 * g_prof.used + 1], st);
     ++g_prof.used;
-    g_prof.open = false;
+    return true;
 }
 
 }  // namespace hisa
@@ -174,7 +200,7 @@ int hisa_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int 
 size_t hisa_index_workspace(int S, int T, int H, int d, int64_t L, int B, int m, int k) {
     if (check_query_shape(S, T, H, d, L, k) != HISA_OK) return 0;
     if (check_hisa_params(B, m) != HISA_OK) return 0;
-    return hisa_layout(S, T, d, L, B, m).total;
+    return hisa_layout(S, T, d, L, B, m, k).total;
 }
 
 int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
@@ -192,7 +218,7 @@ int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uin
     if (st != HISA_OK) return st;
     st = check_pool(pool_mean, pool_seq_stride, S, d, L, B);
     if (st != HISA_OK) return st;
-    const HisaLayout lay = hisa_layout(S, T, d, L, B, m);
+    const HisaLayout lay = hisa_layout(S, T, d, L, B, m, k);
     if (!ws) return HISA_ERR_ARG;
     if (ws_bytes < lay.total) return HISA_ERR_WORKSPACE;
 
@@ -204,12 +230,31 @@ int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uin
     uint32_t *cand_keys = reinterpret_cast<uint32_t *>(base + lay.cand_keys);
     const int nq = S * T;
 
-    // own-block means that the pool does not hold exactly (never the case for a
-    // single query at the newest position L-1)
-    if (qpos || T > 1) {
-        st = hip_status(launch_own_mean(K, k_seq_stride, qpos, L, S, T, d, B, own_rep, hs));
+    SelectArgs se{};
+    se.qpos = qpos; se.L = L; se.T = T; se.B = B; se.m = m;
+    set_stage(se, base, lay.stage);
+
+    if (fused_supported(d, L, B, m)) {
+        FusedArgs fa{};
+        fa.q = q; fa.w = w; fa.qpos = qpos;
+        fa.K = K; fa.k_seq_stride = k_seq_stride; fa.L = L;
+        fa.pool = pool_mean; fa.pool_seq_stride = pool_seq_stride;
+        fa.S = S; fa.T = T; fa.H = H; fa.d = d; fa.B = B; fa.m = m; fa.k = k;
+        fa.sel_blk = sel_blk; fa.out_blk = out_blk;
+        fa.cand_keys = cand_keys; fa.cand_stride = lay.cand_stride;
+        fa.out_idx = out_idx; fa.out_score = out_score;
+        st = hip_status(launch_fused_blocks_refine(fa, hs));
         if (st != HISA_OK) return st;
+        se.keys = cand_keys; se.keys_stride = lay.cand_stride;
+        se.kout = k; se.sel_blk = sel_blk;
+        se.out_id = out_idx; se.out_score = out_score; se.out_id_copy = nullptr;
+        return hip_status(launch_select(kScoreRefine, se, nq, static_cast<int64_t>(m) * B, hs));
     }
+
+    // general path (any supported shape): own-block means, then score and
+    // select twice
+    st = hip_status(launch_own_mean(K, k_seq_stride, qpos, L, S, T, d, B, own_rep, hs));
+    if (st != HISA_OK) return st;
 
     ScoreArgs sa{};
     sa.q = q; sa.w = w; sa.qpos = qpos;
@@ -222,12 +267,10 @@ int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uin
     sa.keys = blk_keys; sa.keys_stride = lay.blk_stride;
     st = hip_status(launch_score(kScoreBlocks, sa, ceil_div(L, B), hs));
     if (st != HISA_OK) return st;
-    SelectArgs se{};
     se.keys = blk_keys; se.keys_stride = lay.blk_stride;
-    se.qpos = qpos; se.L = L; se.T = T; se.B = B; se.m = m;
     se.kout = m; se.sel_blk = nullptr;
     se.out_id = sel_blk; se.out_score = nullptr; se.out_id_copy = out_blk;
-    st = hip_status(launch_select(kScoreBlocks, se, nq, hs));
+    st = hip_status(launch_select(kScoreBlocks, se, nq, ceil_div(L, B), hs));
     if (st != HISA_OK) return st;
 
     // stage 2: token refinement inside the kept blocks and the final top-k
@@ -237,12 +280,12 @@ int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uin
     se.keys = cand_keys; se.keys_stride = lay.cand_stride;
     se.kout = k; se.sel_blk = sel_blk;
     se.out_id = out_idx; se.out_score = out_score; se.out_id_copy = nullptr;
-    return hip_status(launch_select(kScoreRefine, se, nq, hs));
+    return hip_status(launch_select(kScoreRefine, se, nq, static_cast<int64_t>(m) * B, hs));
 }
 
 size_t dsa_flat_workspace(int S, int T, int H, int d, int64_t L, int k) {
     if (check_query_shape(S, T, H, d, L, k) != HISA_OK) return 0;
-    return flat_layout(S, T, L).total;
+    return flat_layout(S, T, L, k).total;
 }
 
 int dsa_flat_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
@@ -254,7 +297,7 @@ int dsa_flat_index(const uint16_t *q, const float *w, const int32_t *qpos, const
     if (!qpos && T > L) return HISA_ERR_ARG;
     st = check_cache(K, k_seq_stride, S, d, L);
     if (st != HISA_OK) return st;
-    const FlatLayout lay = flat_layout(S, T, L);
+    const FlatLayout lay = flat_layout(S, T, L, k);
     if (!ws) return HISA_ERR_ARG;
     if (ws_bytes < lay.total) return HISA_ERR_WORKSPACE;
 
@@ -268,10 +311,11 @@ int dsa_flat_index(const uint16_t *q, const float *w, const int32_t *qpos, const
     st = hip_status(launch_score(kScoreFlat, sa, L, hs));
     if (st != HISA_OK) return st;
     SelectArgs se{};
+    set_stage(se, align_ptr(ws), lay.stage);
     se.keys = keys; se.keys_stride = lay.stride;
     se.qpos = qpos; se.L = L; se.T = T; se.B = 1; se.m = 1;
     se.kout = k; se.out_id = out_idx; se.out_score = out_score;
-    return hip_status(launch_select(kScoreFlat, se, S * T, hs));
+    return hip_status(launch_select(kScoreFlat, se, S * T, L, hs));
 }
 
 int hisa_profile_enable(int max_launches) {

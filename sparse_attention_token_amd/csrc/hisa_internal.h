@@ -1,6 +1,7 @@
 // Internal declarations of libhisa (not part of the C ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -76,7 +77,42 @@ struct SelectArgs {
     int32_t *out_id;          // [S*T][kout]
     float *out_score;         // [S*T][kout] or null
     int32_t *out_id_copy;     // [S*T][kout] or null (second copy of out_id)
+    // chunked selection of long rows: two ping-pong (key, id) buffers of
+    // [S*T][stage_stride] (see select_stage_len)
+    uint32_t *stage_keys[2];
+    int32_t *stage_ids[2];
+    int64_t stage_stride;
 };
+
+constexpr int kSelMaxM = 4096;          // kept blocks the refine-mode select stages in LDS
+
+// Length of one query's row in the chunked-selection buffers (0: not needed).
+int64_t select_stage_len(int64_t max_n, int kout, int B, bool refine);
+
+// ---------------------------------------------------------------- fused HISA path
+constexpr int kFusedOwnElems = 16384;   // B*d of the staged own block
+constexpr int kFusedMaxBlocks = 8192;   // ceil(L/B)
+
+struct FusedArgs {
+    const uint16_t *q;        // [S*T][H][d]
+    const float *w;           // [S*T][H]
+    const int32_t *qpos;      // [S*T] or null
+    const uint16_t *K;
+    int64_t k_seq_stride;
+    int64_t L;
+    const uint16_t *pool;
+    int64_t pool_seq_stride;
+    int S, T, H, d, B, m, k;
+    int32_t *sel_blk;         // ws [S*T][m]: kept blocks, ascending, -1 padded
+    int32_t *out_blk;         // [S*T][m] or null
+    uint32_t *cand_keys;      // ws [S*T][cand_stride]
+    int64_t cand_stride;
+    int32_t *out_idx;         // [S*T][k]
+    float *out_score;         // [S*T][k] or null
+};
+
+bool fused_supported(int d, int64_t L, int B, int m);
+hipError_t launch_fused_blocks_refine(const FusedArgs &a, hipStream_t st);
 
 hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
                               int64_t blk0, int64_t nblk, int64_t L_new, uint16_t *pool,
@@ -88,7 +124,8 @@ hipError_t launch_own_mean(const uint16_t *K, int64_t k_seq_stride, const int32_
 
 hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int64_t max_pos, hipStream_t st);
 
-hipError_t launch_select(ScoreMode mode, const SelectArgs &a, int nq, hipStream_t st);
+// max_n: an upper bound on the candidate count of every query (sizes the per-thread chunk)
+hipError_t launch_select(ScoreMode mode, const SelectArgs &a, int nq, int64_t max_n, hipStream_t st);
 
 // profiler hooks (hisa_abi.hip)
 enum KernelKind {
@@ -102,7 +139,23 @@ enum KernelKind {
     kKindSelectFlat,
     kKindCount
 };
-void prof_begin(KernelKind kind, hipStream_t st);
-void prof_end(KernelKind kind, hipStream_t st);
+
+// When the optional profiler is recording, hands out the event pair for the
+// next launch of `kind` and returns true.
+bool prof_events(KernelKind kind, hipEvent_t *start, hipEvent_t *stop);
+
+// Launch `kernel` on `st`.  While profiling, the start/stop events ride on the
+// dispatch itself (hipExtLaunchKernelGGL), so they time the kernel's execution
+// rather than the gap between separately enqueued markers.
+template <typename F, typename... Args>
+hipError_t launch(KernelKind kind, F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
+                  Args... args) {
+    hipEvent_t e0, e1;
+    if (prof_events(kind, &e0, &e1))
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, e0, e1, 0, args...);
+    else
+        kernel<<<grid, block, shmem, st>>>(args...);
+    return hipGetLastError();
+}
 
 }  // namespace hisa

@@ -6,54 +6,93 @@
 // bf16 so that the block stage feeds the same bf16 matrix-core scorer as the
 // token stage; it is rounded once from the exact-order fp64 sum:
 //     mean = bf16_RNE( fp32_RNE( (sum over rows, increasing row, in fp64) / count ) ).
-// One thread owns one column of one block: the 64 lanes of a wave read 64
-// consecutive bf16 of a key row (128 coalesced bytes) per step.
+//
+// A workgroup owns one run of rows (a block, or the head of a query's own
+// block): all 256 threads first copy the rows into LDS with 16-byte loads
+// (every load in flight at once), then one thread per column adds its column
+// from LDS in row order.  The sequential fp64 order is what makes the result
+// independent of how the rows were appended.
 
 #include "hisa_internal.h"
 
 namespace hisa {
 namespace {
 
-__device__ __forceinline__ uint16_t column_mean(const uint16_t *__restrict__ col, int64_t rows,
-                                                int d) {
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPoolThreads = 256;
+constexpr int kMaxRows = 256;                       // largest supported B
+constexpr int kMaxD = 128;
+
+// Copy rows [0, rows) of `src` (row stride d elements) into LDS and return the
+// bf16 mean of column threadIdx.x (threads >= d return 0 and write nothing).
+__device__ __forceinline__ uint16_t staged_column_mean(const uint16_t *__restrict__ src,
+                                                       int rows, int d, uint16_t *lds) {
+    constexpr int kMaxChunks = kMaxRows * kMaxD / 8 / kPoolThreads;   // 16-byte chunks per thread
+    const int chunks_per_row = d / 8;
+    const int total = rows * chunks_per_row;
+    u32x4 v[kMaxChunks];
+#pragma unroll
+    for (int it = 0; it < kMaxChunks; ++it) {          // all loads in flight before any store
+        const int c = threadIdx.x + it * kPoolThreads;
+        if (c < total) {
+            const int r = c / chunks_per_row;
+            v[it] = *reinterpret_cast<const u32x4 *>(src + static_cast<int64_t>(r) * d + 8 * (c - r * chunks_per_row));
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < kMaxChunks; ++it) {
+        const int c = threadIdx.x + it * kPoolThreads;
+        if (c < total) {
+            const int r = c / chunks_per_row;
+            *reinterpret_cast<u32x4 *>(lds + r * d + 8 * (c - r * chunks_per_row)) = v[it];
+        }
+    }
+    __syncthreads();
+    const int col = threadIdx.x;
+    if (col >= d) return 0;
     double sum = 0.0;
-    for (int64_t j = 0; j < rows; ++j)
-        sum += static_cast<double>(bf16_to_f32(col[j * d]));
+    int r = 0;
+    for (; r + 8 <= rows; r += 8) {                    // 8 LDS reads in flight, adds in row order
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = bf16_to_f32(lds[(r + j) * d + col]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum += static_cast<double>(x[j]);
+    }
+    for (; r < rows; ++r) sum += static_cast<double>(bf16_to_f32(lds[r * d + col]));
     const float mean = static_cast<float>(sum / static_cast<double>(rows));
     return f32_to_bf16_rne(mean);
 }
 
-// grid: (nblk, S), block: d threads.  Recomputes blocks [blk0, blk0 + nblk).
-__global__ void pool_append_kernel(const uint16_t *__restrict__ K, int64_t k_seq_stride, int d,
-                                   int B, int64_t blk0, int64_t L_new,
-                                   uint16_t *__restrict__ pool, int64_t pool_seq_stride) {
+// grid: (nblk, S).  Recomputes blocks [blk0, blk0 + nblk) over rows < L_new.
+__global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(
+        const uint16_t *__restrict__ K, int64_t k_seq_stride, int d, int B, int64_t blk0,
+        int64_t L_new, uint16_t *__restrict__ pool, int64_t pool_seq_stride) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[kMaxRows * kMaxD];
     const int s = blockIdx.y;
     const int64_t b = blk0 + blockIdx.x;
-    const int c = threadIdx.x;
     const int64_t r0 = b * B;
-    const int64_t r1 = (r0 + B < L_new) ? r0 + B : L_new;
-    const uint16_t *col = K + s * k_seq_stride + r0 * d + c;
-    pool[s * pool_seq_stride + b * d + c] = column_mean(col, r1 - r0, d);
+    const int rows = static_cast<int>(((r0 + B < L_new) ? r0 + B : L_new) - r0);
+    const uint16_t m = staged_column_mean(K + s * k_seq_stride + r0 * d, rows, d, lds);
+    if (static_cast<int>(threadIdx.x) < d) pool[s * pool_seq_stride + b * d + threadIdx.x] = m;
 }
 
-// grid: (S*T), block: d threads.  For a query at t whose own block
-// b_t = floor(t/B) is not exactly covered by the pool entry (the entry covers
-// rows [b_t*B, min(b_t*B + B, L)), the query needs [b_t*B, t]), writes the
-// mean of rows [b_t*B, t] to own_rep[qi].
-__global__ void own_mean_kernel(const uint16_t *__restrict__ K, int64_t k_seq_stride,
-                                const int32_t *__restrict__ qpos, int64_t L, int T, int d, int B,
-                                uint16_t *__restrict__ own_rep) {
+// grid: (S*T).  Writes the representative of the query's own block
+// b_t = floor(t/B) -- the mean of rows [b_t*B, t] -- to own_rep[qi].
+__global__ __launch_bounds__(kPoolThreads) void own_mean_kernel(
+        const uint16_t *__restrict__ K, int64_t k_seq_stride, const int32_t *__restrict__ qpos,
+        int64_t L, int T, int d, int B, uint16_t *__restrict__ own_rep) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[kMaxRows * kMaxD];
     const int qi = blockIdx.x;
     const int s = qi / T;
     const int i = qi - s * T;
     const int64_t t = query_pos(qpos, qi, i, L, T);
     if (t < 0) return;
     const int64_t r0 = (t / B) * B;
-    const int64_t covered = (r0 + B < L) ? r0 + B : L;
-    if (covered == t + 1) return;
-    const int c = threadIdx.x;
-    const uint16_t *col = K + s * k_seq_stride + r0 * d + c;
-    own_rep[static_cast<int64_t>(qi) * d + c] = column_mean(col, t + 1 - r0, d);
+    const uint16_t m = staged_column_mean(K + s * k_seq_stride + r0 * d,
+                                          static_cast<int>(t + 1 - r0), d, lds);
+    if (static_cast<int>(threadIdx.x) < d) own_rep[static_cast<int64_t>(qi) * d + threadIdx.x] = m;
 }
 
 }  // namespace
@@ -61,21 +100,16 @@ __global__ void own_mean_kernel(const uint16_t *__restrict__ K, int64_t k_seq_st
 hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
                               int64_t blk0, int64_t nblk, int64_t L_new, uint16_t *pool,
                               int64_t pool_seq_stride, hipStream_t st) {
-    prof_begin(kKindPoolAppend, st);
-    hipLaunchKernelGGL(pool_append_kernel, dim3(static_cast<uint32_t>(nblk), S), dim3(d), 0, st,
-                       K, k_seq_stride, d, B, blk0, L_new, pool, pool_seq_stride);
-    prof_end(kKindPoolAppend, st);
-    return hipGetLastError();
+    return launch(kKindPoolAppend, pool_append_kernel, dim3(static_cast<uint32_t>(nblk), S),
+                  dim3(kPoolThreads), 0, st, K, k_seq_stride, d, B, blk0, L_new, pool,
+                  pool_seq_stride);
 }
 
 hipError_t launch_own_mean(const uint16_t *K, int64_t k_seq_stride, const int32_t *qpos,
                            int64_t L, int S, int T, int d, int B, uint16_t *own_rep,
                            hipStream_t st) {
-    prof_begin(kKindOwnMean, st);
-    hipLaunchKernelGGL(own_mean_kernel, dim3(S * T), dim3(d), 0, st, K, k_seq_stride, qpos, L, T,
-                       d, B, own_rep);
-    prof_end(kKindOwnMean, st);
-    return hipGetLastError();
+    return launch(kKindOwnMean, own_mean_kernel, dim3(S * T), dim3(kPoolThreads), 0, st, K,
+                  k_seq_stride, qpos, L, T, d, B, own_rep);
 }
 
 }  // namespace hisa

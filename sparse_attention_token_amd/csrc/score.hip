@@ -23,33 +23,23 @@
 //
 // Work split: one workgroup = 4 waves = one 128-row tile of one query; each
 // wave owns two N-tiles (32 rows).  Every lane loads its own 16-byte slices of
-// q and of its rows straight into registers (no LDS round trip); all loads of
-// a wave are issued before its first MFMA.
+// q and of its rows straight into registers; the row loads are issued first.
+// The 16-row scoring step is score_rows() of scorer.h, shared with the fused
+// HISA kernels.
 //
 // Rows by mode (tile position p, query position t, own block b_t = t / B):
-//   blocks: p = block id <= b_t; row = pool mean p, or for p == b_t the
-//           recomputed own-block mean when the pool entry does not end at t
+//   blocks: p = block id <= b_t; row = pool mean p for p < b_t, and the
+//           query's own-block mean (rows b_t*B .. t, recomputed from K) for p = b_t
 //   refine: p = slot*B + r over the kept blocks (ascending); row = key
 //           sel[slot]*B + r if that token is <= t, else no candidate
 //   flat:   p = token id <= t; row = key p
 // Output is an order-preserving uint32 key per position (0 = no candidate).
 
 #include "hisa_internal.h"
+#include "scorer.h"
 
 namespace hisa {
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-__device__ __forceinline__ bf16x8 zero_bf16x8() {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    return __builtin_bit_cast(bf16x8, z);
-}
 
 constexpr int kTileRows = 128;
 constexpr int kWaves = 4;
@@ -82,7 +72,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     const int n = lane & 15;
     const int g = lane >> 4;
 
-    // ---- rows of this lane (issue the row loads first: they come from HBM)
+    // ---- rows of this lane (issued first: they come from HBM)
     bf16x8 kb[kNT][KS];
     bool valid[kNT];
     int64_t pos[kNT];
@@ -93,11 +83,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         const uint16_t *row = nullptr;
         if (p < npos) {
             if (MODE == kScoreBlocks) {
-                const int64_t cov = (bt * a.B + a.B < a.L) ? bt * a.B + a.B : a.L;
-                if (p == bt && cov != t + 1)
-                    row = a.own_rep + static_cast<int64_t>(qi) * D;
-                else
-                    row = a.pool + s * a.pool_seq_stride + p * D;
+                row = p == bt ? a.own_rep + static_cast<int64_t>(qi) * D
+                              : a.pool + s * a.pool_seq_stride + p * D;
             } else if (MODE == kScoreRefine) {
                 const int64_t slot = p / a.B;
                 const int64_t r = p - slot * a.B;
@@ -108,66 +95,32 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
             }
         }
         valid[nt] = row != nullptr;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            kb[nt][ks] = row ? load_bf16x8(row + 32 * ks + 8 * g) : zero_bf16x8();
+        load_row_frag<KS>(kb[nt], row, lane);
     }
 
-    // ---- query fragments and head weights
-    bf16x8 qa[MT][KS];
-    const uint16_t *qb = a.q + static_cast<int64_t>(qi) * a.H * D;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int head = 16 * mt + n;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qa[mt][ks] = head < a.H ? load_bf16x8(qb + head * D + 32 * ks + 8 * g) : zero_bf16x8();
-    }
-    float wv[MT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int head = 16 * mt + 4 * g + r;
-            wv[mt][r] = head < a.H ? a.w[static_cast<int64_t>(qi) * a.H + head] : 0.0f;
-        }
-
-    // ---- contraction + fp32 epilogue
+    QFrag<MT, KS> f;
+    load_qfrag_global<MT, KS>(f, a.q + static_cast<int64_t>(qi) * a.H * D,
+                              a.w + static_cast<int64_t>(qi) * a.H, a.H, lane);
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-        float part = 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kb[nt][ks], acc, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                part += wv[mt][r] * fmaxf(acc[r], 0.0f);
-        }
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
+        const float v = score_rows<MT, KS>(f, kb[nt]);
         if (g == 0 && pos[nt] < npos)
             a.keys[static_cast<int64_t>(qi) * a.keys_stride + pos[nt]] =
-                valid[nt] ? score_to_key(part) : kNoCandidate;
+                valid[nt] ? score_to_key(v) : kNoCandidate;
     }
 }
 
 template <int MODE, int MT>
-hipError_t launch_mt(const ScoreArgs &a, dim3 grid, hipStream_t st) {
-    if (a.d == 64)
-        hipLaunchKernelGGL((score_kernel<MODE, MT, 2>), grid, dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL((score_kernel<MODE, MT, 4>), grid, dim3(256), 0, st, a);
-    return hipGetLastError();
+hipError_t launch_mt(KernelKind kind, const ScoreArgs &a, dim3 grid, hipStream_t st) {
+    if (a.d == 64) return launch(kind, score_kernel<MODE, MT, 2>, grid, dim3(256), 0, st, a);
+    return launch(kind, score_kernel<MODE, MT, 4>, grid, dim3(256), 0, st, a);
 }
 
 template <int MODE>
-hipError_t launch_mode(const ScoreArgs &a, dim3 grid, hipStream_t st) {
-    if (a.H <= 16) return launch_mt<MODE, 1>(a, grid, st);
-    if (a.H <= 32) return launch_mt<MODE, 2>(a, grid, st);
-    return launch_mt<MODE, 4>(a, grid, st);
+hipError_t launch_mode(KernelKind kind, const ScoreArgs &a, dim3 grid, hipStream_t st) {
+    if (a.H <= 16) return launch_mt<MODE, 1>(kind, a, grid, st);
+    if (a.H <= 32) return launch_mt<MODE, 2>(kind, a, grid, st);
+    return launch_mt<MODE, 4>(kind, a, grid, st);
 }
 
 }  // namespace
@@ -177,13 +130,9 @@ hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int64_t max_pos, hip
                     static_cast<uint32_t>(a.S * a.T));
     const KernelKind kind = mode == kScoreBlocks ? kKindScoreBlocks
                           : mode == kScoreRefine ? kKindScoreRefine : kKindScoreFlat;
-    prof_begin(kind, st);
-    hipError_t e;
-    if (mode == kScoreBlocks) e = launch_mode<kScoreBlocks>(a, grid, st);
-    else if (mode == kScoreRefine) e = launch_mode<kScoreRefine>(a, grid, st);
-    else e = launch_mode<kScoreFlat>(a, grid, st);
-    prof_end(kind, st);
-    return e;
+    if (mode == kScoreBlocks) return launch_mode<kScoreBlocks>(kind, a, grid, st);
+    if (mode == kScoreRefine) return launch_mode<kScoreRefine>(kind, a, grid, st);
+    return launch_mode<kScoreFlat>(kind, a, grid, st);
 }
 
 }  // namespace hisa

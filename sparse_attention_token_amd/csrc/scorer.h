@@ -1,0 +1,138 @@
+// The indexer scorer on the matrix cores, as device building blocks shared by
+// every kernel that scores rows (block stage, refinement, flat indexer).
+//
+// For one query (H heads of dimension d = 32*KS) and 16 rows x_j,
+//     s_j = sum_h w_h * ReLU(q_h . x_j)
+// -- the DSA lightweight-indexer score that the pages' "original indexer"
+// applies both to block representatives (coarse stage) and to tokens
+// (refinement); arXiv abstract and gptget.net English summary, "Methodology".
+//
+// The contraction over d runs on v_mfma_f32_16x16x32_bf16 (bf16 inputs, fp32
+// accumulation):  A = q (M = heads, 16 per M-tile, zero past H),
+// B = rows (N = 16), K = d (32 per k-step).  Lane l = 16*g + n supplies
+// A[head 16*mt + n][8 consecutive d] and B[same 8 d][row n], so the pairing of
+// the contraction index is the same whatever order the unit sums its slots in.
+// D[head][row] comes back as heads 4g..4g+3 of row n in each lane; the fp32
+// epilogue applies ReLU and w and sums heads: the lane's 4*MT values in a fixed
+// order with explicit fused multiply-adds, then across the four lane groups
+// with two xor-shuffles.  Every kernel
+// calls score_rows(), so a given (query, row) gets the same fp32 bits wherever
+// it is scored.
+#pragma once
+
+#include "hisa_internal.h"
+
+namespace hisa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
+    return as_bf16x8(*reinterpret_cast<const u32x4 *>(p));
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    return as_bf16x8(z);
+}
+
+// Query fragments and head weights held in registers by one wave.
+template <int MT, int KS>
+struct QFrag {
+    bf16x8 qa[MT][KS];
+    float wv[MT][4];
+};
+
+// LDS staging of a query: rows of kQStride elements (d + 8 pad keeps the
+// 16-byte fragment reads of 16 consecutive heads on distinct banks).
+template <int KS>
+struct QStage {
+    static constexpr int D = 32 * KS;
+    static constexpr int kStride = D + 8;
+};
+
+// Copy q [H][D] (global) into s_q [MT*16][D+8] with zero rows past H.
+template <int MT, int KS>
+__device__ __forceinline__ void stage_query(const uint16_t *__restrict__ q, int H, uint16_t *s_q,
+                                            int tid, int nthreads) {
+    constexpr int D = QStage<KS>::D, ST = QStage<KS>::kStride;
+    constexpr int chunks = MT * 16 * D / 8;
+    for (int c = tid; c < chunks; c += nthreads) {
+        const int h = c / (D / 8);
+        const int j = c - h * (D / 8);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (h < H) v = *reinterpret_cast<const u32x4 *>(q + h * D + 8 * j);
+        *reinterpret_cast<u32x4 *>(s_q + h * ST + 8 * j) = v;
+    }
+}
+
+template <int MT, int KS>
+__device__ __forceinline__ void load_qfrag_lds(QFrag<MT, KS> &f, const uint16_t *s_q,
+                                               const float *__restrict__ w, int H, int lane) {
+    constexpr int ST = QStage<KS>::kStride;
+    const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            f.qa[mt][ks] = load_bf16x8(s_q + (16 * mt + n) * ST + 32 * ks + 8 * g);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int head = 16 * mt + 4 * g + r;
+            f.wv[mt][r] = head < H ? w[head] : 0.0f;
+        }
+}
+
+template <int MT, int KS>
+__device__ __forceinline__ void load_qfrag_global(QFrag<MT, KS> &f, const uint16_t *__restrict__ q,
+                                                  const float *__restrict__ w, int H, int lane) {
+    constexpr int D = 32 * KS;
+    const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int head = 16 * mt + n;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            f.qa[mt][ks] = head < H ? load_bf16x8(q + head * D + 32 * ks + 8 * g) : zero_bf16x8();
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int head = 16 * mt + 4 * g + r;
+            f.wv[mt][r] = head < H ? w[head] : 0.0f;
+        }
+}
+
+// The row fragment of lane (n, g): 8 consecutive d of row n for each k-step.
+template <int KS>
+__device__ __forceinline__ void load_row_frag(bf16x8 (&kb)[KS], const uint16_t *row, int lane) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        kb[ks] = row ? load_bf16x8(row + 32 * ks + 8 * g) : zero_bf16x8();
+}
+
+// Score of row (lane & 15) for this query; every lane of the row's column
+// group returns the same value.
+template <int MT, int KS>
+__device__ __forceinline__ float score_rows(const QFrag<MT, KS> &f, const bf16x8 (&kb)[KS]) {
+    float part = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.qa[mt][ks], kb[ks], acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part = __builtin_fmaf(f.wv[mt][r], fmaxf(acc[r], 0.0f), part);
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    return part;
+}
+
+}  // namespace hisa

@@ -3,216 +3,235 @@
 // Both stages of the pages' method end in a "keep the best" step -- the top m
 // blocks after block scoring, then the final top k tokens of the refinement
 // (gptget.net English summary, "Methodology"; Chinese summary, method
-// details) -- and the flat indexer ends in a top k over the whole prefix.
-// This kernel implements all three with one rule: rank by (score desc,
-// index asc), keep min(k, #candidates), pad with -1.
+// details) -- and the flat indexer ends in a top k over the whole prefix.  All
+// of them use one rule: rank by (score desc, index asc), keep
+// min(k, #candidates), pad with -1.  Scores arrive as order-preserving uint32
+// keys (0 = no candidate), laid out by increasing candidate index.
 //
-// Scores arrive as order-preserving uint32 keys (0 = no candidate).  One
-// workgroup of 1024 threads owns one query:
-//   1. Radix select, most significant byte first (4 passes of 8 bits):
-//      an LDS histogram of the next byte over keys that still match the
-//      prefix, then one wave scans the 256 bins from the top to find the byte
-//      holding the rank still needed.  After 4 passes the exact 32-bit key
-//      K* of the k-th best candidate is known, together with the number of
-//      candidates strictly above it.  (The first pass also counts the
-//      candidates, which fixes k_eff.)
-//   2. Compaction in position order: thread i owns positions
-//      [i*16, i*16 + 16) of each 16384-position chunk; one block-wide scan of
-//      the packed pair (#keys > K*, #keys == K*) gives every kept key its
-//      output slot, where keys equal to K* are kept lowest position first up
-//      to the count still needed.
-// Positions are laid out in increasing candidate index (block ids, or token
-// ids of the kept blocks taken in ascending block order), so "lowest
-// position first" is the index-ascending tie rule, and every output row comes
-// out sorted by index.
+// One workgroup (1024 threads) selects over up to 32768 positions of one
+// query: thread t holds positions [t*R, t*R + R) in registers and
+// block_radix_select / block_compact (select_core.h) do the rest.  Longer rows
+// are cut into chunks of 32768 positions; each chunk keeps its own top k as
+// (key, id) pairs in position order, and the next stage selects over the
+// concatenation.  This is exact: a member of the row's top k has fewer than k
+// better keys in its chunk, so it survives its chunk's stage, and chunk
+// outputs stay in increasing index order, so ties still resolve by index.
 
 #include "hisa_internal.h"
+#include "select_core.h"
 
 namespace hisa {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWavesSel = kThreads / 64;
-constexpr int kR = 16;
-constexpr int64_t kChunk = static_cast<int64_t>(kThreads) * kR;   // 16384 < 2^16
+constexpr int kNT = 1024;
+constexpr int kChunkMax = kNT * 32;
 
+// number of candidate positions of query qi for a mode (0 for an invalid t)
 template <int MODE>
-__device__ __forceinline__ int32_t position_to_id(const SelectArgs &a, int qi, int64_t p) {
-    if (MODE == kScoreRefine) {
-        const int64_t slot = p / a.B;
-        return static_cast<int32_t>(
-            static_cast<int64_t>(a.sel_blk[static_cast<int64_t>(qi) * a.m + slot]) * a.B + (p - slot * a.B));
-    }
-    return static_cast<int32_t>(p);
+__device__ __forceinline__ int64_t row_length(const SelectArgs &a, int qi) {
+    const int s = qi / a.T;
+    const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    if (t < 0) return 0;
+    const int64_t bt = t / a.B;
+    if (MODE == kScoreBlocks) return bt + 1;
+    if (MODE == kScoreRefine) return ((a.m < bt + 1) ? a.m : bt + 1) * a.B;
+    return t + 1;
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t wave_tot[kWavesSel];
-    __shared__ uint32_t sh_digit, sh_above, sh_keff;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int qi = blockIdx.x;
-    const int s = qi / a.T;
-    const int i = qi - s * a.T;
-    const int64_t t = query_pos(a.qpos, qi, i, a.L, a.T);
-    int64_t n = 0;
-    if (t >= 0) {
-        const int64_t bt = t / a.B;
-        if (MODE == kScoreBlocks) n = bt + 1;
-        else if (MODE == kScoreRefine) n = ((a.m < bt + 1) ? a.m : bt + 1) * a.B;
-        else n = t + 1;
+template <int R>
+__device__ __forceinline__ void load_run(const uint32_t *__restrict__ keys, int64_t base, int64_t n,
+                                         uint32_t (&kv)[R]) {
+    if constexpr (R >= 4) {
+#pragma unroll
+        for (int v = 0; v < R / 4; ++v) {
+            const int64_t p = base + 4 * v;
+            sel_u32x4 x = {0u, 0u, 0u, 0u};
+            if (p < n) x = *reinterpret_cast<const sel_u32x4 *>(keys + p);   // rows are padded to 64 keys
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kv[4 * v + e] = (p + e < n) ? x[e] : kNoCandidate;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) kv[r] = (base + r < n) ? keys[base + r] : kNoCandidate;
     }
-    const uint32_t *keys = a.keys + static_cast<int64_t>(qi) * a.keys_stride;
+}
+
+// Single-stage select: the whole row (n <= kNT*R) in one workgroup.
+template <int MODE, int R>
+__global__ __launch_bounds__(kNT) void select_kernel(SelectArgs a) {
+    __shared__ __attribute__((aligned(16))) SelectScratch sc;
+    __shared__ int32_t s_sel[kSelMaxM];
+    const int tid = threadIdx.x;
+    const int qi = blockIdx.x;
+    const int64_t n = row_length<MODE>(a, qi);
     int32_t *out = a.out_id + static_cast<int64_t>(qi) * a.kout;
     float *osc = a.out_score ? a.out_score + static_cast<int64_t>(qi) * a.kout : nullptr;
     int32_t *out2 = a.out_id_copy ? a.out_id_copy + static_cast<int64_t>(qi) * a.kout : nullptr;
-
-    // ---------------- 1. radix select of the k-th best key
-    uint32_t prefix = 0, mask = 0;
-    uint32_t need = 0, keff = 0;
-    for (int pass = 0; pass < 4 && n > 0; ++pass) {
-        const int shift = 24 - 8 * pass;
-        if (tid < 256) hist[tid] = 0;
-        __syncthreads();
-        for (int64_t c0 = 0; c0 < n; c0 += kChunk) {
-            const int64_t base = c0 + static_cast<int64_t>(tid) * kR;
-#pragma unroll
-            for (int r = 0; r < kR; ++r) {
-                const int64_t p = base + r;
-                if (p < n) {
-                    const uint32_t key = keys[p];
-                    if (key != kNoCandidate && (key & mask) == prefix)
-                        atomicAdd(&hist[(key >> shift) & 255u], 1u);
-                }
-            }
-        }
-        __syncthreads();
-        if (wave == 0) {
-            const uint32_t h0 = hist[4 * lane + 0], h1 = hist[4 * lane + 1];
-            const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-            const uint32_t c = h0 + h1 + h2 + h3;
-            uint32_t suf = c;                                  // sum over lanes >= this lane
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t v = __shfl_down(suf, off);
-                if (lane + off < 64) suf += v;
-            }
-            // rank still needed among keys matching the prefix; on the first
-            // pass the histogram holds every candidate, which fixes k_eff
-            uint32_t rank = need;
-            if (pass == 0) {
-                const uint32_t total = __shfl(suf, 0);
-                rank = total < static_cast<uint32_t>(a.kout) ? total : static_cast<uint32_t>(a.kout);
-                if (lane == 0) sh_keff = rank;
-            }
-            uint32_t above = suf - c;
-            const uint32_t hb[4] = {h0, h1, h2, h3};
-#pragma unroll
-            for (int b = 3; b >= 0; --b) {
-                if (rank > 0 && above < rank && above + hb[b] >= rank) {
-                    sh_digit = static_cast<uint32_t>(4 * lane + b);
-                    sh_above = above;
-                }
-                above += hb[b];
-            }
-        }
-        __syncthreads();
-        if (pass == 0) {
-            keff = sh_keff;
-            need = keff;
-            if (keff == 0) break;
-        }
-        prefix |= sh_digit << shift;
-        mask |= 0xFFu << shift;
-        need -= sh_above;
-        __syncthreads();   // sh_digit / sh_above / hist are rewritten next pass
+    uint32_t kv[R];
+    load_run<R>(a.keys + static_cast<int64_t>(qi) * a.keys_stride, static_cast<int64_t>(tid) * R, n, kv);
+    if (MODE == kScoreRefine) {
+        const int meff = static_cast<int>(n / a.B);
+        for (int j = tid; j < meff; j += kNT) s_sel[j] = a.sel_blk[static_cast<int64_t>(qi) * a.m + j];
+        // block_radix_select starts with a barrier, which also publishes s_sel
     }
-    const uint32_t kstar = prefix;
-    const uint32_t need_eq = need;   // >= 1 when keff > 0
-
-    // ---------------- 2. compaction in position order
-    if (keff > 0) {
-        uint32_t run_gt = 0, run_eq = 0;
-        for (int64_t c0 = 0; c0 < n; c0 += kChunk) {
-            const int64_t base = c0 + static_cast<int64_t>(tid) * kR;
-            uint32_t kv[kR];
-            uint32_t cg = 0, ce = 0;
-#pragma unroll
-            for (int r = 0; r < kR; ++r) {
-                const int64_t p = base + r;
-                kv[r] = p < n ? keys[p] : kNoCandidate;
-                cg += kv[r] > kstar;
-                ce += kv[r] == kstar;
+    const SelectResult res = block_radix_select<kNT, R>(kv, static_cast<uint32_t>(a.kout), sc);
+    if (res.keff > 0) {
+        const int B = a.B;
+        block_compact<kNT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
+            const int pos = tid * R + r;
+            int32_t id = pos;
+            if (MODE == kScoreRefine) {
+                const int slot = pos / B;
+                id = s_sel[slot] * B + (pos - slot * B);
             }
-            const uint32_t v = (cg << 16) | ce;
-            uint32_t incl = v;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t y = __shfl_up(incl, off);
-                if (lane >= off) incl += y;
-            }
-            if (lane == 63) wave_tot[wave] = incl;
-            __syncthreads();
-            uint32_t ex_wave = 0, tot = 0;
-#pragma unroll
-            for (int wv = 0; wv < kWavesSel; ++wv) {
-                const uint32_t x = wave_tot[wv];
-                ex_wave += wv < wave ? x : 0u;
-                tot += x;
-            }
-            const uint32_t ex = ex_wave + incl - v;
-            uint32_t gt_before = run_gt + (ex >> 16);
-            uint32_t eq_before = run_eq + (ex & 0xFFFFu);
-#pragma unroll
-            for (int r = 0; r < kR; ++r) {
-                const uint32_t key = kv[r];
-                uint32_t op = 0xFFFFFFFFu;
-                if (key > kstar) {
-                    op = gt_before + (eq_before < need_eq ? eq_before : need_eq);
-                    ++gt_before;
-                } else if (key == kstar) {
-                    if (eq_before < need_eq) op = gt_before + eq_before;
-                    ++eq_before;
-                }
-                if (op < keff) {   // always true for a correct threshold; guards the write
-                    const int32_t id = position_to_id<MODE>(a, qi, base + r);
-                    out[op] = id;
-                    if (osc) osc[op] = key_to_score(key);
-                    if (out2) out2[op] = id;
-                }
-            }
-            run_gt += tot >> 16;
-            run_eq += tot & 0xFFFFu;
-            __syncthreads();   // wave_tot is rewritten by the next chunk
-        }
+            out[op] = id;
+            if (osc) osc[op] = key_to_score(key);
+            if (out2) out2[op] = id;
+        });
     }
-
-    // ---------------- 3. padding
-    for (int j = static_cast<int>(keff) + tid; j < a.kout; j += kThreads) {
+    for (int j = static_cast<int>(res.keff) + tid; j < a.kout; j += kNT) {
         out[j] = -1;
         if (osc) osc[j] = -__builtin_huge_valf();
         if (out2) out2[j] = -1;
     }
 }
 
+// Chunk stage: grid (nchunk, nq).  Input row: keys (and ids, or positions
+// mapped by MODE when ids_in is null) of length n_fixed, or the mode's row
+// length when n_fixed < 0; output: for each chunk, its top kout (key, id)
+// pairs in position order, padded with key 0.
+template <int MODE>
+__global__ __launch_bounds__(kNT) void select_chunk_kernel(SelectArgs a, const uint32_t *keys_in,
+                                                           const int32_t *ids_in, int64_t in_stride,
+                                                           int64_t n_fixed, uint32_t *keys_out,
+                                                           int32_t *ids_out, int64_t out_stride) {
+    __shared__ __attribute__((aligned(16))) SelectScratch sc;
+    constexpr int R = 32;
+    const int tid = threadIdx.x;
+    const int qi = blockIdx.y;
+    const int64_t n_row = n_fixed >= 0 ? n_fixed : row_length<MODE>(a, qi);
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kChunkMax;
+    const int64_t n = n_row - c0 < kChunkMax ? n_row - c0 : kChunkMax;   // may be <= 0
+    const uint32_t *krow = keys_in + static_cast<int64_t>(qi) * in_stride + c0;
+    uint32_t kv[R];
+    load_run<R>(krow, static_cast<int64_t>(tid) * R, n > 0 ? n : 0, kv);
+    uint32_t *ko = keys_out + static_cast<int64_t>(qi) * out_stride + static_cast<int64_t>(blockIdx.x) * a.kout;
+    int32_t *io = ids_out + static_cast<int64_t>(qi) * out_stride + static_cast<int64_t>(blockIdx.x) * a.kout;
+    const SelectResult res = block_radix_select<kNT, R>(kv, static_cast<uint32_t>(a.kout), sc);
+    if (res.keff > 0) {
+        const int32_t *irow = ids_in ? ids_in + static_cast<int64_t>(qi) * in_stride + c0 : nullptr;
+        block_compact<kNT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
+            const int64_t p = static_cast<int64_t>(tid) * R + r;
+            int32_t id;
+            if (irow) {
+                id = irow[p];
+            } else if (MODE == kScoreRefine) {
+                const int64_t pos = c0 + p;
+                const int64_t slot = pos / a.B;
+                id = static_cast<int32_t>(static_cast<int64_t>(a.sel_blk[static_cast<int64_t>(qi) * a.m + slot]) * a.B + (pos - slot * a.B));
+            } else {
+                id = static_cast<int32_t>(c0 + p);
+            }
+            ko[op] = key;
+            io[op] = id;
+        });
+    }
+    for (int j = static_cast<int>(res.keff) + tid; j < a.kout; j += kNT) {
+        ko[j] = kNoCandidate;
+        io[j] = -1;
+    }
+}
+
+// Final stage over (key, id) pairs: writes the output row.
+__global__ __launch_bounds__(kNT) void select_final_kernel(SelectArgs a, const uint32_t *keys_in,
+                                                           const int32_t *ids_in, int64_t in_stride,
+                                                           int64_t n) {
+    __shared__ __attribute__((aligned(16))) SelectScratch sc;
+    constexpr int R = 32;
+    const int tid = threadIdx.x;
+    const int qi = blockIdx.x;
+    uint32_t kv[R];
+    load_run<R>(keys_in + static_cast<int64_t>(qi) * in_stride, static_cast<int64_t>(tid) * R, n, kv);
+    int32_t *out = a.out_id + static_cast<int64_t>(qi) * a.kout;
+    float *osc = a.out_score ? a.out_score + static_cast<int64_t>(qi) * a.kout : nullptr;
+    int32_t *out2 = a.out_id_copy ? a.out_id_copy + static_cast<int64_t>(qi) * a.kout : nullptr;
+    const int32_t *irow = ids_in + static_cast<int64_t>(qi) * in_stride;
+    const SelectResult res = block_radix_select<kNT, R>(kv, static_cast<uint32_t>(a.kout), sc);
+    if (res.keff > 0) {
+        block_compact<kNT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
+            const int32_t id = irow[tid * R + r];
+            out[op] = id;
+            if (osc) osc[op] = key_to_score(key);
+            if (out2) out2[op] = id;
+        });
+    }
+    for (int j = static_cast<int>(res.keff) + tid; j < a.kout; j += kNT) {
+        out[j] = -1;
+        if (osc) osc[j] = -__builtin_huge_valf();
+        if (out2) out2[j] = -1;
+    }
+}
+
+template <int MODE>
+hipError_t launch_single(KernelKind kind, const SelectArgs &a, int nq, int64_t max_n, hipStream_t st) {
+    const dim3 g(nq), b(kNT);
+    const int64_t per = (max_n + kNT - 1) / kNT;
+    if (per <= 1) return launch(kind, select_kernel<MODE, 1>, g, b, 0, st, a);
+    if (per <= 2) return launch(kind, select_kernel<MODE, 2>, g, b, 0, st, a);
+    if (per <= 4) return launch(kind, select_kernel<MODE, 4>, g, b, 0, st, a);
+    if (per <= 8) return launch(kind, select_kernel<MODE, 8>, g, b, 0, st, a);
+    if (per <= 16) return launch(kind, select_kernel<MODE, 16>, g, b, 0, st, a);
+    return launch(kind, select_kernel<MODE, 32>, g, b, 0, st, a);
+}
+
+template <int MODE>
+hipError_t launch_chunked(KernelKind kind, const SelectArgs &a, int nq, int64_t max_n, hipStream_t st) {
+    // stage 1 over the raw keys, then chunk stages over (key, id) pairs until
+    // one workgroup can finish the row
+    uint32_t *bufk[2] = {a.stage_keys[0], a.stage_keys[1]};
+    int32_t *bufi[2] = {a.stage_ids[0], a.stage_ids[1]};
+    int64_t nchunk = (max_n + kChunkMax - 1) / kChunkMax;
+    hipError_t e = launch(kind, select_chunk_kernel<MODE>, dim3(static_cast<uint32_t>(nchunk), nq),
+                          dim3(kNT), 0, st, a, static_cast<const uint32_t *>(a.keys),
+                          static_cast<const int32_t *>(nullptr), a.keys_stride, int64_t{-1}, bufk[0],
+                          bufi[0], a.stage_stride);
+    if (e != hipSuccess) return e;
+    int cur = 0;
+    int64_t n = nchunk * a.kout;
+    while (n > kChunkMax) {
+        nchunk = (n + kChunkMax - 1) / kChunkMax;
+        e = launch(kind, select_chunk_kernel<MODE>, dim3(static_cast<uint32_t>(nchunk), nq), dim3(kNT), 0,
+                   st, a, static_cast<const uint32_t *>(bufk[cur]), static_cast<const int32_t *>(bufi[cur]),
+                   a.stage_stride, n, bufk[1 - cur], bufi[1 - cur], a.stage_stride);
+        if (e != hipSuccess) return e;
+        cur = 1 - cur;
+        n = nchunk * a.kout;
+    }
+    return launch(kind, select_final_kernel, dim3(nq), dim3(kNT), 0, st, a,
+                  static_cast<const uint32_t *>(bufk[cur]), static_cast<const int32_t *>(bufi[cur]),
+                  a.stage_stride, n);
+}
+
 }  // namespace
 
-hipError_t launch_select(ScoreMode mode, const SelectArgs &a, int nq, hipStream_t st) {
+int64_t select_stage_len(int64_t max_n, int kout, int B, bool refine) {
+    const bool chunked = max_n > kChunkMax || (refine && max_n / B > kSelMaxM);
+    if (!chunked) return 0;
+    // the first stage is the longest: one kout-row per chunk of the input
+    return (max_n + kChunkMax - 1) / kChunkMax * static_cast<int64_t>(kout);
+}
+
+hipError_t launch_select(ScoreMode mode, const SelectArgs &a, int nq, int64_t max_n, hipStream_t st) {
     const KernelKind kind = mode == kScoreBlocks ? kKindSelectBlocks
                           : mode == kScoreRefine ? kKindSelectRefine : kKindSelectFlat;
-    prof_begin(kind, st);
-    if (mode == kScoreBlocks)
-        hipLaunchKernelGGL(select_kernel<kScoreBlocks>, dim3(nq), dim3(kThreads), 0, st, a);
-    else if (mode == kScoreRefine)
-        hipLaunchKernelGGL(select_kernel<kScoreRefine>, dim3(nq), dim3(kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL(select_kernel<kScoreFlat>, dim3(nq), dim3(kThreads), 0, st, a);
-    prof_end(kind, st);
-    return hipGetLastError();
+    if (select_stage_len(max_n, a.kout, a.B, mode == kScoreRefine) > 0) {
+        if (mode == kScoreBlocks) return launch_chunked<kScoreBlocks>(kind, a, nq, max_n, st);
+        if (mode == kScoreRefine) return launch_chunked<kScoreRefine>(kind, a, nq, max_n, st);
+        return launch_chunked<kScoreFlat>(kind, a, nq, max_n, st);
+    }
+    if (mode == kScoreBlocks) return launch_single<kScoreBlocks>(kind, a, nq, max_n, st);
+    if (mode == kScoreRefine) return launch_single<kScoreRefine>(kind, a, nq, max_n, st);
+    return launch_single<kScoreFlat>(kind, a, nq, max_n, st);
 }
 
 }  // namespace hisa

@@ -154,10 +154,11 @@ def _query_args(q, w, qpos, K, L):
 
 
 def _workspace(nbytes: int, device, workspace):
+    """Allocate the workspace, or pass the caller's through (the library checks its size)."""
     if workspace is None:
         return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
-    if workspace.device != device or workspace.numel() * workspace.element_size() < nbytes:
-        raise ValueError(f"workspace must be a device buffer of >= {nbytes} bytes")
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous buffer on the query's device")
     return workspace
 
 

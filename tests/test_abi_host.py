@@ -126,7 +126,7 @@ def test_argument_checks_with_placeholder_pointers(lib):
     assert idx(T=L + 1) == ARG              # default positions would be negative
     assert idx(H=0) == ARG
     assert idx(S=300, T=300) == UNSUP       # S*T > 65535
-    assert idx(k=70000) == UNSUP
+    assert idx(k=16385) == UNSUP
     assert idx(m=4097) == UNSUP
     fneed = lib.dsa_flat_workspace(S, T, H, d, L, k)
     assert lib.dsa_flat_index(p, p, None, p, kss, L, S, T, H, d, k, p, None, p, fneed - 1, None) == WS

@@ -100,6 +100,13 @@ SMALL = [
     ("c_h64_d64_B256", 1, 2600, 8, 64, 64, 256, 2, 300, "clustered"),
     ("c_pad_k_gt_C", 1, 1500, 8, 32, 128, 128, 1, 600, "clustered"),
     ("c_h1_d128_B64", 1, 900, 5, 1, 128, 64, 5, 40, "clustered"),
+    # shapes outside the fused kernels' limits take the general path
+    ("general_B256_d128", 1, 3000, 6, 64, 128, 256, 3, 300, "clustered"),
+    ("general_mB_25600", 1, 40000, 4, 16, 64, 128, 200, 500, "clustered"),
+    # more than 32768 candidates per query: chunked (two-stage) top-k
+    ("chunked_refine_38400", 1, 60000, 3, 16, 64, 128, 300, 3000, "clustered"),
+    # more than 2048 blocks: the block stage selects with the whole workgroup
+    ("blocks_2344_workgroup_select", 1, 300000, 2, 4, 64, 128, 8, 256, "gaussian"),
 ]
 
 
