@@ -53,17 +53,24 @@ struct QStage {
 };
 
 // Copy q [H][D] (global) into s_q [MT*16][D+8] with zero rows past H.
-template <int MT, int KS>
-__device__ __forceinline__ void stage_query(const uint16_t *__restrict__ q, int H, uint16_t *s_q,
-                                            int tid, int nthreads) {
+template <int MT, int KS, int NT>
+__device__ __forceinline__ void stage_query(const uint16_t *__restrict__ q, int H, uint16_t *s_q, int tid) {
     constexpr int D = QStage<KS>::D, ST = QStage<KS>::kStride;
     constexpr int chunks = MT * 16 * D / 8;
-    for (int c = tid; c < chunks; c += nthreads) {
+    constexpr int kPer = (chunks + NT - 1) / NT;
+    u32x4 v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {                  // every load in flight before the stores
+        const int c = tid + i * NT;
         const int h = c / (D / 8);
-        const int j = c - h * (D / 8);
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (h < H) v = *reinterpret_cast<const u32x4 *>(q + h * D + 8 * j);
-        *reinterpret_cast<u32x4 *>(s_q + h * ST + 8 * j) = v;
+        v[i] = u32x4{0u, 0u, 0u, 0u};
+        if (c < chunks && h < H) v[i] = *reinterpret_cast<const u32x4 *>(q + h * D + 8 * (c - h * (D / 8)));
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int c = tid + i * NT;
+        const int h = c / (D / 8);
+        if (c < chunks) *reinterpret_cast<u32x4 *>(s_q + h * ST + 8 * (c - h * (D / 8))) = v[i];
     }
 }
 

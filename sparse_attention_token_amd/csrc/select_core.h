@@ -191,12 +191,15 @@ __device__ __forceinline__ void block_compact(const uint32_t (&kv)[R], const Sel
 constexpr int kWaveHistRow = 260;                       // 256 bins + pad: copies start 4 banks apart
 constexpr int kWaveHistWords = 4 * 8 * kWaveHistRow;    // 4 passes x 8 copies
 
+// hist: kWaveHistWords words of LDS, 16-byte aligned; cleared here unless
+// the caller already zeroed them (cleared == false means "already zero").
 template <int R>
 __device__ __forceinline__ SelectResult wave_radix_select(const uint32_t (&kv)[R], uint32_t kout,
-                                                          uint32_t *hist) {
+                                                          uint32_t *hist, bool clear = true) {
     const int lane = threadIdx.x & 63;
-    for (int w = lane * 4; w < kWaveHistWords; w += 64 * 4)
-        *reinterpret_cast<sel_u32x4 *>(&hist[w]) = sel_u32x4{0u, 0u, 0u, 0u};
+    if (clear)
+        for (int w = lane * 4; w < kWaveHistWords; w += 64 * 4)
+            *reinterpret_cast<sel_u32x4 *>(&hist[w]) = sel_u32x4{0u, 0u, 0u, 0u};
     uint32_t prefix = 0, mask = 0, need = 0, keff = 0;
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {

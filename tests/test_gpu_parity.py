@@ -73,6 +73,35 @@ def test_pool_bit_exact(hisa, orc, B, d, L, S):
     np.testing.assert_array_equal(bits(inc7), ref)
 
 
+def _wide_spread_keys(c, seed):
+    """Scale some rows by 2^-45 and others by 2^+12 so that block columns span
+    more than 37 binades: the mean must then be summed in row order."""
+    rng = np.random.default_rng(seed)
+    f = synth.bf16_to_f32(c.K).astype(np.float64)
+    scale = rng.choice([2.0 ** -45, 1.0, 2.0 ** 12], size=f.shape[:2] + (1,), p=[0.3, 0.5, 0.2])
+    c.K = synth.bf16_bits((f * scale).astype(np.float32))
+    return c
+
+
+@pytest.mark.parametrize("B,d", [(64, 64), (128, 128)])
+def test_pool_wide_exponent_spread(hisa, orc, B, d):
+    c = _wide_spread_keys(synth.gaussian_case(2, 700, 1, 1, d, B, 1, 1, seed=31), 5)
+    dev = to_dev(c)
+    np.testing.assert_array_equal(bits(build_pool(hisa, dev["K"], 700, B)), orc.pool(c.K, 700, B))
+
+
+def test_hisa_wide_exponent_spread(hisa, orc):
+    # own-block means (recomputed inside the block stage) over rows of very
+    # different magnitudes; queries at every offset inside a block
+    c = synth.clustered_case(1, 1024, 8, 16, 128, 128, 3, 200, seed=32,
+                             qpos=[[1000, 1001, 1010, 1023, 900, 899, 700, 130]])
+    c = _wide_spread_keys(c, 6)
+    out = _run(hisa, c)
+    for i in range(c.T):
+        check_hisa_row(orc, c, 0, i, out["idx"][0, i], out["sc"][0, i], out["blk"][0, i])
+        check_flat_row(orc, c, 0, i, out["fidx"][0, i], out["fsc"][0, i])
+
+
 def test_pool_append_is_idempotent(hisa, orc):
     c = synth.gaussian_case(1, 500, 1, 1, 128, 64, 1, 1, seed=3)
     dev = to_dev(c)
