@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--no-flat", action="store_true", help="skip the flat DSA baseline")
     p.add_argument("--profile-steps", type=int, default=None,
                    help="eager steps bracketed by per-kernel HIP events")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB three times (the known-size "
+                        "reference that scales the HBM byte counters) and exit")
     return p.parse_args()
 
 
@@ -84,6 +87,9 @@ def kernel_models(case, blocks):
         "score_flat": dict(bytes=int((t + 1).sum() * row + qw), flops=int(2 * H * d * (t + 1).sum())),
         "select_flat": dict(bytes=int((t + 1).sum() * 4 + S * T * k * 8), flops=0),
     }
+    # the one-launch decode kernel does the block stage, the top m and the refinement
+    models["index_decode"] = dict(bytes=int((nb.sum() + cand.sum()) * row + qw),
+                                  flops=models["score_blocks"]["flops"] + models["score_refine"]["flops"])
     per_query_hisa = (nb.sum() + cand.sum()) * row + qw + S * T * k * 4
     return models, int(per_query_hisa), int(cand.sum())
 
@@ -127,6 +133,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        n = args.copy_probe * 2**20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return
     hisa.lib()
     case = synth.workload(args.workload)
     S, T, H, d, L, B, m, k = case.S, case.T, case.H, case.d, case.L, case.B, case.m, case.k
@@ -287,18 +302,26 @@ def main():
         import oracle
 
         n = S * T
-        sel = np.arange(n, dtype=np.int32) if n <= 16 else np.linspace(0, n - 1, 64).astype(np.int32)
-        times = []
-        for _ in range(3):
-            t0 = time.perf_counter()
+        # size the sample to about 10 s of oracle work: distinct queries first
+        # (evenly spaced over the batch), then whole repeats of the batch
+        probe = np.linspace(0, n - 1, min(n, 8)).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.hisa_batch(case.q, case.w, case.qpos, case.K, L, B, m, k, sel=probe)
+        per_q = max((time.perf_counter() - t0) / len(probe), 1e-6)
+        target_s = 15.0
+        nsel = int(min(n, max(len(probe), target_s / per_q)))
+        sel = np.linspace(0, n - 1, nsel).astype(np.int32)
+        reps = max(1, min(1000, int(round(target_s / (per_q * nsel)))))
+        t0 = time.perf_counter()
+        for _ in range(reps):
             oracle.hisa_batch(case.q, case.w, case.qpos, case.K, L, B, m, k, sel=sel)
-            times.append(time.perf_counter() - t0)
-        tc = float(np.median(times))
-        cpu = {"value": len(sel) / tc, "unit": "queries/s", "cores": oracle.num_threads(),
+        tc = time.perf_counter() - t0
+        nq_cpu = reps * len(sel)
+        cpu = {"value": nq_cpu / tc, "unit": "queries/s", "cores": oracle.num_threads(),
                "kind": "oracle",
-               "sample": f"{len(sel)} of {n} queries of {case.name} through the fp64 C oracle "
-                         f"(HISA, median of 3 runs, {tc:.2f} s each)",
-               "us_per_query": tc / len(sel) * 1e6}
+               "sample": f"{len(sel)} of {n} queries of {case.name} (evenly spaced), {reps} pass(es), "
+                         f"through the fp64 C oracle (HISA): {nq_cpu} queries in {tc:.1f} s",
+               "us_per_query": tc / nq_cpu * 1e6}
 
     nq = S * T
     value = nq / (hisa_ms * 1e-3)

@@ -146,6 +146,7 @@ void prof_release() {
 const char *const kKindNames[kKindCount] = {
     "pool_append", "own_mean", "score_blocks", "select_blocks",
     "score_refine", "select_refine", "score_flat", "select_flat",
+    "index_decode",
 };
 
 }  // namespace

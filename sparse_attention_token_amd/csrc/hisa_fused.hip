@@ -364,7 +364,7 @@ template <int MT, int KS>
 hipError_t launch_fused_ks(const FusedArgs &a, bool decode, hipStream_t st) {
     const int nq = a.S * a.T;
     const dim3 g2(static_cast<uint32_t>((static_cast<int64_t>(a.m) * a.B + 127) / 128), nq);
-    if (decode) return launch(kKindScoreRefine, hisa_decode_kernel<MT, KS>, g2, dim3(kDecodeThreads), 0, st, a);
+    if (decode) return launch(kKindIndexDecode, hisa_decode_kernel<MT, KS>, g2, dim3(kDecodeThreads), 0, st, a);
     const hipError_t e = launch(kKindScoreBlocks, hisa_blocks_topm_kernel<MT, KS>, dim3(nq), dim3(kK1Threads), 0, st, a);
     if (e != hipSuccess) return e;
     return launch(kKindScoreRefine, hisa_refine_kernel<MT, KS>, g2, dim3(kK2Threads), 0, st, a);

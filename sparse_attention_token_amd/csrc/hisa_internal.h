@@ -137,6 +137,7 @@ enum KernelKind {
     kKindSelectRefine,
     kKindScoreFlat,
     kKindSelectFlat,
+    kKindIndexDecode,      // block stage + top-m + refinement in one launch
     kKindCount
 };
 
