@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhisa.so")
-SOURCES = ["hisa_abi.hip", "pool.hip", "score.hip", "select.hip", "hisa_fused.hip"]
+SOURCES = ["hisa_abi.hip", "pool.hip", "score.hip", "select.hip", "hisa_fused.hip", "hisa_prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -20,6 +20,9 @@ FLAGS = [
     "-Wno-unused-parameter", "-fvisibility=hidden",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: the score epilogue reads every
+    # accumulator, and the AGPR form costs one extra move per value
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

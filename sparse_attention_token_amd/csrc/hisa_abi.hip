@@ -71,7 +71,7 @@ size_t carve_stage(size_t off, int64_t nq, int64_t len, StageBufs &sb) {
 }
 
 struct HisaLayout {
-    size_t own_rep, blk_keys, sel_blk, cand_keys, total;
+    size_t own_rep, blk_keys, sel_blk, cand_keys, bucket_off, bucket_ent, total;
     int64_t blk_stride, cand_stride;
     StageBufs stage;
 };
@@ -87,6 +87,11 @@ HisaLayout hisa_layout(int S, int T, int d, int64_t L, int B, int m, int k) {
     l.blk_keys = off;  off = align_up(off + static_cast<size_t>(nq) * l.blk_stride * sizeof(uint32_t), kAlign);
     l.sel_blk = off;   off = align_up(off + static_cast<size_t>(nq) * m * sizeof(int32_t), kAlign);
     l.cand_keys = off; off = align_up(off + static_cast<size_t>(nq) * l.cand_stride * sizeof(uint32_t), kAlign);
+    if (block_major_mode(S, T, d, L, B, m)) {
+        const size_t nchunk = static_cast<size_t>(bucket_chunks(S, T));
+        l.bucket_off = off; off = align_up(off + nchunk * (nblk + 1) * sizeof(int32_t), kAlign);
+        l.bucket_ent = off; off = align_up(off + nchunk * kChunkQueries * m * sizeof(uint32_t), kAlign);
+    }
     const int64_t len = std::max(select_stage_len(nblk, m, B, false),
                                  select_stage_len(static_cast<int64_t>(m) * B, k, B, true));
     off = carve_stage(off, nq, len, l.stage);
@@ -146,7 +151,7 @@ void prof_release() {
 const char *const kKindNames[kKindCount] = {
     "pool_append", "own_mean", "score_blocks", "select_blocks",
     "score_refine", "select_refine", "score_flat", "select_flat",
-    "index_decode",
+    "index_decode", "bucket",
 };
 
 }  // namespace
@@ -244,6 +249,11 @@ int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uin
         fa.sel_blk = sel_blk; fa.out_blk = out_blk;
         fa.cand_keys = cand_keys; fa.cand_stride = lay.cand_stride;
         fa.out_idx = out_idx; fa.out_score = out_score;
+        fa.nblk = static_cast<int>(ceil_div(L, B));
+        if (block_major_mode(S, T, d, L, B, m)) {
+            fa.bucket_off = reinterpret_cast<int32_t *>(base + lay.bucket_off);
+            fa.bucket_ent = reinterpret_cast<uint32_t *>(base + lay.bucket_ent);
+        }
         st = hip_status(launch_fused_blocks_refine(fa, hs));
         if (st != HISA_OK) return st;
         se.keys = cand_keys; se.keys_stride = lay.cand_stride;

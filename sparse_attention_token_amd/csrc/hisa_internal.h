@@ -109,10 +109,25 @@ struct FusedArgs {
     int64_t cand_stride;
     int32_t *out_idx;         // [S*T][k]
     float *out_score;         // [S*T][k] or null
+    // block-major refinement (see block_major_mode): for each chunk of up to
+    // kChunkQueries consecutive queries of one sequence, the (query, slot)
+    // pairs of its kept blocks grouped by block id
+    int nblk;                 // ceil(L/B)
+    int32_t *bucket_off;      // ws [nchunk][nblk + 1]
+    uint32_t *bucket_ent;     // ws [nchunk][kChunkQueries * m]: (query in chunk) << 16 | slot
 };
 
+constexpr int kChunkQueries = 256;
+
 bool fused_supported(int d, int64_t L, int B, int m);
+// Many queries per sequence: refine block by block (each key block is read
+// once per chunk of queries) instead of query by query.
+bool block_major_mode(int S, int T, int d, int64_t L, int B, int m);
+inline int64_t bucket_chunks(int S, int T) {
+    return static_cast<int64_t>(S) * ((T + kChunkQueries - 1) / kChunkQueries);
+}
 hipError_t launch_fused_blocks_refine(const FusedArgs &a, hipStream_t st);
+hipError_t launch_block_major_refine(const FusedArgs &a, hipStream_t st);
 
 hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
                               int64_t blk0, int64_t nblk, int64_t L_new, uint16_t *pool,
@@ -138,6 +153,7 @@ enum KernelKind {
     kKindScoreFlat,
     kKindSelectFlat,
     kKindIndexDecode,      // block stage + top-m + refinement in one launch
+    kKindBucket,           // (query, slot) pairs grouped by kept block
     kKindCount
 };
 

@@ -1,0 +1,318 @@
+// Token refinement for many queries per sequence (prefill chunks), block by
+// block.
+//
+// The refinement step re-scores, with the original indexer, every token of the
+// blocks each query kept (gptget.net English summary, "Methodology"; Chinese
+// summary, method details).  Done query by query, every (query, kept block)
+// pair gathers the block's B key rows again: with thousands of queries over
+// the same cache the key rows are fetched from the memory fabric once per pair.
+// Here the pairs are grouped by block instead, per chunk of up to
+// kChunkQueries consecutive queries of one sequence:
+//
+//   hisa_bucket_kernel   one workgroup per chunk: counting sort of the chunk's
+//                        (query, slot) pairs by kept block id, in LDS.
+//   hisa_refine_bm_kernel one 2-wave workgroup per (block, chunk) (bm_tile()): the block's
+//                        B rows stay in registers as MFMA operands (each wave
+//                        owns B/2 rows), and the queries that kept the block
+//                        stream through a double-buffered LDS stage filled by
+//                        direct global-to-LDS loads: while the matrix cores
+//                        score query i, the loads of query i+1 are in flight.
+//
+// Each (query, row) score comes from score_tiles_lds(), whose per-tile
+// arithmetic is that of score_rows() in every other kernel, so the results are
+// bit-identical to the query-major refinement's; candidate position p = slot*B + r of query qi gets the key of
+// row r of its slot-th kept block, or "no candidate" past the query position.
+
+#include "hisa_internal.h"
+#include "scorer.h"
+#include "select_core.h"
+
+namespace hisa {
+namespace {
+
+constexpr int kBucketThreads = 1024;
+constexpr int kBucketR = kFusedMaxBlocks / kBucketThreads;   // bins per thread in the scan
+constexpr int kBMThreads = 128;                              // two waves
+
+__global__ __launch_bounds__(kBucketThreads) void hisa_bucket_kernel(FusedArgs a) {
+    __shared__ uint32_t s_cnt[kFusedMaxBlocks];
+    __shared__ uint32_t s_wave[kBucketThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = blockIdx.x;
+    const int cps = (a.T + kChunkQueries - 1) / kChunkQueries;
+    const int s = c / cps;
+    const int i0 = (c - s * cps) * kChunkQueries;
+    const int nqc = min(kChunkQueries, a.T - i0);
+    const int nblk = a.nblk;
+    const int32_t *sel = a.sel_blk + (static_cast<int64_t>(s) * a.T + i0) * a.m;
+    const int n = nqc * a.m;
+
+    for (int b = tid; b < nblk; b += kBucketThreads) s_cnt[b] = 0u;
+    __syncthreads();
+    for (int e = tid; e < n; e += kBucketThreads) {
+        const int b = sel[e];
+        if (b >= 0) atomicAdd(&s_cnt[b], 1u);
+    }
+    __syncthreads();
+
+    // exclusive scan of the bins: thread t owns bins [t*R, t*R + R)
+    uint32_t v[kBucketR];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int r = 0; r < kBucketR; ++r) {
+        const int b = tid * kBucketR + r;
+        v[r] = b < nblk ? s_cnt[b] : 0u;
+        sum += v[r];
+    }
+    const uint32_t incl = wave_prefix_incl(sum);
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    uint32_t run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += s_wave[w];
+    int32_t *off = a.bucket_off + static_cast<int64_t>(c) * (nblk + 1);
+#pragma unroll
+    for (int r = 0; r < kBucketR; ++r) {
+        const int b = tid * kBucketR + r;
+        if (b < nblk) {
+            off[b] = static_cast<int32_t>(run);
+            s_cnt[b] = run;              // becomes the fill cursor
+        }
+        run += v[r];
+    }
+    if (tid == kBucketThreads - 1) off[nblk] = static_cast<int32_t>(run);
+    __syncthreads();
+
+    uint32_t *ent = a.bucket_ent + static_cast<int64_t>(c) * kChunkQueries * a.m;
+    for (int e = tid; e < n; e += kBucketThreads) {
+        const int b = sel[e];
+        if (b >= 0) {
+            const uint32_t pos = atomicAdd(&s_cnt[b], 1u);
+            const int ql = e / a.m;
+            ent[pos] = (static_cast<uint32_t>(ql) << 16) | static_cast<uint32_t>(e - ql * a.m);
+        }
+    }
+}
+
+// Direct-to-LDS staging of one query (q and w) into the padded layout that
+// load_qfrag_lds_w() reads: head row h at h * kStride elements.  One
+// global_load_lds_dwordx4 fills 64 consecutive 16-byte LDS slots, one per
+// lane; slot p holds chunk (p % SL) of head row (p / SL), where SL = kStride/8
+// slots per row and the last slot of a row is padding (never read).  Lanes of
+// padding slots and of rows past H write nothing: those rows are zeroed once.
+// The direct global-to-LDS loads, behind plain device functions: named
+// directly inside a kernel template, the target builtins keep the host pass
+// from emitting some of the template's launch stubs.  Buffer form: the base
+// address and size live in scalar registers (a buffer resource), each lane
+// adds its own byte offset, and M0 holds the LDS destination of lane 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                             0x00020000);
+}
+__device__ __forceinline__ void lds_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, void *lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, reinterpret_cast<__attribute__((address_space(3))) void *>(
+                                                    reinterpret_cast<uintptr_t>(lds)),
+                                             16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_load_b32(__amdgpu_buffer_rsrc_t r, uint32_t voff, void *lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, reinterpret_cast<__attribute__((address_space(3))) void *>(
+                                                    reinterpret_cast<uintptr_t>(lds)),
+                                             4, voff, 0, 0, 0);
+}
+
+// Direct-to-LDS staging of one query (q and w) into the padded layout that
+// the scorer reads: head row h at h * kStride elements.  One 16-byte buffer
+// load to LDS fills 64 consecutive 16-byte slots, one per lane; slot p holds
+// chunk (p % SL) of head row (p / SL), where SL = kStride/8 slots per row and
+// the last slot of a row is padding (never read).  Lanes of padding slots and
+// of rows past H write nothing: those rows are zeroed once.
+template <int MT, int KS, int NW>
+struct QDirect {
+    static constexpr int D = 32 * KS;
+    static constexpr int SL = QStage<KS>::kStride / 8;
+    static constexpr int kSlots = MT * 16 * SL;
+    static constexpr int kInstr = (kSlots + 63) / 64;
+    static constexpr int kPerWave = (kInstr + NW - 1) / NW;   // wave w takes instructions w, w+NW, ...
+    int src[kPerWave];                                        // byte offset in q, or -1: no load
+
+    __device__ __forceinline__ void init(int H, int wave, int lane) {
+#pragma unroll
+        for (int u = 0; u < kPerWave; ++u) {
+            const int j = wave + u * NW;
+            const int p = 64 * j + lane;
+            const int row = p / SL, col = p - row * SL;
+            src[u] = (j < kInstr && p < kSlots && col < SL - 1 && row < H) ? 2 * (row * D + 8 * col) : -1;
+        }
+    }
+    __device__ __forceinline__ void issue(const uint16_t *__restrict__ q, const float *__restrict__ w, int H,
+                                          uint16_t *s_q, float *s_w, int wave, int lane) const {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, static_cast<uint32_t>(H * D * 2));
+#pragma unroll
+        for (int u = 0; u < kPerWave; ++u)
+            if (src[u] >= 0) lds_load_b128(rq, static_cast<uint32_t>(src[u]), s_q + 8 * 64 * (wave + u * NW));
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, static_cast<uint32_t>(H * 4));
+        if (wave == NW - 1 && lane < H) lds_load_b32(rw, 4u * lane, s_w);
+    }
+};
+
+// Workgroup -> (block b, chunk c).  With at least 8 chunks, chunk c runs on
+// XCD c % 8 (workgroups are dealt to the 8 XCDs in turn): every workgroup of
+// an XCD then works on the same chunk, whose queries stay in that XCD's L2
+// while the key blocks stream through.  c = -1: nothing to do.
+__device__ __forceinline__ void bm_tile(int nblk, int nchunk, int &b, int &c) {
+    const int i = blockIdx.x;
+    if (nchunk >= 8) {
+        const int x = i & 7, r = i >> 3;
+        const int cc = r / nblk;
+        b = r - cc * nblk;
+        c = cc * 8 + x;
+        if (c >= nchunk) c = -1;
+    } else {
+        c = i / nblk;
+        b = i - c * nblk;
+    }
+}
+
+inline uint32_t bm_grid(int nblk, int64_t nchunk) {
+    return static_cast<uint32_t>(nchunk >= 8 ? (nchunk + 7) / 8 * 8 * nblk : nchunk * nblk);
+}
+
+// Candidate keys of one query for this wave's NTW tiles: every lane of a row's
+// column group holds that row's score, so lane (n, g) stores tiles g, g+4, ...
+// -- one store per lane per four tiles.  "No candidate" past the query
+// position t.
+template <int NTW>
+__device__ __forceinline__ void store_tiles(uint32_t *cand, const float (&v)[NTW], int tok0, int t, int lane) {
+    const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int nt0 = 0; nt0 < NTW; nt0 += 4) {
+        if (nt0 + g < NTW) {
+            float x = v[nt0];
+#pragma unroll
+            for (int j = 1; j < 4; ++j)
+                if (nt0 + j < NTW && g == j) x = v[nt0 + j];
+            const int r = (nt0 + g) * 16 + n;
+            cand[r] = tok0 + r <= t ? score_to_key(x) : kNoCandidate;
+        }
+    }
+}
+
+// NTW 16-row tiles per wave; the workgroup covers B = 2 * 16 * NTW rows.
+template <int MT, int KS, int NTW>
+__global__ __launch_bounds__(kBMThreads) void hisa_refine_bm_kernel(FusedArgs a) {
+    constexpr int D = 32 * KS;
+    constexpr int NW = kBMThreads / 64;
+    using QD = QDirect<MT, KS, NW>;
+    constexpr int kQElems = QD::kInstr * 64 * 8;                   // whole instructions, padding included
+    constexpr int kRowsPerWave = 16 * NTW;
+    __shared__ __attribute__((aligned(16))) uint16_t s_q[2][kQElems];
+    __shared__ __attribute__((aligned(16))) float s_w[2][64];
+    __shared__ uint32_t s_ent[kChunkQueries];
+    __shared__ int32_t s_t[kChunkQueries];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15;
+    const int cps = (a.T + kChunkQueries - 1) / kChunkQueries;
+    int b, c;
+    bm_tile(a.nblk, a.S * cps, b, c);
+    if (c < 0) return;
+    const int32_t *off = a.bucket_off + static_cast<int64_t>(c) * (a.nblk + 1);
+    const int e0 = off[b];
+    const int np = off[b + 1] - e0;
+    if (np <= 0) return;
+    const int s = c / cps;
+    const int i0 = (c - s * cps) * kChunkQueries;
+    const int qi0 = s * a.T + i0;
+
+    // this wave's rows of block b (rows past the cache end are zero and masked;
+    // positions fit in int: L < 2^31)
+    const int tok0 = b * a.B + wave * kRowsPerWave;
+    bf16x8 kb[NTW][KS];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+        const int tok = tok0 + nt * 16 + n;
+        load_row_frag<KS>(kb[nt], tok < a.L ? a.K + s * a.k_seq_stride + static_cast<int64_t>(tok) * D : nullptr,
+                          lane);
+    }
+    // the pairs (query, slot) and each query's position
+    const uint32_t *ent = a.bucket_ent + static_cast<int64_t>(c) * kChunkQueries * a.m + e0;
+    for (int i = tid; i < np; i += kBMThreads) {
+        const uint32_t e = ent[i];
+        const int ql = static_cast<int>(e >> 16);
+        s_ent[i] = e;
+        s_t[i] = static_cast<int32_t>(query_pos(a.qpos, qi0 + ql, i0 + ql, a.L, a.T));
+    }
+    // rows past H read as zero (q) with weight zero, in both buffers
+    if (a.H < MT * 16) {
+        constexpr int ST = QStage<KS>::kStride;
+        for (int x = tid; x < 2 * (MT * 16 - a.H) * ST; x += kBMThreads) {
+            const int bf = x / ((MT * 16 - a.H) * ST), r = x - bf * (MT * 16 - a.H) * ST;
+            s_q[bf][a.H * ST + r] = 0;
+        }
+        for (int x = tid; x < 2 * 64; x += kBMThreads) s_w[x >> 6][x & 63] = 0.0f;
+    }
+    __syncthreads();
+
+    QD qd;
+    qd.init(a.H, wave, lane);
+    {
+        const int qi = qi0 + static_cast<int>(s_ent[0] >> 16);
+        qd.issue(a.q + static_cast<int64_t>(qi) * a.H * D, a.w + static_cast<int64_t>(qi) * a.H, a.H, s_q[0],
+                 s_w[0], wave, lane);
+    }
+    // Scores of query i are stored during query i+1 (after its loads are
+    // issued), so the wait at the top of an iteration never waits on stores
+    // issued just before it.
+    float v[NTW];
+    uint32_t *cand = nullptr;
+    int t = -1;
+    for (int i = 0; i < np; ++i) {
+        const int buf = i & 1;
+        __builtin_amdgcn_s_waitcnt(0);       // this query's LDS loads (and older stores) are done
+        __syncthreads();                     // ... in every wave; buf ^ 1 is no longer read
+        if (i + 1 < np) {                    // next query's loads fly while this one is scored
+            const int qn = qi0 + static_cast<int>(s_ent[i + 1] >> 16);
+            qd.issue(a.q + static_cast<int64_t>(qn) * a.H * D, a.w + static_cast<int64_t>(qn) * a.H, a.H,
+                     s_q[buf ^ 1], s_w[buf ^ 1], wave, lane);
+        }
+        if (cand) store_tiles<NTW>(cand, v, tok0, t, lane);
+        const uint32_t e = s_ent[i];
+        const int ql = static_cast<int>(e >> 16);
+        const int slot = static_cast<int>(e & 0xffffu);
+        t = s_t[i];
+        score_tiles_lds<MT, KS, NTW>(s_q[buf], s_w[buf], kb, v, lane);
+        cand = a.cand_keys + static_cast<int64_t>(qi0 + ql) * a.cand_stride + slot * a.B + wave * kRowsPerWave;
+    }
+    store_tiles<NTW>(cand, v, tok0, t, lane);
+}
+
+template <int MT, int KS>
+hipError_t launch_bm_ks(const FusedArgs &a, dim3 grid, hipStream_t st) {
+    if (a.B == 64) return launch(kKindScoreRefine, hisa_refine_bm_kernel<MT, KS, 2>, grid, dim3(kBMThreads), 0, st, a);
+    return launch(kKindScoreRefine, hisa_refine_bm_kernel<MT, KS, 4>, grid, dim3(kBMThreads), 0, st, a);
+}
+
+template <int MT>
+hipError_t launch_bm_mt(const FusedArgs &a, dim3 grid, hipStream_t st) {
+    return a.d == 64 ? launch_bm_ks<MT, 2>(a, grid, st) : launch_bm_ks<MT, 4>(a, grid, st);
+}
+
+}  // namespace
+
+bool block_major_mode(int S, int T, int d, int64_t L, int B, int m) {
+    (void)S;
+    return T >= kChunkQueries / 2 && (B == 64 || B == 128) && m <= 65535 && fused_supported(d, L, B, m);
+}
+
+hipError_t launch_block_major_refine(const FusedArgs &a, hipStream_t st) {
+    const int64_t nchunk = bucket_chunks(a.S, a.T);
+    hipError_t e = launch(kKindBucket, hisa_bucket_kernel, dim3(static_cast<uint32_t>(nchunk)),
+                          dim3(kBucketThreads), 0, st, a);
+    if (e != hipSuccess) return e;
+    const dim3 grid(bm_grid(a.nblk, nchunk));
+    if (a.H <= 16) return launch_bm_mt<1>(a, grid, st);
+    if (a.H <= 32) return launch_bm_mt<2>(a, grid, st);
+    return launch_bm_mt<4>(a, grid, st);
+}
+
+}  // namespace hisa

@@ -14,7 +14,8 @@
 // the contraction index is the same whatever order the unit sums its slots in.
 // D[head][row] comes back as heads 4g..4g+3 of row n in each lane; the fp32
 // epilogue applies ReLU and w and sums heads: the lane's 4*MT values in a fixed
-// order with explicit fused multiply-adds, then across the four lane groups
+// order with explicit fused multiply-adds (ReLU as an integer max on the bit
+// pattern), then across the four lane groups
 // with two xor-shuffles.  Every kernel
 // calls score_rows(), so a given (query, row) gets the same fp32 bits wherever
 // it is scored.
@@ -52,26 +53,40 @@ struct QStage {
     static constexpr int kStride = D + 8;
 };
 
-// Copy q [H][D] (global) into s_q [MT*16][D+8] with zero rows past H.
+// Copy q [H][D] (global) into s_q [MT*16][D+8] with zero rows past H, in two
+// halves so that a caller can keep the loads in flight across other work:
+// load() issues every global load into registers, store() writes them to LDS.
+template <int MT, int KS, int NT>
+struct QStager {
+    static constexpr int D = QStage<KS>::D, ST = QStage<KS>::kStride;
+    static constexpr int kChunks = MT * 16 * D / 8;
+    static constexpr int kPer = (kChunks + NT - 1) / NT;
+    u32x4 v[kPer];
+
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ q, int H, int tid) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = tid + i * NT;
+            const int h = c / (D / 8);
+            v[i] = u32x4{0u, 0u, 0u, 0u};
+            if (c < kChunks && h < H) v[i] = *reinterpret_cast<const u32x4 *>(q + h * D + 8 * (c - h * (D / 8)));
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t *s_q, int tid) const {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = tid + i * NT;
+            const int h = c / (D / 8);
+            if (c < kChunks) *reinterpret_cast<u32x4 *>(s_q + h * ST + 8 * (c - h * (D / 8))) = v[i];
+        }
+    }
+};
+
 template <int MT, int KS, int NT>
 __device__ __forceinline__ void stage_query(const uint16_t *__restrict__ q, int H, uint16_t *s_q, int tid) {
-    constexpr int D = QStage<KS>::D, ST = QStage<KS>::kStride;
-    constexpr int chunks = MT * 16 * D / 8;
-    constexpr int kPer = (chunks + NT - 1) / NT;
-    u32x4 v[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {                  // every load in flight before the stores
-        const int c = tid + i * NT;
-        const int h = c / (D / 8);
-        v[i] = u32x4{0u, 0u, 0u, 0u};
-        if (c < chunks && h < H) v[i] = *reinterpret_cast<const u32x4 *>(q + h * D + 8 * (c - h * (D / 8)));
-    }
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int c = tid + i * NT;
-        const int h = c / (D / 8);
-        if (c < chunks) *reinterpret_cast<u32x4 *>(s_q + h * ST + 8 * (c - h * (D / 8))) = v[i];
-    }
+    QStager<MT, KS, NT> st;
+    st.load(q, H, tid);
+    st.store(s_q, tid);
 }
 
 template <int MT, int KS>
@@ -91,6 +106,24 @@ __device__ __forceinline__ void load_qfrag_lds(QFrag<MT, KS> &f, const uint16_t 
             const int head = 16 * mt + 4 * g + r;
             f.wv[mt][r] = head < H ? w[head] : 0.0f;
         }
+}
+
+// As load_qfrag_lds, with the head weights also read from LDS (s_w[MT*16],
+// zero past H).
+template <int MT, int KS>
+__device__ __forceinline__ void load_qfrag_lds_w(QFrag<MT, KS> &f, const uint16_t *s_q, const float *s_w,
+                                                 int lane) {
+    constexpr int ST = QStage<KS>::kStride;
+    const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            f.qa[mt][ks] = load_bf16x8(s_q + (16 * mt + n) * ST + 32 * ks + 8 * g);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f.wv[mt][r] = s_w[16 * mt + 4 * g + r];
 }
 
 template <int MT, int KS>
@@ -123,6 +156,13 @@ __device__ __forceinline__ void load_row_frag(bf16x8 (&kb)[KS], const uint16_t *
         kb[ks] = row ? load_bf16x8(row + 32 * ks + 8 * g) : zero_bf16x8();
 }
 
+// max(x, 0) for finite x, as one integer max on the bit pattern: every
+// negative value (and -0) has a negative two's-complement pattern and becomes
+// +0; non-negative values pass unchanged.
+__device__ __forceinline__ float relu_bits(float x) {
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // Score of row (lane & 15) for this query; every lane of the row's column
 // group returns the same value.
 template <int MT, int KS>
@@ -135,11 +175,52 @@ __device__ __forceinline__ float score_rows(const QFrag<MT, KS> &f, const bf16x8
         for (int ks = 0; ks < KS; ++ks)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.qa[mt][ks], kb[ks], acc, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part = __builtin_fmaf(f.wv[mt][r], fmaxf(acc[r], 0.0f), part);
+        for (int r = 0; r < 4; ++r) part = __builtin_fmaf(f.wv[mt][r], relu_bits(acc[r]), part);
     }
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
     return part;
+}
+
+// NT 16-row tiles of one query at once, q and w read from LDS (padded layout
+// of QStage, w zero past H).  Per tile the arithmetic is exactly score_rows():
+// the same MFMA sequence per head group and the same fused multiply-add order
+// over heads, then the same two xor-shuffles.  Working one head group at a
+// time over all tiles keeps NT accumulators in flight (independent MFMA
+// chains) and needs only one head group's fragments in registers.
+template <int MT, int KS, int NT>
+__device__ __forceinline__ void score_tiles_lds(const uint16_t *s_q, const float *s_w,
+                                                const bf16x8 (&kb)[NT][KS], float (&out)[NT], int lane) {
+    constexpr int ST = QStage<KS>::kStride;
+    const int n = lane & 15, g = lane >> 4;
+    float part[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) part[nt] = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        bf16x8 qa[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qa[ks] = load_bf16x8(s_q + (16 * mt + n) * ST + 32 * ks + 8 * g);
+        float wv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wv[r] = s_w[16 * mt + 4 * g + r];
+        f32x4 acc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb[nt][ks], acc[nt], 0, 0, 0);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part[nt] = __builtin_fmaf(wv[r], relu_bits(acc[nt][r]), part[nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) part[nt] += __shfl_xor(part[nt], 16);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) out[nt] = part[nt] + __shfl_xor(part[nt], 32);
 }
 
 }  // namespace hisa

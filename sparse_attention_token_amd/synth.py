@@ -127,7 +127,7 @@ def clustered_case(S, L, T, H, d, B, m, k, seed, qpos=None, latent_block=128, w_
     for s in range(S):
         K[s] += np.float32(0.6) * np.repeat(z[s], latent_block, axis=0)[:L]
     qp = _default_qpos(S, T, L) if qpos is None else np.asarray(qpos, dtype=np.int32).reshape(S, T)
-    nlat_q = qp.astype(np.int64) // latent_block + 1              # latent blocks visible to each query
+    nlat_q = np.clip(qp.astype(np.int64), 0, L - 1) // latent_block + 1   # latent blocks visible to each query
     lat = rng.integers(0, nlat_q[..., None], size=(S, T, 3))
     q = rng.standard_normal((S, T, H, d), dtype=np.float32)
     sidx = np.arange(S)[:, None, None]

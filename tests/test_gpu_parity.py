@@ -179,6 +179,36 @@ def test_prefill_chunk_small(hisa, orc):
     _say(f"prefill small: {rep}")
 
 
+BLOCK_MAJOR = [
+    # name, S, L, T, H, d, B, m, k: at least 128 queries per sequence refine
+    # block by block, in chunks of 256 queries (ragged last chunk)
+    ("bm_h16_d64_B64", 2, 3000, 200, 16, 64, 64, 5, 200),
+    ("bm_h40_d128_B128", 1, 5077, 520, 40, 128, 128, 8, 300),
+    ("bm_h64_d128_B128_padk", 1, 2100, 130, 64, 128, 128, 3, 500),
+    # 9 chunks (3 sequences x 3): chunks are spread over the XCDs by chunk id
+    ("bm_9chunks_xcd_map", 3, 1500, 700, 8, 64, 64, 4, 64),
+]
+
+
+@pytest.mark.parametrize("spec", BLOCK_MAJOR, ids=[s[0] for s in BLOCK_MAJOR])
+def test_block_major_refine(hisa, orc, spec):
+    name, S, L, T, H, d, B, m, k = spec
+    _say(f"block-major case {name}")
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    qpos = rng.integers(0, L, size=(S, T)).astype(np.int32)
+    qpos[0, :8] = [0, B - 1, B, L - 1, L - 2, -1, L, 2 * B + 1]   # edges and two out-of-range positions
+    c = synth.clustered_case(S, L, T, H, d, B, m, k, seed=11, qpos=qpos, latent_block=B)
+    out = _run(hisa, c, want_flat=False)
+    rep = {}
+    for s in range(S):
+        for i in range(T):
+            if not 0 <= qpos[s, i] < L:
+                assert np.all(out["idx"][s, i] == -1) and np.all(out["blk"][s, i] == -1)
+                continue
+            check_hisa_row(orc, c, s, i, out["idx"][s, i], out["sc"][s, i], out["blk"][s, i], rep)
+    _say(f"  {rep}")
+
+
 def test_keep_all_blocks_equals_flat_bitwise(hisa):
     # with m >= number of blocks, HISA keeps every token <= t, and the shared
     # scorer gives identical fp32 scores: the outputs must match bit for bit
@@ -186,6 +216,16 @@ def test_keep_all_blocks_equals_flat_bitwise(hisa):
                              qpos=[[0, 63, 64, 700, 1499], [5, 127, 128, 1000, 1400]], latent_block=64)
     c.m = -(-c.L // c.B)
     out = _run(hisa, c)
+    np.testing.assert_array_equal(out["idx"], out["fidx"])
+    np.testing.assert_array_equal(out["sc"].view(np.uint32), out["fsc"].view(np.uint32))
+
+
+def test_block_major_keep_all_equals_flat_bitwise(hisa):
+    # the block-by-block refinement (many queries per sequence) scores every
+    # (query, row) with the same arithmetic as the flat indexer
+    c = synth.clustered_case(1, 2000, 140, 64, 128, 64, 1, 200, seed=9, latent_block=64)
+    c.m = -(-c.L // c.B)
+    out = _run(hisa, c, qpos_on_device=False)
     np.testing.assert_array_equal(out["idx"], out["fidx"])
     np.testing.assert_array_equal(out["sc"].view(np.uint32), out["fsc"].view(np.uint32))
 
