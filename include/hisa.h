@@ -109,13 +109,12 @@ HISA_API size_t hisa_index_workspace(int S, int T, int H, int d, int64_t L, int 
  *   w        fp32 [S][T][H]     per-head weights
  *   qpos     int32 [S][T] or NULL; NULL means t = L - T + i for query i.
  *   K        key cache, layout as in hisa_pool_append; rows [0, L) are read.
- *   pool_mean block means as left by hisa_pool_append(); every block
- *            b < floor(t/B) must be current.  The pool entry of the query's own
- *            block floor(t/B) is never read: its representative, the mean of
- *            rows [floor(t/B)*B, t], is recomputed from K with the same
- *            arithmetic.  So the hisa_pool_append() of the newest rows may run
- *            concurrently with (on another stream than) the hisa_index() that
- *            queries them.
+ *   pool_mean block means as left by hisa_pool_append(): the pool must be
+ *            current through row L-1 (hisa_pool_append() with L_new = L has
+ *            completed, e.g. earlier on the same stream).  The representative
+ *            of a query's own block floor(t/B) is the mean of rows
+ *            [floor(t/B)*B, t]: for t = L-1 that is exactly the pool entry;
+ *            for any other t it is recomputed from K with the same arithmetic.
  *   Steps per query (t = its position, b_t = floor(t/B)):
  *     1. sigma_b = s(q, w, mean_b) for b = 0..b_t                      (fp32)
  *     2. M = top min(m, b_t+1) blocks by (sigma desc, b asc)

@@ -18,8 +18,8 @@
 //      one wave when b_t + 1 <= 2048 (no barriers), by the whole workgroup
 //      otherwise.
 // Two ways to run it, chosen by the host:
-//  * decode (few queries): hisa_decode_kernel -- one 4-wave workgroup per 128
-//    candidate positions of a query (position p = slot*B + r: row r of the
+//  * decode (few queries): hisa_decode_kernel -- one 4-wave workgroup per 256
+//    (or, with few queries, 128) candidate positions of a query (position p = slot*B + r: row r of the
 //    slot-th kept block, masked past t).  Each workgroup repeats its query's
 //    block stage (the pooled means it reads are shared through L2) and then
 //    scores its 128 rows: one launch, no communication between workgroups.
@@ -46,6 +46,9 @@ constexpr int kK2Threads = 256;
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeMaxM = 1024;                         // kept blocks staged in LDS (decode mode)
 constexpr int kDecodeMaxQueries = 32;                     // decode mode repeats the block stage per tile
+constexpr int kDecodeRowsWide = 256;                      // candidate rows per decode workgroup, big grids
+constexpr int kDecodeRowsNarrow = 128;                    // ... and when fewer than kDecodeWideMin would run
+constexpr int kDecodeWideMin = 256;
 
 // LDS slot of block position p: the keys are stored so that the select's
 // owner of a contiguous run of positions reads it as conflict-free rows.
@@ -58,14 +61,13 @@ __device__ __forceinline__ int k1_slot(int p, int nb) {
 }
 
 template <int R, typename Emit>
-__device__ __forceinline__ uint32_t k1_wave_select(const uint32_t *s_keys, int nb, int m, uint32_t *hist,
-                                                   Emit &emit) {
+__device__ __forceinline__ uint32_t k1_wave_select(const uint32_t *s_keys, int nb, int m, Emit &emit) {
     const int lane = threadIdx.x & 63;
     const int rd = (nb + 63) / 64;
     uint32_t kv[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) kv[r] = (r < rd && lane * rd + r < nb) ? s_keys[r * 64 + lane] : kNoCandidate;
-    const SelectResult res = wave_radix_select<R>(kv, static_cast<uint32_t>(m), hist);
+    const SelectResult res = wave_ballot_select<R>(kv, static_cast<uint32_t>(m));
     if (res.keff > 0)
         wave_compact<R>(kv, res, [&](uint32_t op, int r, uint32_t) { emit(op, lane * rd + r); });
     return res.keff;
@@ -73,9 +75,9 @@ __device__ __forceinline__ uint32_t k1_wave_select(const uint32_t *s_keys, int n
 
 template <int KS, int NT>
 struct BlockStageLds {
-    static constexpr int kOwnWords = kFusedOwnElems / 2 > kWaveHistWords ? kFusedOwnElems / 2 : kWaveHistWords;
+    static constexpr int kOwnWords = kFusedOwnElems / 2;
     uint16_t q[64 * QStage<KS>::kStride];
-    uint32_t own[kOwnWords];            // own-block rows; then the one-wave select's histograms
+    uint32_t own[kOwnWords];            // own-block rows
     uint16_t mean[128];
 };
 
@@ -83,7 +85,10 @@ struct BlockStageLds {
 // k1_slot) and leaves the query fragments in f.  NT threads; each wave loads
 // TB pool tiles at a time (the first batch before anything else, so that HBM
 // latency overlaps the staging of q and of the own-block rows); ends with a
-// barrier.
+// barrier.  For the query at the cache's last row (t = L-1) the pool entry of
+// its own block is already the mean of rows b_t*B .. t (the pool is current
+// through row L-1), so it is scored like the others; any other query's own
+// block is recomputed from K.
 template <int MT, int KS, int NT, int TB>
 __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, int64_t t,
                                             BlockStageLds<KS, NT> &L, uint32_t *s_keys,
@@ -96,11 +101,12 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
     const int nb = static_cast<int>(bt + 1);
     const int64_t r0 = bt * a.B;
     const int own_rows = static_cast<int>(t + 1 - r0);
+    const bool own_in_pool = t == a.L - 1;
     uint16_t *s_own = reinterpret_cast<uint16_t *>(L.own);
 
-    // complete blocks b < b_t from the pool, 16 per tile, tile i on wave i % NW
+    // pool rows 0 .. full-1, 16 per tile, tile i on wave i % NW
     const uint16_t *pool = a.pool + s * a.pool_seq_stride;
-    const int full = static_cast<int>(bt);
+    const int full = own_in_pool ? nb : static_cast<int>(bt);
     const int ntiles = (full + 15) / 16;
     bf16x8 kb[TB][KS];
 #pragma unroll
@@ -108,7 +114,7 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
         const int p = (wave + u * NW) * 16 + n;
         load_row_frag<KS>(kb[u], p < full ? pool + static_cast<int64_t>(p) * D : nullptr, lane);
     }
-    {   // own-block rows: every load in flight before the first LDS store
+    if (!own_in_pool) {   // own-block rows: every load in flight before the first LDS store
         constexpr int kPer = (kFusedOwnElems / 8 + NT - 1) / NT;   // 16-byte chunks per thread
         const int chunks = own_rows * D / 8;
         const u32x4 *src = reinterpret_cast<const u32x4 *>(a.K + s * a.k_seq_stride + r0 * D);
@@ -144,42 +150,43 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
         }
     }
 
-    // own-block representative: the mean of rows b_t*B .. t, one column per
-    // thread, rows in order, fp64; then wave 0 scores it
-    if (tid < D) {
-        double sum = 0.0;
-        int r = 0;
-        for (; r + 8 <= own_rows; r += 8) {            // 8 LDS reads in flight per step
-            float x[8];
+    if (!own_in_pool) {
+        // own-block representative: the mean of rows b_t*B .. t, one column
+        // per thread, rows in order, fp64; then wave 0 scores it
+        if (tid < D) {
+            double sum = 0.0;
+            int r = 0;
+            for (; r + 8 <= own_rows; r += 8) {            // 8 LDS reads in flight per step
+                float x[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] = bf16_to_f32(s_own[(r + j) * D + tid]);
+                for (int j = 0; j < 8; ++j) x[j] = bf16_to_f32(s_own[(r + j) * D + tid]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sum += static_cast<double>(x[j]);
+                for (int j = 0; j < 8; ++j) sum += static_cast<double>(x[j]);
+            }
+            for (; r < own_rows; ++r) sum += static_cast<double>(bf16_to_f32(s_own[r * D + tid]));
+            L.mean[tid] = f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(own_rows)));
         }
-        for (; r < own_rows; ++r) sum += static_cast<double>(bf16_to_f32(s_own[r * D + tid]));
-        L.mean[tid] = f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(own_rows)));
-    }
-    __syncthreads();
-    if (wave == 0) {
-        bf16x8 kbm[KS];
+        __syncthreads();
+        if (wave == 0) {
+            bf16x8 kbm[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kbm[ks] = n == 0 ? load_bf16x8(L.mean + 32 * ks + 8 * g) : zero_bf16x8();
-        const float v = score_rows<MT, KS>(f, kbm);
-        if (lane == 0) s_keys[k1_slot(nb - 1, nb)] = score_to_key(v);
+            for (int ks = 0; ks < KS; ++ks) kbm[ks] = n == 0 ? load_bf16x8(L.mean + 32 * ks + 8 * g) : zero_bf16x8();
+            const float v = score_rows<MT, KS>(f, kbm);
+            if (lane == 0) s_keys[k1_slot(nb - 1, nb)] = score_to_key(v);
+        }
     }
     __syncthreads();
 }
 
 // One wave selects the top m of the nb <= 2048 block keys; emit(slot, block).
 template <typename Emit>
-__device__ __forceinline__ uint32_t block_topm_wave(const uint32_t *s_keys, int nb, int m, uint32_t *hist,
-                                                    Emit &&emit) {
+__device__ __forceinline__ uint32_t block_topm_wave(const uint32_t *s_keys, int nb, int m, Emit &&emit) {
     const int rd = (nb + 63) / 64;
     uint32_t ke;
-    if (rd <= 4) ke = k1_wave_select<4>(s_keys, nb, m, hist, emit);
-    else if (rd <= 8) ke = k1_wave_select<8>(s_keys, nb, m, hist, emit);
-    else if (rd <= 16) ke = k1_wave_select<16>(s_keys, nb, m, hist, emit);
-    else ke = k1_wave_select<32>(s_keys, nb, m, hist, emit);
+    if (rd <= 4) ke = k1_wave_select<4>(s_keys, nb, m, emit);
+    else if (rd <= 8) ke = k1_wave_select<8>(s_keys, nb, m, emit);
+    else if (rd <= 16) ke = k1_wave_select<16>(s_keys, nb, m, emit);
+    else ke = k1_wave_select<32>(s_keys, nb, m, emit);
     return ke;
 }
 
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(kK1Threads) void hisa_blocks_topm_kernel(FusedArgs 
     if (nb <= kK1WaveMax) {
         // short rows: one wave, no barriers
         if (wave == 0) {
-            const uint32_t ke = block_topm_wave(s_keys, nb, a.m, L.own, [&](uint32_t op, int pos) {
+            const uint32_t ke = block_topm_wave(s_keys, nb, a.m, [&](uint32_t op, int pos) {
                 sel[op] = pos;
                 if (ob) ob[op] = pos;
             });
@@ -239,12 +246,14 @@ __global__ __launch_bounds__(kK1Threads) void hisa_blocks_topm_kernel(FusedArgs 
     }
 }
 
-// Decode mode: grid (ceil(m*B/128), S*T), 256 threads (two workgroups fit a
-// CU).  Block stage, top-m into LDS, then the workgroup's 128 candidate rows
-// (two 16-row tiles per wave).
-template <int MT, int KS>
+// Decode mode: grid (ceil(m*B/ROWS), S*T), 256 threads.  Block stage, top-m
+// into LDS, then the workgroup's ROWS candidate rows (ROWS/64 16-row tiles per
+// wave).  Wider workgroups repeat the block stage less often; narrow ones keep
+// every CU busy when there are few queries.
+template <int MT, int KS, int ROWS>
 __global__ __launch_bounds__(kDecodeThreads) void hisa_decode_kernel(FusedArgs a) {
     constexpr int D = 32 * KS;
+    constexpr int NTW = ROWS / (16 * kDecodeThreads / 64);
     __shared__ __attribute__((aligned(16))) BlockStageLds<KS, kDecodeThreads> L;
     __shared__ __attribute__((aligned(16))) uint32_t s_keys[kK1WaveMax];        // by k1_slot()
     __shared__ int32_t s_sel[kDecodeMaxM];
@@ -270,13 +279,13 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_decode_kernel(FusedArgs a
     const int nb = static_cast<int>(bt + 1);
     const int meff = a.m < nb ? a.m : nb;
     const int npos = meff * a.B;
-    const int tile0 = blockIdx.x * 128;
+    const int tile0 = blockIdx.x * ROWS;
     if (tile0 >= npos) return;
 
     QFrag<MT, KS> f;
     block_stage<MT, KS, kDecodeThreads, 4>(a, qi, s, t, L, s_keys, f);
     if (wave == 0) {
-        const uint32_t ke = block_topm_wave(s_keys, nb, a.m, L.own, [&](uint32_t op, int pos) {
+        const uint32_t ke = block_topm_wave(s_keys, nb, a.m, [&](uint32_t op, int pos) {
             s_sel[op] = pos;
             if (lead) {
                 sel[op] = pos;
@@ -292,27 +301,29 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_decode_kernel(FusedArgs a
             if (ob) ob[j] = -1;
         }
 
-    // this workgroup's 128 candidate rows: two 16-row tiles per wave, both
-    // loads in flight before either is scored
-    bf16x8 kb[2][KS];
-    const uint16_t *row[2];
+    // this workgroup's candidate rows: NTW 16-row tiles per wave, every load
+    // in flight before any is scored
+    bf16x8 kb[NTW][KS];
+    bool valid[NTW];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int p = tile0 + wave * 32 + nt * 16 + n;
-        row[nt] = nullptr;
+    for (int nt = 0; nt < NTW; ++nt) {
+        const int p = tile0 + (wave * NTW + nt) * 16 + n;
+        const uint16_t *row = nullptr;
         if (p < npos) {
             const int slot = p / a.B;
             const int64_t tok = static_cast<int64_t>(s_sel[slot]) * a.B + (p - slot * a.B);
-            if (tok <= t) row[nt] = a.K + s * a.k_seq_stride + tok * D;
+            if (tok <= t) row = a.K + s * a.k_seq_stride + tok * D;
         }
-        load_row_frag<KS>(kb[nt], row[nt], lane);
+        valid[nt] = row != nullptr;
+        load_row_frag<KS>(kb[nt], row, lane);
     }
+    float v[NTW];
+    score_tiles_frag<MT, KS, NTW>(f, kb, v);
+    uint32_t *cand = a.cand_keys + static_cast<int64_t>(qi) * a.cand_stride;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int p = tile0 + wave * 32 + nt * 16 + n;
-        const float v = score_rows<MT, KS>(f, kb[nt]);
-        if (g == 0 && p < npos)
-            a.cand_keys[static_cast<int64_t>(qi) * a.cand_stride + p] = row[nt] ? score_to_key(v) : kNoCandidate;
+    for (int nt = 0; nt < NTW; ++nt) {
+        const int p = tile0 + (wave * NTW + nt) * 16 + n;
+        if (g == 0 && p < npos) cand[p] = valid[nt] ? score_to_key(v[nt]) : kNoCandidate;
     }
 }
 
@@ -366,7 +377,16 @@ template <int MT, int KS>
 hipError_t launch_fused_ks(const FusedArgs &a, bool decode, hipStream_t st) {
     const int nq = a.S * a.T;
     const dim3 g2(static_cast<uint32_t>((static_cast<int64_t>(a.m) * a.B + 127) / 128), nq);
-    if (decode) return launch(kKindIndexDecode, hisa_decode_kernel<MT, KS>, g2, dim3(kDecodeThreads), 0, st, a);
+    if (decode) {
+        const int64_t mb = static_cast<int64_t>(a.m) * a.B;
+        const int64_t wide = (mb + kDecodeRowsWide - 1) / kDecodeRowsWide;
+        if (wide * nq >= kDecodeWideMin)
+            return launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsWide>,
+                          dim3(static_cast<uint32_t>(wide), nq), dim3(kDecodeThreads), 0, st, a);
+        const int64_t narrow = (mb + kDecodeRowsNarrow - 1) / kDecodeRowsNarrow;
+        return launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsNarrow>,
+                      dim3(static_cast<uint32_t>(narrow), nq), dim3(kDecodeThreads), 0, st, a);
+    }
     const hipError_t e = launch(kKindScoreBlocks, hisa_blocks_topm_kernel<MT, KS>, dim3(nq), dim3(kK1Threads), 0, st, a);
     if (e != hipSuccess) return e;
     if (a.bucket_off) return launch_block_major_refine(a, st);

@@ -182,6 +182,35 @@ __device__ __forceinline__ float score_rows(const QFrag<MT, KS> &f, const bf16x8
     return part;
 }
 
+// NT 16-row tiles of one query at once with the fragments in registers; per
+// tile the arithmetic is exactly score_rows(), with NT accumulators in flight.
+template <int MT, int KS, int NT>
+__device__ __forceinline__ void score_tiles_frag(const QFrag<MT, KS> &f, const bf16x8 (&kb)[NT][KS],
+                                                 float (&out)[NT]) {
+    float part[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) part[nt] = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.qa[mt][ks], kb[nt][ks], acc[nt], 0, 0, 0);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part[nt] = __builtin_fmaf(f.wv[mt][r], relu_bits(acc[nt][r]), part[nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) part[nt] += __shfl_xor(part[nt], 16);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) out[nt] = part[nt] + __shfl_xor(part[nt], 32);
+}
+
 // NT 16-row tiles of one query at once, q and w read from LDS (padded layout
 // of QStage, w zero past H).  Per tile the arithmetic is exactly score_rows():
 // the same MFMA sequence per head group and the same fused multiply-add order

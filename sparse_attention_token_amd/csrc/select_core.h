@@ -182,69 +182,34 @@ __device__ __forceinline__ void block_compact(const uint32_t (&kv)[R], const Sel
 
 // ---------------------------------------------------------------- one wave
 // Exact select for short rows (n <= 64*R), run by a single wave with no
-// workgroup barriers: lane l holds positions [l*Rd, l*Rd + Rd) of the row in
-// kv[0..Rd).  Four passes over 8-bit digits.  Each pass has its own LDS
-// histogram kept as 8 copies (copy = lane & 7), so at most 8 lanes of one
-// atomic instruction share an address; lane l then reads bins 4l..4l+3 of
-// every copy with 16-byte loads (conflict-free), a DPP prefix sum gives the
-// count above each lane, and a ballot picks the lane holding the rank.
-constexpr int kWaveHistRow = 260;                       // 256 bins + pad: copies start 4 banks apart
-constexpr int kWaveHistWords = 4 * 8 * kWaveHistRow;    // 4 passes x 8 copies
-
-// hist: kWaveHistWords words of LDS, 16-byte aligned; cleared here unless
-// the caller already zeroed them (cleared == false means "already zero").
+// workgroup barriers and no LDS: lane l holds positions [l*Rd, l*Rd + Rd) of
+// the row in kv[0..Rd).  The cutoff key K* (the largest v with
+// #{key >= v} >= k_eff) is found bit by bit from the top: for each candidate
+// prefix the wave counts the keys at or above it with one ballot and one
+// population count per register, all on scalar registers -- at most 32
+// short dependent steps instead of histogram passes through LDS.  The search
+// stops as soon as exactly k_eff keys lie at or above the candidate.
 template <int R>
-__device__ __forceinline__ SelectResult wave_radix_select(const uint32_t (&kv)[R], uint32_t kout,
-                                                          uint32_t *hist, bool clear = true) {
-    const int lane = threadIdx.x & 63;
-    if (clear)
-        for (int w = lane * 4; w < kWaveHistWords; w += 64 * 4)
-            *reinterpret_cast<sel_u32x4 *>(&hist[w]) = sel_u32x4{0u, 0u, 0u, 0u};
-    uint32_t prefix = 0, mask = 0, need = 0, keff = 0;
+__device__ __forceinline__ SelectResult wave_ballot_select(const uint32_t (&kv)[R], uint32_t kout) {
+    uint32_t nvalid = 0;
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        uint32_t *h = hist + pass * 8 * kWaveHistRow;
-        uint32_t *hc = h + (lane & 7) * kWaveHistRow;
+    for (int r = 0; r < R; ++r) nvalid += static_cast<uint32_t>(__popcll(__ballot(kv[r] != kNoCandidate)));
+    const uint32_t keff = nvalid < kout ? nvalid : kout;
+    if (keff == 0) return SelectResult{0u, 0u, 0u};
+    uint32_t prefix = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = prefix | (1u << bit);
+        uint32_t cnt = 0;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint32_t key = kv[r];
-            if (key != kNoCandidate && (key & mask) == prefix) atomicAdd(&hc[(key >> shift) & 255u], 1u);
-        }
-        uint32_t hb[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const sel_u32x4 x = *reinterpret_cast<const sel_u32x4 *>(&h[c * kWaveHistRow + 4 * lane]);
-            hb[0] += x[0]; hb[1] += x[1]; hb[2] += x[2]; hb[3] += x[3];
-        }
-        const uint32_t cnt = hb[0] + hb[1] + hb[2] + hb[3];
-        const uint32_t incl = wave_prefix_incl(cnt);            // bins of lanes <= l
-        const uint32_t total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
-        if (pass == 0) {
-            keff = total < kout ? total : kout;
-            need = keff;
-            if (keff == 0) return SelectResult{0u, 0u, 0u};
-        }
-        uint32_t above = total - incl;                          // bins of lanes > l
-        uint32_t my_digit = 0, my_above = 0;
-        const bool holds = above < need && above + cnt >= need;
-#pragma unroll
-        for (int j = 3; j >= 0; --j) {
-            if (holds && above < need && above + hb[j] >= need) {
-                my_digit = static_cast<uint32_t>(4 * lane + j);
-                my_above = above;
-            }
-            above += hb[j];
-        }
-        const uint64_t ball = __ballot(holds);
-        const int src = __builtin_ctzll(ball);
-        const uint32_t digit = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(my_digit), src));
-        const uint32_t above_d = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(my_above), src));
-        prefix |= digit << shift;
-        mask |= 0xFFu << shift;
-        need -= above_d;
+        for (int r = 0; r < R; ++r) cnt += static_cast<uint32_t>(__popcll(__ballot(kv[r] >= cand)));
+        // exactly k_eff keys at or above cand: they are the kept set (keys > cand - 1)
+        if (cnt == keff) return SelectResult{cand - 1u, 0u, keff};
+        if (cnt > keff) prefix = cand;
     }
-    return SelectResult{prefix, need, keff};
+    uint32_t gt = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) gt += static_cast<uint32_t>(__popcll(__ballot(kv[r] > prefix)));
+    return SelectResult{prefix, keff - gt, keff};
 }
 
 template <int R, typename Emit>
