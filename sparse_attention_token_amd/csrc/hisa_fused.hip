@@ -77,6 +77,7 @@ template <int KS, int NT>
 struct BlockStageLds {
     static constexpr int kOwnWords = kFusedOwnElems / 2;
     uint16_t q[64 * QStage<KS>::kStride];
+    float w[64];                        // head weights, zero past H
     uint32_t own[kOwnWords];            // own-block rows
     uint16_t mean[128];
 };
@@ -128,9 +129,10 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
             if (tid + i * NT < chunks) dst[tid + i * NT] = v[i];
     }
     stage_query<MT, KS, NT>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, L.q, tid);
+    if (tid < 64) L.w[tid] = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
     __syncthreads();
 
-    load_qfrag_lds<MT, KS>(f, L.q, a.w + static_cast<int64_t>(qi) * a.H, a.H, lane);
+    load_qfrag_lds_w<MT, KS>(f, L.q, L.w, lane);
     for (int base = wave; base < ntiles; base += TB * NW) {
         if (base != wave) {
 #pragma unroll
@@ -246,7 +248,37 @@ __global__ __launch_bounds__(kK1Threads) void hisa_blocks_topm_kernel(FusedArgs 
     }
 }
 
-// Decode mode: grid (ceil(m*B/ROWS), S*T), 256 threads.  Block stage, top-m
+// Workgroup -> (query qi, tile) in decode mode, tiles = ceil(m*B/ROWS) per
+// query.  Workgroups are dealt to the 8 XCDs in turn (linear id i goes to XCD
+// i % 8), so the mapping keeps each query's workgroups on as few XCDs as
+// possible: all of them share that L2's copy of the query, its pooled means
+// and its gathered rows.  qi = -1: nothing to do.
+__host__ __device__ inline int decode_grid(int nq, int tiles) {
+    if (nq % 8 == 0) return nq * tiles;
+    if (8 % nq == 0) {
+        const int per = 8 / nq;                      // XCDs per query
+        return 8 * ((tiles + per - 1) / per);
+    }
+    return nq * tiles;
+}
+
+__device__ __forceinline__ void decode_tile(int nq, int tiles, int &qi, int &tile) {
+    const int i = blockIdx.x, x = i & 7, j = i >> 3;
+    if (nq % 8 == 0) {
+        qi = x + 8 * (j / tiles);
+        tile = j - (j / tiles) * tiles;
+    } else if (8 % nq == 0) {
+        const int per = 8 / nq;
+        qi = x % nq;
+        tile = j * per + x / nq;
+        if (tile >= tiles) qi = -1;
+    } else {
+        qi = i / tiles;
+        tile = i - qi * tiles;
+    }
+}
+
+// Decode mode: grid decode_grid(S*T, ceil(m*B/ROWS)), 256 threads.  Block stage, top-m
 // into LDS, then the workgroup's ROWS candidate rows (ROWS/64 16-row tiles per
 // wave).  Wider workgroups repeat the block stage less often; narrow ones keep
 // every CU busy when there are few queries.
@@ -261,10 +293,12 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_decode_kernel(FusedArgs a
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
-    const int qi = blockIdx.y;
+    int qi, tile;
+    decode_tile(a.S * a.T, static_cast<int>((static_cast<int64_t>(a.m) * a.B + ROWS - 1) / ROWS), qi, tile);
+    if (qi < 0) return;
     const int s = qi / a.T;
     const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
-    const bool lead = blockIdx.x == 0;      // also publishes the kept blocks
+    const bool lead = tile == 0;            // also publishes the kept blocks
     int32_t *sel = a.sel_blk + static_cast<int64_t>(qi) * a.m;
     int32_t *ob = a.out_blk ? a.out_blk + static_cast<int64_t>(qi) * a.m : nullptr;
     if (t < 0) {
@@ -279,7 +313,7 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_decode_kernel(FusedArgs a
     const int nb = static_cast<int>(bt + 1);
     const int meff = a.m < nb ? a.m : nb;
     const int npos = meff * a.B;
-    const int tile0 = blockIdx.x * ROWS;
+    const int tile0 = tile * ROWS;
     if (tile0 >= npos) return;
 
     QFrag<MT, KS> f;
@@ -379,13 +413,13 @@ hipError_t launch_fused_ks(const FusedArgs &a, bool decode, hipStream_t st) {
     const dim3 g2(static_cast<uint32_t>((static_cast<int64_t>(a.m) * a.B + 127) / 128), nq);
     if (decode) {
         const int64_t mb = static_cast<int64_t>(a.m) * a.B;
-        const int64_t wide = (mb + kDecodeRowsWide - 1) / kDecodeRowsWide;
-        if (wide * nq >= kDecodeWideMin)
+        const int wide = static_cast<int>((mb + kDecodeRowsWide - 1) / kDecodeRowsWide);
+        if (static_cast<int64_t>(wide) * nq >= kDecodeWideMin)
             return launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsWide>,
-                          dim3(static_cast<uint32_t>(wide), nq), dim3(kDecodeThreads), 0, st, a);
-        const int64_t narrow = (mb + kDecodeRowsNarrow - 1) / kDecodeRowsNarrow;
+                          dim3(static_cast<uint32_t>(decode_grid(nq, wide))), dim3(kDecodeThreads), 0, st, a);
+        const int narrow = static_cast<int>((mb + kDecodeRowsNarrow - 1) / kDecodeRowsNarrow);
         return launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsNarrow>,
-                      dim3(static_cast<uint32_t>(narrow), nq), dim3(kDecodeThreads), 0, st, a);
+                      dim3(static_cast<uint32_t>(decode_grid(nq, narrow))), dim3(kDecodeThreads), 0, st, a);
     }
     const hipError_t e = launch(kKindScoreBlocks, hisa_blocks_topm_kernel<MT, KS>, dim3(nq), dim3(kK1Threads), 0, st, a);
     if (e != hipSuccess) return e;

@@ -230,6 +230,32 @@ def test_block_major_keep_all_equals_flat_bitwise(hisa):
     np.testing.assert_array_equal(out["sc"].view(np.uint32), out["fsc"].view(np.uint32))
 
 
+def test_many_equal_scores(hisa, orc):
+    # thousands of identical keys (equal scores) plus a few distinct ones: the
+    # boundary of the top k falls inside one huge group of ties, which the
+    # selection resolves by index (and its range histogram cannot split)
+    import dataclasses
+
+    c = synth.gaussian_case(1, 6000, 4, 8, 64, 64, 94, 3000, seed=3, qpos=[[5999, 4000, 2500, 700]])
+    K = c.K.copy()
+    rng = np.random.default_rng(5)
+    keep = rng.choice(6000, size=40, replace=False)
+    K[0, :] = K[0, 17]
+    K[0, keep] = c.K[0, keep]
+    c = dataclasses.replace(c, K=K)
+    out = _run(hisa, c)
+    rep = {}
+    for i in range(c.T):
+        check_hisa_row(orc, c, 0, i, out["idx"][0, i], out["sc"][0, i], out["blk"][0, i], rep)
+        check_flat_row(orc, c, 0, i, out["fidx"][0, i], out["fsc"][0, i], rep)
+        # equal rows give bitwise-equal scores on both sides, so the tie rule
+        # (lowest index first) fixes the set exactly: no cutoff leniency here
+        o_idx, _, _ = orc.flat_query(c.q[0, i], c.w[0, i], c.K[0], int(c.qpos[0, i]), c.k)
+        np.testing.assert_array_equal(np.sort(out["fidx"][0, i]), np.sort(o_idx))
+        np.testing.assert_array_equal(np.sort(out["idx"][0, i]), np.sort(o_idx))
+    _say(f"many ties: {rep}")
+
+
 def test_out_of_range_positions_select_nothing(hisa):
     import torch
 
