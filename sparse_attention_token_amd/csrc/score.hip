@@ -21,8 +21,10 @@
 // (query, row) gets the same fp32 bits from the block stage, the refinement
 // and the flat indexer.
 //
-// Work split: one workgroup = 4 waves = one 128-row tile of one query; each
-// wave owns two N-tiles (32 rows).  Every lane loads its own 16-byte slices of
+// Work split (blocks and refine modes, and the general path): one workgroup =
+// 4 waves = one 128-row tile of one query; each wave owns two N-tiles (32
+// rows).  The flat indexer streams longer runs per workgroup
+// (score_flat_kernel).  Every lane loads its own 16-byte slices of
 // q and of its rows straight into registers; the row loads are issued first.
 // The 16-row scoring step is score_rows() of scorer.h, shared with the fused
 // HISA kernels.
@@ -110,6 +112,77 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     }
 }
 
+// Flat indexer: one workgroup streams a run of `rows_per_wg` keys of one
+// query (a multiple of 128).  q and w are staged in LDS once and held as
+// register fragments; each wave scores two 16-row tiles per 128-row step while
+// the next step's rows are already in flight (two register buffers).  The
+// per-row arithmetic is score_rows()'s, so the scores equal the other
+// kernels' bit for bit.
+constexpr int kFlatThreads = 256;
+
+template <int MT, int KS>
+__device__ __forceinline__ void flat_load(bf16x8 (&kb)[kNT][KS], const uint16_t *Ks, int64_t base, int64_t npos,
+                                          int lane) {
+    constexpr int D = 32 * KS;
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const int64_t p = base + nt * 16 + (lane & 15);
+        load_row_frag<KS>(kb[nt], p < npos ? Ks + p * D : nullptr, lane);
+    }
+}
+
+template <int MT, int KS>
+__device__ __forceinline__ void flat_score_store(const QFrag<MT, KS> &f, const bf16x8 (&kb)[kNT][KS],
+                                                 uint32_t *keys, int64_t base, int64_t npos, int lane) {
+    float v[kNT];
+    score_tiles_frag<MT, KS, kNT>(f, kb, v);
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const int64_t p = base + nt * 16 + (lane & 15);
+        if ((lane >> 4) == 0 && p < npos) keys[p] = score_to_key(v[nt]);
+    }
+}
+
+template <int MT, int KS>
+__global__ __launch_bounds__(kFlatThreads) void score_flat_kernel(ScoreArgs a, int rows_per_wg) {
+    constexpr int D = 32 * KS;
+    __shared__ __attribute__((aligned(16))) uint16_t s_q[64 * QStage<KS>::kStride];
+    __shared__ float s_w[64];
+    const int qi = blockIdx.y;
+    const int s = qi / a.T;
+    const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    if (t < 0) return;
+    const int64_t npos = t + 1;
+    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
+    if (row0 >= npos) return;
+    const int64_t row1 = row0 + rows_per_wg < npos ? row0 + rows_per_wg : npos;
+    const int nsteps = static_cast<int>((row1 - row0 + kTileRows - 1) / kTileRows);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint16_t *Ks = a.K + s * a.k_seq_stride;
+    uint32_t *keys = a.keys + static_cast<int64_t>(qi) * a.keys_stride;
+    const int64_t wbase = row0 + wave * kRowsPerWave;       // this wave's rows of step 0
+
+    bf16x8 ka[kNT][KS], kc[kNT][KS];
+    flat_load<MT, KS>(ka, Ks, wbase, row1, lane);           // first rows in flight before q
+    stage_query<MT, KS, kFlatThreads>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, s_q, tid);
+    if (tid < 64) s_w[tid] = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
+    __syncthreads();
+    QFrag<MT, KS> f;
+    load_qfrag_lds_w<MT, KS>(f, s_q, s_w, lane);
+    for (int st = 0; st < nsteps; st += 2) {
+        if (st + 1 < nsteps) flat_load<MT, KS>(kc, Ks, wbase + (st + 1) * kTileRows, row1, lane);
+        flat_score_store<MT, KS>(f, ka, keys, wbase + st * kTileRows, row1, lane);
+        if (st + 2 < nsteps) flat_load<MT, KS>(ka, Ks, wbase + (st + 2) * kTileRows, row1, lane);
+        if (st + 1 < nsteps) flat_score_store<MT, KS>(f, kc, keys, wbase + (st + 1) * kTileRows, row1, lane);
+    }
+}
+
+template <int MT>
+hipError_t launch_flat_mt(const ScoreArgs &a, dim3 grid, int rows_per_wg, hipStream_t st) {
+    if (a.d == 64) return launch(kKindScoreFlat, score_flat_kernel<MT, 2>, grid, dim3(kFlatThreads), 0, st, a, rows_per_wg);
+    return launch(kKindScoreFlat, score_flat_kernel<MT, 4>, grid, dim3(kFlatThreads), 0, st, a, rows_per_wg);
+}
+
 template <int MODE, int MT>
 hipError_t launch_mt(KernelKind kind, const ScoreArgs &a, dim3 grid, hipStream_t st) {
     if (a.d == 64) return launch(kind, score_kernel<MODE, MT, 2>, grid, dim3(256), 0, st, a);
@@ -132,7 +205,15 @@ hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int64_t max_pos, hip
                           : mode == kScoreRefine ? kKindScoreRefine : kKindScoreFlat;
     if (mode == kScoreBlocks) return launch_mode<kScoreBlocks>(kind, a, grid, st);
     if (mode == kScoreRefine) return launch_mode<kScoreRefine>(kind, a, grid, st);
-    return launch_mode<kScoreFlat>(kind, a, grid, st);
+    // flat: about 512 workgroups of 128..4096 rows each
+    const int64_t nq = static_cast<int64_t>(a.S) * a.T;
+    int64_t rows = (max_pos * nq / 512 + kTileRows - 1) / kTileRows * kTileRows;
+    rows = rows < kTileRows ? kTileRows : (rows > 4096 ? 4096 : rows);
+    const dim3 fgrid(static_cast<uint32_t>((max_pos + rows - 1) / rows), static_cast<uint32_t>(nq));
+    const int r = static_cast<int>(rows);
+    if (a.H <= 16) return launch_flat_mt<1>(a, fgrid, r, st);
+    if (a.H <= 32) return launch_flat_mt<2>(a, fgrid, r, st);
+    return launch_flat_mt<4>(a, fgrid, r, st);
 }
 
 }  // namespace hisa
