@@ -253,6 +253,9 @@ int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uin
         if (block_major_mode(S, T, d, L, B, m)) {
             fa.bucket_off = reinterpret_cast<int32_t *>(base + lay.bucket_off);
             fa.bucket_ent = reinterpret_cast<uint32_t *>(base + lay.bucket_ent);
+            fa.own_rep = own_rep;
+            fa.blk_keys = blk_keys;
+            fa.blk_stride = lay.blk_stride;
         }
         st = hip_status(launch_fused_blocks_refine(fa, hs));
         if (st != HISA_OK) return st;

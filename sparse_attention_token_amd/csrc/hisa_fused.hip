@@ -26,8 +26,8 @@
 //  * batch (many queries): hisa_blocks_topm_kernel runs the block stage once
 //    per query and writes the kept blocks; hisa_refine_kernel then scores
 //    128-row tiles with q staged in LDS.
-//  * many queries per sequence (prefill chunks): the block stage as in batch
-//    mode, then the refinement block by block (hisa_prefill.hip).
+//  * many queries per sequence (prefill chunks): block stage and refinement
+//    both block by block (hisa_prefill.hip).
 // Either way the final top k runs as the selection kernel (select.hip).
 // Limits (checked by the host): B*d <= 16384, ceil(L/B) <= 8192; decode mode
 // also ceil(L/B) <= 2048 and m <= 1024.
@@ -421,7 +421,9 @@ hipError_t launch_fused_ks(const FusedArgs &a, bool decode, hipStream_t st) {
         return launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsNarrow>,
                       dim3(static_cast<uint32_t>(decode_grid(nq, narrow))), dim3(kDecodeThreads), 0, st, a);
     }
-    const hipError_t e = launch(kKindScoreBlocks, hisa_blocks_topm_kernel<MT, KS>, dim3(nq), dim3(kK1Threads), 0, st, a);
+    const hipError_t e = (a.bucket_off && a.nblk <= kBMMaxBlocks)
+        ? launch_block_major_blocks(a, st)
+        : launch(kKindScoreBlocks, hisa_blocks_topm_kernel<MT, KS>, dim3(nq), dim3(kK1Threads), 0, st, a);
     if (e != hipSuccess) return e;
     if (a.bucket_off) return launch_block_major_refine(a, st);
     return launch(kKindScoreRefine, hisa_refine_kernel<MT, KS>, g2, dim3(kK2Threads), 0, st, a);

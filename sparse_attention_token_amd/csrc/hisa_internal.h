@@ -115,7 +115,13 @@ struct FusedArgs {
     int nblk;                 // ceil(L/B)
     int32_t *bucket_off;      // ws [nchunk][nblk + 1]
     uint32_t *bucket_ent;     // ws [nchunk][kChunkQueries * m]: (query in chunk) << 16 | slot
+    // block-major block stage (block_major_mode with nblk <= kBMMaxBlocks)
+    uint16_t *own_rep;        // ws [S*T][d]: own-block representative of every query
+    uint32_t *blk_keys;       // ws [S*T][blk_stride]: block keys by block id
+    int64_t blk_stride;
 };
+
+constexpr int kBMMaxBlocks = 2048;       // block-major block stage: one wave selects the top m
 
 constexpr int kChunkQueries = 256;
 
@@ -128,6 +134,7 @@ inline int64_t bucket_chunks(int S, int T) {
 }
 hipError_t launch_fused_blocks_refine(const FusedArgs &a, hipStream_t st);
 hipError_t launch_block_major_refine(const FusedArgs &a, hipStream_t st);
+hipError_t launch_block_major_blocks(const FusedArgs &a, hipStream_t st);
 
 hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
                               int64_t blk0, int64_t nblk, int64_t L_new, uint16_t *pool,

@@ -1,5 +1,5 @@
-// Token refinement for many queries per sequence (prefill chunks), block by
-// block.
+// The block stage and the token refinement for many queries per sequence
+// (prefill chunks), block by block.
 //
 // The refinement step re-scores, with the original indexer, every token of the
 // blocks each query kept (gptget.net English summary, "Methodology"; Chinese
@@ -9,6 +9,11 @@
 // Here the pairs are grouped by block instead, per chunk of up to
 // kChunkQueries consecutive queries of one sequence:
 //
+//   hisa_blocks_bm_kernel / hisa_topm_kernel: the block stage the same way --
+//                        128 pooled means per workgroup in registers, the
+//                        chunk's queries streamed through LDS -- then one wave
+//                        per query scores its own block's representative
+//                        (own_mean_kernel) and keeps the top m.
 //   hisa_bucket_kernel   one workgroup per chunk: counting sort of the chunk's
 //                        (query, slot) pairs by kept block id, in LDS.
 //   hisa_refine_bm_kernel one 2-wave workgroup per (block, chunk) (bm_tile()): the block's
@@ -186,12 +191,38 @@ __device__ __forceinline__ void store_tiles(uint32_t *cand, const float (&v)[NTW
 #pragma unroll
     for (int nt0 = 0; nt0 < NTW; nt0 += 4) {
         if (nt0 + g < NTW) {
-            float x = v[nt0];
-#pragma unroll
-            for (int j = 1; j < 4; ++j)
-                if (nt0 + j < NTW && g == j) x = v[nt0 + j];
+            // two-level select on the bits of g (kept as selects, not an indexed load)
+            const float a0 = v[nt0];
+            const float a1 = nt0 + 1 < NTW ? v[nt0 + 1] : a0;
+            const float a2 = nt0 + 2 < NTW ? v[nt0 + 2] : a0;
+            const float a3 = nt0 + 3 < NTW ? v[nt0 + 3] : a0;
+            const float lo = (g & 1) ? a1 : a0;
+            const float hi = (g & 1) ? a3 : a2;
+            const float x = (g & 2) ? hi : lo;
             const int r = (nt0 + g) * 16 + n;
             cand[r] = tok0 + r <= t ? score_to_key(x) : kNoCandidate;
+        }
+    }
+}
+
+// Block keys of one query for this wave's NTW tiles of means starting at
+// block p0: only blocks p < bt are written (the rest of the row is never read,
+// and past the last block it may lie beyond the row).
+template <int NTW>
+__device__ __forceinline__ void store_blocks(uint32_t *out, const float (&v)[NTW], int p0, int bt, int lane) {
+    const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int nt0 = 0; nt0 < NTW; nt0 += 4) {
+        if (nt0 + g < NTW) {
+            const float a0 = v[nt0];
+            const float a1 = nt0 + 1 < NTW ? v[nt0 + 1] : a0;
+            const float a2 = nt0 + 2 < NTW ? v[nt0 + 2] : a0;
+            const float a3 = nt0 + 3 < NTW ? v[nt0 + 3] : a0;
+            const float lo = (g & 1) ? a1 : a0;
+            const float hi = (g & 1) ? a3 : a2;
+            const float x = (g & 2) ? hi : lo;
+            const int r = (nt0 + g) * 16 + n;
+            if (p0 + r < bt) out[r] = score_to_key(x);
         }
     }
 }
@@ -286,6 +317,169 @@ __global__ __launch_bounds__(kBMThreads) void hisa_refine_bm_kernel(FusedArgs a)
     store_tiles<NTW>(cand, v, tok0, t, lane);
 }
 
+// ---------------------------------------------------------------- block stage, block by block
+// Block scores of every query of a chunk (kBlkChunk queries) against 128
+// pooled means at once: one 2-wave workgroup per (128-block tile, chunk), the tile's means held in
+// registers as MFMA operands and the chunk's queries streamed through LDS as
+// in the refinement.  Only complete blocks b < b_t are scored here (the own
+// block's representative differs per query; hisa_topm_kernel scores it).
+// blk_keys[qi][b] receives the key of block b for b < b_t.
+constexpr int kBlkTileRows = 128;
+constexpr int kBlkChunk = 32;          // queries per workgroup: enough workgroups to fill the GPU
+
+template <int MT, int KS>
+__global__ __launch_bounds__(kBMThreads) void hisa_blocks_bm_kernel(FusedArgs a) {
+    constexpr int D = 32 * KS;
+    constexpr int NW = kBMThreads / 64;
+    constexpr int NTW = kBlkTileRows / (16 * NW);
+    using QD = QDirect<MT, KS, NW>;
+    constexpr int kQElems = QD::kInstr * 64 * 8;
+    __shared__ __attribute__((aligned(16))) uint16_t s_q[2][kQElems];
+    __shared__ __attribute__((aligned(16))) float s_w[2][64];
+    __shared__ int32_t s_qi[kBlkChunk];
+    __shared__ int32_t s_bt[kBlkChunk];
+    __shared__ uint32_t s_n;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15;
+    const int cps = (a.T + kBlkChunk - 1) / kBlkChunk;
+    int j, c;
+    bm_tile((a.nblk + kBlkTileRows - 1) / kBlkTileRows, a.S * cps, j, c);
+    if (c < 0) return;
+    const int s = c / cps;
+    const int i0 = (c - s * cps) * kBlkChunk;
+    const int nqc = min(kBlkChunk, a.T - i0);
+    const int b0 = j * kBlkTileRows;
+
+    // the chunk's queries that have a complete block in this tile (b_t > b0)
+    if (tid == 0) s_n = 0u;
+    __syncthreads();
+    for (int i = tid; i < nqc; i += kBMThreads) {
+        const int qi = s * a.T + i0 + i;
+        const int64_t t = query_pos(a.qpos, qi, i0 + i, a.L, a.T);
+        if (t >= 0 && t / a.B > b0) {
+            const uint32_t x = atomicAdd(&s_n, 1u);
+            s_qi[x] = qi;
+            s_bt[x] = static_cast<int32_t>(t / a.B);
+        }
+    }
+    // this wave's means (rows past the pool end are zero and never stored)
+    const uint16_t *pool = a.pool + s * a.pool_seq_stride;
+    const int p0 = b0 + wave * 16 * NTW;
+    bf16x8 kb[NTW][KS];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+        const int p = p0 + nt * 16 + n;
+        load_row_frag<KS>(kb[nt], p < a.nblk ? pool + static_cast<int64_t>(p) * D : nullptr, lane);
+    }
+    if (a.H < MT * 16) {
+        constexpr int ST = QStage<KS>::kStride;
+        for (int x = tid; x < 2 * (MT * 16 - a.H) * ST; x += kBMThreads) {
+            const int bf = x / ((MT * 16 - a.H) * ST), r = x - bf * (MT * 16 - a.H) * ST;
+            s_q[bf][a.H * ST + r] = 0;
+        }
+        for (int x = tid; x < 2 * 64; x += kBMThreads) s_w[x >> 6][x & 63] = 0.0f;
+    }
+    __syncthreads();
+    const int np = static_cast<int>(s_n);
+    if (np == 0) return;
+
+    QD qd;
+    qd.init(a.H, wave, lane);
+    qd.issue(a.q + static_cast<int64_t>(s_qi[0]) * a.H * D, a.w + static_cast<int64_t>(s_qi[0]) * a.H, a.H,
+             s_q[0], s_w[0], wave, lane);
+    float v[NTW];
+    uint32_t *out = nullptr;
+    int bt = 0;
+    for (int i = 0; i < np; ++i) {
+        const int buf = i & 1;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (i + 1 < np) {
+            const int qn = s_qi[i + 1];
+            qd.issue(a.q + static_cast<int64_t>(qn) * a.H * D, a.w + static_cast<int64_t>(qn) * a.H, a.H,
+                     s_q[buf ^ 1], s_w[buf ^ 1], wave, lane);
+        }
+        if (out) store_blocks<NTW>(out, v, p0, bt, lane);
+        out = a.blk_keys + static_cast<int64_t>(s_qi[i]) * a.blk_stride + p0;
+        bt = s_bt[i];
+        score_tiles_lds<MT, KS, NTW>(s_q[buf], s_w[buf], kb, v, lane);
+    }
+    store_blocks<NTW>(out, v, p0, bt, lane);
+}
+
+// Per query (one wave each, four per workgroup): score the own block's
+// representative own_rep[qi], read the complete blocks' keys, and keep the
+// top min(m, b_t + 1) blocks (ascending ids) with the one-wave select.
+constexpr int kTopMThreads = 256;
+
+template <int R, typename Emit>
+__device__ __forceinline__ uint32_t topm_select(const uint32_t *keys, uint32_t own_key, int nb, int m, int lane,
+                                                Emit &&emit) {
+    const int rd = (nb + 63) / 64;
+    uint32_t kv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int p = lane * rd + r;
+        kv[r] = (r < rd && p < nb) ? (p == nb - 1 ? own_key : keys[p]) : kNoCandidate;
+    }
+    const SelectResult res = wave_ballot_select<R>(kv, static_cast<uint32_t>(m));
+    if (res.keff > 0) wave_compact<R>(kv, res, [&](uint32_t op, int r, uint32_t) { emit(op, lane * rd + r); });
+    return res.keff;
+}
+
+template <int MT, int KS>
+__global__ __launch_bounds__(kTopMThreads) void hisa_topm_kernel(FusedArgs a) {
+    constexpr int D = 32 * KS;
+    const int lane = threadIdx.x & 63;
+    const int qi = blockIdx.x * (kTopMThreads / 64) + (threadIdx.x >> 6);
+    if (qi >= a.S * a.T) return;                       // whole wave
+    const int s = qi / a.T;
+    const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    int32_t *sel = a.sel_blk + static_cast<int64_t>(qi) * a.m;
+    int32_t *ob = a.out_blk ? a.out_blk + static_cast<int64_t>(qi) * a.m : nullptr;
+    uint32_t keff = 0;
+    if (t >= 0) {
+        const int nb = static_cast<int>(t / a.B + 1);
+        QFrag<MT, KS> f;
+        load_qfrag_global<MT, KS>(f, a.q + static_cast<int64_t>(qi) * a.H * D, a.w + static_cast<int64_t>(qi) * a.H,
+                                  a.H, lane);
+        bf16x8 kbm[KS];
+        load_row_frag<KS>(kbm, (lane & 15) == 0 ? a.own_rep + static_cast<int64_t>(qi) * D : nullptr, lane);
+        const float v = score_rows<MT, KS>(f, kbm);
+        const uint32_t own_key = static_cast<uint32_t>(
+            __builtin_amdgcn_readfirstlane(static_cast<int>(score_to_key(v))));
+        const uint32_t *keys = a.blk_keys + static_cast<int64_t>(qi) * a.blk_stride;
+        auto emit = [&](uint32_t op, int pos) {
+            sel[op] = pos;
+            if (ob) ob[op] = pos;
+        };
+        const int rd = (nb + 63) / 64;
+        if (rd <= 4) keff = topm_select<4>(keys, own_key, nb, a.m, lane, emit);
+        else if (rd <= 8) keff = topm_select<8>(keys, own_key, nb, a.m, lane, emit);
+        else if (rd <= 16) keff = topm_select<16>(keys, own_key, nb, a.m, lane, emit);
+        else keff = topm_select<32>(keys, own_key, nb, a.m, lane, emit);
+    }
+    for (int j = static_cast<int>(keff) + lane; j < a.m; j += 64) {
+        sel[j] = -1;
+        if (ob) ob[j] = -1;
+    }
+}
+
+template <int MT>
+hipError_t launch_blocks_mt(const FusedArgs &a, dim3 g_blk, dim3 g_top, hipStream_t st) {
+    hipError_t e;
+    if (a.d == 64) {
+        e = launch(kKindScoreBlocks, hisa_blocks_bm_kernel<MT, 2>, g_blk, dim3(kBMThreads), 0, st, a);
+        if (e != hipSuccess) return e;
+        return launch(kKindSelectBlocks, hisa_topm_kernel<MT, 2>, g_top, dim3(kTopMThreads), 0, st, a);
+    }
+    e = launch(kKindScoreBlocks, hisa_blocks_bm_kernel<MT, 4>, g_blk, dim3(kBMThreads), 0, st, a);
+    if (e != hipSuccess) return e;
+    return launch(kKindSelectBlocks, hisa_topm_kernel<MT, 4>, g_top, dim3(kTopMThreads), 0, st, a);
+}
+
 template <int MT, int KS>
 hipError_t launch_bm_ks(const FusedArgs &a, dim3 grid, hipStream_t st) {
     if (a.B == 64) return launch(kKindScoreRefine, hisa_refine_bm_kernel<MT, KS, 2>, grid, dim3(kBMThreads), 0, st, a);
@@ -302,6 +496,18 @@ hipError_t launch_bm_mt(const FusedArgs &a, dim3 grid, hipStream_t st) {
 bool block_major_mode(int S, int T, int d, int64_t L, int B, int m) {
     (void)S;
     return T >= kChunkQueries / 2 && (B == 64 || B == 128) && m <= 65535 && fused_supported(d, L, B, m);
+}
+
+hipError_t launch_block_major_blocks(const FusedArgs &a, hipStream_t st) {
+    hipError_t e = launch_own_mean(a.K, a.k_seq_stride, a.qpos, a.L, a.S, a.T, a.d, a.B, a.own_rep, st);
+    if (e != hipSuccess) return e;
+    const int64_t nchunk = static_cast<int64_t>(a.S) * ((a.T + kBlkChunk - 1) / kBlkChunk);
+    const dim3 g_blk(bm_grid((a.nblk + kBlkTileRows - 1) / kBlkTileRows, nchunk));
+    const int nq = a.S * a.T;
+    const dim3 g_top(static_cast<uint32_t>((nq + kTopMThreads / 64 - 1) / (kTopMThreads / 64)));
+    if (a.H <= 16) return launch_blocks_mt<1>(a, g_blk, g_top, st);
+    if (a.H <= 32) return launch_blocks_mt<2>(a, g_blk, g_top, st);
+    return launch_blocks_mt<4>(a, g_blk, g_top, st);
 }
 
 hipError_t launch_block_major_refine(const FusedArgs &a, hipStream_t st) {
