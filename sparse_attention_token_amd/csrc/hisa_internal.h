@@ -140,6 +140,11 @@ hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, in
                               int64_t blk0, int64_t nblk, int64_t L_new, uint16_t *pool,
                               int64_t pool_seq_stride, hipStream_t st);
 
+// Own-block means of queries at the consecutive positions t = L - T + i
+// (requires T <= L): one pass per block.
+hipError_t launch_own_prefix_mean(const uint16_t *K, int64_t k_seq_stride, int64_t L, int S, int T, int d, int B,
+                                  uint16_t *own_rep, hipStream_t st);
+
 hipError_t launch_own_mean(const uint16_t *K, int64_t k_seq_stride, const int32_t *qpos,
                            int64_t L, int S, int T, int d, int B, uint16_t *own_rep,
                            hipStream_t st);

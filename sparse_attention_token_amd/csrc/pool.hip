@@ -95,7 +95,60 @@ __global__ __launch_bounds__(kPoolThreads) void own_mean_kernel(
     if (static_cast<int>(threadIdx.x) < d) own_rep[static_cast<int64_t>(qi) * d + threadIdx.x] = m;
 }
 
+// grid: (blocks b_lo .. b_lo + gridDim.x - 1), d threads.  Consecutive query
+// positions t = L - T + i (one sequence per blockIdx.y): a running fp64 sum
+// down each block's rows, in row order, is at row t exactly the sum of rows
+// [b_t*B, t] in row order, so every query of the block gets its own-block
+// mean from one pass -- the same arithmetic as staged_column_mean().
+__global__ __launch_bounds__(kMaxD) void own_prefix_mean_kernel(
+        const uint16_t *__restrict__ K, int64_t k_seq_stride, int64_t L, int T, int d, int B,
+        int64_t b_lo, uint16_t *__restrict__ own_rep) {
+    const int s = blockIdx.y;
+    const int col = threadIdx.x;
+    if (col >= d) return;
+    const int64_t t0 = L - T;                                  // position of query 0
+    const int64_t r0 = (b_lo + blockIdx.x) * B;
+    const int64_t r_first = r0 > t0 ? r0 : t0;                 // first row that is a query position
+    const int64_t r_end = (r0 + B < L) ? r0 + B : L;
+    const uint16_t *src = K + s * k_seq_stride + col;
+    double sum = 0.0;
+    int64_t r = r0;
+    uint16_t nx[8];                                            // the next 8 rows, loads in flight
+#pragma unroll
+    for (int j = 0; j < 8; ++j) nx[j] = r + j < r_end ? src[(r + j) * d] : 0;
+    for (; r + 8 <= r_end; r += 8) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = bf16_to_f32(nx[j]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) nx[j] = r + 8 + j < r_end ? src[(r + 8 + j) * d] : 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            sum += static_cast<double>(x[j]);
+            const int64_t rr = r + j;
+            if (rr >= r_first) {
+                const float mean = static_cast<float>(sum / static_cast<double>(rr + 1 - r0));
+                own_rep[(static_cast<int64_t>(s) * T + (rr - t0)) * d + col] = f32_to_bf16_rne(mean);
+            }
+        }
+    }
+    for (; r < r_end; ++r) {
+        sum += static_cast<double>(bf16_to_f32(src[r * d]));
+        if (r >= r_first) {
+            const float mean = static_cast<float>(sum / static_cast<double>(r + 1 - r0));
+            own_rep[(static_cast<int64_t>(s) * T + (r - t0)) * d + col] = f32_to_bf16_rne(mean);
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_own_prefix_mean(const uint16_t *K, int64_t k_seq_stride, int64_t L, int S, int T, int d, int B,
+                                  uint16_t *own_rep, hipStream_t st) {
+    const int64_t b_lo = (L - T) / B, b_hi = (L - 1) / B;
+    return launch(kKindOwnMean, own_prefix_mean_kernel, dim3(static_cast<uint32_t>(b_hi - b_lo + 1), S),
+                  dim3(kMaxD), 0, st, K, k_seq_stride, L, T, d, B, b_lo, own_rep);
+}
 
 hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
                               int64_t blk0, int64_t nblk, int64_t L_new, uint16_t *pool,

@@ -25,6 +25,8 @@ namespace {
 
 constexpr int kNT = 1024;
 constexpr int kChunkMax = kNT * 32;
+constexpr int kNarrowNT = 256;          // select workgroup size when there are many queries
+constexpr int kManyQueries = 1024;
 
 // number of candidate positions of query qi for a mode (0 for an invalid t)
 template <int MODE>
@@ -56,9 +58,10 @@ __device__ __forceinline__ void load_run(const uint32_t *__restrict__ keys, int6
     }
 }
 
-// Single-stage select: the whole row (n <= kNT*R) in one workgroup.
-template <int MODE, int R>
-__global__ __launch_bounds__(kNT) void select_kernel(SelectArgs a) {
+// Single-stage select: the whole row (n <= NT*R) in one workgroup of NT
+// threads (1024 for latency with few queries, 256 for throughput with many).
+template <int MODE, int R, int NT>
+__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     __shared__ __attribute__((aligned(16))) SelectScratch sc;
     __shared__ int32_t s_sel[kSelMaxM];
     const int tid = threadIdx.x;
@@ -71,13 +74,13 @@ __global__ __launch_bounds__(kNT) void select_kernel(SelectArgs a) {
     load_run<R>(a.keys + static_cast<int64_t>(qi) * a.keys_stride, static_cast<int64_t>(tid) * R, n, kv);
     if (MODE == kScoreRefine) {
         const int meff = static_cast<int>(n / a.B);
-        for (int j = tid; j < meff; j += kNT) s_sel[j] = a.sel_blk[static_cast<int64_t>(qi) * a.m + j];
+        for (int j = tid; j < meff; j += NT) s_sel[j] = a.sel_blk[static_cast<int64_t>(qi) * a.m + j];
         // block_radix_select starts with a barrier, which also publishes s_sel
     }
-    const SelectResult res = block_radix_select<kNT, R>(kv, static_cast<uint32_t>(a.kout), sc);
+    const SelectResult res = block_radix_select<NT, R>(kv, static_cast<uint32_t>(a.kout), sc);
     if (res.keff > 0) {
         const int B = a.B;
-        block_compact<kNT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
+        block_compact<NT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
             const int pos = tid * R + r;
             int32_t id = pos;
             if (MODE == kScoreRefine) {
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(kNT) void select_kernel(SelectArgs a) {
             if (out2) out2[op] = id;
         });
     }
-    for (int j = static_cast<int>(res.keff) + tid; j < a.kout; j += kNT) {
+    for (int j = static_cast<int>(res.keff) + tid; j < a.kout; j += NT) {
         out[j] = -1;
         if (osc) osc[j] = -__builtin_huge_valf();
         if (out2) out2[j] = -1;
@@ -174,14 +177,23 @@ __global__ __launch_bounds__(kNT) void select_final_kernel(SelectArgs a, const u
 
 template <int MODE>
 hipError_t launch_single(KernelKind kind, const SelectArgs &a, int nq, int64_t max_n, hipStream_t st) {
-    const dim3 g(nq), b(kNT);
+    const dim3 g(nq);
+    if (nq >= kManyQueries && max_n <= kNarrowNT * 32) {
+        const dim3 b(kNarrowNT);
+        const int64_t per = (max_n + kNarrowNT - 1) / kNarrowNT;
+        if (per <= 4) return launch(kind, select_kernel<MODE, 4, kNarrowNT>, g, b, 0, st, a);
+        if (per <= 8) return launch(kind, select_kernel<MODE, 8, kNarrowNT>, g, b, 0, st, a);
+        if (per <= 16) return launch(kind, select_kernel<MODE, 16, kNarrowNT>, g, b, 0, st, a);
+        return launch(kind, select_kernel<MODE, 32, kNarrowNT>, g, b, 0, st, a);
+    }
+    const dim3 b(kNT);
     const int64_t per = (max_n + kNT - 1) / kNT;
-    if (per <= 1) return launch(kind, select_kernel<MODE, 1>, g, b, 0, st, a);
-    if (per <= 2) return launch(kind, select_kernel<MODE, 2>, g, b, 0, st, a);
-    if (per <= 4) return launch(kind, select_kernel<MODE, 4>, g, b, 0, st, a);
-    if (per <= 8) return launch(kind, select_kernel<MODE, 8>, g, b, 0, st, a);
-    if (per <= 16) return launch(kind, select_kernel<MODE, 16>, g, b, 0, st, a);
-    return launch(kind, select_kernel<MODE, 32>, g, b, 0, st, a);
+    if (per <= 1) return launch(kind, select_kernel<MODE, 1, kNT>, g, b, 0, st, a);
+    if (per <= 2) return launch(kind, select_kernel<MODE, 2, kNT>, g, b, 0, st, a);
+    if (per <= 4) return launch(kind, select_kernel<MODE, 4, kNT>, g, b, 0, st, a);
+    if (per <= 8) return launch(kind, select_kernel<MODE, 8, kNT>, g, b, 0, st, a);
+    if (per <= 16) return launch(kind, select_kernel<MODE, 16, kNT>, g, b, 0, st, a);
+    return launch(kind, select_kernel<MODE, 32, kNT>, g, b, 0, st, a);
 }
 
 template <int MODE>
