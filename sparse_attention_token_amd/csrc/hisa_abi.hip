@@ -250,6 +250,8 @@ int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uin
         fa.cand_keys = cand_keys; fa.cand_stride = lay.cand_stride;
         fa.out_idx = out_idx; fa.out_score = out_score;
         fa.nblk = static_cast<int>(ceil_div(L, B));
+        fa.blk_keys = blk_keys;
+        fa.blk_stride = lay.blk_stride;
         if (block_major_mode(S, T, d, L, B, m)) {
             fa.bucket_off = reinterpret_cast<int32_t *>(base + lay.bucket_off);
             fa.bucket_ent = reinterpret_cast<uint32_t *>(base + lay.bucket_ent);

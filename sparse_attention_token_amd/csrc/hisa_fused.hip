@@ -17,12 +17,16 @@
 //    * the top min(m, b_t + 1) blocks (ascending ids) are then selected: by
 //      one wave when b_t + 1 <= 2048 (no barriers), by the whole workgroup
 //      otherwise.
-// Two ways to run it, chosen by the host:
-//  * decode (few queries): hisa_decode_kernel -- one 4-wave workgroup per 256
-//    (or, with few queries, 128) candidate positions of a query (position p = slot*B + r: row r of the
+// Ways to run it, chosen by the host:
+//  * decode (few queries), short context: hisa_decode_kernel -- one 4-wave
+//    workgroup per 256 (or, with few queries, 128) candidate positions of a
+//    query (position p = slot*B + r: row r of the
 //    slot-th kept block, masked past t).  Each workgroup repeats its query's
 //    block stage (the pooled means it reads are shared through L2) and then
 //    scores its 128 rows: one launch, no communication between workgroups.
+//  * decode, longer context: hisa_dblocks_kernel scores the pooled means once
+//    per query (one workgroup per 128 of them), and hisa_dgather_kernel keeps
+//    the top m from the block keys and scores its candidate rows.
 //  * batch (many queries): hisa_blocks_topm_kernel runs the block stage once
 //    per query and writes the kept blocks; hisa_refine_kernel then scores
 //    128-row tiles with q staged in LDS.
@@ -49,6 +53,11 @@ constexpr int kDecodeMaxQueries = 32;                     // decode mode repeats
 constexpr int kDecodeRowsWide = 256;                      // candidate rows per decode workgroup, big grids
 constexpr int kDecodeRowsNarrow = 128;                    // ... and when fewer than kDecodeWideMin would run
 constexpr int kDecodeWideMin = 256;
+// Up to this many blocks every decode workgroup repeats the block stage (one
+// launch); beyond it the block stage runs once per query in its own kernel.
+// Measured per step: 256 blocks 28.8 vs 29.7 us, 512 blocks 30.6 vs 28.9,
+// 1025 blocks 48.4 vs 40.7 (one launch vs two).
+constexpr int kDecodeOneKernelMaxBlocks = 256;
 
 // LDS slot of block position p: the keys are stored so that the select's
 // owner of a contiguous run of positions reads it as conflict-free rows.
@@ -361,6 +370,196 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_decode_kernel(FusedArgs a
     }
 }
 
+// ---------------------------------------------------------------- decode, two kernels
+// Long contexts make every decode workgroup's own copy of the block stage
+// expensive (1025 pooled means per workgroup at 128K), so the block stage runs
+// once per query in hisa_dblocks_kernel -- one workgroup per (query, 128
+// pooled means), writing block keys -- and hisa_dgather_kernel reads a
+// query's n_b keys, keeps the top m with the one-wave select and scores its
+// candidate rows.
+constexpr int kDBlkRows = 128;
+
+template <int MT, int KS>
+__global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs a) {
+    constexpr int D = 32 * KS;
+    constexpr int NTW = kDBlkRows / (16 * kDecodeThreads / 64);
+    __shared__ __attribute__((aligned(16))) BlockStageLds<KS, kDecodeThreads> L;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    int qi, j;
+    decode_tile(a.S * a.T, (a.nblk + kDBlkRows - 1) / kDBlkRows, qi, j);
+    if (qi < 0) return;
+    const int s = qi / a.T;
+    const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    if (t < 0) return;
+    const int bt = static_cast<int>(t / a.B);
+    const bool own_in_pool = t == a.L - 1;          // the pool entry of b_t is the own-block mean
+    const int full = own_in_pool ? bt + 1 : bt;    // pool rows to score
+    const int b0 = j * kDBlkRows;
+    const bool own_here = !own_in_pool && bt >= b0 && bt < b0 + kDBlkRows;
+    if (b0 >= full && !own_here) return;
+    uint32_t *keys = a.blk_keys + static_cast<int64_t>(qi) * a.blk_stride;
+
+    const uint16_t *pool = a.pool + s * a.pool_seq_stride;
+    bf16x8 kb[NTW][KS];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+        const int p = b0 + (wave * NTW + nt) * 16 + n;
+        load_row_frag<KS>(kb[nt], p < full ? pool + static_cast<int64_t>(p) * D : nullptr, lane);
+    }
+    const int64_t r0 = static_cast<int64_t>(bt) * a.B;
+    const int own_rows = static_cast<int>(t + 1 - r0);
+    uint16_t *s_own = reinterpret_cast<uint16_t *>(L.own);
+    if (own_here) {
+        constexpr int kPer = (kFusedOwnElems / 8 + kDecodeThreads - 1) / kDecodeThreads;
+        const int chunks = own_rows * D / 8;
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(a.K + s * a.k_seq_stride + r0 * D);
+        u32x4 *dst = reinterpret_cast<u32x4 *>(s_own);
+        u32x4 v[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (tid + i * kDecodeThreads < chunks) v[i] = src[tid + i * kDecodeThreads];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (tid + i * kDecodeThreads < chunks) dst[tid + i * kDecodeThreads] = v[i];
+    }
+    stage_query<MT, KS, kDecodeThreads>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, L.q, tid);
+    if (tid < 64) L.w[tid] = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
+    __syncthreads();
+    QFrag<MT, KS> f;
+    load_qfrag_lds_w<MT, KS>(f, L.q, L.w, lane);
+    float v[NTW];
+    score_tiles_frag<MT, KS, NTW>(f, kb, v);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+        const int p = b0 + (wave * NTW + nt) * 16 + n;
+        if (g == 0 && p < full) keys[p] = score_to_key(v[nt]);
+    }
+    if (own_here) {
+        // the mean of rows b_t*B .. t, one column per thread, rows in order, fp64
+        if (tid < D) {
+            double sum = 0.0;
+            int r = 0;
+            for (; r + 8 <= own_rows; r += 8) {
+                float x[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) x[jj] = bf16_to_f32(s_own[(r + jj) * D + tid]);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) sum += static_cast<double>(x[jj]);
+            }
+            for (; r < own_rows; ++r) sum += static_cast<double>(bf16_to_f32(s_own[r * D + tid]));
+            L.mean[tid] = f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(own_rows)));
+        }
+        __syncthreads();
+        if (wave == 0) {
+            bf16x8 kbm[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) kbm[ks] = n == 0 ? load_bf16x8(L.mean + 32 * ks + 8 * g) : zero_bf16x8();
+            const float vo = score_rows<MT, KS>(f, kbm);
+            if (lane == 0) keys[bt] = score_to_key(vo);
+        }
+    }
+}
+
+template <int R, typename Emit>
+__device__ __forceinline__ uint32_t dgather_topm(const uint32_t *keys, int nb, int m, int lane, Emit &&emit) {
+    const int rd = (nb + 63) / 64;
+    uint32_t kv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int p = lane * rd + r;
+        kv[r] = (r < rd && p < nb) ? keys[p] : kNoCandidate;
+    }
+    const SelectResult res = wave_ballot_select<R>(kv, static_cast<uint32_t>(m));
+    if (res.keff > 0) wave_compact<R>(kv, res, [&](uint32_t op, int r, uint32_t) { emit(op, lane * rd + r); });
+    return res.keff;
+}
+
+template <int MT, int KS, int ROWS>
+__global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs a) {
+    constexpr int D = 32 * KS;
+    constexpr int NTW = ROWS / (16 * kDecodeThreads / 64);
+    __shared__ __attribute__((aligned(16))) uint16_t s_q[64 * QStage<KS>::kStride];
+    __shared__ float s_w[64];
+    __shared__ int32_t s_sel[kDecodeMaxM];
+    __shared__ uint32_t s_keff;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    int qi, tile;
+    decode_tile(a.S * a.T, static_cast<int>((static_cast<int64_t>(a.m) * a.B + ROWS - 1) / ROWS), qi, tile);
+    if (qi < 0) return;
+    const int s = qi / a.T;
+    const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    const bool lead = tile == 0;            // also publishes the kept blocks
+    int32_t *sel = a.sel_blk + static_cast<int64_t>(qi) * a.m;
+    int32_t *ob = a.out_blk ? a.out_blk + static_cast<int64_t>(qi) * a.m : nullptr;
+    if (t < 0) {
+        if (lead)
+            for (int j = tid; j < a.m; j += kDecodeThreads) {
+                sel[j] = -1;
+                if (ob) ob[j] = -1;
+            }
+        return;
+    }
+    const int nb = static_cast<int>(t / a.B + 1);
+    const int meff = a.m < nb ? a.m : nb;
+    const int npos = meff * a.B;
+    const int tile0 = tile * ROWS;
+    if (tile0 >= npos) return;
+
+    stage_query<MT, KS, kDecodeThreads>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, s_q, tid);
+    if (tid < 64) s_w[tid] = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
+    if (wave == 0) {
+        const uint32_t *keys = a.blk_keys + static_cast<int64_t>(qi) * a.blk_stride;
+        auto emit = [&](uint32_t op, int pos) {
+            s_sel[op] = pos;
+            if (lead) {
+                sel[op] = pos;
+                if (ob) ob[op] = pos;
+            }
+        };
+        const int rd = (nb + 63) / 64;
+        uint32_t ke;
+        if (rd <= 4) ke = dgather_topm<4>(keys, nb, a.m, lane, emit);
+        else if (rd <= 8) ke = dgather_topm<8>(keys, nb, a.m, lane, emit);
+        else if (rd <= 16) ke = dgather_topm<16>(keys, nb, a.m, lane, emit);
+        else ke = dgather_topm<32>(keys, nb, a.m, lane, emit);
+        if (lane == 0) s_keff = ke;
+    }
+    __syncthreads();
+    if (lead)
+        for (int j = static_cast<int>(s_keff) + tid; j < a.m; j += kDecodeThreads) {
+            sel[j] = -1;
+            if (ob) ob[j] = -1;
+        }
+
+    bf16x8 kb[NTW][KS];
+    bool valid[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+        const int p = tile0 + (wave * NTW + nt) * 16 + n;
+        const uint16_t *row = nullptr;
+        if (p < npos) {
+            const int slot = p / a.B;
+            const int64_t tok = static_cast<int64_t>(s_sel[slot]) * a.B + (p - slot * a.B);
+            if (tok <= t) row = a.K + s * a.k_seq_stride + tok * D;
+        }
+        valid[nt] = row != nullptr;
+        load_row_frag<KS>(kb[nt], row, lane);
+    }
+    QFrag<MT, KS> f;
+    load_qfrag_lds_w<MT, KS>(f, s_q, s_w, lane);
+    float v[NTW];
+    score_tiles_frag<MT, KS, NTW>(f, kb, v);
+    uint32_t *cand = a.cand_keys + static_cast<int64_t>(qi) * a.cand_stride;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+        const int p = tile0 + (wave * NTW + nt) * 16 + n;
+        if (g == 0 && p < npos) cand[p] = valid[nt] ? score_to_key(v[nt]) : kNoCandidate;
+    }
+}
+
 template <int MT, int KS>
 __global__ __launch_bounds__(kK2Threads) void hisa_refine_kernel(FusedArgs a) {
     constexpr int D = 32 * KS;
@@ -414,10 +613,24 @@ hipError_t launch_fused_ks(const FusedArgs &a, bool decode, hipStream_t st) {
     if (decode) {
         const int64_t mb = static_cast<int64_t>(a.m) * a.B;
         const int wide = static_cast<int>((mb + kDecodeRowsWide - 1) / kDecodeRowsWide);
-        if (static_cast<int64_t>(wide) * nq >= kDecodeWideMin)
+        const int narrow = static_cast<int>((mb + kDecodeRowsNarrow - 1) / kDecodeRowsNarrow);
+        const bool use_wide = static_cast<int64_t>(wide) * nq >= kDecodeWideMin;
+        if (a.nblk > kDecodeOneKernelMaxBlocks) {
+            // long context: block stage once per query, then the gather
+            const int btiles = (a.nblk + kDBlkRows - 1) / kDBlkRows;
+            const hipError_t e = launch(kKindScoreBlocks, hisa_dblocks_kernel<MT, KS>,
+                                        dim3(static_cast<uint32_t>(decode_grid(nq, btiles))), dim3(kDecodeThreads), 0,
+                                        st, a);
+            if (e != hipSuccess) return e;
+            if (use_wide)
+                return launch(kKindScoreRefine, hisa_dgather_kernel<MT, KS, kDecodeRowsWide>,
+                              dim3(static_cast<uint32_t>(decode_grid(nq, wide))), dim3(kDecodeThreads), 0, st, a);
+            return launch(kKindScoreRefine, hisa_dgather_kernel<MT, KS, kDecodeRowsNarrow>,
+                          dim3(static_cast<uint32_t>(decode_grid(nq, narrow))), dim3(kDecodeThreads), 0, st, a);
+        }
+        if (use_wide)
             return launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsWide>,
                           dim3(static_cast<uint32_t>(decode_grid(nq, wide))), dim3(kDecodeThreads), 0, st, a);
-        const int narrow = static_cast<int>((mb + kDecodeRowsNarrow - 1) / kDecodeRowsNarrow);
         return launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsNarrow>,
                       dim3(static_cast<uint32_t>(decode_grid(nq, narrow))), dim3(kDecodeThreads), 0, st, a);
     }
