@@ -134,6 +134,9 @@ SMALL = [
     ("general_mB_25600", 1, 40000, 4, 16, 64, 128, 200, 500, "clustered"),
     # more than 32768 candidates per query: chunked (two-stage) top-k
     ("chunked_refine_38400", 1, 60000, 3, 16, 64, 128, 300, 3000, "clustered"),
+    # decode beyond 256 blocks: block stage in its own kernel (own block
+    # recomputed there for positions other than the last)
+    ("decode_two_kernel_d64_313blk", 2, 20000, 6, 16, 64, 64, 20, 400, "clustered"),
     # more than 2048 blocks: the block stage selects with the whole workgroup
     ("blocks_2344_workgroup_select", 1, 300000, 2, 4, 64, 128, 8, 256, "gaussian"),
 ]
