@@ -12,6 +12,7 @@ from .oracle import (  # noqa: F401
     flat_query,
     refine_query,
     hisa_query,
+    block_sparse_query,
     hisa_batch,
     flat_batch,
 )

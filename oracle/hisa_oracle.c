@@ -246,6 +246,52 @@ int oracle_hisa_query(const uint16_t *q, const float *w, const uint16_t *K,
  * K + s*k_seq_stride + j*d.  sel (nullable): list of nsel flat query ids
  * (s*T + i) to evaluate; null = all S*T.  Outputs are indexed by flat id.
  * Returns 0, or -1 on a bad position or allocation failure. */
+/*
+ * Block-sparse baseline (the comparison the pages make: HISA is said to beat
+ * block-sparse selection -- arXiv abstract; gptget.net English summary, "Key
+ * Results"; Chinese summary, experiment design).  The pages do not define it;
+ * the reading here: with the same token budget k, keep the floor(k/B) best
+ * blocks by the same block score as HISA's first stage (representatives and
+ * ranking as in oracle_hisa_query), and select every token j <= t of those
+ * blocks.  out_idx [k]: the tokens in increasing order, then -1.  Returns the
+ * number of tokens, or -1 (k < B, or out of memory).
+ */
+int oracle_block_sparse_query(const uint16_t *q, const float *w, const uint16_t *K, int H, int d,
+                              int64_t t, int B, int k, int32_t *out_idx, int32_t *out_blk)
+{
+    int mb = k / B;              /* whole blocks that fit the budget */
+    if (mb < 1) return -1;
+    int64_t bt = t / B;
+    int64_t nb = bt + 1;
+    uint16_t *rep = (uint16_t *)malloc((size_t)d * sizeof *rep);
+    cand_t *bc = (cand_t *)malloc((size_t)nb * sizeof *bc);
+    int32_t *sel = (int32_t *)malloc((size_t)mb * sizeof *sel);
+    if (!rep || !bc || !sel) {
+        free(rep); free(bc); free(sel);
+        return -1;
+    }
+    for (int64_t b = 0; b < nb; ++b) {
+        int64_t r1 = (b < bt) ? (b + 1) * B : t + 1;
+        oracle_mean_rows(K, b * B, r1, d, rep);
+        bc[b].s = oracle_score(q, w, rep, H, d);
+        bc[b].i = b;
+    }
+    qsort(bc, (size_t)nb, sizeof *bc, by_score_then_index);
+    int keep = nb < mb ? (int)nb : mb;
+    for (int i = 0; i < keep; ++i) sel[i] = (int32_t)bc[i].i;
+    qsort(sel, (size_t)keep, sizeof *sel, by_index);
+    int n = 0;
+    for (int i = 0; i < keep; ++i) {
+        for (int64_t j = (int64_t)sel[i] * B; j < (int64_t)(sel[i] + 1) * B && j <= t; ++j)
+            out_idx[n++] = (int32_t)j;
+    }
+    for (int i = n; i < k; ++i) out_idx[i] = -1;
+    if (out_blk)
+        for (int i = 0; i < mb; ++i) out_blk[i] = i < keep ? sel[i] : -1;
+    free(rep); free(bc); free(sel);
+    return n;
+}
+
 int oracle_hisa_batch(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
                       int64_t k_seq_stride, int64_t L, int S, int T, int H, int d, int B, int m,
                       int k, const int32_t *sel, int nsel, int32_t *out_idx, float *out_score,

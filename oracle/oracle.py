@@ -45,6 +45,8 @@ def load():
     lib.oracle_hisa_query.restype = I
     lib.oracle_hisa_query.argtypes = [_u16p, _f32p, _u16p, _u16p, I, I, I64, I, I, I,
                                       _i32p, _f32p, _i32p, _f64p]
+    lib.oracle_block_sparse_query.restype = I
+    lib.oracle_block_sparse_query.argtypes = [_u16p, _f32p, _u16p, I, I, I64, I, I, _i32p, _i32p]
     lib.oracle_hisa_batch.restype = I
     lib.oracle_hisa_batch.argtypes = [_u16p, _f32p, _i32p, _u16p, I64, I64, I, I, I, I, I, I,
                                       I, _i32p, I, _i32p, _f32p, _i32p]
@@ -139,6 +141,19 @@ def hisa_query(q, w, K, t: int, B: int, m: int, k: int):
     if keff < 0:
         raise MemoryError("oracle_hisa_query failed")
     return idx, sc, blk, bsc, keff
+
+
+def block_sparse_query(q, w, K, t: int, B: int, k: int):
+    """Block-sparse baseline for one query: (token idx [k] ascending then -1, blocks [k//B], count)."""
+    q, w, K = _c(q, np.uint16), _c(w, np.float32), _c(K, np.uint16)
+    H, d = q.shape
+    idx = np.zeros(k, dtype=np.int32)
+    blk = np.zeros(max(1, k // B), dtype=np.int32)
+    n = load().oracle_block_sparse_query(_p(q, _u16p), _p(w, _f32p), _p(K, _u16p), H, d, t, B, k,
+                                         _p(idx, _i32p), _p(blk, _i32p))
+    if n < 0:
+        raise ValueError("oracle_block_sparse_query: k < B or out of memory")
+    return idx, blk, n
 
 
 def _sel(sel, S, T):

@@ -259,6 +259,28 @@ def test_many_equal_scores(hisa, orc):
     _say(f"many ties: {rep}")
 
 
+@pytest.mark.parametrize("B", [64, 128])
+def test_block_sparse_budget(hisa, orc, B):
+    # hisa_index with m = k/B is the block-sparse baseline: every candidate is
+    # kept, so the tokens are exactly the kept blocks' tokens up to t
+    k = 2048
+    c = synth.clustered_case(2, 9000, 3, 64, 128, B, k // B, k, seed=31, latent_block=B,
+                             qpos=[[8999, 4000, 1500], [8999, 7777, 600]])
+    out = _run(hisa, c, want_flat=False)
+    rep = {}
+    for s in range(2):
+        for i in range(3):
+            t = int(c.qpos[s, i])
+            check_hisa_row(orc, c, s, i, out["idx"][s, i], out["sc"][s, i], out["blk"][s, i], rep)
+            blk = out["blk"][s, i]
+            expect = [j for b in blk[blk >= 0] for j in range(b * B, min((b + 1) * B, t + 1))]
+            np.testing.assert_array_equal(out["idx"][s, i][:len(expect)], np.array(expect, dtype=np.int32))
+            assert np.all(out["idx"][s, i][len(expect):] == -1)
+            o_idx, o_blk, n = orc.block_sparse_query(c.q[s, i], c.w[s, i], c.K[s], t, B, k)
+            np.testing.assert_array_equal(np.sort(blk[blk >= 0]), np.sort(o_blk[o_blk >= 0]))
+    _say(f"block-sparse B={B}: {rep}")
+
+
 def test_out_of_range_positions_select_nothing(hisa):
     import torch
 

@@ -334,3 +334,45 @@ def test_batch_drivers_match_single_queries(orc):
     sub_idx, _, _ = orc.hisa_batch(c.q, c.w, c.qpos, c.K, c.L, c.B, c.m, c.k, sel=[4])
     np.testing.assert_array_equal(sub_idx[1, 1], idx[1, 1])
     assert np.all(sub_idx[0] == -2)
+
+
+# ---------------------------------------------------------------- block-sparse baseline
+
+@pytest.mark.parametrize("seed", range(4))
+def test_block_sparse_is_hisa_with_whole_blocks(orc, seed):
+    # with m = k/B HISA's candidate set has at most k tokens, so its top k keeps
+    # all of them: the same set as keeping the floor(k/B) best whole blocks
+    rng = np.random.default_rng(100 + seed)
+    L, H, d, B = 700, 4, 64, 32
+    c = clustered_case(1, L, 4, H, d, B, 1, 4 * B, seed=200 + seed, latent_block=B,
+                             qpos=[[L - 1, 500, 257, 31]])
+    k = 4 * B + int(rng.integers(0, B))            # a budget that is not a multiple of B
+    for i in range(4):
+        t = int(c.qpos[0, i])
+        idx, blk, n = orc.block_sparse_query(c.q[0, i], c.w[0, i], c.K[0], t, B, k)
+        h_idx, _, h_blk, _, keff = orc.hisa_query(c.q[0, i], c.w[0, i], c.K[0], t, B, k // B, k)
+        assert n == keff
+        np.testing.assert_array_equal(np.sort(idx[:n]), np.sort(h_idx[:keff]))
+        np.testing.assert_array_equal(blk, h_blk)
+        # every selected token lies in a kept block, and each kept block is complete up to t
+        expect = [j for b in blk[blk >= 0] for j in range(b * B, min((b + 1) * B, t + 1))]
+        np.testing.assert_array_equal(idx[:n], np.array(expect, dtype=np.int32))
+        assert np.all(idx[n:] == -1)
+
+
+def test_block_sparse_with_unit_blocks_is_flat(orc):
+    # B = 1: a block is one token and its representative is the token itself,
+    # so the best k blocks are the flat top k
+    c = gaussian_case(1, 300, 3, 4, 64, 1, 1, 40, seed=12, qpos=[[299, 150, 20]])
+    for i in range(3):
+        t = int(c.qpos[0, i])
+        idx, _, n = orc.block_sparse_query(c.q[0, i], c.w[0, i], c.K[0], t, 1, 40)
+        f_idx, _, f_keff = orc.flat_query(c.q[0, i], c.w[0, i], c.K[0], t, 40)
+        assert n == f_keff
+        np.testing.assert_array_equal(np.sort(idx[:n]), np.sort(f_idx[:f_keff]))
+
+
+def test_block_sparse_rejects_budget_below_one_block(orc):
+    c = gaussian_case(1, 100, 1, 4, 64, 64, 1, 10, seed=1)
+    with pytest.raises(ValueError):
+        orc.block_sparse_query(c.q[0, 0], c.w[0, 0], c.K[0], 99, 64, 10)
