@@ -7,10 +7,11 @@
 // token stage; it is rounded once from the exact-order fp64 sum:
 //     mean = bf16_RNE( fp32_RNE( (sum over rows, increasing row, in fp64) / count ) ).
 //
-// A workgroup owns one run of rows (a block, or the head of a query's own
-// block): all 256 threads first copy the rows into LDS with 16-byte loads
-// (every load in flight at once), then one thread per column adds its column
-// from LDS in row order.  The sequential fp64 order is what makes the result
+// Blocks of up to 128 rows: one thread per column loads its column into
+// registers and adds it in row order (pool_append_direct_kernel).  Longer runs
+// (B = 256, and a query's own block in the general path): all 256 threads
+// first copy the rows into LDS with 16-byte loads (every load in flight at
+// once), then one thread per column adds its column from LDS in row order.  The sequential fp64 order is what makes the result
 // independent of how the rows were appended.
 
 #include "hisa_internal.h"
@@ -63,6 +64,37 @@ __device__ __forceinline__ uint16_t staged_column_mean(const uint16_t *__restric
     for (; r < rows; ++r) sum += static_cast<double>(bf16_to_f32(lds[r * d + col]));
     const float mean = static_cast<float>(sum / static_cast<double>(rows));
     return f32_to_bf16_rne(mean);
+}
+
+// Blocks of at most kDirectRows rows: one thread per column loads its whole
+// column straight into registers, then adds it in row order -- no LDS stage
+// and no barrier.  The loads are buffer loads whose row offset is a uniform
+// scalar (rows past the end re-read the last row and are not added), so all
+// of them issue back to back with no per-load address arithmetic; each row's
+// loads across the threads form one coalesced read.
+constexpr int kDirectRows = 128;
+
+__global__ __launch_bounds__(kMaxD) void pool_append_direct_kernel(
+        const uint16_t *__restrict__ K, int64_t k_seq_stride, int d, int B, int64_t blk0,
+        int64_t L_new, uint16_t *__restrict__ pool, int64_t pool_seq_stride) {
+    const int s = blockIdx.y;
+    const int col = threadIdx.x;
+    if (col >= d) return;
+    const int64_t b = blk0 + blockIdx.x;
+    const int64_t r0 = b * B;
+    const int rows = static_cast<int>(((r0 + B < L_new) ? r0 + B : L_new) - r0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(K + s * k_seq_stride + r0 * d), static_cast<short>(0),
+            rows * d * 2, 0x00020000);
+    uint16_t x[kDirectRows];
+#pragma unroll
+    for (int r = 0; r < kDirectRows; ++r)
+        x[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * col, (r < rows ? r : rows - 1) * d * 2, 0);
+    double sum = 0.0;
+#pragma unroll
+    for (int r = 0; r < kDirectRows; ++r)
+        if (r < rows) sum += static_cast<double>(bf16_to_f32(x[r]));
+    pool[s * pool_seq_stride + b * d + col] = f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(rows)));
 }
 
 // grid: (nblk, S).  Recomputes blocks [blk0, blk0 + nblk) over rows < L_new.
@@ -153,6 +185,9 @@ hipError_t launch_own_prefix_mean(const uint16_t *K, int64_t k_seq_stride, int64
 hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
                               int64_t blk0, int64_t nblk, int64_t L_new, uint16_t *pool,
                               int64_t pool_seq_stride, hipStream_t st) {
+    if (B <= kDirectRows)
+        return launch(kKindPoolAppend, pool_append_direct_kernel, dim3(static_cast<uint32_t>(nblk), S),
+                      dim3(kMaxD), 0, st, K, k_seq_stride, d, B, blk0, L_new, pool, pool_seq_stride);
     return launch(kKindPoolAppend, pool_append_kernel, dim3(static_cast<uint32_t>(nblk), S),
                   dim3(kPoolThreads), 0, st, K, k_seq_stride, d, B, blk0, L_new, pool,
                   pool_seq_stride);
