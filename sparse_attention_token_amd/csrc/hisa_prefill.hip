@@ -98,12 +98,6 @@ __global__ __launch_bounds__(kBucketThreads) void hisa_bucket_kernel(FusedArgs a
     }
 }
 
-// Direct-to-LDS staging of one query (q and w) into the padded layout that
-// load_qfrag_lds_w() reads: head row h at h * kStride elements.  One
-// global_load_lds_dwordx4 fills 64 consecutive 16-byte LDS slots, one per
-// lane; slot p holds chunk (p % SL) of head row (p / SL), where SL = kStride/8
-// slots per row and the last slot of a row is padding (never read).  Lanes of
-// padding slots and of rows past H write nothing: those rows are zeroed once.
 // The direct global-to-LDS loads, behind plain device functions: named
 // directly inside a kernel template, the target builtins keep the host pass
 // from emitting some of the template's launch stubs.  Buffer form: the base
@@ -124,28 +118,27 @@ __device__ __forceinline__ void lds_load_b32(__amdgpu_buffer_rsrc_t r, uint32_t 
                                              4, voff, 0, 0, 0);
 }
 
-// Direct-to-LDS staging of one query (q and w) into the padded layout that
-// the scorer reads: head row h at h * kStride elements.  One 16-byte buffer
-// load to LDS fills 64 consecutive 16-byte slots, one per lane; slot p holds
-// chunk (p % SL) of head row (p / SL), where SL = kStride/8 slots per row and
-// the last slot of a row is padding (never read).  Lanes of padding slots and
-// of rows past H write nothing: those rows are zeroed once.
+// Direct-to-LDS staging of one query (q and w) into the swizzled layout of
+// QSwz that score_tiles_lds() reads.  One 16-byte buffer load to LDS fills 64
+// consecutive 16-byte slots, one per lane; lane p's slot is slot p % CPR of
+// head row p / CPR, so the lane loads the chunk that the swizzle places
+// there.  Lanes of rows past H write nothing: those rows are zeroed once.
 template <int MT, int KS, int NW>
 struct QDirect {
-    static constexpr int D = 32 * KS;
-    static constexpr int SL = QStage<KS>::kStride / 8;
-    static constexpr int kSlots = MT * 16 * SL;
-    static constexpr int kInstr = (kSlots + 63) / 64;
-    static constexpr int kPerWave = (kInstr + NW - 1) / NW;   // wave w takes instructions w, w+NW, ...
+    using L = QSwz<KS>;
+    static constexpr int D = L::D, CPR = L::CPR;
+    static constexpr int kSlots = MT * 16 * CPR;
+    static constexpr int kInstr = kSlots / 64;
+    static constexpr int kPerWave = kInstr / NW;              // wave w takes instructions w, w+NW, ...
+    static_assert(kSlots % 64 == 0 && kInstr % NW == 0, "every wave issues whole loads");
     int src[kPerWave];                                        // byte offset in q, or -1: no load
 
     __device__ __forceinline__ void init(int H, int wave, int lane) {
 #pragma unroll
         for (int u = 0; u < kPerWave; ++u) {
-            const int j = wave + u * NW;
-            const int p = 64 * j + lane;
-            const int row = p / SL, col = p - row * SL;
-            src[u] = (j < kInstr && p < kSlots && col < SL - 1 && row < H) ? 2 * (row * D + 8 * col) : -1;
+            const int p = 64 * (wave + u * NW) + lane;
+            const int row = p / CPR, slot = p - row * CPR;
+            src[u] = row < H ? 2 * (row * D + 8 * (slot ^ L::swz(row))) : -1;
         }
     }
     __device__ __forceinline__ void issue(const uint16_t *__restrict__ q, const float *__restrict__ w, int H,
@@ -233,7 +226,7 @@ __global__ __launch_bounds__(kBMThreads) void hisa_refine_bm_kernel(FusedArgs a)
     constexpr int D = 32 * KS;
     constexpr int NW = kBMThreads / 64;
     using QD = QDirect<MT, KS, NW>;
-    constexpr int kQElems = QD::kInstr * 64 * 8;                   // whole instructions, padding included
+    constexpr int kQElems = QD::kSlots * 8;
     constexpr int kRowsPerWave = 16 * NTW;
     __shared__ __attribute__((aligned(16))) uint16_t s_q[kQElems];
     __shared__ __attribute__((aligned(16))) float s_w[64];
@@ -275,8 +268,7 @@ __global__ __launch_bounds__(kBMThreads) void hisa_refine_bm_kernel(FusedArgs a)
     }
     // rows past H read as zero (q) with weight zero
     if (a.H < MT * 16) {
-        constexpr int ST = QStage<KS>::kStride;
-        for (int x = tid; x < (MT * 16 - a.H) * ST; x += kBMThreads) s_q[a.H * ST + x] = 0;
+        for (int x = tid; x < (MT * 16 - a.H) * D; x += kBMThreads) s_q[a.H * D + x] = 0;
         if (tid < 64) s_w[tid] = 0.0f;
     }
     __syncthreads();
@@ -327,7 +319,7 @@ __global__ __launch_bounds__(kBMThreads) void hisa_blocks_bm_kernel(FusedArgs a)
     constexpr int NW = kBMThreads / 64;
     constexpr int NTW = kBlkTileRows / (16 * NW);
     using QD = QDirect<MT, KS, NW>;
-    constexpr int kQElems = QD::kInstr * 64 * 8;
+    constexpr int kQElems = QD::kSlots * 8;
     __shared__ __attribute__((aligned(16))) uint16_t s_q[2][kQElems];
     __shared__ __attribute__((aligned(16))) float s_w[2][64];
     __shared__ int32_t s_qi[kBlkChunk];
@@ -368,10 +360,9 @@ __global__ __launch_bounds__(kBMThreads) void hisa_blocks_bm_kernel(FusedArgs a)
         load_row_frag<KS>(kb[nt], p < a.nblk ? pool + static_cast<int64_t>(p) * D : nullptr, lane);
     }
     if (a.H < MT * 16) {
-        constexpr int ST = QStage<KS>::kStride;
-        for (int x = tid; x < 2 * (MT * 16 - a.H) * ST; x += kBMThreads) {
-            const int bf = x / ((MT * 16 - a.H) * ST), r = x - bf * (MT * 16 - a.H) * ST;
-            s_q[bf][a.H * ST + r] = 0;
+        for (int x = tid; x < 2 * (MT * 16 - a.H) * D; x += kBMThreads) {
+            const int bf = x / ((MT * 16 - a.H) * D), r = x - bf * (MT * 16 - a.H) * D;
+            s_q[bf][a.H * D + r] = 0;
         }
         for (int x = tid; x < 2 * 64; x += kBMThreads) s_w[x >> 6][x & 63] = 0.0f;
     }

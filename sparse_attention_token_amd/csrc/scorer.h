@@ -163,6 +163,18 @@ __device__ __forceinline__ float relu_bits(float x) {
     return __int_as_float(max(__float_as_int(x), 0));
 }
 
+// Sum of x over the four 16-lane rows of a wave, (x_r + x_(r^1)) summed
+// across the two halves, returned to every lane.  The two lane swaps
+// (v_permlane16_swap, v_permlane32_swap) are VALU operations rather than LDS
+// permutes; addition is commutative, so both lanes of a swapped pair compute
+// the same bits, as an xor-shuffle sum in the same order would.
+__device__ __forceinline__ float rows_sum(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Score of row (lane & 15) for this query; every lane of the row's column
 // group returns the same value.
 template <int MT, int KS>
@@ -177,9 +189,7 @@ __device__ __forceinline__ float score_rows(const QFrag<MT, KS> &f, const bf16x8
 #pragma unroll
         for (int r = 0; r < 4; ++r) part = __builtin_fmaf(f.wv[mt][r], relu_bits(acc[r]), part);
     }
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    return part;
+    return rows_sum(part);
 }
 
 // NT 16-row tiles of one query at once with the fragments in registers; per
@@ -206,21 +216,37 @@ __device__ __forceinline__ void score_tiles_frag(const QFrag<MT, KS> &f, const b
             for (int r = 0; r < 4; ++r) part[nt] = __builtin_fmaf(f.wv[mt][r], relu_bits(acc[nt][r]), part[nt]);
     }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) part[nt] += __shfl_xor(part[nt], 16);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) out[nt] = part[nt] + __shfl_xor(part[nt], 32);
+    for (int nt = 0; nt < NT; ++nt) out[nt] = rows_sum(part[nt]);
 }
 
-// NT 16-row tiles of one query at once, q and w read from LDS (padded layout
-// of QStage, w zero past H).  Per tile the arithmetic is exactly score_rows():
-// the same MFMA sequence per head group and the same fused multiply-add order
-// over heads, then the same two xor-shuffles.  Working one head group at a
-// time over all tiles keeps NT accumulators in flight (independent MFMA
-// chains) and needs only one head group's fragments in registers.
+// Swizzled LDS stage of one query: head row h holds its D elements at h * D
+// with no padding, and its 16-byte chunk c sits in slot c ^ swz(h), where
+// swz(h) is the low four bits of h with bits 0 and 1 exchanged (masked to
+// the chunks of a row).  The 16x16x32 operand reads (16 rows x 4 chunks per
+// wave-wide 16-byte load) then meet no LDS bank twice in one cycle; over
+// rows padded to D + 8 elements they did, about 4 extra cycles per load as
+// counted by the LDS bank-conflict counter.
+template <int KS>
+struct QSwz {
+    static constexpr int D = 32 * KS, CPR = D / 8;   // 16-byte chunks per row
+    __device__ static __forceinline__ int swz(int h) {
+        const int r = h & 15;
+        return ((r & 12) | ((r & 1) << 1) | ((r >> 1) & 1)) & (CPR - 1);
+    }
+    // element offset of chunk c of head row h
+    __device__ static __forceinline__ int elem(int h, int c) { return h * D + 8 * (c ^ swz(h)); }
+};
+
+// NT 16-row tiles of one query at once, q and w read from LDS (swizzled
+// layout of QSwz, w zero past H).  Per tile the arithmetic is exactly
+// score_rows(): the same MFMA sequence per head group and the same fused
+// multiply-add order over heads, then the same row sum.  Working one head
+// group at a time over all tiles keeps NT accumulators in flight (independent
+// MFMA chains) and needs only one head group's fragments in registers.
 template <int MT, int KS, int NT>
 __device__ __forceinline__ void score_tiles_lds(const uint16_t *s_q, const float *s_w,
                                                 const bf16x8 (&kb)[NT][KS], float (&out)[NT], int lane) {
-    constexpr int ST = QStage<KS>::kStride;
+    using L = QSwz<KS>;
     const int n = lane & 15, g = lane >> 4;
     float part[NT];
 #pragma unroll
@@ -229,7 +255,7 @@ __device__ __forceinline__ void score_tiles_lds(const uint16_t *s_q, const float
     for (int mt = 0; mt < MT; ++mt) {
         bf16x8 qa[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qa[ks] = load_bf16x8(s_q + (16 * mt + n) * ST + 32 * ks + 8 * g);
+        for (int ks = 0; ks < KS; ++ks) qa[ks] = load_bf16x8(s_q + 16 * mt * L::D + L::elem(n, 4 * ks + g));
         float wv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) wv[r] = s_w[16 * mt + 4 * g + r];
@@ -247,9 +273,7 @@ __device__ __forceinline__ void score_tiles_lds(const uint16_t *s_q, const float
             for (int r = 0; r < 4; ++r) part[nt] = __builtin_fmaf(wv[r], relu_bits(acc[nt][r]), part[nt]);
     }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) part[nt] += __shfl_xor(part[nt], 16);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) out[nt] = part[nt] + __shfl_xor(part[nt], 32);
+    for (int nt = 0; nt < NT; ++nt) out[nt] = rows_sum(part[nt]);
 }
 
 }  // namespace hisa
