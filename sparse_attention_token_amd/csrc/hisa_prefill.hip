@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kBMThreads) void hisa_refine_bm_kernel(FusedArgs a)
 // block's representative differs per query; hisa_topm_kernel scores it).
 // blk_keys[qi][b] receives the key of block b for b < b_t.
 constexpr int kBlkTileRows = 128;
-constexpr int kBlkChunk = 32;          // queries per workgroup: enough workgroups to fill the GPU
+constexpr int kBlkChunk = 16;          // queries per workgroup: enough workgroups to fill the GPU
 
 template <int MT, int KS>
 __global__ __launch_bounds__(kBMThreads) void hisa_blocks_bm_kernel(FusedArgs a) {
@@ -320,8 +320,8 @@ __global__ __launch_bounds__(kBMThreads) void hisa_blocks_bm_kernel(FusedArgs a)
     constexpr int NTW = kBlkTileRows / (16 * NW);
     using QD = QDirect<MT, KS, NW>;
     constexpr int kQElems = QD::kSlots * 8;
-    __shared__ __attribute__((aligned(16))) uint16_t s_q[2][kQElems];
-    __shared__ __attribute__((aligned(16))) float s_w[2][64];
+    __shared__ __attribute__((aligned(16))) uint16_t s_q[kQElems];
+    __shared__ __attribute__((aligned(16))) float s_w[64];
     __shared__ int32_t s_qi[kBlkChunk];
     __shared__ int32_t s_bt[kBlkChunk];
     __shared__ uint32_t s_n;
@@ -360,36 +360,32 @@ __global__ __launch_bounds__(kBMThreads) void hisa_blocks_bm_kernel(FusedArgs a)
         load_row_frag<KS>(kb[nt], p < a.nblk ? pool + static_cast<int64_t>(p) * D : nullptr, lane);
     }
     if (a.H < MT * 16) {
-        for (int x = tid; x < 2 * (MT * 16 - a.H) * D; x += kBMThreads) {
-            const int bf = x / ((MT * 16 - a.H) * D), r = x - bf * (MT * 16 - a.H) * D;
-            s_q[bf][a.H * D + r] = 0;
-        }
-        for (int x = tid; x < 2 * 64; x += kBMThreads) s_w[x >> 6][x & 63] = 0.0f;
+        for (int x = tid; x < (MT * 16 - a.H) * D; x += kBMThreads) s_q[a.H * D + x] = 0;
+        if (tid < 64) s_w[tid] = 0.0f;
     }
     __syncthreads();
     const int np = static_cast<int>(s_n);
     if (np == 0) return;
 
+    // One LDS stage, as in the refinement: a second stage gains nothing here,
+    // since every LDS read issued after a direct-to-LDS load waits for it,
+    // while it would halve the workgroups that fit on a CU.
     QD qd;
     qd.init(a.H, wave, lane);
-    qd.issue(a.q + static_cast<int64_t>(s_qi[0]) * a.H * D, a.w + static_cast<int64_t>(s_qi[0]) * a.H, a.H,
-             s_q[0], s_w[0], wave, lane);
     float v[NTW];
     uint32_t *out = nullptr;
     int bt = 0;
     for (int i = 0; i < np; ++i) {
-        const int buf = i & 1;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (i + 1 < np) {
-            const int qn = s_qi[i + 1];
-            qd.issue(a.q + static_cast<int64_t>(qn) * a.H * D, a.w + static_cast<int64_t>(qn) * a.H, a.H,
-                     s_q[buf ^ 1], s_w[buf ^ 1], wave, lane);
-        }
+        if (i > 0) __syncthreads();          // every wave is done reading the stage
+        const int qn = s_qi[i];
+        qd.issue(a.q + static_cast<int64_t>(qn) * a.H * D, a.w + static_cast<int64_t>(qn) * a.H, a.H, s_q, s_w,
+                 wave, lane);
+        __builtin_amdgcn_s_waitcnt(0);       // this query's LDS loads (and older stores) are done
+        __syncthreads();                     // ... in every wave
         if (out) store_blocks<NTW>(out, v, p0, bt, lane);
-        out = a.blk_keys + static_cast<int64_t>(s_qi[i]) * a.blk_stride + p0;
+        out = a.blk_keys + static_cast<int64_t>(qn) * a.blk_stride + p0;
         bt = s_bt[i];
-        score_tiles_lds<MT, KS, NTW>(s_q[buf], s_w[buf], kb, v, lane);
+        score_tiles_lds<MT, KS, NTW>(s_q, s_w, kb, v, lane);
     }
     store_blocks<NTW>(out, v, p0, bt, lane);
 }
