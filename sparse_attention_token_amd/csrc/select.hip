@@ -40,6 +40,14 @@ __device__ __forceinline__ int64_t row_length(const SelectArgs &a, int qi) {
     return t + 1;
 }
 
+// Store to element `op` of a row through a 32-bit byte offset (op < 2^30
+// always: rows hold at most k entries), which lets the base stay in scalar
+// registers instead of forming a 64-bit address per element.
+template <typename T>
+__device__ __forceinline__ void put(T *row, uint32_t op, T v) {
+    *reinterpret_cast<T *>(reinterpret_cast<char *>(row) + (op << 2)) = v;
+}
+
 template <int R>
 __device__ __forceinline__ void load_run(const uint32_t *__restrict__ keys, int64_t base, int64_t n,
                                          uint32_t (&kv)[R]) {
@@ -79,17 +87,18 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     }
     const SelectResult res = block_radix_select<NT, R>(kv, static_cast<uint32_t>(a.kout), sc);
     if (res.keff > 0) {
-        const int B = a.B;
+        // refine mode: R divides B (B is 64 or 128, R at most 32), so the
+        // thread's R positions lie in one kept block
+        int32_t id0 = tid * R;
+        if (MODE == kScoreRefine && id0 < n) {
+            const int slot = id0 / a.B;
+            id0 = s_sel[slot] * a.B + (id0 - slot * a.B);
+        }
         block_compact<NT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
-            const int pos = tid * R + r;
-            int32_t id = pos;
-            if (MODE == kScoreRefine) {
-                const int slot = pos / B;
-                id = s_sel[slot] * B + (pos - slot * B);
-            }
-            out[op] = id;
-            if (osc) osc[op] = key_to_score(key);
-            if (out2) out2[op] = id;
+            const int32_t id = id0 + r;
+            put(out, op, id);
+            if (osc) put(osc, op, key_to_score(key));
+            if (out2) put(out2, op, id);
         });
     }
     for (int j = static_cast<int>(res.keff) + tid; j < a.kout; j += NT) {
@@ -123,20 +132,19 @@ __global__ __launch_bounds__(kNT) void select_chunk_kernel(SelectArgs a, const u
     const SelectResult res = block_radix_select<kNT, R>(kv, static_cast<uint32_t>(a.kout), sc);
     if (res.keff > 0) {
         const int32_t *irow = ids_in ? ids_in + static_cast<int64_t>(qi) * in_stride + c0 : nullptr;
+        // position ids: the thread's R positions lie in one kept block in
+        // refine mode (R = 32 divides B, and chunks start on block bounds)
+        const int64_t p0 = c0 + static_cast<int64_t>(tid) * R;
+        int32_t id0 = static_cast<int32_t>(p0);
+        if (!irow && MODE == kScoreRefine && p0 < n_row) {
+            const int64_t slot = p0 / a.B;
+            id0 = static_cast<int32_t>(static_cast<int64_t>(a.sel_blk[static_cast<int64_t>(qi) * a.m + slot]) * a.B +
+                                       (p0 - slot * a.B));
+        }
         block_compact<kNT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
-            const int64_t p = static_cast<int64_t>(tid) * R + r;
-            int32_t id;
-            if (irow) {
-                id = irow[p];
-            } else if (MODE == kScoreRefine) {
-                const int64_t pos = c0 + p;
-                const int64_t slot = pos / a.B;
-                id = static_cast<int32_t>(static_cast<int64_t>(a.sel_blk[static_cast<int64_t>(qi) * a.m + slot]) * a.B + (pos - slot * a.B));
-            } else {
-                id = static_cast<int32_t>(c0 + p);
-            }
-            ko[op] = key;
-            io[op] = id;
+            const int32_t id = irow ? irow[static_cast<int64_t>(tid) * R + r] : id0 + r;
+            put(ko, op, key);
+            put(io, op, id);
         });
     }
     for (int j = static_cast<int>(res.keff) + tid; j < a.kout; j += kNT) {
@@ -163,9 +171,9 @@ __global__ __launch_bounds__(kNT) void select_final_kernel(SelectArgs a, const u
     if (res.keff > 0) {
         block_compact<kNT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
             const int32_t id = irow[tid * R + r];
-            out[op] = id;
-            if (osc) osc[op] = key_to_score(key);
-            if (out2) out2[op] = id;
+            put(out, op, id);
+            if (osc) put(osc, op, key_to_score(key));
+            if (out2) put(out2, op, id);
         });
     }
     for (int j = static_cast<int>(res.keff) + tid; j < a.kout; j += kNT) {

@@ -150,6 +150,26 @@ __device__ __forceinline__ SelectResult block_radix_select(const uint32_t (&kv)[
     return SelectResult{prefix, need, keff};
 }
 
+// Hands the thread's kept keys to emit(slot, r, key) (r = index into its
+// run), given the counts of keys above K* and equal to K* in earlier runs.  A
+// key above K* is kept at slot gt_before + min(eq_before, need_eq); a key
+// equal to K* is kept while eq_before < need_eq, at slot gt_before + eq_before
+// (the same expression).  Only the store is predicated.
+template <int R, typename Emit>
+__device__ __forceinline__ void emit_kept(const uint32_t (&kv)[R], const SelectResult &res, uint32_t gt_before,
+                                          uint32_t eq_before, Emit &&emit) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t key = kv[r];
+        const bool gt = key > res.kstar, eq = key == res.kstar;
+        const uint32_t op = gt_before + (eq_before < res.need_eq ? eq_before : res.need_eq);
+        const bool keep = gt || (eq && eq_before < res.need_eq);
+        gt_before += gt ? 1u : 0u;
+        eq_before += eq ? 1u : 0u;
+        if (keep && op < res.keff) emit(op, r, key);   // op < keff always holds for a kept key; guards the write
+    }
+}
+
 // Slots for the kept keys, in position order; calls emit(slot, r, key) for
 // the thread's kept keys (r = index into its run).
 template <int NT, int R, typename Emit>
@@ -164,20 +184,7 @@ __device__ __forceinline__ void block_compact(const uint32_t (&kv)[R], const Sel
     const uint32_t v = (cg << 16) | ce;                // per-block counts stay below 2^16
     uint32_t total;
     const uint32_t ex = block_exclusive<NT>(v, total, sc);
-    uint32_t gt_before = ex >> 16, eq_before = ex & 0xFFFFu;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const uint32_t key = kv[r];
-        uint32_t op = 0xFFFFFFFFu;
-        if (key > res.kstar) {
-            op = gt_before + (eq_before < res.need_eq ? eq_before : res.need_eq);
-            ++gt_before;
-        } else if (key == res.kstar) {
-            if (eq_before < res.need_eq) op = gt_before + eq_before;
-            ++eq_before;
-        }
-        if (op < res.keff) emit(op, r, key);           // always true for a kept key; guards the write
-    }
+    emit_kept<R>(kv, res, ex >> 16, ex & 0xFFFFu, emit);
 }
 
 // ---------------------------------------------------------------- one wave
@@ -223,20 +230,7 @@ __device__ __forceinline__ void wave_compact(const uint32_t (&kv)[R], const Sele
     }
     const uint32_t v = (cg << 16) | ce;
     const uint32_t ex = wave_prefix_incl(v) - v;
-    uint32_t gt_before = ex >> 16, eq_before = ex & 0xFFFFu;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const uint32_t key = kv[r];
-        uint32_t op = 0xFFFFFFFFu;
-        if (key > res.kstar) {
-            op = gt_before + (eq_before < res.need_eq ? eq_before : res.need_eq);
-            ++gt_before;
-        } else if (key == res.kstar) {
-            if (eq_before < res.need_eq) op = gt_before + eq_before;
-            ++eq_before;
-        }
-        if (op < res.keff) emit(op, r, key);
-    }
+    emit_kept<R>(kv, res, ex >> 16, ex & 0xFFFFu, emit);
 }
 
 }  // namespace hisa
