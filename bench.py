@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--no-flat", action="store_true", help="skip the flat DSA baseline")
     p.add_argument("--profile-steps", type=int, default=None,
                    help="eager steps bracketed by per-kernel HIP events")
+    p.add_argument("--sequences", type=int, default=None, metavar="S",
+                   help="batch size of a decode workload (1..3) in place of its own, for a batch "
+                        "sweep; the line then names the workload with an _S<n> suffix")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB three times (the known-size "
                         "reference that scales the HBM byte counters) and exit")
@@ -143,7 +146,7 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
         return
     hisa.lib()
-    case = synth.workload(args.workload)
+    case = synth.workload(args.workload, args.sequences)
     S, T, H, d, L, B, m, k = case.S, case.T, case.H, case.d, case.L, case.B, case.m, case.k
     prefill = T > 1
     steps = args.steps if args.steps is not None else (20 if prefill else 400)

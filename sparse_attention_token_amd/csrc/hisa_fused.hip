@@ -49,7 +49,11 @@ constexpr int kK1WaveMax = 64 * 32;                       // rows the one-wave s
 constexpr int kK2Threads = 256;
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeMaxM = 1024;                         // kept blocks staged in LDS (decode mode)
-constexpr int kDecodeMaxQueries = 32;                     // decode mode repeats the block stage per tile
+// Decode mode repeats the block stage in every tile's workgroup, which stops
+// paying off with more queries.  Measured per step at 32K keys (one launch
+// against the general blocks + refine path): 8 queries 27.4 vs 28.4 us,
+// 16 queries 31.8 vs 31.9 us, 24 queries 45.5 vs 37.9 us.
+constexpr int kDecodeMaxQueries = 16;
 constexpr int kDecodeRowsWide = 256;                      // candidate rows per decode workgroup, big grids
 constexpr int kDecodeRowsNarrow = 128;                    // ... and when fewer than kDecodeWideMin would run
 constexpr int kDecodeWideMin = 256;

@@ -164,19 +164,24 @@ WORKLOADS = {
 }
 
 
-def workload(i: int) -> Case:
+def workload(i: int, sequences: int | None = None) -> Case:
+    """Workload i; `sequences` replaces the batch size of a decode workload
+    (1..3) to study how the decode path scales with batch (the name then gains
+    an _S<n> suffix)."""
     seed = SEED_BASE + i
+    if sequences is not None and i not in (1, 2, 3):
+        raise ValueError("only the decode workloads (1..3) take another batch size")
     if i == 0:
         c = gaussian_case(1, 1024, 16, 4, 64, 64, 4, 64, seed, w_scale=0.5)
     elif i == 1:
-        c = clustered_case(8, 32768, 1, 64, 128, 128, 64, 2048, seed)
+        c = clustered_case(sequences or 8, 32768, 1, 64, 128, 128, 64, 2048, seed)
     elif i == 2:
-        c = clustered_case(4, 65536, 1, 64, 128, 128, 64, 2048, seed, needles_per_seq=8)
+        c = clustered_case(sequences or 4, 65536, 1, 64, 128, 128, 64, 2048, seed, needles_per_seq=8)
     elif i == 3:
-        c = clustered_case(2, 131072 + 77, 1, 64, 128, 128, 128, 2048, seed, L_bulk=131072)
+        c = clustered_case(sequences or 2, 131072 + 77, 1, 64, 128, 128, 128, 2048, seed, L_bulk=131072)
     elif i == 4:
         c = clustered_case(1, 131072, 4096, 64, 128, 128, 64, 2048, seed)
     else:
         raise ValueError(f"no workload {i}")
-    c.name = WORKLOADS[i]
+    c.name = WORKLOADS[i] + (f"_S{sequences}" if sequences is not None else "")
     return c

@@ -137,6 +137,8 @@ SMALL = [
     # decode beyond 256 blocks: block stage in its own kernel (own block
     # recomputed there for positions other than the last)
     ("decode_two_kernel_d64_313blk", 2, 20000, 6, 16, 64, 64, 20, 400, "clustered"),
+    # just above the one-launch decode's 16 queries: the query-major fused path
+    ("fused_17_queries", 1, 5000, 17, 64, 128, 128, 8, 512, "clustered"),
     # more than 2048 blocks: the block stage selects with the whole workgroup
     ("blocks_2344_workgroup_select", 1, 300000, 2, 4, 64, 128, 8, 256, "gaussian"),
 ]
