@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define HISA_ABI_VERSION 1
+#define HISA_ABI_VERSION 2   /* 2: adds hisa_append_index */
 
 #if defined(__GNUC__)
 #define HISA_API __attribute__((visibility("default")))
@@ -136,6 +136,33 @@ HISA_API int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos,
                         int S, int T, int H, int d, int B, int m, int k,
                         int32_t *out_idx, float *out_score, int32_t *out_blk,
                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * hisa_append_index -- one decode step in one call: exactly
+ *     hisa_pool_append(K, k_seq_stride, S, d, B, L_old, L_new, pool_mean, pool_seq_stride, stream);
+ *     hisa_index(q, w, qpos, K, k_seq_stride, L_new, pool_mean, pool_seq_stride,
+ *                S, T, H, d, B, m, k, out_idx, out_score, out_blk, ws, ws_bytes, stream);
+ * with the same outputs and the pool left with the same bits.  (The pages keep
+ * the block summaries up to date as keys are appended: page "Hierarchical
+ * Indexing Makes Sparse Attention Actually Fast", section "HISA's Approach:
+ * Hierarchical Summarization of the KV Cache".)
+ * When qpos is NULL, every appended row lies in the last block
+ * (floor(L_old/B) == floor((L_new-1)/B) and L_old < L_new) and the batch does
+ * not take the block-by-block prefill path (it does when T >= 128), the last
+ * block's mean is computed once, by the block stage of the query at
+ * t = L_new-1, and stored to the pool from there instead of in a launch of
+ * its own.  Otherwise the two calls run as written above.
+ *   The pool must be current through row L_old-1 on entry (as for a
+ *   hisa_pool_append() / hisa_index() pair).  Workspace: hisa_index_workspace()
+ *   with L = L_new.  Argument checks and errors are those of the two calls;
+ *   nothing is enqueued when either would reject its arguments.
+ */
+HISA_API int hisa_append_index(const uint16_t *K, int64_t k_seq_stride, int64_t L_old, int64_t L_new,
+                               uint16_t *pool_mean, int64_t pool_seq_stride,
+                               const uint16_t *q, const float *w, const int32_t *qpos,
+                               int S, int T, int H, int d, int B, int m, int k,
+                               int32_t *out_idx, float *out_score, int32_t *out_blk,
+                               void *ws, size_t ws_bytes, void *stream);
 
 /* Bytes of device workspace dsa_flat_index needs for these sizes (0 on bad sizes). */
 HISA_API size_t dsa_flat_workspace(int S, int T, int H, int d, int64_t L, int k);

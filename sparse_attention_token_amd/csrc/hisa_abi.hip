@@ -53,6 +53,17 @@ int check_pool(const uint16_t *pool, int64_t pool_seq_stride, int S, int d, int6
     return HISA_OK;
 }
 
+int check_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B, int64_t L_old, int64_t L_new,
+                 const uint16_t *pool_mean, int64_t pool_seq_stride) {
+    if (S < 1 || d < 1 || B < 1 || L_old < 0 || L_new < L_old) return HISA_ERR_ARG;
+    if (d != 64 && d != 128) return HISA_ERR_UNSUPPORTED;
+    if (!block_size_ok(B)) return HISA_ERR_UNSUPPORTED;
+    if (L_new >= (int64_t{1} << 31) || S > 65535) return HISA_ERR_UNSUPPORTED;
+    const int st = check_cache(K, k_seq_stride, S, d, L_new);
+    if (st != HISA_OK) return st;
+    return check_pool(pool_mean, pool_seq_stride, S, d, L_new, B);
+}
+
 // ---------------------------------------------------------------- workspace layouts
 struct StageBufs {
     size_t keys[2], ids[2];
@@ -187,13 +198,7 @@ const char *hisa_status_string(int status) {
 int hisa_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
                      int64_t L_old, int64_t L_new, uint16_t *pool_mean, int64_t pool_seq_stride,
                      void *stream) {
-    if (S < 1 || d < 1 || B < 1 || L_old < 0 || L_new < L_old) return HISA_ERR_ARG;
-    if (d != 64 && d != 128) return HISA_ERR_UNSUPPORTED;
-    if (!block_size_ok(B)) return HISA_ERR_UNSUPPORTED;
-    if (L_new >= (int64_t{1} << 31) || S > 65535) return HISA_ERR_UNSUPPORTED;
-    int st = check_cache(K, k_seq_stride, S, d, L_new);
-    if (st != HISA_OK) return st;
-    st = check_pool(pool_mean, pool_seq_stride, S, d, L_new, B);
+    const int st = check_append(K, k_seq_stride, S, d, B, L_old, L_new, pool_mean, pool_seq_stride);
     if (st != HISA_OK) return st;
     if (L_old == L_new) return HISA_OK;
     const int64_t blk0 = L_old / B;
@@ -209,11 +214,14 @@ size_t hisa_index_workspace(int S, int T, int H, int d, int64_t L, int B, int m,
     return hisa_layout(S, T, d, L, B, m, k).total;
 }
 
-int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
-               int64_t k_seq_stride, int64_t L, const uint16_t *pool_mean,
-               int64_t pool_seq_stride, int S, int T, int H, int d, int B, int m, int k,
-               int32_t *out_idx, float *out_score, int32_t *out_blk, void *ws, size_t ws_bytes,
-               void *stream) {
+}  // extern "C"
+
+namespace {
+
+int check_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
+                int64_t k_seq_stride, int64_t L, const uint16_t *pool_mean, int64_t pool_seq_stride,
+                int S, int T, int H, int d, int B, int m, int k, const int32_t *out_idx, const void *ws,
+                size_t ws_bytes) {
     int st = check_query_shape(S, T, H, d, L, k);
     if (st != HISA_OK) return st;
     st = check_hisa_params(B, m);
@@ -224,11 +232,21 @@ int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uin
     if (st != HISA_OK) return st;
     st = check_pool(pool_mean, pool_seq_stride, S, d, L, B);
     if (st != HISA_OK) return st;
-    const HisaLayout lay = hisa_layout(S, T, d, L, B, m, k);
     if (!ws) return HISA_ERR_ARG;
-    if (ws_bytes < lay.total) return HISA_ERR_WORKSPACE;
+    if (ws_bytes < hisa_layout(S, T, d, L, B, m, k).total) return HISA_ERR_WORKSPACE;
+    return HISA_OK;
+}
 
-    hipStream_t hs = static_cast<hipStream_t>(stream);
+// hisa_index once its arguments are checked.  pool_out (the pool itself, or
+// null): the fused block stage also stores the own-block mean of the query at
+// t = L-1 (only on paths where pool_update_fusable() holds).
+int run_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
+              int64_t k_seq_stride, int64_t L, const uint16_t *pool_mean, uint16_t *pool_out,
+              int64_t pool_seq_stride, int S, int T, int H, int d, int B, int m, int k,
+              int32_t *out_idx, float *out_score, int32_t *out_blk, void *ws, hipStream_t hs) {
+    int st = HISA_OK;
+    const HisaLayout lay = hisa_layout(S, T, d, L, B, m, k);
+
     char *base = align_ptr(ws);
     uint16_t *own_rep = reinterpret_cast<uint16_t *>(base + lay.own_rep);
     uint32_t *blk_keys = reinterpret_cast<uint32_t *>(base + lay.blk_keys);
@@ -252,6 +270,7 @@ int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uin
         fa.nblk = static_cast<int>(ceil_div(L, B));
         fa.blk_keys = blk_keys;
         fa.blk_stride = lay.blk_stride;
+        fa.pool_out = pool_out;
         if (block_major_mode(S, T, d, L, B, m)) {
             fa.bucket_off = reinterpret_cast<int32_t *>(base + lay.bucket_off);
             fa.bucket_ent = reinterpret_cast<uint32_t *>(base + lay.bucket_ent);
@@ -297,6 +316,49 @@ int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uin
     se.kout = k; se.sel_blk = sel_blk;
     se.out_id = out_idx; se.out_score = out_score; se.out_id_copy = nullptr;
     return hip_status(launch_select(kScoreRefine, se, nq, static_cast<int64_t>(m) * B, hs));
+}
+}  // namespace
+
+extern "C" {
+
+int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
+               int64_t k_seq_stride, int64_t L, const uint16_t *pool_mean,
+               int64_t pool_seq_stride, int S, int T, int H, int d, int B, int m, int k,
+               int32_t *out_idx, float *out_score, int32_t *out_blk, void *ws, size_t ws_bytes,
+               void *stream) {
+    const int st = check_index(q, w, qpos, K, k_seq_stride, L, pool_mean, pool_seq_stride, S, T, H, d, B, m, k,
+                               out_idx, ws, ws_bytes);
+    if (st != HISA_OK) return st;
+    return run_index(q, w, qpos, K, k_seq_stride, L, pool_mean, nullptr, pool_seq_stride, S, T, H, d, B, m, k,
+                     out_idx, out_score, out_blk, ws, static_cast<hipStream_t>(stream));
+}
+
+int hisa_append_index(const uint16_t *K, int64_t k_seq_stride, int64_t L_old, int64_t L_new,
+                      uint16_t *pool_mean, int64_t pool_seq_stride, const uint16_t *q, const float *w,
+                      const int32_t *qpos, int S, int T, int H, int d, int B, int m, int k, int32_t *out_idx,
+                      float *out_score, int32_t *out_blk, void *ws, size_t ws_bytes, void *stream) {
+    int st = check_append(K, k_seq_stride, S, d, B, L_old, L_new, pool_mean, pool_seq_stride);
+    if (st != HISA_OK) return st;
+    st = check_index(q, w, qpos, K, k_seq_stride, L_new, pool_mean, pool_seq_stride, S, T, H, d, B, m, k, out_idx,
+                     ws, ws_bytes);
+    if (st != HISA_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    // The fused form needs the query at t = L_new-1 in every sequence (no
+    // explicit positions) and the appended rows all in its own block.
+    const bool fuse = qpos == nullptr && L_old < L_new && L_old / B == (L_new - 1) / B &&
+                      pool_update_fusable(S, T, d, L_new, B, m);
+    if (!fuse) {
+        if (L_old < L_new) {
+            const int64_t blk0 = L_old / B;
+            st = hip_status(launch_pool_append(K, k_seq_stride, S, d, B, blk0, (L_new - 1) / B - blk0 + 1, L_new,
+                                               pool_mean, pool_seq_stride, hs));
+            if (st != HISA_OK) return st;
+        }
+        return run_index(q, w, qpos, K, k_seq_stride, L_new, pool_mean, nullptr, pool_seq_stride, S, T, H, d, B, m,
+                         k, out_idx, out_score, out_blk, ws, hs);
+    }
+    return run_index(q, w, qpos, K, k_seq_stride, L_new, pool_mean, pool_mean, pool_seq_stride, S, T, H, d, B, m, k,
+                     out_idx, out_score, out_blk, ws, hs);
 }
 
 size_t dsa_flat_workspace(int S, int T, int H, int d, int64_t L, int k) {

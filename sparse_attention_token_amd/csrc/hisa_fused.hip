@@ -103,10 +103,13 @@ struct BlockStageLds {
 // its own block is already the mean of rows b_t*B .. t (the pool is current
 // through row L-1), so it is scored like the others; any other query's own
 // block is recomputed from K.
+// With a.pool_out set, every own block is recomputed from K, and when
+// writer is true the query at t = L-1 also stores its own block's mean into
+// the pool.
 template <int MT, int KS, int NT, int TB>
 __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, int64_t t,
                                             BlockStageLds<KS, NT> &L, uint32_t *s_keys,
-                                            QFrag<MT, KS> &f) {
+                                            QFrag<MT, KS> &f, bool writer) {
     constexpr int D = 32 * KS;
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -115,7 +118,8 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
     const int nb = static_cast<int>(bt + 1);
     const int64_t r0 = bt * a.B;
     const int own_rows = static_cast<int>(t + 1 - r0);
-    const bool own_in_pool = t == a.L - 1;
+    const bool own_in_pool = t == a.L - 1 && a.pool_out == nullptr;
+    const bool write_pool = writer && a.pool_out != nullptr && t == a.L - 1;
     uint16_t *s_own = reinterpret_cast<uint16_t *>(L.own);
 
     // pool rows 0 .. full-1, 16 per tile, tile i on wave i % NW
@@ -179,7 +183,9 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
                 for (int j = 0; j < 8; ++j) sum += static_cast<double>(x[j]);
             }
             for (; r < own_rows; ++r) sum += static_cast<double>(bf16_to_f32(s_own[r * D + tid]));
-            L.mean[tid] = f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(own_rows)));
+            const uint16_t mv = f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(own_rows)));
+            L.mean[tid] = mv;
+            if (write_pool) a.pool_out[s * a.pool_seq_stride + bt * D + tid] = mv;
         }
         __syncthreads();
         if (wave == 0) {
@@ -227,7 +233,7 @@ __global__ __launch_bounds__(kK1Threads) void hisa_blocks_topm_kernel(FusedArgs 
     }
     const int nb = static_cast<int>(t / a.B + 1);
     QFrag<MT, KS> f;
-    block_stage<MT, KS, kK1Threads, 1>(a, qi, s, t, L, s_keys, f);
+    block_stage<MT, KS, kK1Threads, 1>(a, qi, s, t, L, s_keys, f, true);
 
     uint32_t keff;
     if (nb <= kK1WaveMax) {
@@ -330,7 +336,7 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_decode_kernel(FusedArgs a
     if (tile0 >= npos) return;
 
     QFrag<MT, KS> f;
-    block_stage<MT, KS, kDecodeThreads, 4>(a, qi, s, t, L, s_keys, f);
+    block_stage<MT, KS, kDecodeThreads, 4>(a, qi, s, t, L, s_keys, f, lead);
     if (wave == 0) {
         const uint32_t ke = block_topm_wave(s_keys, nb, a.m, [&](uint32_t op, int pos) {
             s_sel[op] = pos;
@@ -397,7 +403,8 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs 
     const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
     if (t < 0) return;
     const int bt = static_cast<int>(t / a.B);
-    const bool own_in_pool = t == a.L - 1;          // the pool entry of b_t is the own-block mean
+    // the pool entry of b_t is the own-block mean unless this call writes it
+    const bool own_in_pool = t == a.L - 1 && a.pool_out == nullptr;
     const int full = own_in_pool ? bt + 1 : bt;    // pool rows to score
     const int b0 = j * kDBlkRows;
     const bool own_here = !own_in_pool && bt >= b0 && bt < b0 + kDBlkRows;
@@ -452,7 +459,9 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs 
                 for (int jj = 0; jj < 8; ++jj) sum += static_cast<double>(x[jj]);
             }
             for (; r < own_rows; ++r) sum += static_cast<double>(bf16_to_f32(s_own[r * D + tid]));
-            L.mean[tid] = f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(own_rows)));
+            const uint16_t mv = f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(own_rows)));
+            L.mean[tid] = mv;
+            if (a.pool_out != nullptr && t == a.L - 1) a.pool_out[s * a.pool_seq_stride + static_cast<int64_t>(bt) * D + tid] = mv;
         }
         __syncthreads();
         if (wave == 0) {
@@ -661,6 +670,10 @@ bool fused_supported(int d, int64_t L, int B, int m) {
 bool decode_mode(int S, int T, int64_t L, int B, int m) {
     return static_cast<int64_t>(S) * T <= kDecodeMaxQueries && (L + B - 1) / B <= kK1WaveMax &&
            m <= kDecodeMaxM;
+}
+
+bool pool_update_fusable(int S, int T, int d, int64_t L, int B, int m) {
+    return fused_supported(d, L, B, m) && !block_major_mode(S, T, d, L, B, m);
 }
 
 hipError_t launch_fused_blocks_refine(const FusedArgs &a, hipStream_t st) {

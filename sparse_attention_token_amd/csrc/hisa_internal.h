@@ -119,6 +119,11 @@ struct FusedArgs {
     uint16_t *own_rep;        // ws [S*T][d]: own-block representative of every query
     uint32_t *blk_keys;       // ws [S*T][blk_stride]: block keys by block id
     int64_t blk_stride;
+    // pool entry update fused into the block stage (pool_update_fusable):
+    // non-null, every own block is computed from K, and the query at t = L-1
+    // writes its own block's mean into pool_out[s][b_t] (the same buffer as
+    // pool; no other workgroup reads that entry)
+    uint16_t *pool_out;
 };
 
 constexpr int kBMMaxBlocks = 2048;       // block-major block stage: one wave selects the top m
@@ -133,6 +138,9 @@ inline int64_t bucket_chunks(int S, int T) {
     return static_cast<int64_t>(S) * ((T + kChunkQueries - 1) / kChunkQueries);
 }
 hipError_t launch_fused_blocks_refine(const FusedArgs &a, hipStream_t st);
+// Whether launch_fused_blocks_refine takes a path that honours pool_out (every
+// path but the block-major one).
+bool pool_update_fusable(int S, int T, int d, int64_t L, int B, int m);
 hipError_t launch_block_major_refine(const FusedArgs &a, hipStream_t st);
 hipError_t launch_block_major_blocks(const FusedArgs &a, hipStream_t st);
 

@@ -87,15 +87,21 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     }
     const SelectResult res = block_radix_select<NT, R>(kv, static_cast<uint32_t>(a.kout), sc);
     if (res.keff > 0) {
-        // refine mode: R divides B (B is 64 or 128, R at most 32), so the
-        // thread's R positions lie in one kept block
+        // refine mode: R and B are powers of two, so with R <= B the thread's
+        // R positions lie in one kept block and one lookup serves them all;
+        // with R > B (B = 16, long rows) each position looks up its block
+        const bool per_pos = MODE == kScoreRefine && R > a.B;
         int32_t id0 = tid * R;
-        if (MODE == kScoreRefine && id0 < n) {
+        if (MODE == kScoreRefine && !per_pos && id0 < n) {
             const int slot = id0 / a.B;
             id0 = s_sel[slot] * a.B + (id0 - slot * a.B);
         }
         block_compact<NT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
-            const int32_t id = id0 + r;
+            int32_t id = id0 + r;
+            if (per_pos) {
+                const int slot = id / a.B;
+                id = s_sel[slot] * a.B + (id - slot * a.B);
+            }
             put(out, op, id);
             if (osc) put(osc, op, key_to_score(key));
             if (out2) put(out2, op, id);
@@ -132,17 +138,28 @@ __global__ __launch_bounds__(kNT) void select_chunk_kernel(SelectArgs a, const u
     const SelectResult res = block_radix_select<kNT, R>(kv, static_cast<uint32_t>(a.kout), sc);
     if (res.keff > 0) {
         const int32_t *irow = ids_in ? ids_in + static_cast<int64_t>(qi) * in_stride + c0 : nullptr;
-        // position ids: the thread's R positions lie in one kept block in
-        // refine mode (R = 32 divides B, and chunks start on block bounds)
+        // position ids in refine mode: with R <= B (both powers of two;
+        // chunks start on block bounds) the thread's R positions lie in one
+        // kept block; with B < R each position looks up its block
         const int64_t p0 = c0 + static_cast<int64_t>(tid) * R;
+        const int32_t *sb = a.sel_blk + static_cast<int64_t>(qi) * a.m;
+        const bool per_pos = !irow && MODE == kScoreRefine && R > a.B;
         int32_t id0 = static_cast<int32_t>(p0);
-        if (!irow && MODE == kScoreRefine && p0 < n_row) {
+        if (!irow && MODE == kScoreRefine && !per_pos && p0 < n_row) {
             const int64_t slot = p0 / a.B;
-            id0 = static_cast<int32_t>(static_cast<int64_t>(a.sel_blk[static_cast<int64_t>(qi) * a.m + slot]) * a.B +
-                                       (p0 - slot * a.B));
+            id0 = static_cast<int32_t>(static_cast<int64_t>(sb[slot]) * a.B + (p0 - slot * a.B));
         }
         block_compact<kNT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
-            const int32_t id = irow ? irow[static_cast<int64_t>(tid) * R + r] : id0 + r;
+            int32_t id;
+            if (irow) {
+                id = irow[static_cast<int64_t>(tid) * R + r];
+            } else if (per_pos) {
+                const int64_t pos = p0 + r;
+                const int64_t slot = pos / a.B;
+                id = static_cast<int32_t>(static_cast<int64_t>(sb[slot]) * a.B + (pos - slot * a.B));
+            } else {
+                id = id0 + r;
+            }
             put(ko, op, key);
             put(io, op, id);
         });

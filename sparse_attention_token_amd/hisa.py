@@ -55,6 +55,9 @@ def lib():
     L.hisa_index.restype = i32
     L.hisa_index.argtypes = [vp, vp, vp, vp, i64, i64, vp, i64, i32, i32, i32, i32, i32, i32, i32,
                              vp, vp, vp, vp, sz, vp]
+    L.hisa_append_index.restype = i32
+    L.hisa_append_index.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                    i32, vp, vp, vp, vp, sz, vp]
     L.dsa_flat_workspace.restype = sz
     L.dsa_flat_workspace.argtypes = [i32, i32, i32, i32, i64, i32]
     L.dsa_flat_index.restype = i32
@@ -188,6 +191,38 @@ def hisa_index(q, w, K, L: int, pool_mean, B: int, m: int, k: int, qpos=None, *,
                           pss, S, T, H, d, B, m, k, _ptr(out_idx), _ptr(out_score), _ptr(out_blk),
                           _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check("hisa_index", st)
+    return out_idx, out_score, out_blk
+
+
+def hisa_append_index(K, pool_mean, L_old: int, L_new: int, q, w, B: int, m: int, k: int, qpos=None, *,
+                      want_scores: bool = True, want_blocks: bool = False, out_idx=None, out_score=None,
+                      out_blk=None, workspace=None):
+    """One decode step: hisa_pool_append(K, pool_mean, L_old, L_new, B) then
+    hisa_index(q, w, K, L_new, pool_mean, B, m, k, qpos), with the same results
+    (the last block's mean is stored from the block stage when the appended
+    rows all lie in it).  Returns (idx, score | None, blocks | None)."""
+    S, T, H, d, kss = _query_args(q, w, qpos, K, L_new)
+    _bf16(pool_mean, "pool_mean")
+    pss = _rows(pool_mean, "pool_mean", d)
+    if pool_mean.shape[0] != S or pool_mean.shape[1] * B < L_new:
+        raise ValueError("pool_mean must be [S, >= ceil(L_new/B), d]")
+    dev = q.device
+    if out_idx is None:
+        out_idx = torch.empty((S, T, k), dtype=torch.int32, device=dev)
+    if want_scores and out_score is None:
+        out_score = torch.empty((S, T, k), dtype=torch.float32, device=dev)
+    if want_blocks and out_blk is None:
+        out_blk = torch.empty((S, T, m), dtype=torch.int32, device=dev)
+    nbytes = hisa_index_workspace(S, T, H, d, L_new, B, m, k)
+    if nbytes == 0:
+        _check("hisa_append_index", lib().hisa_append_index(None, 0, int(L_old), int(L_new), None, 0, None, None,
+                                                            None, S, T, H, d, B, m, k, None, None, None, None,
+                                                            0, None))
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().hisa_append_index(_ptr(K), kss, int(L_old), int(L_new), _ptr(pool_mean), pss, _ptr(q), _ptr(w),
+                                 _ptr(qpos), S, T, H, d, B, m, k, _ptr(out_idx), _ptr(out_score), _ptr(out_blk),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    _check("hisa_append_index", st)
     return out_idx, out_score, out_blk
 
 

@@ -42,8 +42,8 @@ def _gpu_visible():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("hisa_pool_append", "hisa_index", "dsa_flat_index", "hisa_index_workspace",
-              "dsa_flat_workspace", "hisa_status_string", "hisa_abi_version"):
+    for n in ("hisa_pool_append", "hisa_index", "hisa_append_index", "dsa_flat_index",
+              "hisa_index_workspace", "dsa_flat_workspace", "hisa_status_string", "hisa_abi_version"):
         assert n in names
 
 
@@ -53,7 +53,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hisa_abi_version() == 1
+    assert lib.hisa_abi_version() == 2
     for code in (OK, ARG, UNSUP, WS, HIP, 12345):
         assert isinstance(lib.hisa_status_string(code), bytes)
     assert lib.hisa_status_string(WS) != lib.hisa_status_string(ARG)
@@ -91,6 +91,13 @@ def test_argument_checks_with_null_pointers(lib):
                           None, None, None, None, 0, None) == UNSUP
     assert lib.hisa_pool_append(None, 0, 1, 64, 64, 10, 5, None, 0, None) == ARG   # L_new < L_old
     assert lib.hisa_pool_append(None, 0, 1, 64, 64, -1, 5, None, 0, None) == ARG
+    # hisa_append_index: the checks of both calls it stands for
+    assert lib.hisa_append_index(None, 0, 0, 10, None, 0, None, None, None, 1, 1, 4, 64, 64, 2, 8,
+                                 None, None, None, None, 0, None) == ARG
+    assert lib.hisa_append_index(None, 0, 0, 10, None, 0, None, None, None, 1, 1, 4, 96, 64, 2, 8,
+                                 None, None, None, None, 0, None) == UNSUP
+    assert lib.hisa_append_index(None, 0, 10, 5, None, 0, None, None, None, 1, 1, 4, 64, 64, 2, 8,
+                                 None, None, None, None, 0, None) == ARG   # L_new < L_old
     # profiler argument checks
     ms, n = C.c_double(), C.c_int()
     assert lib.hisa_profile_read(-1, C.byref(ms), C.byref(n)) == ARG
@@ -133,3 +140,20 @@ def test_argument_checks_with_placeholder_pointers(lib):
     assert lib.hisa_pool_append(p, kss, S, d, B, 0, L, p, 15 * d, None) == ARG
     assert lib.hisa_pool_append(p, kss, S, d, 24, 0, L, p, pss, None) == UNSUP
     assert lib.hisa_pool_append(p, kss, S, d, B, 5, 5, p, pss, None) == OK   # empty range: no work
+
+    def app(**kw):
+        a = dict(K=p, kss=kss, L0=L - 1, L1=L, pool=p, pss=pss, q=p, w=p, qpos=None, S=S, T=T, H=H, d=d,
+                 B=B, m=m, k=k, out=p, sc=None, blk=None, ws=p, wsb=need)
+        a.update(kw)
+        return lib.hisa_append_index(a["K"], a["kss"], a["L0"], a["L1"], a["pool"], a["pss"], a["q"], a["w"],
+                                     a["qpos"], a["S"], a["T"], a["H"], a["d"], a["B"], a["m"], a["k"],
+                                     a["out"], a["sc"], a["blk"], a["ws"], a["wsb"], None)
+
+    assert app(wsb=need - 1) == WS
+    assert app(ws=None) == ARG
+    assert app(pss=15 * d) == ARG
+    assert app(kss=L * d - 8) == ARG
+    assert app(L0=L + 1) == ARG            # L_new < L_old
+    assert app(B=24) == UNSUP
+    assert app(q=odd) == ARG
+    assert app(T=L + 1) == ARG

@@ -50,7 +50,7 @@ def _run(hisa, case, qpos_on_device=True, want_flat=True):
 
 
 def test_abi_version(hisa):
-    assert hisa.hisa_abi_version() == 1
+    assert hisa.hisa_abi_version() == 2
 
 
 # ---------------------------------------------------------------- block pool
@@ -111,6 +111,60 @@ def test_pool_append_is_idempotent(hisa, orc):
     np.testing.assert_array_equal(bits(pool), orc.pool(c.K, 500, 64))
 
 
+# ---------------------------------------------------------------- append + index in one call
+
+APPEND_INDEX = [
+    # name, S, L_old, L_new, T, H, d, B, m, k, explicit positions
+    ("decode_one_launch", 4, 3000, 3001, 1, 64, 128, 128, 8, 300, False),
+    ("decode_new_block", 2, 3072, 3073, 1, 64, 128, 128, 8, 300, False),
+    ("decode_two_kernel", 2, 40000, 40001, 1, 16, 64, 64, 20, 400, False),
+    ("query_major_20q", 1, 5000, 5003, 20, 32, 128, 128, 8, 300, False),
+    # not fused: rows over two blocks, explicit positions, block-by-block prefill, nothing appended
+    ("rows_span_two_blocks", 2, 3070, 3075, 1, 64, 128, 128, 8, 300, False),
+    ("explicit_positions", 2, 3000, 3001, 3, 64, 128, 128, 8, 300, True),
+    ("prefill_128q", 1, 2000, 2128, 128, 16, 64, 64, 6, 128, False),
+    ("nothing_appended", 2, 3001, 3001, 1, 64, 128, 128, 8, 300, False),
+]
+
+
+@pytest.mark.parametrize("spec", APPEND_INDEX, ids=[s[0] for s in APPEND_INDEX])
+def test_append_index_equals_append_then_index(hisa, orc, spec):
+    """hisa_append_index against hisa_pool_append + hisa_index: the same
+    indices, scores, kept blocks and pool bits, whether or not the pool update
+    is fused into the block stage; sampled rows also against the oracle."""
+    import torch
+
+    name, S, L0, L1, T, H, d, B, m, k, explicit = spec
+    _say(f"append+index {name}")
+    qpos = None
+    if explicit:
+        rng = np.random.default_rng(zlib.crc32(name.encode()))
+        qpos = np.stack([np.sort(rng.integers(0, L1, size=T)) for _ in range(S)]).astype(np.int32)
+    c = synth.clustered_case(S, L1, T, H, d, B, m, k, seed=41, qpos=qpos, latent_block=B)
+    dev = to_dev(c)
+    qp = dev["qpos"] if explicit else None
+    base = build_pool(hisa, dev["K"], L0, B) if L0 > 0 else None
+    nblk = -(-L1 // B)
+    pools = []
+    for _ in range(2):
+        p = torch.zeros((S, nblk, d), dtype=torch.bfloat16, device=dev["K"].device)
+        if base is not None:
+            p[:, :base.shape[1]] = base[:, :nblk]
+        pools.append(p)
+    hisa.hisa_pool_append(dev["K"], pools[0], L0, L1, B)
+    a = hisa.hisa_index(dev["q"], dev["w"], dev["K"], L1, pools[0], B, m, k, qp, want_blocks=True)
+    b = hisa.hisa_append_index(dev["K"], pools[1], L0, L1, dev["q"], dev["w"], B, m, k, qp, want_blocks=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x.cpu().numpy().view(np.int32), y.cpu().numpy().view(np.int32))
+    np.testing.assert_array_equal(bits(pools[0]), bits(pools[1]))
+    np.testing.assert_array_equal(bits(pools[1]), orc.pool(c.K, L1, B))
+    idx, sc, blk = (t.cpu().numpy() for t in b)
+    for s in range(S):
+        for i in sorted({0, T - 1}):
+            check_hisa_row(orc, c, s, i, idx[s, i], sc[s, i], blk[s, i])
+
+
 # ---------------------------------------------------------------- small cases
 
 def _edge_qpos(L, B, T, rng):
@@ -137,6 +191,10 @@ SMALL = [
     # decode beyond 256 blocks: block stage in its own kernel (own block
     # recomputed there for positions other than the last)
     ("decode_two_kernel_d64_313blk", 2, 20000, 6, 16, 64, 64, 20, 400, "clustered"),
+    # B = 16 with rows long enough that a select thread's 32 positions span
+    # two kept blocks: single-stage (17600 candidates) and chunked (33600)
+    ("B16_rows_span_blocks", 1, 40000, 2, 8, 64, 16, 1100, 256, "gaussian"),
+    ("B16_chunked", 1, 60000, 2, 8, 64, 16, 2100, 256, "gaussian"),
     # just above the one-launch decode's 16 queries: the query-major fused path
     ("fused_17_queries", 1, 5000, 17, 64, 128, 128, 8, 512, "clustered"),
     # more than 2048 blocks: the block stage selects with the whole workgroup
