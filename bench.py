@@ -2,8 +2,10 @@
 """HISA indexer benchmark on one MI355X.
 
 A step is one pass of the indexing hot path over one batch: fold the batch's
-newest key rows into the block pool (hisa_pool_append), then index every query
-(hisa_index: block scores -> top-m blocks -> token refinement -> top-k).  The
+newest key rows into the block pool, then index every query (block scores ->
+top-m blocks -> token refinement -> top-k), through hisa_append_index (the
+same as hisa_pool_append followed by hisa_index; in decode steps the last
+block's mean is stored from the block stage instead of a launch of its own).  The
 flat DSA indexer (dsa_flat_index) runs on the same inputs as the in-run
 baseline.  Inputs are seeded synthetic workloads resident in HBM before the
 timed region.  Each step reads a different replica of the key cache (and its
@@ -184,9 +186,11 @@ def main():
     L_new_rows = T                       # the step appends the batch's own newest key rows
 
     def hisa_step(r):
-        hisa.hisa_pool_append(Ks[r], pools[r], L - L_new_rows, L, B)
-        hisa.hisa_index(q, w, Ks[r], L, pools[r], B, m, k, None, out_idx=out_idx,
-                        out_score=out_score, workspace=ws)
+        # hisa_pool_append of the new rows, then hisa_index, in one call (the
+        # library stores the last block's mean from the block stage when the
+        # new rows all lie in it: decode steps)
+        hisa.hisa_append_index(Ks[r], pools[r], L - L_new_rows, L, q, w, B, m, k, None, out_idx=out_idx,
+                               out_score=out_score, workspace=ws)
 
     def flat_step(r):
         hisa.dsa_flat_index(q, w, Ks[r], L, k, None, out_idx=f_idx, out_score=f_score, workspace=fws)

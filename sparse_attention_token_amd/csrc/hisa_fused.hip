@@ -95,6 +95,41 @@ struct BlockStageLds {
     uint16_t mean[128];
 };
 
+// Own-block representative: the mean of rows 0 .. n-1 (1 <= n <= 256) of the
+// staged block s_own (row stride D), bf16(fp32(fp64 sum in row order / n))
+// per column, into mean[0 .. D) and, when dst is not null, dst[0 .. D).  One
+// thread per column (the first D threads); ends with a barrier.  Rows are
+// read U at a time, all U reads issued before the first addition (U = 64, or
+// 16 in 1024-thread workgroups, whose register budget is smaller); a round may
+// read past row n-1, never past the staging buffer (its kFusedOwnElems / D
+// rows are a multiple of U), and such rows are not added.
+template <int D, int U>
+__device__ __forceinline__ void own_block_mean(const uint16_t *s_own, int n, uint16_t *mean, uint16_t *dst) {
+    static_assert((kFusedOwnElems / D) % U == 0, "rounds stay inside the staging buffer");
+    const int c = threadIdx.x;
+    if (c < D) {
+        double sum = 0.0;
+        for (int r0 = 0; r0 < n; r0 += U) {
+            const uint16_t *col = s_own + r0 * D + c;
+            uint16_t x[U];
+#pragma unroll
+            for (int j = 0; j < U; ++j) x[j] = col[j * D];
+            if (r0 + U <= n) {
+#pragma unroll
+                for (int j = 0; j < U; ++j) sum += static_cast<double>(bf16_to_f32(x[j]));
+            } else {
+#pragma unroll
+                for (int j = 0; j < U; ++j)
+                    if (r0 + j < n) sum += static_cast<double>(bf16_to_f32(x[j]));
+            }
+        }
+        const uint16_t mv = f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(n)));
+        mean[c] = mv;
+        if (dst) dst[c] = mv;
+    }
+    __syncthreads();
+}
+
 // Scores every block b <= b_t of one query into s_keys (positions laid out by
 // k1_slot) and leaves the query fragments in f.  NT threads; each wave loads
 // TB pool tiles at a time (the first batch before anything else, so that HBM
@@ -170,24 +205,9 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
     }
 
     if (!own_in_pool) {
-        // own-block representative: the mean of rows b_t*B .. t, one column
-        // per thread, rows in order, fp64; then wave 0 scores it
-        if (tid < D) {
-            double sum = 0.0;
-            int r = 0;
-            for (; r + 8 <= own_rows; r += 8) {            // 8 LDS reads in flight per step
-                float x[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = bf16_to_f32(s_own[(r + j) * D + tid]);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) sum += static_cast<double>(x[j]);
-            }
-            for (; r < own_rows; ++r) sum += static_cast<double>(bf16_to_f32(s_own[r * D + tid]));
-            const uint16_t mv = f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(own_rows)));
-            L.mean[tid] = mv;
-            if (write_pool) a.pool_out[s * a.pool_seq_stride + bt * D + tid] = mv;
-        }
-        __syncthreads();
+        // own-block representative: the mean of rows b_t*B .. t; then wave 0 scores it
+        own_block_mean<D, NT >= 1024 ? 16 : 64>(s_own, own_rows, L.mean,
+                                               write_pool ? a.pool_out + s * a.pool_seq_stride + bt * D : nullptr);
         if (wave == 0) {
             bf16x8 kbm[KS];
 #pragma unroll
@@ -389,6 +409,10 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_decode_kernel(FusedArgs a
 // candidate rows.
 constexpr int kDBlkRows = 128;
 
+// Grid decode_grid(S*T, ceil(nblk/128) + 1): per query, one workgroup per 128
+// pooled means, plus one (the last) for the own block when it is not taken
+// from the pool -- its rows are staged and averaged in a workgroup of their
+// own, in parallel with the pool tiles.
 template <int MT, int KS>
 __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs a) {
     constexpr int D = 32 * KS;
@@ -396,8 +420,9 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs 
     __shared__ __attribute__((aligned(16))) BlockStageLds<KS, kDecodeThreads> L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
+    const int btiles = (a.nblk + kDBlkRows - 1) / kDBlkRows;
     int qi, j;
-    decode_tile(a.S * a.T, (a.nblk + kDBlkRows - 1) / kDBlkRows, qi, j);
+    decode_tile(a.S * a.T, btiles + 1, qi, j);
     if (qi < 0) return;
     const int s = qi / a.T;
     const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
@@ -406,71 +431,66 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs 
     // the pool entry of b_t is the own-block mean unless this call writes it
     const bool own_in_pool = t == a.L - 1 && a.pool_out == nullptr;
     const int full = own_in_pool ? bt + 1 : bt;    // pool rows to score
-    const int b0 = j * kDBlkRows;
-    const bool own_here = !own_in_pool && bt >= b0 && bt < b0 + kDBlkRows;
-    if (b0 >= full && !own_here) return;
+    const bool own_wg = j == btiles;
+    if (own_wg ? own_in_pool : j * kDBlkRows >= full) return;
     uint32_t *keys = a.blk_keys + static_cast<int64_t>(qi) * a.blk_stride;
 
-    const uint16_t *pool = a.pool + s * a.pool_seq_stride;
-    bf16x8 kb[NTW][KS];
+    if (!own_wg) {
+        const int b0 = j * kDBlkRows;
+        const uint16_t *pool = a.pool + s * a.pool_seq_stride;
+        bf16x8 kb[NTW][KS];
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-        const int p = b0 + (wave * NTW + nt) * 16 + n;
-        load_row_frag<KS>(kb[nt], p < full ? pool + static_cast<int64_t>(p) * D : nullptr, lane);
+        for (int nt = 0; nt < NTW; ++nt) {
+            const int p = b0 + (wave * NTW + nt) * 16 + n;
+            load_row_frag<KS>(kb[nt], p < full ? pool + static_cast<int64_t>(p) * D : nullptr, lane);
+        }
+        stage_query<MT, KS, kDecodeThreads>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, L.q, tid);
+        if (tid < 64) L.w[tid] = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
+        __syncthreads();
+        QFrag<MT, KS> f;
+        load_qfrag_lds_w<MT, KS>(f, L.q, L.w, lane);
+        float v[NTW];
+        score_tiles_frag<MT, KS, NTW>(f, kb, v);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+            const int p = b0 + (wave * NTW + nt) * 16 + n;
+            if (g == 0 && p < full) keys[p] = score_to_key(v[nt]);
+        }
+        return;
     }
+
+    // the own block: rows b_t*B .. t, every load in flight before the first LDS store
     const int64_t r0 = static_cast<int64_t>(bt) * a.B;
     const int own_rows = static_cast<int>(t + 1 - r0);
     uint16_t *s_own = reinterpret_cast<uint16_t *>(L.own);
-    if (own_here) {
+    {
         constexpr int kPer = (kFusedOwnElems / 8 + kDecodeThreads - 1) / kDecodeThreads;
         const int chunks = own_rows * D / 8;
         const u32x4 *src = reinterpret_cast<const u32x4 *>(a.K + s * a.k_seq_stride + r0 * D);
         u32x4 *dst = reinterpret_cast<u32x4 *>(s_own);
-        u32x4 v[kPer];
+        u32x4 x[kPer];
 #pragma unroll
         for (int i = 0; i < kPer; ++i)
-            if (tid + i * kDecodeThreads < chunks) v[i] = src[tid + i * kDecodeThreads];
+            if (tid + i * kDecodeThreads < chunks) x[i] = src[tid + i * kDecodeThreads];
 #pragma unroll
         for (int i = 0; i < kPer; ++i)
-            if (tid + i * kDecodeThreads < chunks) dst[tid + i * kDecodeThreads] = v[i];
+            if (tid + i * kDecodeThreads < chunks) dst[tid + i * kDecodeThreads] = x[i];
     }
     stage_query<MT, KS, kDecodeThreads>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, L.q, tid);
     if (tid < 64) L.w[tid] = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
     __syncthreads();
-    QFrag<MT, KS> f;
-    load_qfrag_lds_w<MT, KS>(f, L.q, L.w, lane);
-    float v[NTW];
-    score_tiles_frag<MT, KS, NTW>(f, kb, v);
+    own_block_mean<D, 64>(s_own, own_rows, L.mean,
+                      a.pool_out != nullptr && t == a.L - 1
+                          ? a.pool_out + s * a.pool_seq_stride + static_cast<int64_t>(bt) * D
+                          : nullptr);
+    if (wave == 0) {
+        QFrag<MT, KS> f;
+        load_qfrag_lds_w<MT, KS>(f, L.q, L.w, lane);
+        bf16x8 kbm[KS];
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-        const int p = b0 + (wave * NTW + nt) * 16 + n;
-        if (g == 0 && p < full) keys[p] = score_to_key(v[nt]);
-    }
-    if (own_here) {
-        // the mean of rows b_t*B .. t, one column per thread, rows in order, fp64
-        if (tid < D) {
-            double sum = 0.0;
-            int r = 0;
-            for (; r + 8 <= own_rows; r += 8) {
-                float x[8];
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) x[jj] = bf16_to_f32(s_own[(r + jj) * D + tid]);
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) sum += static_cast<double>(x[jj]);
-            }
-            for (; r < own_rows; ++r) sum += static_cast<double>(bf16_to_f32(s_own[r * D + tid]));
-            const uint16_t mv = f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(own_rows)));
-            L.mean[tid] = mv;
-            if (a.pool_out != nullptr && t == a.L - 1) a.pool_out[s * a.pool_seq_stride + static_cast<int64_t>(bt) * D + tid] = mv;
-        }
-        __syncthreads();
-        if (wave == 0) {
-            bf16x8 kbm[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) kbm[ks] = n == 0 ? load_bf16x8(L.mean + 32 * ks + 8 * g) : zero_bf16x8();
-            const float vo = score_rows<MT, KS>(f, kbm);
-            if (lane == 0) keys[bt] = score_to_key(vo);
-        }
+        for (int ks = 0; ks < KS; ++ks) kbm[ks] = n == 0 ? load_bf16x8(L.mean + 32 * ks + 8 * g) : zero_bf16x8();
+        const float vo = score_rows<MT, KS>(f, kbm);
+        if (lane == 0) keys[bt] = score_to_key(vo);
     }
 }
 
@@ -632,8 +652,8 @@ hipError_t launch_fused_ks(const FusedArgs &a, bool decode, hipStream_t st) {
             // long context: block stage once per query, then the gather
             const int btiles = (a.nblk + kDBlkRows - 1) / kDBlkRows;
             const hipError_t e = launch(kKindScoreBlocks, hisa_dblocks_kernel<MT, KS>,
-                                        dim3(static_cast<uint32_t>(decode_grid(nq, btiles))), dim3(kDecodeThreads), 0,
-                                        st, a);
+                                        dim3(static_cast<uint32_t>(decode_grid(nq, btiles + 1))),
+                                        dim3(kDecodeThreads), 0, st, a);
             if (e != hipSuccess) return e;
             if (use_wide)
                 return launch(kKindScoreRefine, hisa_dgather_kernel<MT, KS, kDecodeRowsWide>,
