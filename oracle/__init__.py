@@ -8,6 +8,7 @@ from .oracle import (  # noqa: F401
     num_threads,
     score,
     mean_rows,
+    max_rows,
     pool,
     flat_query,
     refine_query,

@@ -19,6 +19,10 @@
  *   [Abstract]   arXiv abstract (mlsanity.com page): the indexer scores every
  *                historical key of the prefix for each query (flat DSA); HISA
  *                keeps the token-level top-k set the sparse attention consumes.
+ *   [P1-Summary] "Hierarchical Indexing Makes Sparse Attention Actually Fast",
+ *                section "HISA's Approach: Hierarchical Summarization of the KV
+ *                Cache": the coarse summaries pool the keys of a group by mean
+ *                pooling or max pooling.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - indexer score s(q,w,x) = sum_h w_h * max(0, q_h . x), no extra scale;
@@ -94,10 +98,36 @@ void oracle_mean_rows(const uint16_t *K, int64_t row0, int64_t row1, int d, uint
     }
 }
 
+/* ---------- max pooling of a run of key rows [P1-Summary] ---------- */
+
+/* out[i] = the largest of K[j][i] over rows j in [row0, row1), compared as
+ * real values; among equal values (only +0 and -0 can be equal with
+ * different bits) the one of the lowest row is kept.  Exact: no rounding. */
+void oracle_max_rows(const uint16_t *K, int64_t row0, int64_t row1, int d, uint16_t *out)
+{
+    for (int i = 0; i < d; ++i) {
+        uint16_t best = K[(size_t)row0 * d + i];
+        for (int64_t j = row0 + 1; j < row1; ++j) {
+            uint16_t h = K[(size_t)j * d + i];
+            if (bf16_val(h) > bf16_val(best)) best = h;
+        }
+        out[i] = best;
+    }
+}
+
+/* Block representative of rows [row0, row1): mode 0 = mean, 1 = max. */
+static void rep_rows(const uint16_t *K, int64_t row0, int64_t row1, int d, int mode, uint16_t *out)
+{
+    if (mode == 1)
+        oracle_max_rows(K, row0, row1, d, out);
+    else
+        oracle_mean_rows(K, row0, row1, d, out);
+}
+
 /* Block pool of a key cache holding L rows: block b covers rows
- * [b*B, min(b*B + B, L)).  means: [S, ceil(L/B), d]. */
-void oracle_pool(const uint16_t *K, int64_t k_seq_stride, int S, int64_t L, int d, int B,
-                 uint16_t *means)
+ * [b*B, min(b*B + B, L)).  reps: [S, ceil(L/B), d]; mode as rep_rows. */
+void oracle_pool_mode(const uint16_t *K, int64_t k_seq_stride, int S, int64_t L, int d, int B,
+                      int mode, uint16_t *reps)
 {
     int64_t nblk = (L + B - 1) / B;
     for (int s = 0; s < S; ++s) {
@@ -105,9 +135,15 @@ void oracle_pool(const uint16_t *K, int64_t k_seq_stride, int S, int64_t L, int 
 #pragma omp parallel for schedule(static)
         for (int64_t b = 0; b < nblk; ++b) {
             int64_t r1 = (b + 1) * B < L ? (b + 1) * B : L;
-            oracle_mean_rows(Ks, b * B, r1, d, means + ((size_t)s * nblk + b) * d);
+            rep_rows(Ks, b * B, r1, d, mode, reps + ((size_t)s * nblk + b) * d);
         }
     }
+}
+
+void oracle_pool(const uint16_t *K, int64_t k_seq_stride, int S, int64_t L, int d, int B,
+                 uint16_t *means)
+{
+    oracle_pool_mode(K, k_seq_stride, S, L, d, B, 0, means);
 }
 
 /* ---------- ranking: (score desc, index asc) ---------- */
@@ -201,9 +237,10 @@ int oracle_refine_query(const uint16_t *q, const float *w, const uint16_t *K, in
  *  out_blk [m]: kept block ids, ascending, -1 padded.
  *  blk_score (nullable) [floor(t/B)+1]: fp64 block scores.
  *  Returns k_eff. */
-int oracle_hisa_query(const uint16_t *q, const float *w, const uint16_t *K,
-                      const uint16_t *full_means, int H, int d, int64_t t, int B, int m, int k,
-                      int32_t *out_idx, float *out_score, int32_t *out_blk, double *blk_score)
+int oracle_hisa_query_mode(const uint16_t *q, const float *w, const uint16_t *K,
+                           const uint16_t *full_means, int H, int d, int64_t t, int B, int m, int k,
+                           int mode, int32_t *out_idx, float *out_score, int32_t *out_blk,
+                           double *blk_score)
 {
     int64_t bt = t / B;          /* the query's own block */
     int64_t nb = bt + 1;         /* blocks visible to the query */
@@ -221,7 +258,7 @@ int oracle_hisa_query(const uint16_t *q, const float *w, const uint16_t *K,
             r = full_means + (size_t)b * d;
         } else {
             int64_t r1 = (b < bt) ? (b + 1) * B : t + 1;
-            oracle_mean_rows(K, b * B, r1, d, rep);
+            rep_rows(K, b * B, r1, d, mode, rep);
             r = rep;
         }
         bc[b].s = oracle_score(q, w, r, H, d);
@@ -238,6 +275,15 @@ int oracle_hisa_query(const uint16_t *q, const float *w, const uint16_t *K,
     int keff = oracle_refine_query(q, w, K, H, d, t, B, sel, meff, k, out_idx, out_score, NULL);
     free(rep); free(bc); free(sel);
     return keff;
+}
+
+/* Mean-pooled representatives (the pages' main reading). */
+int oracle_hisa_query(const uint16_t *q, const float *w, const uint16_t *K,
+                      const uint16_t *full_means, int H, int d, int64_t t, int B, int m, int k,
+                      int32_t *out_idx, float *out_score, int32_t *out_blk, double *blk_score)
+{
+    return oracle_hisa_query_mode(q, w, K, full_means, H, d, t, B, m, k, 0, out_idx, out_score,
+                                  out_blk, blk_score);
 }
 
 /* ---------- batched drivers (OpenMP over queries) ---------- */
@@ -292,10 +338,10 @@ int oracle_block_sparse_query(const uint16_t *q, const float *w, const uint16_t 
     return n;
 }
 
-int oracle_hisa_batch(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
-                      int64_t k_seq_stride, int64_t L, int S, int T, int H, int d, int B, int m,
-                      int k, const int32_t *sel, int nsel, int32_t *out_idx, float *out_score,
-                      int32_t *out_blk)
+int oracle_hisa_batch_mode(const uint16_t *q, const float *w, const int32_t *qpos,
+                           const uint16_t *K, int64_t k_seq_stride, int64_t L, int S, int T, int H,
+                           int d, int B, int m, int k, int mode, const int32_t *sel, int nsel,
+                           int32_t *out_idx, float *out_score, int32_t *out_blk)
 {
     int n = sel ? nsel : S * T;
     int64_t nfull = L / B;       /* blocks complete within the cache */
@@ -305,7 +351,7 @@ int oracle_hisa_batch(const uint16_t *q, const float *w, const int32_t *qpos, co
         const uint16_t *Ks = K + (size_t)s * k_seq_stride;
 #pragma omp parallel for schedule(static)
         for (int64_t b = 0; b < nfull; ++b)
-            oracle_mean_rows(Ks, b * B, (b + 1) * B, d, means + ((size_t)s * nfull + b) * d);
+            rep_rows(Ks, b * B, (b + 1) * B, d, mode, means + ((size_t)s * nfull + b) * d);
     }
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(|| : bad)
@@ -314,15 +360,24 @@ int oracle_hisa_batch(const uint16_t *q, const float *w, const int32_t *qpos, co
         int s = id / T;
         int64_t t = qpos[id];
         if (t < 0 || t >= L) { bad = 1; continue; }
-        int r = oracle_hisa_query(q + (size_t)id * H * d, w + (size_t)id * H,
-                                  K + (size_t)s * k_seq_stride, means + (size_t)s * nfull * d,
-                                  H, d, t, B, m, k, out_idx + (size_t)id * k,
-                                  out_score ? out_score + (size_t)id * k : NULL,
-                                  out_blk + (size_t)id * m, NULL);
+        int r = oracle_hisa_query_mode(q + (size_t)id * H * d, w + (size_t)id * H,
+                                       K + (size_t)s * k_seq_stride, means + (size_t)s * nfull * d,
+                                       H, d, t, B, m, k, mode, out_idx + (size_t)id * k,
+                                       out_score ? out_score + (size_t)id * k : NULL,
+                                       out_blk + (size_t)id * m, NULL);
         if (r < 0) bad = 1;
     }
     free(means);
     return bad ? -1 : 0;
+}
+
+int oracle_hisa_batch(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
+                      int64_t k_seq_stride, int64_t L, int S, int T, int H, int d, int B, int m,
+                      int k, const int32_t *sel, int nsel, int32_t *out_idx, float *out_score,
+                      int32_t *out_blk)
+{
+    return oracle_hisa_batch_mode(q, w, qpos, K, k_seq_stride, L, S, T, H, d, B, m, k, 0, sel, nsel,
+                                  out_idx, out_score, out_blk);
 }
 
 int oracle_flat_batch(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,

@@ -37,6 +37,10 @@ def load():
     lib.oracle_mean_rows.argtypes = [_u16p, I64, I64, I, _u16p]
     lib.oracle_pool.restype = None
     lib.oracle_pool.argtypes = [_u16p, I64, I, I64, I, I, _u16p]
+    lib.oracle_max_rows.restype = None
+    lib.oracle_max_rows.argtypes = [_u16p, I64, I64, I, _u16p]
+    lib.oracle_pool_mode.restype = None
+    lib.oracle_pool_mode.argtypes = [_u16p, I64, I, I64, I, I, I, _u16p]
     lib.oracle_flat_query.restype = I
     lib.oracle_flat_query.argtypes = [_u16p, _f32p, _u16p, I, I, I64, I, _i32p, _f32p, _f64p]
     lib.oracle_refine_query.restype = I
@@ -45,11 +49,17 @@ def load():
     lib.oracle_hisa_query.restype = I
     lib.oracle_hisa_query.argtypes = [_u16p, _f32p, _u16p, _u16p, I, I, I64, I, I, I,
                                       _i32p, _f32p, _i32p, _f64p]
+    lib.oracle_hisa_query_mode.restype = I
+    lib.oracle_hisa_query_mode.argtypes = [_u16p, _f32p, _u16p, _u16p, I, I, I64, I, I, I, I,
+                                           _i32p, _f32p, _i32p, _f64p]
     lib.oracle_block_sparse_query.restype = I
     lib.oracle_block_sparse_query.argtypes = [_u16p, _f32p, _u16p, I, I, I64, I, I, _i32p, _i32p]
     lib.oracle_hisa_batch.restype = I
     lib.oracle_hisa_batch.argtypes = [_u16p, _f32p, _i32p, _u16p, I64, I64, I, I, I, I, I, I,
                                       I, _i32p, I, _i32p, _f32p, _i32p]
+    lib.oracle_hisa_batch_mode.restype = I
+    lib.oracle_hisa_batch_mode.argtypes = [_u16p, _f32p, _i32p, _u16p, I64, I64, I, I, I, I, I, I,
+                                           I, I, _i32p, I, _i32p, _f32p, _i32p]
     lib.oracle_flat_batch.restype = I
     lib.oracle_flat_batch.argtypes = [_u16p, _f32p, _i32p, _u16p, I64, I64, I, I, I, I, I,
                                       _i32p, I, _i32p, _f32p]
@@ -86,13 +96,31 @@ def mean_rows(K: np.ndarray, row0: int, row1: int) -> np.ndarray:
     return out
 
 
-def pool(K: np.ndarray, L: int, B: int) -> np.ndarray:
-    """Block means [S, ceil(L/B), d] (bf16 bits) of K [S, L_cap, d] holding L rows."""
+_MODES = {"mean": 0, "max": 1}
+
+
+def _mode(mode: str) -> int:
+    if mode not in _MODES:
+        raise ValueError(f"pooling must be one of {sorted(_MODES)}")
+    return _MODES[mode]
+
+
+def max_rows(K: np.ndarray, row0: int, row1: int) -> np.ndarray:
+    """bf16 bits of the max-pooled representative of rows [row0, row1) of K [L, d]."""
+    K = _c(K, np.uint16)
+    out = np.zeros(K.shape[1], dtype=np.uint16)
+    load().oracle_max_rows(_p(K, _u16p), row0, row1, K.shape[1], _p(out, _u16p))
+    return out
+
+
+def pool(K: np.ndarray, L: int, B: int, mode: str = "mean") -> np.ndarray:
+    """Block representatives [S, ceil(L/B), d] (bf16 bits) of K [S, L_cap, d] holding L rows;
+    mode "mean" or "max"."""
     K = _c(K, np.uint16)
     S, Lcap, d = K.shape
     nblk = -(-L // B)
     out = np.zeros((S, nblk, d), dtype=np.uint16)
-    load().oracle_pool(_p(K, _u16p), Lcap * d, S, L, d, B, _p(out, _u16p))
+    load().oracle_pool_mode(_p(K, _u16p), Lcap * d, S, L, d, B, _mode(mode), _p(out, _u16p))
     return out
 
 
@@ -127,17 +155,18 @@ def refine_query(q, w, K, t: int, B: int, blocks, k: int):
     return idx, sc, keff, int(n.value)
 
 
-def hisa_query(q, w, K, t: int, B: int, m: int, k: int):
-    """HISA for one query: (idx [k], score [k], blocks [m], block scores fp64 [t//B+1], k_eff)."""
+def hisa_query(q, w, K, t: int, B: int, m: int, k: int, mode: str = "mean"):
+    """HISA for one query: (idx [k], score [k], blocks [m], block scores fp64 [t//B+1], k_eff).
+    mode: block representatives by "mean" or "max" pooling."""
     q, w, K = _c(q, np.uint16), _c(w, np.float32), _c(K, np.uint16)
     H, d = q.shape
     idx = np.zeros(k, dtype=np.int32)
     sc = np.zeros(k, dtype=np.float32)
     blk = np.zeros(m, dtype=np.int32)
     bsc = np.zeros(t // B + 1, dtype=np.float64)
-    keff = load().oracle_hisa_query(_p(q, _u16p), _p(w, _f32p), _p(K, _u16p), None, H, d, t,
-                                    B, m, k, _p(idx, _i32p), _p(sc, _f32p), _p(blk, _i32p),
-                                    _p(bsc, _f64p))
+    keff = load().oracle_hisa_query_mode(_p(q, _u16p), _p(w, _f32p), _p(K, _u16p), None, H, d, t,
+                                         B, m, k, _mode(mode), _p(idx, _i32p), _p(sc, _f32p),
+                                         _p(blk, _i32p), _p(bsc, _f64p))
     if keff < 0:
         raise MemoryError("oracle_hisa_query failed")
     return idx, sc, blk, bsc, keff
@@ -165,19 +194,19 @@ def _sel(sel, S, T):
     return s, len(s)
 
 
-def hisa_batch(q, w, qpos, K, L: int, B: int, m: int, k: int, sel=None):
+def hisa_batch(q, w, qpos, K, L: int, B: int, m: int, k: int, sel=None, mode: str = "mean"):
     """HISA over a batch q [S,T,H,d]; returns (idx [S,T,k], score [S,T,k], blocks [S,T,m]).
-    With sel (flat ids s*T+i) only those rows are filled."""
+    With sel (flat ids s*T+i) only those rows are filled; mode: "mean" or "max" pooling."""
     q, w, qpos, K = _c(q, np.uint16), _c(w, np.float32), _c(qpos, np.int32), _c(K, np.uint16)
     S, T, H, d = q.shape
     s_arr, ns = _sel(sel, S, T)
     idx = np.full((S, T, k), -2, dtype=np.int32)
     sc = np.zeros((S, T, k), dtype=np.float32)
     blk = np.full((S, T, m), -2, dtype=np.int32)
-    r = load().oracle_hisa_batch(_p(q, _u16p), _p(w, _f32p), _p(qpos, _i32p), _p(K, _u16p),
-                                 K.shape[1] * d, L, S, T, H, d, B, m, k,
-                                 _p(s_arr, _i32p) if s_arr is not None else None, ns,
-                                 _p(idx, _i32p), _p(sc, _f32p), _p(blk, _i32p))
+    r = load().oracle_hisa_batch_mode(_p(q, _u16p), _p(w, _f32p), _p(qpos, _i32p), _p(K, _u16p),
+                                      K.shape[1] * d, L, S, T, H, d, B, m, k, _mode(mode),
+                                      _p(s_arr, _i32p) if s_arr is not None else None, ns,
+                                      _p(idx, _i32p), _p(sc, _f32p), _p(blk, _i32p))
     if r != 0:
         raise ValueError("oracle_hisa_batch failed (bad position or out of memory)")
     return idx, sc, blk

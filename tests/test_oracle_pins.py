@@ -117,6 +117,99 @@ def test_golden_mean_rounding(orc):
         assert int(got[0]) == int(c["mean"], 16), c["why"]
 
 
+# ---------------------------------------------------------------- max pooling
+
+MAX_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "max_pool_example.json")
+
+
+def test_golden_max_pool_example(orc):
+    with open(MAX_GOLDEN) as f:
+        g = json.load(f)
+    q = bf16_bits(np.array(g["q"], dtype=np.float32))
+    w = np.array(g["w"], dtype=np.float32)
+    K = bf16_bits(np.array(g["K"], dtype=np.float32))
+    for mode in ("max", "mean"):
+        e = g[mode]
+        reps = orc.pool(K[None], g["L"], g["B"], mode=mode)[0]
+        np.testing.assert_array_equal(bf16_to_f32(reps), np.array(e["reps"], dtype=np.float32))
+        idx, sc, blk, bsc, keff = orc.hisa_query(q, w, K, g["t"], g["B"], g["m"], g["k"], mode=mode)
+        assert list(bsc) == e["block_scores"], mode
+        assert [b for b in blk if b >= 0] == e["blocks"], mode
+        assert list(idx) == e["idx"], mode
+        np.testing.assert_array_equal(sc, np.array(e["score"], dtype=np.float32))
+
+
+def np_max_bits(rows_bits):
+    """Per column, the bits of the first row holding the largest value (numpy argmax
+    returns the first occurrence; +0 and -0 compare equal)."""
+    f = bf16_to_f32(rows_bits)
+    first = np.argmax(f, axis=0)
+    return rows_bits[first, np.arange(rows_bits.shape[1])]
+
+
+@pytest.mark.parametrize("B,L", [(4, 37), (64, 500), (128, 300)])
+def test_max_pool_is_first_argmax(orc, B, L):
+    rng = np.random.default_rng(B + L)
+    f = rng.standard_normal((L, 8)).astype(np.float32)
+    f[rng.random(f.shape) < 0.2] = 0.0                    # ties: many zeros ...
+    f[rng.random(f.shape) < 0.1] = -0.0                   # ... of both signs
+    f[:, 0] = -np.abs(f[:, 0])                            # a column whose maximum is often a zero
+    K = bf16_bits(f)
+    got = orc.pool(K[None], L, B, mode="max")[0]
+    for b in range(-(-L // B)):
+        np.testing.assert_array_equal(got[b], np_max_bits(K[b * B:min(L, b * B + B)]), err_msg=f"block {b}")
+        np.testing.assert_array_equal(orc.max_rows(K, b * B, min(L, b * B + B)), got[b])
+
+
+def test_max_pool_signed_zero_keeps_first_row(orc):
+    z, nz = bf16_bits(np.float32(0.0)), bf16_bits(np.float32(-0.0))
+    K = np.array([[nz, z, nz], [z, nz, nz], [z, z, z]], dtype=np.uint16)
+    got = orc.max_rows(K, 0, 3)
+    assert list(got) == [int(nz), int(z), int(nz)]
+
+
+def test_unit_blocks_make_max_and_mean_pools_the_keys(orc):
+    rng = np.random.default_rng(11)
+    K = bf16_bits(rng.standard_normal((1, 50, 16)).astype(np.float32))
+    np.testing.assert_array_equal(orc.pool(K, 50, 1, mode="max"), K)
+    np.testing.assert_array_equal(orc.pool(K, 50, 1, mode="mean"), K)
+    q, w = bf16_bits(rng.standard_normal((4, 16)).astype(np.float32)), rng.standard_normal(4).astype(np.float32)
+    a = orc.hisa_query(q, w, K[0], 40, 1, 7, 5, mode="max")
+    b = orc.hisa_query(q, w, K[0], 40, 1, 7, 5, mode="mean")
+    for x, y in zip(a[:4], b[:4]):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("t,B", [(63, 8), (100, 16), (37, 4)])
+def test_max_pool_keep_all_blocks_is_flat(orc, t, B):
+    rng = np.random.default_rng(t * B)
+    q, w, K = int_case(rng, t + 1, 3, 8)
+    nb = t // B + 1
+    idx, sc, blk, bsc, keff = orc.hisa_query(q, w, K, t, B, nb, 17, mode="max")
+    fidx, fsc, _ = orc.flat_query(q, w, K, t, 17)
+    np.testing.assert_array_equal(idx, fidx)
+    np.testing.assert_array_equal(sc, fsc)
+
+
+def test_max_pool_hisa_bruteforce(orc):
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        B = int(rng.choice([2, 4, 8]))
+        t = int(rng.integers(0, 60))
+        q, w, K = int_case(rng, t + 1, 2, 4)
+        m, k = int(rng.integers(1, 5)), int(rng.integers(1, 12))
+        bt = t // B
+        reps = [np_max_bits(K[b * B:((b + 1) * B if b < bt else t + 1)]) for b in range(bt + 1)]
+        sig = np_scores(q, w, np.stack(reps))
+        blocks = np.sort(np_topk(sig, np.arange(bt + 1), min(m, bt + 1)))
+        cand = np.array([j for b in blocks for j in range(b * B, min(b * B + B, t + 1))], dtype=np.int64)
+        want = np_topk(np_scores(q, w, K[cand]), cand, k)
+        idx, sc, blk, bsc, keff = orc.hisa_query(q, w, K, t, B, m, k, mode="max")
+        np.testing.assert_allclose(bsc, sig, rtol=0, atol=0)
+        np.testing.assert_array_equal([b for b in blk if b >= 0], blocks)
+        np.testing.assert_array_equal(idx, want)
+
+
 # ---------------------------------------------------------------- the score
 
 @pytest.mark.parametrize("H,d", [(1, 2), (3, 8), (4, 64), (64, 128)])
