@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define HISA_ABI_VERSION 2   /* 2: adds hisa_append_index */
+#define HISA_ABI_VERSION 3   /* 2: adds hisa_append_index; 3: adds the *_mode calls (max pooling) */
 
 #if defined(__GNUC__)
 #define HISA_API __attribute__((visibility("default")))
@@ -67,6 +67,12 @@ enum hisa_status {
     HISA_ERR_UNSUPPORTED = -2,  /* shape outside the supported set above */
     HISA_ERR_WORKSPACE = -3,    /* ws_bytes smaller than the *_workspace() size */
     HISA_ERR_HIP = -4           /* a HIP runtime error while enqueuing the kernels */
+};
+
+/* How block representatives are pooled (the *_mode calls; the others use mean). */
+enum hisa_pool_kind {
+    HISA_POOL_MEAN = 0,         /* mean of the block's keys (see hisa_pool_append) */
+    HISA_POOL_MAX = 1           /* per-dimension maximum of the block's keys (see hisa_pool_append_mode) */
 };
 
 /* HISA_ABI_VERSION of the loaded library. */
@@ -163,6 +169,36 @@ HISA_API int hisa_append_index(const uint16_t *K, int64_t k_seq_stride, int64_t 
                                int S, int T, int H, int d, int B, int m, int k,
                                int32_t *out_idx, float *out_score, int32_t *out_blk,
                                void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Max pooling (the *_mode calls with pool_kind = HISA_POOL_MAX).  Page
+ * "Hierarchical Indexing Makes Sparse Attention Actually Fast", section "HISA's
+ * Approach: Hierarchical Summarization of the KV Cache", names max pooling
+ * beside mean pooling for the coarse summaries of a group of keys.  Here a
+ * block's representative is then, per dimension, the largest of its keys'
+ * values (compared as real numbers; among equal values, which only +0 and -0
+ * can be with different bits, the one of the lowest row), with no rounding;
+ * a query's own block is represented over its rows up to t, as for the mean.
+ * Each *_mode call is its plain counterpart with that representative; with
+ * pool_kind = HISA_POOL_MEAN it is exactly the plain call.  A pool built with
+ * one kind must be used with the same kind.  pool_kind outside the enum
+ * returns HISA_ERR_ARG.
+ */
+HISA_API int hisa_pool_append_mode(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
+                                   int64_t L_old, int64_t L_new,
+                                   uint16_t *pool_rep, int64_t pool_seq_stride, int pool_kind, void *stream);
+HISA_API int hisa_index_mode(const uint16_t *q, const float *w, const int32_t *qpos,
+                             const uint16_t *K, int64_t k_seq_stride, int64_t L,
+                             const uint16_t *pool_rep, int64_t pool_seq_stride,
+                             int S, int T, int H, int d, int B, int m, int k,
+                             int32_t *out_idx, float *out_score, int32_t *out_blk,
+                             void *ws, size_t ws_bytes, int pool_kind, void *stream);
+HISA_API int hisa_append_index_mode(const uint16_t *K, int64_t k_seq_stride, int64_t L_old, int64_t L_new,
+                                    uint16_t *pool_rep, int64_t pool_seq_stride,
+                                    const uint16_t *q, const float *w, const int32_t *qpos,
+                                    int S, int T, int H, int d, int B, int m, int k,
+                                    int32_t *out_idx, float *out_score, int32_t *out_blk,
+                                    void *ws, size_t ws_bytes, int pool_kind, void *stream);
 
 /* Bytes of device workspace dsa_flat_index needs for these sizes (0 on bad sizes). */
 HISA_API size_t dsa_flat_workspace(int S, int T, int H, int d, int64_t L, int k);

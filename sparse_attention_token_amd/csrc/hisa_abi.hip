@@ -195,17 +195,25 @@ const char *hisa_status_string(int status) {
     }
 }
 
-int hisa_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
-                     int64_t L_old, int64_t L_new, uint16_t *pool_mean, int64_t pool_seq_stride,
-                     void *stream) {
-    const int st = check_append(K, k_seq_stride, S, d, B, L_old, L_new, pool_mean, pool_seq_stride);
+int hisa_pool_append_mode(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
+                          int64_t L_old, int64_t L_new, uint16_t *pool_rep, int64_t pool_seq_stride,
+                          int pool_kind, void *stream) {
+    if (pool_kind != HISA_POOL_MEAN && pool_kind != HISA_POOL_MAX) return HISA_ERR_ARG;
+    const int st = check_append(K, k_seq_stride, S, d, B, L_old, L_new, pool_rep, pool_seq_stride);
     if (st != HISA_OK) return st;
     if (L_old == L_new) return HISA_OK;
     const int64_t blk0 = L_old / B;
     const int64_t blk1 = (L_new - 1) / B;
     return hip_status(launch_pool_append(K, k_seq_stride, S, d, B, blk0, blk1 - blk0 + 1, L_new,
-                                         pool_mean, pool_seq_stride,
+                                         pool_kind == HISA_POOL_MAX, pool_rep, pool_seq_stride,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int hisa_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
+                     int64_t L_old, int64_t L_new, uint16_t *pool_mean, int64_t pool_seq_stride,
+                     void *stream) {
+    return hisa_pool_append_mode(K, k_seq_stride, S, d, B, L_old, L_new, pool_mean, pool_seq_stride,
+                                 HISA_POOL_MEAN, stream);
 }
 
 size_t hisa_index_workspace(int S, int T, int H, int d, int64_t L, int B, int m, int k) {
@@ -243,7 +251,7 @@ int check_index(const uint16_t *q, const float *w, const int32_t *qpos, const ui
 int run_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
               int64_t k_seq_stride, int64_t L, const uint16_t *pool_mean, uint16_t *pool_out,
               int64_t pool_seq_stride, int S, int T, int H, int d, int B, int m, int k,
-              int32_t *out_idx, float *out_score, int32_t *out_blk, void *ws, hipStream_t hs) {
+              int32_t *out_idx, float *out_score, int32_t *out_blk, void *ws, bool pool_max, hipStream_t hs) {
     int st = HISA_OK;
     const HisaLayout lay = hisa_layout(S, T, d, L, B, m, k);
 
@@ -271,6 +279,7 @@ int run_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint
         fa.blk_keys = blk_keys;
         fa.blk_stride = lay.blk_stride;
         fa.pool_out = pool_out;
+        fa.pool_max = pool_max ? 1 : 0;
         if (block_major_mode(S, T, d, L, B, m)) {
             fa.bucket_off = reinterpret_cast<int32_t *>(base + lay.bucket_off);
             fa.bucket_ent = reinterpret_cast<uint32_t *>(base + lay.bucket_ent);
@@ -288,7 +297,7 @@ int run_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint
 
     // general path (any supported shape): own-block means, then score and
     // select twice
-    st = hip_status(launch_own_mean(K, k_seq_stride, qpos, L, S, T, d, B, own_rep, hs));
+    st = hip_status(launch_own_mean(K, k_seq_stride, qpos, L, S, T, d, B, pool_max, own_rep, hs));
     if (st != HISA_OK) return st;
 
     ScoreArgs sa{};
@@ -321,28 +330,41 @@ int run_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint
 
 extern "C" {
 
+int hisa_index_mode(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
+                    int64_t k_seq_stride, int64_t L, const uint16_t *pool_rep,
+                    int64_t pool_seq_stride, int S, int T, int H, int d, int B, int m, int k,
+                    int32_t *out_idx, float *out_score, int32_t *out_blk, void *ws, size_t ws_bytes,
+                    int pool_kind, void *stream) {
+    if (pool_kind != HISA_POOL_MEAN && pool_kind != HISA_POOL_MAX) return HISA_ERR_ARG;
+    const int st = check_index(q, w, qpos, K, k_seq_stride, L, pool_rep, pool_seq_stride, S, T, H, d, B, m, k,
+                               out_idx, ws, ws_bytes);
+    if (st != HISA_OK) return st;
+    return run_index(q, w, qpos, K, k_seq_stride, L, pool_rep, nullptr, pool_seq_stride, S, T, H, d, B, m, k,
+                     out_idx, out_score, out_blk, ws, pool_kind == HISA_POOL_MAX, static_cast<hipStream_t>(stream));
+}
+
 int hisa_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
                int64_t k_seq_stride, int64_t L, const uint16_t *pool_mean,
                int64_t pool_seq_stride, int S, int T, int H, int d, int B, int m, int k,
                int32_t *out_idx, float *out_score, int32_t *out_blk, void *ws, size_t ws_bytes,
                void *stream) {
-    const int st = check_index(q, w, qpos, K, k_seq_stride, L, pool_mean, pool_seq_stride, S, T, H, d, B, m, k,
-                               out_idx, ws, ws_bytes);
-    if (st != HISA_OK) return st;
-    return run_index(q, w, qpos, K, k_seq_stride, L, pool_mean, nullptr, pool_seq_stride, S, T, H, d, B, m, k,
-                     out_idx, out_score, out_blk, ws, static_cast<hipStream_t>(stream));
+    return hisa_index_mode(q, w, qpos, K, k_seq_stride, L, pool_mean, pool_seq_stride, S, T, H, d, B, m, k,
+                           out_idx, out_score, out_blk, ws, ws_bytes, HISA_POOL_MEAN, stream);
 }
 
-int hisa_append_index(const uint16_t *K, int64_t k_seq_stride, int64_t L_old, int64_t L_new,
-                      uint16_t *pool_mean, int64_t pool_seq_stride, const uint16_t *q, const float *w,
-                      const int32_t *qpos, int S, int T, int H, int d, int B, int m, int k, int32_t *out_idx,
-                      float *out_score, int32_t *out_blk, void *ws, size_t ws_bytes, void *stream) {
-    int st = check_append(K, k_seq_stride, S, d, B, L_old, L_new, pool_mean, pool_seq_stride);
+int hisa_append_index_mode(const uint16_t *K, int64_t k_seq_stride, int64_t L_old, int64_t L_new,
+                           uint16_t *pool_rep, int64_t pool_seq_stride, const uint16_t *q, const float *w,
+                           const int32_t *qpos, int S, int T, int H, int d, int B, int m, int k, int32_t *out_idx,
+                           float *out_score, int32_t *out_blk, void *ws, size_t ws_bytes, int pool_kind,
+                           void *stream) {
+    if (pool_kind != HISA_POOL_MEAN && pool_kind != HISA_POOL_MAX) return HISA_ERR_ARG;
+    int st = check_append(K, k_seq_stride, S, d, B, L_old, L_new, pool_rep, pool_seq_stride);
     if (st != HISA_OK) return st;
-    st = check_index(q, w, qpos, K, k_seq_stride, L_new, pool_mean, pool_seq_stride, S, T, H, d, B, m, k, out_idx,
+    st = check_index(q, w, qpos, K, k_seq_stride, L_new, pool_rep, pool_seq_stride, S, T, H, d, B, m, k, out_idx,
                      ws, ws_bytes);
     if (st != HISA_OK) return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool pmax = pool_kind == HISA_POOL_MAX;
     // The fused form needs the query at t = L_new-1 in every sequence (no
     // explicit positions) and the appended rows all in its own block.
     const bool fuse = qpos == nullptr && L_old < L_new && L_old / B == (L_new - 1) / B &&
@@ -351,14 +373,22 @@ int hisa_append_index(const uint16_t *K, int64_t k_seq_stride, int64_t L_old, in
         if (L_old < L_new) {
             const int64_t blk0 = L_old / B;
             st = hip_status(launch_pool_append(K, k_seq_stride, S, d, B, blk0, (L_new - 1) / B - blk0 + 1, L_new,
-                                               pool_mean, pool_seq_stride, hs));
+                                               pmax, pool_rep, pool_seq_stride, hs));
             if (st != HISA_OK) return st;
         }
-        return run_index(q, w, qpos, K, k_seq_stride, L_new, pool_mean, nullptr, pool_seq_stride, S, T, H, d, B, m,
-                         k, out_idx, out_score, out_blk, ws, hs);
+        return run_index(q, w, qpos, K, k_seq_stride, L_new, pool_rep, nullptr, pool_seq_stride, S, T, H, d, B, m,
+                         k, out_idx, out_score, out_blk, ws, pmax, hs);
     }
-    return run_index(q, w, qpos, K, k_seq_stride, L_new, pool_mean, pool_mean, pool_seq_stride, S, T, H, d, B, m, k,
-                     out_idx, out_score, out_blk, ws, hs);
+    return run_index(q, w, qpos, K, k_seq_stride, L_new, pool_rep, pool_rep, pool_seq_stride, S, T, H, d, B, m, k,
+                     out_idx, out_score, out_blk, ws, pmax, hs);
+}
+
+int hisa_append_index(const uint16_t *K, int64_t k_seq_stride, int64_t L_old, int64_t L_new,
+                      uint16_t *pool_mean, int64_t pool_seq_stride, const uint16_t *q, const float *w,
+                      const int32_t *qpos, int S, int T, int H, int d, int B, int m, int k, int32_t *out_idx,
+                      float *out_score, int32_t *out_blk, void *ws, size_t ws_bytes, void *stream) {
+    return hisa_append_index_mode(K, k_seq_stride, L_old, L_new, pool_mean, pool_seq_stride, q, w, qpos, S, T, H, d,
+                                  B, m, k, out_idx, out_score, out_blk, ws, ws_bytes, HISA_POOL_MEAN, stream);
 }
 
 size_t dsa_flat_workspace(int S, int T, int H, int d, int64_t L, int k) {

@@ -95,39 +95,63 @@ struct BlockStageLds {
     uint16_t mean[128];
 };
 
-// Own-block representative: the mean of rows 0 .. n-1 (1 <= n <= 256) of the
-// staged block s_own (row stride D), bf16(fp32(fp64 sum in row order / n))
-// per column, into mean[0 .. D) and, when dst is not null, dst[0 .. D).  One
-// thread per column (the first D threads); ends with a barrier.  Rows are
-// read U at a time, all U reads issued before the first addition (U = 64, or
-// 16 in 1024-thread workgroups, whose register budget is smaller); a round may
-// read past row n-1, never past the staging buffer (its kFusedOwnElems / D
-// rows are a multiple of U), and such rows are not added.
-template <int D, int U>
-__device__ __forceinline__ void own_block_mean(const uint16_t *s_own, int n, uint16_t *mean, uint16_t *dst) {
+// Own-block representative over rows 0 .. n-1 (1 <= n <= 256) of the staged
+// block s_own (row stride D), per column, into mean[0 .. D) and, when dst is
+// not null, dst[0 .. D): the mean bf16(fp32(fp64 sum in row order / n)), or
+// with MAX the largest value (the earliest row among equal values, +0 and
+// -0).  One thread per column (the first D threads); ends with a barrier.
+// Rows are read U at a time, all U reads issued before the first addition
+// (U = 64, or 16 in 1024-thread workgroups, whose register budget is
+// smaller); a round may read past row n-1, never past the staging buffer
+// (its kFusedOwnElems / D rows are a multiple of U), and such rows are not
+// used.
+template <int D, int U, bool MAX>
+__device__ __forceinline__ void own_block_rep(const uint16_t *s_own, int n, uint16_t *mean, uint16_t *dst) {
     static_assert((kFusedOwnElems / D) % U == 0, "rounds stay inside the staging buffer");
     const int c = threadIdx.x;
     if (c < D) {
         double sum = 0.0;
+        float bestf = -__builtin_huge_valf();
+        uint16_t best = 0;
         for (int r0 = 0; r0 < n; r0 += U) {
             const uint16_t *col = s_own + r0 * D + c;
             uint16_t x[U];
 #pragma unroll
             for (int j = 0; j < U; ++j) x[j] = col[j * D];
-            if (r0 + U <= n) {
+            auto take = [&](uint16_t h) {
+                const float v = bf16_to_f32(h);
+                if (MAX) {
+                    if (v > bestf) {
+                        bestf = v;
+                        best = h;
+                    }
+                } else {
+                    sum += static_cast<double>(v);
+                }
+            };
+            if (r0 + U <= n) {           // full round: no per-row test in the chain
 #pragma unroll
-                for (int j = 0; j < U; ++j) sum += static_cast<double>(bf16_to_f32(x[j]));
+                for (int j = 0; j < U; ++j) take(x[j]);
             } else {
 #pragma unroll
                 for (int j = 0; j < U; ++j)
-                    if (r0 + j < n) sum += static_cast<double>(bf16_to_f32(x[j]));
+                    if (r0 + j < n) take(x[j]);
             }
         }
-        const uint16_t mv = f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(n)));
+        const uint16_t mv = MAX ? best : f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(n)));
         mean[c] = mv;
         if (dst) dst[c] = mv;
     }
     __syncthreads();
+}
+
+template <int D, int U>
+__device__ __forceinline__ void own_block_rep(const FusedArgs &a, const uint16_t *s_own, int n, uint16_t *mean,
+                                              uint16_t *dst) {
+    if (a.pool_max)
+        own_block_rep<D, U, true>(s_own, n, mean, dst);
+    else
+        own_block_rep<D, U, false>(s_own, n, mean, dst);
 }
 
 // Scores every block b <= b_t of one query into s_keys (positions laid out by
@@ -205,8 +229,8 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
     }
 
     if (!own_in_pool) {
-        // own-block representative: the mean of rows b_t*B .. t; then wave 0 scores it
-        own_block_mean<D, NT >= 1024 ? 16 : 64>(s_own, own_rows, L.mean,
+        // own-block representative over rows b_t*B .. t; then wave 0 scores it
+        own_block_rep<D, NT >= 1024 ? 16 : 64>(a, s_own, own_rows, L.mean,
                                                write_pool ? a.pool_out + s * a.pool_seq_stride + bt * D : nullptr);
         if (wave == 0) {
             bf16x8 kbm[KS];
@@ -479,7 +503,7 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs 
     stage_query<MT, KS, kDecodeThreads>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, L.q, tid);
     if (tid < 64) L.w[tid] = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
     __syncthreads();
-    own_block_mean<D, 64>(s_own, own_rows, L.mean,
+    own_block_rep<D, 64>(a, s_own, own_rows, L.mean,
                       a.pool_out != nullptr && t == a.L - 1
                           ? a.pool_out + s * a.pool_seq_stride + static_cast<int64_t>(bt) * D
                           : nullptr);

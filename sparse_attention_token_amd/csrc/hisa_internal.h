@@ -119,6 +119,7 @@ struct FusedArgs {
     uint16_t *own_rep;        // ws [S*T][d]: own-block representative of every query
     uint32_t *blk_keys;       // ws [S*T][blk_stride]: block keys by block id
     int64_t blk_stride;
+    int pool_max;             // representatives by max pooling (else mean)
     // pool entry update fused into the block stage (pool_update_fusable):
     // non-null, every own block is computed from K, and the query at t = L-1
     // writes its own block's mean into pool_out[s][b_t] (the same buffer as
@@ -144,17 +145,18 @@ bool pool_update_fusable(int S, int T, int d, int64_t L, int B, int m);
 hipError_t launch_block_major_refine(const FusedArgs &a, hipStream_t st);
 hipError_t launch_block_major_blocks(const FusedArgs &a, hipStream_t st);
 
+// pool_max: max-pooled representatives instead of means (everywhere below)
 hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
-                              int64_t blk0, int64_t nblk, int64_t L_new, uint16_t *pool,
+                              int64_t blk0, int64_t nblk, int64_t L_new, bool pool_max, uint16_t *pool,
                               int64_t pool_seq_stride, hipStream_t st);
 
-// Own-block means of queries at the consecutive positions t = L - T + i
-// (requires T <= L): one pass per block.
+// Own-block representatives of queries at the consecutive positions
+// t = L - T + i (requires T <= L): one pass per block.
 hipError_t launch_own_prefix_mean(const uint16_t *K, int64_t k_seq_stride, int64_t L, int S, int T, int d, int B,
-                                  uint16_t *own_rep, hipStream_t st);
+                                  bool pool_max, uint16_t *own_rep, hipStream_t st);
 
 hipError_t launch_own_mean(const uint16_t *K, int64_t k_seq_stride, const int32_t *qpos,
-                           int64_t L, int S, int T, int d, int B, uint16_t *own_rep,
+                           int64_t L, int S, int T, int d, int B, bool pool_max, uint16_t *own_rep,
                            hipStream_t st);
 
 hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int64_t max_pos, hipStream_t st);

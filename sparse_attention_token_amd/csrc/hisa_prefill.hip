@@ -480,8 +480,10 @@ bool block_major_mode(int S, int T, int d, int64_t L, int B, int m) {
 }
 
 hipError_t launch_block_major_blocks(const FusedArgs &a, hipStream_t st) {
-    hipError_t e = a.qpos ? launch_own_mean(a.K, a.k_seq_stride, a.qpos, a.L, a.S, a.T, a.d, a.B, a.own_rep, st)
-                          : launch_own_prefix_mean(a.K, a.k_seq_stride, a.L, a.S, a.T, a.d, a.B, a.own_rep, st);
+    hipError_t e = a.qpos ? launch_own_mean(a.K, a.k_seq_stride, a.qpos, a.L, a.S, a.T, a.d, a.B, a.pool_max != 0,
+                                            a.own_rep, st)
+                          : launch_own_prefix_mean(a.K, a.k_seq_stride, a.L, a.S, a.T, a.d, a.B, a.pool_max != 0,
+                                                   a.own_rep, st);
     if (e != hipSuccess) return e;
     const int64_t nchunk = static_cast<int64_t>(a.S) * ((a.T + kBlkChunk - 1) / kBlkChunk);
     const dim3 g_blk(bm_grid((a.nblk + kBlkTileRows - 1) / kBlkTileRows, nchunk));

@@ -1,4 +1,4 @@
-// Block representatives: mean pooling of contiguous key blocks.
+// Block representatives: mean (or max) pooling of contiguous key blocks.
 //
 // Mean pooling of contiguous blocks of B keys is how the pages build the
 // coarse-stage block representatives (gptget.net English summary,
@@ -6,6 +6,10 @@
 // bf16 so that the block stage feeds the same bf16 matrix-core scorer as the
 // token stage; it is rounded once from the exact-order fp64 sum:
 //     mean = bf16_RNE( fp32_RNE( (sum over rows, increasing row, in fp64) / count ) ).
+// Max pooling, the alternative one page names for the coarse summaries ("Hierarchical
+// Indexing Makes Sparse Attention Actually Fast", section on the hierarchical
+// summarization of the KV cache), takes per column the largest key value,
+// the earliest row among equal values (+0 and -0), with no rounding at all.
 //
 // Blocks of up to 128 rows: one thread per column loads its column into
 // registers and adds it in row order (pool_append_direct_kernel).  Longer runs
@@ -25,10 +29,35 @@ constexpr int kPoolThreads = 256;
 constexpr int kMaxRows = 256;                       // largest supported B
 constexpr int kMaxD = 128;
 
+// Running representative of one column, rows added in row order: the fp64
+// sum (mean) or the largest value so far, the earliest kept on equal values.
+template <bool MAX>
+struct ColumnRep {
+    double sum = 0.0;
+    float bestf = -__builtin_huge_valf();
+    uint16_t best = 0;
+    __device__ __forceinline__ void add(uint16_t h) {
+        const float x = bf16_to_f32(h);
+        if (MAX) {
+            if (x > bestf) {
+                bestf = x;
+                best = h;
+            }
+        } else {
+            sum += static_cast<double>(x);
+        }
+    }
+    // representative of the n rows added so far
+    __device__ __forceinline__ uint16_t get(int64_t n) const {
+        return MAX ? best : f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(n)));
+    }
+};
+
 // Copy rows [0, rows) of `src` (row stride d elements) into LDS and return the
-// bf16 mean of column threadIdx.x (threads >= d return 0 and write nothing).
-__device__ __forceinline__ uint16_t staged_column_mean(const uint16_t *__restrict__ src,
-                                                       int rows, int d, uint16_t *lds) {
+// bf16 representative of column threadIdx.x (threads >= d return 0 and write nothing).
+template <bool MAX>
+__device__ __forceinline__ uint16_t staged_column_rep(const uint16_t *__restrict__ src,
+                                                      int rows, int d, uint16_t *lds) {
     constexpr int kMaxChunks = kMaxRows * kMaxD / 8 / kPoolThreads;   // 16-byte chunks per thread
     const int chunks_per_row = d / 8;
     const int total = rows * chunks_per_row;
@@ -52,18 +81,17 @@ __device__ __forceinline__ uint16_t staged_column_mean(const uint16_t *__restric
     __syncthreads();
     const int col = threadIdx.x;
     if (col >= d) return 0;
-    double sum = 0.0;
+    ColumnRep<MAX> acc;
     int r = 0;
-    for (; r + 8 <= rows; r += 8) {                    // 8 LDS reads in flight, adds in row order
-        float x[8];
+    for (; r + 8 <= rows; r += 8) {                    // 8 LDS reads in flight, added in row order
+        uint16_t x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = bf16_to_f32(lds[(r + j) * d + col]);
+        for (int j = 0; j < 8; ++j) x[j] = lds[(r + j) * d + col];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sum += static_cast<double>(x[j]);
+        for (int j = 0; j < 8; ++j) acc.add(x[j]);
     }
-    for (; r < rows; ++r) sum += static_cast<double>(bf16_to_f32(lds[r * d + col]));
-    const float mean = static_cast<float>(sum / static_cast<double>(rows));
-    return f32_to_bf16_rne(mean);
+    for (; r < rows; ++r) acc.add(lds[r * d + col]);
+    return acc.get(rows);
 }
 
 // Blocks of at most kDirectRows rows: one thread per column loads its whole
@@ -74,6 +102,7 @@ __device__ __forceinline__ uint16_t staged_column_mean(const uint16_t *__restric
 // loads across the threads form one coalesced read.
 constexpr int kDirectRows = 128;
 
+template <bool MAX>
 __global__ __launch_bounds__(kMaxD) void pool_append_direct_kernel(
         const uint16_t *__restrict__ K, int64_t k_seq_stride, int d, int B, int64_t blk0,
         int64_t L_new, uint16_t *__restrict__ pool, int64_t pool_seq_stride) {
@@ -90,14 +119,15 @@ __global__ __launch_bounds__(kMaxD) void pool_append_direct_kernel(
 #pragma unroll
     for (int r = 0; r < kDirectRows; ++r)
         x[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * col, (r < rows ? r : rows - 1) * d * 2, 0);
-    double sum = 0.0;
+    ColumnRep<MAX> acc;
 #pragma unroll
     for (int r = 0; r < kDirectRows; ++r)
-        if (r < rows) sum += static_cast<double>(bf16_to_f32(x[r]));
-    pool[s * pool_seq_stride + b * d + col] = f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(rows)));
+        if (r < rows) acc.add(x[r]);
+    pool[s * pool_seq_stride + b * d + col] = acc.get(rows);
 }
 
 // grid: (nblk, S).  Recomputes blocks [blk0, blk0 + nblk) over rows < L_new.
+template <bool MAX>
 __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(
         const uint16_t *__restrict__ K, int64_t k_seq_stride, int d, int B, int64_t blk0,
         int64_t L_new, uint16_t *__restrict__ pool, int64_t pool_seq_stride) {
@@ -106,12 +136,13 @@ __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(
     const int64_t b = blk0 + blockIdx.x;
     const int64_t r0 = b * B;
     const int rows = static_cast<int>(((r0 + B < L_new) ? r0 + B : L_new) - r0);
-    const uint16_t m = staged_column_mean(K + s * k_seq_stride + r0 * d, rows, d, lds);
+    const uint16_t m = staged_column_rep<MAX>(K + s * k_seq_stride + r0 * d, rows, d, lds);
     if (static_cast<int>(threadIdx.x) < d) pool[s * pool_seq_stride + b * d + threadIdx.x] = m;
 }
 
 // grid: (S*T).  Writes the representative of the query's own block
-// b_t = floor(t/B) -- the mean of rows [b_t*B, t] -- to own_rep[qi].
+// b_t = floor(t/B) -- over rows [b_t*B, t] -- to own_rep[qi].
+template <bool MAX>
 __global__ __launch_bounds__(kPoolThreads) void own_mean_kernel(
         const uint16_t *__restrict__ K, int64_t k_seq_stride, const int32_t *__restrict__ qpos,
         int64_t L, int T, int d, int B, uint16_t *__restrict__ own_rep) {
@@ -122,16 +153,18 @@ __global__ __launch_bounds__(kPoolThreads) void own_mean_kernel(
     const int64_t t = query_pos(qpos, qi, i, L, T);
     if (t < 0) return;
     const int64_t r0 = (t / B) * B;
-    const uint16_t m = staged_column_mean(K + s * k_seq_stride + r0 * d,
-                                          static_cast<int>(t + 1 - r0), d, lds);
+    const uint16_t m = staged_column_rep<MAX>(K + s * k_seq_stride + r0 * d,
+                                              static_cast<int>(t + 1 - r0), d, lds);
     if (static_cast<int>(threadIdx.x) < d) own_rep[static_cast<int64_t>(qi) * d + threadIdx.x] = m;
 }
 
 // grid: (blocks b_lo .. b_lo + gridDim.x - 1), d threads.  Consecutive query
 // positions t = L - T + i (one sequence per blockIdx.y): a running fp64 sum
-// down each block's rows, in row order, is at row t exactly the sum of rows
-// [b_t*B, t] in row order, so every query of the block gets its own-block
-// mean from one pass -- the same arithmetic as staged_column_mean().
+// (or running maximum) down each block's rows, in row order, is at row t
+// exactly that of rows [b_t*B, t] in row order, so every query of the block
+// gets its own-block representative from one pass -- the same arithmetic as
+// staged_column_rep().
+template <bool MAX>
 __global__ __launch_bounds__(kMaxD) void own_prefix_mean_kernel(
         const uint16_t *__restrict__ K, int64_t k_seq_stride, int64_t L, int T, int d, int B,
         int64_t b_lo, uint16_t *__restrict__ own_rep) {
@@ -143,61 +176,69 @@ __global__ __launch_bounds__(kMaxD) void own_prefix_mean_kernel(
     const int64_t r_first = r0 > t0 ? r0 : t0;                 // first row that is a query position
     const int64_t r_end = (r0 + B < L) ? r0 + B : L;
     const uint16_t *src = K + s * k_seq_stride + col;
-    double sum = 0.0;
+    ColumnRep<MAX> acc;
     int64_t r = r0;
     uint16_t nx[8];                                            // the next 8 rows, loads in flight
 #pragma unroll
     for (int j = 0; j < 8; ++j) nx[j] = r + j < r_end ? src[(r + j) * d] : 0;
     for (; r + 8 <= r_end; r += 8) {
-        float x[8];
+        uint16_t x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = bf16_to_f32(nx[j]);
+        for (int j = 0; j < 8; ++j) x[j] = nx[j];
 #pragma unroll
         for (int j = 0; j < 8; ++j) nx[j] = r + 8 + j < r_end ? src[(r + 8 + j) * d] : 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            sum += static_cast<double>(x[j]);
+            acc.add(x[j]);
             const int64_t rr = r + j;
-            if (rr >= r_first) {
-                const float mean = static_cast<float>(sum / static_cast<double>(rr + 1 - r0));
-                own_rep[(static_cast<int64_t>(s) * T + (rr - t0)) * d + col] = f32_to_bf16_rne(mean);
-            }
+            if (rr >= r_first) own_rep[(static_cast<int64_t>(s) * T + (rr - t0)) * d + col] = acc.get(rr + 1 - r0);
         }
     }
     for (; r < r_end; ++r) {
-        sum += static_cast<double>(bf16_to_f32(src[r * d]));
-        if (r >= r_first) {
-            const float mean = static_cast<float>(sum / static_cast<double>(r + 1 - r0));
-            own_rep[(static_cast<int64_t>(s) * T + (r - t0)) * d + col] = f32_to_bf16_rne(mean);
-        }
+        acc.add(src[r * d]);
+        if (r >= r_first) own_rep[(static_cast<int64_t>(s) * T + (r - t0)) * d + col] = acc.get(r + 1 - r0);
     }
 }
 
 }  // namespace
 
 hipError_t launch_own_prefix_mean(const uint16_t *K, int64_t k_seq_stride, int64_t L, int S, int T, int d, int B,
-                                  uint16_t *own_rep, hipStream_t st) {
+                                  bool pool_max, uint16_t *own_rep, hipStream_t st) {
     const int64_t b_lo = (L - T) / B, b_hi = (L - 1) / B;
-    return launch(kKindOwnMean, own_prefix_mean_kernel, dim3(static_cast<uint32_t>(b_hi - b_lo + 1), S),
-                  dim3(kMaxD), 0, st, K, k_seq_stride, L, T, d, B, b_lo, own_rep);
+    const dim3 g(static_cast<uint32_t>(b_hi - b_lo + 1), S);
+    if (pool_max)
+        return launch(kKindOwnMean, own_prefix_mean_kernel<true>, g, dim3(kMaxD), 0, st, K, k_seq_stride, L, T, d, B,
+                      b_lo, own_rep);
+    return launch(kKindOwnMean, own_prefix_mean_kernel<false>, g, dim3(kMaxD), 0, st, K, k_seq_stride, L, T, d, B,
+                  b_lo, own_rep);
 }
 
 hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
-                              int64_t blk0, int64_t nblk, int64_t L_new, uint16_t *pool,
+                              int64_t blk0, int64_t nblk, int64_t L_new, bool pool_max, uint16_t *pool,
                               int64_t pool_seq_stride, hipStream_t st) {
-    if (B <= kDirectRows)
-        return launch(kKindPoolAppend, pool_append_direct_kernel, dim3(static_cast<uint32_t>(nblk), S),
-                      dim3(kMaxD), 0, st, K, k_seq_stride, d, B, blk0, L_new, pool, pool_seq_stride);
-    return launch(kKindPoolAppend, pool_append_kernel, dim3(static_cast<uint32_t>(nblk), S),
-                  dim3(kPoolThreads), 0, st, K, k_seq_stride, d, B, blk0, L_new, pool,
-                  pool_seq_stride);
+    const dim3 g(static_cast<uint32_t>(nblk), S);
+    if (B <= kDirectRows) {
+        if (pool_max)
+            return launch(kKindPoolAppend, pool_append_direct_kernel<true>, g, dim3(kMaxD), 0, st, K, k_seq_stride,
+                          d, B, blk0, L_new, pool, pool_seq_stride);
+        return launch(kKindPoolAppend, pool_append_direct_kernel<false>, g, dim3(kMaxD), 0, st, K, k_seq_stride, d,
+                      B, blk0, L_new, pool, pool_seq_stride);
+    }
+    if (pool_max)
+        return launch(kKindPoolAppend, pool_append_kernel<true>, g, dim3(kPoolThreads), 0, st, K, k_seq_stride, d,
+                      B, blk0, L_new, pool, pool_seq_stride);
+    return launch(kKindPoolAppend, pool_append_kernel<false>, g, dim3(kPoolThreads), 0, st, K, k_seq_stride, d, B,
+                  blk0, L_new, pool, pool_seq_stride);
 }
 
 hipError_t launch_own_mean(const uint16_t *K, int64_t k_seq_stride, const int32_t *qpos,
-                           int64_t L, int S, int T, int d, int B, uint16_t *own_rep,
+                           int64_t L, int S, int T, int d, int B, bool pool_max, uint16_t *own_rep,
                            hipStream_t st) {
-    return launch(kKindOwnMean, own_mean_kernel, dim3(S * T), dim3(kPoolThreads), 0, st, K,
-                  k_seq_stride, qpos, L, T, d, B, own_rep);
+    if (pool_max)
+        return launch(kKindOwnMean, own_mean_kernel<true>, dim3(S * T), dim3(kPoolThreads), 0, st, K, k_seq_stride,
+                      qpos, L, T, d, B, own_rep);
+    return launch(kKindOwnMean, own_mean_kernel<false>, dim3(S * T), dim3(kPoolThreads), 0, st, K, k_seq_stride,
+                  qpos, L, T, d, B, own_rep);
 }
 
 }  // namespace hisa

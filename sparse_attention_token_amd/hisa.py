@@ -55,6 +55,14 @@ def lib():
     L.hisa_index.restype = i32
     L.hisa_index.argtypes = [vp, vp, vp, vp, i64, i64, vp, i64, i32, i32, i32, i32, i32, i32, i32,
                              vp, vp, vp, vp, sz, vp]
+    L.hisa_pool_append_mode.restype = i32
+    L.hisa_pool_append_mode.argtypes = [vp, i64, i32, i32, i32, i64, i64, vp, i64, i32, vp]
+    L.hisa_index_mode.restype = i32
+    L.hisa_index_mode.argtypes = [vp, vp, vp, vp, i64, i64, vp, i64, i32, i32, i32, i32, i32, i32, i32,
+                                  vp, vp, vp, vp, sz, i32, vp]
+    L.hisa_append_index_mode.restype = i32
+    L.hisa_append_index_mode.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                         i32, vp, vp, vp, vp, sz, i32, vp]
     L.hisa_append_index.restype = i32
     L.hisa_append_index.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                     i32, vp, vp, vp, vp, sz, vp]
@@ -111,8 +119,19 @@ def hisa_abi_version() -> int:
     return int(lib().hisa_abi_version())
 
 
-def hisa_pool_append(K: torch.Tensor, pool_mean: torch.Tensor, L_old: int, L_new: int, B: int):
-    """Fold key rows [L_old, L_new) of K [S, L_cap, d] into pool_mean [S, nblk_cap, d] (in place)."""
+POOL_KINDS = {"mean": 0, "max": 1}
+
+
+def _pool_kind(pool: str) -> int:
+    if pool not in POOL_KINDS:
+        raise ValueError(f"pool must be one of {sorted(POOL_KINDS)}")
+    return POOL_KINDS[pool]
+
+
+def hisa_pool_append(K: torch.Tensor, pool_mean: torch.Tensor, L_old: int, L_new: int, B: int,
+                     pool: str = "mean"):
+    """Fold key rows [L_old, L_new) of K [S, L_cap, d] into pool_mean [S, nblk_cap, d] (in place);
+    pool="max" keeps max-pooled representatives instead of means."""
     _bf16(K, "K")
     _bf16(pool_mean, "pool_mean")
     S, _, d = K.shape
@@ -122,8 +141,8 @@ def hisa_pool_append(K: torch.Tensor, pool_mean: torch.Tensor, L_old: int, L_new
         raise ValueError("pool_mean and K disagree on S")
     if pool_mean.shape[1] * B < L_new or K.shape[1] < L_new:
         raise ValueError("K or pool_mean too short for L_new")
-    st = lib().hisa_pool_append(_ptr(K), kss, S, d, B, int(L_old), int(L_new), _ptr(pool_mean),
-                                pss, _stream(K.device))
+    st = lib().hisa_pool_append_mode(_ptr(K), kss, S, d, B, int(L_old), int(L_new), _ptr(pool_mean),
+                                     pss, _pool_kind(pool), _stream(K.device))
     _check("hisa_pool_append", st)
     return pool_mean
 
@@ -167,9 +186,9 @@ def _workspace(nbytes: int, device, workspace):
 
 def hisa_index(q, w, K, L: int, pool_mean, B: int, m: int, k: int, qpos=None, *,
                want_scores: bool = True, want_blocks: bool = False, out_idx=None, out_score=None,
-               out_blk=None, workspace=None):
+               out_blk=None, workspace=None, pool: str = "mean"):
     """HISA two-stage indexer.  Returns (idx [S,T,k] int32, score [S,T,k] fp32 | None,
-    blocks [S,T,m] int32 | None)."""
+    blocks [S,T,m] int32 | None).  pool: how pool_mean was built ("mean" or "max")."""
     S, T, H, d, kss = _query_args(q, w, qpos, K, L)
     _bf16(pool_mean, "pool_mean")
     pss = _rows(pool_mean, "pool_mean", d)
@@ -187,16 +206,16 @@ def hisa_index(q, w, K, L: int, pool_mean, B: int, m: int, k: int, qpos=None, *,
         _check("hisa_index", lib().hisa_index(None, None, None, None, 0, L, None, 0, S, T, H, d, B,
                                               m, k, None, None, None, None, 0, None))
     ws = _workspace(nbytes, dev, workspace)
-    st = lib().hisa_index(_ptr(q), _ptr(w), _ptr(qpos), _ptr(K), kss, int(L), _ptr(pool_mean),
-                          pss, S, T, H, d, B, m, k, _ptr(out_idx), _ptr(out_score), _ptr(out_blk),
-                          _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    st = lib().hisa_index_mode(_ptr(q), _ptr(w), _ptr(qpos), _ptr(K), kss, int(L), _ptr(pool_mean),
+                               pss, S, T, H, d, B, m, k, _ptr(out_idx), _ptr(out_score), _ptr(out_blk),
+                               _ptr(ws), ws.numel() * ws.element_size(), _pool_kind(pool), _stream(dev))
     _check("hisa_index", st)
     return out_idx, out_score, out_blk
 
 
 def hisa_append_index(K, pool_mean, L_old: int, L_new: int, q, w, B: int, m: int, k: int, qpos=None, *,
                       want_scores: bool = True, want_blocks: bool = False, out_idx=None, out_score=None,
-                      out_blk=None, workspace=None):
+                      out_blk=None, workspace=None, pool: str = "mean"):
     """One decode step: hisa_pool_append(K, pool_mean, L_old, L_new, B) then
     hisa_index(q, w, K, L_new, pool_mean, B, m, k, qpos), with the same results
     (the last block's mean is stored from the block stage when the appended
@@ -219,9 +238,10 @@ def hisa_append_index(K, pool_mean, L_old: int, L_new: int, q, w, B: int, m: int
                                                             None, S, T, H, d, B, m, k, None, None, None, None,
                                                             0, None))
     ws = _workspace(nbytes, dev, workspace)
-    st = lib().hisa_append_index(_ptr(K), kss, int(L_old), int(L_new), _ptr(pool_mean), pss, _ptr(q), _ptr(w),
-                                 _ptr(qpos), S, T, H, d, B, m, k, _ptr(out_idx), _ptr(out_score), _ptr(out_blk),
-                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    st = lib().hisa_append_index_mode(_ptr(K), kss, int(L_old), int(L_new), _ptr(pool_mean), pss, _ptr(q),
+                                      _ptr(w), _ptr(qpos), S, T, H, d, B, m, k, _ptr(out_idx), _ptr(out_score),
+                                      _ptr(out_blk), _ptr(ws), ws.numel() * ws.element_size(), _pool_kind(pool),
+                                      _stream(dev))
     _check("hisa_append_index", st)
     return out_idx, out_score, out_blk
 

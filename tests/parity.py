@@ -44,35 +44,36 @@ def bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def build_pool(hisa, K, L, B, L_bulk=None, step=1):
-    """Pool means for rows [0, L): one bulk append of [0, L_bulk), then appends of `step` rows."""
+def build_pool(hisa, K, L, B, L_bulk=None, step=1, pool="mean"):
+    """Pool representatives for rows [0, L): one bulk append of [0, L_bulk), then appends of `step` rows."""
     import torch
 
     S, _, d = K.shape
     nblk = -(-L // B)
-    pool = torch.zeros((S, nblk, d), dtype=torch.bfloat16, device=K.device)
+    reps = torch.zeros((S, nblk, d), dtype=torch.bfloat16, device=K.device)
     L_bulk = L if L_bulk is None else L_bulk
-    hisa.hisa_pool_append(K, pool, 0, L_bulk, B)
+    hisa.hisa_pool_append(K, reps, 0, L_bulk, B, pool=pool)
     x = L_bulk
     while x < L:
         y = min(L, x + step)
-        hisa.hisa_pool_append(K, pool, x, y, B)
+        hisa.hisa_pool_append(K, reps, x, y, B, pool=pool)
         x = y
-    return pool
+    return reps
 
 
 def _kth(scores_desc, n):
     return scores_desc[n - 1]
 
 
-def check_hisa_row(orc, case, s, i, g_idx, g_score, g_blk, report=None):
-    """Apply the comparison rule to one GPU output row of hisa_index."""
+def check_hisa_row(orc, case, s, i, g_idx, g_score, g_blk, report=None, pool="mean"):
+    """Apply the comparison rule to one GPU output row of hisa_index (block
+    representatives pooled by `pool`, "mean" or "max")."""
     q, w, K = case.q[s, i], case.w[s, i], case.K[s]
     t = int(case.qpos[s, i])
     B, m, k = case.B, case.m, case.k
     nb = t // B + 1
     meff = min(m, nb)
-    o_idx, o_sc, o_blk, o_bsc, o_keff = orc.hisa_query(q, w, K, t, B, m, k)
+    o_idx, o_sc, o_blk, o_bsc, o_keff = orc.hisa_query(q, w, K, t, B, m, k, mode=pool)
 
     # -- blocks
     g_blk = np.asarray(g_blk)

@@ -43,6 +43,7 @@ def _gpu_visible():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("hisa_pool_append", "hisa_index", "hisa_append_index", "dsa_flat_index",
+              "hisa_pool_append_mode", "hisa_index_mode", "hisa_append_index_mode",
               "hisa_index_workspace", "dsa_flat_workspace", "hisa_status_string", "hisa_abi_version"):
         assert n in names
 
@@ -53,7 +54,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hisa_abi_version() == 2
+    assert lib.hisa_abi_version() == 3
     for code in (OK, ARG, UNSUP, WS, HIP, 12345):
         assert isinstance(lib.hisa_status_string(code), bytes)
     assert lib.hisa_status_string(WS) != lib.hisa_status_string(ARG)
@@ -98,6 +99,15 @@ def test_argument_checks_with_null_pointers(lib):
                                  None, None, None, None, 0, None) == UNSUP
     assert lib.hisa_append_index(None, 0, 10, 5, None, 0, None, None, None, 1, 1, 4, 64, 64, 2, 8,
                                  None, None, None, None, 0, None) == ARG   # L_new < L_old
+    # the *_mode calls: an unknown pool kind, then the plain calls' checks
+    assert lib.hisa_pool_append_mode(None, 0, 1, 64, 64, 0, 10, None, 0, 7, None) == ARG
+    assert lib.hisa_pool_append_mode(None, 0, 1, 64, 64, 0, 10, None, 0, 1, None) == ARG
+    assert lib.hisa_index_mode(None, None, None, None, 0, 100, None, 0, 1, 1, 4, 64, 64, 2, 8,
+                               None, None, None, None, 0, -1, None) == ARG
+    assert lib.hisa_index_mode(None, None, None, None, 0, 100, None, 0, 1, 1, 4, 96, 64, 2, 8,
+                               None, None, None, None, 0, 1, None) == UNSUP
+    assert lib.hisa_append_index_mode(None, 0, 0, 10, None, 0, None, None, None, 1, 1, 4, 64, 64, 2, 8,
+                                      None, None, None, None, 0, 2, None) == ARG
     # profiler argument checks
     ms, n = C.c_double(), C.c_int()
     assert lib.hisa_profile_read(-1, C.byref(ms), C.byref(n)) == ARG

@@ -50,7 +50,7 @@ def _run(hisa, case, qpos_on_device=True, want_flat=True):
 
 
 def test_abi_version(hisa):
-    assert hisa.hisa_abi_version() == 2
+    assert hisa.hisa_abi_version() == 3
 
 
 # ---------------------------------------------------------------- block pool
@@ -114,16 +114,19 @@ def test_pool_append_is_idempotent(hisa, orc):
 # ---------------------------------------------------------------- append + index in one call
 
 APPEND_INDEX = [
-    # name, S, L_old, L_new, T, H, d, B, m, k, explicit positions
-    ("decode_one_launch", 4, 3000, 3001, 1, 64, 128, 128, 8, 300, False),
-    ("decode_new_block", 2, 3072, 3073, 1, 64, 128, 128, 8, 300, False),
-    ("decode_two_kernel", 2, 40000, 40001, 1, 16, 64, 64, 20, 400, False),
-    ("query_major_20q", 1, 5000, 5003, 20, 32, 128, 128, 8, 300, False),
+    # name, S, L_old, L_new, T, H, d, B, m, k, explicit positions, pooling
+    ("decode_one_launch", 4, 3000, 3001, 1, 64, 128, 128, 8, 300, False, "mean"),
+    ("decode_new_block", 2, 3072, 3073, 1, 64, 128, 128, 8, 300, False, "mean"),
+    ("decode_two_kernel", 2, 40000, 40001, 1, 16, 64, 64, 20, 400, False, "mean"),
+    ("query_major_20q", 1, 5000, 5003, 20, 32, 128, 128, 8, 300, False, "mean"),
+    ("decode_one_launch_max", 4, 3000, 3001, 1, 64, 128, 128, 8, 300, False, "max"),
+    ("decode_two_kernel_max", 2, 40000, 40001, 1, 16, 64, 64, 20, 400, False, "max"),
     # not fused: rows over two blocks, explicit positions, block-by-block prefill, nothing appended
-    ("rows_span_two_blocks", 2, 3070, 3075, 1, 64, 128, 128, 8, 300, False),
-    ("explicit_positions", 2, 3000, 3001, 3, 64, 128, 128, 8, 300, True),
-    ("prefill_128q", 1, 2000, 2128, 128, 16, 64, 64, 6, 128, False),
-    ("nothing_appended", 2, 3001, 3001, 1, 64, 128, 128, 8, 300, False),
+    ("rows_span_two_blocks", 2, 3070, 3075, 1, 64, 128, 128, 8, 300, False, "mean"),
+    ("explicit_positions", 2, 3000, 3001, 3, 64, 128, 128, 8, 300, True, "mean"),
+    ("prefill_128q", 1, 2000, 2128, 128, 16, 64, 64, 6, 128, False, "mean"),
+    ("prefill_128q_max", 1, 2000, 2128, 128, 16, 64, 64, 6, 128, False, "max"),
+    ("nothing_appended", 2, 3001, 3001, 1, 64, 128, 128, 8, 300, False, "mean"),
 ]
 
 
@@ -134,7 +137,7 @@ def test_append_index_equals_append_then_index(hisa, orc, spec):
     is fused into the block stage; sampled rows also against the oracle."""
     import torch
 
-    name, S, L0, L1, T, H, d, B, m, k, explicit = spec
+    name, S, L0, L1, T, H, d, B, m, k, explicit, pool = spec
     _say(f"append+index {name}")
     qpos = None
     if explicit:
@@ -143,7 +146,7 @@ def test_append_index_equals_append_then_index(hisa, orc, spec):
     c = synth.clustered_case(S, L1, T, H, d, B, m, k, seed=41, qpos=qpos, latent_block=B)
     dev = to_dev(c)
     qp = dev["qpos"] if explicit else None
-    base = build_pool(hisa, dev["K"], L0, B) if L0 > 0 else None
+    base = build_pool(hisa, dev["K"], L0, B, pool=pool) if L0 > 0 else None
     nblk = -(-L1 // B)
     pools = []
     for _ in range(2):
@@ -151,18 +154,82 @@ def test_append_index_equals_append_then_index(hisa, orc, spec):
         if base is not None:
             p[:, :base.shape[1]] = base[:, :nblk]
         pools.append(p)
-    hisa.hisa_pool_append(dev["K"], pools[0], L0, L1, B)
-    a = hisa.hisa_index(dev["q"], dev["w"], dev["K"], L1, pools[0], B, m, k, qp, want_blocks=True)
-    b = hisa.hisa_append_index(dev["K"], pools[1], L0, L1, dev["q"], dev["w"], B, m, k, qp, want_blocks=True)
+    hisa.hisa_pool_append(dev["K"], pools[0], L0, L1, B, pool=pool)
+    a = hisa.hisa_index(dev["q"], dev["w"], dev["K"], L1, pools[0], B, m, k, qp, want_blocks=True, pool=pool)
+    b = hisa.hisa_append_index(dev["K"], pools[1], L0, L1, dev["q"], dev["w"], B, m, k, qp, want_blocks=True,
+                               pool=pool)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x.cpu().numpy().view(np.int32), y.cpu().numpy().view(np.int32))
     np.testing.assert_array_equal(bits(pools[0]), bits(pools[1]))
-    np.testing.assert_array_equal(bits(pools[1]), orc.pool(c.K, L1, B))
+    np.testing.assert_array_equal(bits(pools[1]), orc.pool(c.K, L1, B, mode=pool))
     idx, sc, blk = (t.cpu().numpy() for t in b)
     for s in range(S):
         for i in sorted({0, T - 1}):
-            check_hisa_row(orc, c, s, i, idx[s, i], sc[s, i], blk[s, i])
+            check_hisa_row(orc, c, s, i, idx[s, i], sc[s, i], blk[s, i], pool=pool)
+
+
+# ---------------------------------------------------------------- max pooling
+
+def _with_ties(c, seed):
+    """Plant ties for max pooling: zeros of both signs, repeated values, and a
+    column whose entries are all <= 0."""
+    rng = np.random.default_rng(seed)
+    f = synth.bf16_to_f32(c.K).copy()
+    f[rng.random(f.shape) < 0.15] = 0.0
+    f[rng.random(f.shape) < 0.10] = -0.0
+    f[rng.random(f.shape) < 0.05] = 1.5
+    f[..., 0] = -np.abs(f[..., 0])
+    c.K = synth.bf16_bits(f)
+    return c
+
+
+@pytest.mark.parametrize("B,d,L,S", [(16, 64, 100, 2), (64, 64, 1000, 1), (128, 128, 128 * 5 + 77, 2),
+                                     (256, 128, 3000, 1)])
+def test_max_pool_bit_exact(hisa, orc, B, d, L, S):
+    _say(f"max pool B={B} d={d} L={L} S={S}")
+    c = _with_ties(synth.gaussian_case(S, L, 1, 1, d, B, 1, 1, seed=B * 3 + L), B)
+    dev = to_dev(c)
+    ref = orc.pool(c.K, L, B, mode="max")
+    np.testing.assert_array_equal(bits(build_pool(hisa, dev["K"], L, B, pool="max")), ref)
+    np.testing.assert_array_equal(bits(build_pool(hisa, dev["K"], L, B, L_bulk=L // 3, step=1, pool="max")), ref)
+
+
+MAX_CASES = [
+    # name, S, L, T, H, d, B, m, k, kind, explicit positions
+    ("decode_one_launch", 4, 3000, 1, 64, 128, 128, 8, 300, "clustered", False),
+    ("decode_edge_positions", 2, 2000, 8, 16, 64, 64, 5, 100, "gaussian", True),
+    ("decode_two_kernel", 2, 40000, 1, 16, 64, 64, 20, 400, "clustered", False),
+    ("query_major_20q", 1, 5000, 20, 32, 128, 128, 8, 300, "clustered", False),
+    ("block_major", 1, 8192, 512, 64, 128, 128, 8, 512, "clustered", False),
+    ("block_major_explicit", 1, 6000, 256, 16, 64, 64, 6, 128, "clustered", True),
+    ("general_B256", 1, 3000, 6, 64, 128, 256, 3, 300, "clustered", True),
+]
+
+
+@pytest.mark.parametrize("spec", MAX_CASES, ids=[s[0] for s in MAX_CASES])
+def test_hisa_max_pool(hisa, orc, spec):
+    import torch
+
+    name, S, L, T, H, d, B, m, k, kind, explicit = spec
+    _say(f"max pooling {name}")
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    qpos = np.stack([_edge_qpos(L, B, T, rng) for _ in range(S)]) if explicit else None
+    if kind == "gaussian":
+        c = synth.gaussian_case(S, L, T, H, d, B, m, k, seed=9, qpos=qpos)
+    else:
+        c = synth.clustered_case(S, L, T, H, d, B, m, k, seed=9, qpos=qpos, latent_block=B)
+    c = _with_ties(c, 3)
+    dev = to_dev(c)
+    pool = build_pool(hisa, dev["K"], L, B, pool="max")
+    idx, sc, blk = hisa.hisa_index(dev["q"], dev["w"], dev["K"], L, pool, B, m, k,
+                                   dev["qpos"] if explicit else None, want_blocks=True, pool="max")
+    torch.cuda.synchronize()
+    idx, sc, blk = idx.cpu().numpy(), sc.cpu().numpy(), blk.cpu().numpy()
+    rows = range(T) if T <= 32 else range(0, T, 7)
+    for s in range(S):
+        for i in rows:
+            check_hisa_row(orc, c, s, i, idx[s, i], sc[s, i], blk[s, i], pool="max")
 
 
 # ---------------------------------------------------------------- small cases
