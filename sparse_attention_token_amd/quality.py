@@ -11,9 +11,12 @@ cache stays in the last-level cache across repeats here, unlike bench.py).
 
 The block-sparse baseline keeps the floor(k/B) best whole blocks by the same
 block score; that is hisa_index with m = k/B, whose refinement then keeps
-every candidate.
+every candidate.  Both run with mean-pooled and with max-pooled block
+representatives (the two poolings one page names for the coarse summaries:
+"Hierarchical Indexing Makes Sparse Attention Actually Fast", section on the
+hierarchical summarization of the KV cache).
 
-    python -m sparse_attention_token_amd.quality [--workload 2] [--blocks 64,128,256]
+    python -m sparse_attention_token_amd.quality [--workload 2] [--blocks 64,128,256] [--pools mean,max]
 
 Prints a markdown table.  Every selection runs in the library's HIP kernels.
 """
@@ -36,6 +39,7 @@ def main(argv=None):
     p.add_argument("--multiples", default="1,2,4,8",
                    help="candidate budgets m*B as multiples of k (1 = block-sparse)")
     p.add_argument("--reps", type=int, default=20)
+    p.add_argument("--pools", default="mean,max", help="block representatives: mean and/or max pooling")
     args = p.parse_args(argv)
 
     import torch
@@ -76,27 +80,29 @@ def main(argv=None):
     torch.cuda.synchronize()
     rows.append(("flat", "-", "-", 1.0, recall(flat), e0.elapsed_time(e1) * 1e3 / args.reps))
 
-    for B in (int(x) for x in args.blocks.split(",")):
-        nblk = -(-L // B)
-        pool = torch.zeros((S, nblk, case.d), dtype=torch.bfloat16, device=dev)
-        hisa.hisa_pool_append(K, pool, 0, L, B)
-        for mult in (int(x) for x in args.multiples.split(",")):
-            m = mult * k // B
-            if m < 1 or m > 4096 or m * B > (1 << 20):
-                continue
-            ws = torch.empty(hisa.hisa_index_workspace(S, T, case.H, case.d, L, B, m, k), dtype=torch.uint8,
-                             device=dev)
-            idx, sc, _ = hisa.hisa_index(q, w, K, L, pool, B, m, k, None, workspace=ws)
-            torch.cuda.synchronize()
-            sets = _sets(idx.cpu().numpy())
-            iou = float(np.mean([len(a & b) / max(1, len(a | b)) for a, b in zip(sets, flat)]))
-            e0.record()
-            for _ in range(args.reps):
-                hisa.hisa_index(q, w, K, L, pool, B, m, k, None, out_idx=idx, out_score=sc, workspace=ws)
-            e1.record()
-            torch.cuda.synchronize()
-            name = "block-sparse" if mult == 1 else "HISA"
-            rows.append((name, B, m, iou, recall(sets), e0.elapsed_time(e1) * 1e3 / args.reps))
+    for pk in args.pools.split(","):
+        for B in (int(x) for x in args.blocks.split(",")):
+            nblk = -(-L // B)
+            pool = torch.zeros((S, nblk, case.d), dtype=torch.bfloat16, device=dev)
+            hisa.hisa_pool_append(K, pool, 0, L, B, pool=pk)
+            for mult in (int(x) for x in args.multiples.split(",")):
+                m = mult * k // B
+                if m < 1 or m > 4096 or m * B > (1 << 20):
+                    continue
+                ws = torch.empty(hisa.hisa_index_workspace(S, T, case.H, case.d, L, B, m, k), dtype=torch.uint8,
+                                 device=dev)
+                idx, sc, _ = hisa.hisa_index(q, w, K, L, pool, B, m, k, None, workspace=ws, pool=pk)
+                torch.cuda.synchronize()
+                sets = _sets(idx.cpu().numpy())
+                iou = float(np.mean([len(a & b) / max(1, len(a | b)) for a, b in zip(sets, flat)]))
+                e0.record()
+                for _ in range(args.reps):
+                    hisa.hisa_index(q, w, K, L, pool, B, m, k, None, out_idx=idx, out_score=sc, workspace=ws,
+                                    pool=pk)
+                e1.record()
+                torch.cuda.synchronize()
+                name = ("block-sparse" if mult == 1 else "HISA") + f" ({pk})"
+                rows.append((name, B, m, iou, recall(sets), e0.elapsed_time(e1) * 1e3 / args.reps))
 
     print(f"workload {case.name}: S={S} T={T} L={L} H={case.H} d={case.d} k={k}; "
           f"{0 if needles is None else needles.size} needles")
