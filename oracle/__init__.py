@@ -14,6 +14,7 @@ from .oracle import (  # noqa: F401
     refine_query,
     hisa_query,
     block_sparse_query,
+    tree_query,
     hisa_batch,
     flat_batch,
 )

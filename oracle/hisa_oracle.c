@@ -286,6 +286,69 @@ int oracle_hisa_query(const uint16_t *q, const float *w, const uint16_t *K,
                                   out_blk, blk_score);
 }
 
+/* ---------- three-level hierarchy: super-blocks -> blocks -> tokens [P1-Summary] ---------- */
+
+/* The summary page's tree read as three levels over the key cache: blocks of
+ * B keys grouped into super-blocks of G blocks (G*B keys).  A node's
+ * representative pools its keys like a block's (mode as rep_rows); a node
+ * that holds the query position t is pooled over its keys up to t.  The
+ * query keeps the W best super-blocks, then the m best of the blocks inside
+ * them (blocks b <= floor(t/B)), then the k best tokens j <= t of those
+ * blocks; every ranking is (score desc, id asc).
+ *  out_sblk [W]: kept super-blocks, ascending, -1 padded (nullable).
+ *  out_blk [m]: kept blocks, ascending, -1 padded.
+ * Returns k_eff, or -1 on allocation failure. */
+int oracle_tree_query(const uint16_t *q, const float *w, const uint16_t *K, int H, int d, int64_t t,
+                      int B, int G, int W, int m, int k, int mode, int32_t *out_idx, float *out_score,
+                      int32_t *out_blk, int32_t *out_sblk)
+{
+    int64_t SB = (int64_t)G * B;     /* keys per super-block */
+    int64_t bt = t / B, st = t / SB;
+    int64_t ns = st + 1;             /* super-blocks visible to the query */
+    uint16_t *rep = (uint16_t *)malloc((size_t)d * sizeof *rep);
+    cand_t *sc = (cand_t *)malloc((size_t)ns * sizeof *sc);
+    int32_t *ssel = (int32_t *)malloc((size_t)(W > 0 ? W : 1) * sizeof *ssel);
+    cand_t *bc = (cand_t *)malloc(((size_t)(W > 0 ? W : 1) * G) * sizeof *bc);
+    int32_t *sel = (int32_t *)malloc((size_t)(m > 0 ? m : 1) * sizeof *sel);
+    if (!rep || !sc || !ssel || !bc || !sel) {
+        free(rep); free(sc); free(ssel); free(bc); free(sel);
+        return -1;
+    }
+    /* level 1: every super-block representative */
+    for (int64_t u = 0; u < ns; ++u) {
+        int64_t r1 = (u < st) ? (u + 1) * SB : t + 1;
+        rep_rows(K, u * SB, r1, d, mode, rep);
+        sc[u].s = oracle_score(q, w, rep, H, d);
+        sc[u].i = u;
+    }
+    qsort(sc, (size_t)ns, sizeof *sc, by_score_then_index);
+    int weff = ns < W ? (int)ns : W;
+    for (int i = 0; i < weff; ++i) ssel[i] = (int32_t)sc[i].i;
+    qsort(ssel, (size_t)weff, sizeof *ssel, by_index);
+    if (out_sblk)
+        for (int i = 0; i < W; ++i) out_sblk[i] = i < weff ? ssel[i] : -1;
+    /* level 2: the blocks of the kept super-blocks */
+    int64_t nc = 0;
+    for (int i = 0; i < weff; ++i) {
+        for (int64_t b = (int64_t)ssel[i] * G; b < (int64_t)(ssel[i] + 1) * G && b <= bt; ++b) {
+            int64_t r1 = (b < bt) ? (b + 1) * B : t + 1;
+            rep_rows(K, b * B, r1, d, mode, rep);
+            bc[nc].s = oracle_score(q, w, rep, H, d);
+            bc[nc].i = b;
+            ++nc;
+        }
+    }
+    qsort(bc, (size_t)nc, sizeof *bc, by_score_then_index);
+    int meff = nc < m ? (int)nc : m;
+    for (int i = 0; i < meff; ++i) sel[i] = (int32_t)bc[i].i;
+    qsort(sel, (size_t)meff, sizeof *sel, by_index);
+    for (int i = 0; i < m; ++i) out_blk[i] = i < meff ? sel[i] : -1;
+    /* level 3: the original indexer on the tokens of the kept blocks */
+    int keff = oracle_refine_query(q, w, K, H, d, t, B, sel, meff, k, out_idx, out_score, NULL);
+    free(rep); free(sc); free(ssel); free(bc); free(sel);
+    return keff;
+}
+
 /* ---------- batched drivers (OpenMP over queries) ---------- */
 
 /* Queries are q[S][T][H][d], w[S][T][H], qpos[S][T]; K row j of sequence s at

@@ -52,6 +52,9 @@ def load():
     lib.oracle_hisa_query_mode.restype = I
     lib.oracle_hisa_query_mode.argtypes = [_u16p, _f32p, _u16p, _u16p, I, I, I64, I, I, I, I,
                                            _i32p, _f32p, _i32p, _f64p]
+    lib.oracle_tree_query.restype = I
+    lib.oracle_tree_query.argtypes = [_u16p, _f32p, _u16p, I, I, I64, I, I, I, I, I, I, _i32p, _f32p,
+                                      _i32p, _i32p]
     lib.oracle_block_sparse_query.restype = I
     lib.oracle_block_sparse_query.argtypes = [_u16p, _f32p, _u16p, I, I, I64, I, I, _i32p, _i32p]
     lib.oracle_hisa_batch.restype = I
@@ -170,6 +173,23 @@ def hisa_query(q, w, K, t: int, B: int, m: int, k: int, mode: str = "mean"):
     if keff < 0:
         raise MemoryError("oracle_hisa_query failed")
     return idx, sc, blk, bsc, keff
+
+
+def tree_query(q, w, K, t: int, B: int, G: int, W: int, m: int, k: int, mode: str = "mean"):
+    """Three-level HISA for one query (super-blocks of G blocks of B keys; W super-blocks,
+    m blocks, k tokens kept): (idx [k], score [k], blocks [m], super-blocks [W], k_eff)."""
+    q, w, K = _c(q, np.uint16), _c(w, np.float32), _c(K, np.uint16)
+    H, d = q.shape
+    idx = np.zeros(k, dtype=np.int32)
+    sc = np.zeros(k, dtype=np.float32)
+    blk = np.zeros(m, dtype=np.int32)
+    sblk = np.zeros(W, dtype=np.int32)
+    keff = load().oracle_tree_query(_p(q, _u16p), _p(w, _f32p), _p(K, _u16p), H, d, t, B, G, W, m, k,
+                                    _mode(mode), _p(idx, _i32p), _p(sc, _f32p), _p(blk, _i32p),
+                                    _p(sblk, _i32p))
+    if keff < 0:
+        raise MemoryError("oracle_tree_query failed")
+    return idx, sc, blk, sblk, keff
 
 
 def block_sparse_query(q, w, K, t: int, B: int, k: int):

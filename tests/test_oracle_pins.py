@@ -210,6 +210,93 @@ def test_max_pool_hisa_bruteforce(orc):
         np.testing.assert_array_equal(idx, want)
 
 
+# ---------------------------------------------------------------- three-level hierarchy
+
+TREE_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tree_example.json")
+
+
+def test_golden_tree_example(orc):
+    with open(TREE_GOLDEN) as f:
+        g = json.load(f)
+    q = bf16_bits(np.array(g["q"], dtype=np.float32))
+    w = np.array(g["w"], dtype=np.float32)
+    K = bf16_bits(np.array(g["K"], dtype=np.float32))
+    for mode in ("mean", "max"):
+        e = g[mode]
+        idx, sc, blk, sblk, keff = orc.tree_query(q, w, K, g["t"], g["B"], g["G"], g["W"], g["m"], g["k"], mode=mode)
+        assert [u for u in sblk if u >= 0] == e["sblocks"], mode
+        assert [b for b in blk if b >= 0] == e["blocks"], mode
+        assert list(idx) == e["idx"], mode
+        np.testing.assert_array_equal(sc, np.array(e["score"], dtype=np.float32))
+    fidx, fsc, _ = orc.flat_query(q, w, K, g["t"], g["k"])
+    assert list(fidx) == g["flat"]["idx"]
+
+
+@pytest.mark.parametrize("mode", ["mean", "max"])
+def test_tree_with_every_super_block_is_hisa(orc, mode):
+    rng = np.random.default_rng(21)
+    for trial in range(12):
+        B, G = int(rng.choice([2, 4, 8])), int(rng.choice([2, 3, 4]))
+        t = int(rng.integers(0, 90))
+        q, w, K = int_case(rng, t + 1, 2, 6)
+        m, k = int(rng.integers(1, 6)), int(rng.integers(1, 15))
+        W = t // (B * G) + 1 + int(rng.integers(0, 3))
+        a = orc.tree_query(q, w, K, t, B, G, W, m, k, mode=mode)
+        b = orc.hisa_query(q, w, K, t, B, m, k, mode=mode)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+        np.testing.assert_array_equal(a[2], b[2])
+
+
+@pytest.mark.parametrize("mode", ["mean", "max"])
+def test_tree_with_unit_fanout_is_hisa_with_fewer_blocks(orc, mode):
+    # G = 1: a super-block is a block, pooled over the same keys, so keeping W
+    # of them and then m of those keeps the min(W, m) best blocks
+    rng = np.random.default_rng(22)
+    for trial in range(12):
+        B = int(rng.choice([1, 2, 4]))
+        t = int(rng.integers(0, 60))
+        q, w, K = int_case(rng, t + 1, 2, 5)
+        W, m, k = int(rng.integers(1, 8)), int(rng.integers(1, 8)), int(rng.integers(1, 12))
+        a = orc.tree_query(q, w, K, t, B, 1, W, m, k, mode=mode)
+        b = orc.hisa_query(q, w, K, t, B, min(W, m), k, mode=mode)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+        np.testing.assert_array_equal(a[2][:min(W, m)], b[2][:min(W, m)])
+
+
+def test_tree_keep_everything_is_flat(orc):
+    rng = np.random.default_rng(23)
+    q, w, K = int_case(rng, 80, 3, 8)
+    idx, sc, blk, sblk, keff = orc.tree_query(q, w, K, 79, 4, 3, 50, 50, 25)
+    fidx, fsc, _ = orc.flat_query(q, w, K, 79, 25)
+    np.testing.assert_array_equal(idx, fidx)
+    np.testing.assert_array_equal(sc, fsc)
+
+
+@pytest.mark.parametrize("mode", ["mean", "max"])
+def test_tree_bruteforce(orc, mode):
+    rng = np.random.default_rng(24 if mode == "mean" else 25)
+    rep = np_mean_bits if mode == "mean" else np_max_bits
+    for trial in range(25):
+        B, G = int(rng.choice([1, 2, 4])), int(rng.choice([2, 3, 4]))
+        t = int(rng.integers(0, 70))
+        q, w, K = int_case(rng, t + 1, 2, 4)
+        W, m, k = int(rng.integers(1, 4)), int(rng.integers(1, 6)), int(rng.integers(1, 10))
+        SB, bt, st = B * G, t // B, t // (B * G)
+        srep = [rep(K[u * SB:((u + 1) * SB if u < st else t + 1)]) for u in range(st + 1)]
+        ssel = np.sort(np_topk(np_scores(q, w, np.stack(srep)), np.arange(st + 1), min(W, st + 1)))
+        cb = np.array([b for u in ssel for b in range(u * G, min((u + 1) * G, bt + 1))], dtype=np.int64)
+        brep = [rep(K[b * B:((b + 1) * B if b < bt else t + 1)]) for b in cb]
+        bsel = np.sort(np_topk(np_scores(q, w, np.stack(brep)), cb, min(m, len(cb))))
+        cand = np.array([j for b in bsel for j in range(b * B, min(b * B + B, t + 1))], dtype=np.int64)
+        want = np_topk(np_scores(q, w, K[cand]), cand, k)
+        idx, sc, blk, sblk, keff = orc.tree_query(q, w, K, t, B, G, W, m, k, mode=mode)
+        np.testing.assert_array_equal([u for u in sblk if u >= 0], ssel)
+        np.testing.assert_array_equal([b for b in blk if b >= 0], bsel)
+        np.testing.assert_array_equal(idx, want)
+
+
 # ---------------------------------------------------------------- the score
 
 @pytest.mark.parametrize("H,d", [(1, 2), (3, 8), (4, 64), (64, 128)])
