@@ -53,7 +53,8 @@
 extern "C" {
 #endif
 
-#define HISA_ABI_VERSION 3   /* 2: adds hisa_append_index; 3: adds the *_mode calls (max pooling) */
+#define HISA_ABI_VERSION 4   /* 2: adds hisa_append_index; 3: adds the *_mode calls (max pooling);
+                                4: adds the three-level tree calls hisa_tree_* */
 
 #if defined(__GNUC__)
 #define HISA_API __attribute__((visibility("default")))
@@ -199,6 +200,63 @@ HISA_API int hisa_append_index_mode(const uint16_t *K, int64_t k_seq_stride, int
                                     int S, int T, int H, int d, int B, int m, int k,
                                     int32_t *out_idx, float *out_score, int32_t *out_blk,
                                     void *ws, size_t ws_bytes, int pool_kind, void *stream);
+
+/*
+ * Three-level tree: super-blocks -> blocks -> tokens.  Page "Hierarchical
+ * Indexing Makes Sparse Attention Actually Fast", section "HISA's Approach:
+ * Hierarchical Summarization of the KV Cache", organises the summaries of the
+ * key cache as a tree searched top-down with a beam of W nodes per level, the
+ * tree kept current by refreshing only the nodes on the path from a new key up
+ * to the root.  Here the tree has three levels: blocks of B keys (the pool of
+ * hisa_pool_append) grouped into super-blocks of G consecutive blocks.
+ *
+ *   Super-block representative: the pooling of pool_kind (mean or max, as for
+ *   blocks) over its blocks' representatives, in block order, taken as rows:
+ *       mean_u = bf16_RNE( fp32_RNE( (sum_b pool_b in fp64, increasing b) / cnt_u ) )
+ *   over the blocks b in [u*G, min(u*G + G, ceil(L/B))).  For max pooling it
+ *   equals the max over the super-block's keys.
+ *
+ * hisa_tree_append -- hisa_pool_append_mode of rows [L_old, L_new) into the
+ *   block pool, then the same recomputation one level up: every super-block
+ *   holding a recomputed block is recomputed from the block pool.
+ *   spool_rep bf16 [S][*][d]: entry u of sequence s at spool_rep +
+ *             s*spool_seq_stride + u*d.  For S > 1, spool_seq_stride >=
+ *             ceil(ceil(L_new/B)/G)*d.
+ *   G in {1, 2, 4, ..., 256}.  Other arguments and checks as for
+ *   hisa_pool_append_mode.  Both pools are pure functions of K and L_new.
+ *
+ * hisa_tree_index -- per query (t, b_t = floor(t/B), u_t = floor(b_t/G)):
+ *     1. score every super-block u <= u_t; super-blocks u < u_t use the spool
+ *        entry, u_t uses the pooling of blocks u_t*G .. b_t-1 from the pool
+ *        followed by the query's own-block representative (rows b_t*B .. t);
+ *        keep the top min(W, u_t+1) by (score desc, u asc);
+ *     2. score the blocks b <= b_t of the kept super-blocks (pool entries,
+ *        and the own-block representative for b_t); keep the top m;
+ *     3. score the tokens j <= t of the kept blocks; keep the top k.
+ *   Scores, ranking and tie-break as in hisa_index.  With W >= u_t+1 the
+ *   result is hisa_index's; with G = 1 (a super-block is a block) it is
+ *   hisa_index's with m replaced by min(m, W).
+ *   pool_rep, spool_rep: current through row L-1 (hisa_tree_append with
+ *            L_new = L has completed).
+ *   out_idx, out_score, out_blk: as in hisa_index (out_blk lists the kept
+ *            blocks, at most min(m, number of blocks in step 2)).
+ *   out_sblk int32 [S][T][W] or NULL: kept super-blocks, ascending, -1 padded.
+ *   Supported: B, m, k, H, d, S*T as for hisa_index; G as above;
+ *   1 <= W <= 4096, W*G <= 2^20.
+ *   ws: at least hisa_tree_index_workspace(...) bytes, as for hisa_index.
+ */
+HISA_API int hisa_tree_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B, int G,
+                              int64_t L_old, int64_t L_new,
+                              uint16_t *pool_rep, int64_t pool_seq_stride,
+                              uint16_t *spool_rep, int64_t spool_seq_stride, int pool_kind, void *stream);
+HISA_API size_t hisa_tree_index_workspace(int S, int T, int H, int d, int64_t L, int B, int G, int W, int m, int k);
+HISA_API int hisa_tree_index(const uint16_t *q, const float *w, const int32_t *qpos,
+                             const uint16_t *K, int64_t k_seq_stride, int64_t L,
+                             const uint16_t *pool_rep, int64_t pool_seq_stride,
+                             const uint16_t *spool_rep, int64_t spool_seq_stride,
+                             int S, int T, int H, int d, int B, int G, int W, int m, int k,
+                             int32_t *out_idx, float *out_score, int32_t *out_blk, int32_t *out_sblk,
+                             void *ws, size_t ws_bytes, int pool_kind, void *stream);
 
 /* Bytes of device workspace dsa_flat_index needs for these sizes (0 on bad sizes). */
 HISA_API size_t dsa_flat_workspace(int S, int T, int H, int d, int64_t L, int k);

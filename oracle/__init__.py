@@ -10,11 +10,13 @@ from .oracle import (  # noqa: F401
     mean_rows,
     max_rows,
     pool,
+    super_pool,
     flat_query,
     refine_query,
     hisa_query,
     block_sparse_query,
     tree_query,
+    tree_super_scores,
     hisa_batch,
     flat_batch,
 )

@@ -289,37 +289,52 @@ int oracle_hisa_query(const uint16_t *q, const float *w, const uint16_t *K,
 /* ---------- three-level hierarchy: super-blocks -> blocks -> tokens [P1-Summary] ---------- */
 
 /* The summary page's tree read as three levels over the key cache: blocks of
- * B keys grouped into super-blocks of G blocks (G*B keys).  A node's
- * representative pools its keys like a block's (mode as rep_rows); a node
- * that holds the query position t is pooled over its keys up to t.  The
- * query keeps the W best super-blocks, then the m best of the blocks inside
- * them (blocks b <= floor(t/B)), then the k best tokens j <= t of those
- * blocks; every ranking is (score desc, id asc).
+ * B keys grouped into super-blocks of G blocks.  The page keeps the tree
+ * current by updating only the path from a new key's leaf to the root, so a
+ * node's summary is built from its children's: a block pools its keys, a
+ * super-block pools the representatives of its blocks (mode as rep_rows, the
+ * children in order).  A node that holds the query position t covers its
+ * children up to t: the own block pools its keys j <= t, the own super-block
+ * pools its complete blocks and then the own block's representative.
+ * The query keeps the W best super-blocks, then the m best of the blocks
+ * inside them (blocks b <= floor(t/B)), then the k best tokens j <= t of
+ * those blocks; every ranking is (score desc, id asc).
  *  out_sblk [W]: kept super-blocks, ascending, -1 padded (nullable).
  *  out_blk [m]: kept blocks, ascending, -1 padded.
+ *  out_sscore [floor(t/(B*G)) + 1]: score of every super-block (nullable).
  * Returns k_eff, or -1 on allocation failure. */
+
+/* representative of block b as the query at t sees it (own block: keys <= t) */
+static void block_rep_at(const uint16_t *K, int64_t b, int64_t t, int B, int d, int mode, uint16_t *out)
+{
+    int64_t bt = t / B;
+    rep_rows(K, b * B, b < bt ? (b + 1) * B : t + 1, d, mode, out);
+}
+
 int oracle_tree_query(const uint16_t *q, const float *w, const uint16_t *K, int H, int d, int64_t t,
                       int B, int G, int W, int m, int k, int mode, int32_t *out_idx, float *out_score,
-                      int32_t *out_blk, int32_t *out_sblk)
+                      int32_t *out_blk, int32_t *out_sblk, double *out_sscore)
 {
-    int64_t SB = (int64_t)G * B;     /* keys per super-block */
-    int64_t bt = t / B, st = t / SB;
+    int64_t bt = t / B, st = bt / G;
     int64_t ns = st + 1;             /* super-blocks visible to the query */
     uint16_t *rep = (uint16_t *)malloc((size_t)d * sizeof *rep);
+    uint16_t *kids = (uint16_t *)malloc((size_t)G * d * sizeof *kids);
     cand_t *sc = (cand_t *)malloc((size_t)ns * sizeof *sc);
     int32_t *ssel = (int32_t *)malloc((size_t)(W > 0 ? W : 1) * sizeof *ssel);
     cand_t *bc = (cand_t *)malloc(((size_t)(W > 0 ? W : 1) * G) * sizeof *bc);
     int32_t *sel = (int32_t *)malloc((size_t)(m > 0 ? m : 1) * sizeof *sel);
-    if (!rep || !sc || !ssel || !bc || !sel) {
-        free(rep); free(sc); free(ssel); free(bc); free(sel);
+    if (!rep || !kids || !sc || !ssel || !bc || !sel) {
+        free(rep); free(kids); free(sc); free(ssel); free(bc); free(sel);
         return -1;
     }
-    /* level 1: every super-block representative */
+    /* level 1: every super-block, pooled over its blocks' representatives */
     for (int64_t u = 0; u < ns; ++u) {
-        int64_t r1 = (u < st) ? (u + 1) * SB : t + 1;
-        rep_rows(K, u * SB, r1, d, mode, rep);
+        int64_t b1 = (u < st) ? (u + 1) * G : bt + 1;     /* children u*G .. b1-1 */
+        for (int64_t b = u * G; b < b1; ++b) block_rep_at(K, b, t, B, d, mode, kids + (size_t)(b - u * G) * d);
+        rep_rows(kids, 0, b1 - u * G, d, mode, rep);
         sc[u].s = oracle_score(q, w, rep, H, d);
         sc[u].i = u;
+        if (out_sscore) out_sscore[u] = sc[u].s;
     }
     qsort(sc, (size_t)ns, sizeof *sc, by_score_then_index);
     int weff = ns < W ? (int)ns : W;
@@ -331,8 +346,7 @@ int oracle_tree_query(const uint16_t *q, const float *w, const uint16_t *K, int 
     int64_t nc = 0;
     for (int i = 0; i < weff; ++i) {
         for (int64_t b = (int64_t)ssel[i] * G; b < (int64_t)(ssel[i] + 1) * G && b <= bt; ++b) {
-            int64_t r1 = (b < bt) ? (b + 1) * B : t + 1;
-            rep_rows(K, b * B, r1, d, mode, rep);
+            block_rep_at(K, b, t, B, d, mode, rep);
             bc[nc].s = oracle_score(q, w, rep, H, d);
             bc[nc].i = b;
             ++nc;
@@ -345,7 +359,7 @@ int oracle_tree_query(const uint16_t *q, const float *w, const uint16_t *K, int 
     for (int i = 0; i < m; ++i) out_blk[i] = i < meff ? sel[i] : -1;
     /* level 3: the original indexer on the tokens of the kept blocks */
     int keff = oracle_refine_query(q, w, K, H, d, t, B, sel, meff, k, out_idx, out_score, NULL);
-    free(rep); free(sc); free(ssel); free(bc); free(sel);
+    free(rep); free(kids); free(sc); free(ssel); free(bc); free(sel);
     return keff;
 }
 

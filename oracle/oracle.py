@@ -54,7 +54,7 @@ def load():
                                            _i32p, _f32p, _i32p, _f64p]
     lib.oracle_tree_query.restype = I
     lib.oracle_tree_query.argtypes = [_u16p, _f32p, _u16p, I, I, I64, I, I, I, I, I, I, _i32p, _f32p,
-                                      _i32p, _i32p]
+                                      _i32p, _i32p, _f64p]
     lib.oracle_block_sparse_query.restype = I
     lib.oracle_block_sparse_query.argtypes = [_u16p, _f32p, _u16p, I, I, I64, I, I, _i32p, _i32p]
     lib.oracle_hisa_batch.restype = I
@@ -127,6 +127,13 @@ def pool(K: np.ndarray, L: int, B: int, mode: str = "mean") -> np.ndarray:
     return out
 
 
+def super_pool(K: np.ndarray, L: int, B: int, G: int, mode: str = "mean") -> np.ndarray:
+    """Super-block representatives [S, ceil(ceil(L/B)/G), d] of the three-level tree: the block
+    representatives of pool(K, L, B, mode), pooled G at a time as rows (same mode)."""
+    blocks = pool(K, L, B, mode)
+    return pool(blocks, blocks.shape[1], G, mode)
+
+
 def flat_query(q, w, K, t: int, k: int, want_all=False):
     """Flat DSA top-k for one query: (idx [k], score [k], k_eff[, all fp64 scores [t+1]])."""
     q, w, K = _c(q, np.uint16), _c(w, np.float32), _c(K, np.uint16)
@@ -186,10 +193,25 @@ def tree_query(q, w, K, t: int, B: int, G: int, W: int, m: int, k: int, mode: st
     sblk = np.zeros(W, dtype=np.int32)
     keff = load().oracle_tree_query(_p(q, _u16p), _p(w, _f32p), _p(K, _u16p), H, d, t, B, G, W, m, k,
                                     _mode(mode), _p(idx, _i32p), _p(sc, _f32p), _p(blk, _i32p),
-                                    _p(sblk, _i32p))
+                                    _p(sblk, _i32p), None)
     if keff < 0:
         raise MemoryError("oracle_tree_query failed")
     return idx, sc, blk, sblk, keff
+
+
+def tree_super_scores(q, w, K, t: int, B: int, G: int, mode: str = "mean"):
+    """Scores (fp64) of every super-block u <= t // (B*G) as the three-level tree ranks them."""
+    q, w, K = _c(q, np.uint16), _c(w, np.float32), _c(K, np.uint16)
+    H, d = q.shape
+    idx, sc = np.zeros(1, dtype=np.int32), np.zeros(1, dtype=np.float32)
+    blk, sblk = np.zeros(1, dtype=np.int32), np.zeros(1, dtype=np.int32)
+    ssc = np.zeros(t // (B * G) + 1, dtype=np.float64)
+    keff = load().oracle_tree_query(_p(q, _u16p), _p(w, _f32p), _p(K, _u16p), H, d, t, B, G, 1, 1, 1,
+                                    _mode(mode), _p(idx, _i32p), _p(sc, _f32p), _p(blk, _i32p),
+                                    _p(sblk, _i32p), _p(ssc, _f64p))
+    if keff < 0:
+        raise MemoryError("oracle_tree_query failed")
+    return ssc
 
 
 def block_sparse_query(q, w, K, t: int, B: int, k: int):

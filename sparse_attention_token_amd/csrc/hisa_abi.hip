@@ -110,6 +110,49 @@ HisaLayout hisa_layout(int S, int T, int d, int64_t L, int B, int m, int k) {
     return l;
 }
 
+// three-level tree (hisa_tree_index)
+struct TreeLayout {
+    size_t own_rep, own_srep, sblk_keys, sel_sb, tblk_keys, sel_blk, cand_keys, total;
+    int64_t sblk_stride, tblk_stride, cand_stride;
+    StageBufs stage;
+};
+
+TreeLayout tree_layout(int S, int T, int d, int64_t L, int B, int G, int W, int m, int k) {
+    TreeLayout l{};
+    const int64_t nq = static_cast<int64_t>(S) * T;
+    const int64_t ns = ceil_div(ceil_div(L, B), G);
+    const int64_t ntb = std::min<int64_t>(W, ns) * G;          // blocks of the kept super-blocks
+    l.sblk_stride = static_cast<int64_t>(align_up(static_cast<size_t>(ns), 64));
+    l.tblk_stride = static_cast<int64_t>(align_up(static_cast<size_t>(ntb), 64));
+    l.cand_stride = static_cast<int64_t>(align_up(static_cast<size_t>(m) * B, 64));
+    const size_t rep = static_cast<size_t>(nq) * d * sizeof(uint16_t);
+    size_t off = 0;
+    l.own_rep = off;   off = align_up(off + rep, kAlign);
+    l.own_srep = off;  off = align_up(off + rep, kAlign);
+    l.sblk_keys = off; off = align_up(off + static_cast<size_t>(nq) * l.sblk_stride * sizeof(uint32_t), kAlign);
+    l.sel_sb = off;    off = align_up(off + static_cast<size_t>(nq) * W * sizeof(int32_t), kAlign);
+    l.tblk_keys = off; off = align_up(off + static_cast<size_t>(nq) * l.tblk_stride * sizeof(uint32_t), kAlign);
+    l.sel_blk = off;   off = align_up(off + static_cast<size_t>(nq) * m * sizeof(int32_t), kAlign);
+    l.cand_keys = off; off = align_up(off + static_cast<size_t>(nq) * l.cand_stride * sizeof(uint32_t), kAlign);
+    const int64_t len = std::max({select_stage_len(ns, W, B * G, false),
+                                  select_stage_len(ntb, m, G, true),
+                                  select_stage_len(static_cast<int64_t>(m) * B, k, B, true)});
+    off = carve_stage(off, nq, len, l.stage);
+    l.total = off + kAlign;
+    return l;
+}
+
+inline bool fanout_ok(int G) { return G >= 1 && G <= 256 && (G & (G - 1)) == 0; }
+
+int check_tree_params(int B, int G, int W, int m) {
+    const int st = check_hisa_params(B, m);
+    if (st != HISA_OK) return st;
+    if (G < 1 || W < 1) return HISA_ERR_ARG;
+    if (!fanout_ok(G)) return HISA_ERR_UNSUPPORTED;
+    if (W > kSelMaxM || static_cast<int64_t>(W) * G > (int64_t{1} << 20)) return HISA_ERR_UNSUPPORTED;
+    return HISA_OK;
+}
+
 struct FlatLayout {
     size_t keys, total;
     int64_t stride;
@@ -162,7 +205,7 @@ void prof_release() {
 const char *const kKindNames[kKindCount] = {
     "pool_append", "own_mean", "score_blocks", "select_blocks",
     "score_refine", "select_refine", "score_flat", "select_flat",
-    "index_decode", "bucket",
+    "index_decode", "bucket", "own_super", "score_tree", "select_tree",
 };
 
 }  // namespace
@@ -389,6 +432,125 @@ int hisa_append_index(const uint16_t *K, int64_t k_seq_stride, int64_t L_old, in
                       float *out_score, int32_t *out_blk, void *ws, size_t ws_bytes, void *stream) {
     return hisa_append_index_mode(K, k_seq_stride, L_old, L_new, pool_mean, pool_seq_stride, q, w, qpos, S, T, H, d,
                                   B, m, k, out_idx, out_score, out_blk, ws, ws_bytes, HISA_POOL_MEAN, stream);
+}
+
+int hisa_tree_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B, int G, int64_t L_old,
+                     int64_t L_new, uint16_t *pool_rep, int64_t pool_seq_stride, uint16_t *spool_rep,
+                     int64_t spool_seq_stride, int pool_kind, void *stream) {
+    if (pool_kind != HISA_POOL_MEAN && pool_kind != HISA_POOL_MAX) return HISA_ERR_ARG;
+    if (G < 1) return HISA_ERR_ARG;
+    if (!fanout_ok(G)) return HISA_ERR_UNSUPPORTED;
+    int st = check_append(K, k_seq_stride, S, d, B, L_old, L_new, pool_rep, pool_seq_stride);
+    if (st != HISA_OK) return st;
+    const int64_t nblk = ceil_div(L_new, B);
+    st = check_pool(spool_rep, spool_seq_stride, S, d, nblk, G);
+    if (st != HISA_OK) return st;
+    if (L_old == L_new) return HISA_OK;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool pmax = pool_kind == HISA_POOL_MAX;
+    // leaf level: the blocks holding the new rows
+    const int64_t blk0 = L_old / B;
+    st = hip_status(launch_pool_append(K, k_seq_stride, S, d, B, blk0, nblk - blk0, L_new, pmax, pool_rep,
+                                       pool_seq_stride, hs));
+    if (st != HISA_OK) return st;
+    // next level up: the super-blocks holding those blocks, pooled over the
+    // block representatives as rows (G of them per super-block)
+    const int64_t sb0 = blk0 / G;
+    return hip_status(launch_pool_append(pool_rep, pool_seq_stride, S, d, G, sb0, ceil_div(nblk, G) - sb0, nblk, pmax,
+                                         spool_rep, spool_seq_stride, hs));
+}
+
+size_t hisa_tree_index_workspace(int S, int T, int H, int d, int64_t L, int B, int G, int W, int m, int k) {
+    if (check_query_shape(S, T, H, d, L, k) != HISA_OK) return 0;
+    if (check_tree_params(B, G, W, m) != HISA_OK) return 0;
+    return tree_layout(S, T, d, L, B, G, W, m, k).total;
+}
+
+int hisa_tree_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
+                    int64_t k_seq_stride, int64_t L, const uint16_t *pool_rep, int64_t pool_seq_stride,
+                    const uint16_t *spool_rep, int64_t spool_seq_stride, int S, int T, int H, int d, int B, int G,
+                    int W, int m, int k, int32_t *out_idx, float *out_score, int32_t *out_blk, int32_t *out_sblk,
+                    void *ws, size_t ws_bytes, int pool_kind, void *stream) {
+    if (pool_kind != HISA_POOL_MEAN && pool_kind != HISA_POOL_MAX) return HISA_ERR_ARG;
+    int st = check_query_shape(S, T, H, d, L, k);
+    if (st != HISA_OK) return st;
+    st = check_tree_params(B, G, W, m);
+    if (st != HISA_OK) return st;
+    if (!q || !w || !out_idx || !aligned16(q)) return HISA_ERR_ARG;
+    if (!qpos && T > L) return HISA_ERR_ARG;
+    st = check_cache(K, k_seq_stride, S, d, L);
+    if (st != HISA_OK) return st;
+    st = check_pool(pool_rep, pool_seq_stride, S, d, L, B);
+    if (st != HISA_OK) return st;
+    st = check_pool(spool_rep, spool_seq_stride, S, d, ceil_div(L, B), G);
+    if (st != HISA_OK) return st;
+    if (!ws) return HISA_ERR_ARG;
+    const TreeLayout lay = tree_layout(S, T, d, L, B, G, W, m, k);
+    if (ws_bytes < lay.total) return HISA_ERR_WORKSPACE;
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool pmax = pool_kind == HISA_POOL_MAX;
+    char *base = align_ptr(ws);
+    uint16_t *own_rep = reinterpret_cast<uint16_t *>(base + lay.own_rep);
+    uint16_t *own_srep = reinterpret_cast<uint16_t *>(base + lay.own_srep);
+    uint32_t *sblk_keys = reinterpret_cast<uint32_t *>(base + lay.sblk_keys);
+    int32_t *sel_sb = reinterpret_cast<int32_t *>(base + lay.sel_sb);
+    uint32_t *tblk_keys = reinterpret_cast<uint32_t *>(base + lay.tblk_keys);
+    int32_t *sel_blk = reinterpret_cast<int32_t *>(base + lay.sel_blk);
+    uint32_t *cand_keys = reinterpret_cast<uint32_t *>(base + lay.cand_keys);
+    const int nq = S * T;
+    const int64_t ns = ceil_div(ceil_div(L, B), G);
+    const int64_t ntb = std::min<int64_t>(W, ns) * G;
+
+    // own block and own super-block representatives of every query
+    st = hip_status(launch_own_mean(K, k_seq_stride, qpos, L, S, T, d, B, pmax, own_rep, hs));
+    if (st != HISA_OK) return st;
+    st = hip_status(launch_own_super(pool_rep, pool_seq_stride, own_rep, qpos, L, S, T, d, B, G, pmax, own_srep, hs));
+    if (st != HISA_OK) return st;
+
+    ScoreArgs sa{};
+    sa.q = q; sa.w = w; sa.qpos = qpos;
+    sa.K = K; sa.k_seq_stride = k_seq_stride; sa.L = L;
+    sa.S = S; sa.T = T; sa.H = H; sa.d = d;
+    SelectArgs se{};
+    se.qpos = qpos; se.L = L; se.T = T;
+    set_stage(se, base, lay.stage);
+
+    // level 1: super-blocks are blocks of B*G keys with the super pool as
+    // their representatives; keep the top W
+    sa.pool = spool_rep; sa.pool_seq_stride = spool_seq_stride; sa.own_rep = own_srep;
+    sa.B = B * G; sa.m = 1;
+    sa.keys = sblk_keys; sa.keys_stride = lay.sblk_stride;
+    st = hip_status(launch_score(kScoreBlocks, sa, ns, hs));
+    if (st != HISA_OK) return st;
+    se.B = B * G; se.m = 1; se.kout = W;
+    se.keys = sblk_keys; se.keys_stride = lay.sblk_stride; se.sel_blk = nullptr;
+    se.out_id = sel_sb; se.out_score = nullptr; se.out_id_copy = out_sblk;
+    st = hip_status(launch_select(kScoreBlocks, se, nq, ns, hs));
+    if (st != HISA_OK) return st;
+
+    // level 2: the blocks of the kept super-blocks; keep the top m
+    sa.pool = pool_rep; sa.pool_seq_stride = pool_seq_stride; sa.own_rep = own_rep;
+    sa.B = B; sa.G = G; sa.W = W; sa.sel_sb = sel_sb;
+    sa.keys = tblk_keys; sa.keys_stride = lay.tblk_stride;
+    st = hip_status(launch_score(kScoreTreeBlocks, sa, ntb, hs));
+    if (st != HISA_OK) return st;
+    se.B = B; se.G = G; se.m = W; se.kout = m;
+    se.keys = tblk_keys; se.keys_stride = lay.tblk_stride; se.sel_blk = sel_sb;
+    se.out_id = sel_blk; se.out_score = nullptr; se.out_id_copy = out_blk;
+    st = hip_status(launch_select(kScoreTreeBlocks, se, nq, ntb, hs));
+    if (st != HISA_OK) return st;
+
+    // level 3: the tokens of the kept blocks (slots past the kept count hold
+    // -1 and give no candidate); keep the top k
+    sa.m = m; sa.sel_blk = sel_blk;
+    sa.keys = cand_keys; sa.keys_stride = lay.cand_stride;
+    st = hip_status(launch_score(kScoreRefine, sa, static_cast<int64_t>(m) * B, hs));
+    if (st != HISA_OK) return st;
+    se.B = B; se.m = m; se.kout = k;
+    se.keys = cand_keys; se.keys_stride = lay.cand_stride; se.sel_blk = sel_blk;
+    se.out_id = out_idx; se.out_score = out_score; se.out_id_copy = nullptr;
+    return hip_status(launch_select(kScoreRefine, se, nq, static_cast<int64_t>(m) * B, hs));
 }
 
 size_t dsa_flat_workspace(int S, int T, int H, int d, int64_t L, int k) {

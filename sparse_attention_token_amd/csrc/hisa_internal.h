@@ -48,7 +48,8 @@ __device__ __forceinline__ int64_t query_pos(const int32_t *qpos, int qi, int i,
 }
 
 // ---------------------------------------------------------------- launchers
-enum ScoreMode { kScoreBlocks = 0, kScoreRefine = 1, kScoreFlat = 2 };
+// kScoreTreeBlocks: the blocks inside a query's kept super-blocks (three-level tree)
+enum ScoreMode { kScoreBlocks = 0, kScoreRefine = 1, kScoreFlat = 2, kScoreTreeBlocks = 3 };
 
 struct ScoreArgs {
     const uint16_t *q;        // [S*T][H][d]
@@ -60,10 +61,12 @@ struct ScoreArgs {
     const uint16_t *pool;     // block means
     int64_t pool_seq_stride;
     const uint16_t *own_rep;  // [S*T][d] own-block partial means (blocks mode)
-    const int32_t *sel_blk;   // [S*T][m] kept blocks, ascending (refine mode)
+    const int32_t *sel_blk;   // [S*T][m] kept blocks, ascending, -1 padded (refine mode)
+    const int32_t *sel_sb;    // [S*T][W] kept super-blocks, ascending (tree-blocks mode)
     uint32_t *keys;           // out: [S*T][keys_stride]
     int64_t keys_stride;
     int S, T, H, d, B, m;
+    int G, W;                 // tree-blocks mode: blocks per super-block, kept super-blocks
 };
 
 struct SelectArgs {
@@ -72,8 +75,11 @@ struct SelectArgs {
     const int32_t *qpos;
     int64_t L;
     int T, B, m;
+    int G;                    // tree-blocks mode: blocks per super-block
     int kout;                 // entries per output row
-    const int32_t *sel_blk;   // refine mode: [S*T][m]
+    // refine mode: [S*T][m] kept blocks; tree-blocks mode: [S*T][m] kept
+    // super-blocks (m is then the super-block count W)
+    const int32_t *sel_blk;
     int32_t *out_id;          // [S*T][kout]
     float *out_score;         // [S*T][kout] or null
     int32_t *out_id_copy;     // [S*T][kout] or null (second copy of out_id)
@@ -159,6 +165,12 @@ hipError_t launch_own_mean(const uint16_t *K, int64_t k_seq_stride, const int32_
                            int64_t L, int S, int T, int d, int B, bool pool_max, uint16_t *own_rep,
                            hipStream_t st);
 
+// Own super-block representative of every query (three-level tree): pools the
+// block representatives pool[s][b] for st*G <= b < b_t, then own_rep[qi].
+hipError_t launch_own_super(const uint16_t *pool, int64_t pool_seq_stride, const uint16_t *own_rep,
+                            const int32_t *qpos, int64_t L, int S, int T, int d, int B, int G, bool pool_max,
+                            uint16_t *own_srep, hipStream_t st);
+
 hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int64_t max_pos, hipStream_t st);
 
 // max_n: an upper bound on the candidate count of every query (sizes the per-thread chunk)
@@ -176,6 +188,9 @@ enum KernelKind {
     kKindSelectFlat,
     kKindIndexDecode,      // block stage + top-m + refinement in one launch
     kKindBucket,           // (query, slot) pairs grouped by kept block
+    kKindOwnSuper,         // own super-block representatives (tree)
+    kKindScoreTree,        // blocks inside the kept super-blocks (tree)
+    kKindSelectTree,
     kKindCount
 };
 

@@ -200,7 +200,48 @@ __global__ __launch_bounds__(kMaxD) void own_prefix_mean_kernel(
     }
 }
 
+// grid: (S*T), d threads.  Own super-block representative of the three-level
+// tree: a super-block pools the representatives of its G blocks in block
+// order, and the one holding t covers its blocks up to b_t, the last of them
+// being the query's own-block representative own_rep[qi].
+template <bool MAX>
+__global__ __launch_bounds__(kMaxD) void own_super_kernel(
+        const uint16_t *__restrict__ pool, int64_t pool_seq_stride, const uint16_t *__restrict__ own_rep,
+        const int32_t *__restrict__ qpos, int64_t L, int T, int d, int B, int G,
+        uint16_t *__restrict__ own_srep) {
+    const int qi = blockIdx.x;
+    const int s = qi / T;
+    const int64_t t = query_pos(qpos, qi, qi - s * T, L, T);
+    const int col = threadIdx.x;
+    if (t < 0 || col >= d) return;
+    const int64_t bt = t / B;
+    const int64_t b0 = bt / G * G;
+    const uint16_t *src = pool + s * pool_seq_stride + col;
+    ColumnRep<MAX> acc;
+    int64_t b = b0;
+    for (; b + 8 <= bt; b += 8) {                      // 8 loads in flight, added in block order
+        uint16_t x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = src[(b + j) * d];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc.add(x[j]);
+    }
+    for (; b < bt; ++b) acc.add(src[b * d]);
+    acc.add(own_rep[static_cast<int64_t>(qi) * d + col]);
+    own_srep[static_cast<int64_t>(qi) * d + col] = acc.get(bt - b0 + 1);
+}
+
 }  // namespace
+
+hipError_t launch_own_super(const uint16_t *pool, int64_t pool_seq_stride, const uint16_t *own_rep,
+                            const int32_t *qpos, int64_t L, int S, int T, int d, int B, int G, bool pool_max,
+                            uint16_t *own_srep, hipStream_t st) {
+    if (pool_max)
+        return launch(kKindOwnSuper, own_super_kernel<true>, dim3(S * T), dim3(kMaxD), 0, st, pool, pool_seq_stride,
+                      own_rep, qpos, L, T, d, B, G, own_srep);
+    return launch(kKindOwnSuper, own_super_kernel<false>, dim3(S * T), dim3(kMaxD), 0, st, pool, pool_seq_stride,
+                  own_rep, qpos, L, T, d, B, G, own_srep);
+}
 
 hipError_t launch_own_prefix_mean(const uint16_t *K, int64_t k_seq_stride, int64_t L, int S, int T, int d, int B,
                                   bool pool_max, uint16_t *own_rep, hipStream_t st) {

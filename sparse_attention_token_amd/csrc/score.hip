@@ -33,8 +33,13 @@
 //   blocks: p = block id <= b_t; row = pool mean p for p < b_t, and the
 //           query's own-block mean (rows b_t*B .. t, recomputed from K) for p = b_t
 //   refine: p = slot*B + r over the kept blocks (ascending); row = key
-//           sel[slot]*B + r if that token is <= t, else no candidate
+//           sel[slot]*B + r if that slot holds a block and the token is <= t,
+//           else no candidate
 //   flat:   p = token id <= t; row = key p
+//   tree blocks (three-level tree, super-blocks of G blocks): p = slot*G + c
+//           over the kept super-blocks u = sel_sb[slot]; block b = u*G + c;
+//           row = pool mean b for b < b_t, the own-block mean for b = b_t,
+//           no candidate for b > b_t
 // Output is an order-preserving uint32 key per position (0 = no candidate).
 
 #include "hisa_internal.h"
@@ -63,6 +68,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     } else if (MODE == kScoreRefine) {
         const int64_t meff = (a.m < bt + 1) ? a.m : bt + 1;
         npos = meff * a.B;
+    } else if (MODE == kScoreTreeBlocks) {
+        const int64_t ns = bt / a.G + 1;                  // super-blocks visible to the query
+        npos = (a.W < ns ? a.W : ns) * a.G;
     } else {
         npos = t + 1;
     }
@@ -90,8 +98,15 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
             } else if (MODE == kScoreRefine) {
                 const int64_t slot = p / a.B;
                 const int64_t r = p - slot * a.B;
-                const int64_t tok = static_cast<int64_t>(a.sel_blk[static_cast<int64_t>(qi) * a.m + slot]) * a.B + r;
-                if (tok <= t) row = a.K + s * a.k_seq_stride + tok * D;
+                const int32_t blk = a.sel_blk[static_cast<int64_t>(qi) * a.m + slot];
+                const int64_t tok = static_cast<int64_t>(blk) * a.B + r;
+                if (blk >= 0 && tok <= t) row = a.K + s * a.k_seq_stride + tok * D;
+            } else if (MODE == kScoreTreeBlocks) {
+                const int64_t slot = p / a.G;
+                const int64_t b = static_cast<int64_t>(a.sel_sb[static_cast<int64_t>(qi) * a.W + slot]) * a.G +
+                                  (p - slot * a.G);
+                if (b < bt) row = a.pool + s * a.pool_seq_stride + b * D;
+                else if (b == bt) row = a.own_rep + static_cast<int64_t>(qi) * D;
             } else {
                 row = a.K + s * a.k_seq_stride + p * D;
             }
@@ -202,9 +217,11 @@ hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int64_t max_pos, hip
     const dim3 grid(static_cast<uint32_t>((max_pos + kTileRows - 1) / kTileRows),
                     static_cast<uint32_t>(a.S * a.T));
     const KernelKind kind = mode == kScoreBlocks ? kKindScoreBlocks
-                          : mode == kScoreRefine ? kKindScoreRefine : kKindScoreFlat;
+                          : mode == kScoreRefine ? kKindScoreRefine
+                          : mode == kScoreTreeBlocks ? kKindScoreTree : kKindScoreFlat;
     if (mode == kScoreBlocks) return launch_mode<kScoreBlocks>(kind, a, grid, st);
     if (mode == kScoreRefine) return launch_mode<kScoreRefine>(kind, a, grid, st);
+    if (mode == kScoreTreeBlocks) return launch_mode<kScoreTreeBlocks>(kind, a, grid, st);
     // flat: about 512 workgroups of 128..4096 rows each
     const int64_t nq = static_cast<int64_t>(a.S) * a.T;
     int64_t rows = (max_pos * nq / 512 + kTileRows - 1) / kTileRows * kTileRows;

@@ -7,6 +7,9 @@
 // of them use one rule: rank by (score desc, index asc), keep
 // min(k, #candidates), pad with -1.  Scores arrive as order-preserving uint32
 // keys (0 = no candidate), laid out by increasing candidate index.
+// The three-level tree adds one more such step: the top m blocks among those
+// of its kept super-blocks (tree-blocks mode, ids mapped like refine mode's
+// with the super-block table and G blocks per slot).
 //
 // One workgroup (1024 threads) selects over up to 32768 positions of one
 // query: thread t holds positions [t*R, t*R + R) in registers and
@@ -37,7 +40,20 @@ __device__ __forceinline__ int64_t row_length(const SelectArgs &a, int qi) {
     const int64_t bt = t / a.B;
     if (MODE == kScoreBlocks) return bt + 1;
     if (MODE == kScoreRefine) return ((a.m < bt + 1) ? a.m : bt + 1) * a.B;
+    if (MODE == kScoreTreeBlocks) {
+        const int64_t ns = bt / a.G + 1;
+        return (a.m < ns ? a.m : ns) * a.G;
+    }
     return t + 1;
+}
+
+// Modes whose positions are slot*grp + r over a table of kept parents.
+template <int MODE>
+constexpr bool kMapped = MODE == kScoreRefine || MODE == kScoreTreeBlocks;
+
+template <int MODE>
+__device__ __forceinline__ int group_size(const SelectArgs &a) {
+    return MODE == kScoreTreeBlocks ? a.G : a.B;
 }
 
 // Store to element `op` of a row through a 32-bit byte offset (op < 2^30
@@ -80,27 +96,28 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     int32_t *out2 = a.out_id_copy ? a.out_id_copy + static_cast<int64_t>(qi) * a.kout : nullptr;
     uint32_t kv[R];
     load_run<R>(a.keys + static_cast<int64_t>(qi) * a.keys_stride, static_cast<int64_t>(tid) * R, n, kv);
-    if (MODE == kScoreRefine) {
-        const int meff = static_cast<int>(n / a.B);
+    const int grp = group_size<MODE>(a);
+    if (kMapped<MODE>) {
+        const int meff = static_cast<int>(n / grp);
         for (int j = tid; j < meff; j += NT) s_sel[j] = a.sel_blk[static_cast<int64_t>(qi) * a.m + j];
         // block_radix_select starts with a barrier, which also publishes s_sel
     }
     const SelectResult res = block_radix_select<NT, R>(kv, static_cast<uint32_t>(a.kout), sc);
     if (res.keff > 0) {
-        // refine mode: R and B are powers of two, so with R <= B the thread's
-        // R positions lie in one kept block and one lookup serves them all;
-        // with R > B (B = 16, long rows) each position looks up its block
-        const bool per_pos = MODE == kScoreRefine && R > a.B;
+        // mapped modes: R and the group size are powers of two, so with
+        // R <= grp the thread's R positions lie in one slot and one lookup
+        // serves them all; with R > grp each position looks up its slot
+        const bool per_pos = kMapped<MODE> && R > grp;
         int32_t id0 = tid * R;
-        if (MODE == kScoreRefine && !per_pos && id0 < n) {
-            const int slot = id0 / a.B;
-            id0 = s_sel[slot] * a.B + (id0 - slot * a.B);
+        if (kMapped<MODE> && !per_pos && id0 < n) {
+            const int slot = id0 / grp;
+            id0 = s_sel[slot] * grp + (id0 - slot * grp);
         }
         block_compact<NT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
             int32_t id = id0 + r;
             if (per_pos) {
-                const int slot = id / a.B;
-                id = s_sel[slot] * a.B + (id - slot * a.B);
+                const int slot = id / grp;
+                id = s_sel[slot] * grp + (id - slot * grp);
             }
             put(out, op, id);
             if (osc) put(osc, op, key_to_score(key));
@@ -138,16 +155,17 @@ __global__ __launch_bounds__(kNT) void select_chunk_kernel(SelectArgs a, const u
     const SelectResult res = block_radix_select<kNT, R>(kv, static_cast<uint32_t>(a.kout), sc);
     if (res.keff > 0) {
         const int32_t *irow = ids_in ? ids_in + static_cast<int64_t>(qi) * in_stride + c0 : nullptr;
-        // position ids in refine mode: with R <= B (both powers of two;
-        // chunks start on block bounds) the thread's R positions lie in one
-        // kept block; with B < R each position looks up its block
+        // position ids in the mapped modes: with R <= grp (both powers of
+        // two; chunks start on slot bounds) the thread's R positions lie in
+        // one slot; with grp < R each position looks up its slot
+        const int grp = group_size<MODE>(a);
         const int64_t p0 = c0 + static_cast<int64_t>(tid) * R;
         const int32_t *sb = a.sel_blk + static_cast<int64_t>(qi) * a.m;
-        const bool per_pos = !irow && MODE == kScoreRefine && R > a.B;
+        const bool per_pos = !irow && kMapped<MODE> && R > grp;
         int32_t id0 = static_cast<int32_t>(p0);
-        if (!irow && MODE == kScoreRefine && !per_pos && p0 < n_row) {
-            const int64_t slot = p0 / a.B;
-            id0 = static_cast<int32_t>(static_cast<int64_t>(sb[slot]) * a.B + (p0 - slot * a.B));
+        if (!irow && kMapped<MODE> && !per_pos && p0 < n_row) {
+            const int64_t slot = p0 / grp;
+            id0 = static_cast<int32_t>(static_cast<int64_t>(sb[slot]) * grp + (p0 - slot * grp));
         }
         block_compact<kNT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
             int32_t id;
@@ -155,8 +173,8 @@ __global__ __launch_bounds__(kNT) void select_chunk_kernel(SelectArgs a, const u
                 id = irow[static_cast<int64_t>(tid) * R + r];
             } else if (per_pos) {
                 const int64_t pos = p0 + r;
-                const int64_t slot = pos / a.B;
-                id = static_cast<int32_t>(static_cast<int64_t>(sb[slot]) * a.B + (pos - slot * a.B));
+                const int64_t slot = pos / grp;
+                id = static_cast<int32_t>(static_cast<int64_t>(sb[slot]) * grp + (pos - slot * grp));
             } else {
                 id = id0 + r;
             }
@@ -260,14 +278,18 @@ int64_t select_stage_len(int64_t max_n, int kout, int B, bool refine) {
 
 hipError_t launch_select(ScoreMode mode, const SelectArgs &a, int nq, int64_t max_n, hipStream_t st) {
     const KernelKind kind = mode == kScoreBlocks ? kKindSelectBlocks
-                          : mode == kScoreRefine ? kKindSelectRefine : kKindSelectFlat;
-    if (select_stage_len(max_n, a.kout, a.B, mode == kScoreRefine) > 0) {
+                          : mode == kScoreRefine ? kKindSelectRefine
+                          : mode == kScoreTreeBlocks ? kKindSelectTree : kKindSelectFlat;
+    const bool tree = mode == kScoreTreeBlocks;
+    if (select_stage_len(max_n, a.kout, tree ? a.G : a.B, mode == kScoreRefine || tree) > 0) {
         if (mode == kScoreBlocks) return launch_chunked<kScoreBlocks>(kind, a, nq, max_n, st);
         if (mode == kScoreRefine) return launch_chunked<kScoreRefine>(kind, a, nq, max_n, st);
+        if (tree) return launch_chunked<kScoreTreeBlocks>(kind, a, nq, max_n, st);
         return launch_chunked<kScoreFlat>(kind, a, nq, max_n, st);
     }
     if (mode == kScoreBlocks) return launch_single<kScoreBlocks>(kind, a, nq, max_n, st);
     if (mode == kScoreRefine) return launch_single<kScoreRefine>(kind, a, nq, max_n, st);
+    if (tree) return launch_single<kScoreTreeBlocks>(kind, a, nq, max_n, st);
     return launch_single<kScoreFlat>(kind, a, nq, max_n, st);
 }
 

@@ -66,6 +66,13 @@ def lib():
     L.hisa_append_index.restype = i32
     L.hisa_append_index.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                     i32, vp, vp, vp, vp, sz, vp]
+    L.hisa_tree_append.restype = i32
+    L.hisa_tree_append.argtypes = [vp, i64, i32, i32, i32, i32, i64, i64, vp, i64, vp, i64, i32, vp]
+    L.hisa_tree_index_workspace.restype = sz
+    L.hisa_tree_index_workspace.argtypes = [i32, i32, i32, i32, i64, i32, i32, i32, i32, i32]
+    L.hisa_tree_index.restype = i32
+    L.hisa_tree_index.argtypes = [vp, vp, vp, vp, i64, i64, vp, i64, vp, i64, i32, i32, i32, i32, i32, i32,
+                                  i32, i32, i32, vp, vp, vp, vp, vp, sz, i32, vp]
     L.dsa_flat_workspace.restype = sz
     L.dsa_flat_workspace.argtypes = [i32, i32, i32, i32, i64, i32]
     L.dsa_flat_index.restype = i32
@@ -244,6 +251,70 @@ def hisa_append_index(K, pool_mean, L_old: int, L_new: int, q, w, B: int, m: int
                                       _stream(dev))
     _check("hisa_append_index", st)
     return out_idx, out_score, out_blk
+
+
+def hisa_tree_append(K, pool_rep, spool_rep, L_old: int, L_new: int, B: int, G: int, pool: str = "mean"):
+    """Fold key rows [L_old, L_new) of K [S, L_cap, d] into the block pool [S, nblk_cap, d] and the
+    super-block pool [S, nsblk_cap, d] (super-blocks of G blocks), in place."""
+    _bf16(K, "K")
+    _bf16(pool_rep, "pool_rep")
+    _bf16(spool_rep, "spool_rep")
+    S, _, d = K.shape
+    kss = _rows(K, "K", d)
+    pss = _rows(pool_rep, "pool_rep", d)
+    sss = _rows(spool_rep, "spool_rep", d)
+    if pool_rep.shape[0] != S or spool_rep.shape[0] != S:
+        raise ValueError("pool_rep, spool_rep and K disagree on S")
+    nblk = -(-int(L_new) // B)
+    if K.shape[1] < L_new or pool_rep.shape[1] < nblk or spool_rep.shape[1] * G < nblk:
+        raise ValueError("K, pool_rep or spool_rep too short for L_new")
+    st = lib().hisa_tree_append(_ptr(K), kss, S, d, B, G, int(L_old), int(L_new), _ptr(pool_rep), pss,
+                                _ptr(spool_rep), sss, _pool_kind(pool), _stream(K.device))
+    _check("hisa_tree_append", st)
+    return pool_rep, spool_rep
+
+
+def hisa_tree_index_workspace(S, T, H, d, L, B, G, W, m, k) -> int:
+    return int(lib().hisa_tree_index_workspace(S, T, H, d, L, B, G, W, m, k))
+
+
+def hisa_tree_index(q, w, K, L: int, pool_rep, spool_rep, B: int, G: int, W: int, m: int, k: int, qpos=None, *,
+                    want_scores: bool = True, want_blocks: bool = False, want_super: bool = False,
+                    out_idx=None, out_score=None, out_blk=None, out_sblk=None, workspace=None,
+                    pool: str = "mean"):
+    """Three-level indexer (super-blocks of G blocks, beam W, then m blocks, then k tokens).
+    Returns (idx [S,T,k], score [S,T,k] | None, blocks [S,T,m] | None, super-blocks [S,T,W] | None)."""
+    S, T, H, d, kss = _query_args(q, w, qpos, K, L)
+    _bf16(pool_rep, "pool_rep")
+    _bf16(spool_rep, "spool_rep")
+    pss = _rows(pool_rep, "pool_rep", d)
+    sss = _rows(spool_rep, "spool_rep", d)
+    nblk = -(-int(L) // B)
+    if pool_rep.shape[0] != S or pool_rep.shape[1] < nblk:
+        raise ValueError("pool_rep must be [S, >= ceil(L/B), d]")
+    if spool_rep.shape[0] != S or spool_rep.shape[1] * G < nblk:
+        raise ValueError("spool_rep must be [S, >= ceil(ceil(L/B)/G), d]")
+    dev = q.device
+    if out_idx is None:
+        out_idx = torch.empty((S, T, k), dtype=torch.int32, device=dev)
+    if want_scores and out_score is None:
+        out_score = torch.empty((S, T, k), dtype=torch.float32, device=dev)
+    if want_blocks and out_blk is None:
+        out_blk = torch.empty((S, T, m), dtype=torch.int32, device=dev)
+    if want_super and out_sblk is None:
+        out_sblk = torch.empty((S, T, W), dtype=torch.int32, device=dev)
+    nbytes = hisa_tree_index_workspace(S, T, H, d, L, B, G, W, m, k)
+    if nbytes == 0:
+        _check("hisa_tree_index", lib().hisa_tree_index(None, None, None, None, 0, int(L), None, 0, None, 0, S, T,
+                                                        H, d, B, G, W, m, k, None, None, None, None, None, 0,
+                                                        _pool_kind(pool), None))
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().hisa_tree_index(_ptr(q), _ptr(w), _ptr(qpos), _ptr(K), kss, int(L), _ptr(pool_rep), pss,
+                               _ptr(spool_rep), sss, S, T, H, d, B, G, W, m, k, _ptr(out_idx), _ptr(out_score),
+                               _ptr(out_blk), _ptr(out_sblk), _ptr(ws), ws.numel() * ws.element_size(),
+                               _pool_kind(pool), _stream(dev))
+    _check("hisa_tree_index", st)
+    return out_idx, out_score, out_blk, out_sblk
 
 
 def dsa_flat_index(q, w, K, L: int, k: int, qpos=None, *, want_scores: bool = True,

@@ -86,7 +86,17 @@ def check_hisa_row(orc, case, s, i, g_idx, g_score, g_blk, report=None, pool="me
     for b in diff:
         assert abs(o_bsc[b] - c_m) <= tol(c_m), f"block {b} differs (score {o_bsc[b]} vs cutoff {c_m})"
 
-    # -- tokens, against the conditional oracle on the GPU's blocks
+    tdiff = _check_tokens(orc, q, w, K, t, B, k, gb, g_idx, g_score)
+    if report is not None:
+        report.setdefault("block_diffs", 0)
+        report.setdefault("token_diffs", 0)
+        report["block_diffs"] += len(diff)
+        report["token_diffs"] += len(tdiff)
+    return o_idx, o_keff
+
+
+def _check_tokens(orc, q, w, K, t, B, k, gb, g_idx, g_score):
+    """Token rule against the conditional oracle on the GPU's kept blocks gb; returns the differing ids."""
     c_idx, c_sc, c_keff, nC = orc.refine_query(q, w, K, t, B, gb, k)
     g_idx = np.asarray(g_idx)
     assert np.all(g_idx[c_keff:] == -1), "token padding"
@@ -108,11 +118,69 @@ def check_hisa_row(orc, case, s, i, g_idx, g_score, g_blk, report=None, pool="me
         for pos, j in enumerate(gt.tolist()):
             sj = ref[j] if j in ref else orc.score(q, w, K[j])
             assert abs(g_score[pos] - sj) <= tol(sj), f"score of token {j}: {g_score[pos]} vs {sj}"
+    return tdiff
+
+
+def build_tree_pools(hisa, K, L, B, G, L_bulk=None, step=1, pool="mean"):
+    """Block and super-block pools for rows [0, L) through hisa_tree_append: one bulk append of
+    [0, L_bulk), then appends of `step` rows."""
+    import torch
+
+    S, _, d = K.shape
+    nblk = -(-L // B)
+    reps = torch.zeros((S, nblk, d), dtype=torch.bfloat16, device=K.device)
+    sreps = torch.zeros((S, -(-nblk // G), d), dtype=torch.bfloat16, device=K.device)
+    L_bulk = L if L_bulk is None else L_bulk
+    hisa.hisa_tree_append(K, reps, sreps, 0, L_bulk, B, G, pool=pool)
+    x = L_bulk
+    while x < L:
+        y = min(L, x + step)
+        hisa.hisa_tree_append(K, reps, sreps, x, y, B, G, pool=pool)
+        x = y
+    return reps, sreps
+
+
+def check_tree_row(orc, case, s, i, G, W, g_idx, g_score, g_blk, g_sblk, report=None, pool="mean"):
+    """Comparison rule for one row of hisa_tree_index, level by level: the GPU's super-blocks
+    against the oracle's (differences only at the W-th cutoff), its blocks against the top m of
+    the blocks inside the GPU's super-blocks, its tokens against the refinement of its blocks."""
+    q, w, K = case.q[s, i], case.w[s, i], case.K[s]
+    t = int(case.qpos[s, i])
+    B, m, k = case.B, case.m, case.k
+    bt = t // B
+    ns = bt // G + 1
+    weff = min(W, ns)
+    o_idx, o_sc, o_blk, o_sblk, o_keff = orc.tree_query(q, w, K, t, B, G, W, m, k, mode=pool)
+    ssc = orc.tree_super_scores(q, w, K, t, B, G, mode=pool)
+
+    # -- super-blocks
+    g_sblk = np.asarray(g_sblk)
+    assert np.all(g_sblk[weff:] == -1), "super-block padding"
+    gs = g_sblk[:weff]
+    assert np.all(gs >= 0) and np.all(np.diff(gs) > 0) and gs[-1] < ns
+    c_w = _kth(np.sort(ssc)[::-1], weff)
+    sdiff = set(gs.tolist()) ^ set(o_sblk[:weff].tolist())
+    for u in sdiff:
+        assert abs(ssc[u] - c_w) <= tol(c_w), f"super-block {u} differs (score {ssc[u]} vs cutoff {c_w})"
+
+    # -- blocks, against the top m of the blocks inside the GPU's super-blocks
+    bsc = orc.hisa_query(q, w, K, t, B, 1, 1, mode=pool)[3]
+    cand = [b for u in gs.tolist() for b in range(u * G, min(u * G + G, bt + 1))]
+    meff = min(m, len(cand))
+    ranked = sorted(cand, key=lambda b: (-bsc[b], b))
+    g_blk = np.asarray(g_blk)
+    assert np.all(g_blk[meff:] == -1), "block padding"
+    gb = g_blk[:meff]
+    assert np.all(np.diff(gb) > 0) and np.all(np.isin(gb, cand)), "blocks must come from kept super-blocks"
+    c_m = bsc[ranked[meff - 1]]
+    bdiff = set(gb.tolist()) ^ set(ranked[:meff])
+    for b in bdiff:
+        assert abs(bsc[b] - c_m) <= tol(c_m), f"block {b} differs (score {bsc[b]} vs cutoff {c_m})"
+
+    tdiff = _check_tokens(orc, q, w, K, t, B, k, gb, g_idx, g_score)
     if report is not None:
-        report.setdefault("block_diffs", 0)
-        report.setdefault("token_diffs", 0)
-        report["block_diffs"] += len(diff)
-        report["token_diffs"] += len(tdiff)
+        for key, n in (("super_diffs", len(sdiff)), ("block_diffs", len(bdiff)), ("token_diffs", len(tdiff))):
+            report[key] = report.get(key, 0) + n
     return o_idx, o_keff
 
 

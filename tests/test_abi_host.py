@@ -44,7 +44,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("hisa_pool_append", "hisa_index", "hisa_append_index", "dsa_flat_index",
               "hisa_pool_append_mode", "hisa_index_mode", "hisa_append_index_mode",
-              "hisa_index_workspace", "dsa_flat_workspace", "hisa_status_string", "hisa_abi_version"):
+              "hisa_index_workspace", "dsa_flat_workspace", "hisa_status_string", "hisa_abi_version",
+              "hisa_tree_append", "hisa_tree_index", "hisa_tree_index_workspace"):
         assert n in names
 
 
@@ -54,7 +55,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hisa_abi_version() == 3
+    assert lib.hisa_abi_version() == 4
     for code in (OK, ARG, UNSUP, WS, HIP, 12345):
         assert isinstance(lib.hisa_status_string(code), bytes)
     assert lib.hisa_status_string(WS) != lib.hisa_status_string(ARG)
@@ -76,6 +77,22 @@ def test_workspace_sizes(lib):
                 (1, 1, 64, 128, 100, 64, 0, 8), (1, 1, 64, 128, 100, 64, 4, 0),
                 (1, 1, 64, 128, 1 << 31, 64, 4, 8), (1, 1, 64, 128, 100, 256, 8192, 8)]:
         assert lib.hisa_index_workspace(*bad) == 0, bad
+
+
+def test_tree_workspace_sizes(lib):
+    # 1M keys, B=128 -> 8192 blocks, G=64 -> 128 super-blocks; W=8 -> 512 blocks scored at level 2
+    a = lib.hisa_tree_index_workspace(8, 1, 64, 128, 1 << 20, 128, 64, 8, 64, 2048)
+    need = 8 * (2 * 128 * 2 + 128 * 4 + 8 * 4 + 512 * 4 + 64 * 4 + 64 * 128 * 4)
+    assert need <= a < 2 * need + 8192
+    assert lib.hisa_tree_index_workspace(8, 1, 64, 128, 1 << 20, 128, 1, 8, 64, 2048) > 0
+    for bad in [(1, 1, 64, 128, 1000, 64, 3, 4, 4, 8),       # G not a power of two
+                (1, 1, 64, 128, 1000, 64, 512, 4, 4, 8),     # G > 256
+                (1, 1, 64, 128, 1000, 64, 0, 4, 4, 8),
+                (1, 1, 64, 128, 1000, 64, 4, 0, 4, 8),       # W = 0
+                (1, 1, 64, 128, 1000, 64, 4, 4097, 4, 8),    # W > 4096
+                (1, 1, 64, 128, 1000, 48, 4, 4, 4, 8),       # B unsupported
+                (1, 1, 64, 128, 1000, 64, 4, 4, 0, 8)]:
+        assert lib.hisa_tree_index_workspace(*bad) == 0, bad
 
 
 def test_argument_checks_with_null_pointers(lib):
@@ -108,6 +125,16 @@ def test_argument_checks_with_null_pointers(lib):
                                None, None, None, None, 0, 1, None) == UNSUP
     assert lib.hisa_append_index_mode(None, 0, 0, 10, None, 0, None, None, None, 1, 1, 4, 64, 64, 2, 8,
                                       None, None, None, None, 0, 2, None) == ARG
+    # the tree calls
+    assert lib.hisa_tree_append(None, 0, 1, 64, 64, 4, 0, 10, None, 0, None, 0, 0, None) == ARG
+    assert lib.hisa_tree_append(None, 0, 1, 64, 64, 3, 0, 10, None, 0, None, 0, 0, None) == UNSUP
+    assert lib.hisa_tree_append(None, 0, 1, 64, 64, 4, 0, 10, None, 0, None, 0, 5, None) == ARG
+    assert lib.hisa_tree_index(None, None, None, None, 0, 100, None, 0, None, 0, 1, 1, 4, 64, 64, 4, 2, 2, 8,
+                               None, None, None, None, None, 0, 0, None) == ARG
+    assert lib.hisa_tree_index(None, None, None, None, 0, 100, None, 0, None, 0, 1, 1, 4, 64, 64, 6, 2, 2, 8,
+                               None, None, None, None, None, 0, 0, None) == UNSUP
+    assert lib.hisa_tree_index(None, None, None, None, 0, 100, None, 0, None, 0, 1, 1, 4, 64, 64, 4, 0, 2, 8,
+                               None, None, None, None, None, 0, 0, None) == ARG
     # profiler argument checks
     ms, n = C.c_double(), C.c_int()
     assert lib.hisa_profile_read(-1, C.byref(ms), C.byref(n)) == ARG
@@ -167,3 +194,48 @@ def test_argument_checks_with_placeholder_pointers(lib):
     assert app(B=24) == UNSUP
     assert app(q=odd) == ARG
     assert app(T=L + 1) == ARG
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="placeholder-pointer checks run only where no GPU is visible")
+def test_tree_argument_checks_with_placeholder_pointers(lib):
+    buf = (C.c_uint8 * 4096)()
+    base = (C.addressof(buf) + 255) // 256 * 256
+    p = C.c_void_p(base)
+    odd = C.c_void_p(base + 2)
+    S, T, H, d, L, B, G, W, m, k = 2, 1, 4, 64, 1000, 64, 4, 2, 4, 16
+    need = lib.hisa_tree_index_workspace(S, T, H, d, L, B, G, W, m, k)
+    kss, pss, sss = L * d, 16 * d, 4 * d
+
+    def idx(**kw):
+        a = dict(q=p, w=p, qpos=None, K=p, kss=kss, L=L, pool=p, pss=pss, spool=p, sss=sss, S=S, T=T, H=H, d=d,
+                 B=B, G=G, W=W, m=m, k=k, out=p, ws=p, wsb=need, kind=0)
+        a.update(kw)
+        return lib.hisa_tree_index(a["q"], a["w"], a["qpos"], a["K"], a["kss"], a["L"], a["pool"], a["pss"],
+                                   a["spool"], a["sss"], a["S"], a["T"], a["H"], a["d"], a["B"], a["G"], a["W"],
+                                   a["m"], a["k"], a["out"], None, None, None, a["ws"], a["wsb"], a["kind"], None)
+
+    assert idx(wsb=need - 1) == WS
+    assert idx(ws=None) == ARG
+    assert idx(sss=3 * d) == ARG            # super-pool rows of the sequences overlap
+    assert idx(sss=4 * d + 4) == ARG        # not a multiple of 8 elements
+    assert idx(spool=odd) == ARG
+    assert idx(spool=None) == ARG
+    assert idx(pss=15 * d) == ARG
+    assert idx(kind=2) == ARG
+    assert idx(G=12) == UNSUP
+    assert idx(W=4097) == UNSUP
+
+    def app(**kw):
+        a = dict(K=p, kss=kss, B=B, G=G, L0=0, L1=L, pool=p, pss=pss, spool=p, sss=sss, kind=0)
+        a.update(kw)
+        return lib.hisa_tree_append(a["K"], a["kss"], S, d, a["B"], a["G"], a["L0"], a["L1"], a["pool"], a["pss"],
+                                    a["spool"], a["sss"], a["kind"], None)
+
+    assert app(sss=3 * d) == ARG
+    assert app(spool=odd) == ARG
+    assert app(pss=15 * d) == ARG
+    assert app(L0=L + 1) == ARG
+    assert app(G=5) == UNSUP
+    assert app(B=24) == UNSUP
+    assert app(kind=9) == ARG
+    assert app(L0=L) == OK                  # empty range: no work

@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 
 from sparse_attention_token_amd import synth
-from parity import bits, build_pool, check_flat_row, check_hisa_row, iou, to_dev
+from parity import (bits, build_pool, build_tree_pools, check_flat_row, check_hisa_row, check_tree_row, iou,
+                    to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +51,7 @@ def _run(hisa, case, qpos_on_device=True, want_flat=True):
 
 
 def test_abi_version(hisa):
-    assert hisa.hisa_abi_version() == 3
+    assert hisa.hisa_abi_version() == 4
 
 
 # ---------------------------------------------------------------- block pool
@@ -232,10 +233,117 @@ def test_hisa_max_pool(hisa, orc, spec):
             check_hisa_row(orc, c, s, i, idx[s, i], sc[s, i], blk[s, i], pool="max")
 
 
+# ---------------------------------------------------------------- three-level tree
+
+@pytest.mark.parametrize("B,G,d,L,S,pool", [(16, 4, 64, 1000, 2, "mean"), (64, 1, 64, 1000, 1, "mean"),
+                                            (128, 8, 128, 128 * 21 + 77, 2, "mean"),
+                                            (32, 256, 128, 32 * 600 + 5, 1, "mean"),
+                                            (64, 16, 128, 64 * 40 + 9, 1, "max"),
+                                            (16, 128, 64, 16 * 300, 1, "max")])
+def test_tree_pools_bit_exact(hisa, orc, B, G, d, L, S, pool):
+    _say(f"tree pools B={B} G={G} d={d} L={L} S={S} {pool}")
+    c = synth.gaussian_case(S, L, 1, 1, d, B, 1, 1, seed=B + G + L)
+    c = _with_ties(c, G) if pool == "max" else _wide_spread_keys(c, G)
+    dev = to_dev(c)
+    ref_b, ref_s = orc.pool(c.K, L, B, mode=pool), orc.super_pool(c.K, L, B, G, mode=pool)
+    for kw in (dict(), dict(L_bulk=L // 3, step=1), dict(L_bulk=0, step=37)):
+        reps, sreps = build_tree_pools(hisa, dev["K"], L, B, G, pool=pool, **kw)
+        np.testing.assert_array_equal(bits(reps), ref_b)
+        np.testing.assert_array_equal(bits(sreps), ref_s)
+
+
+TREE_CASES = [
+    # name, S, L, T, H, d, B, G, W, m, k, kind, explicit positions, pooling
+    ("decode_G8_W3", 4, 9000, 1, 64, 128, 128, 8, 3, 8, 512, "clustered", False, "mean"),
+    ("edge_positions_G4", 2, 3000, 8, 16, 64, 64, 4, 2, 5, 100, "gaussian", True, "mean"),
+    # fewer blocks inside the kept super-blocks than m: -1 slots in the refinement
+    ("m_above_candidates", 1, 5000, 6, 32, 128, 64, 2, 2, 16, 300, "clustered", True, "mean"),
+    ("G1_reduces_to_blocks", 1, 4000, 6, 16, 64, 64, 1, 7, 4, 128, "clustered", True, "mean"),
+    ("G256_long_super", 1, 40000, 4, 16, 64, 16, 256, 3, 40, 256, "clustered", True, "mean"),
+    ("max_pool_G16", 2, 20000, 4, 64, 128, 128, 16, 2, 12, 600, "clustered", True, "max"),
+    ("many_queries_G32", 1, 30000, 64, 16, 64, 64, 32, 4, 10, 200, "gaussian", False, "mean"),
+    # more than 32768 candidate blocks at level 2 and tokens at level 3: chunked selection
+    ("chunked_levels", 1, 600000, 2, 4, 64, 16, 128, 280, 2100, 512, "gaussian", True, "mean"),
+]
+
+
+def _tree_case(spec):
+    name, S, L, T, H, d, B, G, W, m, k, kind, explicit, pool = spec
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    qpos = np.stack([_edge_qpos(L, B, T, rng) for _ in range(S)]) if explicit else None
+    if kind == "gaussian":
+        c = synth.gaussian_case(S, L, T, H, d, B, m, k, seed=13, qpos=qpos)
+    else:
+        c = synth.clustered_case(S, L, T, H, d, B, m, k, seed=13, qpos=qpos, latent_block=B)
+    if pool == "max":
+        c = _with_ties(c, 4)
+    return c
+
+
+def _run_tree(hisa, c, G, W, explicit, pool):
+    import torch
+
+    dev = to_dev(c)
+    reps, sreps = build_tree_pools(hisa, dev["K"], c.L, c.B, G, pool=pool)
+    out = hisa.hisa_tree_index(dev["q"], dev["w"], dev["K"], c.L, reps, sreps, c.B, G, W, c.m, c.k,
+                               dev["qpos"] if explicit else None, want_blocks=True, want_super=True, pool=pool)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in out], dev, reps
+
+
+@pytest.mark.parametrize("spec", TREE_CASES, ids=[s[0] for s in TREE_CASES])
+def test_tree_index(hisa, orc, spec):
+    name, S, L, T, H, d, B, G, W, m, k, kind, explicit, pool = spec
+    _say(f"tree {name}")
+    c = _tree_case(spec)
+    (idx, sc, blk, sblk), _, _ = _run_tree(hisa, c, G, W, explicit, pool)
+    rep = {}
+    rows = range(T) if T <= 8 else range(0, T, 9)
+    for s in range(S):
+        for i in rows:
+            check_tree_row(orc, c, s, i, G, W, idx[s, i], sc[s, i], blk[s, i], sblk[s, i], rep, pool=pool)
+    _say(f"  {rep}")
+
+
+@pytest.mark.parametrize("G,pool", [(4, "mean"), (16, "max")])
+def test_tree_covering_every_super_block_is_hisa(hisa, G, pool):
+    # W >= the number of super-blocks: the tree's levels 2-3 are hisa_index, bit for bit
+    import torch
+
+    c = _tree_case(("cover", 2, 7000, 6, 64, 128, 128, G, 0, 9, 700, "clustered", True, pool))
+    W = -(-(-(-c.L // c.B)) // G)
+    (idx, sc, blk, sblk), dev, reps = _run_tree(hisa, c, G, W, True, pool)
+    hidx, hsc, hblk = hisa.hisa_index(dev["q"], dev["w"], dev["K"], c.L, reps, c.B, c.m, c.k, dev["qpos"],
+                                      want_blocks=True, pool=pool)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx, hidx.cpu().numpy())
+    np.testing.assert_array_equal(sc, hsc.cpu().numpy())
+    np.testing.assert_array_equal(blk, hblk.cpu().numpy())
+
+
+def test_tree_unit_fanout_is_hisa_with_fewer_blocks(hisa):
+    # G = 1: super-blocks are blocks, so the tree keeps hisa_index's top min(W, m) blocks
+    import torch
+
+    c = _tree_case(("unit", 1, 6000, 8, 32, 128, 64, 1, 0, 12, 400, "clustered", True, "mean"))
+    W = 5
+    (idx, sc, blk, sblk), dev, reps = _run_tree(hisa, c, 1, W, True, "mean")
+    hidx, hsc, hblk = hisa.hisa_index(dev["q"], dev["w"], dev["K"], c.L, reps, c.B, W, c.k, dev["qpos"],
+                                      want_blocks=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx, hidx.cpu().numpy())
+    np.testing.assert_array_equal(sc, hsc.cpu().numpy())
+    np.testing.assert_array_equal(blk[..., :W], hblk.cpu().numpy())
+    assert np.all(blk[..., W:] == -1)
+    np.testing.assert_array_equal(sblk, hblk.cpu().numpy())
+
+
 # ---------------------------------------------------------------- small cases
 
 def _edge_qpos(L, B, T, rng):
-    cands = [0, B - 1, B, 2 * B - 1, L // 2, L - 2, L - 1, B + 1]
+    # the longest prefix first, so that cases with few queries still fill
+    # their longest rows (several selection chunks, every kept block)
+    cands = [L - 1, 0, B - 1, L // 2, B, 2 * B - 1, L - 2, B + 1]
     cands = [x for x in cands if 0 <= x < L]
     extra = rng.integers(0, L, size=max(0, T - len(cands))).tolist()
     return np.array((cands + extra)[:T], dtype=np.int32)

@@ -283,11 +283,13 @@ def test_tree_bruteforce(orc, mode):
         t = int(rng.integers(0, 70))
         q, w, K = int_case(rng, t + 1, 2, 4)
         W, m, k = int(rng.integers(1, 4)), int(rng.integers(1, 6)), int(rng.integers(1, 10))
-        SB, bt, st = B * G, t // B, t // (B * G)
-        srep = [rep(K[u * SB:((u + 1) * SB if u < st else t + 1)]) for u in range(st + 1)]
+        bt = t // B
+        st = bt // G
+        brep_all = [rep(K[b * B:((b + 1) * B if b < bt else t + 1)]) for b in range(bt + 1)]
+        srep = [rep(np.stack(brep_all[u * G:min((u + 1) * G, bt + 1)])) for u in range(st + 1)]
         ssel = np.sort(np_topk(np_scores(q, w, np.stack(srep)), np.arange(st + 1), min(W, st + 1)))
         cb = np.array([b for u in ssel for b in range(u * G, min((u + 1) * G, bt + 1))], dtype=np.int64)
-        brep = [rep(K[b * B:((b + 1) * B if b < bt else t + 1)]) for b in cb]
+        brep = [brep_all[b] for b in cb]
         bsel = np.sort(np_topk(np_scores(q, w, np.stack(brep)), cb, min(m, len(cb))))
         cand = np.array([j for b in bsel for j in range(b * B, min(b * B + B, t + 1))], dtype=np.int64)
         want = np_topk(np_scores(q, w, K[cand]), cand, k)
@@ -556,3 +558,27 @@ def test_block_sparse_rejects_budget_below_one_block(orc):
     c = gaussian_case(1, 100, 1, 4, 64, 64, 1, 10, seed=1)
     with pytest.raises(ValueError):
         orc.block_sparse_query(c.q[0, 0], c.w[0, 0], c.K[0], 99, 64, 10)
+
+
+def test_super_pool_hand_example(orc):
+    # keys 0 2 | 2 4 | 8 8 (B = 2): block means 1, 3, 8 and maxima 2, 4, 8; super-blocks of
+    # G = 2 blocks pool those: means (1+3)/2 = 2 and 8, maxima 4 and 8
+    K = bf16_bits(np.array([0, 2, 2, 4, 8, 8], dtype=np.float32)).reshape(1, 6, 1)
+    assert bf16_to_f32(orc.super_pool(K, 6, 2, 2, "mean")).ravel().tolist() == [2.0, 8.0]
+    assert bf16_to_f32(orc.super_pool(K, 6, 2, 2, "max")).ravel().tolist() == [4.0, 8.0]
+    # a partial last block (L = 5): block means 1, 3, 8 still; L = 3: blocks 1, 2 -> super 1.5
+    assert bf16_to_f32(orc.super_pool(K, 3, 2, 2, "mean")).ravel().tolist() == [1.5]
+
+
+def test_super_pool_special_cases(orc):
+    rng = np.random.default_rng(11)
+    K = bf16_bits(rng.standard_normal((2, 700, 8)).astype(np.float32) + 0.5)
+    # G = 1: a super-block is a block
+    np.testing.assert_array_equal(orc.super_pool(K, 700, 16, 1), orc.pool(K, 700, 16))
+    # B = 1: a block is a key, so the super-blocks pool the keys directly
+    np.testing.assert_array_equal(orc.super_pool(K, 700, 1, 32), orc.pool(K, 700, 32))
+    # max pooling: the max over the super-block's keys (no zeros here, so no sign ties)
+    sp = bf16_to_f32(orc.super_pool(K, 700, 16, 4, "max"))
+    f = bf16_to_f32(K)
+    for u in range(sp.shape[1]):
+        np.testing.assert_array_equal(sp[:, u], f[:, u * 64:min(700, u * 64 + 64)].max(axis=1))
