@@ -13,6 +13,10 @@ pool), so successive calls miss the 256 MB last-level cache as a real
 per-layer call would; whole steps are captured in HIP graphs and replayed, so
 the timing is of GPU work, not of Python launch overhead.
 
+With --tree G,W the step is the three-level tree instead (super-blocks of G
+blocks, beam of W super-blocks): hisa_tree_append of the newest rows, then
+hisa_tree_index; the two-level step is timed beside it.
+
 Prints one JSON line.  Default workload: decode, 8 sequences x 32K keys.
 """
 from __future__ import annotations
@@ -42,7 +46,10 @@ def parse():
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD,
-                   help="0 tiny, 1 decode 32K, 2 decode 64K, 3 decode 128K, 4 prefill chunk")
+                   help="0 tiny, 1 decode 32K, 2 decode 64K, 3 decode 128K, 4 prefill chunk, "
+                        "5 decode 1M, 6 decode 4M")
+    p.add_argument("--tree", default=None, metavar="G,W",
+                   help="time the three-level tree (super-blocks of G blocks, W kept) as the step")
     p.add_argument("--rotate-mib", type=int, default=1024,
                    help="cycle key-cache replicas until at least this much is touched per cycle")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -64,7 +71,7 @@ def log(msg):
 
 # ---------------------------------------------------------------- algorithmic work models
 
-def kernel_models(case, blocks):
+def kernel_models(case, blocks, tree=None, sblocks=None):
     """Algorithmic bytes and flops per launch of each kernel for this workload.
 
     Bytes count what the method must move: bf16 rows it scores (block means or
@@ -96,6 +103,23 @@ def kernel_models(case, blocks):
     models["index_decode"] = dict(bytes=int((nb.sum() + cand.sum()) * row + qw),
                                   flops=models["score_blocks"]["flops"] + models["score_refine"]["flops"])
     per_query_hisa = (nb.sum() + cand.sum()) * row + qw + S * T * k * 4
+    if tree is not None:
+        # three-level tree: super-block scores replace the block scores; the
+        # blocks scored are those <= b_t inside the kept super-blocks
+        G, W = tree
+        st = (t // B) // G
+        ns = st + 1
+        flat_sb = sblocks.reshape(S * T, W)
+        ntb = np.zeros_like(t)
+        for qi in range(S * T):
+            u = flat_sb[qi][flat_sb[qi] >= 0].astype(np.int64)
+            ntb[qi] = np.clip(t[qi] // B + 1 - u * G, 0, G).sum()
+        models["score_blocks"] = dict(bytes=int(ns.sum() * row + qw), flops=int(2 * H * d * ns.sum()))
+        models["select_blocks"] = dict(bytes=int(ns.sum() * 4 + S * T * W * 4), flops=0)
+        models["score_tree"] = dict(bytes=int(ntb.sum() * row + qw), flops=int(2 * H * d * ntb.sum()))
+        models["select_tree"] = dict(bytes=int(ntb.sum() * 4 + S * T * m * 4), flops=0)
+        models["own_super"] = dict(bytes=int(((t // B) - st * G + 1).sum() * row), flops=0)
+        per_query_hisa = (ns.sum() + ntb.sum() + cand.sum()) * row + qw + S * T * k * 4
     return models, int(per_query_hisa), int(cand.sum())
 
 
@@ -150,6 +174,11 @@ def main():
     hisa.lib()
     case = synth.workload(args.workload, args.sequences)
     S, T, H, d, L, B, m, k = case.S, case.T, case.H, case.d, case.L, case.B, case.m, case.k
+    tree = None
+    if args.tree:
+        G, W = (int(x) for x in args.tree.split(","))
+        tree = (G, W)
+        case.name += f"_tree_G{G}_W{W}"
     prefill = T > 1
     steps = args.steps if args.steps is not None else (20 if prefill else 400)
     warmup = args.warmup if args.warmup is not None else (3 if prefill else 40)
@@ -167,11 +196,16 @@ def main():
     touched_hisa = S * T * (min(m, nblk) * B + nblk) * d * 2 if not prefill else K0.numel() * 2
     R = max(1, math.ceil(args.rotate_mib * 2**20 / touched_hisa))
     R = min(R, 4 if prefill else 128, max(1, (16 * 2**30) // (K0.numel() * 2)))
-    Ks, pools = [], []
+    Ks, pools, spools = [], [], []
     for r in range(R):
         Kr = K0 if r == 0 else K0.clone()
         pr = torch.zeros((S, nblk, d), dtype=torch.bfloat16, device=dev)
-        hisa.hisa_pool_append(Kr, pr, 0, L, B)
+        if tree is None:
+            hisa.hisa_pool_append(Kr, pr, 0, L, B)
+        else:
+            sp = torch.zeros((S, -(-nblk // tree[0]), d), dtype=torch.bfloat16, device=dev)
+            hisa.hisa_tree_append(Kr, pr, sp, 0, L, B, tree[0])
+            spools.append(sp)
         Ks.append(Kr)
         pools.append(pr)
     torch.cuda.synchronize()
@@ -185,12 +219,27 @@ def main():
     fws = torch.empty(hisa.dsa_flat_workspace(S, T, H, d, L, k), dtype=torch.uint8, device=dev)
     L_new_rows = T                       # the step appends the batch's own newest key rows
 
-    def hisa_step(r):
+    def two_level_step(r):
         # hisa_pool_append of the new rows, then hisa_index, in one call (the
         # library stores the last block's mean from the block stage when the
         # new rows all lie in it: decode steps)
         hisa.hisa_append_index(Ks[r], pools[r], L - L_new_rows, L, q, w, B, m, k, None, out_idx=out_idx,
                                out_score=out_score, workspace=ws)
+
+    if tree is not None:
+        G, W = tree
+        tws = torch.empty(hisa.hisa_tree_index_workspace(S, T, H, d, L, B, G, W, m, k), dtype=torch.uint8,
+                          device=dev)
+
+        def tree_index_only(r):
+            hisa.hisa_tree_index(q, w, Ks[r], L, pools[r], spools[r], B, G, W, m, k, None, out_idx=out_idx,
+                                 out_score=out_score, workspace=tws)
+
+        def hisa_step(r):
+            hisa.hisa_tree_append(Ks[r], pools[r], spools[r], L - L_new_rows, L, B, G)
+            tree_index_only(r)
+    else:
+        hisa_step = two_level_step
 
     def flat_step(r):
         hisa.dsa_flat_index(q, w, Ks[r], L, k, None, out_idx=f_idx, out_score=f_score, workspace=fws)
@@ -228,22 +277,32 @@ def main():
         return ms
 
     # ---- correctness snapshot for the reports (kept blocks, IoU vs flat, needles)
-    idx_h, _, blk_h = hisa.hisa_index(q, w, K0, L, pools[0], B, m, k, None, want_blocks=True)
+    idx_2, _, blk_h = hisa.hisa_index(q, w, K0, L, pools[0], B, m, k, None, want_blocks=True)
+    sblocks = None
+    idx_h = idx_2
+    if tree is not None:
+        idx_h, _, blk_h, sb_h = hisa.hisa_tree_index(q, w, K0, L, pools[0], spools[0], B, G, W, m, k, None,
+                                                     want_blocks=True, want_super=True)
+        sblocks = sb_h.cpu().numpy()
     torch.cuda.synchronize()
     blocks = blk_h.cpu().numpy()
-    models, hisa_bytes, n_cand = kernel_models(case, blocks)
+    models, hisa_bytes, n_cand = kernel_models(case, blocks, tree, sblocks)
 
     # ---- timed HISA steps
-    hisa_ms = time_graphs(hisa_step, steps, warmup, "hisa step (pool append + index)")
+    hisa_ms = time_graphs(hisa_step, steps, warmup,
+                          "tree step (tree append + tree index)" if tree else "hisa step (pool append + index)")
+    two_level_ms = time_graphs(two_level_step, steps, 2, "two-level step") if tree else None
 
     # ---- index-only timing, for the speedup of the indexer itself
     def hisa_index_only(r):
         hisa.hisa_index(q, w, Ks[r], L, pools[r], B, m, k, None, out_idx=out_idx,
                         out_score=out_score, workspace=ws)
-    index_ms = time_graphs(hisa_index_only, steps, 2, "hisa_index only")
+    index_ms = time_graphs(tree_index_only if tree else hisa_index_only, steps, 2,
+                           "hisa_tree_index only" if tree else "hisa_index only")
 
     flat_ms = None
     iou = None
+    iou_two = None
     needle = None
     if not args.no_flat:
         flat_steps = max(R, min(steps, 40)) if prefill else steps
@@ -251,16 +310,26 @@ def main():
         fi, _ = hisa.dsa_flat_index(q, w, K0, L, k, None)
         torch.cuda.synchronize()
         a, b = idx_h.cpu().numpy().reshape(S * T, k), fi.cpu().numpy().reshape(S * T, k)
-        ious = []
-        for x, y in zip(a, b):
-            sx, sy = set(x[x >= 0].tolist()), set(y[y >= 0].tolist())
-            ious.append(len(sx & sy) / max(1, len(sx | sy)))
-        iou = float(np.mean(ious))
+
+        def mean_iou(xs, ys):
+            ious = []
+            for x, y in zip(xs, ys):
+                sx, sy = set(x[x >= 0].tolist()), set(y[y >= 0].tolist())
+                ious.append(len(sx & sy) / max(1, len(sx | sy)))
+            return float(np.mean(ious))
+        iou = mean_iou(a, b)
+        if tree is not None:
+            a2 = idx_2.cpu().numpy().reshape(S * T, k)
+            iou_two = {"two_level_vs_flat": mean_iou(a2, b), "tree_vs_two_level": mean_iou(a, a2)}
         if case.needles is not None:
             hit = sum(int(j in set(a[s].tolist())) for s in range(S) for j in case.needles[s])
             fhit = sum(int(j in set(b[s].tolist())) for s in range(S) for j in case.needles[s])
             needle = {"hisa": hit / case.needles.size, "flat": fhit / case.needles.size,
                       "needles": int(case.needles.size)}
+            if tree is not None:
+                a2 = idx_2.cpu().numpy().reshape(S * T, k)
+                needle["two_level"] = sum(int(j in set(a2[s].tolist())) for s in range(S)
+                                          for j in case.needles[s]) / case.needles.size
 
     # ---- per-kernel durations: HIP events around each kernel, eager launches
     # queued behind a long matrix product so the GPU never waits on the host
@@ -271,7 +340,7 @@ def main():
         if n == 0:
             continue
         torch.cuda.synchronize()
-        hisa.profile_enable(8 * n)
+        hisa.profile_enable(16 * n)
         for _ in range(6 if prefill else 12):
             torch.mm(big, big)
         for i in range(n):
@@ -309,11 +378,23 @@ def main():
         import oracle
 
         n = S * T
+        if tree is not None:
+            # the tree oracle runs one query at a time on one core
+            def run(sel):
+                for qi in sel:
+                    s_, i_ = divmod(int(qi), T)
+                    oracle.tree_query(case.q[s_, i_], case.w[s_, i_], case.K[s_], int(case.qpos[s_, i_]), B, G, W,
+                                      m, k)
+            cores, what = 1, "tree"
+        else:
+            def run(sel):
+                oracle.hisa_batch(case.q, case.w, case.qpos, case.K, L, B, m, k, sel=sel)
+            cores, what = oracle.num_threads(), "HISA"
         # size the sample to about 10 s of oracle work: distinct queries first
         # (evenly spaced over the batch), then whole repeats of the batch
         probe = np.linspace(0, n - 1, min(n, 8)).astype(np.int32)
         t0 = time.perf_counter()
-        oracle.hisa_batch(case.q, case.w, case.qpos, case.K, L, B, m, k, sel=probe)
+        run(probe)
         per_q = max((time.perf_counter() - t0) / len(probe), 1e-6)
         target_s = 15.0
         nsel = int(min(n, max(len(probe), target_s / per_q)))
@@ -321,13 +402,13 @@ def main():
         reps = max(1, min(1000, int(round(target_s / (per_q * nsel)))))
         t0 = time.perf_counter()
         for _ in range(reps):
-            oracle.hisa_batch(case.q, case.w, case.qpos, case.K, L, B, m, k, sel=sel)
+            run(sel)
         tc = time.perf_counter() - t0
         nq_cpu = reps * len(sel)
-        cpu = {"value": nq_cpu / tc, "unit": "queries/s", "cores": oracle.num_threads(),
+        cpu = {"value": nq_cpu / tc, "unit": "queries/s", "cores": cores,
                "kind": "oracle",
                "sample": f"{len(sel)} of {n} queries of {case.name} (evenly spaced), {reps} pass(es), "
-                         f"through the fp64 C oracle (HISA): {nq_cpu} queries in {tc:.1f} s",
+                         f"through the fp64 C oracle ({what}): {nq_cpu} queries in {tc:.1f} s",
                "us_per_query": tc / nq_cpu * 1e6}
 
     nq = S * T
@@ -354,6 +435,8 @@ def main():
         "speedup_vs_flat": None if flat_ms is None else flat_ms / hisa_ms,
         "speedup_vs_flat_index_only": None if flat_ms is None else flat_ms / index_ms,
         "iou_vs_flat": iou,
+        "tree": None if tree is None else {"G": tree[0], "W": tree[1], "two_level_ms_per_step": two_level_ms,
+                                           "speedup_vs_two_level": two_level_ms / hisa_ms, **(iou_two or {})},
         "needle_recall": needle,
         "hisa_algorithmic_bytes_per_call": hisa_bytes,
         "candidates_per_call": n_cand,

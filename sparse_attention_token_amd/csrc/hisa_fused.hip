@@ -30,6 +30,9 @@
 //  * batch (many queries): hisa_blocks_topm_kernel runs the block stage once
 //    per query and writes the kept blocks; hisa_refine_kernel then scores
 //    128-row tiles with q staged in LDS.
+//  * more than 2048 blocks, query by query (decode past 256K keys at B = 128,
+//    and batches): hisa_dblocks_kernel as in decode, the top m as a
+//    selection launch, then hisa_refine_kernel.
 //  * many queries per sequence (prefill chunks): block stage and refinement
 //    both block by block (hisa_prefill.hip).
 // Either way the final top k runs as the selection kernel (select.hip).
@@ -663,10 +666,32 @@ __global__ __launch_bounds__(kK2Threads) void hisa_refine_kernel(FusedArgs a) {
     }
 }
 
+// More blocks than the one-wave top m takes, query by query: the block scores
+// are spread over workgroups (hisa_dblocks_kernel, which also stores the
+// fused pool entry), the top m is a selection launch of its own, then the
+// refinement.  A single workgroup per query (hisa_blocks_topm_kernel) would
+// score thousands of pooled means one tile after another.
+template <int MT, int KS>
+hipError_t launch_wide_blocks(const FusedArgs &a, dim3 g2, hipStream_t st) {
+    const int nq = a.S * a.T;
+    const int btiles = (a.nblk + kDBlkRows - 1) / kDBlkRows;
+    hipError_t e = launch(kKindScoreBlocks, hisa_dblocks_kernel<MT, KS>,
+                          dim3(static_cast<uint32_t>(decode_grid(nq, btiles + 1))), dim3(kDecodeThreads), 0, st, a);
+    if (e != hipSuccess) return e;
+    SelectArgs se{};
+    se.keys = a.blk_keys; se.keys_stride = a.blk_stride;
+    se.qpos = a.qpos; se.L = a.L; se.T = a.T; se.B = a.B; se.m = a.m;
+    se.kout = a.m; se.out_id = a.sel_blk; se.out_id_copy = a.out_blk;
+    e = launch_select(kScoreBlocks, se, nq, a.nblk, st);
+    if (e != hipSuccess) return e;
+    return launch(kKindScoreRefine, hisa_refine_kernel<MT, KS>, g2, dim3(kK2Threads), 0, st, a);
+}
+
 template <int MT, int KS>
 hipError_t launch_fused_ks(const FusedArgs &a, bool decode, hipStream_t st) {
     const int nq = a.S * a.T;
     const dim3 g2(static_cast<uint32_t>((static_cast<int64_t>(a.m) * a.B + 127) / 128), nq);
+    if (!a.bucket_off && a.nblk > kK1WaveMax) return launch_wide_blocks<MT, KS>(a, g2, st);
     if (decode) {
         const int64_t mb = static_cast<int64_t>(a.m) * a.B;
         const int wide = static_cast<int>((mb + kDecodeRowsWide - 1) / kDecodeRowsWide);

@@ -16,7 +16,13 @@ representatives (the two poolings one page names for the coarse summaries:
 "Hierarchical Indexing Makes Sparse Attention Actually Fast", section on the
 hierarchical summarization of the KV cache).
 
+The three-level tree (super-blocks of G blocks, W of them kept, then m blocks
+and k tokens; same page and section, which searches a tree of summaries with a
+beam of W nodes per level) runs with --fanouts: for each G and W, its IoU with
+the flat top k and with the two-level HISA of the same B and m.
+
     python -m sparse_attention_token_amd.quality [--workload 2] [--blocks 64,128,256] [--pools mean,max]
+                                                 [--fanouts 16,64 --beams 4,8,16,32]
 
 Prints a markdown table.  Every selection runs in the library's HIP kernels.
 """
@@ -40,6 +46,10 @@ def main(argv=None):
                    help="candidate budgets m*B as multiples of k (1 = block-sparse)")
     p.add_argument("--reps", type=int, default=20)
     p.add_argument("--pools", default="mean,max", help="block representatives: mean and/or max pooling")
+    p.add_argument("--fanouts", default="", help="three-level tree: blocks per super-block (G)")
+    p.add_argument("--beams", default="4,8,16,32", help="three-level tree: super-blocks kept (W)")
+    p.add_argument("--tree-block", type=int, default=128, help="three-level tree: block size B")
+    p.add_argument("--tree-multiple", type=int, default=4, help="three-level tree: m*B as a multiple of k")
     args = p.parse_args(argv)
 
     import torch
@@ -104,6 +114,36 @@ def main(argv=None):
                 name = ("block-sparse" if mult == 1 else "HISA") + f" ({pk})"
                 rows.append((name, B, m, iou, recall(sets), e0.elapsed_time(e1) * 1e3 / args.reps))
 
+    tree_rows = []
+    for pk in args.pools.split(",") if args.fanouts else ():
+        B = args.tree_block
+        m = args.tree_multiple * k // B
+        nblk = -(-L // B)
+        pool = torch.zeros((S, nblk, case.d), dtype=torch.bfloat16, device=dev)
+        hisa.hisa_pool_append(K, pool, 0, L, B, pool=pk)
+        two, _, _ = hisa.hisa_index(q, w, K, L, pool, B, m, k, None, pool=pk)
+        torch.cuda.synchronize()
+        two = _sets(two.cpu().numpy())
+        for G in (int(x) for x in args.fanouts.split(",")):
+            sp = torch.zeros((S, -(-nblk // G), case.d), dtype=torch.bfloat16, device=dev)
+            hisa.hisa_tree_append(K, pool, sp, 0, L, B, G, pool=pk)
+            for W in (int(x) for x in args.beams.split(",")):
+                ws = torch.empty(hisa.hisa_tree_index_workspace(S, T, case.H, case.d, L, B, G, W, m, k),
+                                 dtype=torch.uint8, device=dev)
+                idx, sc, _, _ = hisa.hisa_tree_index(q, w, K, L, pool, sp, B, G, W, m, k, None, workspace=ws,
+                                                     pool=pk)
+                torch.cuda.synchronize()
+                sets = _sets(idx.cpu().numpy())
+                iou_f = float(np.mean([len(a & b) / max(1, len(a | b)) for a, b in zip(sets, flat)]))
+                iou_2 = float(np.mean([len(a & b) / max(1, len(a | b)) for a, b in zip(sets, two)]))
+                e0.record()
+                for _ in range(args.reps):
+                    hisa.hisa_tree_index(q, w, K, L, pool, sp, B, G, W, m, k, None, out_idx=idx, out_score=sc,
+                                         workspace=ws, pool=pk)
+                e1.record()
+                torch.cuda.synchronize()
+                tree_rows.append((pk, B, G, W, m, iou_f, iou_2, recall(sets), e0.elapsed_time(e1) * 1e3 / args.reps))
+
     print(f"workload {case.name}: S={S} T={T} L={L} H={case.H} d={case.d} k={k}; "
           f"{0 if needles is None else needles.size} needles")
     print("| method | B | m | mean IoU with flat top-k | needle recall | µs per call |")
@@ -111,6 +151,14 @@ def main(argv=None):
     for name, B, m, iou, rec, us in rows:
         r = "-" if rec is None else f"{rec:.3f}"
         print(f"| {name} | {B} | {m} | {iou:.3f} | {r} | {us:.1f} |")
+    if tree_rows:
+        print()
+        print("| tree | B | G | W | m | mean IoU with flat top-k | mean IoU with two-level HISA | needle recall "
+              "| µs per call |")
+        print("|---|---|---|---|---|---|---|---|---|")
+        for pk, B, G, W, m, iou_f, iou_2, rec, us in tree_rows:
+            r = "-" if rec is None else f"{rec:.3f}"
+            print(f"| tree ({pk}) | {B} | {G} | {W} | {m} | {iou_f:.3f} | {iou_2:.3f} | {r} | {us:.1f} |")
     return 0
 
 

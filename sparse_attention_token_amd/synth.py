@@ -154,23 +154,26 @@ def clustered_case(S, L, T, H, d, B, m, k, seed, qpos=None, latent_block=128, w_
 
 
 # The five workloads: one tiny correctness case, three long-context decode batches
-# and one prefill chunk.  Index i uses seed SEED_BASE + i.
+# and one prefill chunk; then two decode batches past a million keys, for the
+# three-level tree.  Index i uses seed SEED_BASE + i.
 WORKLOADS = {
     0: "tiny_L1024",
     1: "decode_L32K",
     2: "decode_L64K_needles",
     3: "decode_L128K_tail77",
     4: "prefill_T4096_L128K",
+    5: "decode_L1M",
+    6: "decode_L4M",
 }
 
 
 def workload(i: int, sequences: int | None = None) -> Case:
     """Workload i; `sequences` replaces the batch size of a decode workload
-    (1..3) to study how the decode path scales with batch (the name then gains
+    (1..3, 5, 6) to study how the decode path scales with batch (the name then gains
     an _S<n> suffix)."""
     seed = SEED_BASE + i
-    if sequences is not None and i not in (1, 2, 3):
-        raise ValueError("only the decode workloads (1..3) take another batch size")
+    if sequences is not None and i not in (1, 2, 3, 5, 6):
+        raise ValueError("only the decode workloads (1..3, 5, 6) take another batch size")
     if i == 0:
         c = gaussian_case(1, 1024, 16, 4, 64, 64, 4, 64, seed, w_scale=0.5)
     elif i == 1:
@@ -181,6 +184,10 @@ def workload(i: int, sequences: int | None = None) -> Case:
         c = clustered_case(sequences or 2, 131072 + 77, 1, 64, 128, 128, 128, 2048, seed, L_bulk=131072)
     elif i == 4:
         c = clustered_case(1, 131072, 4096, 64, 128, 128, 64, 2048, seed)
+    elif i == 5:
+        c = clustered_case(sequences or 4, 1 << 20, 1, 64, 128, 128, 64, 2048, seed, needles_per_seq=8)
+    elif i == 6:
+        c = clustered_case(sequences or 1, 1 << 22, 1, 64, 128, 128, 64, 2048, seed, needles_per_seq=8)
     else:
         raise ValueError(f"no workload {i}")
     c.name = WORKLOADS[i] + (f"_S{sequences}" if sequences is not None else "")

@@ -119,6 +119,9 @@ APPEND_INDEX = [
     ("decode_one_launch", 4, 3000, 3001, 1, 64, 128, 128, 8, 300, False, "mean"),
     ("decode_new_block", 2, 3072, 3073, 1, 64, 128, 128, 8, 300, False, "mean"),
     ("decode_two_kernel", 2, 40000, 40001, 1, 16, 64, 64, 20, 400, False, "mean"),
+    # more than 2048 blocks: spread block scores, a top-m launch, then the refinement
+    ("decode_wide_blocks", 2, 300000, 300001, 1, 64, 128, 128, 16, 512, False, "mean"),
+    ("decode_wide_blocks_max", 2, 300000, 300003, 1, 64, 128, 128, 16, 512, False, "max"),
     ("query_major_20q", 1, 5000, 5003, 20, 32, 128, 128, 8, 300, False, "mean"),
     ("decode_one_launch_max", 4, 3000, 3001, 1, 64, 128, 128, 8, 300, False, "max"),
     ("decode_two_kernel_max", 2, 40000, 40001, 1, 16, 64, 64, 20, 400, False, "max"),
@@ -374,6 +377,7 @@ SMALL = [
     ("fused_17_queries", 1, 5000, 17, 64, 128, 128, 8, 512, "clustered"),
     # more than 2048 blocks: the block stage selects with the whole workgroup
     ("blocks_2344_workgroup_select", 1, 300000, 2, 4, 64, 128, 8, 256, "gaussian"),
+    ("blocks_2344_40_queries", 2, 300000, 20, 16, 128, 128, 12, 300, "clustered"),
 ]
 
 
