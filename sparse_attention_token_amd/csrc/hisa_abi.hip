@@ -205,7 +205,7 @@ void prof_release() {
 const char *const kKindNames[kKindCount] = {
     "pool_append", "own_mean", "score_blocks", "select_blocks",
     "score_refine", "select_refine", "score_flat", "select_flat",
-    "index_decode", "bucket", "own_super", "score_tree", "select_tree",
+    "index_decode", "bucket", "own_super", "score_tree", "select_tree", "tree_top",
 };
 
 }  // namespace
@@ -434,6 +434,72 @@ int hisa_append_index(const uint16_t *K, int64_t k_seq_stride, int64_t L_old, in
                                   B, m, k, out_idx, out_score, out_blk, ws, ws_bytes, HISA_POOL_MEAN, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Levels 1-2 of hisa_tree_index as separate launches (any supported shape):
+// own-block and own super-block representatives, super-block scores, top W,
+// the blocks inside them, top m into the workspace's kept-block table.
+int tree_upper_levels(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
+                      int64_t k_seq_stride, int64_t L, const uint16_t *pool_rep, int64_t pool_seq_stride,
+                      const uint16_t *spool_rep, int64_t spool_seq_stride, int S, int T, int H, int d, int B, int G,
+                      int W, int m, int32_t *out_blk, int32_t *out_sblk, const TreeLayout &lay, char *base, bool pmax,
+                      hipStream_t hs) {
+    int st = HISA_OK;
+    uint16_t *own_rep = reinterpret_cast<uint16_t *>(base + lay.own_rep);
+    uint16_t *own_srep = reinterpret_cast<uint16_t *>(base + lay.own_srep);
+    uint32_t *sblk_keys = reinterpret_cast<uint32_t *>(base + lay.sblk_keys);
+    int32_t *sel_sb = reinterpret_cast<int32_t *>(base + lay.sel_sb);
+    uint32_t *tblk_keys = reinterpret_cast<uint32_t *>(base + lay.tblk_keys);
+    int32_t *sel_blk = reinterpret_cast<int32_t *>(base + lay.sel_blk);
+    const int nq = S * T;
+    const int64_t ns = ceil_div(ceil_div(L, B), G);
+    const int64_t ntb = std::min<int64_t>(W, ns) * G;
+
+    // own block and own super-block representatives of every query
+    st = hip_status(launch_own_mean(K, k_seq_stride, qpos, L, S, T, d, B, pmax, own_rep, hs));
+    if (st != HISA_OK) return st;
+    st = hip_status(launch_own_super(pool_rep, pool_seq_stride, own_rep, qpos, L, S, T, d, B, G, pmax, own_srep, hs));
+    if (st != HISA_OK) return st;
+
+    ScoreArgs sa{};
+    sa.q = q; sa.w = w; sa.qpos = qpos;
+    sa.K = K; sa.k_seq_stride = k_seq_stride; sa.L = L;
+    sa.S = S; sa.T = T; sa.H = H; sa.d = d;
+    SelectArgs se{};
+    se.qpos = qpos; se.L = L; se.T = T;
+    set_stage(se, base, lay.stage);
+
+    // level 1: super-blocks are blocks of B*G keys with the super pool as
+    // their representatives; keep the top W
+    sa.pool = spool_rep; sa.pool_seq_stride = spool_seq_stride; sa.own_rep = own_srep;
+    sa.B = B * G; sa.m = 1;
+    sa.keys = sblk_keys; sa.keys_stride = lay.sblk_stride;
+    st = hip_status(launch_score(kScoreBlocks, sa, ns, hs));
+    if (st != HISA_OK) return st;
+    se.B = B * G; se.m = 1; se.kout = W;
+    se.keys = sblk_keys; se.keys_stride = lay.sblk_stride; se.sel_blk = nullptr;
+    se.out_id = sel_sb; se.out_score = nullptr; se.out_id_copy = out_sblk;
+    st = hip_status(launch_select(kScoreBlocks, se, nq, ns, hs));
+    if (st != HISA_OK) return st;
+
+    // level 2: the blocks of the kept super-blocks; keep the top m
+    sa.pool = pool_rep; sa.pool_seq_stride = pool_seq_stride; sa.own_rep = own_rep;
+    sa.B = B; sa.G = G; sa.W = W; sa.sel_sb = sel_sb;
+    sa.keys = tblk_keys; sa.keys_stride = lay.tblk_stride;
+    st = hip_status(launch_score(kScoreTreeBlocks, sa, ntb, hs));
+    if (st != HISA_OK) return st;
+    se.B = B; se.G = G; se.m = W; se.kout = m;
+    se.keys = tblk_keys; se.keys_stride = lay.tblk_stride; se.sel_blk = sel_sb;
+    se.out_id = sel_blk; se.out_score = nullptr; se.out_id_copy = out_blk;
+    return hip_status(launch_select(kScoreTreeBlocks, se, nq, ntb, hs));
+}
+
+}  // namespace
+
+extern "C" {
+
 int hisa_tree_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B, int G, int64_t L_old,
                      int64_t L_new, uint16_t *pool_rep, int64_t pool_seq_stride, uint16_t *spool_rep,
                      int64_t spool_seq_stride, int pool_kind, void *stream) {
@@ -450,6 +516,9 @@ int hisa_tree_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int 
     const bool pmax = pool_kind == HISA_POOL_MAX;
     // leaf level: the blocks holding the new rows
     const int64_t blk0 = L_old / B;
+    if (blk0 == nblk - 1 && tree_append_one_supported(B))     // one block (decode): both levels in one launch
+        return hip_status(launch_tree_append_one(K, k_seq_stride, S, d, B, G, blk0, L_new, pmax, pool_rep,
+                                                 pool_seq_stride, spool_rep, spool_seq_stride, hs));
     st = hip_status(launch_pool_append(K, k_seq_stride, S, d, B, blk0, nblk - blk0, L_new, pmax, pool_rep,
                                        pool_seq_stride, hs));
     if (st != HISA_OK) return st;
@@ -491,67 +560,47 @@ int hisa_tree_index(const uint16_t *q, const float *w, const int32_t *qpos, cons
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool pmax = pool_kind == HISA_POOL_MAX;
     char *base = align_ptr(ws);
-    uint16_t *own_rep = reinterpret_cast<uint16_t *>(base + lay.own_rep);
-    uint16_t *own_srep = reinterpret_cast<uint16_t *>(base + lay.own_srep);
-    uint32_t *sblk_keys = reinterpret_cast<uint32_t *>(base + lay.sblk_keys);
-    int32_t *sel_sb = reinterpret_cast<int32_t *>(base + lay.sel_sb);
-    uint32_t *tblk_keys = reinterpret_cast<uint32_t *>(base + lay.tblk_keys);
     int32_t *sel_blk = reinterpret_cast<int32_t *>(base + lay.sel_blk);
     uint32_t *cand_keys = reinterpret_cast<uint32_t *>(base + lay.cand_keys);
     const int nq = S * T;
-    const int64_t ns = ceil_div(ceil_div(L, B), G);
-    const int64_t ntb = std::min<int64_t>(W, ns) * G;
 
-    // own block and own super-block representatives of every query
-    st = hip_status(launch_own_mean(K, k_seq_stride, qpos, L, S, T, d, B, pmax, own_rep, hs));
-    if (st != HISA_OK) return st;
-    st = hip_status(launch_own_super(pool_rep, pool_seq_stride, own_rep, qpos, L, S, T, d, B, G, pmax, own_srep, hs));
-    if (st != HISA_OK) return st;
-
-    ScoreArgs sa{};
-    sa.q = q; sa.w = w; sa.qpos = qpos;
-    sa.K = K; sa.k_seq_stride = k_seq_stride; sa.L = L;
-    sa.S = S; sa.T = T; sa.H = H; sa.d = d;
-    SelectArgs se{};
-    se.qpos = qpos; se.L = L; se.T = T;
-    set_stage(se, base, lay.stage);
-
-    // level 1: super-blocks are blocks of B*G keys with the super pool as
-    // their representatives; keep the top W
-    sa.pool = spool_rep; sa.pool_seq_stride = spool_seq_stride; sa.own_rep = own_srep;
-    sa.B = B * G; sa.m = 1;
-    sa.keys = sblk_keys; sa.keys_stride = lay.sblk_stride;
-    st = hip_status(launch_score(kScoreBlocks, sa, ns, hs));
-    if (st != HISA_OK) return st;
-    se.B = B * G; se.m = 1; se.kout = W;
-    se.keys = sblk_keys; se.keys_stride = lay.sblk_stride; se.sel_blk = nullptr;
-    se.out_id = sel_sb; se.out_score = nullptr; se.out_id_copy = out_sblk;
-    st = hip_status(launch_select(kScoreBlocks, se, nq, ns, hs));
-    if (st != HISA_OK) return st;
-
-    // level 2: the blocks of the kept super-blocks; keep the top m
-    sa.pool = pool_rep; sa.pool_seq_stride = pool_seq_stride; sa.own_rep = own_rep;
-    sa.B = B; sa.G = G; sa.W = W; sa.sel_sb = sel_sb;
-    sa.keys = tblk_keys; sa.keys_stride = lay.tblk_stride;
-    st = hip_status(launch_score(kScoreTreeBlocks, sa, ntb, hs));
-    if (st != HISA_OK) return st;
-    se.B = B; se.G = G; se.m = W; se.kout = m;
-    se.keys = tblk_keys; se.keys_stride = lay.tblk_stride; se.sel_blk = sel_sb;
-    se.out_id = sel_blk; se.out_score = nullptr; se.out_id_copy = out_blk;
-    st = hip_status(launch_select(kScoreTreeBlocks, se, nq, ntb, hs));
-    if (st != HISA_OK) return st;
+    if (tree_top_supported(d, L, B, G, W)) {
+        // levels 1-2 in one launch, then the token level
+        TreeTopArgs ta{};
+        ta.q = q; ta.w = w; ta.qpos = qpos;
+        ta.K = K; ta.k_seq_stride = k_seq_stride; ta.L = L;
+        ta.pool = pool_rep; ta.pool_seq_stride = pool_seq_stride;
+        ta.spool = spool_rep; ta.spool_seq_stride = spool_seq_stride;
+        ta.S = S; ta.T = T; ta.H = H; ta.d = d; ta.B = B; ta.G = G; ta.W = W; ta.m = m;
+        ta.pool_max = pmax ? 1 : 0;
+        ta.sel_blk = sel_blk; ta.out_blk = out_blk; ta.out_sblk = out_sblk;
+        st = hip_status(launch_tree_top(ta, hs));
+        if (st != HISA_OK) return st;
+    } else {
+        st = tree_upper_levels(q, w, qpos, K, k_seq_stride, L, pool_rep, pool_seq_stride, spool_rep,
+                               spool_seq_stride, S, T, H, d, B, G, W, m, out_blk, out_sblk, lay, base, pmax, hs);
+        if (st != HISA_OK) return st;
+    }
 
     // level 3: the tokens of the kept blocks (slots past the kept count hold
     // -1 and give no candidate); keep the top k
-    sa.m = m; sa.sel_blk = sel_blk;
+    ScoreArgs sa{};
+    sa.q = q; sa.w = w; sa.qpos = qpos;
+    sa.K = K; sa.k_seq_stride = k_seq_stride; sa.L = L;
+    sa.S = S; sa.T = T; sa.H = H; sa.d = d; sa.B = B; sa.m = m; sa.sel_blk = sel_blk;
     sa.keys = cand_keys; sa.keys_stride = lay.cand_stride;
     st = hip_status(launch_score(kScoreRefine, sa, static_cast<int64_t>(m) * B, hs));
     if (st != HISA_OK) return st;
+    SelectArgs se{};
+    se.qpos = qpos; se.L = L; se.T = T;
+    set_stage(se, base, lay.stage);
     se.B = B; se.m = m; se.kout = k;
     se.keys = cand_keys; se.keys_stride = lay.cand_stride; se.sel_blk = sel_blk;
     se.out_id = out_idx; se.out_score = out_score; se.out_id_copy = nullptr;
     return hip_status(launch_select(kScoreRefine, se, nq, static_cast<int64_t>(m) * B, hs));
 }
+
+
 
 size_t dsa_flat_workspace(int S, int T, int H, int d, int64_t L, int k) {
     if (check_query_shape(S, T, H, d, L, k) != HISA_OK) return 0;

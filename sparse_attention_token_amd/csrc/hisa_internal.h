@@ -156,6 +156,13 @@ hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, in
                               int64_t blk0, int64_t nblk, int64_t L_new, bool pool_max, uint16_t *pool,
                               int64_t pool_seq_stride, hipStream_t st);
 
+// Both tree levels in one launch when the new rows all lie in block blk (the
+// last one) and B <= 128: block blk from K, then its super-block from the pool.
+bool tree_append_one_supported(int B);
+hipError_t launch_tree_append_one(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B, int G, int64_t blk,
+                                  int64_t L_new, bool pool_max, uint16_t *pool, int64_t pool_seq_stride,
+                                  uint16_t *spool, int64_t spool_seq_stride, hipStream_t st);
+
 // Own-block representatives of queries at the consecutive positions
 // t = L - T + i (requires T <= L): one pass per block.
 hipError_t launch_own_prefix_mean(const uint16_t *K, int64_t k_seq_stride, int64_t L, int S, int T, int d, int B,
@@ -170,6 +177,30 @@ hipError_t launch_own_mean(const uint16_t *K, int64_t k_seq_stride, const int32_
 hipError_t launch_own_super(const uint16_t *pool, int64_t pool_seq_stride, const uint16_t *own_rep,
                             const int32_t *qpos, int64_t L, int S, int T, int d, int B, int G, bool pool_max,
                             uint16_t *own_srep, hipStream_t st);
+
+// ---------------------------------------------------------------- three-level tree
+// Upper two levels of hisa_tree_index in one kernel (hisa_tree.hip): for every
+// query the top W super-blocks, then the top m blocks inside them.
+struct TreeTopArgs {
+    const uint16_t *q;        // [S*T][H][d]
+    const float *w;           // [S*T][H]
+    const int32_t *qpos;      // [S*T] or null
+    const uint16_t *K;
+    int64_t k_seq_stride;
+    int64_t L;
+    const uint16_t *pool;     // block representatives, current through row L-1
+    int64_t pool_seq_stride;
+    const uint16_t *spool;    // super-block representatives, current through row L-1
+    int64_t spool_seq_stride;
+    int S, T, H, d, B, G, W, m;
+    int pool_max;
+    int32_t *sel_blk;         // [S*T][m]: kept blocks, ascending, -1 padded
+    int32_t *out_blk;         // [S*T][m] or null
+    int32_t *out_sblk;        // [S*T][W] or null
+};
+
+bool tree_top_supported(int d, int64_t L, int B, int G, int W);
+hipError_t launch_tree_top(const TreeTopArgs &a, hipStream_t st);
 
 hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int64_t max_pos, hipStream_t st);
 
@@ -191,6 +222,7 @@ enum KernelKind {
     kKindOwnSuper,         // own super-block representatives (tree)
     kKindScoreTree,        // blocks inside the kept super-blocks (tree)
     kKindSelectTree,
+    kKindTreeTop,          // super-blocks -> top W -> blocks -> top m in one launch (tree)
     kKindCount
 };
 

@@ -126,6 +126,54 @@ __global__ __launch_bounds__(kMaxD) void pool_append_direct_kernel(
     pool[s * pool_seq_stride + b * d + col] = acc.get(rows);
 }
 
+// grid: (S).  Both levels of the three-level tree when the new rows all lie
+// in block b (B <= kDirectRows, b the cache's last block): block b is
+// recomputed as in pool_append_direct_kernel, then its super-block u = b / G,
+// whose children are the blocks u*G .. b, from their pool entries in order
+// with block b's new representative last.
+template <bool MAX>
+__global__ __launch_bounds__(kMaxD) void tree_append_one_kernel(
+        const uint16_t *__restrict__ K, int64_t k_seq_stride, int d, int B, int G, int64_t b, int64_t L_new,
+        uint16_t *__restrict__ pool, int64_t pool_seq_stride, uint16_t *__restrict__ spool,
+        int64_t spool_seq_stride) {
+    const int s = blockIdx.x;
+    const int col = threadIdx.x;
+    if (col >= d) return;
+    const int64_t r0 = b * B;
+    const int rows = static_cast<int>(((r0 + B < L_new) ? r0 + B : L_new) - r0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(K + s * k_seq_stride + r0 * d), static_cast<short>(0),
+            rows * d * 2, 0x00020000);
+    uint16_t x[kDirectRows];
+#pragma unroll
+    for (int r = 0; r < kDirectRows; ++r)
+        x[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * col, (r < rows ? r : rows - 1) * d * 2, 0);
+    // the complete children b0 .. b-1, kChildRound loads in flight per round
+    // (the first round's issued with the block's rows); a round may re-read
+    // child b0 past the last one, and such reads are not added
+    constexpr int kChildRound = 64;
+    const int64_t b0 = b / G * G;
+    const int nchild = static_cast<int>(b - b0);
+    const uint16_t *pcol = pool + s * pool_seq_stride + b0 * d + col;
+    ColumnRep<MAX> sup;
+    for (int c0 = 0; c0 < nchild; c0 += kChildRound) {
+        uint16_t y[kChildRound];
+#pragma unroll
+        for (int j = 0; j < kChildRound; ++j) y[j] = pcol[(c0 + j < nchild ? c0 + j : 0) * d];
+#pragma unroll
+        for (int j = 0; j < kChildRound; ++j)
+            if (c0 + j < nchild) sup.add(y[j]);
+    }
+    ColumnRep<MAX> acc;
+#pragma unroll
+    for (int r = 0; r < kDirectRows; ++r)
+        if (r < rows) acc.add(x[r]);
+    const uint16_t rep = acc.get(rows);
+    pool[s * pool_seq_stride + b * d + col] = rep;
+    sup.add(rep);
+    spool[s * spool_seq_stride + (b / G) * d + col] = sup.get(b - b0 + 1);
+}
+
 // grid: (nblk, S).  Recomputes blocks [blk0, blk0 + nblk) over rows < L_new.
 template <bool MAX>
 __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(
@@ -270,6 +318,18 @@ hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, in
                       B, blk0, L_new, pool, pool_seq_stride);
     return launch(kKindPoolAppend, pool_append_kernel<false>, g, dim3(kPoolThreads), 0, st, K, k_seq_stride, d, B,
                   blk0, L_new, pool, pool_seq_stride);
+}
+
+bool tree_append_one_supported(int B) { return B <= kDirectRows; }
+
+hipError_t launch_tree_append_one(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B, int G, int64_t blk,
+                                  int64_t L_new, bool pool_max, uint16_t *pool, int64_t pool_seq_stride,
+                                  uint16_t *spool, int64_t spool_seq_stride, hipStream_t st) {
+    if (pool_max)
+        return launch(kKindPoolAppend, tree_append_one_kernel<true>, dim3(S), dim3(kMaxD), 0, st, K, k_seq_stride, d,
+                      B, G, blk, L_new, pool, pool_seq_stride, spool, spool_seq_stride);
+    return launch(kKindPoolAppend, tree_append_one_kernel<false>, dim3(S), dim3(kMaxD), 0, st, K, k_seq_stride, d, B,
+                  G, blk, L_new, pool, pool_seq_stride, spool, spool_seq_stride);
 }
 
 hipError_t launch_own_mean(const uint16_t *K, int64_t k_seq_stride, const int32_t *qpos,

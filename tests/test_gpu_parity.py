@@ -265,6 +265,8 @@ TREE_CASES = [
     ("G256_long_super", 1, 40000, 4, 16, 64, 16, 256, 3, 40, 256, "clustered", True, "mean"),
     ("max_pool_G16", 2, 20000, 4, 64, 128, 128, 16, 2, 12, 600, "clustered", True, "max"),
     ("many_queries_G32", 1, 30000, 64, 16, 64, 64, 32, 4, 10, 200, "gaussian", False, "mean"),
+    # more than 2048 super-blocks: the levels run as separate score / select launches
+    ("general_2500_super", 1, 40000, 4, 16, 64, 16, 1, 8, 30, 256, "gaussian", True, "mean"),
     # more than 32768 candidate blocks at level 2 and tokens at level 3: chunked selection
     ("chunked_levels", 1, 600000, 2, 4, 64, 16, 128, 280, 2100, 512, "gaussian", True, "mean"),
 ]
