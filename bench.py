@@ -119,6 +119,9 @@ def kernel_models(case, blocks, tree=None, sblocks=None):
         models["score_tree"] = dict(bytes=int(ntb.sum() * row + qw), flops=int(2 * H * d * ntb.sum()))
         models["select_tree"] = dict(bytes=int(ntb.sum() * 4 + S * T * m * 4), flops=0)
         models["own_super"] = dict(bytes=int(((t // B) - st * G + 1).sum() * row), flops=0)
+        # the one-launch form of the upper two levels (tree_top_kernel)
+        models["tree_top"] = dict(bytes=int((ns.sum() + ntb.sum()) * row + qw + S * T * m * 4),
+                                  flops=int(2 * H * d * (ns.sum() + ntb.sum())))
         per_query_hisa = (ns.sum() + ntb.sum() + cand.sum()) * row + qw + S * T * k * 4
     return models, int(per_query_hisa), int(cand.sum())
 
