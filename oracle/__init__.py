@@ -1,4 +1,4 @@
-"""CPU oracle for the HISA and flat DSA indexers -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the HISA and flat DSA indexers and the sparse attention after them -- TEST INFRASTRUCTURE ONLY.
 
 Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
 leg may import this package.  The product path never calls it.
@@ -19,4 +19,6 @@ from .oracle import (  # noqa: F401
     tree_super_scores,
     hisa_batch,
     flat_batch,
+    sparse_attention,
+    sparse_attention_batch,
 )

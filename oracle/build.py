@@ -4,13 +4,13 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "hisa_oracle.c")
+SRCS = [os.path.join(HERE, "hisa_oracle.c"), os.path.join(HERE, "attention_oracle.c")]
 LIB = os.path.join(HERE, "libhisa_oracle.so")
 
 
 def build(verbose: bool = False) -> str:
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-Wall", "-Wextra", "-shared", "-fPIC", "-o", LIB + ".tmp", SRC, "-lm"]
+           "-Wall", "-Wextra", "-shared", "-fPIC", "-o", LIB + ".tmp", *SRCS, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

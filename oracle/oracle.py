@@ -1,4 +1,4 @@
-"""ctypes wrapper over the C oracle (oracle/hisa_oracle.c) -- TEST INFRASTRUCTURE ONLY.
+"""ctypes wrapper over the C oracle (oracle/hisa_oracle.c, oracle/attention_oracle.c) -- TEST INFRASTRUCTURE ONLY.
 
 Arguments are numpy arrays; bf16 tensors are passed as uint16 bit patterns.
 Every function here only marshals arguments; all arithmetic is in the C file.
@@ -66,6 +66,12 @@ def load():
     lib.oracle_flat_batch.restype = I
     lib.oracle_flat_batch.argtypes = [_u16p, _f32p, _i32p, _u16p, I64, I64, I, I, I, I, I,
                                       _i32p, I, _i32p, _f32p]
+    lib.oracle_sparse_attention.restype = I
+    lib.oracle_sparse_attention.argtypes = [_u16p, I, I, I, _u16p, I64, I64, _i32p, I, C.c_double, _f64p, _f64p,
+                                            _f64p]
+    lib.oracle_sparse_attention_batch.restype = I
+    lib.oracle_sparse_attention_batch.argtypes = [_u16p, I, I, I, I, I, _u16p, I64, I64, I64, _i32p, I,
+                                                  C.c_double, _i32p, I, _f64p, _f64p, _f64p]
     lib.oracle_num_threads.restype = I
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -268,3 +274,40 @@ def flat_batch(q, w, qpos, K, L: int, k: int, sel=None):
     if r != 0:
         raise ValueError("oracle_flat_batch failed (bad position or out of memory)")
     return idx, sc
+
+
+def sparse_attention(q, kv, idx, Dv: int, scale: float, L: int | None = None):
+    """Attention of one query q [Ha, Dk] over the listed tokens idx [k] of the latent cache kv
+    [L, >= Dk] (key = first Dk entries of a row, value = first Dv).  Entries outside [0, L) are
+    skipped.  Returns (out [Ha, Dv], lse [Ha], absw [Ha, Dv]) in fp64."""
+    q, kv, idx = _c(q, np.uint16), _c(kv, np.uint16), _c(idx, np.int32)
+    Ha, Dk = q.shape
+    L = kv.shape[0] if L is None else L
+    out = np.zeros((Ha, Dv), dtype=np.float64)
+    absw = np.zeros((Ha, Dv), dtype=np.float64)
+    lse = np.zeros(Ha, dtype=np.float64)
+    st = load().oracle_sparse_attention(_p(q, _u16p), Ha, Dk, Dv, _p(kv, _u16p), kv.shape[1], L,
+                                        _p(idx, _i32p), len(idx), float(scale), _p(out, _f64p), _p(lse, _f64p),
+                                        _p(absw, _f64p))
+    if st != 0:
+        raise MemoryError("oracle_sparse_attention failed")
+    return out, lse, absw
+
+
+def sparse_attention_batch(q, kv, idx, Dv: int, scale: float, L: int, sel=None):
+    """Batch form: q [S, T, Ha, Dk], kv [S, L_cap, row], idx [S, T, k]; returns (out [S,T,Ha,Dv],
+    lse [S,T,Ha], absw [S,T,Ha,Dv]) (rows not in sel are left zero)."""
+    q, kv, idx = _c(q, np.uint16), _c(kv, np.uint16), _c(idx, np.int32)
+    S, T, Ha, Dk = q.shape
+    k = idx.shape[-1]
+    out = np.zeros((S, T, Ha, Dv), dtype=np.float64)
+    absw = np.zeros((S, T, Ha, Dv), dtype=np.float64)
+    lse = np.zeros((S, T, Ha), dtype=np.float64)
+    s, n = _sel(sel, S, T)
+    st = load().oracle_sparse_attention_batch(_p(q, _u16p), S, T, Ha, Dk, Dv, _p(kv, _u16p),
+                                              kv.shape[1] * kv.shape[2], kv.shape[2], L, _p(idx, _i32p), k,
+                                              float(scale), None if s is None else _p(s, _i32p), n,
+                                              _p(out, _f64p), _p(lse, _f64p), _p(absw, _f64p))
+    if st != 0:
+        raise MemoryError("oracle_sparse_attention_batch failed")
+    return out, lse, absw

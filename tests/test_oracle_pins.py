@@ -582,3 +582,113 @@ def test_super_pool_special_cases(orc):
     f = bf16_to_f32(K)
     for u in range(sp.shape[1]):
         np.testing.assert_array_equal(sp[:, u], f[:, u * 64:min(700, u * 64 + 64)].max(axis=1))
+
+
+# ---------------------------------------------------------------- sparse attention over the selected set
+
+def _ln(x):
+    """"ln<n>" -> ln n; "-inf" -> -inf."""
+    return -math.inf if x == "-inf" else math.log(float(x[2:]))
+
+
+def test_golden_attention_example(orc):
+    g = json.load(open(os.path.join(os.path.dirname(GOLDEN), "attention_example.json")))
+    kv = bf16_bits(np.array(g["kv"], dtype=np.float32))
+    q = bf16_bits(np.array(g["q"], dtype=np.float32))
+    scale = math.log(3.0)
+    for case in g["cases"]:
+        out, lse, absw = orc.sparse_attention(q, kv, np.array(case["idx"]), g["Dv"], scale, L=g["L"])
+        np.testing.assert_allclose(out, np.array(case["out"]), rtol=1e-12, atol=1e-12)
+        for h, x in enumerate(case["lse"]):
+            want = _ln(x)
+            if math.isinf(want):
+                assert lse[h] == -math.inf
+            else:
+                assert abs(lse[h] - want) < 1e-12
+        # every value here is >= 0, so the weighted magnitudes are the output itself
+        np.testing.assert_allclose(absw, np.abs(np.array(case["out"])), rtol=1e-12, atol=1e-12)
+
+
+def _attn_inputs(seed, L=300, Ha=4, Dk=96, k=40):
+    rng = np.random.default_rng(seed)
+    kv = bf16_bits(rng.standard_normal((L, Dk)).astype(np.float32))
+    q = bf16_bits((rng.standard_normal((Ha, Dk)) * 0.3).astype(np.float32))
+    idx = rng.choice(L, size=k, replace=False).astype(np.int32)
+    return q, kv, idx
+
+
+def test_attention_single_token_is_its_value(orc):
+    q, kv, idx = _attn_inputs(1)
+    for j in (0, 17, 299):
+        out, lse, _ = orc.sparse_attention(q, kv, np.array([-1, j, -1]), 64, 0.125)
+        v = bf16_to_f32(kv[j, :64]).astype(np.float64)
+        for h in range(q.shape[0]):
+            np.testing.assert_array_equal(out[h], v)
+            dot = float(np.dot(bf16_to_f32(q[h]).astype(np.float64), bf16_to_f32(kv[j]).astype(np.float64)))
+            assert abs(lse[h] - 0.125 * dot) < 1e-12
+
+
+def test_attention_zero_query_is_the_mean_value(orc):
+    q, kv, idx = _attn_inputs(2)
+    q[:] = 0
+    out, lse, _ = orc.sparse_attention(q, kv, idx, 48, 1.0)
+    mean = bf16_to_f32(kv[idx, :48]).astype(np.float64).mean(axis=0)
+    for h in range(q.shape[0]):
+        np.testing.assert_allclose(out[h], mean, rtol=0, atol=1e-13)
+        assert abs(lse[h] - math.log(len(idx))) < 1e-12
+
+
+def test_attention_large_scale_is_the_best_token(orc):
+    # with an overwhelming scale the softmax is the indicator of the best score
+    q, kv, idx = _attn_inputs(3)
+    f = bf16_to_f32(kv).astype(np.float64)
+    out, _, _ = orc.sparse_attention(q, kv, idx, 64, 1e5)
+    for h in range(q.shape[0]):
+        s = f[idx] @ bf16_to_f32(q[h]).astype(np.float64)
+        best = idx[int(np.argmax(s))]
+        np.testing.assert_array_equal(out[h], f[best, :64])
+
+
+def test_attention_order_padding_and_convexity(orc):
+    q, kv, idx = _attn_inputs(4)
+    out, lse, absw = orc.sparse_attention(q, kv, idx, 64, 0.2)
+    perm = np.concatenate([idx[::-1], [-1, -1, 10_000]]).astype(np.int32)
+    out2, lse2, _ = orc.sparse_attention(q, kv, perm, 64, 0.2)
+    np.testing.assert_allclose(out2, out, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-12)
+    v = bf16_to_f32(kv[idx, :64]).astype(np.float64)
+    assert np.all(out >= v.min(axis=0) - 1e-12) and np.all(out <= v.max(axis=0) + 1e-12)
+    assert np.all(absw >= np.abs(out) - 1e-12)
+
+
+def test_attention_values_are_the_first_dv_entries(orc):
+    # entries past Dv take part in the scores only: where the query is zero they change nothing
+    q, kv, idx = _attn_inputs(5)
+    q[:, 64:] = 0
+    out, lse, _ = orc.sparse_attention(q, kv, idx, 64, 0.3)
+    kv2 = kv.copy()
+    kv2[:, 64:] = bf16_bits(np.full((kv.shape[0], kv.shape[1] - 64), 7.0, dtype=np.float32))
+    out2, lse2, _ = orc.sparse_attention(q, kv2, idx, 64, 0.3)
+    np.testing.assert_array_equal(out2, out)
+    np.testing.assert_array_equal(lse2, lse)
+    # and where the query is not, they move the weights but never enter the output
+    q[:, 64:] = bf16_bits(np.full((q.shape[0], kv.shape[1] - 64), 0.5, dtype=np.float32))
+    out3, _, _ = orc.sparse_attention(q, kv2, idx, 64, 0.3)
+    v = bf16_to_f32(kv[idx, :64]).astype(np.float64)
+    assert np.all(out3 >= v.min(axis=0) - 1e-12) and np.all(out3 <= v.max(axis=0) + 1e-12)
+
+
+def test_attention_batch_equals_single_queries(orc):
+    rng = np.random.default_rng(6)
+    S, T, Ha, Dk, L, k = 2, 3, 4, 64, 200, 30
+    kv = bf16_bits(rng.standard_normal((S, L, Dk)).astype(np.float32))
+    q = bf16_bits(rng.standard_normal((S, T, Ha, Dk)).astype(np.float32))
+    idx = np.stack([[rng.choice(L, size=k, replace=False) for _ in range(T)] for _ in range(S)]).astype(np.int32)
+    idx[0, 1, 5:] = -1
+    out, lse, absw = orc.sparse_attention_batch(q, kv, idx, 48, 0.1, L)
+    for s in range(S):
+        for i in range(T):
+            o1, l1, a1 = orc.sparse_attention(q[s, i], kv[s], idx[s, i], 48, 0.1)
+            np.testing.assert_array_equal(out[s, i], o1)
+            np.testing.assert_array_equal(lse[s, i], l1)
+            np.testing.assert_array_equal(absw[s, i], a1)
