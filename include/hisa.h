@@ -53,8 +53,9 @@
 extern "C" {
 #endif
 
-#define HISA_ABI_VERSION 4   /* 2: adds hisa_append_index; 3: adds the *_mode calls (max pooling);
-                                4: adds the three-level tree calls hisa_tree_* */
+#define HISA_ABI_VERSION 5   /* 2: adds hisa_append_index; 3: adds the *_mode calls (max pooling);
+                                4: adds the three-level tree calls hisa_tree_*;
+                                5: adds hisa_sparse_attention */
 
 #if defined(__GNUC__)
 #define HISA_API __attribute__((visibility("default")))
@@ -257,6 +258,44 @@ HISA_API int hisa_tree_index(const uint16_t *q, const float *w, const int32_t *q
                              int S, int T, int H, int d, int B, int G, int W, int m, int k,
                              int32_t *out_idx, float *out_score, int32_t *out_blk, int32_t *out_sblk,
                              void *ws, size_t ws_bytes, int pool_kind, void *stream);
+
+/*
+ * hisa_sparse_attention -- the step after the indexer: attention computed
+ * only over each query's selected tokens (arXiv abstract, mlsanity.com page:
+ * the downstream sparse attention attends over the selected subset, the
+ * token-level top-k set the Sparse MLA operator consumes).  The pages give no
+ * formula for that operator; here it is softmax attention restricted to the
+ * set, in the decode form of multi-head latent attention: every token stores
+ * one latent row shared by all heads, whose first Dk entries are its key and
+ * whose first Dv entries (Dv <= Dk) are its value.  For head h of query
+ * (s, i) and the listed tokens j = idx[s][i][0..k) with 0 <= j < L (other
+ * entries, such as the -1 padding of the indexers' outputs, are skipped; a
+ * token listed twice counts twice):
+ *     s_j   = scale * (q_h . kv_j[0..Dk))          (bf16 x bf16, fp32 accumulation)
+ *     out_h = sum_j softmax(s)_j kv_j[0..Dv)
+ *     lse_h = ln sum_j exp(s_j)
+ * An empty set gives out = 0 and lse = -inf.
+ *   Precision: each softmax weight is rounded to bf16 for the value product
+ *   (fp32 accumulation) and the output is normalised by the sum of the
+ *   rounded weights, so it is a convex combination of the values with
+ *   weights within 2^-8 (relative) of the exact softmax.
+ *   q      bf16 [S][T][Ha][Dk], contiguous.
+ *   kv     bf16 latent cache: row j of sequence s at kv + s*kv_seq_stride +
+ *          j*kv_row_stride (kv_row_stride >= Dk, a multiple of 8; for S > 1
+ *          kv_seq_stride >= L*kv_row_stride).
+ *   idx    int32 [S][T][k] (e.g. out_idx of hisa_index).
+ *   out    fp32 [S][T][Ha][Dv]; lse fp32 [S][T][Ha] or NULL.
+ *   ws     at least hisa_sparse_attention_workspace(...) bytes (partial
+ *          results when a query's set is split over several workgroups).
+ *   Supported: (Dk, Dv) in {(64,64), (128,128), (192,128), (576,512)};
+ *   Ha a multiple of 16 up to 128; 1 <= k <= 2^20; S*T <= 65535;
+ *   1 <= L < 2^31; scale finite.
+ */
+HISA_API size_t hisa_sparse_attention_workspace(int S, int T, int Ha, int Dk, int Dv, int k);
+HISA_API int hisa_sparse_attention(const uint16_t *q, const uint16_t *kv, int64_t kv_seq_stride,
+                                   int64_t kv_row_stride, int64_t L, const int32_t *idx,
+                                   int S, int T, int Ha, int Dk, int Dv, int k, float scale,
+                                   float *out, float *lse, void *ws, size_t ws_bytes, void *stream);
 
 /* Bytes of device workspace dsa_flat_index needs for these sizes (0 on bad sizes). */
 HISA_API size_t dsa_flat_workspace(int S, int T, int H, int d, int64_t L, int k);

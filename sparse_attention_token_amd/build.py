@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhisa.so")
-SOURCES = ["hisa_abi.hip", "pool.hip", "score.hip", "select.hip", "hisa_fused.hip", "hisa_prefill.hip", "hisa_tree.hip"]
+SOURCES = ["hisa_abi.hip", "pool.hip", "score.hip", "select.hip", "hisa_fused.hip", "hisa_prefill.hip", "hisa_tree.hip", "attention.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -206,6 +206,7 @@ const char *const kKindNames[kKindCount] = {
     "pool_append", "own_mean", "score_blocks", "select_blocks",
     "score_refine", "select_refine", "score_flat", "select_flat",
     "index_decode", "bucket", "own_super", "score_tree", "select_tree", "tree_top",
+    "sparse_attention", "attention_combine",
 };
 
 }  // namespace
@@ -601,6 +602,76 @@ int hisa_tree_index(const uint16_t *q, const float *w, const int32_t *qpos, cons
 }
 
 
+
+}  // extern "C"
+
+namespace {
+
+int check_attention_shape(int S, int T, int Ha, int Dk, int Dv, int k) {
+    if (S < 1 || T < 1 || Ha < 1 || Dk < 1 || Dv < 1 || k < 1) return HISA_ERR_ARG;
+    if (!attention_shape_supported(Dk, Dv)) return HISA_ERR_UNSUPPORTED;
+    if (Ha % 16 != 0 || Ha > 128) return HISA_ERR_UNSUPPORTED;
+    if (k > (1 << 20) || static_cast<int64_t>(S) * T > 65535) return HISA_ERR_UNSUPPORTED;
+    return HISA_OK;
+}
+
+struct AttnLayout {
+    int nsplit, tps;
+    size_t part_o, part_m, part_l, total;
+};
+
+AttnLayout attention_layout(int S, int T, int Ha, int Dv, int k) {
+    AttnLayout l{};
+    attention_split(S * T, Ha, k, l.nsplit, l.tps);
+    size_t off = 0;
+    if (l.nsplit > 1) {
+        const size_t rows = static_cast<size_t>(S) * T * l.nsplit * Ha;
+        l.part_o = off; off = align_up(off + rows * Dv * sizeof(float), kAlign);
+        l.part_m = off; off = align_up(off + rows * sizeof(float), kAlign);
+        l.part_l = off; off = align_up(off + rows * sizeof(float), kAlign);
+    }
+    l.total = off + kAlign;
+    return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hisa_sparse_attention_workspace(int S, int T, int Ha, int Dk, int Dv, int k) {
+    if (check_attention_shape(S, T, Ha, Dk, Dv, k) != HISA_OK) return 0;
+    return attention_layout(S, T, Ha, Dv, k).total;
+}
+
+int hisa_sparse_attention(const uint16_t *q, const uint16_t *kv, int64_t kv_seq_stride, int64_t kv_row_stride,
+                          int64_t L, const int32_t *idx, int S, int T, int Ha, int Dk, int Dv, int k, float scale,
+                          float *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    int st = check_attention_shape(S, T, Ha, Dk, Dv, k);
+    if (st != HISA_OK) return st;
+    if (L < 1) return HISA_ERR_ARG;
+    if (L >= (int64_t{1} << 31)) return HISA_ERR_UNSUPPORTED;
+    if (!q || !kv || !idx || !out || !aligned16(q) || !aligned16(kv) || !aligned16(out)) return HISA_ERR_ARG;
+    if (kv_row_stride < Dk || (kv_row_stride & 7) != 0) return HISA_ERR_ARG;
+    if (kv_seq_stride < 0 || (kv_seq_stride & 7) != 0 || (S > 1 && kv_seq_stride < L * kv_row_stride))
+        return HISA_ERR_ARG;
+    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return HISA_ERR_ARG;
+    if (!ws) return HISA_ERR_ARG;
+    const AttnLayout lay = attention_layout(S, T, Ha, Dv, k);
+    if (ws_bytes < lay.total) return HISA_ERR_WORKSPACE;
+    char *base = align_ptr(ws);
+    AttnArgs a{};
+    a.q = q; a.kv = kv; a.kv_seq_stride = kv_seq_stride; a.kv_row_stride = kv_row_stride; a.L = L;
+    a.idx = idx; a.S = S; a.T = T; a.Ha = Ha; a.Dk = Dk; a.Dv = Dv; a.k = k;
+    a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    a.nsplit = lay.nsplit; a.tps = lay.tps; a.npair = S * T * lay.nsplit;
+    a.out = out; a.lse = lse;
+    if (lay.nsplit > 1) {
+        a.part_o = reinterpret_cast<float *>(base + lay.part_o);
+        a.part_m = reinterpret_cast<float *>(base + lay.part_m);
+        a.part_l = reinterpret_cast<float *>(base + lay.part_l);
+    }
+    return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)));
+}
 
 size_t dsa_flat_workspace(int S, int T, int H, int d, int64_t L, int k) {
     if (check_query_shape(S, T, H, d, L, k) != HISA_OK) return 0;

@@ -202,6 +202,30 @@ struct TreeTopArgs {
 bool tree_top_supported(int d, int64_t L, int B, int G, int W);
 hipError_t launch_tree_top(const TreeTopArgs &a, hipStream_t st);
 
+// ---------------------------------------------------------------- sparse attention (attention.hip)
+struct AttnArgs {
+    const uint16_t *q;        // [S*T][Ha][Dk]
+    const uint16_t *kv;       // latent rows: key = first Dk entries, value = first Dv
+    int64_t kv_seq_stride;
+    int64_t kv_row_stride;
+    int64_t L;
+    const int32_t *idx;       // [S*T][k], entries outside [0, L) skipped
+    int S, T, Ha, Dk, Dv, k;
+    float scale_log2;         // scale * log2(e)
+    int nsplit;               // workgroups per (query, head group) along the set
+    int tps;                  // set entries per split (a multiple of 64)
+    int npair;                // S*T*nsplit
+    float *out;               // [S*T][Ha][Dv]
+    float *lse;               // [S*T][Ha] or null
+    float *part_o;            // ws [S*T*nsplit][Ha][Dv] (nsplit > 1)
+    float *part_m;            // ws [S*T*nsplit][Ha]
+    float *part_l;            // ws [S*T*nsplit][Ha]
+};
+
+bool attention_shape_supported(int Dk, int Dv);
+void attention_split(int nq, int Ha, int k, int &nsplit, int &tps);
+hipError_t launch_attention(const AttnArgs &a, hipStream_t st);
+
 hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int64_t max_pos, hipStream_t st);
 
 // max_n: an upper bound on the candidate count of every query (sizes the per-thread chunk)
@@ -223,6 +247,8 @@ enum KernelKind {
     kKindScoreTree,        // blocks inside the kept super-blocks (tree)
     kKindSelectTree,
     kKindTreeTop,          // super-blocks -> top W -> blocks -> top m in one launch (tree)
+    kKindAttention,        // sparse attention over the selected set
+    kKindAttnCombine,      // merge of the attention's split partials
     kKindCount
 };
 

@@ -73,6 +73,11 @@ def lib():
     L.hisa_tree_index.restype = i32
     L.hisa_tree_index.argtypes = [vp, vp, vp, vp, i64, i64, vp, i64, vp, i64, i32, i32, i32, i32, i32, i32,
                                   i32, i32, i32, vp, vp, vp, vp, vp, sz, i32, vp]
+    L.hisa_sparse_attention_workspace.restype = sz
+    L.hisa_sparse_attention_workspace.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.hisa_sparse_attention.restype = i32
+    L.hisa_sparse_attention.argtypes = [vp, vp, i64, i64, i64, vp, i32, i32, i32, i32, i32, i32, C.c_float,
+                                        vp, vp, vp, sz, vp]
     L.dsa_flat_workspace.restype = sz
     L.dsa_flat_workspace.argtypes = [i32, i32, i32, i32, i64, i32]
     L.dsa_flat_index.restype = i32
@@ -336,6 +341,45 @@ def dsa_flat_index(q, w, K, L: int, k: int, qpos=None, *, want_scores: bool = Tr
                               ws.numel() * ws.element_size(), _stream(dev))
     _check("dsa_flat_index", st)
     return out_idx, out_score
+
+
+def hisa_sparse_attention_workspace(S, T, Ha, Dk, Dv, k) -> int:
+    return int(lib().hisa_sparse_attention_workspace(S, T, Ha, Dk, Dv, k))
+
+
+def hisa_sparse_attention(q, kv, L: int, idx, Dv: int, scale: float, *, want_lse: bool = True, out=None,
+                          lse=None, workspace=None):
+    """Attention of q [S, T, Ha, Dk] over the listed tokens idx [S, T, k] (int32; entries outside
+    [0, L) skipped) of the latent cache kv [S, L_cap, row] (key = first Dk entries of a row, value
+    = first Dv).  Returns (out [S, T, Ha, Dv] fp32, lse [S, T, Ha] fp32 | None)."""
+    _bf16(q, "q")
+    _bf16(kv, "kv")
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [S, T, Ha, Dk] tensor")
+    S, T, Ha, Dk = q.shape
+    if kv.dim() != 3 or kv.shape[0] != S or kv.shape[1] < L or kv.shape[2] < Dk or kv.stride(2) != 1:
+        raise ValueError("kv must be [S, >= L, >= Dk] with unit-stride rows")
+    if idx.dtype != torch.int32 or idx.dim() != 3 or tuple(idx.shape[:2]) != (S, T) or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 [S, T, k] tensor")
+    k = idx.shape[2]
+    dev = q.device
+    for t in (kv, idx):
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    if out is None:
+        out = torch.empty((S, T, Ha, Dv), dtype=torch.float32, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((S, T, Ha), dtype=torch.float32, device=dev)
+    nbytes = hisa_sparse_attention_workspace(S, T, Ha, Dk, Dv, k)
+    if nbytes == 0:
+        _check("hisa_sparse_attention", lib().hisa_sparse_attention(None, None, 0, 0, int(L), None, S, T, Ha, Dk,
+                                                                    Dv, k, float(scale), None, None, None, 0, None))
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().hisa_sparse_attention(_ptr(q), _ptr(kv), kv.stride(0), kv.stride(1), int(L), _ptr(idx), S, T, Ha,
+                                     Dk, Dv, k, float(scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(dev))
+    _check("hisa_sparse_attention", st)
+    return out, lse
 
 
 # ---------------------------------------------------------------- profiler

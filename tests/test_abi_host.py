@@ -45,7 +45,8 @@ def test_header_declares_the_entry_points():
     for n in ("hisa_pool_append", "hisa_index", "hisa_append_index", "dsa_flat_index",
               "hisa_pool_append_mode", "hisa_index_mode", "hisa_append_index_mode",
               "hisa_index_workspace", "dsa_flat_workspace", "hisa_status_string", "hisa_abi_version",
-              "hisa_tree_append", "hisa_tree_index", "hisa_tree_index_workspace"):
+              "hisa_tree_append", "hisa_tree_index", "hisa_tree_index_workspace",
+              "hisa_sparse_attention", "hisa_sparse_attention_workspace"):
         assert n in names
 
 
@@ -55,7 +56,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hisa_abi_version() == 4
+    assert lib.hisa_abi_version() == 5
     for code in (OK, ARG, UNSUP, WS, HIP, 12345):
         assert isinstance(lib.hisa_status_string(code), bytes)
     assert lib.hisa_status_string(WS) != lib.hisa_status_string(ARG)
