@@ -59,6 +59,9 @@ def parse():
     p.add_argument("--sequences", type=int, default=None, metavar="S",
                    help="batch size of a decode workload (1..3) in place of its own, for a batch "
                         "sweep; the line then names the workload with an _S<n> suffix")
+    p.add_argument("--attention", action="store_true",
+                   help="also time the sparse attention over the indexer's output (latent rows of 576 entries, "
+                        "512-entry values, 128 heads)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB three times (the known-size "
                         "reference that scales the HBM byte counters) and exit")
@@ -146,6 +149,86 @@ def traffic_from_profiles(kernel, workload_name):
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+# ---------------------------------------------------------------- sparse attention after the indexer
+
+ATT_HEADS, ATT_DK, ATT_DV = 128, 576, 512      # the latent decode shape of multi-head latent attention
+
+
+def time_attention(hisa, case, idx, time_graphs_fn, steps, dev, hisa_step, R_index, want_cpu):
+    """Time hisa_sparse_attention over the index set idx of this workload, on a synthetic latent
+    cache of the same length, and the indexer step followed by the attention."""
+    import torch
+
+    S, T, L, k = case.S, case.T, case.L, case.k
+    nq = S * T
+    rng = np.random.default_rng(7)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    replica_bytes = S * L * ATT_DK * 2
+    n_valid = int((idx >= 0).sum().item())
+    touched = n_valid * ATT_DK * 2
+    # replicas so that one cycle touches more than the last-level cache, within 16 GiB
+    R = max(1, min(32, math.ceil(512 * 2**20 / max(touched, 1)), (16 * 2**30) // replica_bytes))
+    kvs = [torch.randn((S, L, ATT_DK), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+           for _ in range(R)]
+    qa = torch.from_numpy((rng.standard_normal((S, T, ATT_HEADS, ATT_DK)) * 0.05).astype(np.float32)).to(dev)
+    qa = qa.to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(ATT_DK)
+    out = torch.empty((S, T, ATT_HEADS, ATT_DV), dtype=torch.float32, device=dev)
+    lse = torch.empty((S, T, ATT_HEADS), dtype=torch.float32, device=dev)
+    ws = torch.empty(hisa.hisa_sparse_attention_workspace(S, T, ATT_HEADS, ATT_DK, ATT_DV, k), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+    log(f"attention: {R} latent replicas ({R * replica_bytes / 2**30:.2f} GiB), {n_valid} selected rows per call")
+
+    def att_step(r):
+        hisa.hisa_sparse_attention(qa, kvs[r % R], L, idx, ATT_DV, scale, out=out, lse=lse, workspace=ws)
+
+    att_steps = steps if T == 1 else max(R, min(steps, 20))
+    att_ms = time_graphs_fn(att_step, att_steps, 2, "sparse attention", R_override=R)
+
+    def both(r):
+        hisa_step(r % R_index)
+        hisa.hisa_sparse_attention(qa, kvs[r % R], L, idx, ATT_DV, scale, out=out, lse=lse, workspace=ws)
+    both_ms = time_graphs_fn(both, att_steps, 2, "indexer step + attention", R_override=max(R, R_index))
+
+    # per-kernel durations
+    hisa.profile_enable(64)
+    for i in range(min(8, R)):
+        att_step(i)
+    res = hisa.profile_read()
+    hisa.profile_enable(0)
+    kern = {name: {"avg_us": tot * 1e3 / cnt, "launches_per_call": cnt / min(8, R)} for name, (tot, cnt) in res.items()}
+    byts = n_valid * ATT_DK * 2 + nq * ATT_HEADS * (ATT_DK * 2 + ATT_DV * 4 + 4)
+    flops = 2 * ATT_HEADS * (ATT_DK + ATT_DV) * n_valid
+    main_us = kern.get("sparse_attention", {}).get("avg_us")
+    roof = None
+    if main_us:
+        gbs = byts / (main_us * 1e-6) / 1e9
+        tfs = flops / (main_us * 1e-6) / 1e12
+        roof = {"kernel": "sparse_attention", "avg_launch_us": main_us, "hbm_achieved": gbs,
+                "hbm_frac": gbs / HBM_PEAK_GBS, "mfma_achieved": tfs, "mfma_frac": tfs / BF16_PEAK_TFLOPS,
+                "bound": "hbm" if flops / byts < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma",
+                "algorithmic_bytes_per_launch": byts, "algorithmic_flops_per_launch": flops}
+    cpu = None
+    if want_cpu:
+        import oracle
+
+        kv0 = kvs[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        q0 = qa.view(torch.int16).cpu().numpy().view(np.uint16)
+        idx0 = idx.cpu().numpy()
+        sel = np.arange(min(nq, 8), dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.sparse_attention_batch(q0, kv0, idx0, ATT_DV, scale, L, sel=sel)
+        tc = time.perf_counter() - t0
+        cpu = {"value": len(sel) / tc, "unit": "queries/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"{len(sel)} of {nq} queries (fp64 C oracle) in {tc:.2f} s"}
+    return {"heads": ATT_HEADS, "Dk": ATT_DK, "Dv": ATT_DV, "selected_rows_per_call": n_valid,
+            "latent_replicas": R, "ms_per_call": att_ms, "us_per_query": att_ms * 1e3 / nq,
+            "queries_per_s": nq / (att_ms * 1e-3), "indexer_plus_attention_ms_per_step": both_ms,
+            "kernels": kern, "roofline": roof, "cpu_baseline": cpu}
 
 
 # ---------------------------------------------------------------- main
@@ -247,15 +330,16 @@ def main():
     def flat_step(r):
         hisa.dsa_flat_index(q, w, Ks[r], L, k, None, out_idx=f_idx, out_score=f_score, workspace=fws)
 
-    def time_graphs(step_fn, nsteps, nwarm, label):
+    def time_graphs(step_fn, nsteps, nwarm, label, R_override=None):
+        RR = R if R_override is None else R_override
         for i in range(nwarm):
-            step_fn(i % R)
+            step_fn(i % RR)
         torch.cuda.synchronize()
         full = torch.cuda.CUDAGraph()
         with torch.cuda.graph(full):
-            for r in range(R):
+            for r in range(RR):
                 step_fn(r)
-        rem = nsteps % R
+        rem = nsteps % RR
         part = None
         if rem:
             part = torch.cuda.CUDAGraph()
@@ -268,7 +352,7 @@ def main():
         e1 = torch.cuda.Event(enable_timing=True)
         w0 = time.perf_counter()
         e0.record()
-        for _ in range(nsteps // R):
+        for _ in range(nsteps // RR):
             full.replay()
         if part is not None:
             part.replay()
@@ -375,6 +459,12 @@ def main():
         roofline["avg_launch_us"] = hisa_kern[dom]["avg_us"]
         roofline["traffic"] = traffic_from_profiles(dom, case.name)
 
+    # ---- the sparse attention over the indexer's output (opt-in)
+    attention = None
+    if args.attention:
+        attention = time_attention(hisa, case, idx_h, time_graphs_fn=time_graphs, steps=steps, dev=dev,
+                                   hisa_step=hisa_step, R_index=R, want_cpu=not args.no_cpu)
+
     # ---- CPU oracle baseline (bounded sample of the same workload)
     cpu = None
     if not args.no_cpu:
@@ -446,6 +536,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "attention": attention,
     }
     print(json.dumps(res), flush=True)
 

@@ -10,22 +10,23 @@
 //     lse_h = ln sum_j exp(s_j).
 //
 // One workgroup (4 waves) takes one query, a group of HG = 16*HT heads and a
-// run of the set, in steps of 64 tokens:
-//   1. the step's 64 latent rows are gathered into LDS (16-byte loads; rows
+// run of the set, in steps of 64/HT tokens:
+//   1. the step's latent rows are gathered into LDS (16-byte loads; rows
 //      padded to Dk + 8 elements so 16 consecutive rows start on distinct
-//      banks);
-//   2. wave w scores tokens 16w..16w+15 against the group's heads:
-//      S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = the token rows from LDS,
-//      M = tokens; B = q, held in registers for the whole run, N = heads), so
-//      each latent row is read from LDS once per workgroup;
+//      banks); the next step's rows are loaded into registers while the
+//      current step is computed;
+//   2. each wave scores one 16-token tile of the step against one 16-head
+//      tile: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = the token rows
+//      from LDS, M = tokens; B = q, held in registers for the whole run,
+//      N = heads);
 //   3. online softmax in the exp2 domain: the step's maximum per head is
 //      combined across the waves through LDS, P = exp2(s - m) is rounded to
 //      bf16 and written to LDS as P^T [head][token];
 //   4. wave w accumulates its quarter of the value columns for every head:
 //      O^T += V^T P^T (A = V^T, read with the gfx950 transposing LDS load
-//      ds_read_b64_tr_b16 straight from the token-major rows; B = P^T; K = 64
-//      tokens).  O^T keeps one head per lane column, so the per-head rescale
-//      of the online softmax is a per-lane scalar.
+//      ds_read_b64_tr_b16 straight from the token-major rows; B = P^T; K = the
+//      step's tokens).  O^T keeps one head per lane column, so the per-head
+//      rescale of the online softmax is a per-lane scalar.
 // The denominator sums the bf16-rounded weights, so the result is an exact
 // convex combination of the values with weights within a bf16 rounding of the
 // softmax.  When the set is split over several workgroups (few queries), each
@@ -38,8 +39,7 @@ namespace hisa {
 namespace {
 
 constexpr int kAttnThreads = 256;
-constexpr int kAttnStep = 64;                 // tokens per step
-constexpr int kAttnPStride = kAttnStep + 8;   // P^T row stride (elements)
+constexpr int kAttnStep = 64;                 // splits hold whole multiples of this many entries
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -80,28 +80,41 @@ template <int HT, int KSK, int DVW>
 struct AttnLds {
     static constexpr int kDk = 32 * KSK;
     static constexpr int kRowStride = kDk + 8;
-    uint16_t rows[kAttnStep * kRowStride];
-    uint16_t pt[16 * HT * kAttnPStride];
-    float wmax[4][16 * HT];
-    float wsum[4][16 * HT];
-    int valid[kAttnStep];
+    static constexpr int kTT = 4 / HT;                  // token tiles per step (one per wave and head tile)
+    static constexpr int kStep = 16 * kTT;              // tokens per step: 32 (HT = 2) or 64 (HT = 1)
+    static constexpr int kPStride = kStep + 8;
+    uint16_t rows[kStep * kRowStride];
+    uint16_t pt[16 * HT * kPStride];
+    float wmax[kTT][16 * HT];
+    float wsum[kTT][16 * HT];
+    int32_t tok[2][kStep];                              // token of each row of a step, -1 if none
 };
 
 // grid: attn_grid(npair, nhg) with npair = S*T*nsplit; workgroup (pair, hg)
 // takes query pair / nsplit, heads hg*16*HT.., and set entries
-// [split*tps, min(k, split*tps + tps)).
+// [split*tps, min(k, split*tps + tps)).  Wave w scores token tile w % kTT of
+// each step against head tile w / kTT, and accumulates value columns
+// 16*DVW*w .. for every head of the group.  The next step's rows are loaded
+// into registers while the current step is computed (every load is issued,
+// rows of no candidate re-read the cache's first row and are masked), and its
+// set entries one step further ahead.
 template <int HT, int KSK, int DVW>
-__global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, HT == 2 ? 2 : 1) void sparse_attn_kernel(AttnArgs a) {
     constexpr int Dk = 32 * KSK;
     constexpr int HG = 16 * HT;
     using Lds = AttnLds<HT, KSK, DVW>;
     constexpr int RS = Lds::kRowStride;
+    constexpr int TT = Lds::kTT;
+    constexpr int STEP = Lds::kStep;
+    constexpr int PS = Lds::kPStride;
+    constexpr int KST = STEP / 32;                              // value k-steps per step
     constexpr int CPR = Dk / 8;                                 // 16-byte chunks per row
-    constexpr int kPer = (kAttnStep * CPR + kAttnThreads - 1) / kAttnThreads;
+    constexpr int kPer = (STEP * CPR + kAttnThreads - 1) / kAttnThreads;
     __shared__ __attribute__((aligned(16))) Lds L;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
+    const int tt = wave % TT, hw = wave / TT;                  // this wave's token tile and head tile
     // workgroup -> (pair, head group): the head groups of one pair share an XCD
     const int nhg = a.Ha / HG;
     const int bx = blockIdx.x, x = bx & 7, j8 = bx >> 3;
@@ -113,118 +126,116 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(AttnArgs a) {
     const int s = qi / a.T;
     const int e0 = split * a.tps;
     const int e1 = min(a.k, e0 + a.tps);
+    const int nsteps = (e1 - e0 + STEP - 1) / STEP;
     const int32_t *idx = a.idx + static_cast<int64_t>(qi) * a.k;
     const uint16_t *kv = a.kv + s * a.kv_seq_stride;
 
-    // q fragments (B operand of S^T = K Q^T): lane (g, n) holds head n's 8
-    // entries 32*ks + 8g .. of each k-step
-    bf16x8 qb[HT][KSK];
+    auto entry = [&](int e) -> int32_t {                       // the set entry e as a row, or -1
+        const int32_t t = e < e1 ? idx[e] : -1;
+        return (t >= 0 && t < a.L) ? t : -1;
+    };
+    u32x4 v[kPer];
+    auto load_rows = [&](const int32_t *toks) {
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const uint16_t *qh = a.q + (static_cast<int64_t>(qi) * a.Ha + hg * HG + 16 * ht + n) * Dk;
+        for (int i = 0; i < kPer; ++i) {
+            const int c = tid + i * kAttnThreads;
+            const bool in = c < STEP * CPR;
+            const int r = in ? c / CPR : 0;
+            const int32_t t = toks[r];
+            v[i] = *reinterpret_cast<const u32x4 *>(kv + static_cast<int64_t>(t < 0 ? 0 : t) * a.kv_row_stride +
+                                                    (in ? 8 * (c - r * CPR) : 0));
+        }
+    };
+    auto store_rows = [&]() {
 #pragma unroll
-        for (int ks = 0; ks < KSK; ++ks) qb[ht][ks] = load_bf16x8(qh + 32 * ks + 8 * g);
-    }
+        for (int i = 0; i < kPer; ++i) {
+            const int c = tid + i * kAttnThreads;
+            if (c < STEP * CPR) {
+                const int r = c / CPR;
+                *reinterpret_cast<u32x4 *>(L.rows + r * RS + 8 * (c - r * CPR)) = v[i];
+            }
+        }
+    };
 
+    // q fragments of this wave's head tile (B operand of S^T = K Q^T)
+    bf16x8 qb[KSK];
+    {
+        const uint16_t *qh = a.q + (static_cast<int64_t>(qi) * a.Ha + hg * HG + 16 * hw + n) * Dk;
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks) qb[ks] = load_bf16x8(qh + 32 * ks + 8 * g);
+    }
     f32x4 oacc[DVW][HT];
 #pragma unroll
     for (int dt = 0; dt < DVW; ++dt)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) oacc[dt][ht] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float mrun[HT], lpart[HT];
+    float mrun[HT];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        mrun[ht] = -__builtin_huge_valf();
-        lpart[ht] = 0.0f;
+    for (int ht = 0; ht < HT; ++ht) mrun[ht] = -__builtin_huge_valf();
+    float lpart = 0.0f;
+
+    // prologue: entries of steps 0 and 1, rows of step 0
+    if (tid < STEP) {
+        L.tok[0][tid] = entry(e0 + tid);
+        L.tok[1][tid] = entry(e0 + STEP + tid);
     }
+    __syncthreads();
+    load_rows(L.tok[0]);
+    store_rows();
+    __syncthreads();
 
-    for (int base = e0; base < e1; base += kAttnStep) {
-        __syncthreads();                                        // the previous step's LDS reads are done
-        // ---- gather the step's rows (invalid entries: zero rows)
-        {
-            u32x4 v[kPer];
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                const int c = tid + i * kAttnThreads;
-                v[i] = u32x4{0u, 0u, 0u, 0u};
-                if (c < kAttnStep * CPR) {
-                    const int r = c / CPR;
-                    const int e = base + r;
-                    const int32_t tok = e < e1 ? idx[e] : -1;
-                    if (tok >= 0 && tok < a.L)
-                        v[i] = *reinterpret_cast<const u32x4 *>(kv + static_cast<int64_t>(tok) * a.kv_row_stride +
-                                                                8 * (c - r * CPR));
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                const int c = tid + i * kAttnThreads;
-                if (c < kAttnStep * CPR) {
-                    const int r = c / CPR;
-                    *reinterpret_cast<u32x4 *>(L.rows + r * RS + 8 * (c - r * CPR)) = v[i];
-                }
-            }
-            if (tid < kAttnStep) {
-                const int e = base + tid;
-                const int32_t tok = e < e1 ? idx[e] : -1;
-                L.valid[tid] = tok >= 0 && tok < a.L;
-            }
-        }
-        __syncthreads();
+    for (int i = 0; i < nsteps; ++i) {
+        const int cur = i & 1;
+        // ---- in flight during this step: the next step's rows, entries two steps ahead
+        if (i + 1 < nsteps) load_rows(L.tok[cur ^ 1]);
+        int32_t ahead = -1;
+        if (tid < STEP) ahead = entry(e0 + (i + 2) * STEP + tid);
 
-        // ---- scores of this wave's 16 tokens for every head of the group
-        f32x4 sacc[HT];
+        // ---- scores of token tile tt against head tile hw
+        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+        const uint16_t *krow = L.rows + (16 * tt + n) * RS + 8 * g;
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) sacc[ht] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        const uint16_t *krow = L.rows + (16 * wave + n) * RS + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < KSK; ++ks) {
-            const bf16x8 kfrag = load_bf16x8(krow + 32 * ks);
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
-                sacc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qb[ht][ks], sacc[ht], 0, 0, 0);
-        }
-        // lane (g, n): tokens 16w + 4g + r (r = 0..3), head n of each tile
+        for (int ks = 0; ks < KSK; ++ks)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(load_bf16x8(krow + 32 * ks), qb[ks], sacc, 0, 0, 0);
+        // lane (g, n): tokens 16*tt + 4g + r of the step, head n of tile hw
         bool ok[4];
+        float sv[4];
+        float mx = -__builtin_huge_valf();
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ok[r] = L.valid[16 * wave + 4 * g + r] != 0;
-        float sv[HT][4];
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            float mx = -__builtin_huge_valf();
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sv[ht][r] = ok[r] ? sacc[ht][r] * a.scale_log2 : -__builtin_huge_valf();
-                mx = fmaxf(mx, sv[ht][r]);
-            }
-            mx = rows_max(mx);
-            if (g == 0) L.wmax[wave][16 * ht + n] = mx;
+        for (int r = 0; r < 4; ++r) {
+            ok[r] = L.tok[cur][16 * tt + 4 * g + r] >= 0;
+            sv[r] = ok[r] ? sacc[r] * a.scale_log2 : -__builtin_huge_valf();
+            mx = fmaxf(mx, sv[r]);
         }
+        mx = rows_max(mx);
+        if (g == 0) L.wmax[tt][16 * hw + n] = mx;
         __syncthreads();
 
-        // ---- online softmax: new running max, rescale, P^T into LDS
+        // ---- online softmax: running max of every head tile, rescale, P^T into LDS
         float alpha[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
             float mstep = L.wmax[0][16 * ht + n];
 #pragma unroll
-            for (int w = 1; w < 4; ++w) mstep = fmaxf(mstep, L.wmax[w][16 * ht + n]);
+            for (int u = 1; u < TT; ++u) mstep = fmaxf(mstep, L.wmax[u][16 * ht + n]);
             const float mnew = fmaxf(mrun[ht], mstep);
             alpha[ht] = mnew == -__builtin_huge_valf() ? 1.0f : __builtin_amdgcn_exp2f(mrun[ht] - mnew);
             mrun[ht] = mnew;
+        }
+        {
+            const float mw = mrun[hw];
             uint32_t packed[2];
             float psum = 0.0f;
 #pragma unroll
             for (int r = 0; r < 4; r += 2) {
-                const float p0 = ok[r] ? __builtin_amdgcn_exp2f(sv[ht][r] - mnew) : 0.0f;
-                const float p1 = ok[r + 1] ? __builtin_amdgcn_exp2f(sv[ht][r + 1] - mnew) : 0.0f;
+                const float p0 = ok[r] ? __builtin_amdgcn_exp2f(sv[r] - mw) : 0.0f;
+                const float p1 = ok[r + 1] ? __builtin_amdgcn_exp2f(sv[r + 1] - mw) : 0.0f;
                 const uint16_t b0 = f32_to_bf16_rne(p0), b1 = f32_to_bf16_rne(p1);
                 psum += bf16_to_f32(b0) + bf16_to_f32(b1);
                 packed[r / 2] = static_cast<uint32_t>(b0) | (static_cast<uint32_t>(b1) << 16);
             }
-            lpart[ht] = lpart[ht] * alpha[ht] + psum;
-            *reinterpret_cast<uint2 *>(L.pt + (16 * ht + n) * kAttnPStride + 16 * wave + 4 * g) =
-                make_uint2(packed[0], packed[1]);
+            lpart = lpart * alpha[hw] + psum;
+            *reinterpret_cast<uint2 *>(L.pt + (16 * hw + n) * PS + 16 * tt + 4 * g) = make_uint2(packed[0], packed[1]);
         }
 #pragma unroll
         for (int dt = 0; dt < DVW; ++dt)
@@ -232,13 +243,12 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(AttnArgs a) {
             for (int ht = 0; ht < HT; ++ht) oacc[dt][ht] *= alpha[ht];
         __syncthreads();
 
-        // ---- O^T += V^T P^T over the step's 64 tokens (two k-steps of 32)
+        // ---- O^T += V^T P^T over the step's tokens
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < KST; ++kk) {
             bf16x8 pb[HT];
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
-                pb[ht] = load_bf16x8(L.pt + (16 * ht + n) * kAttnPStride + 32 * kk + 8 * g);
+            for (int ht = 0; ht < HT; ++ht) pb[ht] = load_bf16x8(L.pt + (16 * ht + n) * PS + 32 * kk + 8 * g);
 #pragma unroll
             for (int dt = 0; dt < DVW; ++dt) {
                 const bf16x8 va = load_vt_frag(L.rows, RS, 32 * kk + 8 * g, (wave * DVW + dt) * 16, lane);
@@ -247,34 +257,35 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(AttnArgs a) {
                     oacc[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ht], oacc[dt][ht], 0, 0, 0);
             }
         }
+        __syncthreads();                                        // rows, P^T and this step's entries are free
+        if (i + 1 < nsteps) store_rows();
+        if (tid < STEP) L.tok[cur][tid] = ahead;
+        __syncthreads();
     }
 
     // ---- the denominators: this lane's tokens, then the wave, then the workgroup
-    __syncthreads();
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const float l = rows_add(lpart[ht]);
-        if (g == 0) L.wsum[wave][16 * ht + n] = l;
+    {
+        const float l = rows_add(lpart);
+        if (g == 0) L.wsum[tt][16 * hw + n] = l;
     }
     __syncthreads();
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const int head = hg * HG + 16 * ht + n;
-        const float lsum = L.wsum[0][16 * ht + n] + L.wsum[1][16 * ht + n] + L.wsum[2][16 * ht + n] +
-                           L.wsum[3][16 * ht + n];
+        float lsum = 0.0f;
+#pragma unroll
+        for (int u = 0; u < TT; ++u) lsum += L.wsum[u][16 * ht + n];
         if (a.nsplit == 1) {
             float *orow = a.out + (static_cast<int64_t>(qi) * a.Ha + head) * a.Dv;
             const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
-            for (int dt = 0; dt < DVW; ++dt) {
-                const f32x4 o = oacc[dt][ht] * inv;
-                *reinterpret_cast<f32x4 *>(orow + (wave * DVW + dt) * 16 + 4 * g) = o;
-            }
+            for (int dt = 0; dt < DVW; ++dt)
+                *reinterpret_cast<f32x4 *>(orow + (wave * DVW + dt) * 16 + 4 * g) = oacc[dt][ht] * inv;
             if (a.lse && wave == 0 && g == 0)
                 a.lse[static_cast<int64_t>(qi) * a.Ha + head] =
                     lsum > 0.0f ? (mrun[ht] + __builtin_log2f(lsum)) * kLn2 : -__builtin_huge_valf();
         } else {
-            const int64_t prow = (static_cast<int64_t>(pair) * a.Ha + head);
+            const int64_t prow = static_cast<int64_t>(pair) * a.Ha + head;
             float *orow = a.part_o + prow * a.Dv;
 #pragma unroll
             for (int dt = 0; dt < DVW; ++dt)
@@ -288,26 +299,40 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(AttnArgs a) {
 }
 
 // grid: (S*T*Ha), Dv/4 threads: merges the nsplit partials of one (query, head).
+// The splits are read 8 at a time with every load issued before the sums.
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
+    constexpr int U = 8;
     const int qh = blockIdx.x;                      // query * Ha + head
     const int qi = qh / a.Ha, head = qh - qi * a.Ha;
     const int c = threadIdx.x * 4;
     if (c >= a.Dv) return;
+    const int64_t row0 = static_cast<int64_t>(qi) * a.nsplit * a.Ha + head;    // split sp at row0 + sp*Ha
     float M = -__builtin_huge_valf();
     for (int sp = 0; sp < a.nsplit; ++sp) {
-        const int64_t prow = (static_cast<int64_t>(qi) * a.nsplit + sp) * a.Ha + head;
+        const int64_t prow = row0 + static_cast<int64_t>(sp) * a.Ha;
         if (a.part_l[prow] > 0.0f) M = fmaxf(M, a.part_m[prow]);
     }
     f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
     float lsum = 0.0f;
     if (M != -__builtin_huge_valf()) {
-        for (int sp = 0; sp < a.nsplit; ++sp) {
-            const int64_t prow = (static_cast<int64_t>(qi) * a.nsplit + sp) * a.Ha + head;
-            const float l = a.part_l[prow];
-            if (!(l > 0.0f)) continue;
-            const float wgt = __builtin_amdgcn_exp2f(a.part_m[prow] - M);
-            lsum += wgt * l;
-            o += wgt * *reinterpret_cast<const f32x4 *>(a.part_o + prow * a.Dv + c);
+        for (int sp0 = 0; sp0 < a.nsplit; sp0 += U) {
+            f32x4 po[U];
+            float wl[U], ll[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int sp = sp0 + u < a.nsplit ? sp0 + u : sp0;
+                const int64_t prow = row0 + static_cast<int64_t>(sp) * a.Ha;
+                po[u] = *reinterpret_cast<const f32x4 *>(a.part_o + prow * a.Dv + c);
+                ll[u] = sp0 + u < a.nsplit ? a.part_l[prow] : 0.0f;
+                wl[u] = a.part_m[prow];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (!(ll[u] > 0.0f)) continue;
+                const float wgt = __builtin_amdgcn_exp2f(wl[u] - M);
+                lsum += wgt * ll[u];
+                o += wgt * po[u];
+            }
         }
     }
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
@@ -338,14 +363,19 @@ bool attention_shape_supported(int Dk, int Dv) {
            (Dk == 576 && Dv == 512);
 }
 
-void attention_split(int nq, int Ha, int k, int &nsplit, int &tps) {
+void attention_split(int nq, int Ha, int Dk, int Dv, int k, int &nsplit, int &tps) {
     const int hg = Ha % 32 == 0 ? 32 : 16;
     const int64_t base = static_cast<int64_t>(nq) * (Ha / hg);
-    const int steps = (k + kAttnStep - 1) / kAttnStep;
-    int want = static_cast<int>((512 + base - 1) / base);
+    const int64_t steps = (k + kAttnStep - 1) / kAttnStep;
+    // enough workgroups for two per compute unit, but the partials one split
+    // writes (Ha*Dv fp32 per query) no larger than the rows it reads (Dk bf16
+    // per entry)
+    int64_t want = (512 + base - 1) / base;
+    const int64_t cap = static_cast<int64_t>(k) * Dk * 2 / (static_cast<int64_t>(Ha) * Dv * 4);
+    want = want < cap ? want : cap;
     want = want < 1 ? 1 : (want > steps ? steps : want);
-    tps = (steps + want - 1) / want * kAttnStep;
-    nsplit = (k + tps - 1) / tps;
+    tps = static_cast<int>((steps + want - 1) / want * kAttnStep);
+    nsplit = static_cast<int>((k + tps - 1) / tps);
 }
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t st) {

@@ -620,9 +620,9 @@ struct AttnLayout {
     size_t part_o, part_m, part_l, total;
 };
 
-AttnLayout attention_layout(int S, int T, int Ha, int Dv, int k) {
+AttnLayout attention_layout(int S, int T, int Ha, int Dk, int Dv, int k) {
     AttnLayout l{};
-    attention_split(S * T, Ha, k, l.nsplit, l.tps);
+    attention_split(S * T, Ha, Dk, Dv, k, l.nsplit, l.tps);
     size_t off = 0;
     if (l.nsplit > 1) {
         const size_t rows = static_cast<size_t>(S) * T * l.nsplit * Ha;
@@ -640,7 +640,7 @@ extern "C" {
 
 size_t hisa_sparse_attention_workspace(int S, int T, int Ha, int Dk, int Dv, int k) {
     if (check_attention_shape(S, T, Ha, Dk, Dv, k) != HISA_OK) return 0;
-    return attention_layout(S, T, Ha, Dv, k).total;
+    return attention_layout(S, T, Ha, Dk, Dv, k).total;
 }
 
 int hisa_sparse_attention(const uint16_t *q, const uint16_t *kv, int64_t kv_seq_stride, int64_t kv_row_stride,
@@ -656,7 +656,7 @@ int hisa_sparse_attention(const uint16_t *q, const uint16_t *kv, int64_t kv_seq_
         return HISA_ERR_ARG;
     if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return HISA_ERR_ARG;
     if (!ws) return HISA_ERR_ARG;
-    const AttnLayout lay = attention_layout(S, T, Ha, Dv, k);
+    const AttnLayout lay = attention_layout(S, T, Ha, Dk, Dv, k);
     if (ws_bytes < lay.total) return HISA_ERR_WORKSPACE;
     char *base = align_ptr(ws);
     AttnArgs a{};

@@ -223,7 +223,7 @@ struct AttnArgs {
 };
 
 bool attention_shape_supported(int Dk, int Dv);
-void attention_split(int nq, int Ha, int k, int &nsplit, int &tps);
+void attention_split(int nq, int Ha, int Dk, int Dv, int k, int &nsplit, int &tps);
 hipError_t launch_attention(const AttnArgs &a, hipStream_t st);
 
 hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int64_t max_pos, hipStream_t st);
