@@ -14,7 +14,7 @@
 //   1. the step's latent rows are gathered into LDS (16-byte loads; rows
 //      padded to Dk + 8 elements so 16 consecutive rows start on distinct
 //      banks); the next step's rows are loaded into registers while the
-//      current step is computed;
+//      current step is computed and stored to the second row buffer;
 //   2. each wave scores one 16-token tile of the step against one 16-head
 //      tile: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = the token rows
 //      from LDS, M = tokens; B = q, held in registers for the whole run,
@@ -43,6 +43,7 @@ constexpr int kAttnStep = 64;                 // splits hold whole multiples of 
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 // max over the four 16-lane rows of a wave (lanes n, n+16, n+32, n+48)
@@ -67,12 +68,9 @@ __device__ __forceinline__ float rows_add(float x) {
 __device__ __forceinline__ bf16x8 load_vt_frag(const uint16_t *rows, int stride, int tok0, int dv0, int lane) {
     const int s = lane & 15;
     const uint16_t *p0 = rows + (tok0 + (s >> 2)) * stride + dv0 + 4 * (s & 3);
-    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(p0));
-    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(p0 + 4 * stride));
-    const u32x4 u = {static_cast<uint32_t>(static_cast<uint16_t>(a[0])) | (static_cast<uint32_t>(static_cast<uint16_t>(a[1])) << 16),
-                     static_cast<uint32_t>(static_cast<uint16_t>(a[2])) | (static_cast<uint32_t>(static_cast<uint16_t>(a[3])) << 16),
-                     static_cast<uint32_t>(static_cast<uint16_t>(b[0])) | (static_cast<uint32_t>(static_cast<uint16_t>(b[1])) << 16),
-                     static_cast<uint32_t>(static_cast<uint16_t>(b[2])) | (static_cast<uint32_t>(static_cast<uint16_t>(b[3])) << 16)};
+    const u32x2 a = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(p0)));
+    const u32x2 b = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(p0 + 4 * stride)));
+    const u32x4 u = {a.x, a.y, b.x, b.y};
     return as_bf16x8(u);
 }
 
@@ -83,7 +81,7 @@ struct AttnLds {
     static constexpr int kTT = 4 / HT;                  // token tiles per step (one per wave and head tile)
     static constexpr int kStep = 16 * kTT;              // tokens per step: 32 (HT = 2) or 64 (HT = 1)
     static constexpr int kPStride = kStep + 8;
-    uint16_t rows[kStep * kRowStride];
+    uint16_t rows[1][kStep * kRowStride];
     uint16_t pt[16 * HT * kPStride];
     float wmax[kTT][16 * HT];
     float wsum[kTT][16 * HT];
@@ -134,11 +132,15 @@ __global__ __launch_bounds__(kAttnThreads, HT == 2 ? 2 : 1) void sparse_attn_ker
         const int32_t t = e < e1 ? idx[e] : -1;
         return (t >= 0 && t < a.L) ? t : -1;
     };
+    // 16-byte chunk of the rows this thread moves in round i: a wave covers 64
+    // consecutive chunks, its upper half interleaved with the lower, so the 16
+    // lanes one LDS cycle serves (8 from each half) write 64 consecutive dwords
+    const int cbase = wave * 64 + (((lane & 31) << 1) | (lane >> 5));
     u32x4 v[kPer];
     auto load_rows = [&](const int32_t *toks) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            const int c = tid + i * kAttnThreads;
+            const int c = cbase + i * kAttnThreads;
             const bool in = c < STEP * CPR;
             const int r = in ? c / CPR : 0;
             const int32_t t = toks[r];
@@ -146,13 +148,13 @@ __global__ __launch_bounds__(kAttnThreads, HT == 2 ? 2 : 1) void sparse_attn_ker
                                                     (in ? 8 * (c - r * CPR) : 0));
         }
     };
-    auto store_rows = [&]() {
+    auto store_rows = [&](uint16_t *rows) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            const int c = tid + i * kAttnThreads;
+            const int c = cbase + i * kAttnThreads;
             if (c < STEP * CPR) {
                 const int r = c / CPR;
-                *reinterpret_cast<u32x4 *>(L.rows + r * RS + 8 * (c - r * CPR)) = v[i];
+                *reinterpret_cast<u32x4 *>(rows + r * RS + 8 * (c - r * CPR)) = v[i];
             }
         }
     };
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(kAttnThreads, HT == 2 ? 2 : 1) void sparse_attn_ker
     }
     __syncthreads();
     load_rows(L.tok[0]);
-    store_rows();
+    store_rows(L.rows[0]);
     __syncthreads();
 
     for (int i = 0; i < nsteps; ++i) {
@@ -192,11 +194,18 @@ __global__ __launch_bounds__(kAttnThreads, HT == 2 ? 2 : 1) void sparse_attn_ker
         if (tid < STEP) ahead = entry(e0 + (i + 2) * STEP + tid);
 
         // ---- scores of token tile tt against head tile hw
-        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
-        const uint16_t *krow = L.rows + (16 * tt + n) * RS + 8 * g;
+        // two accumulator chains (even and odd k-steps) halve the dependent MFMA latency
+        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f}, sacc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        const uint16_t *rows = L.rows[0];
+        const uint16_t *krow = rows + (16 * tt + n) * RS + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < KSK; ++ks)
+        for (int ks = 0; ks < KSK; ks += 2) {
             sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(load_bf16x8(krow + 32 * ks), qb[ks], sacc, 0, 0, 0);
+            if (ks + 1 < KSK)
+                sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(load_bf16x8(krow + 32 * ks + 32), qb[ks + 1], sacc1, 0,
+                                                                0, 0);
+        }
+        sacc += sacc1;
         // lane (g, n): tokens 16*tt + 4g + r of the step, head n of tile hw
         bool ok[4];
         float sv[4];
@@ -251,14 +260,14 @@ __global__ __launch_bounds__(kAttnThreads, HT == 2 ? 2 : 1) void sparse_attn_ker
             for (int ht = 0; ht < HT; ++ht) pb[ht] = load_bf16x8(L.pt + (16 * ht + n) * PS + 32 * kk + 8 * g);
 #pragma unroll
             for (int dt = 0; dt < DVW; ++dt) {
-                const bf16x8 va = load_vt_frag(L.rows, RS, 32 * kk + 8 * g, (wave * DVW + dt) * 16, lane);
+                const bf16x8 va = load_vt_frag(rows, RS, 32 * kk + 8 * g, (wave * DVW + dt) * 16, lane);
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht)
                     oacc[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ht], oacc[dt][ht], 0, 0, 0);
             }
         }
         __syncthreads();                                        // rows, P^T and this step's entries are free
-        if (i + 1 < nsteps) store_rows();
+        if (i + 1 < nsteps) store_rows(L.rows[0]);
         if (tid < STEP) L.tok[cur][tid] = ahead;
         __syncthreads();
     }
