@@ -96,6 +96,18 @@ def test_tree_workspace_sizes(lib):
         assert lib.hisa_tree_index_workspace(*bad) == 0, bad
 
 
+def test_attention_workspace_sizes(lib):
+    # 8 decode queries, 128 heads, 2048 entries: split partials of Ha*Dv fp32 plus (m, l) per split
+    a = lib.hisa_sparse_attention_workspace(8, 1, 128, 576, 512, 2048)
+    assert a >= 8 * 2 * 128 * 512 * 4
+    assert a < 8 * 16 * 128 * (512 + 2) * 4 + 4096
+    # many queries need no partials
+    assert lib.hisa_sparse_attention_workspace(1, 4096, 128, 576, 512, 2048) <= 4096
+    for bad in [(0, 1, 128, 576, 512, 64), (1, 1, 128, 576, 64, 64), (1, 1, 8, 64, 64, 64), (1, 1, 144, 64, 64, 64),
+                (1, 1, 16, 64, 64, 0), (300, 300, 16, 64, 64, 8)]:
+        assert lib.hisa_sparse_attention_workspace(*bad) == 0, bad
+
+
 def test_argument_checks_with_null_pointers(lib):
     # null tensors: rejected before anything is enqueued
     assert lib.hisa_index(None, None, None, None, 0, 100, None, 0, 1, 1, 4, 64, 64, 2, 8,
@@ -136,6 +148,13 @@ def test_argument_checks_with_null_pointers(lib):
                                None, None, None, None, None, 0, 0, None) == UNSUP
     assert lib.hisa_tree_index(None, None, None, None, 0, 100, None, 0, None, 0, 1, 1, 4, 64, 64, 4, 0, 2, 8,
                                None, None, None, None, None, 0, 0, None) == ARG
+    # the sparse attention
+    assert lib.hisa_sparse_attention(None, None, 0, 576, 100, None, 1, 1, 128, 576, 512, 64, 0.1, None, None,
+                                     None, 0, None) == ARG
+    assert lib.hisa_sparse_attention(None, None, 0, 576, 100, None, 1, 1, 128, 576, 256, 64, 0.1, None, None,
+                                     None, 0, None) == UNSUP       # (Dk, Dv) not supported
+    assert lib.hisa_sparse_attention(None, None, 0, 128, 100, None, 1, 1, 24, 128, 128, 64, 0.1, None, None,
+                                     None, 0, None) == UNSUP       # Ha not a multiple of 16
     # profiler argument checks
     ms, n = C.c_double(), C.c_int()
     assert lib.hisa_profile_read(-1, C.byref(ms), C.byref(n)) == ARG
@@ -240,3 +259,33 @@ def test_tree_argument_checks_with_placeholder_pointers(lib):
     assert app(B=24) == UNSUP
     assert app(kind=9) == ARG
     assert app(L0=L) == OK                  # empty range: no work
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="placeholder-pointer checks run only where no GPU is visible")
+def test_attention_argument_checks_with_placeholder_pointers(lib):
+    buf = (C.c_uint8 * 4096)()
+    base = (C.addressof(buf) + 255) // 256 * 256
+    p = C.c_void_p(base)
+    odd = C.c_void_p(base + 2)
+    S, T, Ha, Dk, Dv, L, k = 2, 1, 32, 128, 128, 100, 64
+    need = lib.hisa_sparse_attention_workspace(S, T, Ha, Dk, Dv, k)
+
+    def att(**kw):
+        a = dict(q=p, kv=p, kss=L * Dk, krs=Dk, L=L, idx=p, S=S, T=T, Ha=Ha, Dk=Dk, Dv=Dv, k=k, scale=0.1, out=p,
+                 ws=p, wsb=need)
+        a.update(kw)
+        return lib.hisa_sparse_attention(a["q"], a["kv"], a["kss"], a["krs"], a["L"], a["idx"], a["S"], a["T"],
+                                         a["Ha"], a["Dk"], a["Dv"], a["k"], a["scale"], a["out"], None, a["ws"],
+                                         a["wsb"], None)
+
+    assert att(wsb=need - 1) == WS
+    assert att(ws=None) == ARG
+    assert att(krs=Dk - 8) == ARG          # rows shorter than the key
+    assert att(krs=Dk + 4) == ARG          # not a multiple of 8 elements
+    assert att(kss=L * Dk - 8) == ARG      # sequences overlap
+    assert att(q=odd) == ARG
+    assert att(kv=odd) == ARG
+    assert att(out=odd) == ARG
+    assert att(L=0) == ARG
+    assert att(scale=float("inf")) == ARG
+    assert att(scale=float("nan")) == ARG
