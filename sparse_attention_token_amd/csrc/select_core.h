@@ -12,7 +12,9 @@
 //      within each wave plus one exchange of wave totals gives every thread
 //      the count of keys in higher bins; the thread whose run holds the rank
 //      still needed records the digit.  Three passes give the exact key K* of
-//      the k-th best candidate and the count of keys above it.
+//      the k-th best candidate and the count of keys above it; the passes stop
+//      early when every key of the cutoff bin is kept (the kept set is then
+//      every key at or above the bin's lowest value).
 //   2. Compaction: a DPP prefix sum over the packed pair (#keys > K*,
 //      #keys == K*) per thread gives each kept key its slot; keys equal to K*
 //      are kept lowest position first.
@@ -46,7 +48,7 @@ constexpr int kCoreBins0 = 2048, kCoreBins1 = 2048, kCoreBins2 = 1024;
 struct SelectScratch {
     uint32_t hist[kCoreBins0 + kCoreBins1 + kCoreBins2];
     uint32_t wave_tot[16];
-    uint32_t digit, above;
+    uint32_t digit, above, count;
 };
 
 // Block-wide exclusive prefix over threads of a per-thread count; also returns
@@ -134,6 +136,7 @@ __device__ __forceinline__ SelectResult block_radix_select(const uint32_t (&kv)[
                     if (above + hb[j] >= need) {
                         sc.digit = static_cast<uint32_t>(b0 + j);
                         sc.above = above;
+                        sc.count = hb[j];
                         done = true;
                     } else {
                         above += hb[j];
@@ -145,7 +148,12 @@ __device__ __forceinline__ SelectResult block_radix_select(const uint32_t (&kv)[
         prefix |= sc.digit << shift;
         mask |= static_cast<uint32_t>(nb - 1) << shift;
         need -= sc.above;
-        __syncthreads();   // digit/above and wave_tot are rewritten by the next pass
+        const uint32_t in_bin = sc.count;
+        __syncthreads();   // digit/above/count and wave_tot are rewritten by the next pass
+        // every key of the cutoff bin is kept: the kept set is exactly the keys
+        // >= prefix (low bits still open), i.e. the keys > prefix - 1, with
+        // none kept at equality -- no further pass needed
+        if (pass < 2 && need == in_bin) return SelectResult{prefix == 0u ? 0u : prefix - 1u, 0u, keff};
     }
     return SelectResult{prefix, need, keff};
 }
