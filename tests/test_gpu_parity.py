@@ -402,6 +402,34 @@ def test_hisa_and_flat_small(hisa, orc, spec):
     _say(f"  {rep}")
 
 
+LIMITS = [
+    # name, S, T, H, d, B, m, k, L, sampled rows -- each at one of the documented limits
+    ("k_16384", 1, 3, 8, 64, 128, 200, 16384, 40000, None),          # the largest k (25600 candidates)
+    ("m_4096", 1, 2, 4, 64, 16, 4096, 512, 70000, None),             # the largest m (65536 candidates, chunked)
+    ("queries_65535", 3, 21845, 4, 64, 64, 4, 32, 24000, 24),        # the largest S*T (block-by-block path)
+    ("H_1_B_256", 1, 4, 1, 128, 256, 3, 300, 3000, None),            # one head, the largest block
+]
+
+
+@pytest.mark.parametrize("spec", LIMITS, ids=[x[0] for x in LIMITS])
+def test_documented_limits(hisa, orc, spec):
+    name, S, T, H, d, B, m, k, L, nsample = spec
+    _say(f"limits {name}")
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    qpos = None if T > 16 else np.stack([_edge_qpos(L, B, T, rng) for _ in range(S)])
+    c = synth.gaussian_case(S, L, T, H, d, B, m, k, seed=17, qpos=qpos)
+    out = _run(hisa, c, qpos_on_device=qpos is not None, want_flat=nsample is None)
+    n = S * T
+    ids = range(n) if nsample is None else sorted(set(np.linspace(0, n - 1, nsample).astype(int).tolist()))
+    rep = {}
+    for qid in ids:
+        s, i = divmod(int(qid), T)
+        check_hisa_row(orc, c, s, i, out["idx"][s, i], out["sc"][s, i], out["blk"][s, i], rep)
+        if nsample is None:
+            check_flat_row(orc, c, s, i, out["fidx"][s, i], out["fsc"][s, i], rep)
+    _say(f"  {rep}")
+
+
 def test_tiny_workload(hisa, orc):
     c = synth.workload(0)
     out = _run(hisa, c, qpos_on_device=False)
