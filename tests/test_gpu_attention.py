@@ -129,11 +129,12 @@ def test_empty_and_single_sets(hisa, orc):
 
 
 def test_attention_over_indexer_output(hisa, orc):
-    """End to end: the HISA index set of the decode workload at 32K keys feeds the attention over
-    a latent cache of the same length (576-entry keys, 512-entry values, 128 heads)."""
+    """End to end, in the benchmark's launch configuration: the HISA index set of the decode
+    workload (8 sequences x 32K keys) feeds the attention over a latent cache of the same length
+    (576-entry keys, 512-entry values, 128 heads), every query checked."""
     import torch
 
-    c = synth.workload(1, sequences=2)
+    c = synth.workload(1)
     from parity import to_dev, build_pool
 
     dev = to_dev(c)

@@ -310,6 +310,28 @@ def test_tree_index(hisa, orc, spec):
     _say(f"  {rep}")
 
 
+def test_tree_benchmark_configuration(hisa, orc):
+    """The tree in the benchmark's launch configuration: decode, 4 sequences x 1M keys, super-blocks
+    of 64 blocks, 16 kept; the pools built by a bulk append and one single-row append (the fused
+    one-launch form), every query checked level by level."""
+    import torch
+
+    c = synth.workload(5)
+    G, W = 64, 16
+    _say(f"tree benchmark configuration: S={c.S} L={c.L} G={G} W={W}")
+    dev = to_dev(c)
+    reps, sreps = build_tree_pools(hisa, dev["K"], c.L, c.B, G, L_bulk=c.L - 1, step=1)
+    np.testing.assert_array_equal(bits(sreps), orc.super_pool(c.K, c.L, c.B, G))
+    idx, sc, blk, sblk = hisa.hisa_tree_index(dev["q"], dev["w"], dev["K"], c.L, reps, sreps, c.B, G, W, c.m, c.k,
+                                              None, want_blocks=True, want_super=True)
+    torch.cuda.synchronize()
+    idx, sc, blk, sblk = (t.cpu().numpy() for t in (idx, sc, blk, sblk))
+    rep = {}
+    for s in range(c.S):
+        check_tree_row(orc, c, s, 0, G, W, idx[s, 0], sc[s, 0], blk[s, 0], sblk[s, 0], rep)
+    _say(f"  {rep}")
+
+
 @pytest.mark.parametrize("G,pool", [(4, "mean"), (16, "max")])
 def test_tree_covering_every_super_block_is_hisa(hisa, G, pool):
     # W >= the number of super-blocks: the tree's levels 2-3 are hisa_index, bit for bit
