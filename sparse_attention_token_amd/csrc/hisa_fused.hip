@@ -18,9 +18,10 @@
 //      one wave when b_t + 1 <= 2048 (no barriers), by the whole workgroup
 //      otherwise.
 // Ways to run it, chosen by the host:
-//  * decode (few queries), short context: hisa_decode_kernel -- one 4-wave
+//  * decode (few queries), short context: hisa_decode_kernel -- one
 //    workgroup per 256 (or, with few queries, 128) candidate positions of a
-//    query (position p = slot*B + r: row r of the
+//    query, 8 waves when the grid has at most one workgroup per compute unit
+//    and 4 otherwise (position p = slot*B + r: row r of the
 //    slot-th kept block, masked past t).  Each workgroup repeats its query's
 //    block stage (the pooled means it reads are shared through L2) and then
 //    scores its 128 rows: one launch, no communication between workgroups.
@@ -61,6 +62,11 @@ constexpr int kDecodeMaxQueries = 16;
 constexpr int kDecodeRowsWide = 256;                      // candidate rows per decode workgroup, big grids
 constexpr int kDecodeRowsNarrow = 128;                    // ... and when fewer than kDecodeWideMin would run
 constexpr int kDecodeWideMin = 256;
+// Grids of at most this many workgroups (one per compute unit) run the decode
+// kernel with 8 waves per workgroup instead of 4.  Measured per step at 32K
+// keys: 8 queries 25.0 -> 21.8 us; 16 queries (512 workgroups) 29.2 -> 33.8 us,
+// so larger grids keep 4 waves.
+constexpr int kDecodeEightWaveMaxGrid = 256;
 // Up to this many blocks every decode workgroup repeats the block stage (one
 // launch); beyond it the block stage runs once per query in its own kernel.
 // Measured per step: 256 blocks 28.8 vs 29.7 us, 512 blocks 30.6 vs 28.9,
@@ -295,15 +301,15 @@ __device__ __forceinline__ void decode_tile(int nq, int tiles, int &qi, int &til
     }
 }
 
-// Decode mode: grid decode_grid(S*T, ceil(m*B/ROWS)), 256 threads.  Block stage, top-m
+// Decode mode: grid decode_grid(S*T, ceil(m*B/ROWS)), DT threads (256 or 512).  Block stage, top-m
 // into LDS, then the workgroup's ROWS candidate rows (ROWS/64 16-row tiles per
 // wave).  Wider workgroups repeat the block stage less often; narrow ones keep
 // every CU busy when there are few queries.
-template <int MT, int KS, int ROWS>
-__global__ __launch_bounds__(kDecodeThreads) void hisa_decode_kernel(FusedArgs a) {
+template <int MT, int KS, int ROWS, int DT>
+__global__ __launch_bounds__(DT) void hisa_decode_kernel(FusedArgs a) {
     constexpr int D = 32 * KS;
-    constexpr int NTW = ROWS / (16 * kDecodeThreads / 64);
-    __shared__ __attribute__((aligned(16))) BlockStageLds<KS, kDecodeThreads> L;
+    constexpr int NTW = ROWS / (16 * DT / 64);
+    __shared__ __attribute__((aligned(16))) BlockStageLds<KS, DT> L;
     __shared__ __attribute__((aligned(16))) uint32_t s_keys[kK1WaveMax];        // by k1_slot()
     __shared__ int32_t s_sel[kDecodeMaxM];
     __shared__ uint32_t s_keff;
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_decode_kernel(FusedArgs a
     int32_t *ob = a.out_blk ? a.out_blk + static_cast<int64_t>(qi) * a.m : nullptr;
     if (t < 0) {
         if (lead)
-            for (int j = tid; j < a.m; j += kDecodeThreads) {
+            for (int j = tid; j < a.m; j += DT) {
                 sel[j] = -1;
                 if (ob) ob[j] = -1;
             }
@@ -334,7 +340,7 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_decode_kernel(FusedArgs a
     if (tile0 >= npos) return;
 
     QFrag<MT, KS> f;
-    block_stage<MT, KS, kDecodeThreads, 4>(a, qi, s, t, L, s_keys, f, lead);
+    block_stage<MT, KS, DT, DT == 256 ? 4 : 2>(a, qi, s, t, L, s_keys, f, lead);
     if (wave == 0) {
         const uint32_t ke = block_topm_wave(s_keys, nb, a.m, [&](uint32_t op, int pos) {
             s_sel[op] = pos;
@@ -347,7 +353,7 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_decode_kernel(FusedArgs a
     }
     __syncthreads();
     if (lead)
-        for (int j = static_cast<int>(s_keff) + tid; j < a.m; j += kDecodeThreads) {
+        for (int j = static_cast<int>(s_keff) + tid; j < a.m; j += DT) {
             sel[j] = -1;
             if (ob) ob[j] = -1;
         }
@@ -661,11 +667,20 @@ hipError_t launch_fused_ks(const FusedArgs &a, bool decode, hipStream_t st) {
             return launch(kKindScoreRefine, hisa_dgather_kernel<MT, KS, kDecodeRowsNarrow>,
                           dim3(static_cast<uint32_t>(decode_grid(nq, narrow))), dim3(kDecodeThreads), 0, st, a);
         }
+        // one workgroup per compute unit or fewer: eight waves per workgroup
+        // share its block stage and split its rows more finely
+        const int tiles = use_wide ? wide : narrow;
+        const bool eight = static_cast<int64_t>(tiles) * nq <= kDecodeEightWaveMaxGrid;
+        const dim3 grid(static_cast<uint32_t>(decode_grid(nq, tiles)));
         if (use_wide)
-            return launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsWide>,
-                          dim3(static_cast<uint32_t>(decode_grid(nq, wide))), dim3(kDecodeThreads), 0, st, a);
-        return launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsNarrow>,
-                      dim3(static_cast<uint32_t>(decode_grid(nq, narrow))), dim3(kDecodeThreads), 0, st, a);
+            return eight ? launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsWide, 512>, grid, dim3(512),
+                                  0, st, a)
+                         : launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsWide, 256>, grid, dim3(256),
+                                  0, st, a);
+        return eight ? launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsNarrow, 512>, grid, dim3(512), 0,
+                              st, a)
+                     : launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsNarrow, 256>, grid, dim3(256), 0,
+                              st, a);
     }
     const hipError_t e = (a.bucket_off && a.nblk <= kBMMaxBlocks)
         ? launch_block_major_blocks(a, st)
