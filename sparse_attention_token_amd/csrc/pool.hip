@@ -206,12 +206,17 @@ __global__ __launch_bounds__(kPoolThreads) void own_mean_kernel(
     if (static_cast<int>(threadIdx.x) < d) own_rep[static_cast<int64_t>(qi) * d + threadIdx.x] = m;
 }
 
-// grid: (blocks b_lo .. b_lo + gridDim.x - 1), d threads.  Consecutive query
-// positions t = L - T + i (one sequence per blockIdx.y): a running fp64 sum
-// (or running maximum) down each block's rows, in row order, is at row t
-// exactly that of rows [b_t*B, t] in row order, so every query of the block
-// gets its own-block representative from one pass -- the same arithmetic as
-// staged_column_rep().
+// grid: (blocks b_lo .. b_lo + gridDim.x - 1, S, kPrefixSegments), d threads.
+// Consecutive query positions t = L - T + i: a running fp64 sum (or running
+// maximum) down each block's rows, in row order, is at row t exactly that of
+// rows [b_t*B, t] in row order, so every query of the block gets its own-block
+// representative from one pass -- the same arithmetic as staged_column_rep().
+// The block's rows are split into kPrefixSegments runs of outputs: the
+// workgroup of run z sums from the block's first row and writes the
+// representatives of the rows of its run, so the divisions of different runs
+// proceed in parallel.
+constexpr int kPrefixSegments = 4;
+
 template <bool MAX>
 __global__ __launch_bounds__(kMaxD) void own_prefix_mean_kernel(
         const uint16_t *__restrict__ K, int64_t k_seq_stride, int64_t L, int T, int d, int B,
@@ -221,30 +226,35 @@ __global__ __launch_bounds__(kMaxD) void own_prefix_mean_kernel(
     if (col >= d) return;
     const int64_t t0 = L - T;                                  // position of query 0
     const int64_t r0 = (b_lo + blockIdx.x) * B;
-    const int64_t r_first = r0 > t0 ? r0 : t0;                 // first row that is a query position
-    const int64_t r_end = (r0 + B < L) ? r0 + B : L;
+    const int seg = B / kPrefixSegments;
+    const int64_t out_lo = r0 + static_cast<int64_t>(blockIdx.z) * seg;
+    const int64_t blk_end = (r0 + B < L) ? r0 + B : L;
+    const int64_t r_end = (out_lo + seg < blk_end) ? out_lo + seg : blk_end;   // rows summed: r0 .. r_end-1
+    const int64_t r_first = out_lo > t0 ? out_lo : t0;         // first row written
+    if (r_first >= r_end) return;
     const uint16_t *src = K + s * k_seq_stride + col;
     ColumnRep<MAX> acc;
-    int64_t r = r0;
-    uint16_t nx[8];                                            // the next 8 rows, loads in flight
+    // rows in rounds of U, the next round's loads in flight while the current
+    // round is summed (rows past the end re-read the last row, unused)
+    constexpr int U = 16;
+    const int64_t last = r_end - 1;
+    uint16_t nx[U];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) nx[j] = r + j < r_end ? src[(r + j) * d] : 0;
-    for (; r + 8 <= r_end; r += 8) {
-        uint16_t x[8];
+    for (int j = 0; j < U; ++j) nx[j] = src[(r0 + j < r_end ? r0 + j : last) * d];
+    for (int64_t r = r0; r < r_end; r += U) {
+        uint16_t x[U];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = nx[j];
+        for (int j = 0; j < U; ++j) x[j] = nx[j];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) nx[j] = r + 8 + j < r_end ? src[(r + 8 + j) * d] : 0;
+        for (int j = 0; j < U; ++j) nx[j] = src[(r + U + j < r_end ? r + U + j : last) * d];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            acc.add(x[j]);
+        for (int j = 0; j < U; ++j) {
             const int64_t rr = r + j;
-            if (rr >= r_first) own_rep[(static_cast<int64_t>(s) * T + (rr - t0)) * d + col] = acc.get(rr + 1 - r0);
+            if (rr < r_end) {
+                acc.add(x[j]);
+                if (rr >= r_first) own_rep[(static_cast<int64_t>(s) * T + (rr - t0)) * d + col] = acc.get(rr + 1 - r0);
+            }
         }
-    }
-    for (; r < r_end; ++r) {
-        acc.add(src[r * d]);
-        if (r >= r_first) own_rep[(static_cast<int64_t>(s) * T + (r - t0)) * d + col] = acc.get(r + 1 - r0);
     }
 }
 
@@ -294,7 +304,7 @@ hipError_t launch_own_super(const uint16_t *pool, int64_t pool_seq_stride, const
 hipError_t launch_own_prefix_mean(const uint16_t *K, int64_t k_seq_stride, int64_t L, int S, int T, int d, int B,
                                   bool pool_max, uint16_t *own_rep, hipStream_t st) {
     const int64_t b_lo = (L - T) / B, b_hi = (L - 1) / B;
-    const dim3 g(static_cast<uint32_t>(b_hi - b_lo + 1), S);
+    const dim3 g(static_cast<uint32_t>(b_hi - b_lo + 1), S, kPrefixSegments);
     if (pool_max)
         return launch(kKindOwnMean, own_prefix_mean_kernel<true>, g, dim3(kMaxD), 0, st, K, k_seq_stride, L, T, d, B,
                       b_lo, own_rep);
