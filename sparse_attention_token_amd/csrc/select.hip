@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kNT = 1024;
 constexpr int kChunkMax = kNT * 32;
-constexpr int kNarrowNT = 256;          // select workgroup size when there are many queries
+constexpr int kNarrowNT = 512;          // select workgroup size when there are many queries (prefill top k: 115 -> 99 us against 256)
 constexpr int kManyQueries = 1024;
 
 // number of candidate positions of query qi for a mode (0 for an invalid t)
@@ -83,7 +83,7 @@ __device__ __forceinline__ void load_run(const uint32_t *__restrict__ keys, int6
 }
 
 // Single-stage select: the whole row (n <= NT*R) in one workgroup of NT
-// threads (1024 for latency with few queries, 256 for throughput with many).
+// threads (1024 for latency with few queries, 512 for throughput with many).
 template <int MODE, int R, int NT>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     __shared__ __attribute__((aligned(16))) SelectScratch sc;
