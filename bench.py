@@ -418,6 +418,23 @@ def main():
                 needle["two_level"] = sum(int(j in set(a2[s].tolist())) for s in range(S)
                                           for j in case.needles[s]) / case.needles.size
 
+    # ---- single-call latency: one eager call, then wait for it (host clock,
+    # median), as a caller that needs each result before the next call sees it
+    def latency_us(step_fn, n):
+        vals = []
+        for i in range(n):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            step_fn(i % R)
+            torch.cuda.synchronize()
+            vals.append((time.perf_counter() - t0) * 1e6)
+        return float(np.median(vals))
+
+    n_lat = 8 if prefill else 100
+    latency = {"hisa_step_us": latency_us(hisa_step, n_lat), "calls": n_lat,
+               "flat_us": None if args.no_flat else latency_us(flat_step, n_lat)}
+    log(f"single-call latency: HISA step {latency['hisa_step_us']:.1f} us, flat {latency['flat_us']} us")
+
     # ---- per-kernel durations: HIP events around each kernel, eager launches
     # queued behind a long matrix product so the GPU never waits on the host
     pro_steps = args.profile_steps if args.profile_steps is not None else (4 if prefill else min(2 * R, 64))
@@ -522,6 +539,7 @@ def main():
         "config": {"workload": case.name, "S": S, "T": T, "L": L, "H": H, "d": d, "B": B, "m": m,
                    "k": k, "key_cache_replicas": R, "parallelism": "single GPU"},
         "us_per_query": hisa_ms * 1e3 / nq,
+        "single_call_latency": latency,
         "index_only": {"ms_per_call": index_ms, "queries_per_s": nq / (index_ms * 1e-3)},
         "flat": None if flat_ms is None else {"ms_per_call": flat_ms, "queries_per_s": nq / (flat_ms * 1e-3),
                                               "us_per_query": flat_ms * 1e3 / nq},
