@@ -538,9 +538,14 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs 
         };
         const int rd = (nb + 63) / 64;
         uint32_t ke;
+        // the ballot select's work grows with R: above 16 keep R close to rd
+        // (1025 blocks, rd = 17: R = 20 took the kernel from 17.3 to 13.9 us;
+        // R = 12 for rd = 9 was slower than 16)
         if (rd <= 4) ke = dgather_topm<4>(keys, nb, a.m, lane, emit);
         else if (rd <= 8) ke = dgather_topm<8>(keys, nb, a.m, lane, emit);
         else if (rd <= 16) ke = dgather_topm<16>(keys, nb, a.m, lane, emit);
+        else if (rd <= 20) ke = dgather_topm<20>(keys, nb, a.m, lane, emit);
+        else if (rd <= 24) ke = dgather_topm<24>(keys, nb, a.m, lane, emit);
         else ke = dgather_topm<32>(keys, nb, a.m, lane, emit);
         if (lane == 0) s_keff = ke;
     }

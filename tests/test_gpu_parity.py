@@ -399,6 +399,9 @@ SMALL = [
     ("B16_chunked", 1, 60000, 2, 8, 64, 16, 2100, 256, "gaussian"),
     # just above the one-launch decode's 16 queries: the query-major fused path
     ("fused_17_queries", 1, 5000, 17, 64, 128, 128, 8, 512, "clustered"),
+    # decode with 1407 blocks: the gather kernel's one-wave top m holds 22
+    # block keys per lane (the 24-register select)
+    ("decode_gather_1407_blocks", 2, 90000, 2, 16, 64, 64, 24, 400, "gaussian"),
     # more than 2048 blocks: the block stage selects with the whole workgroup
     ("blocks_2344_workgroup_select", 1, 300000, 2, 4, 64, 128, 8, 256, "gaussian"),
     ("blocks_2344_40_queries", 2, 300000, 20, 16, 128, 128, 12, 300, "clustered"),
