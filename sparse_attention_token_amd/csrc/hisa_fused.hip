@@ -443,10 +443,14 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs 
         return;
     }
 
-    // the own block: rows b_t*B .. t, every load in flight before the first LDS store
+    // the own block: rows b_t*B .. t, every load (and those of q and w) in
+    // flight before the first LDS store
     const int64_t r0 = static_cast<int64_t>(bt) * a.B;
     const int own_rows = static_cast<int>(t + 1 - r0);
     uint16_t *s_own = reinterpret_cast<uint16_t *>(L.own);
+    QStager<MT, KS, kDecodeThreads> qst;
+    qst.load(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, tid);
+    const float wq = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
     {
         constexpr int kPer = (kFusedOwnElems / 8 + kDecodeThreads - 1) / kDecodeThreads;
         const int chunks = own_rows * D / 8;
@@ -460,8 +464,8 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs 
         for (int i = 0; i < kPer; ++i)
             if (tid + i * kDecodeThreads < chunks) dst[tid + i * kDecodeThreads] = x[i];
     }
-    stage_query<MT, KS, kDecodeThreads>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, L.q, tid);
-    if (tid < 64) L.w[tid] = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
+    qst.store(L.q, tid);
+    if (tid < 64) L.w[tid] = wq;
     __syncthreads();
     own_block_rep<D, 64>(a, s_own, own_rows, L.mean,
                       a.pool_out != nullptr && t == a.L - 1
@@ -525,8 +529,10 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs 
     const int tile0 = tile * ROWS;
     if (tile0 >= npos) return;
 
-    stage_query<MT, KS, kDecodeThreads>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, s_q, tid);
-    if (tid < 64) s_w[tid] = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
+    // q and w are loaded while wave 0 reads the block keys and selects
+    QStager<MT, KS, kDecodeThreads> qst;
+    qst.load(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, tid);
+    const float wq = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
     if (wave == 0) {
         const uint32_t *keys = a.blk_keys + static_cast<int64_t>(qi) * a.blk_stride;
         auto emit = [&](uint32_t op, int pos) {
@@ -549,6 +555,8 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs 
         else ke = dgather_topm<32>(keys, nb, a.m, lane, emit);
         if (lane == 0) s_keff = ke;
     }
+    qst.store(s_q, tid);
+    if (tid < 64) s_w[tid] = wq;
     __syncthreads();
     if (lead)
         for (int j = static_cast<int>(s_keff) + tid; j < a.m; j += kDecodeThreads) {

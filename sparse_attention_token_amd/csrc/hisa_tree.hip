@@ -175,6 +175,9 @@ __global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a) {
     const int64_t r0 = bt * a.B;
     const int own_rows = static_cast<int>(t + 1 - r0);
     uint16_t *s_own = reinterpret_cast<uint16_t *>(L.own);
+    QStager<MT, KS, kTopThreads> qst;           // q and w loads in flight with the rows'
+    qst.load(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, tid);
+    const float wq = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
     if (!own_from_pool) {
         constexpr int kPer = (kFusedOwnElems / 8 + kTopThreads - 1) / kTopThreads;
         const int chunks = own_rows * D / 8;
@@ -188,8 +191,8 @@ __global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a) {
         for (int i = 0; i < kPer; ++i)
             if (tid + i * kTopThreads < chunks) dst[tid + i * kTopThreads] = v[i];
     }
-    stage_query<MT, KS, kTopThreads>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, L.q, tid);
-    if (tid < 64) L.w[tid] = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
+    qst.store(L.q, tid);
+    if (tid < 64) L.w[tid] = wq;
     __syncthreads();
     if (!own_from_pool) {
         own_rows_rep<D, 64, MAX>(s_own, own_rows, L.rep, nullptr);     // ends with a barrier
