@@ -72,6 +72,20 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def host_cpu():
+    """The host's CPU model and logical CPU count, for the CPU baseline."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count()}
+
+
 # ---------------------------------------------------------------- algorithmic work models
 
 def kernel_models(case, blocks, tree=None, sblocks=None):
@@ -519,7 +533,21 @@ def main():
                "kind": "oracle",
                "sample": f"{len(sel)} of {n} queries of {case.name} (evenly spaced), {reps} pass(es), "
                          f"through the fp64 C oracle ({what}): {nq_cpu} queries in {tc:.1f} s",
-               "us_per_query": tc / nq_cpu * 1e6}
+               "us_per_query": tc / nq_cpu * 1e6,
+               "host": host_cpu()}
+        if not args.no_flat:
+            # the flat indexer's oracle on a few of the same queries (about 5 s)
+            fsel = probe[:1]
+            t0 = time.perf_counter()
+            oracle.flat_batch(case.q, case.w, case.qpos, case.K, L, k, sel=fsel)
+            per_f = max(time.perf_counter() - t0, 1e-6)
+            nf = int(min(n, max(1, 5.0 / per_f)))
+            fsel = np.linspace(0, n - 1, nf).astype(np.int32)
+            t0 = time.perf_counter()
+            oracle.flat_batch(case.q, case.w, case.qpos, case.K, L, k, sel=fsel)
+            tf = time.perf_counter() - t0
+            cpu["flat"] = {"value": nf / tf, "unit": "queries/s", "cores": oracle.num_threads(),
+                           "sample": f"{nf} of {n} queries (evenly spaced) in {tf:.1f} s"}
 
     nq = S * T
     value = nq / (hisa_ms * 1e-3)
