@@ -37,6 +37,7 @@ namespace {
 
 constexpr int kBucketThreads = 1024;
 constexpr int kBucketR = kFusedMaxBlocks / kBucketThreads;   // bins per thread in the scan
+constexpr int kBucketU = 16;                                 // kept-block entries per thread in flight
 constexpr int kBMThreads = 128;                              // two waves
 
 __global__ __launch_bounds__(kBucketThreads) void hisa_bucket_kernel(FusedArgs a) {
@@ -54,9 +55,19 @@ __global__ __launch_bounds__(kBucketThreads) void hisa_bucket_kernel(FusedArgs a
 
     for (int b = tid; b < nblk; b += kBucketThreads) s_cnt[b] = 0u;
     __syncthreads();
-    for (int e = tid; e < n; e += kBucketThreads) {
-        const int b = sel[e];
-        if (b >= 0) atomicAdd(&s_cnt[b], 1u);
+    // the chunk's kept blocks, kBucketU per thread at a time with every load
+    // issued before the first atomic (a load per iteration would serialise
+    // n / kBucketThreads memory round trips)
+    for (int e0 = 0; e0 < n; e0 += kBucketU * kBucketThreads) {
+        int bb[kBucketU];
+#pragma unroll
+        for (int u = 0; u < kBucketU; ++u) {
+            const int e = e0 + u * kBucketThreads + tid;
+            bb[u] = e < n ? sel[e] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kBucketU; ++u)
+            if (bb[u] >= 0) atomicAdd(&s_cnt[bb[u]], 1u);
     }
     __syncthreads();
 
@@ -88,12 +99,21 @@ __global__ __launch_bounds__(kBucketThreads) void hisa_bucket_kernel(FusedArgs a
     __syncthreads();
 
     uint32_t *ent = a.bucket_ent + static_cast<int64_t>(c) * kChunkQueries * a.m;
-    for (int e = tid; e < n; e += kBucketThreads) {
-        const int b = sel[e];
-        if (b >= 0) {
-            const uint32_t pos = atomicAdd(&s_cnt[b], 1u);
-            const int ql = e / a.m;
-            ent[pos] = (static_cast<uint32_t>(ql) << 16) | static_cast<uint32_t>(e - ql * a.m);
+    for (int e0 = 0; e0 < n; e0 += kBucketU * kBucketThreads) {
+        int bb[kBucketU];
+#pragma unroll
+        for (int u = 0; u < kBucketU; ++u) {
+            const int e = e0 + u * kBucketThreads + tid;
+            bb[u] = e < n ? sel[e] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kBucketU; ++u) {
+            if (bb[u] >= 0) {
+                const int e = e0 + u * kBucketThreads + tid;
+                const uint32_t pos = atomicAdd(&s_cnt[bb[u]], 1u);
+                const int ql = e / a.m;
+                ent[pos] = (static_cast<uint32_t>(ql) << 16) | static_cast<uint32_t>(e - ql * a.m);
+            }
         }
     }
 }
