@@ -377,6 +377,20 @@ def main():
         log(f"{label}: {nsteps} steps, {ms * 1e3:.2f} us/step (wall {wall * 1e3 / nsteps * 1e3:.2f} us/step)")
         return ms
 
+    # ---- bulk pool build (hisa_pool_append of rows [0, L)), reported as GB/s:
+    # it reads every key row and writes every block's mean
+    def pool_build(r):
+        if tree is None:
+            hisa.hisa_pool_append(Ks[r], pools[r], 0, L, B)
+        else:
+            hisa.hisa_tree_append(Ks[r], pools[r], spools[r], 0, L, B, tree[0])
+    pool_steps = max(R, min(steps, 64)) if not prefill else max(R, 8)
+    pool_ms = time_graphs(pool_build, pool_steps, 2, "bulk pool build")
+    pool_bytes = S * L * d * 2 + S * nblk * d * 2
+    pool_build_rep = {"ms_per_call": pool_ms, "bytes_per_call": pool_bytes,
+                      "GB_per_s": pool_bytes / (pool_ms * 1e-3) / 1e9,
+                      "hbm_frac": pool_bytes / (pool_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
     # ---- correctness snapshot for the reports (kept blocks, IoU vs flat, needles)
     idx_2, _, blk_h = hisa.hisa_index(q, w, K0, L, pools[0], B, m, k, None, want_blocks=True)
     sblocks = None
@@ -568,6 +582,7 @@ def main():
                    "k": k, "key_cache_replicas": R, "parallelism": "single GPU"},
         "us_per_query": hisa_ms * 1e3 / nq,
         "single_call_latency": latency,
+        "pool_build": pool_build_rep,
         "index_only": {"ms_per_call": index_ms, "queries_per_s": nq / (index_ms * 1e-3)},
         "flat": None if flat_ms is None else {"ms_per_call": flat_ms, "queries_per_s": nq / (flat_ms * 1e-3),
                                               "us_per_query": flat_ms * 1e3 / nq},
