@@ -11,8 +11,9 @@
  *   scorer over the key cache; the per-head weighted ReLU form is the DSA one.)
  *
  *   dsa_flat_index   -- the flat indexer: score every key j <= t of the
- *                       prefix, keep the k best ("the indexer must still scan
- *                       the entire prefix for every query", arXiv abstract).
+ *                       prefix for each query and keep the k best; it reads
+ *                       the whole prefix per query, the cost HISA removes
+ *                       (arXiv abstract).
  *   hisa_pool_append -- block representatives: mean pooling of contiguous
  *                       blocks of B keys (gptget.net English summary,
  *                       "Methodology"; Chinese summary, method details),

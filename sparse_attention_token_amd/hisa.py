@@ -125,6 +125,26 @@ def _check(fn: str, st: int):
         raise HisaError(fn, st)
 
 
+def _out(t: Optional[torch.Tensor], name: str, shape, dtype: torch.dtype, device) -> torch.Tensor:
+    """A caller-supplied output: exactly `shape` and `dtype`, contiguous, on `device`; a new
+    tensor when t is None.  The kernels write every element of the shape through the raw
+    pointer, so anything smaller, strided or of another type is refused before the call."""
+    shape = tuple(int(x) for x in shape)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
 # ---------------------------------------------------------------- the ABI calls
 
 def hisa_abi_version() -> int:
@@ -151,6 +171,8 @@ def hisa_pool_append(K: torch.Tensor, pool_mean: torch.Tensor, L_old: int, L_new
     pss = _rows(pool_mean, "pool_mean", d)
     if pool_mean.shape[0] != S:
         raise ValueError("pool_mean and K disagree on S")
+    if pool_mean.device != K.device:
+        raise ValueError("pool_mean and K must be on the same device")
     if pool_mean.shape[1] * B < L_new or K.shape[1] < L_new:
         raise ValueError("K or pool_mean too short for L_new")
     st = lib().hisa_pool_append_mode(_ptr(K), kss, S, d, B, int(L_old), int(L_new), _ptr(pool_mean),
@@ -206,13 +228,14 @@ def hisa_index(q, w, K, L: int, pool_mean, B: int, m: int, k: int, qpos=None, *,
     pss = _rows(pool_mean, "pool_mean", d)
     if pool_mean.shape[0] != S or pool_mean.shape[1] * B < L:
         raise ValueError("pool_mean must be [S, >= ceil(L/B), d]")
+    if pool_mean.device != q.device:
+        raise ValueError("pool_mean must be on the query's device")
     dev = q.device
-    if out_idx is None:
-        out_idx = torch.empty((S, T, k), dtype=torch.int32, device=dev)
-    if want_scores and out_score is None:
-        out_score = torch.empty((S, T, k), dtype=torch.float32, device=dev)
-    if want_blocks and out_blk is None:
-        out_blk = torch.empty((S, T, m), dtype=torch.int32, device=dev)
+    out_idx = _out(out_idx, "out_idx", (S, T, k), torch.int32, dev)
+    if want_scores or out_score is not None:
+        out_score = _out(out_score, "out_score", (S, T, k), torch.float32, dev)
+    if want_blocks or out_blk is not None:
+        out_blk = _out(out_blk, "out_blk", (S, T, m), torch.int32, dev)
     nbytes = hisa_index_workspace(S, T, H, d, L, B, m, k)
     if nbytes == 0:
         _check("hisa_index", lib().hisa_index(None, None, None, None, 0, L, None, 0, S, T, H, d, B,
@@ -237,13 +260,14 @@ def hisa_append_index(K, pool_mean, L_old: int, L_new: int, q, w, B: int, m: int
     pss = _rows(pool_mean, "pool_mean", d)
     if pool_mean.shape[0] != S or pool_mean.shape[1] * B < L_new:
         raise ValueError("pool_mean must be [S, >= ceil(L_new/B), d]")
+    if pool_mean.device != q.device:
+        raise ValueError("pool_mean must be on the query's device")
     dev = q.device
-    if out_idx is None:
-        out_idx = torch.empty((S, T, k), dtype=torch.int32, device=dev)
-    if want_scores and out_score is None:
-        out_score = torch.empty((S, T, k), dtype=torch.float32, device=dev)
-    if want_blocks and out_blk is None:
-        out_blk = torch.empty((S, T, m), dtype=torch.int32, device=dev)
+    out_idx = _out(out_idx, "out_idx", (S, T, k), torch.int32, dev)
+    if want_scores or out_score is not None:
+        out_score = _out(out_score, "out_score", (S, T, k), torch.float32, dev)
+    if want_blocks or out_blk is not None:
+        out_blk = _out(out_blk, "out_blk", (S, T, m), torch.int32, dev)
     nbytes = hisa_index_workspace(S, T, H, d, L_new, B, m, k)
     if nbytes == 0:
         _check("hisa_append_index", lib().hisa_append_index(None, 0, int(L_old), int(L_new), None, 0, None, None,
@@ -270,6 +294,8 @@ def hisa_tree_append(K, pool_rep, spool_rep, L_old: int, L_new: int, B: int, G: 
     sss = _rows(spool_rep, "spool_rep", d)
     if pool_rep.shape[0] != S or spool_rep.shape[0] != S:
         raise ValueError("pool_rep, spool_rep and K disagree on S")
+    if pool_rep.device != K.device or spool_rep.device != K.device:
+        raise ValueError("pool_rep, spool_rep and K must be on the same device")
     nblk = -(-int(L_new) // B)
     if K.shape[1] < L_new or pool_rep.shape[1] < nblk or spool_rep.shape[1] * G < nblk:
         raise ValueError("K, pool_rep or spool_rep too short for L_new")
@@ -299,15 +325,16 @@ def hisa_tree_index(q, w, K, L: int, pool_rep, spool_rep, B: int, G: int, W: int
         raise ValueError("pool_rep must be [S, >= ceil(L/B), d]")
     if spool_rep.shape[0] != S or spool_rep.shape[1] * G < nblk:
         raise ValueError("spool_rep must be [S, >= ceil(ceil(L/B)/G), d]")
+    if pool_rep.device != q.device or spool_rep.device != q.device:
+        raise ValueError("pool_rep and spool_rep must be on the query's device")
     dev = q.device
-    if out_idx is None:
-        out_idx = torch.empty((S, T, k), dtype=torch.int32, device=dev)
-    if want_scores and out_score is None:
-        out_score = torch.empty((S, T, k), dtype=torch.float32, device=dev)
-    if want_blocks and out_blk is None:
-        out_blk = torch.empty((S, T, m), dtype=torch.int32, device=dev)
-    if want_super and out_sblk is None:
-        out_sblk = torch.empty((S, T, W), dtype=torch.int32, device=dev)
+    out_idx = _out(out_idx, "out_idx", (S, T, k), torch.int32, dev)
+    if want_scores or out_score is not None:
+        out_score = _out(out_score, "out_score", (S, T, k), torch.float32, dev)
+    if want_blocks or out_blk is not None:
+        out_blk = _out(out_blk, "out_blk", (S, T, m), torch.int32, dev)
+    if want_super or out_sblk is not None:
+        out_sblk = _out(out_sblk, "out_sblk", (S, T, W), torch.int32, dev)
     nbytes = hisa_tree_index_workspace(S, T, H, d, L, B, G, W, m, k)
     if nbytes == 0:
         _check("hisa_tree_index", lib().hisa_tree_index(None, None, None, None, 0, int(L), None, 0, None, 0, S, T,
@@ -327,10 +354,9 @@ def dsa_flat_index(q, w, K, L: int, k: int, qpos=None, *, want_scores: bool = Tr
     """Flat DSA indexer.  Returns (idx [S,T,k] int32, score [S,T,k] fp32 | None)."""
     S, T, H, d, kss = _query_args(q, w, qpos, K, L)
     dev = q.device
-    if out_idx is None:
-        out_idx = torch.empty((S, T, k), dtype=torch.int32, device=dev)
-    if want_scores and out_score is None:
-        out_score = torch.empty((S, T, k), dtype=torch.float32, device=dev)
+    out_idx = _out(out_idx, "out_idx", (S, T, k), torch.int32, dev)
+    if want_scores or out_score is not None:
+        out_score = _out(out_score, "out_score", (S, T, k), torch.float32, dev)
     nbytes = dsa_flat_workspace(S, T, H, d, L, k)
     if nbytes == 0:
         _check("dsa_flat_index", lib().dsa_flat_index(None, None, None, None, 0, L, S, T, H, d, k,
@@ -366,10 +392,9 @@ def hisa_sparse_attention(q, kv, L: int, idx, Dv: int, scale: float, *, want_lse
     for t in (kv, idx):
         if t.device != dev:
             raise ValueError("all tensors must be on the same device")
-    if out is None:
-        out = torch.empty((S, T, Ha, Dv), dtype=torch.float32, device=dev)
-    if want_lse and lse is None:
-        lse = torch.empty((S, T, Ha), dtype=torch.float32, device=dev)
+    out = _out(out, "out", (S, T, Ha, Dv), torch.float32, dev)
+    if want_lse or lse is not None:
+        lse = _out(lse, "lse", (S, T, Ha), torch.float32, dev)
     nbytes = hisa_sparse_attention_workspace(S, T, Ha, Dk, Dv, k)
     if nbytes == 0:
         _check("hisa_sparse_attention", lib().hisa_sparse_attention(None, None, 0, 0, int(L), None, S, T, Ha, Dk,

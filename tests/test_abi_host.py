@@ -289,3 +289,36 @@ def test_attention_argument_checks_with_placeholder_pointers(lib):
     assert att(L=0) == ARG
     assert att(scale=float("inf")) == ARG
     assert att(scale=float("nan")) == ARG
+
+
+# ---------------------------------------------------------------- binding: caller-supplied outputs
+
+def test_binding_refuses_bad_outputs_before_the_call():
+    # The kernels write every element of an output row through a raw pointer,
+    # so a buffer of the wrong shape, type, device or layout must be refused
+    # by the binding before anything reaches the library.
+    import torch
+
+    from sparse_attention_token_amd import hisa
+
+    dev = torch.device("cpu")
+    good = torch.empty((2, 3, 16), dtype=torch.int32)
+    assert hisa._out(good, "out_idx", (2, 3, 16), torch.int32, dev) is good
+    fresh = hisa._out(None, "out_idx", (2, 3, 16), torch.int32, dev)
+    assert fresh.shape == (2, 3, 16) and fresh.dtype == torch.int32
+    bad = {
+        "short row": torch.empty((2, 3, 15), dtype=torch.int32),
+        "too few queries": torch.empty((2, 2, 16), dtype=torch.int32),
+        "flattened": torch.empty((96,), dtype=torch.int32),
+        "wrong type": torch.empty((2, 3, 16), dtype=torch.float32),
+        "int64": torch.empty((2, 3, 16), dtype=torch.int64),
+        "strided": torch.empty((2, 3, 32), dtype=torch.int32)[:, :, ::2],
+        "transposed": torch.empty((16, 3, 2), dtype=torch.int32).permute(2, 1, 0),
+    }
+    for why, t in bad.items():
+        with pytest.raises(ValueError):
+            hisa._out(t, "out_idx", (2, 3, 16), torch.int32, dev)
+    with pytest.raises(ValueError):
+        hisa._out(good, "out_idx", (2, 3, 16), torch.int32, torch.device("cuda:0"))
+    with pytest.raises(TypeError):
+        hisa._out([0] * 96, "out_idx", (2, 3, 16), torch.int32, dev)
