@@ -289,13 +289,20 @@ int oracle_hisa_query(const uint16_t *q, const float *w, const uint16_t *K,
 /* ---------- three-level hierarchy: super-blocks -> blocks -> tokens [P1-Summary] ---------- */
 
 /* The summary page's tree read as three levels over the key cache: blocks of
- * B keys grouped into super-blocks of G blocks.  The page keeps the tree
- * current by updating only the path from a new key's leaf to the root, so a
- * node's summary is built from its children's: a block pools its keys, a
- * super-block pools the representatives of its blocks (mode as rep_rows, the
- * children in order).  A node that holds the query position t covers its
- * children up to t: the own block pools its keys j <= t, the own super-block
- * pools its complete blocks and then the own block's representative.
+ * B keys grouped into super-blocks of G blocks.  Every node summarises a
+ * group of tokens by mean (or max) pooling over those tokens; the page keeps
+ * the tree current by updating only the path from a new key's leaf to the
+ * root, so a node's summary is formed from its children's:
+ *   - a block pools its keys (rep_rows);
+ *   - a super-block's mean is the mean over its tokens written through its
+ *     children: each child block's representative weighted by the number of
+ *     keys it covers, bf16(fp32(sum_b cnt_b * r_b / sum_b cnt_b)), the sum in
+ *     fp64 in block order (cnt_b * r_b is exact);
+ *   - a super-block's max is the max of its children's maxima, which is the
+ *     max over its tokens.
+ * A node that holds the query position t covers its tokens up to t: the own
+ * block pools its keys j <= t, and the own super-block its complete blocks
+ * (B keys each) and then the own block (t + 1 - floor(t/B)*B keys).
  * The query keeps the W best super-blocks, then the m best of the blocks
  * inside them (blocks b <= floor(t/B)), then the k best tokens j <= t of
  * those blocks; every ranking is (score desc, id asc).
@@ -311,6 +318,54 @@ static void block_rep_at(const uint16_t *K, int64_t b, int64_t t, int B, int d, 
     rep_rows(K, b * B, b < bt ? (b + 1) * B : t + 1, d, mode, out);
 }
 
+/* Summary of a super-block from its n children in order: kids [n][d] (their
+ * representatives) covering cnt[c] keys each.  mode 0: the count-weighted
+ * mean; mode 1: the max of the children (the earliest among equal values). */
+static void super_rep(const uint16_t *kids, const int64_t *cnt, int64_t n, int d, int mode, uint16_t *out)
+{
+    if (mode == 1) {
+        oracle_max_rows(kids, 0, n, d, out);
+        return;
+    }
+    double total = 0.0;
+    for (int64_t c = 0; c < n; ++c) total += (double)cnt[c];
+    for (int i = 0; i < d; ++i) {
+        double sum = 0.0;
+        for (int64_t c = 0; c < n; ++c)
+            sum += (double)cnt[c] * bf16_val(kids[(size_t)c * d + i]);
+        out[i] = bf16_round((float)(sum / total));
+    }
+}
+
+/* Super-block pool of a key cache holding L rows: super-block u covers blocks
+ * [u*G, min(u*G + G, ceil(L/B))), the last block holding L - (ceil(L/B)-1)*B
+ * keys.  reps: [S, ceil(ceil(L/B)/G), d]; mode as rep_rows. */
+int oracle_super_pool(const uint16_t *K, int64_t k_seq_stride, int S, int64_t L, int d, int B, int G,
+                      int mode, uint16_t *reps)
+{
+    int64_t nblk = (L + B - 1) / B, nsb = (nblk + G - 1) / G;
+    uint16_t *kids = (uint16_t *)malloc((size_t)G * d * sizeof *kids);
+    int64_t *cnt = (int64_t *)malloc((size_t)G * sizeof *cnt);
+    if (!kids || !cnt) {
+        free(kids); free(cnt);
+        return -1;
+    }
+    for (int s = 0; s < S; ++s) {
+        const uint16_t *Ks = K + (size_t)s * k_seq_stride;
+        for (int64_t u = 0; u < nsb; ++u) {
+            int64_t b1 = (u + 1) * G < nblk ? (u + 1) * G : nblk;
+            for (int64_t b = u * G; b < b1; ++b) {
+                int64_t r1 = (b + 1) * B < L ? (b + 1) * B : L;
+                rep_rows(Ks, b * B, r1, d, mode, kids + (size_t)(b - u * G) * d);
+                cnt[b - u * G] = r1 - b * B;
+            }
+            super_rep(kids, cnt, b1 - u * G, d, mode, reps + ((size_t)s * nsb + u) * d);
+        }
+    }
+    free(kids); free(cnt);
+    return 0;
+}
+
 int oracle_tree_query(const uint16_t *q, const float *w, const uint16_t *K, int H, int d, int64_t t,
                       int B, int G, int W, int m, int k, int mode, int32_t *out_idx, float *out_score,
                       int32_t *out_blk, int32_t *out_sblk, double *out_sscore)
@@ -319,19 +374,24 @@ int oracle_tree_query(const uint16_t *q, const float *w, const uint16_t *K, int 
     int64_t ns = st + 1;             /* super-blocks visible to the query */
     uint16_t *rep = (uint16_t *)malloc((size_t)d * sizeof *rep);
     uint16_t *kids = (uint16_t *)malloc((size_t)G * d * sizeof *kids);
+    int64_t *cnt = (int64_t *)malloc((size_t)G * sizeof *cnt);
     cand_t *sc = (cand_t *)malloc((size_t)ns * sizeof *sc);
     int32_t *ssel = (int32_t *)malloc((size_t)(W > 0 ? W : 1) * sizeof *ssel);
     cand_t *bc = (cand_t *)malloc(((size_t)(W > 0 ? W : 1) * G) * sizeof *bc);
     int32_t *sel = (int32_t *)malloc((size_t)(m > 0 ? m : 1) * sizeof *sel);
-    if (!rep || !kids || !sc || !ssel || !bc || !sel) {
-        free(rep); free(kids); free(sc); free(ssel); free(bc); free(sel);
+    if (!rep || !kids || !cnt || !sc || !ssel || !bc || !sel) {
+        free(rep); free(kids); free(cnt); free(sc); free(ssel); free(bc); free(sel);
         return -1;
     }
-    /* level 1: every super-block, pooled over its blocks' representatives */
+    /* level 1: every super-block, summarised over its tokens j <= t through
+     * its children (complete blocks B keys each, the own block t+1-bt*B) */
     for (int64_t u = 0; u < ns; ++u) {
         int64_t b1 = (u < st) ? (u + 1) * G : bt + 1;     /* children u*G .. b1-1 */
-        for (int64_t b = u * G; b < b1; ++b) block_rep_at(K, b, t, B, d, mode, kids + (size_t)(b - u * G) * d);
-        rep_rows(kids, 0, b1 - u * G, d, mode, rep);
+        for (int64_t b = u * G; b < b1; ++b) {
+            block_rep_at(K, b, t, B, d, mode, kids + (size_t)(b - u * G) * d);
+            cnt[b - u * G] = b < bt ? B : t + 1 - bt * B;
+        }
+        super_rep(kids, cnt, b1 - u * G, d, mode, rep);
         sc[u].s = oracle_score(q, w, rep, H, d);
         sc[u].i = u;
         if (out_sscore) out_sscore[u] = sc[u].s;
@@ -359,7 +419,7 @@ int oracle_tree_query(const uint16_t *q, const float *w, const uint16_t *K, int 
     for (int i = 0; i < m; ++i) out_blk[i] = i < meff ? sel[i] : -1;
     /* level 3: the original indexer on the tokens of the kept blocks */
     int keff = oracle_refine_query(q, w, K, H, d, t, B, sel, meff, k, out_idx, out_score, NULL);
-    free(rep); free(kids); free(sc); free(ssel); free(bc); free(sel);
+    free(rep); free(kids); free(cnt); free(sc); free(ssel); free(bc); free(sel);
     return keff;
 }
 

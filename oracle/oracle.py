@@ -52,6 +52,8 @@ def load():
     lib.oracle_hisa_query_mode.restype = I
     lib.oracle_hisa_query_mode.argtypes = [_u16p, _f32p, _u16p, _u16p, I, I, I64, I, I, I, I,
                                            _i32p, _f32p, _i32p, _f64p]
+    lib.oracle_super_pool.restype = I
+    lib.oracle_super_pool.argtypes = [_u16p, I64, I, I64, I, I, I, I, _u16p]
     lib.oracle_tree_query.restype = I
     lib.oracle_tree_query.argtypes = [_u16p, _f32p, _u16p, I, I, I64, I, I, I, I, I, I, _i32p, _f32p,
                                       _i32p, _i32p, _f64p]
@@ -134,10 +136,17 @@ def pool(K: np.ndarray, L: int, B: int, mode: str = "mean") -> np.ndarray:
 
 
 def super_pool(K: np.ndarray, L: int, B: int, G: int, mode: str = "mean") -> np.ndarray:
-    """Super-block representatives [S, ceil(ceil(L/B)/G), d] of the three-level tree: the block
-    representatives of pool(K, L, B, mode), pooled G at a time as rows (same mode)."""
-    blocks = pool(K, L, B, mode)
-    return pool(blocks, blocks.shape[1], G, mode)
+    """Super-block representatives [S, ceil(ceil(L/B)/G), d] of the three-level tree over
+    K [S, L_cap, d] holding L rows: per super-block of G blocks, the mean over its keys
+    formed from its block representatives weighted by their key counts ("mean"), or the
+    max of their maxima ("max")."""
+    K = _c(K, np.uint16)
+    S, Lcap, d = K.shape
+    nsb = -(-(-(-L // B)) // G)
+    out = np.zeros((S, nsb, d), dtype=np.uint16)
+    if load().oracle_super_pool(_p(K, _u16p), Lcap * d, S, L, d, B, G, _mode(mode), _p(out, _u16p)) != 0:
+        raise MemoryError("oracle_super_pool failed")
+    return out
 
 
 def flat_query(q, w, K, t: int, k: int, want_all=False):

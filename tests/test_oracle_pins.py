@@ -46,6 +46,15 @@ def np_mean_bits(rows_bits):
     return bf16_bits(means.astype(np.float32))
 
 
+def np_weighted_mean_bits(rows_bits, counts):
+    """bf16(fp32(exact sum_r c_r * x_r / sum_r c_r)) of bf16 rows [n, d] -- exact sum via math.fsum."""
+    f = bf16_to_f32(rows_bits).astype(np.float64)
+    c = [float(x) for x in counts]
+    means = np.array([math.fsum(ci * f[r, i] for r, ci in enumerate(c)) / math.fsum(c)
+                      for i in range(f.shape[1])], dtype=np.float64)
+    return bf16_bits(means.astype(np.float32))
+
+
 def int_case(rng, L, H, d, lo=-3, hi=4):
     """Small-integer keys/queries/weights: every score is exact in binary64."""
     K = bf16_bits(rng.integers(lo, hi, size=(L, d)).astype(np.float32))
@@ -232,6 +241,28 @@ def test_golden_tree_example(orc):
     assert list(fidx) == g["flat"]["idx"]
 
 
+def test_golden_tree_partial_own_block(orc):
+    # the own super-block's mean is over its tokens: a partial own block counts
+    # with its key count, not as a whole child (the hand derivation in the file)
+    with open(os.path.join(os.path.dirname(TREE_GOLDEN), "tree_partial_example.json")) as f:
+        g = json.load(f)
+    q = bf16_bits(np.array(g["q"], dtype=np.float32))
+    w = np.array(g["w"], dtype=np.float32)
+    K = bf16_bits(np.array(g["K"], dtype=np.float32))
+    for mode in ("mean", "max"):
+        e = g[mode]
+        idx, sc, blk, sblk, keff = orc.tree_query(q, w, K, g["t"], g["B"], g["G"], g["W"], g["m"], g["k"], mode=mode)
+        assert [u for u in sblk if u >= 0] == e["sblocks"], mode
+        assert [b for b in blk if b >= 0] == e["blocks"], mode
+        assert list(idx) == e["idx"], mode
+        np.testing.assert_array_equal(sc, np.array(e["score"], dtype=np.float32))
+    sp = orc.super_pool(K.reshape(1, -1, 1), g["L"], g["B"], g["G"])
+    assert bf16_to_f32(sp).ravel().tolist() == g["super_pool_mean_at_L7"]
+    np.testing.assert_array_equal(orc.tree_super_scores(q, w, K, g["t"], g["B"], g["G"]), [2.5, 2.0])
+    fidx, fsc, _ = orc.flat_query(q, w, K, g["t"], g["k"])
+    assert list(fidx) == g["flat"]["idx"]
+
+
 @pytest.mark.parametrize("mode", ["mean", "max"])
 def test_tree_with_every_super_block_is_hisa(orc, mode):
     rng = np.random.default_rng(21)
@@ -286,7 +317,12 @@ def test_tree_bruteforce(orc, mode):
         bt = t // B
         st = bt // G
         brep_all = [rep(K[b * B:((b + 1) * B if b < bt else t + 1)]) for b in range(bt + 1)]
-        srep = [rep(np.stack(brep_all[u * G:min((u + 1) * G, bt + 1)])) for u in range(st + 1)]
+        cnt_all = [B if b < bt else t + 1 - bt * B for b in range(bt + 1)]
+        if mode == "mean":   # over the super-block's tokens: children weighted by key count
+            srep = [np_weighted_mean_bits(np.stack(brep_all[u * G:min((u + 1) * G, bt + 1)]),
+                                          cnt_all[u * G:min((u + 1) * G, bt + 1)]) for u in range(st + 1)]
+        else:
+            srep = [rep(np.stack(brep_all[u * G:min((u + 1) * G, bt + 1)])) for u in range(st + 1)]
         ssel = np.sort(np_topk(np_scores(q, w, np.stack(srep)), np.arange(st + 1), min(W, st + 1)))
         cb = np.array([b for u in ssel for b in range(u * G, min((u + 1) * G, bt + 1))], dtype=np.int64)
         brep = [brep_all[b] for b in cb]
@@ -561,13 +597,62 @@ def test_block_sparse_rejects_budget_below_one_block(orc):
 
 
 def test_super_pool_hand_example(orc):
-    # keys 0 2 | 2 4 | 8 8 (B = 2): block means 1, 3, 8 and maxima 2, 4, 8; super-blocks of
-    # G = 2 blocks pool those: means (1+3)/2 = 2 and 8, maxima 4 and 8
-    K = bf16_bits(np.array([0, 2, 2, 4, 8, 8], dtype=np.float32)).reshape(1, 6, 1)
-    assert bf16_to_f32(orc.super_pool(K, 6, 2, 2, "mean")).ravel().tolist() == [2.0, 8.0]
+    # keys 0 2 | 4 4 | 8 8 (B = 2): block means 1, 4, 8 and maxima 2, 4, 8; super-blocks of
+    # G = 2 blocks: means over their keys (0+2+4+4)/4 = 2.5 and 8, maxima 4 and 8
+    K = bf16_bits(np.array([0, 2, 4, 4, 8, 8], dtype=np.float32)).reshape(1, 6, 1)
+    assert bf16_to_f32(orc.super_pool(K, 6, 2, 2, "mean")).ravel().tolist() == [2.5, 8.0]
     assert bf16_to_f32(orc.super_pool(K, 6, 2, 2, "max")).ravel().tolist() == [4.0, 8.0]
-    # a partial last block (L = 5): block means 1, 3, 8 still; L = 3: blocks 1, 2 -> super 1.5
-    assert bf16_to_f32(orc.super_pool(K, 3, 2, 2, "mean")).ravel().tolist() == [1.5]
+    # a partial last block: L = 3 holds keys 0 2 | 4, so super-block 0 is (0+2+4)/3 = 2 (its
+    # children 1 and 4 weighted 2 : 1; weighted equally they would give 2.5); L = 5 holds
+    # 0 2 | 4 4 | 8: super-blocks 2.5 and 8
+    assert bf16_to_f32(orc.super_pool(K, 3, 2, 2, "mean")).ravel().tolist() == [2.0]
+    assert bf16_to_f32(orc.super_pool(K, 3, 2, 2, "max")).ravel().tolist() == [4.0]
+    assert bf16_to_f32(orc.super_pool(K, 5, 2, 2, "mean")).ravel().tolist() == [2.5, 8.0]
+
+
+def test_super_pool_is_the_token_mean_within_rounding(orc):
+    # A super-block's mean is the mean over its keys, reached through bf16
+    # block means: each child carries at most one bf16 rounding (relative
+    # 2^-8 counting the fp32 step) and the result one more, so
+    #   |super - mean of keys| <= 2^-8 * (sum_b c_b |mean_b| / N + |mean of keys|).
+    # The last block of each cache is short and offset by +40, so averaging the
+    # children with equal weight (the wrong reading) misses this bound severalfold.
+    rng = np.random.default_rng(12)
+    for B, G, L in [(4, 4, 37), (16, 8, 1000), (64, 4, 700), (8, 16, 999)]:
+        f = rng.standard_normal((2, L, 6)).astype(np.float32) + 0.5
+        last = (L - 1) // B * B
+        f[:, last:] += 40.0
+        K = bf16_bits(f)
+        kf = bf16_to_f32(K).astype(np.float64)
+        sp = bf16_to_f32(orc.super_pool(K, L, B, G)).astype(np.float64)
+        nblk = -(-L // B)
+        worst_equal = 0.0
+        for u in range(sp.shape[1]):
+            j0, j1 = u * G * B, min(L, (u + 1) * G * B)
+            blocks = [(b * B, min(L, b * B + B)) for b in range(u * G, min(nblk, u * G + G))]
+            for s in range(2):
+                for i in range(6):
+                    mu = math.fsum(kf[s, j0:j1, i]) / (j1 - j0)
+                    mb = [math.fsum(kf[s, a:e, i]) / (e - a) for a, e in blocks]
+                    bound = 2.0 ** -8 * (math.fsum((e - a) * abs(x) for (a, e), x in zip(blocks, mb)) / (j1 - j0)
+                                         + abs(mu)) + 1e-30
+                    assert abs(sp[s, u, i] - mu) <= bound, (B, G, L, u, s, i)
+                    worst_equal = max(worst_equal, abs(sum(mb) / len(mb) - mu) / bound)
+        assert worst_equal > 2.0, "the constructed case does not tell the readings apart"
+
+
+def test_own_super_block_is_the_super_pool_at_t(orc):
+    # the own super-block of a query at t is the super-block pool of the cache
+    # cut at L = t + 1 (both cover the tokens j <= t)
+    rng = np.random.default_rng(13)
+    for trial in range(8):
+        B, G = int(rng.choice([2, 4, 8])), int(rng.choice([2, 4]))
+        t = int(rng.integers(1, 200))
+        q, w, K = int_case(rng, t + 1, 3, 5)
+        for mode in ("mean", "max"):
+            sp = orc.super_pool(K.reshape(1, t + 1, 5), t + 1, B, G, mode)[0]
+            want = [orc.score(q, w, sp[u]) for u in range(sp.shape[0])]
+            np.testing.assert_array_equal(orc.tree_super_scores(q, w, K, t, B, G, mode), want)
 
 
 def test_super_pool_special_cases(orc):
