@@ -54,6 +54,27 @@ def test_abi_version(hisa):
     assert hisa.hisa_abi_version() == 5
 
 
+def test_binding_refuses_bad_outputs(hisa):
+    """Outputs passed in must have exactly the shape, type and device the call writes."""
+    import torch
+
+    c = synth.gaussian_case(2, 300, 3, 4, 64, 64, 2, 16, seed=3)
+    dev = to_dev(c)
+    pool = build_pool(hisa, dev["K"], c.L, c.B)
+    g = dev["q"].device
+    for kw in (dict(out_idx=torch.empty((2, 3, 15), dtype=torch.int32, device=g)),
+               dict(out_idx=torch.empty((2, 3, 16), dtype=torch.int64, device=g)),
+               dict(out_score=torch.empty((2, 3, 16), dtype=torch.float32)),
+               dict(out_blk=torch.empty((2, 3, 1), dtype=torch.int32, device=g)),
+               dict(out_idx=torch.empty((2, 3, 32), dtype=torch.int32, device=g)[:, :, ::2])):
+        with pytest.raises(ValueError):
+            hisa.hisa_index(dev["q"], dev["w"], dev["K"], c.L, pool, c.B, c.m, c.k, **kw)
+    with pytest.raises(ValueError):
+        hisa.dsa_flat_index(dev["q"], dev["w"], dev["K"], c.L, c.k,
+                            out_idx=torch.empty((2, 3, 8), dtype=torch.int32, device=g))
+    torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------- block pool
 
 @pytest.mark.parametrize("B,d,L,S", [(16, 64, 100, 2), (64, 64, 1000, 1), (128, 128, 128 * 5 + 77, 2),
