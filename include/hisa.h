@@ -54,9 +54,10 @@
 extern "C" {
 #endif
 
-#define HISA_ABI_VERSION 5   /* 2: adds hisa_append_index; 3: adds the *_mode calls (max pooling);
+#define HISA_ABI_VERSION 6   /* 2: adds hisa_append_index; 3: adds the *_mode calls (max pooling);
                                 4: adds the three-level tree calls hisa_tree_*;
-                                5: adds hisa_sparse_attention */
+                                5: adds hisa_sparse_attention;
+                                6: adds hisa_append_index_static and HISA_ERR_SCRATCH */
 
 #if defined(__GNUC__)
 #define HISA_API __attribute__((visibility("default")))
@@ -69,7 +70,9 @@ enum hisa_status {
     HISA_ERR_ARG = -1,          /* null pointer, negative size, inconsistent stride or length */
     HISA_ERR_UNSUPPORTED = -2,  /* shape outside the supported set above */
     HISA_ERR_WORKSPACE = -3,    /* ws_bytes smaller than the *_workspace() size */
-    HISA_ERR_HIP = -4           /* a HIP runtime error while enqueuing the kernels */
+    HISA_ERR_HIP = -4,          /* a HIP runtime error while enqueuing the kernels */
+    HISA_ERR_SCRATCH = -5       /* hisa_append_index_static: the call needs more than
+                                   HISA_STATIC_SCRATCH_BYTES of workspace */
 };
 
 /* How block representatives are pooled (the *_mode calls; the others use mean). */
@@ -202,6 +205,35 @@ HISA_API int hisa_append_index_mode(const uint16_t *K, int64_t k_seq_stride, int
                                     int S, int T, int H, int d, int B, int m, int k,
                                     int32_t *out_idx, float *out_score, int32_t *out_blk,
                                     void *ws, size_t ws_bytes, int pool_kind, void *stream);
+
+/*
+ * hisa_append_index_static -- hisa_append_index (mean pooling) for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, and harnesses that forbid hipMalloc.  The arguments, results
+ * and errors are those of hisa_append_index without ws / ws_bytes: the
+ * workspace is instead a device array inside the library of
+ * HISA_STATIC_SCRATCH_BYTES (16 MiB), one copy per GPU, held until the
+ * process ends.  The call itself allocates nothing (no hipMalloc, no library
+ * routine that allocates); on its first use on a device it looks up that
+ * device's copy of the array (the device that owns `stream`, or the current
+ * device for the NULL stream).
+ *   - A call whose workspace, hisa_index_workspace(S, T, H, d, L_new, B, m, k),
+ *     exceeds HISA_STATIC_SCRATCH_BYTES returns HISA_ERR_SCRATCH and enqueues
+ *     nothing.  16 MiB holds, for example, a decode batch of 64 queries with
+ *     m*B = 16384 candidates each over 2^20 keys (6.1 MiB); a 4096-query
+ *     prefill chunk over 2^17 keys (147 MiB) does not fit.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (nothing in it needs to start at zero).  Calls that can
+ *     overlap on one GPU -- on different streams, or from different threads
+ *     without ordering -- race on it and must not be issued; calls ordered on
+ *     one stream are fine.
+ */
+#define HISA_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+HISA_API int hisa_append_index_static(const uint16_t *K, int64_t k_seq_stride, int64_t L_old, int64_t L_new,
+                                      uint16_t *pool_mean, int64_t pool_seq_stride,
+                                      const uint16_t *q, const float *w, const int32_t *qpos,
+                                      int S, int T, int H, int d, int B, int m, int k,
+                                      int32_t *out_idx, float *out_score, int32_t *out_blk, void *stream);
 
 /*
  * Three-level tree: super-blocks -> blocks -> tokens.  Page "Hierarchical

@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/hisa.h"
@@ -235,6 +236,7 @@ const char *hisa_status_string(int status) {
         case HISA_ERR_UNSUPPORTED: return "unsupported shape";
         case HISA_ERR_WORKSPACE: return "workspace too small";
         case HISA_ERR_HIP: return "HIP runtime error while enqueuing";
+        case HISA_ERR_SCRATCH: return "the call needs more workspace than the library's static scratch (16 MiB)";
         default: return "unknown status";
     }
 }
@@ -433,6 +435,68 @@ int hisa_append_index(const uint16_t *K, int64_t k_seq_stride, int64_t L_old, in
                       float *out_score, int32_t *out_blk, void *ws, size_t ws_bytes, void *stream) {
     return hisa_append_index_mode(K, k_seq_stride, L_old, L_new, pool_mean, pool_seq_stride, q, w, qpos, S, T, H, d,
                                   B, m, k, out_idx, out_score, out_blk, ws, ws_bytes, HISA_POOL_MEAN, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- static scratch
+// The workspace of hisa_append_index_static: a device array in the library,
+// one copy per GPU.  In host code `scratch` names a host-side stand-in for the
+// symbol, not a device address; the device address of each GPU's copy comes
+// from hipGetSymbolAddress with that GPU current, looked up once per device,
+// and only that address is ever handed to a kernel.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[HISA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the GPU that runs `stream`.
+int static_scratch(hipStream_t stream, void **out) {
+    int dev = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return HISA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return HISA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> guard(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return HISA_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return HISA_ERR_HIP;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || p == nullptr) return HISA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return HISA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hisa_append_index_static(const uint16_t *K, int64_t k_seq_stride, int64_t L_old, int64_t L_new,
+                             uint16_t *pool_mean, int64_t pool_seq_stride, const uint16_t *q, const float *w,
+                             const int32_t *qpos, int S, int T, int H, int d, int B, int m, int k,
+                             int32_t *out_idx, float *out_score, int32_t *out_blk, void *stream) {
+    // the plain call's checks, with the scratch array standing in for the
+    // workspace (its address is not needed to size it); all of them run
+    // before the device is touched
+    int st = check_append(K, k_seq_stride, S, d, B, L_old, L_new, pool_mean, pool_seq_stride);
+    if (st != HISA_OK) return st;
+    static const char kSized = 0;
+    st = check_index(q, w, qpos, K, k_seq_stride, L_new, pool_mean, pool_seq_stride, S, T, H, d, B, m, k, out_idx,
+                     &kSized, HISA_STATIC_SCRATCH_BYTES);
+    if (st == HISA_ERR_WORKSPACE) return HISA_ERR_SCRATCH;
+    if (st != HISA_OK) return st;
+    void *ws = nullptr;
+    st = static_scratch(static_cast<hipStream_t>(stream), &ws);
+    if (st != HISA_OK) return st;
+    return hisa_append_index_mode(K, k_seq_stride, L_old, L_new, pool_mean, pool_seq_stride, q, w, qpos, S, T, H, d,
+                                  B, m, k, out_idx, out_score, out_blk, ws, HISA_STATIC_SCRATCH_BYTES, HISA_POOL_MEAN,
+                                  stream);
 }
 
 }  // extern "C"

@@ -22,6 +22,8 @@ HISA_ERR_ARG = -1
 HISA_ERR_UNSUPPORTED = -2
 HISA_ERR_WORKSPACE = -3
 HISA_ERR_HIP = -4
+HISA_ERR_SCRATCH = -5
+STATIC_SCRATCH_BYTES = 16 << 20      # HISA_STATIC_SCRATCH_BYTES
 
 
 class HisaError(RuntimeError):
@@ -66,6 +68,9 @@ def lib():
     L.hisa_append_index.restype = i32
     L.hisa_append_index.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                     i32, vp, vp, vp, vp, sz, vp]
+    L.hisa_append_index_static.restype = i32
+    L.hisa_append_index_static.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                           i32, vp, vp, vp, vp]
     L.hisa_tree_append.restype = i32
     L.hisa_tree_append.argtypes = [vp, i64, i32, i32, i32, i32, i64, i64, vp, i64, vp, i64, i32, vp]
     L.hisa_tree_index_workspace.restype = sz
@@ -279,6 +284,32 @@ def hisa_append_index(K, pool_mean, L_old: int, L_new: int, q, w, B: int, m: int
                                       _ptr(out_blk), _ptr(ws), ws.numel() * ws.element_size(), _pool_kind(pool),
                                       _stream(dev))
     _check("hisa_append_index", st)
+    return out_idx, out_score, out_blk
+
+
+def hisa_append_index_static(K, pool_mean, L_old: int, L_new: int, q, w, B: int, m: int, k: int, qpos=None, *,
+                             want_scores: bool = True, want_blocks: bool = False, out_idx=None, out_score=None,
+                             out_blk=None):
+    """hisa_append_index with the library's own static scratch as the workspace (mean pooling):
+    the library allocates nothing.  With every output passed in, neither does this binding.
+    Calls that could overlap on one GPU must not be issued (they share the scratch)."""
+    S, T, H, d, kss = _query_args(q, w, qpos, K, L_new)
+    _bf16(pool_mean, "pool_mean")
+    pss = _rows(pool_mean, "pool_mean", d)
+    if pool_mean.shape[0] != S or pool_mean.shape[1] * B < L_new:
+        raise ValueError("pool_mean must be [S, >= ceil(L_new/B), d]")
+    if pool_mean.device != q.device:
+        raise ValueError("pool_mean must be on the query's device")
+    dev = q.device
+    out_idx = _out(out_idx, "out_idx", (S, T, k), torch.int32, dev)
+    if want_scores or out_score is not None:
+        out_score = _out(out_score, "out_score", (S, T, k), torch.float32, dev)
+    if want_blocks or out_blk is not None:
+        out_blk = _out(out_blk, "out_blk", (S, T, m), torch.int32, dev)
+    st = lib().hisa_append_index_static(_ptr(K), kss, int(L_old), int(L_new), _ptr(pool_mean), pss, _ptr(q),
+                                        _ptr(w), _ptr(qpos), S, T, H, d, B, m, k, _ptr(out_idx), _ptr(out_score),
+                                        _ptr(out_blk), _stream(dev))
+    _check("hisa_append_index_static", st)
     return out_idx, out_score, out_blk
 
 

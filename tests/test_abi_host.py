@@ -16,7 +16,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hisa.h")
 
-OK, ARG, UNSUP, WS, HIP = 0, -1, -2, -3, -4
+OK, ARG, UNSUP, WS, HIP, SCRATCH = 0, -1, -2, -3, -4, -5
 
 
 def declared_functions():
@@ -56,10 +56,11 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.hisa_abi_version() == 5
-    for code in (OK, ARG, UNSUP, WS, HIP, 12345):
+    assert lib.hisa_abi_version() == 6
+    for code in (OK, ARG, UNSUP, WS, HIP, SCRATCH, 12345):
         assert isinstance(lib.hisa_status_string(code), bytes)
     assert lib.hisa_status_string(WS) != lib.hisa_status_string(ARG)
+    assert lib.hisa_status_string(SCRATCH) not in (lib.hisa_status_string(WS), lib.hisa_status_string(12345))
     assert lib.hisa_kernel_kinds() >= 8
     assert lib.hisa_kernel_name(0) == b"pool_append"
 
@@ -129,6 +130,13 @@ def test_argument_checks_with_null_pointers(lib):
                                  None, None, None, None, 0, None) == UNSUP
     assert lib.hisa_append_index(None, 0, 10, 5, None, 0, None, None, None, 1, 1, 4, 64, 64, 2, 8,
                                  None, None, None, None, 0, None) == ARG   # L_new < L_old
+    # the static-scratch form of hisa_append_index: the same checks, nothing enqueued
+    assert lib.hisa_append_index_static(None, 0, 0, 10, None, 0, None, None, None, 1, 1, 4, 64, 64, 2, 8,
+                                        None, None, None, None) == ARG
+    assert lib.hisa_append_index_static(None, 0, 0, 10, None, 0, None, None, None, 1, 1, 4, 96, 64, 2, 8,
+                                        None, None, None, None) == UNSUP
+    assert lib.hisa_append_index_static(None, 0, 10, 5, None, 0, None, None, None, 1, 1, 4, 64, 64, 2, 8,
+                                        None, None, None, None) == ARG
     # the *_mode calls: an unknown pool kind, then the plain calls' checks
     assert lib.hisa_pool_append_mode(None, 0, 1, 64, 64, 0, 10, None, 0, 7, None) == ARG
     assert lib.hisa_pool_append_mode(None, 0, 1, 64, 64, 0, 10, None, 0, 1, None) == ARG
@@ -197,6 +205,15 @@ def test_argument_checks_with_placeholder_pointers(lib):
     assert lib.hisa_pool_append(p, kss, S, d, B, 0, L, p, 15 * d, None) == ARG
     assert lib.hisa_pool_append(p, kss, S, d, 24, 0, L, p, pss, None) == UNSUP
     assert lib.hisa_pool_append(p, kss, S, d, B, 5, 5, p, pss, None) == OK   # empty range: no work
+    # the static-scratch call: a problem whose workspace exceeds the 16 MiB
+    # array is refused before the device is looked at (4096 queries x 8192
+    # candidates need 128 MiB of candidate keys alone)
+    T2, L2 = 4096, 8192
+    assert lib.hisa_index_workspace(1, T2, H, d, L2, B, 128, k) > (16 << 20)
+    assert lib.hisa_append_index_static(p, L2 * d, 0, L2, p, 128 * d, p, p, None, 1, T2, H, d, B, 128, k, p, None,
+                                        None, None) == SCRATCH
+    assert lib.hisa_append_index_static(odd, L2 * d, 0, L2, p, 128 * d, p, p, None, 1, T2, H, d, B, 128, k, p, None,
+                                        None, None) == ARG
 
     def app(**kw):
         a = dict(K=p, kss=kss, L0=L - 1, L1=L, pool=p, pss=pss, q=p, w=p, qpos=None, S=S, T=T, H=H, d=d,

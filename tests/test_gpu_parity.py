@@ -51,7 +51,7 @@ def _run(hisa, case, qpos_on_device=True, want_flat=True):
 
 
 def test_abi_version(hisa):
-    assert hisa.hisa_abi_version() == 5
+    assert hisa.hisa_abi_version() == 6
 
 
 def test_binding_refuses_bad_outputs(hisa):
