@@ -587,11 +587,11 @@ int hisa_tree_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int 
     st = hip_status(launch_pool_append(K, k_seq_stride, S, d, B, blk0, nblk - blk0, L_new, pmax, pool_rep,
                                        pool_seq_stride, hs));
     if (st != HISA_OK) return st;
-    // next level up: the super-blocks holding those blocks, pooled over the
-    // block representatives as rows (G of them per super-block)
+    // next level up: the super-blocks holding those blocks, from their block
+    // representatives weighted by key counts
     const int64_t sb0 = blk0 / G;
-    return hip_status(launch_pool_append(pool_rep, pool_seq_stride, S, d, G, sb0, ceil_div(nblk, G) - sb0, nblk, pmax,
-                                         spool_rep, spool_seq_stride, hs));
+    return hip_status(launch_super_append(pool_rep, pool_seq_stride, S, d, B, G, sb0, ceil_div(nblk, G) - sb0, L_new,
+                                          pmax, spool_rep, spool_seq_stride, hs));
 }
 
 size_t hisa_tree_index_workspace(int S, int T, int H, int d, int64_t L, int B, int G, int W, int m, int k) {

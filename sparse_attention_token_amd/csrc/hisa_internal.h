@@ -156,6 +156,12 @@ hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, in
                               int64_t blk0, int64_t nblk, int64_t L_new, bool pool_max, uint16_t *pool,
                               int64_t pool_seq_stride, hipStream_t st);
 
+// Super-blocks [sb0, sb0 + nsb) of the three-level tree from the block pool of
+// a cache holding L_new rows (children weighted by their key counts).
+hipError_t launch_super_append(const uint16_t *pool, int64_t pool_seq_stride, int S, int d, int B, int G,
+                               int64_t sb0, int64_t nsb, int64_t L_new, bool pool_max, uint16_t *spool,
+                               int64_t spool_seq_stride, hipStream_t st);
+
 // Both tree levels in one launch when the new rows all lie in block blk (the
 // last one) and B <= 128: block blk from K, then its super-block from the pool.
 bool tree_append_one_supported(int B);
@@ -173,7 +179,8 @@ hipError_t launch_own_mean(const uint16_t *K, int64_t k_seq_stride, const int32_
                            hipStream_t st);
 
 // Own super-block representative of every query (three-level tree): pools the
-// block representatives pool[s][b] for st*G <= b < b_t, then own_rep[qi].
+// block representatives pool[s][b] for st*G <= b < b_t (B keys each), then
+// own_rep[qi] (t + 1 - b_t*B keys), weighted by those counts.
 hipError_t launch_own_super(const uint16_t *pool, int64_t pool_seq_stride, const uint16_t *own_rep,
                             const int32_t *qpos, int64_t L, int S, int T, int d, int B, int G, bool pool_max,
                             uint16_t *own_srep, hipStream_t st);

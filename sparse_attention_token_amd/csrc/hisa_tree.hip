@@ -7,7 +7,8 @@
 // query at t (b_t = t / B, u_t = b_t / G) does:
 //   1. score every super-block u <= u_t with the indexer score: the super pool
 //      entry for u < u_t, and for u_t the pooling of the pool entries
-//      u_t*G .. b_t-1 followed by the own-block representative (rows b_t*B..t);
+//      u_t*G .. b_t-1 followed by the own-block representative (rows b_t*B..t),
+//      each weighted by its key count (the mean over the super-block's tokens);
 //   2. keep the top W super-blocks;
 //   3. score the blocks b <= b_t inside them (pool entries, own block for b_t);
 //   4. keep the top m blocks.
@@ -112,15 +113,16 @@ __device__ __forceinline__ void score_into(const QFrag<MT, KS> &f, int n, uint32
 }
 
 // Own super-block representative: per column, the pool entries b0 .. bt-1 in
-// order and then the own-block representative, pooled like the pool's rows
-// (fp64 sum in order then bf16(fp32(sum / n)), or the first largest value).
+// order (B keys each) and then the own-block representative (own_cnt keys):
+// the count-weighted mean over the super-block's tokens, bf16(fp32(fp64
+// sum_b cnt_b * r_b in block order / sum_b cnt_b)), or the first largest value.
 template <bool MAX>
-__device__ __forceinline__ uint16_t super_column(const uint16_t *pool_col, int d, int64_t b0, int64_t bt,
-                                                 uint16_t own) {
+__device__ __forceinline__ uint16_t super_column(const uint16_t *pool_col, int d, int64_t b0, int64_t bt, int B,
+                                                 uint16_t own, int own_cnt) {
     double sum = 0.0;
     float bestf = -__builtin_huge_valf();
     uint16_t best = 0;
-    auto take = [&](uint16_t h) {
+    auto take = [&](uint16_t h, int cnt) {
         const float v = bf16_to_f32(h);
         if (MAX) {
             if (v > bestf) {
@@ -128,7 +130,7 @@ __device__ __forceinline__ uint16_t super_column(const uint16_t *pool_col, int d
                 best = h;
             }
         } else {
-            sum += static_cast<double>(v);
+            sum += static_cast<double>(v) * static_cast<double>(cnt);   // exact product
         }
     };
     int64_t b = b0;
@@ -137,11 +139,12 @@ __device__ __forceinline__ uint16_t super_column(const uint16_t *pool_col, int d
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = pool_col[(b + j) * d];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) take(x[j]);
+        for (int j = 0; j < 8; ++j) take(x[j], B);
     }
-    for (; b < bt; ++b) take(pool_col[b * d]);
-    take(own);
-    return MAX ? best : f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(bt - b0 + 1)));
+    for (; b < bt; ++b) take(pool_col[b * d], B);
+    take(own, own_cnt);
+    return MAX ? best
+               : f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>((bt - b0) * B + own_cnt)));
 }
 
 template <int MT, int KS, bool MAX>
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a) {
     __syncthreads();
     if (!own_from_pool) {
         own_rows_rep<D, 64, MAX>(s_own, own_rows, L.rep, nullptr);     // ends with a barrier
-        if (tid < D) L.srep[tid] = super_column<MAX>(pool + tid, D, st * a.G, bt, L.rep[tid]);
+        if (tid < D) L.srep[tid] = super_column<MAX>(pool + tid, D, st * a.G, bt, a.B, L.rep[tid], own_rows);
         __syncthreads();
     }
     const uint16_t *own_rep = own_from_pool ? pool + bt * D : L.rep;

@@ -53,6 +53,34 @@ struct ColumnRep {
     }
 };
 
+// Running summary of one column of a tree super-block over its child blocks,
+// added in block order, each child's representative h covering cnt keys: the
+// count-weighted fp64 sum (mean over the super-block's tokens; cnt * x is
+// exact, so a fused multiply-add rounds exactly as the product then the sum),
+// or the largest value so far, the earliest kept on equal values.
+template <bool MAX>
+struct SuperRep {
+    double sum = 0.0;
+    int64_t total = 0;
+    float bestf = -__builtin_huge_valf();
+    uint16_t best = 0;
+    __device__ __forceinline__ void add(uint16_t h, int64_t cnt) {
+        const float x = bf16_to_f32(h);
+        if (MAX) {
+            if (x > bestf) {
+                bestf = x;
+                best = h;
+            }
+        } else {
+            sum += static_cast<double>(x) * static_cast<double>(cnt);
+            total += cnt;
+        }
+    }
+    __device__ __forceinline__ uint16_t get() const {
+        return MAX ? best : f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>(total)));
+    }
+};
+
 // Copy rows [0, rows) of `src` (row stride d elements) into LDS and return the
 // bf16 representative of column threadIdx.x (threads >= d return 0 and write nothing).
 template <bool MAX>
@@ -130,7 +158,7 @@ __global__ __launch_bounds__(kMaxD) void pool_append_direct_kernel(
 // in block b (B <= kDirectRows, b the cache's last block): block b is
 // recomputed as in pool_append_direct_kernel, then its super-block u = b / G,
 // whose children are the blocks u*G .. b, from their pool entries in order
-// with block b's new representative last.
+// (B keys each) with block b's new representative last (its row count).
 template <bool MAX>
 __global__ __launch_bounds__(kMaxD) void tree_append_one_kernel(
         const uint16_t *__restrict__ K, int64_t k_seq_stride, int d, int B, int G, int64_t b, int64_t L_new,
@@ -155,14 +183,14 @@ __global__ __launch_bounds__(kMaxD) void tree_append_one_kernel(
     const int64_t b0 = b / G * G;
     const int nchild = static_cast<int>(b - b0);
     const uint16_t *pcol = pool + s * pool_seq_stride + b0 * d + col;
-    ColumnRep<MAX> sup;
+    SuperRep<MAX> sup;
     for (int c0 = 0; c0 < nchild; c0 += kChildRound) {
         uint16_t y[kChildRound];
 #pragma unroll
         for (int j = 0; j < kChildRound; ++j) y[j] = pcol[(c0 + j < nchild ? c0 + j : 0) * d];
 #pragma unroll
         for (int j = 0; j < kChildRound; ++j)
-            if (c0 + j < nchild) sup.add(y[j]);
+            if (c0 + j < nchild) sup.add(y[j], B);
     }
     ColumnRep<MAX> acc;
 #pragma unroll
@@ -170,8 +198,39 @@ __global__ __launch_bounds__(kMaxD) void tree_append_one_kernel(
         if (r < rows) acc.add(x[r]);
     const uint16_t rep = acc.get(rows);
     pool[s * pool_seq_stride + b * d + col] = rep;
-    sup.add(rep);
-    spool[s * spool_seq_stride + (b / G) * d + col] = sup.get(b - b0 + 1);
+    sup.add(rep, rows);
+    spool[s * spool_seq_stride + (b / G) * d + col] = sup.get();
+}
+
+// grid: (nsb, S), d threads.  Super-blocks [sb0, sb0 + nsb) of the three-level
+// tree from the block pool of a cache holding L_new rows: super-block u pools
+// its blocks u*G .. min(u*G + G, nblk) - 1 in order, each weighted by its key
+// count (B, and L_new - b*B for a short last block).
+template <bool MAX>
+__global__ __launch_bounds__(kMaxD) void super_append_kernel(
+        const uint16_t *__restrict__ pool, int64_t pool_seq_stride, int d, int B, int G, int64_t sb0, int64_t L_new,
+        uint16_t *__restrict__ spool, int64_t spool_seq_stride) {
+    const int s = blockIdx.y;
+    const int col = threadIdx.x;
+    if (col >= d) return;
+    const int64_t u = sb0 + blockIdx.x;
+    const int64_t nblk = (L_new + B - 1) / B;
+    const int64_t b0 = u * G;
+    const int64_t b1 = (b0 + G < nblk) ? b0 + G : nblk;
+    const uint16_t *pcol = pool + s * pool_seq_stride + col;
+    SuperRep<MAX> sup;
+    constexpr int kRound = 16;                          // loads in flight, added in block order
+    for (int64_t c0 = b0; c0 < b1; c0 += kRound) {
+        uint16_t y[kRound];
+#pragma unroll
+        for (int j = 0; j < kRound; ++j) y[j] = pcol[(c0 + j < b1 ? c0 + j : b0) * d];
+#pragma unroll
+        for (int j = 0; j < kRound; ++j) {
+            const int64_t b = c0 + j;
+            if (b < b1) sup.add(y[j], (b + 1) * B <= L_new ? B : L_new - b * B);
+        }
+    }
+    spool[s * spool_seq_stride + u * d + col] = sup.get();
 }
 
 // grid: (nblk, S).  Recomputes blocks [blk0, blk0 + nblk) over rows < L_new.
@@ -260,8 +319,9 @@ __global__ __launch_bounds__(kMaxD) void own_prefix_mean_kernel(
 
 // grid: (S*T), d threads.  Own super-block representative of the three-level
 // tree: a super-block pools the representatives of its G blocks in block
-// order, and the one holding t covers its blocks up to b_t, the last of them
-// being the query's own-block representative own_rep[qi].
+// order, each weighted by its key count, and the one holding t covers its
+// blocks up to b_t: the complete ones (B keys each), then the query's
+// own-block representative own_rep[qi] (t + 1 - b_t*B keys).
 template <bool MAX>
 __global__ __launch_bounds__(kMaxD) void own_super_kernel(
         const uint16_t *__restrict__ pool, int64_t pool_seq_stride, const uint16_t *__restrict__ own_rep,
@@ -275,18 +335,18 @@ __global__ __launch_bounds__(kMaxD) void own_super_kernel(
     const int64_t bt = t / B;
     const int64_t b0 = bt / G * G;
     const uint16_t *src = pool + s * pool_seq_stride + col;
-    ColumnRep<MAX> acc;
+    SuperRep<MAX> acc;
     int64_t b = b0;
     for (; b + 8 <= bt; b += 8) {                      // 8 loads in flight, added in block order
         uint16_t x[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = src[(b + j) * d];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc.add(x[j]);
+        for (int j = 0; j < 8; ++j) acc.add(x[j], B);
     }
-    for (; b < bt; ++b) acc.add(src[b * d]);
-    acc.add(own_rep[static_cast<int64_t>(qi) * d + col]);
-    own_srep[static_cast<int64_t>(qi) * d + col] = acc.get(bt - b0 + 1);
+    for (; b < bt; ++b) acc.add(src[b * d], B);
+    acc.add(own_rep[static_cast<int64_t>(qi) * d + col], t + 1 - bt * B);
+    own_srep[static_cast<int64_t>(qi) * d + col] = acc.get();
 }
 
 }  // namespace
@@ -328,6 +388,17 @@ hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, in
                       B, blk0, L_new, pool, pool_seq_stride);
     return launch(kKindPoolAppend, pool_append_kernel<false>, g, dim3(kPoolThreads), 0, st, K, k_seq_stride, d, B,
                   blk0, L_new, pool, pool_seq_stride);
+}
+
+hipError_t launch_super_append(const uint16_t *pool, int64_t pool_seq_stride, int S, int d, int B, int G,
+                               int64_t sb0, int64_t nsb, int64_t L_new, bool pool_max, uint16_t *spool,
+                               int64_t spool_seq_stride, hipStream_t st) {
+    const dim3 g(static_cast<uint32_t>(nsb), S);
+    if (pool_max)
+        return launch(kKindPoolAppend, super_append_kernel<true>, g, dim3(kMaxD), 0, st, pool, pool_seq_stride, d, B,
+                      G, sb0, L_new, spool, spool_seq_stride);
+    return launch(kKindPoolAppend, super_append_kernel<false>, g, dim3(kMaxD), 0, st, pool, pool_seq_stride, d, B, G,
+                  sb0, L_new, spool, spool_seq_stride);
 }
 
 bool tree_append_one_supported(int B) { return B <= kDirectRows; }
