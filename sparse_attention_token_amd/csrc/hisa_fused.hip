@@ -84,13 +84,16 @@ __device__ __forceinline__ int k1_slot(int p, int nb) {
 }
 
 template <int R, typename Emit>
-__device__ __forceinline__ uint32_t k1_wave_select(const uint32_t *s_keys, int nb, int m, Emit &emit) {
+__device__ __forceinline__ uint32_t k1_wave_select(const uint32_t *s_keys, int nb, int m, uint32_t *win, Emit &emit) {
     const int lane = threadIdx.x & 63;
     const int rd = (nb + 63) / 64;
     uint32_t kv[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) kv[r] = (r < rd && lane * rd + r < nb) ? s_keys[r * 64 + lane] : kNoCandidate;
-    const SelectResult res = wave_ballot_select<R>(kv, static_cast<uint32_t>(m));
+    // up to 256 keys the ballot select's 32 short rounds cost less than the
+    // histogram's set-up; beyond, its rounds grow with R and the window wins
+    const SelectResult res = R <= 4 ? wave_ballot_select<R>(kv, static_cast<uint32_t>(m))
+                                    : wave_window_select<R>(kv, static_cast<uint32_t>(m), win);
     if (res.keff > 0)
         wave_compact<R>(kv, res, [&](uint32_t op, int r, uint32_t) { emit(op, lane * rd + r); });
     return res.keff;
@@ -101,7 +104,7 @@ struct BlockStageLds {
     static constexpr int kOwnWords = kFusedOwnElems / 2;
     uint16_t q[64 * QStage<KS>::kStride];
     float w[64];                        // head weights, zero past H
-    uint32_t own[kOwnWords];            // own-block rows
+    uint32_t own[kOwnWords];            // own-block rows; after the block stage, the top m's window
     uint16_t mean[128];
 };
 
@@ -204,14 +207,16 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
 }
 
 // One wave selects the top m of the nb <= 2048 block keys; emit(slot, block).
+// win: kWindowWords words of LDS for the select's histogram.
 template <typename Emit>
-__device__ __forceinline__ uint32_t block_topm_wave(const uint32_t *s_keys, int nb, int m, Emit &&emit) {
+__device__ __forceinline__ uint32_t block_topm_wave(const uint32_t *s_keys, int nb, int m, uint32_t *win,
+                                                    Emit &&emit) {
     const int rd = (nb + 63) / 64;
     uint32_t ke;
-    if (rd <= 4) ke = k1_wave_select<4>(s_keys, nb, m, emit);
-    else if (rd <= 8) ke = k1_wave_select<8>(s_keys, nb, m, emit);
-    else if (rd <= 16) ke = k1_wave_select<16>(s_keys, nb, m, emit);
-    else ke = k1_wave_select<32>(s_keys, nb, m, emit);
+    if (rd <= 4) ke = k1_wave_select<4>(s_keys, nb, m, win, emit);
+    else if (rd <= 8) ke = k1_wave_select<8>(s_keys, nb, m, win, emit);
+    else if (rd <= 16) ke = k1_wave_select<16>(s_keys, nb, m, win, emit);
+    else ke = k1_wave_select<32>(s_keys, nb, m, win, emit);
     return ke;
 }
 
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(kK1Threads) void hisa_blocks_topm_kernel(FusedArgs 
     if (nb <= kK1WaveMax) {
         // short rows: one wave, no barriers
         if (wave == 0) {
-            const uint32_t ke = block_topm_wave(s_keys, nb, a.m, [&](uint32_t op, int pos) {
+            const uint32_t ke = block_topm_wave(s_keys, nb, a.m, L.own, [&](uint32_t op, int pos) {
                 sel[op] = pos;
                 if (ob) ob[op] = pos;
             });
@@ -342,7 +347,7 @@ __global__ __launch_bounds__(DT) void hisa_decode_kernel(FusedArgs a) {
     QFrag<MT, KS> f;
     block_stage<MT, KS, DT, DT == 256 ? 4 : 2>(a, qi, s, t, L, s_keys, f, lead);
     if (wave == 0) {
-        const uint32_t ke = block_topm_wave(s_keys, nb, a.m, [&](uint32_t op, int pos) {
+        const uint32_t ke = block_topm_wave(s_keys, nb, a.m, L.own, [&](uint32_t op, int pos) {
             s_sel[op] = pos;
             if (lead) {
                 sel[op] = pos;
@@ -483,7 +488,8 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs 
 }
 
 template <int R, typename Emit>
-__device__ __forceinline__ uint32_t dgather_topm(const uint32_t *keys, int nb, int m, int lane, Emit &&emit) {
+__device__ __forceinline__ uint32_t dgather_topm(const uint32_t *keys, int nb, int m, int lane, uint32_t *win,
+                                                 Emit &&emit) {
     const int rd = (nb + 63) / 64;
     uint32_t kv[R];
 #pragma unroll
@@ -491,7 +497,8 @@ __device__ __forceinline__ uint32_t dgather_topm(const uint32_t *keys, int nb, i
         const int p = lane * rd + r;
         kv[r] = (r < rd && p < nb) ? keys[p] : kNoCandidate;
     }
-    const SelectResult res = wave_ballot_select<R>(kv, static_cast<uint32_t>(m));
+    const SelectResult res = R <= 4 ? wave_ballot_select<R>(kv, static_cast<uint32_t>(m))
+                                    : wave_window_select<R>(kv, static_cast<uint32_t>(m), win);
     if (res.keff > 0) wave_compact<R>(kv, res, [&](uint32_t op, int r, uint32_t) { emit(op, lane * rd + r); });
     return res.keff;
 }
@@ -503,6 +510,7 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs 
     __shared__ __attribute__((aligned(16))) uint16_t s_q[64 * QStage<KS>::kStride];
     __shared__ float s_w[64];
     __shared__ int32_t s_sel[kDecodeMaxM];
+    __shared__ __attribute__((aligned(16))) uint32_t s_win[kWindowWords];
     __shared__ uint32_t s_keff;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -547,12 +555,12 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs 
         // the ballot select's work grows with R: above 16 keep R close to rd
         // (1025 blocks, rd = 17: R = 20 took the kernel from 17.3 to 13.9 us;
         // R = 12 for rd = 9 was slower than 16)
-        if (rd <= 4) ke = dgather_topm<4>(keys, nb, a.m, lane, emit);
-        else if (rd <= 8) ke = dgather_topm<8>(keys, nb, a.m, lane, emit);
-        else if (rd <= 16) ke = dgather_topm<16>(keys, nb, a.m, lane, emit);
-        else if (rd <= 20) ke = dgather_topm<20>(keys, nb, a.m, lane, emit);
-        else if (rd <= 24) ke = dgather_topm<24>(keys, nb, a.m, lane, emit);
-        else ke = dgather_topm<32>(keys, nb, a.m, lane, emit);
+        if (rd <= 4) ke = dgather_topm<4>(keys, nb, a.m, lane, s_win, emit);
+        else if (rd <= 8) ke = dgather_topm<8>(keys, nb, a.m, lane, s_win, emit);
+        else if (rd <= 16) ke = dgather_topm<16>(keys, nb, a.m, lane, s_win, emit);
+        else if (rd <= 20) ke = dgather_topm<20>(keys, nb, a.m, lane, s_win, emit);
+        else if (rd <= 24) ke = dgather_topm<24>(keys, nb, a.m, lane, s_win, emit);
+        else ke = dgather_topm<32>(keys, nb, a.m, lane, s_win, emit);
         if (lane == 0) s_keff = ke;
     }
     qst.store(s_q, tid);

@@ -417,7 +417,7 @@ constexpr int kTopMThreads = 256;
 
 template <int R, typename Emit>
 __device__ __forceinline__ uint32_t topm_select(const uint32_t *keys, uint32_t own_key, int nb, int m, int lane,
-                                                Emit &&emit) {
+                                                uint32_t *win, Emit &&emit) {
     const int rd = (nb + 63) / 64;
     uint32_t kv[R];
 #pragma unroll
@@ -425,7 +425,10 @@ __device__ __forceinline__ uint32_t topm_select(const uint32_t *keys, uint32_t o
         const int p = lane * rd + r;
         kv[r] = (r < rd && p < nb) ? (p == nb - 1 ? own_key : keys[p]) : kNoCandidate;
     }
-    const SelectResult res = wave_ballot_select<R>(kv, static_cast<uint32_t>(m));
+    // the ballot select for up to 256 blocks; beyond, its rounds grow with R
+    // and the LDS histogram of wave_window_select costs less
+    const SelectResult res = R <= 4 ? wave_ballot_select<R>(kv, static_cast<uint32_t>(m))
+                                    : wave_window_select<R>(kv, static_cast<uint32_t>(m), win);
     if (res.keff > 0) wave_compact<R>(kv, res, [&](uint32_t op, int r, uint32_t) { emit(op, lane * rd + r); });
     return res.keff;
 }
@@ -433,6 +436,7 @@ __device__ __forceinline__ uint32_t topm_select(const uint32_t *keys, uint32_t o
 template <int MT, int KS>
 __global__ __launch_bounds__(kTopMThreads) void hisa_topm_kernel(FusedArgs a) {
     constexpr int D = 32 * KS;
+    __shared__ __attribute__((aligned(16))) uint32_t s_win[kTopMThreads / 64][kWindowWords];
     const int lane = threadIdx.x & 63;
     const int qi = blockIdx.x * (kTopMThreads / 64) + (threadIdx.x >> 6);
     if (qi >= a.S * a.T) return;                       // whole wave
@@ -457,10 +461,11 @@ __global__ __launch_bounds__(kTopMThreads) void hisa_topm_kernel(FusedArgs a) {
             if (ob) ob[op] = pos;
         };
         const int rd = (nb + 63) / 64;
-        if (rd <= 4) keff = topm_select<4>(keys, own_key, nb, a.m, lane, emit);
-        else if (rd <= 8) keff = topm_select<8>(keys, own_key, nb, a.m, lane, emit);
-        else if (rd <= 16) keff = topm_select<16>(keys, own_key, nb, a.m, lane, emit);
-        else keff = topm_select<32>(keys, own_key, nb, a.m, lane, emit);
+        uint32_t *win = s_win[threadIdx.x >> 6];
+        if (rd <= 4) keff = topm_select<4>(keys, own_key, nb, a.m, lane, win, emit);
+        else if (rd <= 8) keff = topm_select<8>(keys, own_key, nb, a.m, lane, win, emit);
+        else if (rd <= 16) keff = topm_select<16>(keys, own_key, nb, a.m, lane, win, emit);
+        else keff = topm_select<32>(keys, own_key, nb, a.m, lane, win, emit);
     }
     for (int j = static_cast<int>(keff) + lane; j < a.m; j += 64) {
         sel[j] = -1;

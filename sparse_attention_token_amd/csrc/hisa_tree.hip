@@ -51,6 +51,7 @@ struct TreeTopLds {
     uint32_t keys[kTopMaxRows];        // keys by select slot
     int32_t sb[kTopMaxRows];           // kept super-blocks, ascending
     uint32_t keff;
+    OwnRepScratch ors;
 };
 
 // Select slot of position p among n <= 2048: lane p / rd holds it in register
@@ -61,9 +62,10 @@ __device__ __forceinline__ int top_slot(int p, int n) {
 }
 
 // One wave: top kout of the n keys in s_keys; emit(op, position) for each kept
-// one in increasing position order.  Returns the number kept.
+// one in increasing position order.  Returns the number kept.  win: 2112 words
+// of LDS for the select's histogram.
 template <typename Emit>
-__device__ __forceinline__ uint32_t top_select(const uint32_t *s_keys, int n, int kout, Emit &&emit) {
+__device__ __forceinline__ uint32_t top_select(const uint32_t *s_keys, int n, int kout, uint32_t *win, Emit &&emit) {
     const int lane = threadIdx.x & 63;
     const int rd = (n + 63) / 64;
     auto run = [&](auto tag) -> uint32_t {
@@ -71,7 +73,8 @@ __device__ __forceinline__ uint32_t top_select(const uint32_t *s_keys, int n, in
         uint32_t kv[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) kv[r] = (r < rd && lane * rd + r < n) ? s_keys[r * 64 + lane] : kNoCandidate;
-        const SelectResult res = wave_ballot_select<R>(kv, static_cast<uint32_t>(kout));
+        const SelectResult res = R <= 4 ? wave_ballot_select<R>(kv, static_cast<uint32_t>(kout))
+                                        : wave_window_select<R>(kv, static_cast<uint32_t>(kout), win);
         if (res.keff > 0) wave_compact<R>(kv, res, [&](uint32_t op, int r, uint32_t) { emit(op, lane * rd + r); });
         return res.keff;
     };
@@ -198,7 +201,7 @@ __global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a) {
     if (tid < 64) L.w[tid] = wq;
     __syncthreads();
     if (!own_from_pool) {
-        own_rows_rep<D, 64, MAX>(s_own, own_rows, L.rep, nullptr);     // ends with a barrier
+        own_rows_rep_par<D, kTopThreads, MAX>(s_own, own_rows, L.rep, nullptr, L.ors);   // ends with a barrier
         if (tid < D) L.srep[tid] = super_column<MAX>(pool + tid, D, st * a.G, bt, a.B, L.rep[tid], own_rows);
         __syncthreads();
     }
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a) {
         return u < st ? spool + static_cast<int64_t>(u) * D : own_srep;
     });
     if (wave == 0) {
-        const uint32_t ke = top_select(L.keys, ns, a.W, [&](uint32_t op, int u) {
+        const uint32_t ke = top_select(L.keys, ns, a.W, L.own, [&](uint32_t op, int u) {
             L.sb[op] = u;
             if (osb) osb[op] = u;
         });
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a) {
         return b < bt ? pool + b * D : (b == bt ? own_rep : nullptr);
     });
     if (wave == 0) {
-        const uint32_t ke = top_select(L.keys, nt, a.m, [&](uint32_t op, int p) {
+        const uint32_t ke = top_select(L.keys, nt, a.m, L.own, [&](uint32_t op, int p) {
             const int slot = p / a.G;
             const int32_t b = L.sb[slot] * a.G + (p - slot * a.G);
             sel[op] = b;

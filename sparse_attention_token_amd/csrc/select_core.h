@@ -19,10 +19,18 @@
 //      #keys == K*) per thread gives each kept key its slot; keys equal to K*
 //      are kept lowest position first.
 //
+// One wave alone (top m over at most 2048 block keys): wave_ballot_select
+// finds K* bit by bit with ballots (about 110 cycles a round, 32 rounds), and
+// wave_window_select takes one LDS histogram over the four binades below the
+// best key instead, which costs less once a lane holds more than 4 keys.
+//
 // Costs on gfx950 that shaped this: LDS atomics to one address from many lanes
 // serialize (about 16x a conflict-free one), cross-lane shuffles through LDS
 // cost about 75 cycles each while DPP row operations cost a few, and 16-byte
-// LDS reads whose lanes stride by 128 bytes conflict on every bank.
+// LDS reads whose lanes stride by 128 bytes conflict on every bank.  A
+// workgroup's select over 8192 keys is bound by its one CU's vector ALUs (some
+// 30 operations a key): a histogram range fitted to the keys, which avoids
+// the atomics' contention, measured no faster there.
 #pragma once
 
 #include "hisa_internal.h"
@@ -53,6 +61,9 @@ struct SelectScratch {
 
 // Block-wide exclusive prefix over threads of a per-thread count; also returns
 // the block total.  Uses sc.wave_tot; ends with the wave totals consumed.
+// After the exchange each wave reads the NW wave totals with one lane-parallel
+// LDS load (lane w takes wave w's) and scans them with DPP, rather than every
+// thread reading all NW of them.
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive(uint32_t v, uint32_t &total, SelectScratch &sc) {
     constexpr int NW = NT / 64;
@@ -60,14 +71,10 @@ __device__ __forceinline__ uint32_t block_exclusive(uint32_t v, uint32_t &total,
     const uint32_t incl = wave_prefix_incl(v);
     if (lane == 63) sc.wave_tot[wave] = incl;
     __syncthreads();
-    uint32_t before = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const uint32_t x = sc.wave_tot[w];
-        before += w < wave ? x : 0u;
-        tot += x;
-    }
-    total = tot;
+    const uint32_t wt = wave_prefix_incl(lane < NW ? sc.wave_tot[lane] : 0u);
+    const uint32_t before =
+        wave == 0 ? 0u : static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wt), wave - 1));
+    total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wt), NW - 1));
     return before + incl - v;
 }
 
@@ -225,6 +232,134 @@ __device__ __forceinline__ SelectResult wave_ballot_select(const uint32_t (&kv)[
 #pragma unroll
     for (int r = 0; r < R; ++r) gt += static_cast<uint32_t>(__popcll(__ballot(kv[r] > prefix)));
     return SelectResult{prefix, keff - gt, keff};
+}
+
+// Reduction across a 64-lane wave with DPP row shifts and row broadcasts;
+// lanes past a row edge contribute `id`.  Every lane gets lane 63's result.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x, uint32_t id, Op op) {
+    const int i = static_cast<int>(id);
+    x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(i, static_cast<int>(x), 0x111, 0xf, 0xf, false)));
+    x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(i, static_cast<int>(x), 0x112, 0xf, 0xf, false)));
+    x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(i, static_cast<int>(x), 0x114, 0xf, 0xf, false)));
+    x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(i, static_cast<int>(x), 0x118, 0xf, 0xf, false)));
+    x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(i, static_cast<int>(x), 0x142, 0xa, 0xf, false)));
+    x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(i, static_cast<int>(x), 0x143, 0xc, 0xf, false)));
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+
+constexpr int kWindowWords = 2048 + 64;    // LDS words of one wave_window_select
+
+// One-wave select with the contract of wave_ballot_select, through an LDS
+// histogram fitted to the keys: no workgroup barrier, and a handful of short
+// steps instead of up to 32 ballot rounds.
+//   1. The largest key kmax (a DPP reduction).  The window [lo, kmax] with
+//      lo = kmax - (4 << 23) holds the scores within a factor 16 of the
+//      largest (subtracting 4 << 23 from a key divides a positive score by 16);
+//      digit(key) = (key - lo) >> shift spreads it over 2048 bins.
+//   2. A histogram of the window's keys (LDS atomics, spread over the bins);
+//      lane l then owns 32 bins from the top, and a DPP prefix over the lanes'
+//      counts gives the bin holding the k_eff-th key.
+//   3. Every key of that bin kept, or the bin one key value: done.  Otherwise
+//      its keys (at most 64) are gathered in LDS and ranked against each other,
+//      one per lane.
+// Fewer than k_eff keys in the window, or more than 64 in the cutoff bin: the
+// ballot select does it instead.  lds: kWindowWords words of LDS that no
+// other wave touches meanwhile.
+template <int R>
+__device__ __forceinline__ SelectResult wave_window_select(const uint32_t (&kv)[R], uint32_t kout, uint32_t *lds) {
+    constexpr int kBins = 2048;
+    const int lane = threadIdx.x & 63;
+    uint32_t nvalid = 0, mx = 0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        nvalid += static_cast<uint32_t>(__popcll(__ballot(kv[r] != kNoCandidate)));
+        mx = kv[r] > mx ? kv[r] : mx;
+    }
+    const uint32_t keff = nvalid < kout ? nvalid : kout;
+    if (keff == 0 || keff == nvalid) return SelectResult{0u, 0u, keff};   // nothing, or every key > 0
+    const uint32_t kmax = wave_reduce(mx, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+    constexpr uint32_t kWindow = 4u << 23;
+    const uint32_t lo = kmax > kWindow ? kmax - kWindow : 1u;
+    const int bits = 32 - __clz(kmax - lo);
+    const int shift = bits > 11 ? bits - 11 : 0;
+    uint32_t *hist = lds, *bin = lds + kBins;
+#pragma unroll
+    for (int i = 0; i < kBins / 256; ++i)
+        *reinterpret_cast<sel_u32x4 *>(&hist[(i * 64 + lane) * 4]) = sel_u32x4{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (kv[r] != kNoCandidate && kv[r] >= lo) atomicAdd(&hist[(kv[r] - lo) >> shift], 1u);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // lane l owns bins [kBins - 32(l+1), kBins - 32 l), highest first
+    uint32_t hb[32];
+    const int b0 = kBins - 32 * (lane + 1);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        const sel_u32x4 x = *reinterpret_cast<const sel_u32x4 *>(&hist[b0 + 4 * v]);
+        hb[4 * v + 0] = x[0]; hb[4 * v + 1] = x[1]; hb[4 * v + 2] = x[2]; hb[4 * v + 3] = x[3];
+    }
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) c += hb[j];
+    const uint32_t incl = wave_prefix_incl(c);
+    const uint32_t total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+    if (total < keff) return wave_ballot_select<R>(kv, kout);    // the cutoff lies below the window
+    const uint32_t above_me = incl - c;
+    // the lane whose bins hold the k_eff-th key finds the bin
+    uint32_t dig = 0, abv = 0, cnt = 0;
+    const bool mine = above_me < keff && above_me + c >= keff;
+    if (mine) {
+        uint32_t above = above_me;
+        bool done = false;
+#pragma unroll
+        for (int j = 31; j >= 0; --j) {
+            if (!done) {
+                if (above + hb[j] >= keff) {
+                    dig = static_cast<uint32_t>(b0 + j);
+                    abv = above;
+                    cnt = hb[j];
+                    done = true;
+                } else {
+                    above += hb[j];
+                }
+            }
+        }
+    }
+    const int owner = __builtin_ctzll(__ballot(mine));
+    const uint32_t dstar = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(dig), owner));
+    const uint32_t need = keff - static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(abv), owner));
+    const uint32_t in_bin = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(cnt), owner));
+    const uint32_t blo = lo + (dstar << shift);
+    if (need == in_bin) return SelectResult{blo - 1u, 0u, keff};   // the keys >= blo
+    if (shift == 0) return SelectResult{blo, need, keff};         // the bin is one key value
+    if (in_bin > 64u) return wave_ballot_select<R>(kv, kout);
+    // gather the bin's keys into LDS (slots by ballot prefix), one per lane
+    uint32_t base = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const bool inb = kv[r] != kNoCandidate && kv[r] >= lo && ((kv[r] - lo) >> shift) == dstar;
+        const uint64_t bal = __ballot(inb);
+        if (inb) bin[base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u))] = kv[r];
+        base += static_cast<uint32_t>(__popcll(bal));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // lane j ranks bin key j against the others (broadcast from their lanes):
+    // K* has fewer than `need` keys above it and at least `need` at or above it
+    const uint32_t me = static_cast<uint32_t>(lane) < in_bin ? bin[lane] : 0u;
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t i = 0; i < in_bin; ++i) {
+        const uint32_t o = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(me), static_cast<int>(i)));
+        gt += o > me ? 1u : 0u;
+        ge += o >= me ? 1u : 0u;
+    }
+    const bool is_k = static_cast<uint32_t>(lane) < in_bin && gt < need && ge >= need;
+    const int kl = __builtin_ctzll(__ballot(is_k));
+    const uint32_t kstar = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(me), kl));
+    const uint32_t gtk = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(gt), kl));
+    return SelectResult{kstar, need - gtk, keff};
 }
 
 template <int R, typename Emit>

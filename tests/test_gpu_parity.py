@@ -331,6 +331,18 @@ def test_tree_index(hisa, orc, spec):
     _say(f"  {rep}")
 
 
+def test_tree_wide_exponent_spread(hisa, orc):
+    # the tree's one-launch upper levels average a query's own block over its
+    # threads; rows of very different magnitudes make the partial fp64 sums
+    # round, so the average must fall back to the row-order sum
+    c = synth.clustered_case(1, 4096, 6, 16, 128, 128, 4, 200, seed=33,
+                             qpos=[[4000, 4001, 3970, 4095, 2100, 129]])
+    c = _wide_spread_keys(c, 6)
+    (idx, sc, blk, sblk), dev, reps = _run_tree(hisa, c, 4, 3, True, "mean")
+    for i in range(c.T):
+        check_tree_row(orc, c, 0, i, 4, 3, idx[0, i], sc[0, i], blk[0, i], sblk[0, i])
+
+
 def test_tree_benchmark_configuration(hisa, orc):
     """The tree in the benchmark's launch configuration: decode, 4 sequences x 1M keys, super-blocks
     of 64 blocks, 16 kept; the pools built by a bulk append and one single-row append (the fused
@@ -572,6 +584,69 @@ def test_many_equal_scores(hisa, orc):
         np.testing.assert_array_equal(np.sort(out["fidx"][0, i]), np.sort(o_idx))
         np.testing.assert_array_equal(np.sort(out["idx"][0, i]), np.sort(o_idx))
     _say(f"many ties: {rep}")
+
+
+# Block-score distributions that drive the one-wave top m over more than 256
+# blocks (an LDS histogram over the four binades below the best score) down
+# each of its branches: every key of the cutoff bin kept ("spread"); the
+# cutoff bin resolved by ranking its few keys ("near": block scores within
+# 30% of each other); a run of equal scores too long to rank ("ties": the
+# ballot select takes over); and a best block so far above the rest that the
+# cutoff lies below the window ("outlier": ditto).
+WINDOW_CASES = ["spread", "near", "ties", "outlier"]
+
+
+def _window_case(kind, B, T):
+    import dataclasses
+
+    nb = 700
+    L = B * nb
+    qpos = [[L - T + i for i in range(T)]] * 2
+    c = synth.gaussian_case(2, L, T, 4, 64, B, 40, 300, seed=71, qpos=qpos)
+    if kind == "spread":
+        return c
+    rng = np.random.default_rng(9)
+    base = rng.standard_normal(64).astype(np.float32)
+    K = np.empty((2, L, 64), dtype=np.float32)
+    if kind == "ties":
+        # blocks cycle through three constant rows: three block scores,
+        # hundreds of blocks each
+        rows = rng.standard_normal((3, 64)).astype(np.float32)
+        for b in range(nb):
+            K[:, B * b:B * (b + 1)] = rows[b % 3]
+    else:
+        # every block a scaled copy of one row, scales in [1, 1.3)
+        scale = 1.0 + 0.3 * rng.random((2, nb)).astype(np.float32)
+        K[:] = np.repeat(scale, B, axis=1)[:, :, None] * base
+        if kind == "outlier":
+            K[:, B * 350:B * 351] *= 4096.0
+    # queries along the same row with positive weights: the scores follow the scales
+    q = np.broadcast_to(base, (2, T, 4, 64)).astype(np.float32)
+    w = np.abs(rng.standard_normal((2, T, 4))).astype(np.float32) + 0.1
+    return dataclasses.replace(c, K=synth.bf16_bits(K), q=synth.bf16_bits(q), w=w)
+
+
+def bf16_to_f32_np(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# (path, B, T): two-kernel decode; query-major batch; block-by-block chunk
+WINDOW_PATHS = [("decode", 16, 1), ("batch", 16, 160), ("chunk", 64, 160)]
+
+
+@pytest.mark.parametrize("kind", WINDOW_CASES)
+@pytest.mark.parametrize("path", WINDOW_PATHS, ids=[p[0] for p in WINDOW_PATHS])
+def test_window_top_m_branches(hisa, orc, kind, path):
+    """700 blocks per query, so each path keeps its top m with the one-wave
+    window select; blocks and tokens are checked against the oracle on
+    sampled queries of both sequences."""
+    name, B, T = path
+    c = _window_case(kind, B, T)
+    _say(f"window top m: {kind} {name}")
+    out = _run(hisa, c, want_flat=False)
+    for s_ in range(2):
+        for i in sorted({0, T // 2, T - 1}):
+            check_hisa_row(orc, c, s_, i, out["idx"][s_, i], out["sc"][s_, i], out["blk"][s_, i])
 
 
 @pytest.mark.parametrize("B", [64, 128])
