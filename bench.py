@@ -37,7 +37,8 @@ sys.path.insert(0, ROOT)
 METRIC = "indexer queries/s & µs/query at L=32K/64K/128K; speedup vs flat DSA; % roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
-DEFAULT_WORKLOAD = 1
+DEFAULT_WORKLOAD = 1          # decode 8 x 32K keys: the headline
+SUB_WORKLOADS = (2, 3, 4)     # decode 64K with needles, decode 128K + 77-row tail, prefill chunk
 
 
 def parse():
@@ -45,9 +46,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
-    p.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD,
+    p.add_argument("--workload", type=int, default=None,
                    help="0 tiny, 1 decode 32K, 2 decode 64K, 3 decode 128K, 4 prefill chunk, "
-                        "5 decode 1M, 6 decode 4M")
+                        "5 decode 1M, 6 decode 4M (default: decode 32K as the headline, with 64K, "
+                        "128K and the prefill chunk as sub-records)")
     p.add_argument("--tree", default=None, metavar="G,W",
                    help="time the three-level tree (super-blocks of G blocks, W kept) as the step")
     p.add_argument("--rotate-mib", type=int, default=1024,
@@ -62,6 +64,9 @@ def parse():
     p.add_argument("--attention", action="store_true",
                    help="also time the sparse attention over the indexer's output (latent rows of 576 entries, "
                         "512-entry values, 128 heads)")
+    p.add_argument("--sweep-lengths", action="store_true",
+                   help="time the HISA step and the flat indexer against the cache length L (8K .. 1M keys) "
+                        "at 8 sequences, B=128, m=64, k=2048, and fit how each grows with L")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB three times (the known-size "
                         "reference that scales the HBM byte counters) and exit")
@@ -247,32 +252,10 @@ def time_attention(hisa, case, idx, time_graphs_fn, steps, dev, hisa_step, R_ind
 
 # ---------------------------------------------------------------- main
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the indexer has no "
-                                   "multi-GPU path here (sequences would shard across GPUs "
-                                   "without communication). Use --gpus 1."}), flush=True)
-        sys.exit(2)
-
-    import torch
-
-    from sparse_attention_token_amd import hisa, synth
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.copy_probe:
-        n = args.copy_probe * 2**20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
-        return
-    hisa.lib()
-    case = synth.workload(args.workload, args.sequences)
+def bench_case(args, hisa, torch, dev, case, cpu_seconds=15.0):
+    """Time one workload: the HISA step, index only, the flat indexer, latency,
+    per-kernel durations, the dominant kernel's roofline and the CPU oracle
+    baseline.  Returns the record (without the top-level metric fields)."""
     S, T, H, d, L, B, m, k = case.S, case.T, case.H, case.d, case.L, case.B, case.m, case.k
     tree = None
     if args.tree:
@@ -280,8 +263,6 @@ def main():
         tree = (G, W)
         case.name += f"_tree_G{G}_W{W}"
     prefill = T > 1
-    steps = args.steps if args.steps is not None else (20 if prefill else 400)
-    warmup = args.warmup if args.warmup is not None else (3 if prefill else 40)
     log(f"workload {case.name}: S={S} T={T} L={L} H={H} d={d} B={B} m={m} k={k}")
 
     def bf(a):
@@ -292,10 +273,17 @@ def main():
     w = torch.from_numpy(case.w).to(dev)
     nblk = -(-L // B)
 
-    # replicas of the key cache and its pool
+    # replicas of the key cache and its pool, enough that one cycle through
+    # them touches --rotate-mib (1 GiB) of what the step reads: a decode step
+    # reads the kept blocks and the pooled means, a prefill chunk the whole
+    # cache (32 replicas of its 32 MiB)
     touched_hisa = S * T * (min(m, nblk) * B + nblk) * d * 2 if not prefill else K0.numel() * 2
     R = max(1, math.ceil(args.rotate_mib * 2**20 / touched_hisa))
-    R = min(R, 4 if prefill else 128, max(1, (16 * 2**30) // (K0.numel() * 2)))
+    R = min(R, 128, max(1, (16 * 2**30) // (K0.numel() * 2)))
+    # a prefill run times one step per replica (each step reads a replica
+    # cold); decode runs many steps over the cycle
+    steps = args.steps if args.steps is not None else (max(20, R) if prefill else 400)
+    warmup = args.warmup if args.warmup is not None else (3 if prefill else 40)
     Ks, pools, spools = [], [], []
     for r in range(R):
         Kr = K0 if r == 0 else K0.clone()
@@ -503,6 +491,21 @@ def main():
                         "algorithmic_bytes_per_launch": mdl["bytes"]}
         roofline["avg_launch_us"] = hisa_kern[dom]["avg_us"]
         roofline["traffic"] = traffic_from_profiles(dom, case.name)
+    # every HISA kernel's own rate against the roof that bounds it
+    roofline_by_kernel = {}
+    for name, v in hisa_kern.items():
+        mdl = models[name]
+        sec = v["avg_us"] * 1e-6
+        if prefill and mdl["flops"] > 0:
+            ach = mdl["flops"] / sec / 1e12
+            roofline_by_kernel[name] = {"bound": "mfma", "achieved": ach, "unit": "TFLOP/s",
+                                        "frac": ach / BF16_PEAK_TFLOPS, "avg_launch_us": v["avg_us"]}
+        else:
+            ach = mdl["bytes"] / sec / 1e9
+            roofline_by_kernel[name] = {"bound": "hbm", "achieved": ach, "unit": "GB/s",
+                                        "frac": ach / HBM_PEAK_GBS, "avg_launch_us": v["avg_us"],
+                                        "algorithmic_bytes_per_launch": mdl["bytes"],
+                                        "traffic": traffic_from_profiles(name, case.name)}
 
     # ---- the sparse attention over the indexer's output (opt-in)
     attention = None
@@ -534,7 +537,7 @@ def main():
         t0 = time.perf_counter()
         run(probe)
         per_q = max((time.perf_counter() - t0) / len(probe), 1e-6)
-        target_s = 15.0
+        target_s = cpu_seconds
         nsel = int(min(n, max(len(probe), target_s / per_q)))
         sel = np.linspace(0, n - 1, nsel).astype(np.int32)
         reps = max(1, min(1000, int(round(target_s / (per_q * nsel)))))
@@ -555,7 +558,7 @@ def main():
             t0 = time.perf_counter()
             oracle.flat_batch(case.q, case.w, case.qpos, case.K, L, k, sel=fsel)
             per_f = max(time.perf_counter() - t0, 1e-6)
-            nf = int(min(n, max(1, 5.0 / per_f)))
+            nf = int(min(n, max(1, cpu_seconds / 3.0 / per_f)))
             fsel = np.linspace(0, n - 1, nf).astype(np.int32)
             t0 = time.perf_counter()
             oracle.flat_batch(case.q, case.w, case.qpos, case.K, L, k, sel=fsel)
@@ -564,20 +567,12 @@ def main():
                            "sample": f"{nf} of {n} queries (evenly spaced) in {tf:.1f} s"}
 
     nq = S * T
-    value = nq / (hisa_ms * 1e-3)
-    res = {
-        "metric": METRIC,
-        "value": value,
+    return {
+        "value": nq / (hisa_ms * 1e-3),
         "unit": "queries/s",
-        "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": hisa_ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
         "config": {"workload": case.name, "S": S, "T": T, "L": L, "H": H, "d": d, "B": B, "m": m,
                    "k": k, "key_cache_replicas": R, "parallelism": "single GPU"},
         "us_per_query": hisa_ms * 1e3 / nq,
@@ -596,9 +591,157 @@ def main():
         "candidates_per_call": n_cand,
         "kernels": kernels,
         "roofline": roofline,
+        "roofline_by_kernel": roofline_by_kernel,
         "cpu_baseline": cpu,
         "attention": attention,
     }
+
+
+SWEEP_LENGTHS = (8192, 16384, 32768, 65536, 131072, 262144, 1 << 20)
+
+
+def sweep_lengths(args, hisa, torch, dev, synth):
+    """HISA step and flat indexer time against L at fixed S=8, B=128, m=64,
+    k=2048 (the decode 32K generator at other lengths).  The pages give the
+    per-query cost as O(L/B + mB) for HISA against O(L) for the flat indexer;
+    the record carries each point and the slope of log(time) against log(L)
+    over the doublings from 32K up."""
+    S, H, d, B, m, k = 8, 64, 128, 128, 64, 2048
+    steps = args.steps if args.steps is not None else 200
+    points = []
+    for L in SWEEP_LENGTHS:
+        c = synth.clustered_case(S, L, 1, H, d, B, m, k, seed=synth.SEED_BASE + 40 + L.bit_length())
+        K0 = torch.from_numpy(c.K.view(np.int16)).to(dev).view(torch.bfloat16)
+        q = torch.from_numpy(c.q.view(np.int16)).to(dev).view(torch.bfloat16)
+        w = torch.from_numpy(c.w).to(dev)
+        del c
+        nblk = -(-L // B)
+        touched = S * (m * B + nblk) * d * 2
+        R = max(1, min(64, math.ceil(args.rotate_mib * 2**20 / touched), (16 * 2**30) // (K0.numel() * 2)))
+        Ks, pools = [], []
+        for r in range(R):
+            Kr = K0 if r == 0 else K0.clone()
+            pr = torch.zeros((S, nblk, d), dtype=torch.bfloat16, device=dev)
+            hisa.hisa_pool_append(Kr, pr, 0, L, B)
+            Ks.append(Kr)
+            pools.append(pr)
+        out_idx = torch.empty((S, 1, k), dtype=torch.int32, device=dev)
+        out_score = torch.empty((S, 1, k), dtype=torch.float32, device=dev)
+        ws = torch.empty(hisa.hisa_index_workspace(S, 1, H, d, L, B, m, k), dtype=torch.uint8, device=dev)
+        fws = torch.empty(hisa.dsa_flat_workspace(S, 1, H, d, L, k), dtype=torch.uint8, device=dev)
+        f_idx = torch.empty_like(out_idx)
+        f_score = torch.empty_like(out_score)
+
+        def hisa_step(r):
+            hisa.hisa_append_index(Ks[r], pools[r], L - 1, L, q, w, B, m, k, None, out_idx=out_idx,
+                                   out_score=out_score, workspace=ws)
+
+        def flat_step(r):
+            hisa.dsa_flat_index(q, w, Ks[r], L, k, None, out_idx=f_idx, out_score=f_score, workspace=fws)
+
+        def timed(fn, n):
+            for i in range(3):
+                fn(i % R)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for r in range(R):
+                    fn(r)
+            g.replay()
+            torch.cuda.synchronize()
+            reps = max(1, n // R)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / (reps * R)
+
+        h_ms, f_ms = timed(hisa_step, steps), timed(flat_step, steps)
+        points.append({"L": L, "blocks": nblk, "replicas": R, "hisa_us": h_ms * 1e3, "flat_us": f_ms * 1e3,
+                       "speedup": f_ms / h_ms})
+        log(f"sweep L={L}: HISA {h_ms * 1e3:.2f} us, flat {f_ms * 1e3:.2f} us ({f_ms / h_ms:.2f}x)")
+        del Ks, pools, K0, ws, fws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    def slope(key):
+        xs = [math.log2(p_["L"]) for p_ in points if p_["L"] >= 32768]
+        ys = [math.log2(p_[key]) for p_ in points if p_["L"] >= 32768]
+        return float(np.polyfit(xs, ys, 1)[0])
+
+    def linfit(key):
+        # time = a + b * L over the whole sweep (least squares), b in ns per key
+        xs = np.array([p_["L"] for p_ in points], dtype=np.float64)
+        ys = np.array([p_[key] for p_ in points], dtype=np.float64)
+        b, a = np.polyfit(xs, ys, 1)
+        return {"intercept_us": float(a), "ns_per_1k_keys": float(b * 1e3 * 1e3)}
+
+    return {"sweep": "cache length", "S": S, "H": H, "d": d, "B": B, "m": m, "k": k,
+            "points": points, "loglog_slope_from_32K": {"hisa": slope("hisa_us"), "flat": slope("flat_us")},
+            "linear_fit": {"hisa": linfit("hisa_us"), "flat": linfit("flat_us")}}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the indexer has no "
+                                   "multi-GPU path here (sequences would shard across GPUs "
+                                   "without communication). Use --gpus 1."}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_token_amd import hisa, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_probe:
+        n = args.copy_probe * 2**20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return
+    hisa.lib()
+    if args.sweep_lengths:
+        print(json.dumps(sweep_lengths(args, hisa, torch, dev, synth)), flush=True)
+        return
+    if args.workload is not None:
+        wids = [args.workload]
+    else:
+        wids = [DEFAULT_WORKLOAD] + ([] if args.sequences is not None else list(SUB_WORKLOADS))
+    records = []
+    for wid in wids:
+        case = synth.workload(wid, args.sequences)
+        records.append(bench_case(args, hisa, torch, dev, case,
+                                  cpu_seconds=15.0 if wid == wids[0] else 8.0))
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    head = records[0]
+    res = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": head["steps"],
+        "warmup": head["warmup"],
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        **{k_: v for k_, v in head.items() if k_ not in ("value", "unit", "steps", "warmup", "ms_per_step")},
+    }
+    if len(records) > 1:
+        # the metric's other lengths and the prefill chunk, each with its own
+        # timing, flat baseline, roofline and CPU oracle baseline
+        res["configs"] = {r["config"]["workload"]: r for r in records[1:]}
     print(json.dumps(res), flush=True)
 
 

@@ -51,7 +51,6 @@ struct TreeTopLds {
     uint32_t keys[kTopMaxRows];        // keys by select slot
     int32_t sb[kTopMaxRows];           // kept super-blocks, ascending
     uint32_t keff;
-    OwnRepScratch ors;
 };
 
 // Select slot of position p among n <= 2048: lane p / rd holds it in register
@@ -201,7 +200,7 @@ __global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a) {
     if (tid < 64) L.w[tid] = wq;
     __syncthreads();
     if (!own_from_pool) {
-        own_rows_rep_par<D, kTopThreads, MAX>(s_own, own_rows, L.rep, nullptr, L.ors);   // ends with a barrier
+        own_rows_rep<D, 64, MAX>(s_own, own_rows, L.rep, nullptr);     // ends with a barrier
         if (tid < D) L.srep[tid] = super_column<MAX>(pool + tid, D, st * a.G, bt, a.B, L.rep[tid], own_rows);
         __syncthreads();
     }

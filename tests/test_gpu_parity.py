@@ -112,11 +112,15 @@ def test_pool_wide_exponent_spread(hisa, orc, B, d):
     np.testing.assert_array_equal(bits(build_pool(hisa, dev["K"], 700, B)), orc.pool(c.K, 700, B))
 
 
-def test_hisa_wide_exponent_spread(hisa, orc):
-    # own-block means (recomputed inside the block stage) over rows of very
-    # different magnitudes; queries at every offset inside a block
-    c = synth.clustered_case(1, 1024, 8, 16, 128, 128, 3, 200, seed=32,
-                             qpos=[[1000, 1001, 1010, 1023, 900, 899, 700, 130]])
+@pytest.mark.parametrize("L", [1024, 40000])
+def test_hisa_wide_exponent_spread(hisa, orc, L):
+    # own-block means (recomputed inside the block stage, or at 40000 keys in
+    # the own-block workgroup of the two-kernel decode, whose partial sums must
+    # then fall back to the row order) over rows of very different magnitudes;
+    # queries at every offset inside a block
+    qp = [[1000, 1001, 1010, 1023, 900, 899, 700, 130]] if L == 1024 else \
+         [[39999, 39990, 39936, 39935, 38000, 33001, 20000, 129]]
+    c = synth.clustered_case(1, L, 8, 16, 128, 128, 3, 200, seed=32, qpos=qp)
     c = _wide_spread_keys(c, 6)
     out = _run(hisa, c)
     for i in range(c.T):
