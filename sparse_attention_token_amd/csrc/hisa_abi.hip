@@ -155,17 +155,28 @@ int check_tree_params(int B, int G, int W, int m) {
 }
 
 struct FlatLayout {
-    size_t keys, total;
+    size_t keys, bucket_off, bucket_ent, total;
     int64_t stride;
+    bool block_major;         // prefill chunks: flat_block_major_mode
     StageBufs stage;
 };
 
-FlatLayout flat_layout(int S, int T, int64_t L, int k) {
+FlatLayout flat_layout(int S, int T, int d, int64_t L, int k) {
     FlatLayout l{};
     const int64_t nq = static_cast<int64_t>(S) * T;
-    l.stride = static_cast<int64_t>(align_up(static_cast<size_t>(L), 64));
+    l.block_major = flat_block_major_mode(S, T, d, L);
+    const int64_t nblk = ceil_div(L, kFlatBlock);
+    // block by block, every block's rows are written whole (positions past t
+    // as "no candidate"), so a row holds nblk * kFlatBlock keys
+    const int64_t row = l.block_major ? nblk * kFlatBlock : L;
+    l.stride = static_cast<int64_t>(align_up(static_cast<size_t>(row), 64));
     l.keys = 0;
     size_t off = align_up(static_cast<size_t>(nq) * l.stride * sizeof(uint32_t), kAlign);
+    if (l.block_major) {
+        const size_t nchunk = static_cast<size_t>(bucket_chunks(S, T));
+        l.bucket_off = off; off = align_up(off + nchunk * (nblk + 1) * sizeof(int32_t), kAlign);
+        l.bucket_ent = off; off = align_up(off + nchunk * kChunkQueries * nblk * sizeof(uint32_t), kAlign);
+    }
     off = carve_stage(off, nq, select_stage_len(L, k, 1, false), l.stage);
     l.total = off + kAlign;
     return l;
@@ -207,7 +218,7 @@ const char *const kKindNames[kKindCount] = {
     "pool_append", "own_mean", "score_blocks", "select_blocks",
     "score_refine", "select_refine", "score_flat", "select_flat",
     "index_decode", "bucket", "own_super", "score_tree", "select_tree", "tree_top",
-    "sparse_attention", "attention_combine",
+    "sparse_attention", "attention_combine", "bucket_flat",
 };
 
 }  // namespace
@@ -739,7 +750,7 @@ int hisa_sparse_attention(const uint16_t *q, const uint16_t *kv, int64_t kv_seq_
 
 size_t dsa_flat_workspace(int S, int T, int H, int d, int64_t L, int k) {
     if (check_query_shape(S, T, H, d, L, k) != HISA_OK) return 0;
-    return flat_layout(S, T, L, k).total;
+    return flat_layout(S, T, d, L, k).total;
 }
 
 int dsa_flat_index(const uint16_t *q, const float *w, const int32_t *qpos, const uint16_t *K,
@@ -751,18 +762,34 @@ int dsa_flat_index(const uint16_t *q, const float *w, const int32_t *qpos, const
     if (!qpos && T > L) return HISA_ERR_ARG;
     st = check_cache(K, k_seq_stride, S, d, L);
     if (st != HISA_OK) return st;
-    const FlatLayout lay = flat_layout(S, T, L, k);
+    const FlatLayout lay = flat_layout(S, T, d, L, k);
     if (!ws) return HISA_ERR_ARG;
     if (ws_bytes < lay.total) return HISA_ERR_WORKSPACE;
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    uint32_t *keys = reinterpret_cast<uint32_t *>(align_ptr(ws) + lay.keys);
-    ScoreArgs sa{};
-    sa.q = q; sa.w = w; sa.qpos = qpos;
-    sa.K = K; sa.k_seq_stride = k_seq_stride; sa.L = L;
-    sa.keys = keys; sa.keys_stride = lay.stride;
-    sa.S = S; sa.T = T; sa.H = H; sa.d = d; sa.B = 1; sa.m = 1;
-    st = hip_status(launch_score(kScoreFlat, sa, L, hs));
+    char *base = align_ptr(ws);
+    uint32_t *keys = reinterpret_cast<uint32_t *>(base + lay.keys);
+    if (lay.block_major) {
+        // many queries per sequence: the block-major refinement with every
+        // block b <= b_t kept, in slot b, so key position p is token p
+        FusedArgs fa{};
+        fa.q = q; fa.w = w; fa.qpos = qpos;
+        fa.K = K; fa.k_seq_stride = k_seq_stride; fa.L = L;
+        fa.S = S; fa.T = T; fa.H = H; fa.d = d; fa.B = kFlatBlock;
+        fa.nblk = static_cast<int>(ceil_div(L, kFlatBlock));
+        fa.m = fa.nblk;
+        fa.cand_keys = keys; fa.cand_stride = lay.stride;
+        fa.bucket_off = reinterpret_cast<int32_t *>(base + lay.bucket_off);
+        fa.bucket_ent = reinterpret_cast<uint32_t *>(base + lay.bucket_ent);
+        st = hip_status(launch_flat_block_major(fa, hs));
+    } else {
+        ScoreArgs sa{};
+        sa.q = q; sa.w = w; sa.qpos = qpos;
+        sa.K = K; sa.k_seq_stride = k_seq_stride; sa.L = L;
+        sa.keys = keys; sa.keys_stride = lay.stride;
+        sa.S = S; sa.T = T; sa.H = H; sa.d = d; sa.B = 1; sa.m = 1;
+        st = hip_status(launch_score(kScoreFlat, sa, L, hs));
+    }
     if (st != HISA_OK) return st;
     SelectArgs se{};
     set_stage(se, align_ptr(ws), lay.stage);

@@ -151,6 +151,15 @@ bool pool_update_fusable(int S, int T, int d, int64_t L, int B, int m);
 hipError_t launch_block_major_refine(const FusedArgs &a, hipStream_t st);
 hipError_t launch_block_major_blocks(const FusedArgs &a, hipStream_t st);
 
+// The flat indexer block by block for many queries per sequence: every query
+// scores every block b <= b_t of kFlatBlock keys through the block-major
+// refinement (a.m = a.nblk slots, slot b = block b, so candidate position p
+// is token p).  Workspace: bucket_off / bucket_ent as for block_major_mode,
+// cand_keys rows of at least nblk * kFlatBlock keys.
+constexpr int kFlatBlock = 128;
+bool flat_block_major_mode(int S, int T, int d, int64_t L);
+hipError_t launch_flat_block_major(const FusedArgs &a, hipStream_t st);
+
 // pool_max: max-pooled representatives instead of means (everywhere below)
 hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
                               int64_t blk0, int64_t nblk, int64_t L_new, bool pool_max, uint16_t *pool,
@@ -256,6 +265,7 @@ enum KernelKind {
     kKindTreeTop,          // super-blocks -> top W -> blocks -> top m in one launch (tree)
     kKindAttention,        // sparse attention over the selected set
     kKindAttnCombine,      // merge of the attention's split partials
+    kKindBucketFlat,       // the flat indexer's (query, block) pairs grouped by block (prefill chunks)
     kKindCount
 };
 

@@ -40,9 +40,13 @@ constexpr int kBucketR = kFusedMaxBlocks / kBucketThreads;   // bins per thread 
 constexpr int kBucketU = 16;                                 // kept-block entries per thread in flight
 constexpr int kBMThreads = 128;                              // two waves
 
+// ALL: the flat indexer's form -- every query takes every block b <= b_t, in
+// slot b (a.m = nblk slots per query), instead of its kept blocks.
+template <bool ALL>
 __global__ __launch_bounds__(kBucketThreads) void hisa_bucket_kernel(FusedArgs a) {
     __shared__ uint32_t s_cnt[kFusedMaxBlocks];
     __shared__ uint32_t s_wave[kBucketThreads / 64];
+    __shared__ int32_t s_bt[kChunkQueries];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = blockIdx.x;
     const int cps = (a.T + kChunkQueries - 1) / kChunkQueries;
@@ -50,11 +54,23 @@ __global__ __launch_bounds__(kBucketThreads) void hisa_bucket_kernel(FusedArgs a
     const int i0 = (c - s * cps) * kChunkQueries;
     const int nqc = min(kChunkQueries, a.T - i0);
     const int nblk = a.nblk;
-    const int32_t *sel = a.sel_blk + (static_cast<int64_t>(s) * a.T + i0) * a.m;
+    const int32_t *sel = ALL ? nullptr : a.sel_blk + (static_cast<int64_t>(s) * a.T + i0) * a.m;
     const int n = nqc * a.m;
 
     for (int b = tid; b < nblk; b += kBucketThreads) s_cnt[b] = 0u;
+    if (ALL)
+        for (int i = tid; i < nqc; i += kBucketThreads) {
+            const int64_t t = query_pos(a.qpos, s * a.T + i0 + i, i0 + i, a.L, a.T);
+            s_bt[i] = t < 0 ? -1 : static_cast<int32_t>(t / a.B);
+        }
     __syncthreads();
+    // slot e of the chunk: the kept block sel[e], or with ALL block e % m of
+    // query e / m while it is <= that query's own block
+    auto block_of = [&](int e) -> int {
+        if (!ALL) return sel[e];
+        const int ql = e / a.m, j = e - ql * a.m;
+        return j <= s_bt[ql] ? j : -1;
+    };
     // the chunk's kept blocks, kBucketU per thread at a time with every load
     // issued before the first atomic (a load per iteration would serialise
     // n / kBucketThreads memory round trips)
@@ -63,7 +79,7 @@ __global__ __launch_bounds__(kBucketThreads) void hisa_bucket_kernel(FusedArgs a
 #pragma unroll
         for (int u = 0; u < kBucketU; ++u) {
             const int e = e0 + u * kBucketThreads + tid;
-            bb[u] = e < n ? sel[e] : -1;
+            bb[u] = e < n ? block_of(e) : -1;
         }
 #pragma unroll
         for (int u = 0; u < kBucketU; ++u)
@@ -104,7 +120,7 @@ __global__ __launch_bounds__(kBucketThreads) void hisa_bucket_kernel(FusedArgs a
 #pragma unroll
         for (int u = 0; u < kBucketU; ++u) {
             const int e = e0 + u * kBucketThreads + tid;
-            bb[u] = e < n ? sel[e] : -1;
+            bb[u] = e < n ? block_of(e) : -1;
         }
 #pragma unroll
         for (int u = 0; u < kBucketU; ++u) {
@@ -487,14 +503,14 @@ hipError_t launch_blocks_mt(const FusedArgs &a, dim3 g_blk, dim3 g_top, hipStrea
 }
 
 template <int MT, int KS>
-hipError_t launch_bm_ks(const FusedArgs &a, dim3 grid, hipStream_t st) {
-    if (a.B == 64) return launch(kKindScoreRefine, hisa_refine_bm_kernel<MT, KS, 2>, grid, dim3(kBMThreads), 0, st, a);
-    return launch(kKindScoreRefine, hisa_refine_bm_kernel<MT, KS, 4>, grid, dim3(kBMThreads), 0, st, a);
+hipError_t launch_bm_ks(const FusedArgs &a, dim3 grid, KernelKind kind, hipStream_t st) {
+    if (a.B == 64) return launch(kind, hisa_refine_bm_kernel<MT, KS, 2>, grid, dim3(kBMThreads), 0, st, a);
+    return launch(kind, hisa_refine_bm_kernel<MT, KS, 4>, grid, dim3(kBMThreads), 0, st, a);
 }
 
 template <int MT>
-hipError_t launch_bm_mt(const FusedArgs &a, dim3 grid, hipStream_t st) {
-    return a.d == 64 ? launch_bm_ks<MT, 2>(a, grid, st) : launch_bm_ks<MT, 4>(a, grid, st);
+hipError_t launch_bm_mt(const FusedArgs &a, dim3 grid, hipStream_t st, KernelKind kind = kKindScoreRefine) {
+    return a.d == 64 ? launch_bm_ks<MT, 2>(a, grid, kind, st) : launch_bm_ks<MT, 4>(a, grid, kind, st);
 }
 
 }  // namespace
@@ -521,13 +537,28 @@ hipError_t launch_block_major_blocks(const FusedArgs &a, hipStream_t st) {
 
 hipError_t launch_block_major_refine(const FusedArgs &a, hipStream_t st) {
     const int64_t nchunk = bucket_chunks(a.S, a.T);
-    hipError_t e = launch(kKindBucket, hisa_bucket_kernel, dim3(static_cast<uint32_t>(nchunk)),
+    hipError_t e = launch(kKindBucket, hisa_bucket_kernel<false>, dim3(static_cast<uint32_t>(nchunk)),
                           dim3(kBucketThreads), 0, st, a);
     if (e != hipSuccess) return e;
     const dim3 grid(bm_grid(a.nblk, nchunk));
     if (a.H <= 16) return launch_bm_mt<1>(a, grid, st);
     if (a.H <= 32) return launch_bm_mt<2>(a, grid, st);
     return launch_bm_mt<4>(a, grid, st);
+}
+
+bool flat_block_major_mode(int S, int T, int d, int64_t L) {
+    return block_major_mode(S, T, d, L, kFlatBlock, static_cast<int>((L + kFlatBlock - 1) / kFlatBlock));
+}
+
+hipError_t launch_flat_block_major(const FusedArgs &a, hipStream_t st) {
+    const int64_t nchunk = bucket_chunks(a.S, a.T);
+    hipError_t e = launch(kKindBucketFlat, hisa_bucket_kernel<true>, dim3(static_cast<uint32_t>(nchunk)),
+                          dim3(kBucketThreads), 0, st, a);
+    if (e != hipSuccess) return e;
+    const dim3 grid(bm_grid(a.nblk, nchunk));
+    if (a.H <= 16) return launch_bm_mt<1>(a, grid, st, kKindScoreFlat);
+    if (a.H <= 32) return launch_bm_mt<2>(a, grid, st, kKindScoreFlat);
+    return launch_bm_mt<4>(a, grid, st, kKindScoreFlat);
 }
 
 }  // namespace hisa
