@@ -9,11 +9,12 @@
 //    * every wave scores pooled means of the complete blocks b < b_t with the
 //      shared MFMA scorer (its first tile loads are issued before anything
 //      else, to overlap HBM latency with the staging below);
-//    * q and the rows of the query's own block b_t = t / B (rows b_t*B .. t)
-//      are staged in LDS; the own-block representative is their mean,
-//      bf16(fp32(fp64 sum in row order / count)) -- the same arithmetic as the
-//      block pool, so the pool entry of the own block is never read -- and it
-//      is scored like the others;
+//    * q is staged in LDS; the rows of the query's own block b_t = t / B
+//      (rows b_t*B .. t) are summed by all threads, each over a run of rows
+//      of two columns, into the own-block representative
+//      bf16(fp32(fp64 sum in row order / count)) -- the same arithmetic and
+//      bits as the block pool (OwnRowsPar, block_rep.h), so the pool entry of
+//      the own block is never read -- and it is scored like the others;
 //    * the top min(m, b_t + 1) blocks (ascending ids) are then selected: by
 //      one wave when b_t + 1 <= 2048 (no barriers), by the whole workgroup
 //      otherwise.
@@ -120,8 +121,10 @@ __device__ __forceinline__ void own_block_rep(const FusedArgs &a, const uint16_t
 // Scores every block b <= b_t of one query into s_keys (positions laid out by
 // k1_slot) and leaves the query fragments in f.  NT threads; each wave loads
 // TB pool tiles at a time (the first batch before anything else, so that HBM
-// latency overlaps the staging of q and of the own-block rows); ends with a
-// barrier.  For the query at the cache's last row (t = L-1) the pool entry of
+// latency overlaps the staging of q and the loads of the own-block rows, which
+// go straight into registers and are summed by all NT threads; a 128-row own
+// block took about 3,900 cycles summed column by column in 128 threads, 1,200
+// this way); ends with a barrier.  For the query at the cache's last row (t = L-1) the pool entry of
 // its own block is already the mean of rows b_t*B .. t (the pool is current
 // through row L-1), so it is scored like the others; any other query's own
 // block is recomputed from K.
@@ -142,7 +145,10 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
     const int own_rows = static_cast<int>(t + 1 - r0);
     const bool own_in_pool = t == a.L - 1 && a.pool_out == nullptr;
     const bool write_pool = writer && a.pool_out != nullptr && t == a.L - 1;
-    uint16_t *s_own = reinterpret_cast<uint16_t *>(L.own);
+    using Own = OwnRowsPar<D, NT>;
+    static_assert(sizeof(typename Own::Scratch) <= sizeof(L.own), "own-block scratch fits the staging words");
+    auto &osc = *reinterpret_cast<typename Own::Scratch *>(L.own);
+    const uint16_t *own_src = a.K + s * a.k_seq_stride + r0 * D;
 
     // pool rows 0 .. full-1, 16 per tile, tile i on wave i % NW
     const uint16_t *pool = a.pool + s * a.pool_seq_stride;
@@ -154,22 +160,25 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
         const int p = (wave + u * NW) * 16 + n;
         load_row_frag<KS>(kb[u], p < full ? pool + static_cast<int64_t>(p) * D : nullptr, lane);
     }
-    if (!own_in_pool) {   // own-block rows: every load in flight before the first LDS store
-        constexpr int kPer = (kFusedOwnElems / 8 + NT - 1) / NT;   // 16-byte chunks per thread
-        const int chunks = own_rows * D / 8;
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(a.K + s * a.k_seq_stride + r0 * D);
-        u32x4 *dst = reinterpret_cast<u32x4 *>(s_own);
-        u32x4 v[kPer];
-#pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (tid + i * NT < chunks) v[i] = src[tid + i * NT];
-#pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (tid + i * NT < chunks) dst[tid + i * NT] = v[i];
-    }
+    Own own;
+    if (!own_in_pool) own.load(own_src, own_rows, tid);   // own-block rows: in flight with the pool tiles
     stage_query<MT, KS, NT>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, L.q, tid);
     if (tid < 64) L.w[tid] = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
+    if (!own_in_pool) {
+        if (a.pool_max)
+            own.template partial<true>(own_rows, tid, osc);
+        else
+            own.template partial<false>(own_rows, tid, osc);
+    }
     __syncthreads();
+    if (!own_in_pool && tid < D) {
+        // own-block representative over rows b_t*B .. t (the block pool's arithmetic)
+        uint16_t *dst = write_pool ? a.pool_out + s * a.pool_seq_stride + bt * D : nullptr;
+        if (a.pool_max)
+            own.template combine<true>(own_src, own_rows, tid, osc, L.mean, dst);
+        else
+            own.template combine<false>(own_src, own_rows, tid, osc, L.mean, dst);
+    }
 
     load_qfrag_lds_w<MT, KS>(f, L.q, L.w, lane);
     for (int base = wave; base < ntiles; base += TB * NW) {
@@ -192,9 +201,7 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
     }
 
     if (!own_in_pool) {
-        // own-block representative over rows b_t*B .. t; then wave 0 scores it
-        own_block_rep<D, NT >= 1024 ? 16 : 64>(a, s_own, own_rows, L.mean,
-                                               write_pool ? a.pool_out + s * a.pool_seq_stride + bt * D : nullptr);
+        __syncthreads();                  // the own-block representative is in L.mean
         if (wave == 0) {
             bf16x8 kbm[KS];
 #pragma unroll

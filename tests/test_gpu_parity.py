@@ -128,6 +128,33 @@ def test_hisa_wide_exponent_spread(hisa, orc, L):
         check_flat_row(orc, c, 0, i, out["fidx"][0, i], out["fsc"][0, i])
 
 
+@pytest.mark.parametrize("pool", ["mean", "max"])
+def test_append_index_wide_exponent_spread(hisa, orc, pool):
+    # the decode step's fused pool update: the block stage averages the own
+    # block (57 rows here) over all its threads in parts, and columns spanning
+    # more than 37 binades must fall back to the row-order sum
+    import torch
+
+    S, L0, L1 = 4, 3000, 3001
+    c = _wide_spread_keys(synth.clustered_case(S, L1, 1, 64, 128, 128, 8, 300, seed=43), 7)
+    dev = to_dev(c)
+    base = build_pool(hisa, dev["K"], L0, 128, pool=pool)
+    pools = [torch.zeros((S, 24, 128), dtype=torch.bfloat16, device=dev["K"].device) for _ in range(2)]
+    for p_ in pools:
+        p_[:, :base.shape[1]] = base
+    hisa.hisa_pool_append(dev["K"], pools[0], L0, L1, 128, pool=pool)
+    a = hisa.hisa_index(dev["q"], dev["w"], dev["K"], L1, pools[0], 128, 8, 300, want_blocks=True, pool=pool)
+    b = hisa.hisa_append_index(dev["K"], pools[1], L0, L1, dev["q"], dev["w"], 128, 8, 300, want_blocks=True,
+                               pool=pool)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x.cpu().numpy().view(np.int32), y.cpu().numpy().view(np.int32))
+    np.testing.assert_array_equal(bits(pools[1]), orc.pool(c.K, L1, 128, mode=pool))
+    idx, sc, blk = (t.cpu().numpy() for t in b)
+    for s in range(S):
+        check_hisa_row(orc, c, s, 0, idx[s, 0], sc[s, 0], blk[s, 0], pool=pool)
+
+
 def test_pool_append_is_idempotent(hisa, orc):
     c = synth.gaussian_case(1, 500, 1, 1, 128, 64, 1, 1, seed=3)
     dev = to_dev(c)
