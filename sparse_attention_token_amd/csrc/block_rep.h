@@ -100,13 +100,16 @@ struct OwnRowsPar {
     };
     uint32_t v[MAXR];
 
+    // Every load is issued (rows past the part read row n-1, masked out by
+    // partial()): a load under a branch can make the wave wait for it at once.
     __device__ __forceinline__ void load(const uint16_t *rows, int n, int tid) {
         const int cp = tid % CP, p = tid / CP;
         const int rp = (n + P - 1) / P;
 #pragma unroll
         for (int j = 0; j < MAXR; ++j) {
             const int r = p * rp + j;
-            v[j] = (j < rp && r < n) ? reinterpret_cast<const uint32_t *>(rows + static_cast<int64_t>(r) * D)[cp] : 0u;
+            const int rc = (j < rp && r < n) ? r : n - 1;
+            v[j] = reinterpret_cast<const uint32_t *>(rows + static_cast<int64_t>(rc) * D)[cp];
         }
     }
 
@@ -132,12 +135,13 @@ struct OwnRowsPar {
             own_u16x2 lo = {0xFFFFu, 0xFFFFu}, hi = {0u, 0u};
             const own_u16x2 one = {1u, 1u};
 #pragma unroll
-            for (int j = 0; j < MAXR; ++j) {      // padding words are zero: they add +0 and no magnitude
-                const own_u16x2 mag = __builtin_bit_cast(own_u16x2, v[j] & 0x7FFF7FFFu);
+            for (int j = 0; j < MAXR; ++j) {      // rows past the part count as zero: +0, no magnitude
+                const uint32_t x = (j < rp && p * rp + j < n) ? v[j] : 0u;
+                const own_u16x2 mag = __builtin_bit_cast(own_u16x2, x & 0x7FFF7FFFu);
                 lo = __builtin_elementwise_min(lo, mag - one);     // a zero wraps to 0xFFFF
                 hi = __builtin_elementwise_max(hi, mag);
-                s0 += static_cast<double>(__uint_as_float(v[j] << 16));
-                s1 += static_cast<double>(__uint_as_float(v[j] & 0xFFFF0000u));
+                s0 += static_cast<double>(__uint_as_float(x << 16));
+                s1 += static_cast<double>(__uint_as_float(x & 0xFFFF0000u));
             }
             sc.sum[p][2 * cp] = s0;
             sc.sum[p][2 * cp + 1] = s1;

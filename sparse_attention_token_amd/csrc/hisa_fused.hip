@@ -109,22 +109,13 @@ struct BlockStageLds {
     uint16_t mean[128];
 };
 
-template <int D, int U>
-__device__ __forceinline__ void own_block_rep(const FusedArgs &a, const uint16_t *s_own, int n, uint16_t *mean,
-                                              uint16_t *dst) {
-    if (a.pool_max)
-        own_rows_rep<D, U, true>(s_own, n, mean, dst);
-    else
-        own_rows_rep<D, U, false>(s_own, n, mean, dst);
-}
-
 // Scores every block b <= b_t of one query into s_keys (positions laid out by
 // k1_slot) and leaves the query fragments in f.  NT threads; each wave loads
 // TB pool tiles at a time (the first batch before anything else, so that HBM
 // latency overlaps the staging of q and the loads of the own-block rows, which
-// go straight into registers and are summed by all NT threads; a 128-row own
-// block took about 3,900 cycles summed column by column in 128 threads, 1,200
-// this way); ends with a barrier.  For the query at the cache's last row (t = L-1) the pool entry of
+// go straight into registers and are summed by all NT threads: at decode
+// 32K the block stage took about 800 cycles less than with the rows staged in
+// LDS and summed column by column by 128 threads); ends with a barrier.  For the query at the cache's last row (t = L-1) the pool entry of
 // its own block is already the mean of rows b_t*B .. t (the pool is current
 // through row L-1), so it is scored like the others; any other query's own
 // block is recomputed from K.
@@ -158,12 +149,15 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
 #pragma unroll
     for (int u = 0; u < TB; ++u) {
         const int p = (wave + u * NW) * 16 + n;
-        load_row_frag<KS>(kb[u], p < full ? pool + static_cast<int64_t>(p) * D : nullptr, lane);
+        load_row_frag_any<KS>(kb[u], pool + static_cast<int64_t>(p < full ? p : 0) * D, lane);
     }
     Own own;
     if (!own_in_pool) own.load(own_src, own_rows, tid);   // own-block rows: in flight with the pool tiles
-    stage_query<MT, KS, NT>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, L.q, tid);
-    if (tid < 64) L.w[tid] = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
+    QStager<MT, KS, NT> qst;
+    qst.load(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, tid);
+    const float wq = a.w[static_cast<int64_t>(qi) * a.H + (tid < a.H ? tid : a.H - 1)];
+    qst.store(L.q, a.H, tid);
+    if (tid < 64) L.w[tid] = tid < a.H ? wq : 0.0f;
     if (!own_in_pool) {
         if (a.pool_max)
             own.template partial<true>(own_rows, tid, osc);
@@ -186,7 +180,7 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
 #pragma unroll
             for (int u = 0; u < TB; ++u) {
                 const int p = (base + u * NW) * 16 + n;
-                load_row_frag<KS>(kb[u], p < full ? pool + static_cast<int64_t>(p) * D : nullptr, lane);
+                load_row_frag_any<KS>(kb[u], pool + static_cast<int64_t>(p < full ? p : 0) * D, lane);
             }
         }
 #pragma unroll
@@ -377,14 +371,11 @@ __global__ __launch_bounds__(DT) void hisa_decode_kernel(FusedArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
         const int p = tile0 + (wave * NTW + nt) * 16 + n;
-        const uint16_t *row = nullptr;
-        if (p < npos) {
-            const int slot = p / a.B;
-            const int64_t tok = static_cast<int64_t>(s_sel[slot]) * a.B + (p - slot * a.B);
-            if (tok <= t) row = a.K + s * a.k_seq_stride + tok * D;
-        }
-        valid[nt] = row != nullptr;
-        load_row_frag<KS>(kb[nt], row, lane);
+        const int pc = p < npos ? p : npos - 1;         // npos >= 1: tile0 < npos
+        const int slot = pc / a.B;
+        const int64_t tok = static_cast<int64_t>(s_sel[slot]) * a.B + (pc - slot * a.B);
+        valid[nt] = p < npos && tok <= t;
+        load_row_frag_any<KS>(kb[nt], a.K + s * a.k_seq_stride + (tok <= t ? tok : t) * D, lane);
     }
     float v[NTW];
     score_tiles_frag<MT, KS, NTW>(f, kb, v);
@@ -438,10 +429,13 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs 
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
             const int p = b0 + (wave * NTW + nt) * 16 + n;
-            load_row_frag<KS>(kb[nt], p < full ? pool + static_cast<int64_t>(p) * D : nullptr, lane);
+            load_row_frag_any<KS>(kb[nt], pool + static_cast<int64_t>(p < full ? p : 0) * D, lane);
         }
-        stage_query<MT, KS, kDecodeThreads>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, L.q, tid);
-        if (tid < 64) L.w[tid] = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
+        QStager<MT, KS, kDecodeThreads> qst;
+        qst.load(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, tid);
+        const float wq = a.w[static_cast<int64_t>(qi) * a.H + (tid < a.H ? tid : a.H - 1)];
+        qst.store(L.q, a.H, tid);
+        if (tid < 64) L.w[tid] = tid < a.H ? wq : 0.0f;
         __syncthreads();
         QFrag<MT, KS> f;
         load_qfrag_lds_w<MT, KS>(f, L.q, L.w, lane);
@@ -455,34 +449,37 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs 
         return;
     }
 
-    // the own block: rows b_t*B .. t, every load (and those of q and w) in
-    // flight before the first LDS store
+    // the own block: rows b_t*B .. t summed by all threads (OwnRowsPar), their
+    // loads in flight with those of q and w
     const int64_t r0 = static_cast<int64_t>(bt) * a.B;
     const int own_rows = static_cast<int>(t + 1 - r0);
-    uint16_t *s_own = reinterpret_cast<uint16_t *>(L.own);
+    using Own = OwnRowsPar<D, kDecodeThreads>;
+    static_assert(sizeof(typename Own::Scratch) <= sizeof(L.own), "own-block scratch fits the staging words");
+    auto &osc = *reinterpret_cast<typename Own::Scratch *>(L.own);
+    const uint16_t *own_src = a.K + s * a.k_seq_stride + r0 * D;
+    Own own;
+    own.load(own_src, own_rows, tid);
     QStager<MT, KS, kDecodeThreads> qst;
     qst.load(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, tid);
-    const float wq = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
-    {
-        constexpr int kPer = (kFusedOwnElems / 8 + kDecodeThreads - 1) / kDecodeThreads;
-        const int chunks = own_rows * D / 8;
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(a.K + s * a.k_seq_stride + r0 * D);
-        u32x4 *dst = reinterpret_cast<u32x4 *>(s_own);
-        u32x4 x[kPer];
-#pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (tid + i * kDecodeThreads < chunks) x[i] = src[tid + i * kDecodeThreads];
-#pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (tid + i * kDecodeThreads < chunks) dst[tid + i * kDecodeThreads] = x[i];
-    }
-    qst.store(L.q, tid);
+    const float wq0 = a.w[static_cast<int64_t>(qi) * a.H + (tid < a.H ? tid : a.H - 1)];   // unconditional load
+    const float wq = tid < a.H ? wq0 : 0.0f;
+    qst.store(L.q, a.H, tid);
     if (tid < 64) L.w[tid] = wq;
+    if (a.pool_max)
+        own.template partial<true>(own_rows, tid, osc);
+    else
+        own.template partial<false>(own_rows, tid, osc);
     __syncthreads();
-    own_block_rep<D, 64>(a, s_own, own_rows, L.mean,
-                      a.pool_out != nullptr && t == a.L - 1
-                          ? a.pool_out + s * a.pool_seq_stride + static_cast<int64_t>(bt) * D
-                          : nullptr);
+    if (tid < D) {
+        uint16_t *dst = a.pool_out != nullptr && t == a.L - 1
+                            ? a.pool_out + s * a.pool_seq_stride + static_cast<int64_t>(bt) * D
+                            : nullptr;
+        if (a.pool_max)
+            own.template combine<true>(own_src, own_rows, tid, osc, L.mean, dst);
+        else
+            own.template combine<false>(own_src, own_rows, tid, osc, L.mean, dst);
+    }
+    __syncthreads();
     if (wave == 0) {
         QFrag<MT, KS> f;
         load_qfrag_lds_w<MT, KS>(f, L.q, L.w, lane);
@@ -547,7 +544,8 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs 
     // q and w are loaded while wave 0 reads the block keys and selects
     QStager<MT, KS, kDecodeThreads> qst;
     qst.load(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, tid);
-    const float wq = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
+    const float wq0 = a.w[static_cast<int64_t>(qi) * a.H + (tid < a.H ? tid : a.H - 1)];   // unconditional load
+    const float wq = tid < a.H ? wq0 : 0.0f;
     if (wave == 0) {
         const uint32_t *keys = a.blk_keys + static_cast<int64_t>(qi) * a.blk_stride;
         auto emit = [&](uint32_t op, int pos) {
@@ -570,7 +568,7 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs 
         else ke = dgather_topm<32>(keys, nb, a.m, lane, s_win, emit);
         if (lane == 0) s_keff = ke;
     }
-    qst.store(s_q, tid);
+    qst.store(s_q, a.H, tid);
     if (tid < 64) s_w[tid] = wq;
     __syncthreads();
     if (lead)
@@ -584,14 +582,11 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs 
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
         const int p = tile0 + (wave * NTW + nt) * 16 + n;
-        const uint16_t *row = nullptr;
-        if (p < npos) {
-            const int slot = p / a.B;
-            const int64_t tok = static_cast<int64_t>(s_sel[slot]) * a.B + (p - slot * a.B);
-            if (tok <= t) row = a.K + s * a.k_seq_stride + tok * D;
-        }
-        valid[nt] = row != nullptr;
-        load_row_frag<KS>(kb[nt], row, lane);
+        const int pc = p < npos ? p : npos - 1;         // npos >= 1: tile0 < npos
+        const int slot = pc / a.B;
+        const int64_t tok = static_cast<int64_t>(s_sel[slot]) * a.B + (pc - slot * a.B);
+        valid[nt] = p < npos && tok <= t;
+        load_row_frag_any<KS>(kb[nt], a.K + s * a.k_seq_stride + (tok <= t ? tok : t) * D, lane);
     }
     QFrag<MT, KS> f;
     load_qfrag_lds_w<MT, KS>(f, s_q, s_w, lane);
@@ -630,14 +625,11 @@ __global__ __launch_bounds__(kK2Threads) void hisa_refine_kernel(FusedArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
         const int p = tile0 + wave * 32 + nt * 16 + n;
-        const uint16_t *row = nullptr;
-        if (p < npos) {
-            const int slot = p / a.B;
-            const int64_t tok = static_cast<int64_t>(selq[slot]) * a.B + (p - slot * a.B);
-            if (tok <= t) row = a.K + s * a.k_seq_stride + tok * D;
-        }
-        valid[nt] = row != nullptr;
-        load_row_frag<KS>(kb[nt], row, lane);
+        const int pc = p < npos ? p : npos - 1;         // npos >= 1: tile0 < npos
+        const int slot = pc / a.B;
+        const int64_t tok = static_cast<int64_t>(selq[slot]) * a.B + (pc - slot * a.B);
+        valid[nt] = p < npos && tok <= t;
+        load_row_frag_any<KS>(kb[nt], a.K + s * a.k_seq_stride + (tok <= t ? tok : t) * D, lane);
     }
     stage_query<MT, KS, kK2Threads>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, s_q, tid);
     __syncthreads();

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a) {
         for (int i = 0; i < kPer; ++i)
             if (tid + i * kTopThreads < chunks) dst[tid + i * kTopThreads] = v[i];
     }
-    qst.store(L.q, tid);
+    qst.store(L.q, a.H, tid);
     if (tid < 64) L.w[tid] = wq;
     __syncthreads();
     if (!own_from_pool) {

@@ -63,21 +63,26 @@ struct QStager {
     static constexpr int kPer = (kChunks + NT - 1) / NT;
     u32x4 v[kPer];
 
+    // Loads are unconditional (heads past H read head H-1, zeroed by
+    // store()): a load under a branch can make the wave wait for it at once.
     __device__ __forceinline__ void load(const uint16_t *__restrict__ q, int H, int tid) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int c = tid + i * NT;
             const int h = c / (D / 8);
-            v[i] = u32x4{0u, 0u, 0u, 0u};
-            if (c < kChunks && h < H) v[i] = *reinterpret_cast<const u32x4 *>(q + h * D + 8 * (c - h * (D / 8)));
+            const int hc = h < H ? h : H - 1;
+            if (kChunks % NT == 0 || c < kChunks)
+                v[i] = *reinterpret_cast<const u32x4 *>(q + hc * D + 8 * (c - h * (D / 8)));
         }
     }
-    __device__ __forceinline__ void store(uint16_t *s_q, int tid) const {
+    __device__ __forceinline__ void store(uint16_t *s_q, int H, int tid) const {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int c = tid + i * NT;
             const int h = c / (D / 8);
-            if (c < kChunks) *reinterpret_cast<u32x4 *>(s_q + h * ST + 8 * (c - h * (D / 8))) = v[i];
+            if (kChunks % NT == 0 || c < kChunks)
+                *reinterpret_cast<u32x4 *>(s_q + h * ST + 8 * (c - h * (D / 8))) =
+                    h < H ? v[i] : u32x4{0u, 0u, 0u, 0u};
         }
     }
 };
@@ -86,7 +91,7 @@ template <int MT, int KS, int NT>
 __device__ __forceinline__ void stage_query(const uint16_t *__restrict__ q, int H, uint16_t *s_q, int tid) {
     QStager<MT, KS, NT> st;
     st.load(q, H, tid);
-    st.store(s_q, tid);
+    st.store(s_q, H, tid);
 }
 
 template <int MT, int KS>
@@ -154,6 +159,19 @@ __device__ __forceinline__ void load_row_frag(bf16x8 (&kb)[KS], const uint16_t *
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         kb[ks] = row ? load_bf16x8(row + 32 * ks + 8 * g) : zero_bf16x8();
+}
+
+// As load_row_frag for a pointer that is always a valid row: the loads are
+// unconditional.  A load under a null test compiles to a branch on the exec
+// mask, and the register copy that joins its two sides makes the wave wait
+// for the load right there (one full memory round trip before the next
+// load is even issued); callers that have no row for a lane point it at any
+// valid row instead and discard that row's score.
+template <int KS>
+__device__ __forceinline__ void load_row_frag_any(bf16x8 (&kb)[KS], const uint16_t *row, int lane) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kb[ks] = load_bf16x8(row + 32 * ks + 8 * g);
 }
 
 // max(x, 0) for finite x, as one integer max on the bit pattern: every

@@ -68,11 +68,13 @@ template <int R>
 __device__ __forceinline__ void load_run(const uint32_t *__restrict__ keys, int64_t base, int64_t n,
                                          uint32_t (&kv)[R]) {
     if constexpr (R >= 4) {
+        // every load is issued (past the row end it reads the row's first
+        // keys, masked below): a load under a branch can make the wave wait
+        // for it at once
 #pragma unroll
         for (int v = 0; v < R / 4; ++v) {
             const int64_t p = base + 4 * v;
-            sel_u32x4 x = {0u, 0u, 0u, 0u};
-            if (p < n) x = *reinterpret_cast<const sel_u32x4 *>(keys + p);   // rows are padded to 64 keys
+            const sel_u32x4 x = *reinterpret_cast<const sel_u32x4 *>(keys + (p < n ? p : 0));   // rows are padded to 64 keys
 #pragma unroll
             for (int e = 0; e < 4; ++e) kv[4 * v + e] = (p + e < n) ? x[e] : kNoCandidate;
         }

@@ -103,11 +103,20 @@ def lib():
 # ---------------------------------------------------------------- helpers
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else C.c_void_p(t.data_ptr())
+    # the prototypes declare void*: ctypes converts a plain int (or None)
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(device: torch.device):
-    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    """torch's current HIP stream on `device`, as an integer handle.  torch's
+    raw-stream accessor skips building a Stream object (about 2 us a call);
+    the public route serves where it is absent."""
+    if _raw_stream is not None:
+        return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _bf16(t: torch.Tensor, name: str) -> torch.Tensor:
@@ -134,9 +143,12 @@ def _out(t: Optional[torch.Tensor], name: str, shape, dtype: torch.dtype, device
     """A caller-supplied output: exactly `shape` and `dtype`, contiguous, on `device`; a new
     tensor when t is None.  The kernels write every element of the shape through the raw
     pointer, so anything smaller, strided or of another type is refused before the call."""
-    shape = tuple(int(x) for x in shape)
     if t is None:
         return torch.empty(shape, dtype=dtype, device=device)
+    if (isinstance(t, torch.Tensor) and t.dtype == dtype and t.shape == shape and t.device == device
+            and t.is_contiguous()):
+        return t                                  # the usual case, checked in one pass
+    shape = tuple(int(x) for x in shape)
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if t.dtype != dtype:
@@ -214,8 +226,9 @@ def _query_args(q, w, qpos, K, L):
     return S, T, H, d, kss
 
 
-def _workspace(nbytes: int, device, workspace):
-    """Allocate the workspace, or pass the caller's through (the library checks its size)."""
+def _workspace(nbytes: Optional[int], device, workspace):
+    """Allocate the workspace, or pass the caller's through (the library checks its size:
+    a short one returns HISA_ERR_WORKSPACE, so its size need not be queried per call)."""
     if workspace is None:
         return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
     if workspace.device != device or not workspace.is_contiguous():
@@ -241,11 +254,12 @@ def hisa_index(q, w, K, L: int, pool_mean, B: int, m: int, k: int, qpos=None, *,
         out_score = _out(out_score, "out_score", (S, T, k), torch.float32, dev)
     if want_blocks or out_blk is not None:
         out_blk = _out(out_blk, "out_blk", (S, T, m), torch.int32, dev)
-    nbytes = hisa_index_workspace(S, T, H, d, L, B, m, k)
-    if nbytes == 0:
-        _check("hisa_index", lib().hisa_index(None, None, None, None, 0, L, None, 0, S, T, H, d, B,
-                                              m, k, None, None, None, None, 0, None))
-    ws = _workspace(nbytes, dev, workspace)
+    if workspace is None:
+        nbytes = hisa_index_workspace(S, T, H, d, L, B, m, k)
+        if nbytes == 0:
+            _check("hisa_index", lib().hisa_index(None, None, None, None, 0, L, None, 0, S, T, H, d, B,
+                                                  m, k, None, None, None, None, 0, None))
+    ws = _workspace(None if workspace is not None else nbytes, dev, workspace)
     st = lib().hisa_index_mode(_ptr(q), _ptr(w), _ptr(qpos), _ptr(K), kss, int(L), _ptr(pool_mean),
                                pss, S, T, H, d, B, m, k, _ptr(out_idx), _ptr(out_score), _ptr(out_blk),
                                _ptr(ws), ws.numel() * ws.element_size(), _pool_kind(pool), _stream(dev))
@@ -273,12 +287,13 @@ def hisa_append_index(K, pool_mean, L_old: int, L_new: int, q, w, B: int, m: int
         out_score = _out(out_score, "out_score", (S, T, k), torch.float32, dev)
     if want_blocks or out_blk is not None:
         out_blk = _out(out_blk, "out_blk", (S, T, m), torch.int32, dev)
-    nbytes = hisa_index_workspace(S, T, H, d, L_new, B, m, k)
-    if nbytes == 0:
-        _check("hisa_append_index", lib().hisa_append_index(None, 0, int(L_old), int(L_new), None, 0, None, None,
-                                                            None, S, T, H, d, B, m, k, None, None, None, None,
-                                                            0, None))
-    ws = _workspace(nbytes, dev, workspace)
+    if workspace is None:
+        nbytes = hisa_index_workspace(S, T, H, d, L_new, B, m, k)
+        if nbytes == 0:
+            _check("hisa_append_index", lib().hisa_append_index(None, 0, int(L_old), int(L_new), None, 0, None,
+                                                                None, None, S, T, H, d, B, m, k, None, None, None,
+                                                                None, 0, None))
+    ws = _workspace(None if workspace is not None else nbytes, dev, workspace)
     st = lib().hisa_append_index_mode(_ptr(K), kss, int(L_old), int(L_new), _ptr(pool_mean), pss, _ptr(q),
                                       _ptr(w), _ptr(qpos), S, T, H, d, B, m, k, _ptr(out_idx), _ptr(out_score),
                                       _ptr(out_blk), _ptr(ws), ws.numel() * ws.element_size(), _pool_kind(pool),
@@ -388,11 +403,12 @@ def dsa_flat_index(q, w, K, L: int, k: int, qpos=None, *, want_scores: bool = Tr
     out_idx = _out(out_idx, "out_idx", (S, T, k), torch.int32, dev)
     if want_scores or out_score is not None:
         out_score = _out(out_score, "out_score", (S, T, k), torch.float32, dev)
-    nbytes = dsa_flat_workspace(S, T, H, d, L, k)
-    if nbytes == 0:
-        _check("dsa_flat_index", lib().dsa_flat_index(None, None, None, None, 0, L, S, T, H, d, k,
-                                                      None, None, None, 0, None))
-    ws = _workspace(nbytes, dev, workspace)
+    if workspace is None:
+        nbytes = dsa_flat_workspace(S, T, H, d, L, k)
+        if nbytes == 0:
+            _check("dsa_flat_index", lib().dsa_flat_index(None, None, None, None, 0, L, S, T, H, d, k,
+                                                          None, None, None, 0, None))
+    ws = _workspace(None if workspace is not None else nbytes, dev, workspace)
     st = lib().dsa_flat_index(_ptr(q), _ptr(w), _ptr(qpos), _ptr(K), kss, int(L), S, T, H, d, k,
                               _ptr(out_idx), _ptr(out_score), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(dev))
