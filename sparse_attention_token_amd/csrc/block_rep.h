@@ -151,7 +151,7 @@ struct OwnRowsPar {
     }
 
     // Thread c < D: the representative of column c, into mean[c] and dst[c]
-    // (dst may be null).  rows: as for load().
+    // (either may be null).  rows: as for load().
     template <bool MAX>
     __device__ __forceinline__ void combine(const uint16_t *rows, int n, int c, const Scratch &sc, uint16_t *mean,
                                             uint16_t *dst) const {
@@ -190,7 +190,7 @@ struct OwnRowsPar {
             }
             mv = f32_to_bf16_rne(static_cast<float>(total / static_cast<double>(n)));
         }
-        mean[c] = mv;
+        if (mean) mean[c] = mv;
         if (dst) dst[c] = mv;
     }
 };

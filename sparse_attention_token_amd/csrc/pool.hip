@@ -18,6 +18,7 @@
 // once), then one thread per column adds its column from LDS in row order.  The sequential fp64 order is what makes the result
 // independent of how the rows were appended.
 
+#include "block_rep.h"
 #include "hisa_internal.h"
 
 namespace hisa {
@@ -152,6 +153,35 @@ __global__ __launch_bounds__(kMaxD) void pool_append_direct_kernel(
     for (int r = 0; r < kDirectRows; ++r)
         if (r < rows) acc.add(x[r]);
     pool[s * pool_seq_stride + b * d + col] = acc.get(rows);
+}
+
+// Blocks of at most kFusedOwnElems keys' worth of rows (B*d <= 16384): one
+// 512-thread workgroup per block, every thread summing a run of rows of two
+// columns straight from global memory (OwnRowsPar: exact fp64 part sums whose
+// total is the row-order sum whenever a column's exponents span at most 37
+// binades, the row-order sum itself otherwise), so a block costs a few
+// dozen dependent additions per thread instead of B.  A step's append
+// touches few blocks, so their latency is the append's time (a prefill chunk
+// of 4096 rows: 32 blocks).
+constexpr int kParThreads = 512;
+
+template <int D, bool MAX>
+__global__ __launch_bounds__(kParThreads) void pool_append_par_kernel(
+        const uint16_t *__restrict__ K, int64_t k_seq_stride, int B, int64_t blk0, int64_t L_new,
+        uint16_t *__restrict__ pool, int64_t pool_seq_stride) {
+    using Own = OwnRowsPar<D, kParThreads>;
+    __shared__ __attribute__((aligned(16))) typename Own::Scratch sc;
+    const int s = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int64_t b = blk0 + blockIdx.x;
+    const int64_t r0 = b * B;
+    const int rows = static_cast<int>(((r0 + B < L_new) ? r0 + B : L_new) - r0);
+    const uint16_t *src = K + s * k_seq_stride + r0 * D;
+    Own own;
+    own.load(src, rows, tid);
+    own.template partial<MAX>(rows, tid, sc);
+    __syncthreads();
+    if (tid < D) own.template combine<MAX>(src, rows, tid, sc, nullptr, pool + s * pool_seq_stride + b * D);
 }
 
 // grid: (S).  Both levels of the three-level tree when the new rows all lie
@@ -376,6 +406,17 @@ hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, in
                               int64_t blk0, int64_t nblk, int64_t L_new, bool pool_max, uint16_t *pool,
                               int64_t pool_seq_stride, hipStream_t st) {
     const dim3 g(static_cast<uint32_t>(nblk), S);
+    if (static_cast<int64_t>(B) * d <= kFusedOwnElems) {
+        if (d == 64)
+            return pool_max ? launch(kKindPoolAppend, pool_append_par_kernel<64, true>, g, dim3(kParThreads), 0, st,
+                                     K, k_seq_stride, B, blk0, L_new, pool, pool_seq_stride)
+                            : launch(kKindPoolAppend, pool_append_par_kernel<64, false>, g, dim3(kParThreads), 0, st,
+                                     K, k_seq_stride, B, blk0, L_new, pool, pool_seq_stride);
+        return pool_max ? launch(kKindPoolAppend, pool_append_par_kernel<128, true>, g, dim3(kParThreads), 0, st, K,
+                                 k_seq_stride, B, blk0, L_new, pool, pool_seq_stride)
+                        : launch(kKindPoolAppend, pool_append_par_kernel<128, false>, g, dim3(kParThreads), 0, st, K,
+                                 k_seq_stride, B, blk0, L_new, pool, pool_seq_stride);
+    }
     if (B <= kDirectRows) {
         if (pool_max)
             return launch(kKindPoolAppend, pool_append_direct_kernel<true>, g, dim3(kMaxD), 0, st, K, k_seq_stride,
