@@ -284,15 +284,15 @@ __global__ __launch_bounds__(kBMThreads) void hisa_refine_bm_kernel(FusedArgs a)
     const int i0 = (c - s * cps) * kChunkQueries;
     const int qi0 = s * a.T + i0;
 
-    // this wave's rows of block b (rows past the cache end are zero and masked;
-    // positions fit in int: L < 2^31)
+    // this wave's rows of block b (rows past the cache end read the last row
+    // and are masked when stored; positions fit in int: L < 2^31)
     const int tok0 = b * a.B + wave * kRowsPerWave;
     bf16x8 kb[NTW][KS];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
         const int tok = tok0 + nt * 16 + n;
-        load_row_frag<KS>(kb[nt], tok < a.L ? a.K + s * a.k_seq_stride + static_cast<int64_t>(tok) * D : nullptr,
-                          lane);
+        load_row_frag_any<KS>(kb[nt], a.K + s * a.k_seq_stride + static_cast<int64_t>(tok < a.L ? tok : a.L - 1) * D,
+                              lane);
     }
     // the pairs (query, slot) and each query's position
     const uint32_t *ent = a.bucket_ent + static_cast<int64_t>(c) * kChunkQueries * a.m + e0;
@@ -386,14 +386,15 @@ __global__ __launch_bounds__(kBMThreads) void hisa_blocks_bm_kernel(FusedArgs a)
             s_bt[x] = static_cast<int32_t>(t / a.B);
         }
     }
-    // this wave's means (rows past the pool end are zero and never stored)
+    // this wave's means (rows past the pool end read the first mean and are
+    // never stored; the loads are unconditional so none waits for another)
     const uint16_t *pool = a.pool + s * a.pool_seq_stride;
     const int p0 = b0 + wave * 16 * NTW;
     bf16x8 kb[NTW][KS];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
         const int p = p0 + nt * 16 + n;
-        load_row_frag<KS>(kb[nt], p < a.nblk ? pool + static_cast<int64_t>(p) * D : nullptr, lane);
+        load_row_frag_any<KS>(kb[nt], pool + static_cast<int64_t>(p < a.nblk ? p : 0) * D, lane);
     }
     if (a.H < MT * 16) {
         for (int x = tid; x < (MT * 16 - a.H) * D; x += kBMThreads) s_q[a.H * D + x] = 0;
@@ -431,15 +432,29 @@ __global__ __launch_bounds__(kBMThreads) void hisa_blocks_bm_kernel(FusedArgs a)
 // top min(m, b_t + 1) blocks (ascending ids) with the one-wave select.
 constexpr int kTopMThreads = 256;
 
-template <int R, typename Emit>
-__device__ __forceinline__ uint32_t topm_select(const uint32_t *keys, uint32_t own_key, int nb, int m, int lane,
-                                                uint32_t *win, Emit &&emit) {
+// The block keys of one lane (positions lane*rd .. lane*rd + R - 1), every
+// load issued at once before anything waits on them (positions past the
+// complete blocks read the row's first key and are masked by topm_select):
+// a load under a branch makes the wave wait for it on the spot, and R of them
+// in a row were as many serial memory round trips.
+template <int R>
+__device__ __forceinline__ void topm_load(const uint32_t *keys, int nb, int lane, uint32_t (&kv)[R]) {
     const int rd = (nb + 63) / 64;
-    uint32_t kv[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int p = lane * rd + r;
-        kv[r] = (r < rd && p < nb) ? (p == nb - 1 ? own_key : keys[p]) : kNoCandidate;
+        kv[r] = keys[(r < rd && p < nb - 1) ? p : 0];
+    }
+}
+
+template <int R, typename Emit>
+__device__ __forceinline__ uint32_t topm_select(uint32_t (&kv)[R], uint32_t own_key, int nb, int m, int lane,
+                                                uint32_t *win, Emit &&emit) {
+    const int rd = (nb + 63) / 64;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int p = lane * rd + r;
+        kv[r] = (r < rd && p < nb) ? (p == nb - 1 ? own_key : kv[r]) : kNoCandidate;
     }
     // the ballot select for up to 256 blocks; beyond, its rounds grow with R
     // and the LDS histogram of wave_window_select costs less
@@ -449,9 +464,32 @@ __device__ __forceinline__ uint32_t topm_select(const uint32_t *keys, uint32_t o
     return res.keff;
 }
 
-template <int MT, int KS>
-__global__ __launch_bounds__(kTopMThreads) void hisa_topm_kernel(FusedArgs a) {
+// The own-block score, then the top m of one query.  The block keys (R per
+// lane) are loaded after the score, all at once: loaded together with q the
+// keys and the query's fragments were live together, which cost a wave per
+// SIMD in occupancy and measured slower.
+template <int R, int MT, int KS, typename Emit>
+__device__ __forceinline__ uint32_t topm_query(const FusedArgs &a, int qi, int nb, const uint32_t *keys, int lane,
+                                               uint32_t *win, Emit &&emit) {
     constexpr int D = 32 * KS;
+    QFrag<MT, KS> f;
+    load_qfrag_global_any<MT, KS>(f, a.q + static_cast<int64_t>(qi) * a.H * D, a.w + static_cast<int64_t>(qi) * a.H,
+                                  a.H, lane);
+    bf16x8 kbm[KS];
+    // every lane reads the representative; only row 0's score (lane 0) is used
+    load_row_frag_any<KS>(kbm, a.own_rep + static_cast<int64_t>(qi) * D, lane);
+    const float v = score_rows<MT, KS>(f, kbm);
+    const uint32_t own_key = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(score_to_key(v))));
+    uint32_t kv[R];
+    topm_load<R>(keys, nb, lane, kv);
+    return topm_select<R>(kv, own_key, nb, a.m, lane, win, emit);
+}
+
+// R: block keys per lane, at least ceil(n_b / 64) for every query of the
+// launch (one instantiation per R keeps the register budget of the short
+// rows' variants small: all four in one kernel took 194 registers).
+template <int MT, int KS, int R>
+__global__ __launch_bounds__(kTopMThreads) void hisa_topm_kernel(FusedArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t s_win[kTopMThreads / 64][kWindowWords];
     const int lane = threadIdx.x & 63;
     const int qi = blockIdx.x * (kTopMThreads / 64) + (threadIdx.x >> 6);
@@ -463,30 +501,26 @@ __global__ __launch_bounds__(kTopMThreads) void hisa_topm_kernel(FusedArgs a) {
     uint32_t keff = 0;
     if (t >= 0) {
         const int nb = static_cast<int>(t / a.B + 1);
-        QFrag<MT, KS> f;
-        load_qfrag_global<MT, KS>(f, a.q + static_cast<int64_t>(qi) * a.H * D, a.w + static_cast<int64_t>(qi) * a.H,
-                                  a.H, lane);
-        bf16x8 kbm[KS];
-        load_row_frag<KS>(kbm, (lane & 15) == 0 ? a.own_rep + static_cast<int64_t>(qi) * D : nullptr, lane);
-        const float v = score_rows<MT, KS>(f, kbm);
-        const uint32_t own_key = static_cast<uint32_t>(
-            __builtin_amdgcn_readfirstlane(static_cast<int>(score_to_key(v))));
         const uint32_t *keys = a.blk_keys + static_cast<int64_t>(qi) * a.blk_stride;
         auto emit = [&](uint32_t op, int pos) {
             sel[op] = pos;
             if (ob) ob[op] = pos;
         };
-        const int rd = (nb + 63) / 64;
-        uint32_t *win = s_win[threadIdx.x >> 6];
-        if (rd <= 4) keff = topm_select<4>(keys, own_key, nb, a.m, lane, win, emit);
-        else if (rd <= 8) keff = topm_select<8>(keys, own_key, nb, a.m, lane, win, emit);
-        else if (rd <= 16) keff = topm_select<16>(keys, own_key, nb, a.m, lane, win, emit);
-        else keff = topm_select<32>(keys, own_key, nb, a.m, lane, win, emit);
+        keff = topm_query<R, MT, KS>(a, qi, nb, keys, lane, s_win[threadIdx.x >> 6], emit);
     }
     for (int j = static_cast<int>(keff) + lane; j < a.m; j += 64) {
         sel[j] = -1;
         if (ob) ob[j] = -1;
     }
+}
+
+template <int MT, int KS>
+hipError_t launch_topm(const FusedArgs &a, dim3 g_top, hipStream_t st) {
+    const int rd = (a.nblk + 63) / 64;                 // n_b <= nblk for every query
+    if (rd <= 4) return launch(kKindSelectBlocks, hisa_topm_kernel<MT, KS, 4>, g_top, dim3(kTopMThreads), 0, st, a);
+    if (rd <= 8) return launch(kKindSelectBlocks, hisa_topm_kernel<MT, KS, 8>, g_top, dim3(kTopMThreads), 0, st, a);
+    if (rd <= 16) return launch(kKindSelectBlocks, hisa_topm_kernel<MT, KS, 16>, g_top, dim3(kTopMThreads), 0, st, a);
+    return launch(kKindSelectBlocks, hisa_topm_kernel<MT, KS, 32>, g_top, dim3(kTopMThreads), 0, st, a);
 }
 
 template <int MT>
@@ -495,11 +529,11 @@ hipError_t launch_blocks_mt(const FusedArgs &a, dim3 g_blk, dim3 g_top, hipStrea
     if (a.d == 64) {
         e = launch(kKindScoreBlocks, hisa_blocks_bm_kernel<MT, 2>, g_blk, dim3(kBMThreads), 0, st, a);
         if (e != hipSuccess) return e;
-        return launch(kKindSelectBlocks, hisa_topm_kernel<MT, 2>, g_top, dim3(kTopMThreads), 0, st, a);
+        return launch_topm<MT, 2>(a, g_top, st);
     }
     e = launch(kKindScoreBlocks, hisa_blocks_bm_kernel<MT, 4>, g_blk, dim3(kBMThreads), 0, st, a);
     if (e != hipSuccess) return e;
-    return launch(kKindSelectBlocks, hisa_topm_kernel<MT, 4>, g_top, dim3(kTopMThreads), 0, st, a);
+    return launch_topm<MT, 4>(a, g_top, st);
 }
 
 template <int MT, int KS>

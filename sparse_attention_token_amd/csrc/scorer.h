@@ -152,6 +152,40 @@ __device__ __forceinline__ void load_qfrag_global(QFrag<MT, KS> &f, const uint16
         }
 }
 
+// As load_qfrag_global with every load issued unconditionally (heads past H
+// read head H-1 and are zeroed afterwards, weights past H are zero), so the
+// loads do not wait for each other.
+template <int MT, int KS>
+__device__ __forceinline__ void load_qfrag_global_any(QFrag<MT, KS> &f, const uint16_t *__restrict__ q,
+                                                      const float *__restrict__ w, int H, int lane) {
+    constexpr int D = 32 * KS;
+    const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int head = 16 * mt + n;
+        const int hc = head < H ? head : H - 1;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) f.qa[mt][ks] = load_bf16x8(q + hc * D + 32 * ks + 8 * g);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int head = 16 * mt + 4 * g + r;
+            f.wv[mt][r] = w[head < H ? head : H - 1];
+        }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int head = 16 * mt + n;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            if (head >= H) f.qa[mt][ks] = zero_bf16x8();
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (16 * mt + 4 * g + r >= H) f.wv[mt][r] = 0.0f;
+    }
+}
+
 // The row fragment of lane (n, g): 8 consecutive d of row n for each k-step.
 template <int KS>
 __device__ __forceinline__ void load_row_frag(bf16x8 (&kb)[KS], const uint16_t *row, int lane) {
