@@ -86,10 +86,17 @@ __device__ __forceinline__ void load_run(const uint32_t *__restrict__ keys, int6
 
 // Single-stage select: the whole row (n <= NT*R) in one workgroup of NT
 // threads (1024 for latency with few queries, 512 for throughput with many).
-template <int MODE, int R, int NT>
+// STAGE: the kept (id, key) pairs are first written to LDS at their slots,
+// then the row is stored with consecutive threads on consecutive entries
+// (kout <= kStageOut), instead of each thread storing its kept keys where
+// they fall.
+constexpr int kStageOut = 2048;
+
+template <int MODE, int R, int NT, bool STAGE>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     __shared__ __attribute__((aligned(16))) SelectScratch sc;
     __shared__ int32_t s_sel[kSelMaxM];
+    __shared__ uint32_t s_out[STAGE ? 2 * kStageOut : 1];      // ids, then keys
     const int tid = threadIdx.x;
     const int qi = blockIdx.x;
     const int64_t n = row_length<MODE>(a, qi);
@@ -121,10 +128,26 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
                 const int slot = id / grp;
                 id = s_sel[slot] * grp + (id - slot * grp);
             }
-            put(out, op, id);
-            if (osc) put(osc, op, key_to_score(key));
-            if (out2) put(out2, op, id);
+            if (STAGE) {
+                s_out[op] = static_cast<uint32_t>(id);
+                s_out[kStageOut + op] = key;
+            } else {
+                put(out, op, id);
+                if (osc) put(osc, op, key_to_score(key));
+                if (out2) put(out2, op, id);
+            }
         });
+    }
+    if (STAGE) {
+        __syncthreads();
+        for (int j = tid; j < a.kout; j += NT) {
+            const bool kept = j < static_cast<int>(res.keff);
+            const int32_t id = kept ? static_cast<int32_t>(s_out[j]) : -1;
+            out[j] = id;
+            if (osc) osc[j] = kept ? key_to_score(s_out[kStageOut + j]) : -__builtin_huge_valf();
+            if (out2) out2[j] = id;
+        }
+        return;
     }
     for (int j = static_cast<int>(res.keff) + tid; j < a.kout; j += NT) {
         out[j] = -1;
@@ -226,19 +249,27 @@ hipError_t launch_single(KernelKind kind, const SelectArgs &a, int nq, int64_t m
     if (nq >= kManyQueries && max_n <= kNarrowNT * 32) {
         const dim3 b(kNarrowNT);
         const int64_t per = (max_n + kNarrowNT - 1) / kNarrowNT;
-        if (per <= 4) return launch(kind, select_kernel<MODE, 4, kNarrowNT>, g, b, 0, st, a);
-        if (per <= 8) return launch(kind, select_kernel<MODE, 8, kNarrowNT>, g, b, 0, st, a);
-        if (per <= 16) return launch(kind, select_kernel<MODE, 16, kNarrowNT>, g, b, 0, st, a);
-        return launch(kind, select_kernel<MODE, 32, kNarrowNT>, g, b, 0, st, a);
+        if (per <= 4) return launch(kind, select_kernel<MODE, 4, kNarrowNT, false>, g, b, 0, st, a);
+        if (per <= 8) return launch(kind, select_kernel<MODE, 8, kNarrowNT, false>, g, b, 0, st, a);
+        if (per <= 16) return launch(kind, select_kernel<MODE, 16, kNarrowNT, false>, g, b, 0, st, a);
+        return launch(kind, select_kernel<MODE, 32, kNarrowNT, false>, g, b, 0, st, a);
     }
     const dim3 b(kNT);
     const int64_t per = (max_n + kNT - 1) / kNT;
-    if (per <= 1) return launch(kind, select_kernel<MODE, 1, kNT>, g, b, 0, st, a);
-    if (per <= 2) return launch(kind, select_kernel<MODE, 2, kNT>, g, b, 0, st, a);
-    if (per <= 4) return launch(kind, select_kernel<MODE, 4, kNT>, g, b, 0, st, a);
-    if (per <= 8) return launch(kind, select_kernel<MODE, 8, kNT>, g, b, 0, st, a);
-    if (per <= 16) return launch(kind, select_kernel<MODE, 16, kNT>, g, b, 0, st, a);
-    return launch(kind, select_kernel<MODE, 32, kNT>, g, b, 0, st, a);
+    if (a.kout <= kStageOut) {
+        if (per <= 1) return launch(kind, select_kernel<MODE, 1, kNT, true>, g, b, 0, st, a);
+        if (per <= 2) return launch(kind, select_kernel<MODE, 2, kNT, true>, g, b, 0, st, a);
+        if (per <= 4) return launch(kind, select_kernel<MODE, 4, kNT, true>, g, b, 0, st, a);
+        if (per <= 8) return launch(kind, select_kernel<MODE, 8, kNT, true>, g, b, 0, st, a);
+        if (per <= 16) return launch(kind, select_kernel<MODE, 16, kNT, true>, g, b, 0, st, a);
+        return launch(kind, select_kernel<MODE, 32, kNT, true>, g, b, 0, st, a);
+    }
+    if (per <= 1) return launch(kind, select_kernel<MODE, 1, kNT, false>, g, b, 0, st, a);
+    if (per <= 2) return launch(kind, select_kernel<MODE, 2, kNT, false>, g, b, 0, st, a);
+    if (per <= 4) return launch(kind, select_kernel<MODE, 4, kNT, false>, g, b, 0, st, a);
+    if (per <= 8) return launch(kind, select_kernel<MODE, 8, kNT, false>, g, b, 0, st, a);
+    if (per <= 16) return launch(kind, select_kernel<MODE, 16, kNT, false>, g, b, 0, st, a);
+    return launch(kind, select_kernel<MODE, 32, kNT, false>, g, b, 0, st, a);
 }
 
 template <int MODE>
