@@ -295,24 +295,29 @@ __global__ __launch_bounds__(kPoolThreads) void own_mean_kernel(
     if (static_cast<int>(threadIdx.x) < d) own_rep[static_cast<int64_t>(qi) * d + threadIdx.x] = m;
 }
 
-// grid: (blocks b_lo .. b_lo + gridDim.x - 1, S, kPrefixSegments), d threads.
-// Consecutive query positions t = L - T + i: a running fp64 sum (or running
-// maximum) down each block's rows, in row order, is at row t exactly that of
-// rows [b_t*B, t] in row order, so every query of the block gets its own-block
-// representative from one pass -- the same arithmetic as staged_column_rep().
-// The block's rows are split into kPrefixSegments runs of outputs: the
-// workgroup of run z sums from the block's first row and writes the
-// representatives of the rows of its run, so the divisions of different runs
-// proceed in parallel.
+// grid: (blocks b_lo .. b_lo + gridDim.x - 1, S, kPrefixSegments),
+// kPrefixThreads threads.  Consecutive query positions t = L - T + i: the
+// own-block representative of the query at t is the running fp64 sum (or
+// running maximum) down its block's rows in row order, taken at row t -- the
+// same arithmetic as staged_column_rep().  The block's rows are split into
+// kPrefixSegments runs of outputs, one workgroup each; the workgroup stages
+// the block's rows up to its run's end in LDS, and thread (g, c) takes column
+// c and outputs g*per .. g*per + per - 1 of the run: it sums the column from
+// the block's first row in row order, then writes a representative after each
+// of its own rows.  The prefix before a thread's outputs is summed again by
+// every thread that needs it (at most B additions from LDS), which costs less
+// than the divisions of a whole run done one after another by a single thread
+// per column: 16 us for a 4096-query chunk that way.
 constexpr int kPrefixSegments = 4;
+constexpr int kPrefixThreads = 1024;
 
 template <bool MAX>
-__global__ __launch_bounds__(kMaxD) void own_prefix_mean_kernel(
+__global__ __launch_bounds__(kPrefixThreads) void own_prefix_mean_kernel(
         const uint16_t *__restrict__ K, int64_t k_seq_stride, int64_t L, int T, int d, int B,
         int64_t b_lo, uint16_t *__restrict__ own_rep) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[kMaxRows * kMaxD];
     const int s = blockIdx.y;
-    const int col = threadIdx.x;
-    if (col >= d) return;
+    const int tid = threadIdx.x;
     const int64_t t0 = L - T;                                  // position of query 0
     const int64_t r0 = (b_lo + blockIdx.x) * B;
     const int seg = B / kPrefixSegments;
@@ -320,30 +325,34 @@ __global__ __launch_bounds__(kMaxD) void own_prefix_mean_kernel(
     const int64_t blk_end = (r0 + B < L) ? r0 + B : L;
     const int64_t r_end = (out_lo + seg < blk_end) ? out_lo + seg : blk_end;   // rows summed: r0 .. r_end-1
     const int64_t r_first = out_lo > t0 ? out_lo : t0;         // first row written
-    if (r_first >= r_end) return;
-    const uint16_t *src = K + s * k_seq_stride + col;
+    if (r_first >= r_end) return;                              // whole workgroup
+    // stage rows r0 .. r_end-1 (16-byte chunks; d is a multiple of 8)
+    const int rows = static_cast<int>(r_end - r0);
+    const int cpr = d / 8;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(K + s * k_seq_stride + r0 * d);
+    for (int c = tid; c < rows * cpr; c += kPrefixThreads)
+        *reinterpret_cast<u32x4 *>(lds + 8 * c) = src[c];
+    __syncthreads();
+    const int groups = kPrefixThreads / d;                     // 8 (d = 128) or 16 (d = 64)
+    const int col = tid % d, g = tid / d;
+    const int per = (seg + groups - 1) / groups;
+    const int64_t o_lo = out_lo + static_cast<int64_t>(g) * per;
+    const int64_t o_hi = (o_lo + per < r_end) ? o_lo + per : r_end;
+    if (o_lo >= o_hi) return;
     ColumnRep<MAX> acc;
-    // rows in rounds of U, the next round's loads in flight while the current
-    // round is summed (rows past the end re-read the last row, unused)
-    constexpr int U = 16;
-    const int64_t last = r_end - 1;
-    uint16_t nx[U];
+    const int pre = static_cast<int>(o_lo - r0);               // rows before this thread's outputs
+    int r = 0;
+    for (; r + 8 <= pre; r += 8) {                             // 8 LDS reads in flight, added in row order
+        uint16_t x[8];
 #pragma unroll
-    for (int j = 0; j < U; ++j) nx[j] = src[(r0 + j < r_end ? r0 + j : last) * d];
-    for (int64_t r = r0; r < r_end; r += U) {
-        uint16_t x[U];
+        for (int j = 0; j < 8; ++j) x[j] = lds[(r + j) * d + col];
 #pragma unroll
-        for (int j = 0; j < U; ++j) x[j] = nx[j];
-#pragma unroll
-        for (int j = 0; j < U; ++j) nx[j] = src[(r + U + j < r_end ? r + U + j : last) * d];
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-            const int64_t rr = r + j;
-            if (rr < r_end) {
-                acc.add(x[j]);
-                if (rr >= r_first) own_rep[(static_cast<int64_t>(s) * T + (rr - t0)) * d + col] = acc.get(rr + 1 - r0);
-            }
-        }
+        for (int j = 0; j < 8; ++j) acc.add(x[j]);
+    }
+    for (; r < pre; ++r) acc.add(lds[r * d + col]);
+    for (int64_t o = o_lo; o < o_hi; ++o) {
+        acc.add(lds[(o - r0) * d + col]);
+        if (o >= r_first) own_rep[(static_cast<int64_t>(s) * T + (o - t0)) * d + col] = acc.get(o + 1 - r0);
     }
 }
 
@@ -396,10 +405,10 @@ hipError_t launch_own_prefix_mean(const uint16_t *K, int64_t k_seq_stride, int64
     const int64_t b_lo = (L - T) / B, b_hi = (L - 1) / B;
     const dim3 g(static_cast<uint32_t>(b_hi - b_lo + 1), S, kPrefixSegments);
     if (pool_max)
-        return launch(kKindOwnMean, own_prefix_mean_kernel<true>, g, dim3(kMaxD), 0, st, K, k_seq_stride, L, T, d, B,
-                      b_lo, own_rep);
-    return launch(kKindOwnMean, own_prefix_mean_kernel<false>, g, dim3(kMaxD), 0, st, K, k_seq_stride, L, T, d, B,
-                  b_lo, own_rep);
+        return launch(kKindOwnMean, own_prefix_mean_kernel<true>, g, dim3(kPrefixThreads), 0, st, K, k_seq_stride, L,
+                      T, d, B, b_lo, own_rep);
+    return launch(kKindOwnMean, own_prefix_mean_kernel<false>, g, dim3(kPrefixThreads), 0, st, K, k_seq_stride, L, T,
+                  d, B, b_lo, own_rep);
 }
 
 hipError_t launch_pool_append(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B,
