@@ -456,10 +456,12 @@ __device__ __forceinline__ uint32_t topm_select(uint32_t (&kv)[R], uint32_t own_
         const int p = lane * rd + r;
         kv[r] = (r < rd && p < nb) ? (p == nb - 1 ? own_key : kv[r]) : kNoCandidate;
     }
-    // the ballot select for up to 256 blocks; beyond, its rounds grow with R
-    // and the LDS histogram of wave_window_select costs less
-    const SelectResult res = R <= 4 ? wave_ballot_select<R>(kv, static_cast<uint32_t>(m))
-                                    : wave_window_select<R>(kv, static_cast<uint32_t>(m), win);
+    // the ballot select up to 1024 blocks (R <= 16): with sixteen waves per
+    // compute unit it measured slightly faster than the LDS histogram of
+    // wave_window_select (4096-query chunk, 1008-1024 blocks: 32.8 -> 31.4 us
+    // in a same-box A/B); beyond, its rounds grow with R and the window wins
+    const SelectResult res = R <= 16 ? wave_ballot_select<R>(kv, static_cast<uint32_t>(m))
+                                     : wave_window_select<R>(kv, static_cast<uint32_t>(m), win);
     if (res.keff > 0) wave_compact<R>(kv, res, [&](uint32_t op, int r, uint32_t) { emit(op, lane * rd + r); });
     return res.keff;
 }
