@@ -668,9 +668,11 @@ WINDOW_PATHS = [("decode", 16, 1), ("batch", 16, 160), ("chunk", 64, 160)]
 @pytest.mark.parametrize("kind", WINDOW_CASES)
 @pytest.mark.parametrize("path", WINDOW_PATHS, ids=[p[0] for p in WINDOW_PATHS])
 def test_window_top_m_branches(hisa, orc, kind, path):
-    """700 blocks per query, so each path keeps its top m with the one-wave
-    window select; blocks and tokens are checked against the oracle on
-    sampled queries of both sequences."""
+    """700 blocks per query: the two-kernel decode and the query-major batch
+    keep their top m with the one-wave window select, the block-by-block
+    chunk with the ballot select (its choice up to 1024 blocks); blocks and
+    tokens are checked against the oracle on sampled queries of both
+    sequences."""
     name, B, T = path
     c = _window_case(kind, B, T)
     _say(f"window top m: {kind} {name}")
