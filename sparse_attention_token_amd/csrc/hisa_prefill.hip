@@ -47,6 +47,13 @@ __global__ __launch_bounds__(kBucketThreads) void hisa_bucket_kernel(FusedArgs a
     __shared__ uint32_t s_cnt[kFusedMaxBlocks];
     __shared__ uint32_t s_wave[kBucketThreads / 64];
     __shared__ int32_t s_bt[kChunkQueries];
+    // a chunk of at most kBucketU * kBucketThreads pairs (the kept blocks of
+    // 256 queries with m <= 64) is sorted in one pass: its block ids stay in
+    // registers, and the sorted pairs are gathered in LDS and stored in order
+    // (stored where they fall they took 16 scattered stores per thread)
+    constexpr int kStagePairs = ALL ? 1 : kBucketU * kBucketThreads;
+    __shared__ uint32_t s_stage[kStagePairs];
+    __shared__ uint32_t s_total;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = blockIdx.x;
     const int cps = (a.T + kChunkQueries - 1) / kChunkQueries;
@@ -74,6 +81,10 @@ __global__ __launch_bounds__(kBucketThreads) void hisa_bucket_kernel(FusedArgs a
     // the chunk's kept blocks, kBucketU per thread at a time with every load
     // issued before the first atomic (a load per iteration would serialise
     // n / kBucketThreads memory round trips)
+    const bool one_pass = !ALL && n <= kStagePairs;
+    int bb1[kBucketU];                            // one_pass: the chunk's block ids, kept for the fill
+#pragma unroll
+    for (int u = 0; u < kBucketU; ++u) bb1[u] = -1;
     for (int e0 = 0; e0 < n; e0 += kBucketU * kBucketThreads) {
         int bb[kBucketU];
 #pragma unroll
@@ -82,8 +93,10 @@ __global__ __launch_bounds__(kBucketThreads) void hisa_bucket_kernel(FusedArgs a
             bb[u] = e < n ? block_of(e) : -1;
         }
 #pragma unroll
-        for (int u = 0; u < kBucketU; ++u)
+        for (int u = 0; u < kBucketU; ++u) {
             if (bb[u] >= 0) atomicAdd(&s_cnt[bb[u]], 1u);
+            bb1[u] = bb[u];
+        }
     }
     __syncthreads();
 
@@ -111,10 +124,28 @@ __global__ __launch_bounds__(kBucketThreads) void hisa_bucket_kernel(FusedArgs a
         }
         run += v[r];
     }
-    if (tid == kBucketThreads - 1) off[nblk] = static_cast<int32_t>(run);
+    if (tid == kBucketThreads - 1) {
+        off[nblk] = static_cast<int32_t>(run);
+        s_total = run;                            // the pair count
+    }
     __syncthreads();
 
     uint32_t *ent = a.bucket_ent + static_cast<int64_t>(c) * kChunkQueries * a.m;
+    if (one_pass) {
+        const uint32_t total = s_total;
+#pragma unroll
+        for (int u = 0; u < kBucketU; ++u) {
+            if (bb1[u] >= 0) {
+                const int e = u * kBucketThreads + tid;
+                const uint32_t pos = atomicAdd(&s_cnt[bb1[u]], 1u);
+                const int ql = e / a.m;
+                s_stage[pos] = (static_cast<uint32_t>(ql) << 16) | static_cast<uint32_t>(e - ql * a.m);
+            }
+        }
+        __syncthreads();
+        for (uint32_t i = tid; i < total; i += kBucketThreads) ent[i] = s_stage[i];
+        return;
+    }
     for (int e0 = 0; e0 < n; e0 += kBucketU * kBucketThreads) {
         int bb[kBucketU];
 #pragma unroll
