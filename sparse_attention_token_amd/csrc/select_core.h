@@ -156,7 +156,10 @@ __device__ __forceinline__ SelectResult block_radix_select(const uint32_t (&kv)[
         mask |= static_cast<uint32_t>(nb - 1) << shift;
         need -= sc.above;
         const uint32_t in_bin = sc.count;
-        __syncthreads();   // digit/above/count and wave_tot are rewritten by the next pass
+        // No barrier here: the next pass rewrites wave_tot and digit/above/count
+        // only after its histogram barrier, which every thread reaches after
+        // these reads; after a return, block_compact rewrites only wave_tot,
+        // whose reads all came before the barrier above.
         // every key of the cutoff bin is kept: the kept set is exactly the keys
         // >= prefix (low bits still open), i.e. the keys > prefix - 1, with
         // none kept at equality -- no further pass needed
