@@ -639,9 +639,11 @@ int hisa_tree_index(const uint16_t *q, const float *w, const int32_t *qpos, cons
     int32_t *sel_blk = reinterpret_cast<int32_t *>(base + lay.sel_blk);
     uint32_t *cand_keys = reinterpret_cast<uint32_t *>(base + lay.cand_keys);
     const int nq = S * T;
+    bool scored = false;     // the token level's scores already in cand_keys
 
     if (tree_top_supported(d, L, B, G, W)) {
-        // levels 1-2 in one launch, then the token level
+        // levels 1-2 in two launches (tree_top_kernel, then tree_gather_kernel
+        // with the token scores for few queries, else tree_topm_kernel)
         TreeTopArgs ta{};
         ta.q = q; ta.w = w; ta.qpos = qpos;
         ta.K = K; ta.k_seq_stride = k_seq_stride; ta.L = L;
@@ -650,7 +652,11 @@ int hisa_tree_index(const uint16_t *q, const float *w, const int32_t *qpos, cons
         ta.S = S; ta.T = T; ta.H = H; ta.d = d; ta.B = B; ta.G = G; ta.W = W; ta.m = m;
         ta.pool_max = pmax ? 1 : 0;
         ta.sel_blk = sel_blk; ta.out_blk = out_blk; ta.out_sblk = out_sblk;
-        st = hip_status(launch_tree_top(ta, hs));
+        ta.sel_sb = reinterpret_cast<int32_t *>(base + lay.sel_sb);
+        ta.tblk_keys = reinterpret_cast<uint32_t *>(base + lay.tblk_keys);
+        ta.tblk_stride = lay.tblk_stride;
+        ta.cand_keys = cand_keys; ta.cand_stride = lay.cand_stride;
+        st = hip_status(launch_tree_top(ta, hs, &scored));
         if (st != HISA_OK) return st;
     } else {
         st = tree_upper_levels(q, w, qpos, K, k_seq_stride, L, pool_rep, pool_seq_stride, spool_rep,
@@ -660,13 +666,15 @@ int hisa_tree_index(const uint16_t *q, const float *w, const int32_t *qpos, cons
 
     // level 3: the tokens of the kept blocks (slots past the kept count hold
     // -1 and give no candidate); keep the top k
-    ScoreArgs sa{};
-    sa.q = q; sa.w = w; sa.qpos = qpos;
-    sa.K = K; sa.k_seq_stride = k_seq_stride; sa.L = L;
-    sa.S = S; sa.T = T; sa.H = H; sa.d = d; sa.B = B; sa.m = m; sa.sel_blk = sel_blk;
-    sa.keys = cand_keys; sa.keys_stride = lay.cand_stride;
-    st = hip_status(launch_score(kScoreRefine, sa, static_cast<int64_t>(m) * B, hs));
-    if (st != HISA_OK) return st;
+    if (!scored) {
+        ScoreArgs sa{};
+        sa.q = q; sa.w = w; sa.qpos = qpos;
+        sa.K = K; sa.k_seq_stride = k_seq_stride; sa.L = L;
+        sa.S = S; sa.T = T; sa.H = H; sa.d = d; sa.B = B; sa.m = m; sa.sel_blk = sel_blk;
+        sa.keys = cand_keys; sa.keys_stride = lay.cand_stride;
+        st = hip_status(launch_score(kScoreRefine, sa, static_cast<int64_t>(m) * B, hs));
+        if (st != HISA_OK) return st;
+    }
     SelectArgs se{};
     se.qpos = qpos; se.L = L; se.T = T;
     set_stage(se, base, lay.stage);

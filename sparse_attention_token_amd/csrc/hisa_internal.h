@@ -213,10 +213,17 @@ struct TreeTopArgs {
     int32_t *sel_blk;         // [S*T][m]: kept blocks, ascending, -1 padded
     int32_t *out_blk;         // [S*T][m] or null
     int32_t *out_sblk;        // [S*T][W] or null
+    int32_t *sel_sb;          // [S*T][W]: kept super-blocks, ascending, -1 padded (workspace)
+    uint32_t *tblk_keys;      // [S*T][tblk_stride]: keys of the kept super-blocks' blocks (workspace)
+    int64_t tblk_stride;
+    uint32_t *cand_keys;      // [S*T][cand_stride]: token keys, refine-mode layout (workspace)
+    int64_t cand_stride;
 };
 
 bool tree_top_supported(int d, int64_t L, int B, int G, int W);
-hipError_t launch_tree_top(const TreeTopArgs &a, hipStream_t st);
+// Levels 1-2 and the top m; for few queries also the token level's scores
+// (cand_keys), which *scored reports -- otherwise the caller scores them.
+hipError_t launch_tree_top(const TreeTopArgs &a, hipStream_t st, bool *scored);
 
 // ---------------------------------------------------------------- sparse attention (attention.hip)
 struct AttnArgs {

@@ -14,15 +14,22 @@
 //   4. keep the top m blocks.
 // The token level (gather, score, top k) then runs as in the two-level path.
 //
-// tree_top_kernel does steps 1-4 for one query per 512-thread workgroup:
-// q and w are staged in LDS and held as MFMA fragments (the shared scorer of
-// scorer.h, so every score has the bits of the general path's kernels); the
-// 8 waves score 16-row tiles, four tiles in flight per wave; each top-W / top-m
-// is the one-wave ballot select over keys kept in LDS.  For the query at the
-// cache's last row the pools already hold its own block and own super-block
-// (the caller keeps them current through row L-1), so both are read like the
-// other rows; any other query's own block is staged and pooled here (the pool's
-// arithmetic), and its own super-block pooled from the pool entries and that.
+// tree_top_kernel does steps 1-3 with several 512-thread workgroups per
+// query: each stages q and w in LDS and holds them as MFMA fragments (the
+// shared scorer of scorer.h, so every score has the bits of the general
+// path's kernels), scores the super-blocks with its 8 waves (16-row tiles,
+// four in flight per wave) and keeps the top W with the one-wave ballot select
+// over keys kept in LDS -- the same in every workgroup of the query -- and then
+// scores its own slice of 128 of the kept super-blocks' blocks (one tile per
+// wave) into the workspace.  tree_topm_kernel then keeps the top m of those
+// keys for each query in one wave (step 4).  Done by one workgroup per query,
+// the block level's 1024 rows took four rounds of one workgroup, and a decode
+// batch of a few sequences kept a few compute units busy.  For the query at
+// the cache's last row the pools already hold its own block and own
+// super-block (the caller keeps them current through row L-1), so both are
+// read like the other rows; any other query's own block is staged and pooled
+// here (the pool's arithmetic), and its own super-block pooled from the pool
+// entries and that.
 // Limits (checked by the host, tree_top_supported): at most 2048 super-blocks
 // visible, W*G <= 2048, B*d <= 16384.
 
@@ -40,6 +47,9 @@ constexpr int kTopThreads = 512;
 constexpr int kTopWaves = kTopThreads / 64;
 constexpr int kTopMaxRows = 2048;      // rows one ballot select takes (64 lanes x 32)
 constexpr int kTopTB = 4;              // tiles in flight per wave
+constexpr int kSliceRows = 16 * kTopWaves;   // fewest blocks per workgroup at the block level: a tile per wave
+constexpr int kTopGroups = 512;        // workgroups sought per launch: slices repeat the super-block stage
+constexpr int kTopmWaves = 4;          // queries per tree_topm_kernel workgroup, one wave each
 
 template <int KS>
 struct TreeTopLds {
@@ -83,11 +93,11 @@ __device__ __forceinline__ uint32_t top_select(const uint32_t *s_keys, int n, in
     return run(std::integral_constant<int, 32>{});
 }
 
-// Scores n rows, row(p) giving row p's address (null: no candidate), into
-// keys[top_slot(p, n)].  Waves take 16-row tiles round-robin, kTopTB at a time
-// with their loads issued first.  Ends with a barrier.
-template <int MT, int KS, typename RowOf>
-__device__ __forceinline__ void score_into(const QFrag<MT, KS> &f, int n, uint32_t *keys, RowOf &&row_of) {
+// Scores n rows, row(p) giving row p's address (null: no candidate), and
+// hands each key to store(p, key).  Waves take 16-row tiles round-robin,
+// kTopTB at a time with their loads issued first.
+template <int MT, int KS, typename RowOf, typename Store>
+__device__ __forceinline__ void score_into(const QFrag<MT, KS> &f, int n, RowOf &&row_of, Store &&store) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int ntiles = (n + 15) / 16;
@@ -107,11 +117,10 @@ __device__ __forceinline__ void score_into(const QFrag<MT, KS> &f, int n, uint32
             if (tile < ntiles) {
                 const int p = tile * 16 + r;
                 const float v = score_rows<MT, KS>(f, kb[u]);
-                if (g == 0 && p < n) keys[top_slot(p, n)] = valid[u] ? score_to_key(v) : kNoCandidate;
+                if (g == 0 && p < n) store(p, valid[u] ? score_to_key(v) : kNoCandidate);
             }
         }
     }
-    __syncthreads();
 }
 
 // Own super-block representative: per column, the pool entries b0 .. bt-1 in
@@ -149,24 +158,27 @@ __device__ __forceinline__ uint16_t super_column(const uint16_t *pool_col, int d
                : f32_to_bf16_rne(static_cast<float>(sum / static_cast<double>((bt - b0) * B + own_cnt)));
 }
 
+// Grid S*T*nslice: workgroup (query qi, slice) scores blocks
+// slice*rows .. slice*rows+rows-1 of the kept super-blocks' blocks (in kept
+// order) into tblk_keys[qi]; slice 0 also publishes the kept super-blocks.
 template <int MT, int KS, bool MAX>
-__global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a) {
+__global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a, int nslice, int rows) {
     constexpr int D = 32 * KS;
     __shared__ __attribute__((aligned(16))) TreeTopLds<KS> L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int qi = blockIdx.x;
+    const int qi = blockIdx.x / nslice;
+    const int slice = blockIdx.x - qi * nslice;
+    const bool lead = slice == 0;
     const int s = qi / a.T;
     const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
-    int32_t *sel = a.sel_blk + static_cast<int64_t>(qi) * a.m;
-    int32_t *ob = a.out_blk ? a.out_blk + static_cast<int64_t>(qi) * a.m : nullptr;
+    int32_t *ssb = a.sel_sb + static_cast<int64_t>(qi) * a.W;
     int32_t *osb = a.out_sblk ? a.out_sblk + static_cast<int64_t>(qi) * a.W : nullptr;
-    if (t < 0) {                                 // no candidate at all
-        for (int j = tid; j < a.m; j += kTopThreads) {
-            sel[j] = -1;
-            if (ob) ob[j] = -1;
-        }
-        if (osb)
-            for (int j = tid; j < a.W; j += kTopThreads) osb[j] = -1;
+    if (t < 0) {                                 // no candidate at all (tree_topm_kernel pads the blocks)
+        if (lead)
+            for (int j = tid; j < a.W; j += kTopThreads) {
+                ssb[j] = -1;
+                if (osb) osb[j] = -1;
+            }
         return;
     }
     const int64_t bt = t / a.B;
@@ -209,55 +221,248 @@ __global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a) {
     QFrag<MT, KS> f;
     load_qfrag_lds_w<MT, KS>(f, L.q, L.w, lane);
 
-    // ---- levels 1-2: super-block scores, top W
-    score_into<MT, KS>(f, ns, L.keys, [&](int u) -> const uint16_t * {
-        return u < st ? spool + static_cast<int64_t>(u) * D : own_srep;
-    });
+    // ---- levels 1-2: super-block scores, top W (the same in every slice)
+    score_into<MT, KS>(
+        f, ns,
+        [&](int u) -> const uint16_t * { return u < st ? spool + static_cast<int64_t>(u) * D : own_srep; },
+        [&](int u, uint32_t key) { L.keys[top_slot(u, ns)] = key; });
+    __syncthreads();
     if (wave == 0) {
         const uint32_t ke = top_select(L.keys, ns, a.W, L.own, [&](uint32_t op, int u) {
             L.sb[op] = u;
-            if (osb) osb[op] = u;
+            if (lead) {
+                ssb[op] = u;
+                if (osb) osb[op] = u;
+            }
         });
         if (lane == 0) L.keff = ke;
     }
     __syncthreads();
     const int weff = static_cast<int>(L.keff);
-    if (osb)
-        for (int j = weff + tid; j < a.W; j += kTopThreads) osb[j] = -1;
+    if (lead)
+        for (int j = weff + tid; j < a.W; j += kTopThreads) {
+            ssb[j] = -1;
+            if (osb) osb[j] = -1;
+        }
 
-    // ---- levels 2-3: the blocks of the kept super-blocks, top m
+    // ---- level 2: this workgroup's slice of the kept super-blocks' blocks
     const int nt = weff * a.G;
-    score_into<MT, KS>(f, nt, L.keys, [&](int p) -> const uint16_t * {
-        const int slot = p / a.G;
-        const int64_t b = static_cast<int64_t>(L.sb[slot]) * a.G + (p - slot * a.G);
-        return b < bt ? pool + b * D : (b == bt ? own_rep : nullptr);
-    });
-    if (wave == 0) {
-        const uint32_t ke = top_select(L.keys, nt, a.m, L.own, [&](uint32_t op, int p) {
+    const int p0 = slice * rows;
+    if (p0 >= nt) return;
+    uint32_t *keys = a.tblk_keys + static_cast<int64_t>(qi) * a.tblk_stride + p0;
+    score_into<MT, KS>(
+        f, nt - p0 < rows ? nt - p0 : rows,
+        [&](int i) -> const uint16_t * {
+            const int p = p0 + i;
             const int slot = p / a.G;
-            const int32_t b = L.sb[slot] * a.G + (p - slot * a.G);
+            const int64_t b = static_cast<int64_t>(L.sb[slot]) * a.G + (p - slot * a.G);
+            return b < bt ? pool + b * D : (b == bt ? own_rep : nullptr);
+        },
+        [&](int i, uint32_t key) { keys[i] = key; });
+}
+
+// Level 3 of the search for query qi (t >= 0), by one wave: the top m of the
+// W*G block keys tree_top_kernel wrote (kept super-block order); emit(op, b)
+// gets the kept block ids in ascending order.  Returns the number kept.
+// Lane l holds positions l*rd .. l*rd + rd - 1 with rd = ceil(ntb / 64) for
+// the launch's bound ntb on weff*G, so the keys are loaded together with the
+// kept super-blocks rather than after them; positions past the query's
+// weff*G are dropped once weff is known.  R >= rd.  s_sb: W ints of LDS,
+// win: kWindowWords words, both this wave's alone.
+template <int R, typename Emit>
+__device__ __forceinline__ uint32_t tree_topm_wave(const TreeTopArgs &a, int qi, int ntb, int32_t *s_sb,
+                                                   uint32_t *win, Emit &&emit) {
+    const int lane = threadIdx.x & 63;
+    const int rd = (ntb + 63) / 64;
+    const uint32_t *keys = a.tblk_keys + static_cast<int64_t>(qi) * a.tblk_stride;
+    uint32_t kv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {                      // every load issued before any is used
+        const int p = lane * rd + r;
+        kv[r] = keys[(r < rd && p < ntb) ? p : 0];
+    }
+    // the kept super-blocks (ascending, then -1) into LDS for the block ids
+    const int32_t *ssb = a.sel_sb + static_cast<int64_t>(qi) * a.W;
+    int weff = 0;
+    for (int j0 = 0; j0 < a.W; j0 += 64) {
+        const int j = j0 + lane;
+        const int32_t u = ssb[j < a.W ? j : a.W - 1];
+        if (j < a.W) s_sb[j] = u;
+        weff += static_cast<int>(__popcll(__ballot(j < a.W && u >= 0)));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int nt = weff * a.G;                         // <= ntb
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (!(r < rd && lane * rd + r < nt)) kv[r] = kNoCandidate;
+    const SelectResult res = R <= 4 ? wave_ballot_select<R>(kv, static_cast<uint32_t>(a.m))
+                                    : wave_window_select<R>(kv, static_cast<uint32_t>(a.m), win);
+    if (res.keff > 0)
+        wave_compact<R>(kv, res, [&](uint32_t op, int r, uint32_t) {
+            const int p = lane * rd + r;
+            const int slot = p / a.G;
+            emit(op, s_sb[slot] * a.G + (p - slot * a.G));
+        });
+    return res.keff;
+}
+
+// Level 3 alone, one wave per query (many queries: the refinement then runs
+// as score_kernel).
+template <int R>
+__global__ __launch_bounds__(64 * kTopmWaves) void tree_topm_kernel(TreeTopArgs a, int ntb) {
+    __shared__ int32_t s_sb[kTopmWaves][kTopMaxRows];
+    __shared__ __attribute__((aligned(16))) uint32_t s_win[kTopmWaves][kWindowWords];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int qi = blockIdx.x * kTopmWaves + wv;
+    if (qi >= a.S * a.T) return;                       // whole wave
+    const int s = qi / a.T;
+    const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    int32_t *sel = a.sel_blk + static_cast<int64_t>(qi) * a.m;
+    int32_t *ob = a.out_blk ? a.out_blk + static_cast<int64_t>(qi) * a.m : nullptr;
+    uint32_t keff = 0;
+    if (t >= 0)
+        keff = tree_topm_wave<R>(a, qi, ntb, s_sb[wv], s_win[wv], [&](uint32_t op, int32_t b) {
             sel[op] = b;
             if (ob) ob[op] = b;
         });
-        if (lane == 0) L.keff = ke;
-    }
-    __syncthreads();
-    for (int j = static_cast<int>(L.keff) + tid; j < a.m; j += kTopThreads) {
+    for (int j = static_cast<int>(keff) + lane; j < a.m; j += 64) {
         sel[j] = -1;
         if (ob) ob[j] = -1;
     }
 }
 
+// Level 3 and the token level's scores for few queries, grid S*T*tiles: every
+// workgroup of a query repeats its top m in wave 0 while the others stage q
+// and w (a launch of its own cost more than the repeated select), then scores
+// its kTreeGatherRows candidate rows (tile) into cand_keys, as score_kernel's
+// refine mode does: row p is token p % B of kept slot p / B; slots past the
+// kept count, and tokens past t, give no candidate.
+constexpr int kTreeGatherThreads = 256;
+constexpr int kTreeGatherRows = 128;          // 2 tiles of 16 rows per wave
+constexpr int kTreeGatherMaxQueries = 16;
+constexpr int kTreeGatherMaxM = 1024;
+
+template <int MT, int KS, int R>
+__global__ __launch_bounds__(kTreeGatherThreads) void tree_gather_kernel(TreeTopArgs a, int ntb, int tiles) {
+    constexpr int D = 32 * KS;
+    constexpr int NTW = kTreeGatherRows / (16 * kTreeGatherThreads / 64);
+    __shared__ __attribute__((aligned(16))) uint16_t s_q[64 * QStage<KS>::kStride];
+    __shared__ float s_w[64];
+    __shared__ int32_t s_sb[kTopMaxRows];
+    __shared__ int32_t s_sel[kTreeGatherMaxM];
+    __shared__ __attribute__((aligned(16))) uint32_t s_win[kWindowWords];
+    __shared__ uint32_t s_keff;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int qi = blockIdx.x / tiles;
+    const int tile = blockIdx.x - qi * tiles;
+    const bool lead = tile == 0;                       // also publishes the kept blocks
+    const int s = qi / a.T;
+    const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    int32_t *sel = a.sel_blk + static_cast<int64_t>(qi) * a.m;
+    int32_t *ob = a.out_blk ? a.out_blk + static_cast<int64_t>(qi) * a.m : nullptr;
+    if (t < 0) {                                       // the select reads no candidate row
+        if (lead)
+            for (int j = tid; j < a.m; j += kTreeGatherThreads) {
+                sel[j] = -1;
+                if (ob) ob[j] = -1;
+            }
+        return;
+    }
+    const int64_t bt = t / a.B;
+    // the refine-mode row length the select reads: min(m, b_t + 1) slots of B
+    const int npos = static_cast<int>((a.m < bt + 1 ? a.m : bt + 1) * a.B);
+    const int tile0 = tile * kTreeGatherRows;
+    if (tile0 >= npos) return;
+
+    QStager<MT, KS, kTreeGatherThreads> qst;
+    qst.load(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, tid);
+    const float wq0 = a.w[static_cast<int64_t>(qi) * a.H + (tid < a.H ? tid : a.H - 1)];   // unconditional load
+    const float wq = tid < a.H ? wq0 : 0.0f;
+    if (wave == 0) {
+        const uint32_t ke = tree_topm_wave<R>(a, qi, ntb, s_sb, s_win, [&](uint32_t op, int32_t b) {
+            s_sel[op] = b;
+            if (lead) {
+                sel[op] = b;
+                if (ob) ob[op] = b;
+            }
+        });
+        if (lane == 0) s_keff = ke;
+    }
+    qst.store(s_q, a.H, tid);
+    if (tid < 64) s_w[tid] = wq;
+    __syncthreads();
+    const int keff = static_cast<int>(s_keff);
+    if (lead)
+        for (int j = keff + tid; j < a.m; j += kTreeGatherThreads) {
+            sel[j] = -1;
+            if (ob) ob[j] = -1;
+        }
+
+    // rows past the kept slots, or past t, load row t (a valid row) and are
+    // stored as no candidate
+    bf16x8 kb[NTW][KS];
+    bool valid[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+        const int p = tile0 + (wave * NTW + nt) * 16 + n;
+        const int slot = p / a.B;
+        const int64_t tok = slot < keff ? static_cast<int64_t>(s_sel[slot]) * a.B + (p - slot * a.B) : t;
+        valid[nt] = p < npos && slot < keff && tok <= t;
+        load_row_frag_any<KS>(kb[nt], a.K + s * a.k_seq_stride + (tok <= t ? tok : t) * D, lane);
+    }
+    QFrag<MT, KS> f;
+    load_qfrag_lds_w<MT, KS>(f, s_q, s_w, lane);
+    float v[NTW];
+    score_tiles_frag<MT, KS, NTW>(f, kb, v);
+    uint32_t *cand = a.cand_keys + static_cast<int64_t>(qi) * a.cand_stride;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+        const int p = tile0 + (wave * NTW + nt) * 16 + n;
+        if (g == 0 && p < npos) cand[p] = valid[nt] ? score_to_key(v[nt]) : kNoCandidate;
+    }
+}
+
 template <int MT, int KS>
-hipError_t launch_top_ks(const TreeTopArgs &a, hipStream_t st) {
-    const dim3 grid(static_cast<uint32_t>(a.S * a.T)), block(kTopThreads);
-    if (a.pool_max) return launch(kKindTreeTop, tree_top_kernel<MT, KS, true>, grid, block, 0, st, a);
-    return launch(kKindTreeTop, tree_top_kernel<MT, KS, false>, grid, block, 0, st, a);
+hipError_t launch_top_ks(const TreeTopArgs &a, hipStream_t st, bool *scored) {
+    const int nq = a.S * a.T;
+    const int64_t ns = ((a.L + a.B - 1) / a.B + a.G - 1) / a.G;
+    const int64_t ntb = (a.W < ns ? a.W : ns) * a.G;   // at most 2048 (tree_top_supported)
+    // slices of at least 128 blocks, as many as keep about kTopGroups
+    // workgroups busy (one for large batches: no repeated super-block stage)
+    const int most = static_cast<int>((ntb + kSliceRows - 1) / kSliceRows);
+    const int want = (kTopGroups + nq - 1) / nq;
+    const int nslice = want < most ? want : most;
+    const int rows = static_cast<int>((ntb + nslice - 1) / nslice + 15) / 16 * 16;
+    const dim3 grid(static_cast<uint32_t>(nq * nslice)), block(kTopThreads);
+    hipError_t e = a.pool_max
+                       ? launch(kKindTreeTop, tree_top_kernel<MT, KS, true>, grid, block, 0, st, a, nslice, rows)
+                       : launch(kKindTreeTop, tree_top_kernel<MT, KS, false>, grid, block, 0, st, a, nslice, rows);
+    if (e != hipSuccess) return e;
+    const int nt = static_cast<int>(ntb);
+    const int rd = (nt + 63) / 64;
+    *scored = nq <= kTreeGatherMaxQueries && a.m <= kTreeGatherMaxM;
+    if (*scored) {
+        const int tiles = static_cast<int>((static_cast<int64_t>(a.m) * a.B + kTreeGatherRows - 1) / kTreeGatherRows);
+        const dim3 g3(static_cast<uint32_t>(nq * tiles)), b3(kTreeGatherThreads);
+        if (rd <= 4) return launch(kKindScoreRefine, tree_gather_kernel<MT, KS, 4>, g3, b3, 0, st, a, nt, tiles);
+        if (rd <= 8) return launch(kKindScoreRefine, tree_gather_kernel<MT, KS, 8>, g3, b3, 0, st, a, nt, tiles);
+        if (rd <= 16) return launch(kKindScoreRefine, tree_gather_kernel<MT, KS, 16>, g3, b3, 0, st, a, nt, tiles);
+        return launch(kKindScoreRefine, tree_gather_kernel<MT, KS, 32>, g3, b3, 0, st, a, nt, tiles);
+    }
+    const dim3 g2(static_cast<uint32_t>((nq + kTopmWaves - 1) / kTopmWaves)), b2(64 * kTopmWaves);
+    if (rd <= 4) return launch(kKindSelectTree, tree_topm_kernel<4>, g2, b2, 0, st, a, nt);
+    if (rd <= 8) return launch(kKindSelectTree, tree_topm_kernel<8>, g2, b2, 0, st, a, nt);
+    if (rd <= 16) return launch(kKindSelectTree, tree_topm_kernel<16>, g2, b2, 0, st, a, nt);
+    return launch(kKindSelectTree, tree_topm_kernel<32>, g2, b2, 0, st, a, nt);
 }
 
 template <int MT>
-hipError_t launch_top_mt(const TreeTopArgs &a, hipStream_t st) {
-    return a.d == 64 ? launch_top_ks<MT, 2>(a, st) : launch_top_ks<MT, 4>(a, st);
+hipError_t launch_top_mt(const TreeTopArgs &a, hipStream_t st, bool *scored) {
+    return a.d == 64 ? launch_top_ks<MT, 2>(a, st, scored) : launch_top_ks<MT, 4>(a, st, scored);
 }
 
 }  // namespace
@@ -268,10 +473,10 @@ bool tree_top_supported(int d, int64_t L, int B, int G, int W) {
            static_cast<int64_t>(W) * G <= kTopMaxRows;
 }
 
-hipError_t launch_tree_top(const TreeTopArgs &a, hipStream_t st) {
-    if (a.H <= 16) return launch_top_mt<1>(a, st);
-    if (a.H <= 32) return launch_top_mt<2>(a, st);
-    return launch_top_mt<4>(a, st);
+hipError_t launch_tree_top(const TreeTopArgs &a, hipStream_t st, bool *scored) {
+    if (a.H <= 16) return launch_top_mt<1>(a, st, scored);
+    if (a.H <= 32) return launch_top_mt<2>(a, st, scored);
+    return launch_top_mt<4>(a, st, scored);
 }
 
 }  // namespace hisa

@@ -317,6 +317,10 @@ TREE_CASES = [
     ("G256_long_super", 1, 40000, 4, 16, 64, 16, 256, 3, 40, 256, "clustered", True, "mean"),
     ("max_pool_G16", 2, 20000, 4, 64, 128, 128, 16, 2, 12, 600, "clustered", True, "max"),
     ("many_queries_G32", 1, 30000, 64, 16, 64, 64, 32, 4, 10, 200, "gaussian", False, "mean"),
+    # the upper levels' block slices: 288 candidate blocks over 3 workgroups of 96 per query
+    ("ragged_slices_G32", 2, 50000, 2, 16, 64, 64, 32, 9, 12, 300, "gaussian", True, "mean"),
+    # 300 queries: 2 slices of 512 blocks each (few workgroups per query for large batches)
+    ("sliced_batch_G64", 1, 140000, 300, 16, 64, 128, 64, 16, 20, 256, "clustered", True, "mean"),
     # more than 2048 super-blocks: the levels run as separate score / select launches
     ("general_2500_super", 1, 40000, 4, 16, 64, 16, 1, 8, 30, 256, "gaussian", True, "mean"),
     # more than 32768 candidate blocks at level 2 and tokens at level 3: chunked selection
