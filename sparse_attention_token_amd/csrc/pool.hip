@@ -184,6 +184,60 @@ __global__ __launch_bounds__(kParThreads) void pool_append_par_kernel(
     if (tid < D) own.template combine<MAX>(src, rows, tid, sc, nullptr, pool + s * pool_seq_stride + b * D);
 }
 
+// grid: (S).  tree_append_one_kernel's work with block b's mean spread over
+// all kParThreads threads (OwnRowsPar: the bits of the row-order mean) for
+// B*D <= kFusedOwnElems; threads c < D then pool the super-block column c as
+// that kernel does, the first round of children loaded with the block's rows.
+// At 4 sequences of 1M keys: 8.6 us with one thread per column (two
+// dependent memory round trips after a long load queue per thread), 4.8 us
+// spread.
+template <int D, bool MAX>
+__global__ __launch_bounds__(kParThreads) void tree_append_par_kernel(
+        const uint16_t *__restrict__ K, int64_t k_seq_stride, int B, int G, int64_t b, int64_t L_new,
+        uint16_t *__restrict__ pool, int64_t pool_seq_stride, uint16_t *__restrict__ spool,
+        int64_t spool_seq_stride) {
+    using Own = OwnRowsPar<D, kParThreads>;
+    __shared__ __attribute__((aligned(16))) typename Own::Scratch sc;
+    __shared__ uint16_t s_rep[D];
+    constexpr int kChildRound = 64;
+    const int s = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t r0 = b * B;
+    const int rows = static_cast<int>(((r0 + B < L_new) ? r0 + B : L_new) - r0);
+    const uint16_t *src = K + s * k_seq_stride + r0 * D;
+    Own own;
+    own.load(src, rows, tid);
+    // the complete children b0 .. b-1 of column c = tid (threads c < D, whole
+    // waves), the first round in flight with the rows; reads past the last
+    // child re-read child b0 and are not added
+    const int64_t b0 = b / G * G;
+    const int nchild = static_cast<int>(b - b0);
+    const uint16_t *pcol = pool + s * pool_seq_stride + b0 * D + (tid & (D - 1));
+    uint16_t y[kChildRound];
+    if (tid < D) {
+#pragma unroll
+        for (int j = 0; j < kChildRound; ++j) y[j] = pcol[(j < nchild ? j : 0) * D];
+    }
+    own.template partial<MAX>(rows, tid, sc);
+    __syncthreads();
+    if (tid < D) {
+        SuperRep<MAX> sup;
+#pragma unroll
+        for (int j = 0; j < kChildRound; ++j)
+            if (j < nchild) sup.add(y[j], B);
+        for (int c0 = kChildRound; c0 < nchild; c0 += kChildRound) {
+#pragma unroll
+            for (int j = 0; j < kChildRound; ++j) y[j] = pcol[(c0 + j < nchild ? c0 + j : 0) * D];
+#pragma unroll
+            for (int j = 0; j < kChildRound; ++j)
+                if (c0 + j < nchild) sup.add(y[j], B);
+        }
+        own.template combine<MAX>(src, rows, tid, sc, s_rep, pool + s * pool_seq_stride + b * D);
+        sup.add(s_rep[tid], rows);                      // written by this thread
+        spool[s * spool_seq_stride + (b / G) * D + tid] = sup.get();
+    }
+}
+
 // grid: (S).  Both levels of the three-level tree when the new rows all lie
 // in block b (B <= kDirectRows, b the cache's last block): block b is
 // recomputed as in pool_append_direct_kernel, then its super-block u = b / G,
@@ -456,6 +510,18 @@ bool tree_append_one_supported(int B) { return B <= kDirectRows; }
 hipError_t launch_tree_append_one(const uint16_t *K, int64_t k_seq_stride, int S, int d, int B, int G, int64_t blk,
                                   int64_t L_new, bool pool_max, uint16_t *pool, int64_t pool_seq_stride,
                                   uint16_t *spool, int64_t spool_seq_stride, hipStream_t st) {
+    if ((d == 64 || d == 128) && static_cast<int64_t>(B) * d <= kFusedOwnElems) {
+        const dim3 g(S), blk_(kParThreads);
+        if (d == 64)
+            return pool_max ? launch(kKindPoolAppend, tree_append_par_kernel<64, true>, g, blk_, 0, st, K, k_seq_stride,
+                                     B, G, blk, L_new, pool, pool_seq_stride, spool, spool_seq_stride)
+                            : launch(kKindPoolAppend, tree_append_par_kernel<64, false>, g, blk_, 0, st, K,
+                                     k_seq_stride, B, G, blk, L_new, pool, pool_seq_stride, spool, spool_seq_stride);
+        return pool_max ? launch(kKindPoolAppend, tree_append_par_kernel<128, true>, g, blk_, 0, st, K, k_seq_stride, B,
+                                 G, blk, L_new, pool, pool_seq_stride, spool, spool_seq_stride)
+                        : launch(kKindPoolAppend, tree_append_par_kernel<128, false>, g, blk_, 0, st, K, k_seq_stride,
+                                 B, G, blk, L_new, pool, pool_seq_stride, spool, spool_seq_stride);
+    }
     if (pool_max)
         return launch(kKindPoolAppend, tree_append_one_kernel<true>, dim3(S), dim3(kMaxD), 0, st, K, k_seq_stride, d,
                       B, G, blk, L_new, pool, pool_seq_stride, spool, spool_seq_stride);
