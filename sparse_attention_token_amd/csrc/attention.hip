@@ -308,7 +308,10 @@ __global__ __launch_bounds__(kAttnThreads, HT == 2 ? 2 : 1) void sparse_attn_ker
 }
 
 // grid: (S*T*Ha), Dv/4 threads: merges the nsplit partials of one (query, head).
-// The splits are read 8 at a time with every load issued before the sums.
+// Every load is issued before any value is used, 8 splits at a time (a load
+// under a test of an earlier one waits for it).  Up to 8 splits everything is
+// read in one round; beyond, the maxima first, then the weighted sums, in the
+// same split order either way.
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
     constexpr int U = 8;
     const int qh = blockIdx.x;                      // query * Ha + head
@@ -317,32 +320,50 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
     if (c >= a.Dv) return;
     const int64_t row0 = static_cast<int64_t>(qi) * a.nsplit * a.Ha + head;    // split sp at row0 + sp*Ha
     float M = -__builtin_huge_valf();
-    for (int sp = 0; sp < a.nsplit; ++sp) {
-        const int64_t prow = row0 + static_cast<int64_t>(sp) * a.Ha;
-        if (a.part_l[prow] > 0.0f) M = fmaxf(M, a.part_m[prow]);
-    }
     f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
     float lsum = 0.0f;
-    if (M != -__builtin_huge_valf()) {
-        for (int sp0 = 0; sp0 < a.nsplit; sp0 += U) {
-            f32x4 po[U];
-            float wl[U], ll[U];
+    // splits sp0 .. sp0+U-1: partial rows (when `rows`), weights and maxima;
+    // splits past nsplit re-read split sp0 and get weight 0
+    auto load = [&](int sp0, bool rows, f32x4 (&po)[U], float (&wl)[U], float (&ll)[U]) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int sp = sp0 + u < a.nsplit ? sp0 + u : sp0;
-                const int64_t prow = row0 + static_cast<int64_t>(sp) * a.Ha;
-                po[u] = *reinterpret_cast<const f32x4 *>(a.part_o + prow * a.Dv + c);
-                ll[u] = sp0 + u < a.nsplit ? a.part_l[prow] : 0.0f;
-                wl[u] = a.part_m[prow];
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (!(ll[u] > 0.0f)) continue;
-                const float wgt = __builtin_amdgcn_exp2f(wl[u] - M);
-                lsum += wgt * ll[u];
-                o += wgt * po[u];
-            }
+        for (int u = 0; u < U; ++u) {
+            const int sp = sp0 + u < a.nsplit ? sp0 + u : sp0;
+            const int64_t prow = row0 + static_cast<int64_t>(sp) * a.Ha;
+            if (rows) po[u] = *reinterpret_cast<const f32x4 *>(a.part_o + prow * a.Dv + c);
+            const float l = a.part_l[prow];
+            ll[u] = sp0 + u < a.nsplit ? l : 0.0f;
+            wl[u] = a.part_m[prow];
         }
+    };
+    auto accumulate = [&](const f32x4 (&po)[U], const float (&wl)[U], const float (&ll)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (!(ll[u] > 0.0f)) continue;
+            const float wgt = __builtin_amdgcn_exp2f(wl[u] - M);
+            lsum += wgt * ll[u];
+            o += wgt * po[u];
+        }
+    };
+    f32x4 po[U];
+    float wl[U], ll[U];
+    if (a.nsplit <= U) {
+        load(0, true, po, wl, ll);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (ll[u] > 0.0f) M = fmaxf(M, wl[u]);
+        if (M != -__builtin_huge_valf()) accumulate(po, wl, ll);
+    } else {
+        for (int sp0 = 0; sp0 < a.nsplit; sp0 += U) {
+            load(sp0, false, po, wl, ll);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ll[u] > 0.0f) M = fmaxf(M, wl[u]);
+        }
+        if (M != -__builtin_huge_valf())
+            for (int sp0 = 0; sp0 < a.nsplit; sp0 += U) {
+                load(sp0, true, po, wl, ll);
+                accumulate(po, wl, ll);
+            }
     }
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
     *reinterpret_cast<f32x4 *>(a.out + static_cast<int64_t>(qh) * a.Dv + c) = o * inv;
