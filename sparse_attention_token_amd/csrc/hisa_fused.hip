@@ -155,7 +155,8 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
     if (!own_in_pool) own.load(own_src, own_rows, tid);   // own-block rows: in flight with the pool tiles
     QStager<MT, KS, NT> qst;
     qst.load(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, tid);
-    const float wq = a.w[static_cast<int64_t>(qi) * a.H + (tid < a.H ? tid : a.H - 1)];
+    const float wq = a.w[static_cast<int64_t>(qi) * a.H + (lane < a.H ? lane : a.H - 1)];
+    pin_loaded(wq);                     // issued with q, not behind the wait for it
     qst.store(L.q, a.H, tid);
     if (tid < 64) L.w[tid] = tid < a.H ? wq : 0.0f;
     if (!own_in_pool) {
@@ -372,11 +373,15 @@ __global__ __launch_bounds__(DT) void hisa_decode_kernel(FusedArgs a) {
     for (int nt = 0; nt < NTW; ++nt) {
         const int p = tile0 + (wave * NTW + nt) * 16 + n;
         const int pc = p < npos ? p : npos - 1;         // npos >= 1: tile0 < npos
-        const int slot = pc / a.B;
-        const int64_t tok = static_cast<int64_t>(s_sel[slot]) * a.B + (pc - slot * a.B);
+        const int slot = pc >> __builtin_ctz(a.B);      // B is a power of two
+        const int64_t tok = static_cast<int64_t>(s_sel[slot]) * a.B + (pc & (a.B - 1));
         valid[nt] = p < npos && tok <= t;
         load_row_frag_any<KS>(kb[nt], a.K + s * a.k_seq_stride + (tok <= t ? tok : t) * D, lane);
     }
+    // every row load is issued before the first MFMA: left to itself the
+    // scheduler issued five of the eight, waited for the first and issued the
+    // rest between MFMAs, one more memory round trip for those three
+    __builtin_amdgcn_sched_barrier(0);
     float v[NTW];
     score_tiles_frag<MT, KS, NTW>(f, kb, v);
     uint32_t *cand = a.cand_keys + static_cast<int64_t>(qi) * a.cand_stride;
@@ -434,6 +439,7 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs 
         QStager<MT, KS, kDecodeThreads> qst;
         qst.load(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, tid);
         const float wq = a.w[static_cast<int64_t>(qi) * a.H + (tid < a.H ? tid : a.H - 1)];
+        pin_loaded(wq);
         qst.store(L.q, a.H, tid);
         if (tid < 64) L.w[tid] = tid < a.H ? wq : 0.0f;
         __syncthreads();
@@ -463,6 +469,7 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs 
     qst.load(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, tid);
     const float wq0 = a.w[static_cast<int64_t>(qi) * a.H + (tid < a.H ? tid : a.H - 1)];   // unconditional load
     const float wq = tid < a.H ? wq0 : 0.0f;
+    pin_loaded(wq0);
     qst.store(L.q, a.H, tid);
     if (tid < 64) L.w[tid] = wq;
     if (a.pool_max)
@@ -568,6 +575,7 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs 
         else ke = dgather_topm<32>(keys, nb, a.m, lane, s_win, emit);
         if (lane == 0) s_keff = ke;
     }
+    pin_loaded(wq0);
     qst.store(s_q, a.H, tid);
     if (tid < 64) s_w[tid] = wq;
     __syncthreads();
@@ -583,11 +591,12 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs 
     for (int nt = 0; nt < NTW; ++nt) {
         const int p = tile0 + (wave * NTW + nt) * 16 + n;
         const int pc = p < npos ? p : npos - 1;         // npos >= 1: tile0 < npos
-        const int slot = pc / a.B;
-        const int64_t tok = static_cast<int64_t>(s_sel[slot]) * a.B + (pc - slot * a.B);
+        const int slot = pc >> __builtin_ctz(a.B);      // B is a power of two
+        const int64_t tok = static_cast<int64_t>(s_sel[slot]) * a.B + (pc & (a.B - 1));
         valid[nt] = p < npos && tok <= t;
         load_row_frag_any<KS>(kb[nt], a.K + s * a.k_seq_stride + (tok <= t ? tok : t) * D, lane);
     }
+    __builtin_amdgcn_sched_barrier(0);                  // every row load in flight before the MFMAs
     QFrag<MT, KS> f;
     load_qfrag_lds_w<MT, KS>(f, s_q, s_w, lane);
     float v[NTW];
@@ -626,8 +635,8 @@ __global__ __launch_bounds__(kK2Threads) void hisa_refine_kernel(FusedArgs a) {
     for (int nt = 0; nt < 2; ++nt) {
         const int p = tile0 + wave * 32 + nt * 16 + n;
         const int pc = p < npos ? p : npos - 1;         // npos >= 1: tile0 < npos
-        const int slot = pc / a.B;
-        const int64_t tok = static_cast<int64_t>(selq[slot]) * a.B + (pc - slot * a.B);
+        const int slot = pc >> __builtin_ctz(a.B);      // B is a power of two
+        const int64_t tok = static_cast<int64_t>(selq[slot]) * a.B + (pc & (a.B - 1));
         valid[nt] = p < npos && tok <= t;
         load_row_frag_any<KS>(kb[nt], a.K + s * a.k_seq_stride + (tok <= t ? tok : t) * D, lane);
     }

@@ -194,7 +194,8 @@ __global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a, in
     uint16_t *s_own = reinterpret_cast<uint16_t *>(L.own);
     QStager<MT, KS, kTopThreads> qst;           // q and w loads in flight with the rows'
     qst.load(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, tid);
-    const float wq = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
+    const float wq0 = a.w[static_cast<int64_t>(qi) * a.H + (tid < a.H ? tid : a.H - 1)];   // unconditional load
+    const float wq = tid < a.H ? wq0 : 0.0f;
     if (!own_from_pool) {
         constexpr int kPer = (kFusedOwnElems / 8 + kTopThreads - 1) / kTopThreads;
         const int chunks = own_rows * D / 8;
@@ -208,6 +209,7 @@ __global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a, in
         for (int i = 0; i < kPer; ++i)
             if (tid + i * kTopThreads < chunks) dst[tid + i * kTopThreads] = v[i];
     }
+    pin_loaded(wq0);
     qst.store(L.q, a.H, tid);
     if (tid < 64) L.w[tid] = wq;
     __syncthreads();
@@ -392,6 +394,7 @@ __global__ __launch_bounds__(kTreeGatherThreads) void tree_gather_kernel(TreeTop
         });
         if (lane == 0) s_keff = ke;
     }
+    pin_loaded(wq0);
     qst.store(s_q, a.H, tid);
     if (tid < 64) s_w[tid] = wq;
     __syncthreads();

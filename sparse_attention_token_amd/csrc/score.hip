@@ -179,8 +179,12 @@ __global__ __launch_bounds__(kFlatThreads) void score_flat_kernel(ScoreArgs a, i
 
     bf16x8 ka[kNT][KS], kc[kNT][KS];
     flat_load<MT, KS>(ka, Ks, wbase, row1, lane);           // first rows in flight before q
-    stage_query<MT, KS, kFlatThreads>(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, s_q, tid);
-    if (tid < 64) s_w[tid] = tid < a.H ? a.w[static_cast<int64_t>(qi) * a.H + tid] : 0.0f;
+    QStager<MT, KS, kFlatThreads> qst;
+    qst.load(a.q + static_cast<int64_t>(qi) * a.H * D, a.H, tid);
+    const float wq = a.w[static_cast<int64_t>(qi) * a.H + (tid < a.H ? tid : a.H - 1)];   // unconditional load
+    pin_loaded(wq);
+    qst.store(s_q, a.H, tid);
+    if (tid < 64) s_w[tid] = tid < a.H ? wq : 0.0f;
     __syncthreads();
     QFrag<MT, KS> f;
     load_qfrag_lds_w<MT, KS>(f, s_q, s_w, lane);

@@ -29,6 +29,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Marks x as consumed by every lane at this point.  A value loaded by all
+// threads but used only under a branch (a head weight stored to LDS by
+// tid < 64) has its load sunk into that branch by the compiler, behind the
+// wait for every load issued earlier: one more memory round trip, which the
+// next barrier hands on to every wave.  Pinned where those loads are awaited
+// anyway, the load issues with them.
+__device__ __forceinline__ void pin_loaded(float x) { asm volatile("" ::"v"(x)); }
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
     return as_bf16x8(*reinterpret_cast<const u32x4 *>(p));
 }
