@@ -93,12 +93,20 @@ __device__ __forceinline__ void load_run(const uint32_t *__restrict__ keys, int6
 // threads each) 94 -> 66.5 us; decode 128K 9.5 -> 9.25 us; decode 32K
 // unchanged.
 constexpr int kStageOut = 2048;
+// A kept entry staged in LDS: (id, key) in one 64-bit word, one LDS write per
+// kept key (two 32-bit writes before: decode top k's emit 2,270 cycles).
+typedef uint32_t stage_u32x2 __attribute__((ext_vector_type(2)));
+// Workgroups of 1024 threads count the first digit into four histogram
+// copies (block_radix_select's NC): decode top k's first pass 2,430 cycles.
+template <int NT>
+constexpr int kFirstCopies = NT == 1024 ? 4 : 1;
 
 template <int MODE, int R, int NT, bool STAGE>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     __shared__ __attribute__((aligned(16))) SelectScratch sc;
     __shared__ int32_t s_sel[kSelMaxM];
-    __shared__ uint32_t s_out[STAGE ? 2 * kStageOut : 1];      // ids, then keys
+    __shared__ stage_u32x2 s_out[STAGE ? kStageOut : 1];       // (id, key) by output slot
+    __shared__ __attribute__((aligned(16))) uint32_t s_h0[kFirstCopies<NT> > 1 ? kFirstCopies<NT> * kCopyStride : 4];
     const int tid = threadIdx.x;
     const int qi = blockIdx.x;
     const int64_t n = row_length<MODE>(a, qi);
@@ -113,26 +121,20 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         for (int j = tid; j < meff; j += NT) s_sel[j] = a.sel_blk[static_cast<int64_t>(qi) * a.m + j];
         // block_radix_select starts with a barrier, which also publishes s_sel
     }
-    const SelectResult res = block_radix_select<NT, R>(kv, static_cast<uint32_t>(a.kout), sc);
+    const SelectResult res = block_radix_select<NT, R, kFirstCopies<NT>>(kv, static_cast<uint32_t>(a.kout), sc, s_h0);
     if (res.keff > 0) {
         // mapped modes: R and the group size are powers of two, so with
         // R <= grp the thread's R positions lie in one slot and one lookup
         // serves them all; with R > grp each position looks up its slot
         const bool per_pos = kMapped<MODE> && R > grp;
+        const int lg = __builtin_ctz(static_cast<unsigned>(grp));      // grp is a power of two
         int32_t id0 = tid * R;
-        if (kMapped<MODE> && !per_pos && id0 < n) {
-            const int slot = id0 / grp;
-            id0 = s_sel[slot] * grp + (id0 - slot * grp);
-        }
+        if (kMapped<MODE> && !per_pos && id0 < n) id0 = s_sel[id0 >> lg] * grp + (id0 & (grp - 1));
         block_compact<NT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
             int32_t id = id0 + r;
-            if (per_pos) {
-                const int slot = id / grp;
-                id = s_sel[slot] * grp + (id - slot * grp);
-            }
+            if (per_pos) id = s_sel[id >> lg] * grp + (id & (grp - 1));
             if (STAGE) {
-                s_out[op] = static_cast<uint32_t>(id);
-                s_out[kStageOut + op] = key;
+                s_out[op] = stage_u32x2{static_cast<uint32_t>(id), key};
             } else {
                 put(out, op, id);
                 if (osc) put(osc, op, key_to_score(key));
@@ -144,9 +146,10 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         __syncthreads();
         for (int j = tid; j < a.kout; j += NT) {
             const bool kept = j < static_cast<int>(res.keff);
-            const int32_t id = kept ? static_cast<int32_t>(s_out[j]) : -1;
+            const stage_u32x2 e = s_out[kept ? j : 0];
+            const int32_t id = kept ? static_cast<int32_t>(e[0]) : -1;
             out[j] = id;
-            if (osc) osc[j] = kept ? key_to_score(s_out[kStageOut + j]) : -__builtin_huge_valf();
+            if (osc) osc[j] = kept ? key_to_score(e[1]) : -__builtin_huge_valf();
             if (out2) out2[j] = id;
         }
         return;
@@ -168,7 +171,8 @@ __global__ __launch_bounds__(kNT) void select_chunk_kernel(SelectArgs a, const u
                                                            int64_t n_fixed, uint32_t *keys_out,
                                                            int32_t *ids_out, int64_t out_stride) {
     __shared__ __attribute__((aligned(16))) SelectScratch sc;
-    __shared__ uint32_t s_out[2 * kStageOut];       // ids, then keys
+    __shared__ stage_u32x2 s_out[kStageOut];        // (id, key) by output slot
+    __shared__ __attribute__((aligned(16))) uint32_t s_h0[kFirstCopies<kNT> * kCopyStride];
     constexpr int R = 32;
     const int tid = threadIdx.x;
     const int qi = blockIdx.y;
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(kNT) void select_chunk_kernel(SelectArgs a, const u
     uint32_t *ko = keys_out + static_cast<int64_t>(qi) * out_stride + static_cast<int64_t>(blockIdx.x) * a.kout;
     int32_t *io = ids_out + static_cast<int64_t>(qi) * out_stride + static_cast<int64_t>(blockIdx.x) * a.kout;
     const bool stage = a.kout <= kStageOut;          // staged output, as in select_kernel
-    const SelectResult res = block_radix_select<kNT, R>(kv, static_cast<uint32_t>(a.kout), sc);
+    const SelectResult res = block_radix_select<kNT, R, kFirstCopies<kNT>>(kv, static_cast<uint32_t>(a.kout), sc, s_h0);
     if (res.keff > 0) {
         const int32_t *irow = ids_in ? ids_in + static_cast<int64_t>(qi) * in_stride + c0 : nullptr;
         // position ids in the mapped modes: with R <= grp (both powers of
@@ -193,8 +197,8 @@ __global__ __launch_bounds__(kNT) void select_chunk_kernel(SelectArgs a, const u
         const bool per_pos = !irow && kMapped<MODE> && R > grp;
         int32_t id0 = static_cast<int32_t>(p0);
         if (!irow && kMapped<MODE> && !per_pos && p0 < n_row) {
-            const int64_t slot = p0 / grp;
-            id0 = static_cast<int32_t>(static_cast<int64_t>(sb[slot]) * grp + (p0 - slot * grp));
+            const int64_t slot = p0 >> __builtin_ctz(static_cast<unsigned>(grp));   // grp is a power of two
+            id0 = static_cast<int32_t>(static_cast<int64_t>(sb[slot]) * grp + (p0 & (grp - 1)));
         }
         block_compact<kNT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
             int32_t id;
@@ -202,14 +206,13 @@ __global__ __launch_bounds__(kNT) void select_chunk_kernel(SelectArgs a, const u
                 id = irow[static_cast<int64_t>(tid) * R + r];
             } else if (per_pos) {
                 const int64_t pos = p0 + r;
-                const int64_t slot = pos / grp;
-                id = static_cast<int32_t>(static_cast<int64_t>(sb[slot]) * grp + (pos - slot * grp));
+                const int64_t slot = pos >> __builtin_ctz(static_cast<unsigned>(grp));
+                id = static_cast<int32_t>(static_cast<int64_t>(sb[slot]) * grp + (pos & (grp - 1)));
             } else {
                 id = id0 + r;
             }
             if (stage) {
-                s_out[op] = static_cast<uint32_t>(id);
-                s_out[kStageOut + op] = key;
+                s_out[op] = stage_u32x2{static_cast<uint32_t>(id), key};
             } else {
                 put(ko, op, key);
                 put(io, op, id);
@@ -220,8 +223,9 @@ __global__ __launch_bounds__(kNT) void select_chunk_kernel(SelectArgs a, const u
         __syncthreads();
         for (int j = tid; j < a.kout; j += kNT) {
             const bool kept = j < static_cast<int>(res.keff);
-            ko[j] = kept ? s_out[kStageOut + j] : kNoCandidate;
-            io[j] = kept ? static_cast<int32_t>(s_out[j]) : -1;
+            const stage_u32x2 e = s_out[kept ? j : 0];
+            ko[j] = kept ? e[1] : kNoCandidate;
+            io[j] = kept ? static_cast<int32_t>(e[0]) : -1;
         }
         return;
     }
@@ -236,7 +240,8 @@ __global__ __launch_bounds__(kNT) void select_final_kernel(SelectArgs a, const u
                                                            const int32_t *ids_in, int64_t in_stride,
                                                            int64_t n) {
     __shared__ __attribute__((aligned(16))) SelectScratch sc;
-    __shared__ uint32_t s_out[2 * kStageOut];       // ids, then keys
+    __shared__ stage_u32x2 s_out[kStageOut];        // (id, key) by output slot
+    __shared__ __attribute__((aligned(16))) uint32_t s_h0[kFirstCopies<kNT> * kCopyStride];
     constexpr int R = 32;
     const int tid = threadIdx.x;
     const int qi = blockIdx.x;
@@ -247,13 +252,12 @@ __global__ __launch_bounds__(kNT) void select_final_kernel(SelectArgs a, const u
     int32_t *out2 = a.out_id_copy ? a.out_id_copy + static_cast<int64_t>(qi) * a.kout : nullptr;
     const int32_t *irow = ids_in + static_cast<int64_t>(qi) * in_stride;
     const bool stage = a.kout <= kStageOut;          // staged output, as in select_kernel
-    const SelectResult res = block_radix_select<kNT, R>(kv, static_cast<uint32_t>(a.kout), sc);
+    const SelectResult res = block_radix_select<kNT, R, kFirstCopies<kNT>>(kv, static_cast<uint32_t>(a.kout), sc, s_h0);
     if (res.keff > 0) {
         block_compact<kNT, R>(kv, res, sc, [&](uint32_t op, int r, uint32_t key) {
             const int32_t id = irow[tid * R + r];
             if (stage) {
-                s_out[op] = static_cast<uint32_t>(id);
-                s_out[kStageOut + op] = key;
+                s_out[op] = stage_u32x2{static_cast<uint32_t>(id), key};
             } else {
                 put(out, op, id);
                 if (osc) put(osc, op, key_to_score(key));
@@ -265,9 +269,10 @@ __global__ __launch_bounds__(kNT) void select_final_kernel(SelectArgs a, const u
         __syncthreads();
         for (int j = tid; j < a.kout; j += kNT) {
             const bool kept = j < static_cast<int>(res.keff);
-            const int32_t id = kept ? static_cast<int32_t>(s_out[j]) : -1;
+            const stage_u32x2 e = s_out[kept ? j : 0];
+            const int32_t id = kept ? static_cast<int32_t>(e[0]) : -1;
             out[j] = id;
-            if (osc) osc[j] = kept ? key_to_score(s_out[kStageOut + j]) : -__builtin_huge_valf();
+            if (osc) osc[j] = kept ? key_to_score(e[1]) : -__builtin_huge_valf();
             if (out2) out2[j] = id;
         }
         return;

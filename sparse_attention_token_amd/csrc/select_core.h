@@ -84,12 +84,24 @@ struct SelectResult {
     uint32_t keff;       // number of kept keys
 };
 
-template <int NT, int R>
+// The first digit's histogram in NC copies (NC = 1, 2 or 4), lane l adding
+// into copy l % NC: the top 11 bits of clustered scores fall into a handful
+// of bins, and LDS atomics of one wave to one address serialize, so spreading
+// a bin over NC addresses (in different banks: copies kCopyStride words
+// apart) divides that wait by up to NC.  h0 holds NC * kCopyStride words
+// (unused when NC = 1: sc.hist serves).
+constexpr int kCopyStride = kCoreBins0 + 16;
+
+template <int NT, int R, int NC = 1>
 __device__ __forceinline__ SelectResult block_radix_select(const uint32_t (&kv)[R], uint32_t kout,
-                                                           SelectScratch &sc) {
+                                                           SelectScratch &sc, uint32_t *h0 = nullptr) {
+    static_assert(NC == 1 || NC == 2 || NC == 4, "histogram copies");
     const int tid = threadIdx.x;
     for (int b = tid * 4; b < kCoreBins0 + kCoreBins1 + kCoreBins2; b += NT * 4)
         *reinterpret_cast<sel_u32x4 *>(&sc.hist[b]) = sel_u32x4{0u, 0u, 0u, 0u};
+    if (NC > 1)
+        for (int b = tid * 4; b < NC * kCopyStride; b += NT * 4)
+            *reinterpret_cast<sel_u32x4 *>(&h0[b]) = sel_u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
     uint32_t prefix = 0, mask = 0, need = 0, keff = 0;
 #pragma unroll
@@ -98,11 +110,14 @@ __device__ __forceinline__ SelectResult block_radix_select(const uint32_t (&kv)[
         constexpr int kNB[3] = {kCoreBins0, kCoreBins1, kCoreBins2};
         const int nb = kNB[pass];
         uint32_t *h = sc.hist + (pass == 0 ? 0 : (pass == 1 ? kCoreBins0 : kCoreBins0 + kCoreBins1));
+        const int ncp = pass == 0 ? NC : 1;                // histogram copies of this pass
+        if (pass == 0 && NC > 1) h = h0;
+        uint32_t *ha = ncp > 1 ? h + (threadIdx.x & (ncp - 1)) * kCopyStride : h;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint32_t key = kv[r];
             if (key != kNoCandidate && (key & mask) == prefix)
-                atomicAdd(&h[(key >> shift) & static_cast<uint32_t>(nb - 1)], 1u);
+                atomicAdd(&ha[(key >> shift) & static_cast<uint32_t>(nb - 1)], 1u);
         }
         __syncthreads();
         // thread t owns bins [nb - (t+1)*bpt, nb - t*bpt): descending ownership
@@ -110,17 +125,23 @@ __device__ __forceinline__ SelectResult block_radix_select(const uint32_t (&kv)[
         const int b0 = nb - (tid + 1) * bpt;
         uint32_t hb[8];
         uint32_t c = 0;
-        if (bpt >= 4) {
 #pragma unroll
-            for (int v = 0; v < 2; ++v) {
-                if (v * 4 < bpt) {
-                    const sel_u32x4 x = *reinterpret_cast<const sel_u32x4 *>(&h[b0 + 4 * v]);
-                    hb[4 * v + 0] = x[0]; hb[4 * v + 1] = x[1]; hb[4 * v + 2] = x[2]; hb[4 * v + 3] = x[3];
+        for (int j = 0; j < 8; ++j) hb[j] = 0u;
+#pragma unroll
+        for (int cp = 0; cp < (pass == 0 ? NC : 1); ++cp) {   // a bin's count: the sum over its copies
+            const uint32_t *hc = h + cp * kCopyStride;
+            if (bpt >= 4) {
+#pragma unroll
+                for (int v = 0; v < 2; ++v) {
+                    if (v * 4 < bpt) {
+                        const sel_u32x4 x = *reinterpret_cast<const sel_u32x4 *>(&hc[b0 + 4 * v]);
+                        hb[4 * v + 0] += x[0]; hb[4 * v + 1] += x[1]; hb[4 * v + 2] += x[2]; hb[4 * v + 3] += x[3];
+                    }
                 }
-            }
-        } else {
+            } else {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) hb[j] = j < bpt ? h[b0 + j] : 0u;
+                for (int j = 0; j < 2; ++j) hb[j] += j < bpt ? hc[b0 + j] : 0u;
+            }
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) c += j < bpt ? hb[j] : 0u;
@@ -164,6 +185,10 @@ __device__ __forceinline__ SelectResult block_radix_select(const uint32_t (&kv)[
         // >= prefix (low bits still open), i.e. the keys > prefix - 1, with
         // none kept at equality -- no further pass needed
         if (pass < 2 && need == in_bin) return SelectResult{prefix == 0u ? 0u : prefix - 1u, 0u, keff};
+        // all 32 bits resolved: the bin holds the keys equal to K*; when every
+        // one of them is kept the kept set is the keys > K* - 1 (K* >= 1: key 0
+        // is no candidate), the form whose compaction needs no tie counts
+        if (pass == 2 && need == in_bin) return SelectResult{prefix - 1u, 0u, keff};
     }
     return SelectResult{prefix, need, keff};
 }
@@ -193,6 +218,24 @@ __device__ __forceinline__ void emit_kept(const uint32_t (&kv)[R], const SelectR
 template <int NT, int R, typename Emit>
 __device__ __forceinline__ void block_compact(const uint32_t (&kv)[R], const SelectResult &res,
                                               SelectScratch &sc, Emit &&emit) {
+    if (res.need_eq == 0) {
+        // no key equal to K* is kept (block_radix_select returns every case
+        // without a partial tie in this form): a key is kept iff it is > K*,
+        // at slot = kept keys before it -- one compare a key instead of the
+        // (greater, equal) pair below, the same slots
+        uint32_t cg = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) cg += kv[r] > res.kstar;
+        uint32_t total;
+        uint32_t op = block_exclusive<NT>(cg, total, sc);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t key = kv[r];
+            if (key > res.kstar && op < res.keff) emit(op, r, key);   // op < keff always holds; guards the write
+            op += key > res.kstar;
+        }
+        return;
+    }
     uint32_t cg = 0, ce = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
