@@ -27,9 +27,15 @@ FLAGS = [
 ]
 
 
+# Per-source flags.  select.hip: the dispatcher preloads the first two kernel
+# arguments (the key rows' address and stride) into scalar registers, so the
+# top k's key loads need not wait for the argument block to be read.
+SOURCE_FLAGS = {"select.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
