@@ -30,7 +30,10 @@ FLAGS = [
 # Per-source flags.  select.hip: the dispatcher preloads the first two kernel
 # arguments (the key rows' address and stride) into scalar registers, so the
 # top k's key loads need not wait for the argument block to be read.
-SOURCE_FLAGS = {"select.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"]}
+# Kernels whose first argument is a struct preload nothing.
+# hisa_fused.hip: the one-launch decode kernel's nine leading arguments.
+SOURCE_FLAGS = {"select.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"],
+                "hisa_fused.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=9"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -125,7 +125,7 @@ struct BlockStageLds {
 template <int MT, int KS, int NT, int TB>
 __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, int64_t t,
                                             BlockStageLds<KS, NT> &L, uint32_t *s_keys,
-                                            QFrag<MT, KS> &f, bool writer) {
+                                            QFrag<MT, KS> &f, bool writer, bool pool_out_set) {
     constexpr int D = 32 * KS;
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -134,8 +134,8 @@ __device__ __forceinline__ void block_stage(const FusedArgs &a, int qi, int s, i
     const int nb = static_cast<int>(bt + 1);
     const int64_t r0 = bt * a.B;
     const int own_rows = static_cast<int>(t + 1 - r0);
-    const bool own_in_pool = t == a.L - 1 && a.pool_out == nullptr;
-    const bool write_pool = writer && a.pool_out != nullptr && t == a.L - 1;
+    const bool own_in_pool = t == a.L - 1 && !pool_out_set;
+    const bool write_pool = writer && pool_out_set && t == a.L - 1;
     using Own = OwnRowsPar<D, NT>;
     static_assert(sizeof(typename Own::Scratch) <= sizeof(L.own), "own-block scratch fits the staging words");
     auto &osc = *reinterpret_cast<typename Own::Scratch *>(L.own);
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kK1Threads) void hisa_blocks_topm_kernel(FusedArgs 
     }
     const int nb = static_cast<int>(t / a.B + 1);
     QFrag<MT, KS> f;
-    block_stage<MT, KS, kK1Threads, 1>(a, qi, s, t, L, s_keys, f, true);
+    block_stage<MT, KS, kK1Threads, 1>(a, qi, s, t, L, s_keys, f, true, a.pool_out != nullptr);
 
     uint32_t keff;
     if (nb <= kK1WaveMax) {
@@ -312,8 +312,28 @@ __device__ __forceinline__ void decode_tile(int nq, int tiles, int &qi, int &til
 // into LDS, then the workgroup's ROWS candidate rows (ROWS/64 16-row tiles per
 // wave).  Wider workgroups repeat the block stage less often; narrow ones keep
 // every CU busy when there are few queries.
+// Packed decode arguments: pk = T | H << 8 | log2(B) << 16 | queries << 20,
+// pk2 = tiles | m << 12 | (qpos null) << 24 | (pool_out set) << 25.  The
+// leading arguments are everything a workgroup needs before its first loads;
+// this file is built with kernarg preloading, so they arrive in scalar
+// registers with the dispatch, and the loads of the pool tiles, own-block
+// rows, q and w go out without waiting a memory round trip for the argument
+// block (which the rest of FusedArgs still comes from).
 template <int MT, int KS, int ROWS, int DT>
-__global__ __launch_bounds__(DT) void hisa_decode_kernel(FusedArgs a) {
+__global__ __launch_bounds__(DT) void hisa_decode_kernel(const uint16_t *q, const uint16_t *pool, const uint16_t *K,
+                                                         const float *w, int32_t k_seq_stride, int32_t pool_seq_stride,
+                                                         int32_t Lk, uint32_t pk, uint32_t pk2, FusedArgs a_in) {
+    FusedArgs a = a_in;
+    a.q = q; a.pool = pool; a.K = K; a.w = w;
+    a.k_seq_stride = k_seq_stride; a.pool_seq_stride = pool_seq_stride; a.L = Lk;
+    a.T = static_cast<int>(pk & 0xffu);
+    a.H = static_cast<int>((pk >> 8) & 0xffu);
+    a.B = 1 << ((pk >> 16) & 0xfu);
+    a.m = static_cast<int>((pk2 >> 12) & 0xfffu);
+    const int nq_all = static_cast<int>((pk >> 20) & 0xffu);
+    const int ntiles = static_cast<int>(pk2 & 0xfffu);
+    const bool qpos_null = ((pk2 >> 24) & 1u) != 0;
+    const bool pool_out_set = ((pk2 >> 25) & 1u) != 0;
     constexpr int D = 32 * KS;
     constexpr int NTW = ROWS / (16 * DT / 64);
     __shared__ __attribute__((aligned(16))) BlockStageLds<KS, DT> L;
@@ -324,18 +344,22 @@ __global__ __launch_bounds__(DT) void hisa_decode_kernel(FusedArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
     int qi, tile;
-    decode_tile(a.S * a.T, static_cast<int>((static_cast<int64_t>(a.m) * a.B + ROWS - 1) / ROWS), qi, tile);
+    decode_tile(nq_all, ntiles, qi, tile);
     if (qi < 0) return;
     const int s = qi / a.T;
-    const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    int64_t t;
+    if (qpos_null) {
+        t = a.L - a.T + (qi - s * a.T);
+        t = t >= 0 && t < a.L ? t : -1;
+    } else {
+        t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    }
     const bool lead = tile == 0;            // also publishes the kept blocks
-    int32_t *sel = a.sel_blk + static_cast<int64_t>(qi) * a.m;
-    int32_t *ob = a.out_blk ? a.out_blk + static_cast<int64_t>(qi) * a.m : nullptr;
     if (t < 0) {
         if (lead)
             for (int j = tid; j < a.m; j += DT) {
-                sel[j] = -1;
-                if (ob) ob[j] = -1;
+                a.sel_blk[static_cast<int64_t>(qi) * a.m + j] = -1;
+                if (a.out_blk) a.out_blk[static_cast<int64_t>(qi) * a.m + j] = -1;
             }
         return;
     }
@@ -347,7 +371,11 @@ __global__ __launch_bounds__(DT) void hisa_decode_kernel(FusedArgs a) {
     if (tile0 >= npos) return;
 
     QFrag<MT, KS> f;
-    block_stage<MT, KS, DT, DT == 256 ? 4 : 2>(a, qi, s, t, L, s_keys, f, lead);
+    block_stage<MT, KS, DT, DT == 256 ? 4 : 2>(a, qi, s, t, L, s_keys, f, lead, pool_out_set);
+    // output rows from the argument block: formed after the block stage, so
+    // that no wait for it comes before the stage's first loads
+    int32_t *sel = a.sel_blk + static_cast<int64_t>(qi) * a.m;
+    int32_t *ob = a.out_blk ? a.out_blk + static_cast<int64_t>(qi) * a.m : nullptr;
     if (wave == 0) {
         const uint32_t ke = block_topm_wave(s_keys, nb, a.m, L.own, [&](uint32_t op, int pos) {
             s_sel[op] = pos;
@@ -683,7 +711,10 @@ hipError_t launch_fused_ks(const FusedArgs &a, bool decode, hipStream_t st) {
         const int wide = static_cast<int>((mb + kDecodeRowsWide - 1) / kDecodeRowsWide);
         const int narrow = static_cast<int>((mb + kDecodeRowsNarrow - 1) / kDecodeRowsNarrow);
         const bool use_wide = static_cast<int64_t>(wide) * nq >= kDecodeWideMin;
-        if (a.nblk > kDecodeOneKernelMaxBlocks) {
+        // the one-launch kernel takes the sequence strides as 32-bit preloaded
+        // arguments; caches laid out wider take the two-kernel path
+        const bool strides32 = a.k_seq_stride < (int64_t{1} << 31) && a.pool_seq_stride < (int64_t{1} << 31);
+        if (a.nblk > kDecodeOneKernelMaxBlocks || !strides32) {
             // long context: block stage once per query, then the gather
             const int btiles = (a.nblk + kDBlkRows - 1) / kDBlkRows;
             const hipError_t e = launch(kKindScoreBlocks, hisa_dblocks_kernel<MT, KS>,
@@ -701,15 +732,24 @@ hipError_t launch_fused_ks(const FusedArgs &a, bool decode, hipStream_t st) {
         const int tiles = use_wide ? wide : narrow;
         const bool eight = static_cast<int64_t>(tiles) * nq <= kDecodeEightWaveMaxGrid;
         const dim3 grid(static_cast<uint32_t>(decode_grid(nq, tiles)));
+        // the preloaded words: strides below 2^31 elements (above), and
+        // decode_mode() admits only S*T <= 16, H <= 64, m <= 1024 (tiles <= 2048)
+        const uint32_t pk = static_cast<uint32_t>(a.T) | static_cast<uint32_t>(a.H) << 8 |
+                            static_cast<uint32_t>(__builtin_ctz(static_cast<unsigned>(a.B))) << 16 |
+                            static_cast<uint32_t>(nq) << 20;
+        const uint32_t pk2 = static_cast<uint32_t>(tiles) | static_cast<uint32_t>(a.m) << 12 |
+                             (a.qpos == nullptr ? 1u : 0u) << 24 | (a.pool_out != nullptr ? 1u : 0u) << 25;
+        const int32_t kss = static_cast<int32_t>(a.k_seq_stride), pss = static_cast<int32_t>(a.pool_seq_stride);
+        const int32_t Lk = static_cast<int32_t>(a.L);
+        auto go = [&](auto kernel, int threads) {
+            return launch(kKindIndexDecode, kernel, grid, dim3(threads), 0, st, a.q, a.pool, a.K, a.w, kss, pss, Lk,
+                          pk, pk2, a);
+        };
         if (use_wide)
-            return eight ? launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsWide, 512>, grid, dim3(512),
-                                  0, st, a)
-                         : launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsWide, 256>, grid, dim3(256),
-                                  0, st, a);
-        return eight ? launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsNarrow, 512>, grid, dim3(512), 0,
-                              st, a)
-                     : launch(kKindIndexDecode, hisa_decode_kernel<MT, KS, kDecodeRowsNarrow, 256>, grid, dim3(256), 0,
-                              st, a);
+            return eight ? go(hisa_decode_kernel<MT, KS, kDecodeRowsWide, 512>, 512)
+                         : go(hisa_decode_kernel<MT, KS, kDecodeRowsWide, 256>, 256);
+        return eight ? go(hisa_decode_kernel<MT, KS, kDecodeRowsNarrow, 512>, 512)
+                     : go(hisa_decode_kernel<MT, KS, kDecodeRowsNarrow, 256>, 256);
     }
     const hipError_t e = (a.bucket_off && a.nblk <= kBMMaxBlocks)
         ? launch_block_major_blocks(a, st)
