@@ -312,28 +312,48 @@ __device__ __forceinline__ void decode_tile(int nq, int tiles, int &qi, int &til
 // into LDS, then the workgroup's ROWS candidate rows (ROWS/64 16-row tiles per
 // wave).  Wider workgroups repeat the block stage less often; narrow ones keep
 // every CU busy when there are few queries.
-// Packed decode arguments: pk = T | H << 8 | log2(B) << 16 | queries << 20,
-// pk2 = tiles | m << 12 | (qpos null) << 24 | (pool_out set) << 25.  The
-// leading arguments are everything a workgroup needs before its first loads;
-// this file is built with kernarg preloading, so they arrive in scalar
-// registers with the dispatch, and the loads of the pool tiles, own-block
-// rows, q and w go out without waiting a memory round trip for the argument
-// block (which the rest of FusedArgs still comes from).
+// Decode kernels take everything a workgroup needs before its first loads
+// as leading arguments, which this file's build preloads into scalar
+// registers at dispatch: their first loads go out without waiting a memory
+// round trip for the argument block (the rest of FusedArgs still comes from
+// it).  Packed words: pk = T | H << 8 | log2(B) << 16 | queries << 20,
+// pk2 = n2 | m << 12 | (qpos null) << 24 | (pool_out set) << 25, where n2 is
+// the kernel's own count (tiles per query, or pooled means).
+struct DecodeEarly {
+    int nq, n2;
+    bool qpos_null, pool_out_set;
+};
+
+__device__ __forceinline__ DecodeEarly decode_early(FusedArgs &a, const uint16_t *q, const uint16_t *K,
+                                                    const float *w, int32_t k_seq_stride, int32_t Lk, uint32_t pk,
+                                                    uint32_t pk2) {
+    a.q = q; a.K = K; a.w = w; a.k_seq_stride = k_seq_stride; a.L = Lk;
+    a.T = static_cast<int>(pk & 0xffu);
+    a.H = static_cast<int>((pk >> 8) & 0xffu);
+    a.B = 1 << ((pk >> 16) & 0xfu);
+    a.m = static_cast<int>((pk2 >> 12) & 0xfffu);
+    return DecodeEarly{static_cast<int>((pk >> 20) & 0xffu), static_cast<int>(pk2 & 0xfffu),
+                       ((pk2 >> 24) & 1u) != 0, ((pk2 >> 25) & 1u) != 0};
+}
+
+// query_pos() without reading qpos from the argument block when it is null
+__device__ __forceinline__ int64_t decode_pos(const FusedArgs &a, const DecodeEarly &e, int qi, int i) {
+    if (e.qpos_null) {
+        const int64_t t = a.L - a.T + i;
+        return t >= 0 && t < a.L ? t : -1;
+    }
+    return query_pos(a.qpos, qi, i, a.L, a.T);
+}
+
+// Early arguments (decode_early): n2 = tiles per query.
 template <int MT, int KS, int ROWS, int DT>
 __global__ __launch_bounds__(DT) void hisa_decode_kernel(const uint16_t *q, const uint16_t *pool, const uint16_t *K,
                                                          const float *w, int32_t k_seq_stride, int32_t pool_seq_stride,
                                                          int32_t Lk, uint32_t pk, uint32_t pk2, FusedArgs a_in) {
     FusedArgs a = a_in;
-    a.q = q; a.pool = pool; a.K = K; a.w = w;
-    a.k_seq_stride = k_seq_stride; a.pool_seq_stride = pool_seq_stride; a.L = Lk;
-    a.T = static_cast<int>(pk & 0xffu);
-    a.H = static_cast<int>((pk >> 8) & 0xffu);
-    a.B = 1 << ((pk >> 16) & 0xfu);
-    a.m = static_cast<int>((pk2 >> 12) & 0xfffu);
-    const int nq_all = static_cast<int>((pk >> 20) & 0xffu);
-    const int ntiles = static_cast<int>(pk2 & 0xfffu);
-    const bool qpos_null = ((pk2 >> 24) & 1u) != 0;
-    const bool pool_out_set = ((pk2 >> 25) & 1u) != 0;
+    const DecodeEarly e = decode_early(a, q, K, w, k_seq_stride, Lk, pk, pk2);
+    a.pool = pool; a.pool_seq_stride = pool_seq_stride;
+    const bool pool_out_set = e.pool_out_set;
     constexpr int D = 32 * KS;
     constexpr int NTW = ROWS / (16 * DT / 64);
     __shared__ __attribute__((aligned(16))) BlockStageLds<KS, DT> L;
@@ -344,16 +364,10 @@ __global__ __launch_bounds__(DT) void hisa_decode_kernel(const uint16_t *q, cons
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
     int qi, tile;
-    decode_tile(nq_all, ntiles, qi, tile);
+    decode_tile(e.nq, e.n2, qi, tile);
     if (qi < 0) return;
     const int s = qi / a.T;
-    int64_t t;
-    if (qpos_null) {
-        t = a.L - a.T + (qi - s * a.T);
-        t = t >= 0 && t < a.L ? t : -1;
-    } else {
-        t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
-    }
+    const int64_t t = decode_pos(a, e, qi, qi - s * a.T);
     const bool lead = tile == 0;            // also publishes the kept blocks
     if (t < 0) {
         if (lead)
@@ -433,27 +447,39 @@ constexpr int kDBlkRows = 128;
 // pooled means, plus one (the last) for the own block when it is not taken
 // from the pool -- its rows are staged and averaged in a workgroup of their
 // own, in parallel with the pool tiles.
-template <int MT, int KS>
-__global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs a) {
+// Early arguments (decode_early): n2 = pooled means per sequence (nblk).
+// EARLY = false (more blocks or queries than the packed words hold): the
+// leading arguments are ignored and everything comes from a_in.
+template <int MT, int KS, bool EARLY>
+__global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(const uint16_t *q, const uint16_t *pool,
+                                                                      const uint16_t *K, const float *w,
+                                                                      int32_t k_seq_stride, int32_t pool_seq_stride,
+                                                                      int32_t Lk, uint32_t pk, uint32_t pk2,
+                                                                      FusedArgs a_in) {
     constexpr int D = 32 * KS;
     constexpr int NTW = kDBlkRows / (16 * kDecodeThreads / 64);
     __shared__ __attribute__((aligned(16))) BlockStageLds<KS, kDecodeThreads> L;
+    FusedArgs a = a_in;
+    DecodeEarly e{a.S * a.T, a.nblk, a.qpos == nullptr, a.pool_out != nullptr};
+    if constexpr (EARLY) {
+        e = decode_early(a, q, K, w, k_seq_stride, Lk, pk, pk2);
+        a.pool = pool; a.pool_seq_stride = pool_seq_stride; a.nblk = e.n2;
+    }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int btiles = (a.nblk + kDBlkRows - 1) / kDBlkRows;
     int qi, j;
-    decode_tile(a.S * a.T, btiles + 1, qi, j);
+    decode_tile(e.nq, btiles + 1, qi, j);
     if (qi < 0) return;
     const int s = qi / a.T;
-    const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    const int64_t t = decode_pos(a, e, qi, qi - s * a.T);
     if (t < 0) return;
     const int bt = static_cast<int>(t / a.B);
     // the pool entry of b_t is the own-block mean unless this call writes it
-    const bool own_in_pool = t == a.L - 1 && a.pool_out == nullptr;
+    const bool own_in_pool = t == a.L - 1 && !e.pool_out_set;
     const int full = own_in_pool ? bt + 1 : bt;    // pool rows to score
     const bool own_wg = j == btiles;
     if (own_wg ? own_in_pool : j * kDBlkRows >= full) return;
-    uint32_t *keys = a.blk_keys + static_cast<int64_t>(qi) * a.blk_stride;
 
     if (!own_wg) {
         const int b0 = j * kDBlkRows;
@@ -475,6 +501,7 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs 
         load_qfrag_lds_w<MT, KS>(f, L.q, L.w, lane);
         float v[NTW];
         score_tiles_frag<MT, KS, NTW>(f, kb, v);
+        uint32_t *keys = a.blk_keys + static_cast<int64_t>(qi) * a.blk_stride;
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
             const int p = b0 + (wave * NTW + nt) * 16 + n;
@@ -522,7 +549,7 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dblocks_kernel(FusedArgs 
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kbm[ks] = n == 0 ? load_bf16x8(L.mean + 32 * ks + 8 * g) : zero_bf16x8();
         const float vo = score_rows<MT, KS>(f, kbm);
-        if (lane == 0) keys[bt] = score_to_key(vo);
+        if (lane == 0) a.blk_keys[static_cast<int64_t>(qi) * a.blk_stride + bt] = score_to_key(vo);
     }
 }
 
@@ -542,8 +569,14 @@ __device__ __forceinline__ uint32_t dgather_topm(const uint32_t *keys, int nb, i
     return res.keff;
 }
 
+// Early arguments (decode_early): n2 = tiles per query; the block keys'
+// address and row stride take the places of the pool's.
 template <int MT, int KS, int ROWS>
-__global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs a) {
+__global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(const uint16_t *q, const uint32_t *blk_keys,
+                                                                      const uint16_t *K, const float *w,
+                                                                      int32_t k_seq_stride, int32_t blk_stride,
+                                                                      int32_t Lk, uint32_t pk, uint32_t pk2,
+                                                                      FusedArgs a_in) {
     constexpr int D = 32 * KS;
     constexpr int NTW = ROWS / (16 * kDecodeThreads / 64);
     __shared__ __attribute__((aligned(16))) uint16_t s_q[64 * QStage<KS>::kStride];
@@ -552,21 +585,21 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs 
     __shared__ __attribute__((aligned(16))) uint32_t s_win[kWindowWords];
     __shared__ uint32_t s_keff;
 
+    FusedArgs a = a_in;
+    const DecodeEarly e = decode_early(a, q, K, w, k_seq_stride, Lk, pk, pk2);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
     int qi, tile;
-    decode_tile(a.S * a.T, static_cast<int>((static_cast<int64_t>(a.m) * a.B + ROWS - 1) / ROWS), qi, tile);
+    decode_tile(e.nq, e.n2, qi, tile);
     if (qi < 0) return;
     const int s = qi / a.T;
-    const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    const int64_t t = decode_pos(a, e, qi, qi - s * a.T);
     const bool lead = tile == 0;            // also publishes the kept blocks
-    int32_t *sel = a.sel_blk + static_cast<int64_t>(qi) * a.m;
-    int32_t *ob = a.out_blk ? a.out_blk + static_cast<int64_t>(qi) * a.m : nullptr;
     if (t < 0) {
         if (lead)
             for (int j = tid; j < a.m; j += kDecodeThreads) {
-                sel[j] = -1;
-                if (ob) ob[j] = -1;
+                a.sel_blk[static_cast<int64_t>(qi) * a.m + j] = -1;
+                if (a.out_blk) a.out_blk[static_cast<int64_t>(qi) * a.m + j] = -1;
             }
         return;
     }
@@ -582,12 +615,14 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs 
     const float wq0 = a.w[static_cast<int64_t>(qi) * a.H + (tid < a.H ? tid : a.H - 1)];   // unconditional load
     const float wq = tid < a.H ? wq0 : 0.0f;
     if (wave == 0) {
-        const uint32_t *keys = a.blk_keys + static_cast<int64_t>(qi) * a.blk_stride;
+        const uint32_t *keys = blk_keys + static_cast<int64_t>(qi) * blk_stride;
         auto emit = [&](uint32_t op, int pos) {
             s_sel[op] = pos;
             if (lead) {
-                sel[op] = pos;
-                if (ob) ob[op] = pos;
+                // output rows from the argument block, formed here (after the
+                // key loads) so that no wait for it comes before them
+                a.sel_blk[static_cast<int64_t>(qi) * a.m + op] = pos;
+                if (a.out_blk) a.out_blk[static_cast<int64_t>(qi) * a.m + op] = pos;
             }
         };
         const int rd = (nb + 63) / 64;
@@ -609,8 +644,8 @@ __global__ __launch_bounds__(kDecodeThreads) void hisa_dgather_kernel(FusedArgs 
     __syncthreads();
     if (lead)
         for (int j = static_cast<int>(s_keff) + tid; j < a.m; j += kDecodeThreads) {
-            sel[j] = -1;
-            if (ob) ob[j] = -1;
+            a.sel_blk[static_cast<int64_t>(qi) * a.m + j] = -1;
+            if (a.out_blk) a.out_blk[static_cast<int64_t>(qi) * a.m + j] = -1;
         }
 
     bf16x8 kb[NTW][KS];
@@ -689,8 +724,10 @@ template <int MT, int KS>
 hipError_t launch_wide_blocks(const FusedArgs &a, dim3 g2, hipStream_t st) {
     const int nq = a.S * a.T;
     const int btiles = (a.nblk + kDBlkRows - 1) / kDBlkRows;
-    hipError_t e = launch(kKindScoreBlocks, hisa_dblocks_kernel<MT, KS>,
-                          dim3(static_cast<uint32_t>(decode_grid(nq, btiles + 1))), dim3(kDecodeThreads), 0, st, a);
+    hipError_t e = launch(kKindScoreBlocks, hisa_dblocks_kernel<MT, KS, false>,
+                          dim3(static_cast<uint32_t>(decode_grid(nq, btiles + 1))), dim3(kDecodeThreads), 0, st,
+                          static_cast<const uint16_t *>(nullptr), static_cast<const uint16_t *>(nullptr),
+                          static_cast<const uint16_t *>(nullptr), static_cast<const float *>(nullptr), 0, 0, 0, 0u, 0u, a);
     if (e != hipSuccess) return e;
     SelectArgs se{};
     se.keys = a.blk_keys; se.keys_stride = a.blk_stride;
@@ -711,45 +748,54 @@ hipError_t launch_fused_ks(const FusedArgs &a, bool decode, hipStream_t st) {
         const int wide = static_cast<int>((mb + kDecodeRowsWide - 1) / kDecodeRowsWide);
         const int narrow = static_cast<int>((mb + kDecodeRowsNarrow - 1) / kDecodeRowsNarrow);
         const bool use_wide = static_cast<int64_t>(wide) * nq >= kDecodeWideMin;
-        // the one-launch kernel takes the sequence strides as 32-bit preloaded
-        // arguments; caches laid out wider take the two-kernel path
-        const bool strides32 = a.k_seq_stride < (int64_t{1} << 31) && a.pool_seq_stride < (int64_t{1} << 31);
-        if (a.nblk > kDecodeOneKernelMaxBlocks || !strides32) {
-            // long context: block stage once per query, then the gather
-            const int btiles = (a.nblk + kDBlkRows - 1) / kDBlkRows;
-            const hipError_t e = launch(kKindScoreBlocks, hisa_dblocks_kernel<MT, KS>,
-                                        dim3(static_cast<uint32_t>(decode_grid(nq, btiles + 1))),
-                                        dim3(kDecodeThreads), 0, st, a);
-            if (e != hipSuccess) return e;
+        // the decode kernels take the sequence strides as 32-bit preloaded
+        // arguments (decode_early); caches laid out wider take the batch path
+        // below.  decode_mode() admits only S*T <= 16, H <= 64, m <= 1024, so
+        // the packed words hold every count (tiles <= 2048, nblk <= 2048).
+        const bool strides32 = a.k_seq_stride < (int64_t{1} << 31) && a.pool_seq_stride < (int64_t{1} << 31) &&
+                               a.blk_stride < (int64_t{1} << 31);
+        if (strides32) {
+            const uint32_t pk = static_cast<uint32_t>(a.T) | static_cast<uint32_t>(a.H) << 8 |
+                                static_cast<uint32_t>(__builtin_ctz(static_cast<unsigned>(a.B))) << 16 |
+                                static_cast<uint32_t>(nq) << 20;
+            const uint32_t flags = (a.qpos == nullptr ? 1u : 0u) << 24 | (a.pool_out != nullptr ? 1u : 0u) << 25 |
+                                   static_cast<uint32_t>(a.m) << 12;
+            const int32_t kss = static_cast<int32_t>(a.k_seq_stride), pss = static_cast<int32_t>(a.pool_seq_stride);
+            const int32_t bstride = static_cast<int32_t>(a.blk_stride), Lk = static_cast<int32_t>(a.L);
+            if (a.nblk > kDecodeOneKernelMaxBlocks) {
+                // long context: block stage once per query, then the gather
+                const int btiles = (a.nblk + kDBlkRows - 1) / kDBlkRows;
+                const hipError_t e = launch(kKindScoreBlocks, hisa_dblocks_kernel<MT, KS, true>,
+                                            dim3(static_cast<uint32_t>(decode_grid(nq, btiles + 1))),
+                                            dim3(kDecodeThreads), 0, st, a.q, a.pool, a.K, a.w, kss, pss, Lk, pk,
+                                            flags | static_cast<uint32_t>(a.nblk), a);
+                if (e != hipSuccess) return e;
+                const int tiles = use_wide ? wide : narrow;
+                const dim3 grid(static_cast<uint32_t>(decode_grid(nq, tiles)));
+                const uint32_t pk2 = flags | static_cast<uint32_t>(tiles);
+                const uint32_t *bk = a.blk_keys;
+                if (use_wide)
+                    return launch(kKindScoreRefine, hisa_dgather_kernel<MT, KS, kDecodeRowsWide>, grid,
+                                  dim3(kDecodeThreads), 0, st, a.q, bk, a.K, a.w, kss, bstride, Lk, pk, pk2, a);
+                return launch(kKindScoreRefine, hisa_dgather_kernel<MT, KS, kDecodeRowsNarrow>, grid,
+                              dim3(kDecodeThreads), 0, st, a.q, bk, a.K, a.w, kss, bstride, Lk, pk, pk2, a);
+            }
+            // one workgroup per compute unit or fewer: eight waves per
+            // workgroup share its block stage and split its rows more finely
+            const int tiles = use_wide ? wide : narrow;
+            const bool eight = static_cast<int64_t>(tiles) * nq <= kDecodeEightWaveMaxGrid;
+            const dim3 grid(static_cast<uint32_t>(decode_grid(nq, tiles)));
+            const uint32_t pk2 = flags | static_cast<uint32_t>(tiles);
+            auto go = [&](auto kernel, int threads) {
+                return launch(kKindIndexDecode, kernel, grid, dim3(threads), 0, st, a.q, a.pool, a.K, a.w, kss, pss,
+                              Lk, pk, pk2, a);
+            };
             if (use_wide)
-                return launch(kKindScoreRefine, hisa_dgather_kernel<MT, KS, kDecodeRowsWide>,
-                              dim3(static_cast<uint32_t>(decode_grid(nq, wide))), dim3(kDecodeThreads), 0, st, a);
-            return launch(kKindScoreRefine, hisa_dgather_kernel<MT, KS, kDecodeRowsNarrow>,
-                          dim3(static_cast<uint32_t>(decode_grid(nq, narrow))), dim3(kDecodeThreads), 0, st, a);
+                return eight ? go(hisa_decode_kernel<MT, KS, kDecodeRowsWide, 512>, 512)
+                             : go(hisa_decode_kernel<MT, KS, kDecodeRowsWide, 256>, 256);
+            return eight ? go(hisa_decode_kernel<MT, KS, kDecodeRowsNarrow, 512>, 512)
+                         : go(hisa_decode_kernel<MT, KS, kDecodeRowsNarrow, 256>, 256);
         }
-        // one workgroup per compute unit or fewer: eight waves per workgroup
-        // share its block stage and split its rows more finely
-        const int tiles = use_wide ? wide : narrow;
-        const bool eight = static_cast<int64_t>(tiles) * nq <= kDecodeEightWaveMaxGrid;
-        const dim3 grid(static_cast<uint32_t>(decode_grid(nq, tiles)));
-        // the preloaded words: strides below 2^31 elements (above), and
-        // decode_mode() admits only S*T <= 16, H <= 64, m <= 1024 (tiles <= 2048)
-        const uint32_t pk = static_cast<uint32_t>(a.T) | static_cast<uint32_t>(a.H) << 8 |
-                            static_cast<uint32_t>(__builtin_ctz(static_cast<unsigned>(a.B))) << 16 |
-                            static_cast<uint32_t>(nq) << 20;
-        const uint32_t pk2 = static_cast<uint32_t>(tiles) | static_cast<uint32_t>(a.m) << 12 |
-                             (a.qpos == nullptr ? 1u : 0u) << 24 | (a.pool_out != nullptr ? 1u : 0u) << 25;
-        const int32_t kss = static_cast<int32_t>(a.k_seq_stride), pss = static_cast<int32_t>(a.pool_seq_stride);
-        const int32_t Lk = static_cast<int32_t>(a.L);
-        auto go = [&](auto kernel, int threads) {
-            return launch(kKindIndexDecode, kernel, grid, dim3(threads), 0, st, a.q, a.pool, a.K, a.w, kss, pss, Lk,
-                          pk, pk2, a);
-        };
-        if (use_wide)
-            return eight ? go(hisa_decode_kernel<MT, KS, kDecodeRowsWide, 512>, 512)
-                         : go(hisa_decode_kernel<MT, KS, kDecodeRowsWide, 256>, 256);
-        return eight ? go(hisa_decode_kernel<MT, KS, kDecodeRowsNarrow, 512>, 512)
-                     : go(hisa_decode_kernel<MT, KS, kDecodeRowsNarrow, 256>, 256);
     }
     const hipError_t e = (a.bucket_off && a.nblk <= kBMMaxBlocks)
         ? launch_block_major_blocks(a, st)
