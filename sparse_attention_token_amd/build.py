@@ -33,7 +33,10 @@ FLAGS = [
 # Kernels whose first argument is a struct preload nothing.
 # hisa_fused.hip: the one-launch decode kernel's nine leading arguments.
 SOURCE_FLAGS = {"select.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"],
-                "hisa_fused.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=9"]}
+                "hisa_fused.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=9"],
+                # pool.hip: every kernel takes plain pointers and sizes; the
+                # dispatcher preloads as many as fit (14 dwords)
+                "pool.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 
 
 def _compile(src: str, verbose: bool) -> str:
