@@ -28,9 +28,11 @@
 // serialize (about 16x a conflict-free one), cross-lane shuffles through LDS
 // cost about 75 cycles each while DPP row operations cost a few, and 16-byte
 // LDS reads whose lanes stride by 128 bytes conflict on every bank.  A
-// workgroup's select over 8192 keys is bound by its one CU's vector ALUs (some
-// 30 operations a key): a histogram range fitted to the keys, which avoids
-// the atomics' contention, measured no faster there.
+// workgroup's select over 8192 keys is bound by its one CU's vector ALUs and
+// LDS (some 30 operations a key): a histogram range fitted to the keys
+// measured no faster there (its extra reduction and barrier cost what the
+// avoided contention saved); copies of the first histogram (NC) cut the
+// contention without either.
 #pragma once
 
 #include "hisa_internal.h"
