@@ -36,7 +36,10 @@ SOURCE_FLAGS = {"select.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"],
                 "hisa_fused.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=9"],
                 # pool.hip: every kernel takes plain pointers and sizes; the
                 # dispatcher preloads as many as fit (14 dwords)
-                "pool.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+                "pool.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+                # attention.hip: the attention kernel's eleven and the
+                # combine's five leading arguments
+                "attention.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -96,8 +96,24 @@ struct AttnLds {
 // into registers while the current step is computed (every load is issued,
 // rows of no candidate re-read the cache's first row and are masked), and its
 // set entries one step further ahead.
-template <int HT, int KSK, int DVW>
-__global__ __launch_bounds__(kAttnThreads, HT == 2 ? 2 : 1) void sparse_attn_kernel(AttnArgs a) {
+// The leading arguments are what a workgroup needs before its first loads
+// (the set, the latent rows and q): this file is built with kernarg
+// preloading, so they arrive in scalar registers at dispatch and the set's
+// loads go out without waiting a memory round trip for the argument block.
+// pk = Ha | nsplit << 16.  EARLY = false (latent strides past 2^31 elements):
+// they are ignored and everything comes from a_in.
+template <int HT, int KSK, int DVW, bool EARLY>
+__global__ __launch_bounds__(kAttnThreads, HT == 2 ? 2 : 1) void sparse_attn_kernel(
+        const int32_t *idx_, const uint16_t *kv_, const uint16_t *q_, int32_t kv_seq_stride, int32_t kv_row_stride,
+        int32_t Lk, int32_t k_, int32_t tps, uint32_t pk, int32_t T_, int32_t npair, AttnArgs a_in) {
+    AttnArgs a = a_in;
+    if constexpr (EARLY) {
+        a.idx = idx_; a.kv = kv_; a.q = q_;
+        a.kv_seq_stride = kv_seq_stride; a.kv_row_stride = kv_row_stride; a.L = Lk;
+        a.k = k_; a.tps = tps; a.T = T_; a.npair = npair;
+        a.Ha = static_cast<int>(pk & 0xffffu);
+        a.nsplit = static_cast<int>(pk >> 16);
+    }
     constexpr int Dk = 32 * KSK;
     constexpr int HG = 16 * HT;
     using Lds = AttnLds<HT, KSK, DVW>;
@@ -312,7 +328,14 @@ __global__ __launch_bounds__(kAttnThreads, HT == 2 ? 2 : 1) void sparse_attn_ker
 // under a test of an earlier one waits for it).  Up to 8 splits everything is
 // read in one round; beyond, the maxima first, then the weighted sums, in the
 // same split order either way.
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
+// Leading arguments preloaded at dispatch (pk = Ha | nsplit << 16), the rest
+// of the struct used only for the outputs.
+__global__ __launch_bounds__(128) void attn_combine_kernel(float *part_o, float *part_m, float *part_l, uint32_t pk,
+                                                           int32_t Dv, AttnArgs a_in) {
+    AttnArgs a = a_in;
+    a.part_o = part_o; a.part_m = part_m; a.part_l = part_l; a.Dv = Dv;
+    a.Ha = static_cast<int>(pk & 0xffffu);
+    a.nsplit = static_cast<int>(pk >> 16);
     constexpr int U = 8;
     const int qh = blockIdx.x;                      // query * Ha + head
     const int qi = qh / a.Ha, head = qh - qi * a.Ha;
@@ -374,10 +397,19 @@ template <int HT, int KSK, int DVW>
 hipError_t launch_attn(const AttnArgs &a, hipStream_t st) {
     const int nhg = a.Ha / (16 * HT);
     const dim3 grid(static_cast<uint32_t>((a.npair + 7) / 8 * 8 * nhg));
-    hipError_t e = launch(kKindAttention, sparse_attn_kernel<HT, KSK, DVW>, grid, dim3(kAttnThreads), 0, st, a);
+    // Ha <= 128 and nsplit <= k / 64 < 2^16 (the ABI's limits): pk holds both
+    const uint32_t pk = static_cast<uint32_t>(a.Ha) | static_cast<uint32_t>(a.nsplit) << 16;
+    const bool fits = a.kv_seq_stride < (int64_t{1} << 31) && a.kv_row_stride < (int64_t{1} << 31);
+    hipError_t e = fits
+        ? launch(kKindAttention, sparse_attn_kernel<HT, KSK, DVW, true>, grid, dim3(kAttnThreads), 0, st, a.idx,
+                 a.kv, a.q, static_cast<int32_t>(a.kv_seq_stride), static_cast<int32_t>(a.kv_row_stride),
+                 static_cast<int32_t>(a.L), a.k, a.tps, pk, a.T, a.npair, a)
+        : launch(kKindAttention, sparse_attn_kernel<HT, KSK, DVW, false>, grid, dim3(kAttnThreads), 0, st,
+                 static_cast<const int32_t *>(nullptr), static_cast<const uint16_t *>(nullptr),
+                 static_cast<const uint16_t *>(nullptr), 0, 0, 0, 0, 0, 0u, 0, 0, a);
     if (e != hipSuccess || a.nsplit == 1) return e;
     return launch(kKindAttnCombine, attn_combine_kernel, dim3(static_cast<uint32_t>(a.S * a.T * a.Ha)),
-                  dim3(128), 0, st, a);
+                  dim3(128), 0, st, a.part_o, a.part_m, a.part_l, pk, a.Dv, a);
 }
 
 template <int KSK, int DVW>
