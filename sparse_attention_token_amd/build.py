@@ -39,7 +39,9 @@ SOURCE_FLAGS = {"select.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"],
                 "pool.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
                 # attention.hip: the attention kernel's eleven and the
                 # combine's five leading arguments
-                "attention.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11"]}
+                "attention.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11"],
+                # hisa_tree.hip: the tree's top and gather kernels
+                "hisa_tree.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -161,23 +161,45 @@ __device__ __forceinline__ uint16_t super_column(const uint16_t *pool_col, int d
 // Grid S*T*nslice: workgroup (query qi, slice) scores blocks
 // slice*rows .. slice*rows+rows-1 of the kept super-blocks' blocks (in kept
 // order) into tblk_keys[qi]; slice 0 also publishes the kept super-blocks.
-template <int MT, int KS, bool MAX>
-__global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a, int nslice, int rows) {
+//
+// The leading arguments are what a workgroup needs before its first loads (q,
+// w and the own block's rows); this file is built with kernarg preloading,
+// so they arrive in scalar registers at dispatch instead of after a memory
+// round trip for the argument block.  pk = H | log2(B) << 8 | log2(G) << 12 |
+// (qpos null) << 16.  EARLY = false (a key stride past 2^31 elements): they
+// are ignored and everything comes from a_in.
+template <int MT, int KS, bool MAX, bool EARLY>
+__global__ __launch_bounds__(kTopThreads) void tree_top_kernel(const uint16_t *q, const float *w, const uint16_t *K,
+                                                               int32_t k_seq_stride, int32_t Lk, int32_t T,
+                                                               uint32_t pk, int nslice, int rows, TreeTopArgs a_in) {
     constexpr int D = 32 * KS;
     __shared__ __attribute__((aligned(16))) TreeTopLds<KS> L;
+    TreeTopArgs a = a_in;
+    bool qpos_null = a.qpos == nullptr;
+    if constexpr (EARLY) {
+        a.q = q; a.w = w; a.K = K; a.k_seq_stride = k_seq_stride; a.L = Lk; a.T = T;
+        a.H = static_cast<int>(pk & 0xffu);
+        a.B = 1 << ((pk >> 8) & 0xfu);
+        a.G = 1 << ((pk >> 12) & 0xfu);
+        qpos_null = ((pk >> 16) & 1u) != 0;
+    }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int qi = blockIdx.x / nslice;
     const int slice = blockIdx.x - qi * nslice;
     const bool lead = slice == 0;
     const int s = qi / a.T;
-    const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
-    int32_t *ssb = a.sel_sb + static_cast<int64_t>(qi) * a.W;
-    int32_t *osb = a.out_sblk ? a.out_sblk + static_cast<int64_t>(qi) * a.W : nullptr;
+    int64_t t;
+    if (qpos_null) {
+        t = a.L - a.T + (qi - s * a.T);
+        t = t >= 0 && t < a.L ? t : -1;
+    } else {
+        t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    }
     if (t < 0) {                                 // no candidate at all (tree_topm_kernel pads the blocks)
         if (lead)
             for (int j = tid; j < a.W; j += kTopThreads) {
-                ssb[j] = -1;
-                if (osb) osb[j] = -1;
+                a.sel_sb[static_cast<int64_t>(qi) * a.W + j] = -1;
+                if (a.out_sblk) a.out_sblk[static_cast<int64_t>(qi) * a.W + j] = -1;
             }
         return;
     }
@@ -185,8 +207,6 @@ __global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a, in
     const int64_t st = bt / a.G;
     const int ns = static_cast<int>(st + 1);
     const bool own_from_pool = t == a.L - 1;
-    const uint16_t *pool = a.pool + s * a.pool_seq_stride;
-    const uint16_t *spool = a.spool + s * a.spool_seq_stride;
 
     // ---- stage q, w and (when the pools do not hold them) the own block's rows
     const int64_t r0 = bt * a.B;
@@ -213,6 +233,12 @@ __global__ __launch_bounds__(kTopThreads) void tree_top_kernel(TreeTopArgs a, in
     qst.store(L.q, a.H, tid);
     if (tid < 64) L.w[tid] = wq;
     __syncthreads();
+    // the pools and output rows from the argument block, formed after the
+    // first loads so that no wait for it comes before them
+    const uint16_t *pool = a.pool + s * a.pool_seq_stride;
+    const uint16_t *spool = a.spool + s * a.spool_seq_stride;
+    int32_t *ssb = a.sel_sb + static_cast<int64_t>(qi) * a.W;
+    int32_t *osb = a.out_sblk ? a.out_sblk + static_cast<int64_t>(qi) * a.W : nullptr;
     if (!own_from_pool) {
         own_rows_rep<D, 64, MAX>(s_own, own_rows, L.rep, nullptr);     // ends with a barrier
         if (tid < D) L.srep[tid] = super_column<MAX>(pool + tid, D, st * a.G, bt, a.B, L.rep[tid], own_rows);
@@ -346,8 +372,16 @@ constexpr int kTreeGatherRows = 128;          // 2 tiles of 16 rows per wave
 constexpr int kTreeGatherMaxQueries = 16;
 constexpr int kTreeGatherMaxM = 1024;
 
+// Leading arguments preloaded at dispatch (as tree_top_kernel's): q, w, the
+// block keys and kept super-blocks with the keys' row stride, L, pk = T | H
+// << 8 | log2(B) << 16 | (qpos null) << 24 and pk2 = m | W << 16 (the launch
+// holds at most 16 queries and m <= 1024, W <= 2048).
 template <int MT, int KS, int R>
-__global__ __launch_bounds__(kTreeGatherThreads) void tree_gather_kernel(TreeTopArgs a, int ntb, int tiles) {
+__global__ __launch_bounds__(kTreeGatherThreads) void tree_gather_kernel(const uint16_t *q, const float *w,
+                                                                         const uint32_t *tblk_keys,
+                                                                         const int32_t *sel_sb, int32_t tblk_stride,
+                                                                         int32_t Lk, uint32_t pk, uint32_t pk2,
+                                                                         int ntb, int tiles, TreeTopArgs a_in) {
     constexpr int D = 32 * KS;
     constexpr int NTW = kTreeGatherRows / (16 * kTreeGatherThreads / 64);
     __shared__ __attribute__((aligned(16))) uint16_t s_q[64 * QStage<KS>::kStride];
@@ -357,20 +391,33 @@ __global__ __launch_bounds__(kTreeGatherThreads) void tree_gather_kernel(TreeTop
     __shared__ __attribute__((aligned(16))) uint32_t s_win[kWindowWords];
     __shared__ uint32_t s_keff;
 
+    TreeTopArgs a = a_in;
+    a.q = q; a.w = w; a.tblk_keys = const_cast<uint32_t *>(tblk_keys); a.sel_sb = const_cast<int32_t *>(sel_sb);
+    a.tblk_stride = tblk_stride; a.L = Lk;
+    a.T = static_cast<int>(pk & 0xffu);
+    a.H = static_cast<int>((pk >> 8) & 0xffu);
+    a.B = 1 << ((pk >> 16) & 0xfu);
+    const bool qpos_null = ((pk >> 24) & 1u) != 0;
+    a.m = static_cast<int>(pk2 & 0xffffu);
+    a.W = static_cast<int>(pk2 >> 16);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int qi = blockIdx.x / tiles;
     const int tile = blockIdx.x - qi * tiles;
     const bool lead = tile == 0;                       // also publishes the kept blocks
     const int s = qi / a.T;
-    const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
-    int32_t *sel = a.sel_blk + static_cast<int64_t>(qi) * a.m;
-    int32_t *ob = a.out_blk ? a.out_blk + static_cast<int64_t>(qi) * a.m : nullptr;
+    int64_t t;
+    if (qpos_null) {
+        t = a.L - a.T + (qi - s * a.T);
+        t = t >= 0 && t < a.L ? t : -1;
+    } else {
+        t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    }
     if (t < 0) {                                       // the select reads no candidate row
         if (lead)
             for (int j = tid; j < a.m; j += kTreeGatherThreads) {
-                sel[j] = -1;
-                if (ob) ob[j] = -1;
+                a.sel_blk[static_cast<int64_t>(qi) * a.m + j] = -1;
+                if (a.out_blk) a.out_blk[static_cast<int64_t>(qi) * a.m + j] = -1;
             }
         return;
     }
@@ -388,8 +435,10 @@ __global__ __launch_bounds__(kTreeGatherThreads) void tree_gather_kernel(TreeTop
         const uint32_t ke = tree_topm_wave<R>(a, qi, ntb, s_sb, s_win, [&](uint32_t op, int32_t b) {
             s_sel[op] = b;
             if (lead) {
-                sel[op] = b;
-                if (ob) ob[op] = b;
+                // output rows from the argument block, formed here, after the
+                // first loads
+                a.sel_blk[static_cast<int64_t>(qi) * a.m + op] = b;
+                if (a.out_blk) a.out_blk[static_cast<int64_t>(qi) * a.m + op] = b;
             }
         });
         if (lane == 0) s_keff = ke;
@@ -401,8 +450,8 @@ __global__ __launch_bounds__(kTreeGatherThreads) void tree_gather_kernel(TreeTop
     const int keff = static_cast<int>(s_keff);
     if (lead)
         for (int j = keff + tid; j < a.m; j += kTreeGatherThreads) {
-            sel[j] = -1;
-            if (ob) ob[j] = -1;
+            a.sel_blk[static_cast<int64_t>(qi) * a.m + j] = -1;
+            if (a.out_blk) a.out_blk[static_cast<int64_t>(qi) * a.m + j] = -1;
         }
 
     // rows past the kept slots, or past t, load row t (a valid row) and are
@@ -441,9 +490,18 @@ hipError_t launch_top_ks(const TreeTopArgs &a, hipStream_t st, bool *scored) {
     const int nslice = want < most ? want : most;
     const int rows = static_cast<int>((ntb + nslice - 1) / nslice + 15) / 16 * 16;
     const dim3 grid(static_cast<uint32_t>(nq * nslice)), block(kTopThreads);
-    hipError_t e = a.pool_max
-                       ? launch(kKindTreeTop, tree_top_kernel<MT, KS, true>, grid, block, 0, st, a, nslice, rows)
-                       : launch(kKindTreeTop, tree_top_kernel<MT, KS, false>, grid, block, 0, st, a, nslice, rows);
+    // preloaded words (tree_top_kernel); a key stride past 2^31 elements takes
+    // the variant reading the struct
+    const bool early = a.k_seq_stride < (int64_t{1} << 31);
+    const uint32_t pk = static_cast<uint32_t>(a.H) | static_cast<uint32_t>(__builtin_ctz(static_cast<unsigned>(a.B))) << 8 |
+                        static_cast<uint32_t>(__builtin_ctz(static_cast<unsigned>(a.G))) << 12 |
+                        (a.qpos == nullptr ? 1u : 0u) << 16;
+    const int32_t kss = early ? static_cast<int32_t>(a.k_seq_stride) : 0, Lk = static_cast<int32_t>(a.L);
+    auto top = [&](auto kernel) {
+        return launch(kKindTreeTop, kernel, grid, block, 0, st, a.q, a.w, a.K, kss, Lk, a.T, pk, nslice, rows, a);
+    };
+    hipError_t e = a.pool_max ? (early ? top(tree_top_kernel<MT, KS, true, true>) : top(tree_top_kernel<MT, KS, true, false>))
+                              : (early ? top(tree_top_kernel<MT, KS, false, true>) : top(tree_top_kernel<MT, KS, false, false>));
     if (e != hipSuccess) return e;
     const int nt = static_cast<int>(ntb);
     const int rd = (nt + 63) / 64;
@@ -451,10 +509,21 @@ hipError_t launch_top_ks(const TreeTopArgs &a, hipStream_t st, bool *scored) {
     if (*scored) {
         const int tiles = static_cast<int>((static_cast<int64_t>(a.m) * a.B + kTreeGatherRows - 1) / kTreeGatherRows);
         const dim3 g3(static_cast<uint32_t>(nq * tiles)), b3(kTreeGatherThreads);
-        if (rd <= 4) return launch(kKindScoreRefine, tree_gather_kernel<MT, KS, 4>, g3, b3, 0, st, a, nt, tiles);
-        if (rd <= 8) return launch(kKindScoreRefine, tree_gather_kernel<MT, KS, 8>, g3, b3, 0, st, a, nt, tiles);
-        if (rd <= 16) return launch(kKindScoreRefine, tree_gather_kernel<MT, KS, 16>, g3, b3, 0, st, a, nt, tiles);
-        return launch(kKindScoreRefine, tree_gather_kernel<MT, KS, 32>, g3, b3, 0, st, a, nt, tiles);
+        // nq <= 16 (so T <= 16), m <= 1024, W <= 2048 and the key rows' stride
+        // below 2^31: every field fits its packed place
+        const uint32_t gk = static_cast<uint32_t>(a.T) | static_cast<uint32_t>(a.H) << 8 |
+                            static_cast<uint32_t>(__builtin_ctz(static_cast<unsigned>(a.B))) << 16 |
+                            (a.qpos == nullptr ? 1u : 0u) << 24;
+        const uint32_t gk2 = static_cast<uint32_t>(a.m) | static_cast<uint32_t>(a.W) << 16;
+        const int32_t ts = static_cast<int32_t>(a.tblk_stride);
+        auto gather = [&](auto kernel) {
+            return launch(kKindScoreRefine, kernel, g3, b3, 0, st, a.q, a.w, static_cast<const uint32_t *>(a.tblk_keys),
+                          static_cast<const int32_t *>(a.sel_sb), ts, Lk, gk, gk2, nt, tiles, a);
+        };
+        if (rd <= 4) return gather(tree_gather_kernel<MT, KS, 4>);
+        if (rd <= 8) return gather(tree_gather_kernel<MT, KS, 8>);
+        if (rd <= 16) return gather(tree_gather_kernel<MT, KS, 16>);
+        return gather(tree_gather_kernel<MT, KS, 32>);
     }
     const dim3 g2(static_cast<uint32_t>((nq + kTopmWaves - 1) / kTopmWaves)), b2(64 * kTopmWaves);
     if (rd <= 4) return launch(kKindSelectTree, tree_topm_kernel<4>, g2, b2, 0, st, a, nt);
