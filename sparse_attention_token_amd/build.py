@@ -41,7 +41,10 @@ SOURCE_FLAGS = {"select.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"],
                 # combine's five leading arguments
                 "attention.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11"],
                 # hisa_tree.hip: the tree's top and gather kernels
-                "hisa_tree.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
+                "hisa_tree.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"],
+                # score.hip: the flat indexer's scorer (the same treatment as
+                # the decode kernels, so that the baseline is engineered alike)
+                "score.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -158,14 +158,34 @@ __device__ __forceinline__ void flat_score_store(const QFrag<MT, KS> &f, const b
     }
 }
 
-template <int MT, int KS>
-__global__ __launch_bounds__(kFlatThreads) void score_flat_kernel(ScoreArgs a, int rows_per_wg) {
+// The leading arguments are what a workgroup needs before its first loads (K
+// rows, q, w); this file is built with kernarg preloading, so they arrive in
+// scalar registers at dispatch instead of after a memory round trip for the
+// argument block.  pk = H | (qpos null) << 8.  EARLY = false (a key stride
+// past 2^31 elements): they are ignored and everything comes from a_in.
+template <int MT, int KS, bool EARLY>
+__global__ __launch_bounds__(kFlatThreads) void score_flat_kernel(const uint16_t *K, const uint16_t *q, const float *w,
+                                                                  int32_t k_seq_stride, int32_t Lk, int32_t T,
+                                                                  uint32_t pk, int rows_per_wg, ScoreArgs a_in) {
     constexpr int D = 32 * KS;
     __shared__ __attribute__((aligned(16))) uint16_t s_q[64 * QStage<KS>::kStride];
     __shared__ float s_w[64];
+    ScoreArgs a = a_in;
+    bool qpos_null = a.qpos == nullptr;
+    if constexpr (EARLY) {
+        a.K = K; a.q = q; a.w = w; a.k_seq_stride = k_seq_stride; a.L = Lk; a.T = T;
+        a.H = static_cast<int>(pk & 0xffu);
+        qpos_null = ((pk >> 8) & 1u) != 0;
+    }
     const int qi = blockIdx.y;
     const int s = qi / a.T;
-    const int64_t t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    int64_t t;
+    if (qpos_null) {
+        t = a.L - a.T + (qi - s * a.T);
+        t = t >= 0 && t < a.L ? t : -1;
+    } else {
+        t = query_pos(a.qpos, qi, qi - s * a.T, a.L, a.T);
+    }
     if (t < 0) return;
     const int64_t npos = t + 1;
     const int64_t row0 = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
@@ -198,8 +218,15 @@ __global__ __launch_bounds__(kFlatThreads) void score_flat_kernel(ScoreArgs a, i
 
 template <int MT>
 hipError_t launch_flat_mt(const ScoreArgs &a, dim3 grid, int rows_per_wg, hipStream_t st) {
-    if (a.d == 64) return launch(kKindScoreFlat, score_flat_kernel<MT, 2>, grid, dim3(kFlatThreads), 0, st, a, rows_per_wg);
-    return launch(kKindScoreFlat, score_flat_kernel<MT, 4>, grid, dim3(kFlatThreads), 0, st, a, rows_per_wg);
+    const bool early = a.k_seq_stride < (int64_t{1} << 31);
+    const uint32_t pk = static_cast<uint32_t>(a.H) | (a.qpos == nullptr ? 1u : 0u) << 8;
+    auto go = [&](auto kernel) {
+        return launch(kKindScoreFlat, kernel, grid, dim3(kFlatThreads), 0, st, a.K, a.q, a.w,
+                      early ? static_cast<int32_t>(a.k_seq_stride) : 0, static_cast<int32_t>(a.L), a.T, pk,
+                      rows_per_wg, a);
+    };
+    if (a.d == 64) return early ? go(score_flat_kernel<MT, 2, true>) : go(score_flat_kernel<MT, 2, false>);
+    return early ? go(score_flat_kernel<MT, 4, true>) : go(score_flat_kernel<MT, 4, false>);
 }
 
 template <int MODE, int MT>
