@@ -150,3 +150,82 @@ def test_attention_spare_rows_and_columns(hisa, Dk, Dv, Ha):
     _same(o1, o2, "attention output")
     _same(l1, l2, "attention lse")
     assert torch.isfinite(o1[1]).all().item()
+
+
+def _wide(t, min_stride):
+    """t [S, N, c] in the leading corner of a NaN-filled [S, N', c] buffer whose
+    sequence stride N' * c is at least min_stride elements."""
+    S, N, c = t.shape
+    return _spare(t, max(0, -(-min_stride // c) - N))
+
+
+def test_strides_past_2g_elements_give_identical_results(hisa):
+    """Sequence strides of 2^31 elements or more: the decode, tree and flat
+    kernels take their leading arguments preloaded as 32-bit values, so such
+    caches run other variants (the batch path for decode, the tree's and the
+    flat scorer's struct-reading kernels); they must give the bits the tight
+    layout gives.  The wide key cache is 8.6 GB."""
+    import torch
+
+    S, L, T, H, d, B, m, k = 2, 3001, 1, 64, 128, 128, 8, 300
+    print("layout case strides past 2^31 elements", flush=True)
+    c = synth.clustered_case(S, L, T, H, d, B, m, k, seed=31, latent_block=B)
+    dev = to_dev(c)
+    q, w = dev["q"], dev["w"]
+    nblk = -(-L // B)
+    G, W = 4, 2
+
+    def run(K):
+        pool = torch.zeros((S, nblk, d), dtype=torch.bfloat16, device=K.device)
+        hisa.hisa_pool_append(K, pool, 0, L - 1, B)
+        pool2 = pool.clone()
+        hisa.hisa_pool_append(K, pool, L - 1, L, B)
+        res = {"pool": pool.clone()}
+        res["index"] = hisa.hisa_index(q, w, K, L, pool, B, m, k, want_blocks=True)
+        res["flat"] = hisa.dsa_flat_index(q, w, K, L, k)
+        res["append_index"] = hisa.hisa_append_index(K, pool2, L - 1, L, q, w, B, m, k, want_blocks=True)
+        res["pool_after_append_index"] = pool2.clone()
+        tp = torch.zeros((S, nblk, d), dtype=torch.bfloat16, device=K.device)
+        sp = torch.zeros((S, -(-nblk // G), d), dtype=torch.bfloat16, device=K.device)
+        hisa.hisa_tree_append(K, tp, sp, 0, L, B, G)
+        res["tree"] = hisa.hisa_tree_index(q, w, K, L, tp, sp, B, G, W, m, k, want_blocks=True, want_super=True)
+        torch.cuda.synchronize()
+        return res
+
+    tight = run(dev["K"])
+    Kw = _wide(dev["K"], (1 << 31) + 64)
+    assert Kw.stride(0) >= (1 << 31)
+    wide = run(Kw)
+    del Kw
+    _same(tight["pool"], wide["pool"], "pool")
+    _same(tight["pool_after_append_index"], wide["pool_after_append_index"], "pool after append+index")
+    for key in ("index", "flat", "append_index", "tree"):
+        for j, (a, b) in enumerate(zip(tight[key], wide[key])):
+            _same(a, b, f"{key} output {j}")
+    assert (tight["index"][0] >= 0).sum().item() > 0
+
+
+def test_attention_stride_past_2g_elements(hisa):
+    """A latent cache whose sequence stride is 2^31 elements or more runs the
+    attention variant that reads its struct argument: the same bits."""
+    import torch
+
+    S, T, L, k, Dk, Dv, Ha = 2, 3, 5000, 700, 576, 512, 16
+    print("attention layout stride past 2^31 elements", flush=True)
+    rng = np.random.default_rng(43)
+    kv = synth.bf16_bits(rng.standard_normal((S, L, Dk)).astype(np.float32))
+    q = synth.bf16_bits((rng.standard_normal((S, T, Ha, Dk)) * 0.1).astype(np.float32))
+    idx = rng.integers(-1, L, size=(S, T, k)).astype(np.int32)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    kv_t, q_t = to(kv), to(q)
+    idx_t = torch.from_numpy(idx).cuda()
+    scale = 1.0 / np.sqrt(Dk)
+    o1, l1 = hisa.hisa_sparse_attention(q_t, kv_t, L, idx_t, Dv, scale)
+    kvw = _wide(kv_t, (1 << 31) + 64)
+    assert kvw.stride(0) >= (1 << 31)
+    o2, l2 = hisa.hisa_sparse_attention(q_t, kvw, L, idx_t, Dv, scale)
+    torch.cuda.synchronize()
+    del kvw
+    _same(o1, o2, "attention output")
+    _same(l1, l2, "attention lse")
+    assert torch.isfinite(o1).all().item()
