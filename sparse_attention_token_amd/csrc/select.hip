@@ -121,10 +121,12 @@ __device__ __forceinline__ void mask_run(int64_t base, int64_t n, uint32_t (&kv)
 // unchanged.
 constexpr int kStageOut = 2048;
 // A kept entry staged in LDS: (id, key) in one 64-bit word, one LDS write per
-// kept key (two 32-bit writes before: decode top k's emit 2,270 cycles).
+// kept key rather than two.
 typedef uint32_t stage_u32x2 __attribute__((ext_vector_type(2)));
 // Workgroups of 1024 threads count the first digit into four histogram
-// copies (block_radix_select's NC): decode top k's first pass 2,430 cycles.
+// copies (block_radix_select's NC): the decode top k's first pass took 1,730
+// cycles instead of 2,430.  512-thread workgroups (many queries) keep one
+// copy, whose LDS lets more workgroups share a compute unit.
 template <int NT>
 constexpr int kFirstCopies = NT == 1024 ? 4 : 1;
 
