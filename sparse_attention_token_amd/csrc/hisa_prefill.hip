@@ -196,8 +196,8 @@ struct QDirect {
     static constexpr int D = L::D, CPR = L::CPR;
     static constexpr int kSlots = MT * 16 * CPR;
     static constexpr int kInstr = kSlots / 64;
-    static constexpr int kPerWave = kInstr / NW;              // wave w takes instructions w, w+NW, ...
-    static_assert(kSlots % 64 == 0 && kInstr % NW == 0, "every wave issues whole loads");
+    static constexpr int kPerWave = (kInstr + NW - 1) / NW;   // wave w takes instructions w, w+NW, ...
+    static_assert(kSlots % 64 == 0, "every wave issues whole loads");
     int src[kPerWave];                                        // byte offset in q, or -1: no load
 
     __device__ __forceinline__ void init(int H, int wave, int lane) {
@@ -205,7 +205,7 @@ struct QDirect {
         for (int u = 0; u < kPerWave; ++u) {
             const int p = 64 * (wave + u * NW) + lane;
             const int row = p / CPR, slot = p - row * CPR;
-            src[u] = row < H ? 2 * (row * D + 8 * (slot ^ L::swz(row))) : -1;
+            src[u] = wave + u * NW < kInstr && row < H ? 2 * (row * D + 8 * (slot ^ L::swz(row))) : -1;
         }
     }
     __device__ __forceinline__ void issue(const uint16_t *__restrict__ q, const float *__restrict__ w, int H,
@@ -377,13 +377,17 @@ __global__ __launch_bounds__(kBMThreads) void hisa_refine_bm_kernel(FusedArgs a)
 // in the refinement.  Only complete blocks b < b_t are scored here (the own
 // block's representative differs per query; hisa_topm_kernel scores it).
 // blk_keys[qi][b] receives the key of block b for b < b_t.
-constexpr int kBlkTileRows = 128;
+// Four waves of 64 pooled means each: every query staged in LDS serves 256
+// means (with two waves and 128 means, each query's 16 KB of q was fetched
+// from L2 twice as often for the same matrix-core work).
+constexpr int kBlkThreads = 256;
+constexpr int kBlkTileRows = 256;
 constexpr int kBlkChunk = 16;          // queries per workgroup: enough workgroups to fill the GPU
 
 template <int MT, int KS>
-__global__ __launch_bounds__(kBMThreads) void hisa_blocks_bm_kernel(FusedArgs a) {
+__global__ __launch_bounds__(kBlkThreads) void hisa_blocks_bm_kernel(FusedArgs a) {
     constexpr int D = 32 * KS;
-    constexpr int NW = kBMThreads / 64;
+    constexpr int NW = kBlkThreads / 64;
     constexpr int NTW = kBlkTileRows / (16 * NW);
     using QD = QDirect<MT, KS, NW>;
     constexpr int kQElems = QD::kSlots * 8;
@@ -408,7 +412,7 @@ __global__ __launch_bounds__(kBMThreads) void hisa_blocks_bm_kernel(FusedArgs a)
     // the chunk's queries that have a complete block in this tile (b_t > b0)
     if (tid == 0) s_n = 0u;
     __syncthreads();
-    for (int i = tid; i < nqc; i += kBMThreads) {
+    for (int i = tid; i < nqc; i += kBlkThreads) {
         const int qi = s * a.T + i0 + i;
         const int64_t t = query_pos(a.qpos, qi, i0 + i, a.L, a.T);
         if (t >= 0 && t / a.B > b0) {
@@ -428,7 +432,7 @@ __global__ __launch_bounds__(kBMThreads) void hisa_blocks_bm_kernel(FusedArgs a)
         load_row_frag_any<KS>(kb[nt], pool + static_cast<int64_t>(p < a.nblk ? p : 0) * D, lane);
     }
     if (a.H < MT * 16) {
-        for (int x = tid; x < (MT * 16 - a.H) * D; x += kBMThreads) s_q[a.H * D + x] = 0;
+        for (int x = tid; x < (MT * 16 - a.H) * D; x += kBlkThreads) s_q[a.H * D + x] = 0;
         if (tid < 64) s_w[tid] = 0.0f;
     }
     __syncthreads();
@@ -560,11 +564,11 @@ template <int MT>
 hipError_t launch_blocks_mt(const FusedArgs &a, dim3 g_blk, dim3 g_top, hipStream_t st) {
     hipError_t e;
     if (a.d == 64) {
-        e = launch(kKindScoreBlocks, hisa_blocks_bm_kernel<MT, 2>, g_blk, dim3(kBMThreads), 0, st, a);
+        e = launch(kKindScoreBlocks, hisa_blocks_bm_kernel<MT, 2>, g_blk, dim3(kBlkThreads), 0, st, a);
         if (e != hipSuccess) return e;
         return launch_topm<MT, 2>(a, g_top, st);
     }
-    e = launch(kKindScoreBlocks, hisa_blocks_bm_kernel<MT, 4>, g_blk, dim3(kBMThreads), 0, st, a);
+    e = launch(kKindScoreBlocks, hisa_blocks_bm_kernel<MT, 4>, g_blk, dim3(kBlkThreads), 0, st, a);
     if (e != hipSuccess) return e;
     return launch_topm<MT, 4>(a, g_top, st);
 }
