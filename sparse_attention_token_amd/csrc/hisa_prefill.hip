@@ -10,7 +10,7 @@
 // kChunkQueries consecutive queries of one sequence:
 //
 //   hisa_blocks_bm_kernel / hisa_topm_kernel: the block stage the same way --
-//                        128 pooled means per workgroup in registers, the
+//                        256 pooled means per workgroup in registers, the
 //                        chunk's queries streamed through LDS -- then one wave
 //                        per query scores its own block's representative
 //                        (own_mean_kernel) and keeps the top m.
